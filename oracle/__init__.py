@@ -1,0 +1,9 @@
+"""CPU reference (oracle) for dense GEMM -- test infrastructure only.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It shares no code with the GPU library.
+"""
+from .oracle import (  # noqa: F401
+    build, lib_path, gemm_f32, gemm_bf16, gemm_bf16_batched, dot_bf16, dot_f32,
+    round_bf16, num_threads,
+)

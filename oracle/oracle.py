@@ -1,0 +1,144 @@
+"""ctypes wrapper around oracle_gemm.c -- test infrastructure only.
+
+The C file holds the arithmetic (plain FP64 triple loop, bit-level bf16
+rounding); this module only builds it with gcc, loads it and marshals numpy
+arrays.  Nothing here imports the GPU package.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle_gemm.c")
+_LIB = os.path.join(_HERE, "liboracle_gemm.so")
+_lib = None
+
+
+def lib_path():
+    return _LIB
+
+
+def build(verbose=False):
+    """Compile the oracle with gcc (-O2, OpenMP, no FP contraction)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-shared", "-fPIC", "-std=c11", "-Wall", "-o", _LIB + ".tmp", _SRC]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    i64, p = ctypes.c_int64, ctypes.c_void_p
+    lib.oracle_gemm_f64_from_f32.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64]
+    lib.oracle_gemm_f64_from_bf16.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64]
+    lib.oracle_gemm_f64_batched_from_bf16.argtypes = [i64, i64, i64, i64, p, i64, i64,
+                                                      p, i64, i64, p, i64, i64]
+    lib.oracle_dot_f64_from_bf16.argtypes = [i64, p, p, i64, i64]
+    lib.oracle_dot_f64_from_bf16.restype = ctypes.c_double
+    lib.oracle_dot_f64_from_f32.argtypes = [i64, p, p, i64, i64]
+    lib.oracle_dot_f64_from_f32.restype = ctypes.c_double
+    lib.oracle_round_bf16_array.argtypes = [i64, p, p]
+    lib.oracle_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _rows(a, dtype):
+    """Return (array, leading dimension) for a 2-D row-major view with unit
+    column stride (rows may be padded, e.g. a column slice of a wider array)."""
+    if a.ndim != 2 or a.dtype != dtype:
+        raise TypeError(f"expected a 2-D {dtype} array, got {a.dtype} {a.shape}")
+    item = a.dtype.itemsize
+    if a.size == 0:
+        return a, max(a.shape[1], 1)
+    if a.shape[1] > 1 and a.strides[1] != item:
+        raise ValueError("column stride must be 1 element")
+    if a.shape[0] > 1 and (a.strides[0] % item or a.strides[0] < a.shape[1] * item):
+        raise ValueError("row stride must be a whole number of elements >= columns")
+    ld = a.strides[0] // item if a.shape[0] > 1 else max(a.shape[1], 1)
+    return a, ld
+
+
+def gemm_f32(A, B):
+    """C = A.B in double from float32 inputs (unrounded)."""
+    A, lda = _rows(A, np.float32)
+    B, ldb = _rows(B, np.float32)
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    C = np.empty((M, N), np.float64)
+    _load().oracle_gemm_f64_from_f32(M, N, K, A.ctypes.data, lda, B.ctypes.data, ldb,
+                                     C.ctypes.data, max(N, 1))
+    return C
+
+
+def gemm_bf16(A, B):
+    """C = A.B in double from bf16 bit patterns (uint16 arrays)."""
+    A, lda = _rows(A, np.uint16)
+    B, ldb = _rows(B, np.uint16)
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    C = np.empty((M, N), np.float64)
+    _load().oracle_gemm_f64_from_bf16(M, N, K, A.ctypes.data, lda, B.ctypes.data, ldb,
+                                      C.ctypes.data, max(N, 1))
+    return C
+
+
+def gemm_bf16_batched(A, B):
+    """C[b] = A[b].B[b] for contiguous 3-D uint16 stacks; returns double [batch,M,N]."""
+    if A.ndim != 3 or B.ndim != 3 or A.dtype != np.uint16 or B.dtype != np.uint16:
+        raise TypeError("expected 3-D uint16 stacks")
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    batch, M, K = A.shape
+    b2, K2, N = B.shape
+    if batch != b2 or K != K2:
+        raise ValueError("shape mismatch")
+    C = np.empty((batch, M, N), np.float64)
+    _load().oracle_gemm_f64_batched_from_bf16(batch, M, N, K, A.ctypes.data, K, M * K,
+                                              B.ctypes.data, N, K * N,
+                                              C.ctypes.data, N, M * N)
+    return C
+
+
+def dot_bf16(A, B, i, j):
+    """One element C[i, j] of A.B (bf16 bit patterns), in double."""
+    A, lda = _rows(A, np.uint16)
+    B, ldb = _rows(B, np.uint16)
+    K = A.shape[1]
+    row = A[i]
+    return _load().oracle_dot_f64_from_bf16(K, row.ctypes.data, B.ctypes.data, ldb, int(j))
+
+
+def dot_f32(A, B, i, j):
+    """One element C[i, j] of A.B (float32), in double."""
+    A, lda = _rows(A, np.float32)
+    B, ldb = _rows(B, np.float32)
+    K = A.shape[1]
+    row = A[i]
+    return _load().oracle_dot_f64_from_f32(K, row.ctypes.data, B.ctypes.data, ldb, int(j))
+
+
+def round_bf16(x):
+    """float32 array -> bf16 bit patterns (uint16), round to nearest even."""
+    x = np.ascontiguousarray(np.asarray(x, np.float32))
+    out = np.empty(x.shape, np.uint16)
+    _load().oracle_round_bf16_array(x.size, x.ctypes.data, out.ctypes.data)
+    return out
+
+
+def num_threads():
+    return int(_load().oracle_num_threads())

@@ -1,0 +1,152 @@
+/*
+ * oracle_gemm.c -- CPU reference for dense GEMM.  TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load this library.  It shares no code, header, table or helper with the
+ * GPU library; the two are built and linked separately.
+ *
+ * What it computes is the plain definition of the product, written out:
+ *
+ *     C[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j]
+ *
+ * (page "4.1 Tối ưu hiệu năng toán tử GEMM trên CUDA", §1.1 and the naive
+ * kernel of §3.1; MUSA learning center lesson m11-l5, case 4 "GEMM 优化",
+ * problem statement; page "Operator & Runtime", §5.2.1 loop nest).  All three
+ * matrices are row-major; lda/ldb/ldc are row strides in elements.
+ *
+ * Precision: every input element is widened exactly to double, the products
+ * of two float (or bf16) values are exact in double (24+24 significant bits
+ * < 53), and the sum runs in double with k ascending for every (i,j).  The
+ * result is returned unrounded, in double.  The loop order is i, then k, then
+ * j over a double row accumulator -- the same per-element summation order as
+ * the i-j-k nest of the pages, arranged so the inner loop walks contiguous
+ * rows of B ("Operator & Runtime", §5.2.1, discussion of loop order).
+ *
+ * Rows of C are independent; OpenMP splits the i loop, so every element is
+ * produced by one thread in the same order regardless of thread count.
+ *
+ * bf16 handling: a bf16 value is the upper 16 bits of an IEEE binary32
+ * pattern, so widening places the 16 bits in the high half of a float.
+ * The rounding helper turns a binary32 value into bf16 by round to nearest,
+ * ties to even, as the pages require a single round_to_bf16 of the finished
+ * FP32 accumulator ("Operator & Runtime", §5.2.2 and §5.4.3); it is
+ * written from the bit-level definition of that rounding.
+ */
+#include <stdint.h>
+#include <string.h>
+#include <stdlib.h>
+
+static double widen_bf16(uint16_t h)
+{
+    uint32_t u = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* C (double, ldc) := A (float, lda) * B (float, ldb). */
+void oracle_gemm_f64_from_f32(int64_t M, int64_t N, int64_t K,
+                              const float *A, int64_t lda,
+                              const float *B, int64_t ldb,
+                              double *C, int64_t ldc)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < M; ++i) {
+        double *acc = C + i * ldc;
+        for (int64_t j = 0; j < N; ++j) acc[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = (double)A[i * lda + k];
+            const float *brow = B + k * ldb;
+            for (int64_t j = 0; j < N; ++j) acc[j] += a * (double)brow[j];
+        }
+    }
+}
+
+/* C (double, ldc) := A (bf16 bits, lda) * B (bf16 bits, ldb). */
+void oracle_gemm_f64_from_bf16(int64_t M, int64_t N, int64_t K,
+                               const uint16_t *A, int64_t lda,
+                               const uint16_t *B, int64_t ldb,
+                               double *C, int64_t ldc)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < M; ++i) {
+        double *acc = C + i * ldc;
+        for (int64_t j = 0; j < N; ++j) acc[j] = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = widen_bf16(A[i * lda + k]);
+            const uint16_t *brow = B + k * ldb;
+            for (int64_t j = 0; j < N; ++j) acc[j] += a * widen_bf16(brow[j]);
+        }
+    }
+}
+
+/* Batched form: entry b uses A + b*sA, B + b*sB, C + b*sC (elements);
+ * each entry is the single product above ("4.1 Tối ưu hiệu năng toán tử GEMM
+ * trên CUDA", §1.2 names batched GEMM for multi-head attention). */
+void oracle_gemm_f64_batched_from_bf16(int64_t batch, int64_t M, int64_t N, int64_t K,
+                                       const uint16_t *A, int64_t lda, int64_t sA,
+                                       const uint16_t *B, int64_t ldb, int64_t sB,
+                                       double *C, int64_t ldc, int64_t sC)
+{
+    for (int64_t b = 0; b < batch; ++b)
+        oracle_gemm_f64_from_bf16(M, N, K, A + b * sA, lda, B + b * sB, ldb,
+                                  C + b * sC, ldc);
+}
+
+/* One output element, for spot checks at full size: sum_k A[i][k]*B[k][j]
+ * with k ascending, in double. */
+double oracle_dot_f64_from_bf16(int64_t K, const uint16_t *arow, const uint16_t *B,
+                                int64_t ldb, int64_t j)
+{
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k) acc += widen_bf16(arow[k]) * widen_bf16(B[k * ldb + j]);
+    return acc;
+}
+
+double oracle_dot_f64_from_f32(int64_t K, const float *arow, const float *B,
+                               int64_t ldb, int64_t j)
+{
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k) acc += (double)arow[k] * (double)B[k * ldb + j];
+    return acc;
+}
+
+/* binary32 -> bf16 bits, round to nearest, ties to even.
+ * Finite values: keep the upper 16 bits, add one unit in the last kept place
+ * when the dropped 16 bits exceed half a unit, or equal half a unit and the
+ * kept part is odd.  A carry out of the significand moves into the exponent,
+ * which is how the largest finite values round up to infinity.  Infinities
+ * keep their sign; a NaN stays a NaN (its quiet bit is set so that dropping
+ * low payload bits cannot turn it into an infinity). */
+uint16_t oracle_round_bf16(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    const uint32_t exp_bits = (u >> 23) & 0xffu;
+    const uint32_t man_bits = u & 0x7fffffu;
+    if (exp_bits == 0xffu) {
+        if (man_bits != 0) return (uint16_t)((u >> 16) | 0x0040u); /* NaN */
+        return (uint16_t)(u >> 16);                                /* +-Inf */
+    }
+    uint32_t kept = u >> 16;
+    const uint32_t dropped = u & 0xffffu;
+    if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u;
+    return (uint16_t)kept;
+}
+
+void oracle_round_bf16_array(int64_t n, const float *x, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_round_bf16(x[i]);
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
