@@ -1,0 +1,81 @@
+"""Loads libgemm05.so and declares the C signatures of include/gemm05.h.
+
+There is no fallback: if the library is missing or does not load, every
+entry point raises.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgemm05.so")
+
+GEMM_OK = 0
+GEMM_ERR_INVALID_ARG = -1
+GEMM_ERR_UNSUPPORTED = -2
+GEMM_ERR_LAUNCH = -3
+GEMM_ERR_NO_DEVICE = -4
+
+GEMM_OUT_BF16 = 0
+GEMM_OUT_F32 = 1
+
+GEMM_OP_SGEMM = 0
+GEMM_OP_BF16 = 1
+
+GEMM_FAMILY = {0: "none", 1: "zero", 2: "bf16_mfma", 3: "f32_mfma", 4: "decode", 5: "generic"}
+
+# Every symbol declared by include/gemm05.h.
+EXPORTS = ("gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_status_string",
+           "gemm_plan_query", "gemm_model_local_bytes", "gemm_model_traffic_bytes",
+           "gemm_tile_map")
+
+
+class GemmPlan(ctypes.Structure):
+    _fields_ = [("family", ctypes.c_int), ("config_id", ctypes.c_int),
+                ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("tile_k", ctypes.c_int),
+                ("threads", ctypes.c_int), ("vec_a", ctypes.c_int), ("vec_b", ctypes.c_int),
+                ("even", ctypes.c_int), ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int64),
+                ("model_bytes", ctypes.c_double), ("name", ctypes.c_char * 48)]
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run dense_gemm_05_amd.build.build_library()")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, p, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    u64 = ctypes.c_uint64
+    L.gemm_sgemm.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
+    L.gemm_sgemm.restype = i32
+    L.gemm_bf16.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i32, p]
+    L.gemm_bf16.restype = i32
+    L.gemm_bf16_batched.argtypes = [i64, i64, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64, i32, p]
+    L.gemm_bf16_batched.restype = i32
+    L.gemm_status_string.argtypes = [i32]
+    L.gemm_status_string.restype = ctypes.c_char_p
+    L.gemm_plan_query.argtypes = [i32, i64, i64, i64, i64, u64, i64, i64, u64, i64, i64, u64, i64, i64,
+                                  i32, ctypes.POINTER(GemmPlan)]
+    L.gemm_plan_query.restype = i32
+    L.gemm_model_local_bytes.argtypes = [i64, i64, i64, i64]
+    L.gemm_model_local_bytes.restype = i64
+    L.gemm_model_traffic_bytes.argtypes = [i64, i64, i64, i64, i64, i64]
+    L.gemm_model_traffic_bytes.restype = ctypes.c_double
+    L.gemm_tile_map.argtypes = [i64, i64, i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                ctypes.POINTER(i64)]
+    L.gemm_tile_map.restype = i32
+    _lib = L
+    return L
+
+
+def status_string(status):
+    return lib().gemm_status_string(int(status)).decode()

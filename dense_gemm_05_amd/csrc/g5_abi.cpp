@@ -1,0 +1,424 @@
+// g5_abi.cpp -- C entry points of the dense-GEMM library: argument
+// validation, the tile-configuration selector and kernel dispatch.
+//
+// Validation and selection run on the host only and touch no GPU state, so
+// they are usable (through gemm_plan_query) without a device.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/gemm05.h"
+#include "g5_common.h"
+#include "g5_kernels.h"
+
+namespace g5 {
+namespace {
+
+// ------------------------------------------------------------ config table
+const ConfigInfo kConfigs[CFG_COUNT] = {
+    {CFG_NONE, GEMM_FAMILY_NONE, 0, 0, 0, 0, 0, "none"},
+    {CFG_ZERO, GEMM_FAMILY_ZERO, 0, 0, 0, 256, 0, "zero"},
+    {CFG_BF16_256x192, GEMM_FAMILY_BF16_MFMA, 256, 192, 64, 256, 2 * (256 * 64 + 64 * 192) * 2, "bf16_256x192"},
+    {CFG_BF16_256x256, GEMM_FAMILY_BF16_MFMA, 256, 256, 64, 256, 2 * (256 * 64 + 64 * 256) * 2, "bf16_256x256"},
+    {CFG_BF16_128x128, GEMM_FAMILY_BF16_MFMA, 128, 128, 64, 256, 2 * (128 * 64 + 64 * 128) * 2, "bf16_128x128"},
+    {CFG_BF16_256x128, GEMM_FAMILY_BF16_MFMA, 256, 128, 64, 256, 2 * (256 * 64 + 64 * 128) * 2, "bf16_256x128"},
+    {CFG_F32_128x128, GEMM_FAMILY_F32_MFMA, 128, 128, 32, 256, 2 * (128 * 32 + 32 * 132) * 4, "f32_128x128"},
+    {CFG_F32_64x64, GEMM_FAMILY_F32_MFMA, 64, 64, 32, 256, 2 * (64 * 32 + 32 * 68) * 4, "f32_64x64"},
+    {CFG_DECODE_64, GEMM_FAMILY_DECODE, 16, 64, 32, 1024, 16 * 64 * 16 * 4, "decode_64"},
+    {CFG_GENERIC, GEMM_FAMILY_GENERIC, 16, 16, 16, 256, 2 * 16 * 17 * 4, "generic"},
+};
+
+// MI355X figures used by the selector's cost model.
+constexpr int kNumCU = 256;
+constexpr int64_t kLdsPerCU = 160 * 1024;
+constexpr double kHbmBytesPerS = 8.0e12;
+constexpr double kBf16FlopsPerCUperS = 2.5166e15 / kNumCU;
+constexpr double kF32FlopsPerCUperS = 157.3e12 / kNumCU;
+
+struct Problem {
+    int op;  // gemm_op
+    int64_t batch, M, N, K;
+    uint64_t a, b, c;
+    int64_t lda, ldb, ldc, sA, sB, sC;
+    int c_type;
+};
+
+struct Plan {
+    int config = CFG_NONE;
+    bool even = false;
+    int64_t grid = 0;
+    int64_t tiles_m = 0, tiles_n = 0, group_m = 1;
+    int align_a = 2, align_b = 2, align_c = 2;
+    double model_bytes = 0.0;
+};
+
+int elem_a(const Problem &p) { return p.op == GEMM_OP_SGEMM ? 4 : 2; }
+int elem_c(const Problem &p) { return (p.op == GEMM_OP_SGEMM || p.c_type == GEMM_OUT_F32) ? 4 : 2; }
+
+// Largest power of two <= 16 dividing the address of every row start of an
+// operand (pointer, row stride and batch stride all in bytes).
+int row_alignment(uint64_t ptr, int64_t ld, int64_t stride, int64_t batch, int esz)
+{
+    uint64_t bits = ptr | (uint64_t)(ld * esz);
+    if (batch > 1) bits |= (uint64_t)(stride * esz);
+    int a = 16;
+    while (a > 1 && (bits % (uint64_t)a) != 0) a >>= 1;
+    return a;
+}
+
+// [lo, hi) byte range touched by an operand with rows x cols elements.
+struct Range {
+    __int128 lo, hi;
+};
+Range extent(uint64_t ptr, int64_t batch, int64_t rows, int64_t cols, int64_t ld, int64_t stride, int esz)
+{
+    __int128 last = (__int128)(batch - 1) * stride + (__int128)(rows - 1) * ld + cols;
+    return Range{(__int128)ptr, (__int128)ptr + last * esz};
+}
+bool overlap(const Range &x, const Range &y) { return x.lo < y.hi && y.lo < x.hi; }
+
+int validate(const Problem &p)
+{
+    if (p.op != GEMM_OP_SGEMM && p.op != GEMM_OP_BF16) return GEMM_ERR_INVALID_ARG;
+    if (p.batch < 0 || p.M < 0 || p.N < 0 || p.K < 0) return GEMM_ERR_INVALID_ARG;
+    if (p.op == GEMM_OP_BF16 && p.c_type != GEMM_OUT_BF16 && p.c_type != GEMM_OUT_F32)
+        return GEMM_ERR_INVALID_ARG;
+    if (p.sA < 0 || p.sB < 0 || p.sC < 0) return GEMM_ERR_INVALID_ARG;
+    if (p.batch == 0 || p.M == 0 || p.N == 0) return GEMM_OK;  // nothing to do
+    if (p.ldc < p.N || p.c == 0) return GEMM_ERR_INVALID_ARG;
+    if (p.batch > 1 && (__int128)p.sC < (__int128)(p.M - 1) * p.ldc + p.N) return GEMM_ERR_INVALID_ARG;
+    const Range rc = extent(p.c, p.batch, p.M, p.N, p.ldc, p.sC, elem_c(p));
+    if (rc.hi > ((__int128)1 << 63)) return GEMM_ERR_INVALID_ARG;
+    if (p.K == 0) return GEMM_OK;
+    if (p.lda < p.K || p.ldb < p.N || p.a == 0 || p.b == 0) return GEMM_ERR_INVALID_ARG;
+    const Range ra = extent(p.a, p.batch, p.M, p.K, p.lda, p.sA, elem_a(p));
+    const Range rb = extent(p.b, p.batch, p.K, p.N, p.ldb, p.sB, elem_a(p));
+    if (ra.hi > ((__int128)1 << 63) || rb.hi > ((__int128)1 << 63)) return GEMM_ERR_INVALID_ARG;
+    if (overlap(rc, ra) || overlap(rc, rb)) return GEMM_ERR_INVALID_ARG;
+    return GEMM_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Workgroups of a config that fit on one CU at once (LDS-limited; every
+// tiled config here runs 4 waves per workgroup).
+int wg_per_cu(const ConfigInfo &c)
+{
+    if (c.lds_bytes <= 0) return 8;
+    int64_t n = kLdsPerCU / c.lds_bytes;
+    if (n < 1) n = 1;
+    if (c.family == GEMM_FAMILY_BF16_MFMA && c.tile_m * c.tile_n > 128 * 128) n = 1;  // 1 wave/SIMD (registers)
+    if (n > 2) n = 2;
+    return (int)n;
+}
+
+// Cost model of a tiled config (seconds): the slower of the matrix-core time
+// -- whole waves of tiles over the CUs, each tile padded to full size -- and
+// the interface traffic of "Operator & Runtime" §5.2.2 over HBM bandwidth,
+// divided by a relative efficiency measured per tile shape.
+double model_time(const Problem &p, const ConfigInfo &c, double eff)
+{
+    const int64_t tm = cdiv(p.M, c.tile_m), tn = cdiv(p.N, c.tile_n);
+    const int64_t tiles = p.batch * tm * tn;
+    const int occ = wg_per_cu(c);
+    const int64_t waves = cdiv(tiles, (int64_t)kNumCU * occ);
+    const double rate = (p.op == GEMM_OP_SGEMM ? kF32FlopsPerCUperS : kBf16FlopsPerCUperS);
+    const double kpad = (double)cdiv(p.K, c.tile_k) * c.tile_k;
+    const double t_compute = (double)waves * occ * (2.0 * c.tile_m * c.tile_n * kpad) / rate;
+    const double bytes = p.batch * gemm_model_traffic_bytes(p.M, p.N, p.K, c.tile_m, c.tile_n, elem_a(p)) +
+                         (double)p.batch * p.M * p.N * (elem_c(p) - elem_a(p));
+    const double t_mem = bytes / kHbmBytesPerS;
+    return (t_compute > t_mem ? t_compute : t_mem) / eff;
+}
+
+int find_config_by_name(const char *name)
+{
+    for (int i = 0; i < CFG_COUNT; ++i)
+        if (std::strcmp(kConfigs[i].name, name) == 0) return i;
+    return -1;
+}
+
+bool config_fits(const Problem &p, int id)
+{
+    const ConfigInfo &c = kConfigs[id];
+    switch (c.family) {
+    case GEMM_FAMILY_BF16_MFMA: return p.op == GEMM_OP_BF16;
+    case GEMM_FAMILY_F32_MFMA: return p.op == GEMM_OP_SGEMM;
+    case GEMM_FAMILY_DECODE: return p.op == GEMM_OP_BF16 && p.M <= 16 && p.batch <= 65535;
+    case GEMM_FAMILY_GENERIC: return true;
+    default: return false;
+    }
+}
+
+void fill_grid(const Problem &p, Plan &pl)
+{
+    const ConfigInfo &c = kConfigs[pl.config];
+    switch (c.family) {
+    case GEMM_FAMILY_ZERO: {
+        const int64_t total = p.batch * p.M * p.N;
+        int64_t g = cdiv(total, 256);
+        if (g > 4096) g = 4096;
+        pl.grid = g;
+        break;
+    }
+    case GEMM_FAMILY_DECODE:
+        pl.tiles_m = 1;
+        pl.tiles_n = cdiv(p.N, c.tile_n);
+        pl.grid = pl.tiles_n;  // x; batch goes to grid y
+        break;
+    default:
+        pl.tiles_m = cdiv(p.M, c.tile_m);
+        pl.tiles_n = cdiv(p.N, c.tile_n);
+        pl.grid = p.batch * pl.tiles_m * pl.tiles_n;
+        break;
+    }
+    // Column bands as tall as the whole M extent when it is only a few tiles
+    // (each XCD then owns whole column panels of B), else 8 tiles tall.
+    pl.group_m = pl.tiles_m <= 8 ? (pl.tiles_m > 0 ? pl.tiles_m : 1) : 8;
+    pl.model_bytes = (c.tile_m > 0 && p.K > 0)
+                         ? p.batch * gemm_model_traffic_bytes(p.M, p.N, p.K, c.tile_m, c.tile_n, elem_a(p))
+                         : 0.0;
+}
+
+bool even_ok(const Problem &p, const Plan &pl)
+{
+    const ConfigInfo &c = kConfigs[pl.config];
+    if (c.family != GEMM_FAMILY_BF16_MFMA && c.family != GEMM_FAMILY_F32_MFMA) return false;
+    if (p.M % c.tile_m || p.N % c.tile_n || p.K % c.tile_k) return false;
+    if (pl.align_a < 16 || pl.align_b < 16) return false;
+    if (pl.align_c < (elem_c(p) == 4 ? 16 : 8)) return false;
+    return true;
+}
+
+// Returns GEMM_OK or GEMM_ERR_UNSUPPORTED.
+int select_plan(const Problem &p, Plan &pl)
+{
+    pl = Plan();
+    if (p.batch == 0 || p.M == 0 || p.N == 0) {
+        pl.config = CFG_NONE;
+        return GEMM_OK;
+    }
+    const int ea = elem_a(p), ec = elem_c(p);
+    pl.align_a = row_alignment(p.a, p.lda, p.sA, p.batch, ea);
+    pl.align_b = row_alignment(p.b, p.ldb, p.sB, p.batch, ea);
+    pl.align_c = row_alignment(p.c, p.ldc, p.sC, p.batch, ec);
+    if (p.K == 0) {
+        pl.config = CFG_ZERO;
+        fill_grid(p, pl);
+        return GEMM_OK;
+    }
+
+    const char *force = std::getenv("GEMM_FORCE_CONFIG");
+    if (force && *force) {
+        const int id = find_config_by_name(force);
+        if (id < 0 || !config_fits(p, id) || kConfigs[id].family == GEMM_FAMILY_ZERO ||
+            kConfigs[id].family == GEMM_FAMILY_NONE)
+            return GEMM_ERR_UNSUPPORTED;
+        pl.config = id;
+    } else if (p.op == GEMM_OP_BF16 && p.M <= 16 && p.batch <= 65535) {
+        pl.config = CFG_DECODE_64;
+    } else {
+        // Candidates with their measured relative efficiency; the model
+        // picks the fastest (page "Operator & Runtime" §5.4.5: feasibility,
+        // then an estimate, then measurement).
+        struct Cand {
+            int id;
+            double eff;
+        };
+        static const Cand bf16c[] = {{CFG_BF16_256x192, 1.0}, {CFG_BF16_256x128, 0.95}, {CFG_BF16_128x128, 0.85}};
+        static const Cand f32c[] = {{CFG_F32_128x128, 1.0}, {CFG_F32_64x64, 0.8}};
+        const Cand *cands = p.op == GEMM_OP_BF16 ? bf16c : f32c;
+        const int nc = p.op == GEMM_OP_BF16 ? 3 : 2;
+        double best = 0.0;
+        for (int i = 0; i < nc; ++i) {
+            const double t = model_time(p, kConfigs[cands[i].id], cands[i].eff);
+            if (pl.config == CFG_NONE || t < best) {
+                best = t;
+                pl.config = cands[i].id;
+            }
+        }
+    }
+    fill_grid(p, pl);
+    if (pl.grid <= 0 || pl.grid > (int64_t)1 << 24) return GEMM_ERR_UNSUPPORTED;
+    pl.even = even_ok(p, pl);
+    return GEMM_OK;
+}
+
+void fill_public_plan(const Problem &p, const Plan &pl, gemm_plan *out)
+{
+    if (!out) return;
+    std::memset(out, 0, sizeof *out);
+    const ConfigInfo &c = kConfigs[pl.config];
+    out->family = c.family;
+    out->config_id = pl.config;
+    out->tile_m = c.tile_m;
+    out->tile_n = c.tile_n;
+    out->tile_k = c.tile_k;
+    out->threads = c.threads;
+    out->vec_a = pl.align_a;
+    out->vec_b = pl.align_b;
+    out->even = pl.even ? 1 : 0;
+    out->grid = pl.grid * (c.family == GEMM_FAMILY_DECODE ? p.batch : 1);
+    out->lds_bytes = c.lds_bytes;
+    out->model_bytes = pl.model_bytes;
+    std::snprintf(out->name, sizeof out->name, "%s", c.name);
+}
+
+// ------------------------------------------------------------ device check
+std::mutex g_dev_mu;
+int g_dev_state[64];  // 0 unknown, 1 ok, -1 unsupported
+
+int check_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_ERR_NO_DEVICE;
+    if (dev >= 64) return GEMM_OK;
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_dev_state[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_NO_DEVICE;
+        g_dev_state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+    return g_dev_state[dev] == 1 ? GEMM_OK : GEMM_ERR_UNSUPPORTED;
+}
+
+bool log_enabled()
+{
+    static int v = -1;
+    if (v < 0) {
+        const char *e = std::getenv("GEMM_LOG");
+        v = (e && *e && *e != '0') ? 1 : 0;
+    }
+    return v == 1;
+}
+
+int run(const Problem &p, void *stream)
+{
+    int st = validate(p);
+    if (st != GEMM_OK) return st;
+    Plan pl;
+    st = select_plan(p, pl);
+    if (st != GEMM_OK) return st;
+    if (pl.config == CFG_NONE) return GEMM_OK;
+    st = check_device();
+    if (st != GEMM_OK) return st;
+    if (log_enabled())
+        std::fprintf(stderr, "[gemm05] op=%d batch=%lld M=%lld N=%lld K=%lld -> %s even=%d grid=%lld align=(%d,%d,%d)\n",
+                     p.op, (long long)p.batch, (long long)p.M, (long long)p.N, (long long)p.K,
+                     kConfigs[pl.config].name, pl.even ? 1 : 0, (long long)pl.grid, pl.align_a, pl.align_b,
+                     pl.align_c);
+    GemmArgs a;
+    a.A = (const void *)p.a;
+    a.B = (const void *)p.b;
+    a.C = (void *)p.c;
+    a.M = p.M;
+    a.N = p.N;
+    a.K = p.K;
+    a.lda = p.lda;
+    a.ldb = p.ldb;
+    a.ldc = p.ldc;
+    a.sA = p.sA;
+    a.sB = p.sB;
+    a.sC = p.sC;
+    a.batch = p.batch;
+    a.tiles_m = pl.tiles_m;
+    a.tiles_n = pl.tiles_n;
+    a.group_m = pl.group_m;
+    a.align_a = pl.align_a;
+    a.align_b = pl.align_b;
+    a.align_c = pl.align_c;
+    a.out_f32 = elem_c(p) == 4 ? 1 : 0;
+    const hipError_t e = launch_config(pl.config, p.op == GEMM_OP_SGEMM, a, pl.even, pl.grid, (hipStream_t)stream);
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace g5
+
+using g5::Problem;
+
+extern "C" {
+
+int gemm_sgemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B, int64_t ldb,
+               float *C, int64_t ldc, void *stream)
+{
+    const Problem p{GEMM_OP_SGEMM, 1, M, N, K, (uint64_t)A, (uint64_t)B, (uint64_t)C, lda, ldb, ldc, 0, 0, 0,
+                    GEMM_OUT_F32};
+    return g5::run(p, stream);
+}
+
+int gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+              void *C, int64_t ldc, int c_type, void *stream)
+{
+    const Problem p{GEMM_OP_BF16, 1, M, N, K, (uint64_t)A, (uint64_t)B, (uint64_t)C, lda, ldb, ldc, 0, 0, 0,
+                    c_type};
+    return g5::run(p, stream);
+}
+
+int gemm_bf16_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                      int64_t strideA, const uint16_t *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc,
+                      int64_t strideC, int c_type, void *stream)
+{
+    const Problem p{GEMM_OP_BF16, batch, M, N, K, (uint64_t)A, (uint64_t)B, (uint64_t)C, lda, ldb, ldc,
+                    strideA, strideB, strideC, c_type};
+    return g5::run(p, stream);
+}
+
+const char *gemm_status_string(int status)
+{
+    switch (status) {
+    case GEMM_OK: return "GEMM_OK: success";
+    case GEMM_ERR_INVALID_ARG: return "GEMM_ERR_INVALID_ARG: invalid size, stride, pointer, output type or overlap";
+    case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED: no compiled kernel configuration can run this call";
+    case GEMM_ERR_LAUNCH: return "GEMM_ERR_LAUNCH: kernel launch failed";
+    case GEMM_ERR_NO_DEVICE: return "GEMM_ERR_NO_DEVICE: no usable HIP device is current";
+    default: return "unknown gemm status";
+    }
+}
+
+int gemm_plan_query(int op, int64_t batch, int64_t M, int64_t N, int64_t K, uint64_t a_addr, int64_t lda,
+                    int64_t strideA, uint64_t b_addr, int64_t ldb, int64_t strideB, uint64_t c_addr, int64_t ldc,
+                    int64_t strideC, int c_type, gemm_plan *out)
+{
+    const Problem p{op, batch, M, N, K, a_addr, b_addr, c_addr, lda, ldb, ldc, strideA, strideB, strideC,
+                    op == GEMM_OP_SGEMM ? (int)GEMM_OUT_F32 : c_type};
+    int st = g5::validate(p);
+    if (st != GEMM_OK) return st;
+    g5::Plan pl;
+    st = g5::select_plan(p, pl);
+    if (st != GEMM_OK) return st;
+    g5::fill_public_plan(p, pl, out);
+    return GEMM_OK;
+}
+
+int64_t gemm_model_local_bytes(int64_t m, int64_t n, int64_t k, int64_t elem_bytes)
+{
+    return elem_bytes * m * k + elem_bytes * k * n + 4 * m * n;
+}
+
+double gemm_model_traffic_bytes(int64_t M, int64_t N, int64_t K, int64_t m, int64_t n, int64_t elem_bytes)
+{
+    if (m <= 0 || n <= 0) return 0.0;
+    const double e = (double)elem_bytes;
+    return e * M * K * (double)((N + n - 1) / n) + e * K * N * (double)((M + m - 1) / m) + e * M * N;
+}
+
+int gemm_tile_map(int64_t wg, int64_t batch, int64_t tiles_m, int64_t tiles_n, int64_t group_m, int64_t *b,
+                  int64_t *tm, int64_t *tn)
+{
+    if (batch <= 0 || tiles_m <= 0 || tiles_n <= 0 || group_m <= 0 || wg < 0 ||
+        wg >= batch * tiles_m * tiles_n || !b || !tm || !tn)
+        return -1;
+    const g5::TileCoord t = g5::tile_map(wg, batch, tiles_m, tiles_n, group_m);
+    *b = t.b;
+    *tm = t.tm;
+    *tn = t.tn;
+    return 0;
+}
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// g5_common.h -- definitions shared by the host dispatcher and the gfx950
+// kernels of the dense-GEMM library: the workgroup -> tile map, the kernel
+// argument block and the table of compiled kernel configurations.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define G5_HD __host__ __device__
+#else
+#define G5_HD
+#endif
+
+namespace g5 {
+
+// Workgroups of one launch are handed to the 8 XCDs of an MI355X in
+// round-robin order (workgroup w runs on XCD w % 8).  Each XCD has a private
+// L2, so the map below first gathers the ids that land on one XCD into a
+// contiguous run of logical tile indices, then walks the tile grid in column
+// bands `group_m` tiles tall, column by column.  Tiles resident on one XCD at
+// the same time then share a few row panels of A and column panels of B.
+// This is the block-order argument of page "4.1 Tối ưu hiệu năng toán tử GEMM
+// trên CUDA" (§2.3: block order moves the L2 hit rate) and the block-id
+// swizzle of MUSA lesson m11-l5 (case 4: changing rows every few blocks lets
+// A and B panels both be reused), re-derived for an XCD-partitioned L2.
+constexpr int kNumXcd = 8;
+
+struct TileCoord {
+    int64_t b, tm, tn;
+};
+
+G5_HD inline TileCoord tile_map(int64_t wg, int64_t batch, int64_t tiles_m, int64_t tiles_n,
+                                int64_t group_m)
+{
+    const int64_t per_batch = tiles_m * tiles_n;
+    const int64_t total = batch * per_batch;
+    const int64_t rounds = total / kNumXcd;
+    int64_t L = wg;
+    if (wg < rounds * kNumXcd) L = (wg % kNumXcd) * rounds + wg / kNumXcd;
+    TileCoord t;
+    t.b = L / per_batch;
+    const int64_t r = L - t.b * per_batch;
+    const int64_t band_tiles = group_m * tiles_n;
+    const int64_t band = r / band_tiles;
+    const int64_t first_m = band * group_m;
+    const int64_t rem_m = tiles_m - first_m;
+    const int64_t h = rem_m < group_m ? rem_m : group_m;
+    const int64_t rr = r - band * band_tiles;
+    t.tm = first_m + rr % h;
+    t.tn = rr / h;
+    return t;
+}
+
+// Argument block shared by all tiled kernels (passed by value).
+struct GemmArgs {
+    const void *A;
+    const void *B;
+    void *C;
+    int64_t M, N, K;
+    int64_t lda, ldb, ldc;
+    int64_t sA, sB, sC;      // batch strides in elements
+    int64_t batch;
+    int64_t tiles_m, tiles_n;
+    int64_t group_m;
+    int32_t align_a;         // 16, 8, 4 or 2: alignment of every row start of A
+    int32_t align_b;
+    int32_t align_c;
+    int32_t out_f32;         // 1: C is float, 0: C is bf16 bits
+};
+
+// Compiled configurations.  The selector picks one; GEMM_FORCE_CONFIG may
+// name one explicitly.
+enum ConfigId {
+    CFG_NONE = 0,
+    CFG_ZERO,
+    CFG_BF16_256x192,      // 4 waves (2x2), wave tile 128x96
+    CFG_BF16_256x256,      // 4 waves (2x2), wave tile 128x128
+    CFG_BF16_128x128,      // 4 waves (2x2), wave tile 64x64
+    CFG_BF16_256x128,      // 4 waves (2x2), wave tile 128x64
+    CFG_F32_128x128,       // 4 waves (2x2), wave tile 64x64
+    CFG_F32_64x64,         // 4 waves (2x2), wave tile 32x32
+    CFG_DECODE_64,         // small M, 64 columns per workgroup, 16 waves
+    CFG_GENERIC,
+    CFG_COUNT
+};
+
+struct ConfigInfo {
+    int id;
+    int family;            // gemm_family
+    int tile_m, tile_n, tile_k;
+    int threads;
+    int lds_bytes;
+    const char *name;
+};
+
+}  // namespace g5

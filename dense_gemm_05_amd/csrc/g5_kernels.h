@@ -1,0 +1,16 @@
+// g5_kernels.h -- launch entry of the gfx950 kernels (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "g5_common.h"
+
+namespace g5 {
+
+// Enqueue compiled configuration `config_id` on stream `s` with `grid`
+// workgroups.  `even` selects the variant without edge masking; the caller
+// guarantees its preconditions.  Returns the launch status.
+hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, bool even, int64_t grid,
+                         hipStream_t s);
+
+}  // namespace g5

@@ -1,0 +1,617 @@
+// g5_kernels.hip -- gfx950 (CDNA4) kernels of the dense-GEMM library.
+//
+// Every kernel computes C[i][j] = sum_k A[i][k] B[k][j] for row-major
+// operands (page "4.1 Tối ưu hiệu năng toán tử GEMM trên CUDA", §1.1; page
+// "Operator & Runtime", §5.2.1).  The tiled kernels follow the structure that
+// both pages build up -- an output tile per workgroup, K walked in slabs
+// staged through on-chip memory, double buffered, accumulators kept in
+// registers -- re-designed for the CDNA4 execution model:
+//
+//  * 64-lane waves; the inner product runs on the matrix cores
+//    (v_mfma_f32_16x16x32_bf16 for bf16, v_mfma_f32_16x16x4_f32 for fp32).
+//  * Each wave computes its sub-tile transposed, D = B^T A^T, so that a lane
+//    ends up owning 4 consecutive columns of one row of C and can store them
+//    with one 8-byte (bf16) or 16-byte (fp32) write.
+//  * The bf16 B operand (N-contiguous in memory, needed K-contiguous per lane
+//    by the matrix core) is read from LDS with the gfx950 transposing read
+//    ds_read_b64_tr_b16; A (K-contiguous) is read with ds_read_b128.
+//  * LDS layouts use XOR swizzles of 16-byte chunks so that the fragment
+//    reads spread over the LDS banks (the padding/XOR remedies of page "4.1"
+//    §8.5 and "Operator & Runtime" §5.2.3, with gfx950 constants).
+//  * Out-of-range elements of A and B load as zero and only in-range
+//    elements of C are written (page "4.1" §4.5; "Operator & Runtime" §5.4.2
+//    masked last tile).  The FP32 sum of a bf16 output is rounded once, to
+//    nearest even ("Operator & Runtime" §5.4.3).
+#include <hip/hip_runtime.h>
+
+#include "g5_common.h"
+#include "g5_kernels.h"
+
+namespace g5 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define G5_LDS(T, p) ((__attribute__((address_space(3))) T *)(p))
+
+// ---------------------------------------------------------------- helpers
+
+// FP32 -> bf16 bits, round to nearest even; NaN stays NaN (quiet bit set),
+// infinities keep their sign.
+__device__ __forceinline__ uint32_t bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u) return (u & 0x007fffffu) ? ((u >> 16) | 0x40u) : (u >> 16);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return bf16_rne(lo) | (bf16_rne(hi) << 16);
+}
+
+// Load 8 consecutive bf16 elements (one 16-byte chunk) starting at element
+// `col` of a row, zero for elements at or beyond `limit` or when the row is
+// out of range.  `align` is the byte alignment of the row start (16/8/4/2);
+// col is a multiple of 8, so the chunk has the same alignment.
+__device__ __forceinline__ u32x4 load_chunk8_bf16(const uint16_t *row, int64_t col, int64_t limit,
+                                                  bool row_ok, int align)
+{
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (!row_ok) return v;
+    const uint16_t *p = row + col;
+    if (col + 8 <= limit) {
+        if (align >= 16) return *(const u32x4 *)p;
+        if (align >= 8) {
+            u32x2 lo = *(const u32x2 *)p, hi = *(const u32x2 *)(p + 4);
+            v[0] = lo[0]; v[1] = lo[1]; v[2] = hi[0]; v[3] = hi[1];
+            return v;
+        }
+        if (align >= 4) {
+            const uint32_t *q = (const uint32_t *)p;
+            v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
+            return v;
+        }
+    }
+    uint32_t e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = (col + i < limit) ? (uint32_t)p[i] : 0u;
+    v[0] = e[0] | (e[1] << 16); v[1] = e[2] | (e[3] << 16);
+    v[2] = e[4] | (e[5] << 16); v[3] = e[6] | (e[7] << 16);
+    return v;
+}
+
+// Same for 4 consecutive floats (one 16-byte chunk of an fp32 row).
+__device__ __forceinline__ u32x4 load_chunk4_f32(const float *row, int64_t col, int64_t limit,
+                                                 bool row_ok, int align)
+{
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (!row_ok) return v;
+    const float *p = row + col;
+    if (col + 4 <= limit) {
+        if (align >= 16) return *(const u32x4 *)p;
+        if (align >= 8) {
+            u32x2 lo = *(const u32x2 *)p, hi = *(const u32x2 *)(p + 2);
+            v[0] = lo[0]; v[1] = lo[1]; v[2] = hi[0]; v[3] = hi[1];
+            return v;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (col + i < limit) ? __float_as_uint(p[i]) : 0u;
+    return v;
+}
+
+// Store 4 consecutive results of one row of C (columns n..n+3).
+__device__ __forceinline__ void store4(void *Cbase, bool out_f32, int64_t ldc, int64_t m, int64_t n,
+                                       f32x4 v, bool full, int64_t M, int64_t N, int align_c)
+{
+    if (out_f32) {
+        float *c = (float *)Cbase + m * ldc + n;
+        if (full && align_c >= 16) {
+            *(f32x4 *)c = v;
+            return;
+        }
+        if (m >= M) return;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (n + j < N) c[j] = v[j];
+    } else {
+        uint16_t *c = (uint16_t *)Cbase + m * ldc + n;
+        const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+        if (full && align_c >= 8) {
+            u32x2 w = {lo, hi};
+            *(u32x2 *)c = w;
+            return;
+        }
+        if (m >= M) return;
+        const uint16_t e[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (n + j < N) c[j] = e[j];
+    }
+}
+
+// XOR swizzles of 16-byte chunk indices.
+//  A slab rows hold 8 chunks (64 bf16 or 32 fp32): the chunk index is XORed
+//  with a function of the row that is distinct over any 8 consecutive rows
+//  and, paired with the row's parity, over any 16 consecutive rows.
+__device__ __forceinline__ int swz_a(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+//  bf16 B slab rows (k) are read 4 rows x 32 bytes per 16 lanes by the
+//  transposing read; XORing chunk bits 1..2 (a 32-byte segment inside an
+//  aligned group of 4 segments) with this function of k spreads the 8 rows
+//  {k0..k0+3, k0+8..k0+11} that 32 lanes read over distinct banks.
+__device__ __forceinline__ int swz_b(int k) { return ((((k >> 1) & 1) | (((k >> 3) & 1) << 1))) << 1; }
+
+// ===================================================== bf16 tiled MFMA kernel
+//
+// Workgroup tile BM x BN, K slab 64, WGM x WGN waves each owning a
+// (BM/WGM) x (BN/WGN) sub-tile as 16x16 MFMA blocks.  Two LDS buffers; the
+// global loads of slab k+1 are issued before the MFMAs of slab k and written
+// to the other buffer after them, with one barrier per slab (page "4.1" §9.4;
+// MUSA lesson m11-l5 case 4 double buffering).
+template <int BM, int BN, int WGM, int WGN, bool EVEN>
+__global__ void __launch_bounds__(WGM *WGN * 64, 1) k_bf16_mfma(GemmArgs p)
+{
+    constexpr int T = WGM * WGN * 64;
+    constexpr int BK = 64;
+    constexpr int TM = BM / WGM, TN = BN / WGN;
+    constexpr int FM = TM / 16, FN = TN / 16;
+    constexpr int A_CPR = BK / 8;            // 16-byte chunks per A slab row
+    constexpr int B_CPR = BN / 8;            // chunks per B slab row
+    constexpr int CA = BM * A_CPR / T;       // A chunks per thread
+    constexpr int CB = BK * B_CPR / T;       // B chunks per thread
+    constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN;
+    static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole MFMA blocks");
+    static_assert((BM * A_CPR) % T == 0 && (BK * B_CPR) % T == 0, "slab chunks must divide threads");
+    static_assert(B_CPR % 8 == 0, "B slab rows must be whole swizzle groups");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (A_ELEMS + B_ELEMS)];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int g = lane >> 4, li = lane & 15;
+
+    const TileCoord tc = tile_map(blockIdx.x, p.batch, p.tiles_m, p.tiles_n, p.group_m);
+    const int64_t m0 = tc.tm * BM, n0 = tc.tn * BN;
+    const int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const uint16_t *Ab = (const uint16_t *)p.A + tc.b * p.sA + m0 * lda;
+    const uint16_t *Bb = (const uint16_t *)p.B + tc.b * p.sB + n0;
+
+    // Per-thread chunk coordinates in the slabs.
+    int a_row[CA], a_c[CA], b_row[CB], b_c[CB];
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+        const int q = tid + T * i;
+        a_row[i] = q / A_CPR;
+        a_c[i] = q % A_CPR;
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+        const int q = tid + T * i;
+        b_row[i] = q / B_CPR;
+        b_c[i] = q % B_CPR;
+    }
+
+    u32x4 ra[CA], rb[CB];
+    auto load_slab = [&](int kt) {
+        const int64_t k0 = (int64_t)kt * BK;
+#pragma unroll
+        for (int i = 0; i < CA; ++i) {
+            const uint16_t *row = Ab + (int64_t)a_row[i] * lda;
+            if (EVEN) {
+                ra[i] = *(const u32x4 *)(row + k0 + a_c[i] * 8);
+            } else {
+                ra[i] = load_chunk8_bf16(row, k0 + a_c[i] * 8, K, m0 + a_row[i] < M, p.align_a);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            const int64_t k = k0 + b_row[i];
+            const uint16_t *row = Bb + k * ldb;
+            if (EVEN) {
+                rb[i] = *(const u32x4 *)(row + b_c[i] * 8);
+            } else {
+                rb[i] = load_chunk8_bf16(row, b_c[i] * 8, N - n0, k < K, p.align_b);
+            }
+        }
+    };
+    auto store_slab = [&](int buf) {
+        uint16_t *As = smem + buf * (A_ELEMS + B_ELEMS);
+        uint16_t *Bs = As + A_ELEMS;
+#pragma unroll
+        for (int i = 0; i < CA; ++i)
+            *(u32x4 *)(As + a_row[i] * BK + ((a_c[i] ^ swz_a(a_row[i])) * 8)) = ra[i];
+#pragma unroll
+        for (int i = 0; i < CB; ++i)
+            *(u32x4 *)(Bs + b_row[i] * BN + ((b_c[i] ^ swz_b(b_row[i])) * 8)) = rb[i];
+    };
+
+    f32x4 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int KT = (int)((K + BK - 1) / BK);
+    load_slab(0);
+    store_slab(0);
+    __syncthreads();
+
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < KT) load_slab(kt + 1);
+        const uint16_t *As = smem + cur * (A_ELEMS + B_ELEMS);
+        const uint16_t *Bs = As + A_ELEMS;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 af[FM], bfr[FN];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int row = wm * TM + fm * 16 + li;
+                const int c = ks * 4 + g;
+                const u32x4 v = *(const u32x4 *)(As + row * BK + ((c ^ swz_a(row)) * 8));
+                af[fm] = __builtin_bit_cast(bf16x8, v);
+            }
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int k = ks * 32 + g * 8 + (li >> 2);
+                const int ncol = wn * TN + fn * 16 + (li & 3) * 4;
+                const int c = ncol >> 3, half = (ncol >> 2) & 1;
+                const uint16_t *p0 = Bs + k * BN + ((c ^ swz_b(k)) * 8) + half * 4;
+                const uint16_t *p1 = Bs + (k + 4) * BN + ((c ^ swz_b(k + 4)) * 8) + half * 4;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G5_LDS(i16x4, p0));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G5_LDS(i16x4, p1));
+                typedef short i16x8 __attribute__((ext_vector_type(8)));
+                const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                bfr[fn] = __builtin_bit_cast(bf16x8, v);
+            }
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+                    acc[fn][fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[fn], af[fm], acc[fn][fm], 0, 0, 0);
+        }
+        if (kt + 1 < KT) store_slab(cur ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue: lane (g, li) of block (fn, fm) holds C[m][n..n+3].
+    void *Cb = (char *)p.C + tc.b * p.sC * (p.out_f32 ? 4 : 2);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int64_t m = m0 + wm * TM + fm * 16 + li;
+            const int64_t n = n0 + wn * TN + fn * 16 + g * 4;
+            const bool full = EVEN || (m < M && n + 4 <= N);
+            if (!EVEN && (m >= M || n >= N)) continue;
+            store4(Cb, p.out_f32 != 0, p.ldc, m, n, acc[fn][fm], full, M, N, p.align_c);
+        }
+}
+
+// ===================================================== fp32 tiled MFMA kernel
+//
+// Same structure with fp32 operands: K slab 32 floats, MFMA 16x16x4 f32.
+// Within a 16-deep K step, the 4 MFMAs q = 0..3 use k = 4*g + q for lane
+// group g, so one 16-byte LDS read of an A row feeds 4 MFMAs.  B rows are
+// padded by 4 floats so the 4 lane groups (rows 4 apart) hit different banks.
+template <int BM, int BN, int WGM, int WGN, bool EVEN>
+__global__ void __launch_bounds__(WGM *WGN * 64, 2) k_f32_mfma(GemmArgs p)
+{
+    constexpr int T = WGM * WGN * 64;
+    constexpr int BK = 32;
+    constexpr int TM = BM / WGM, TN = BN / WGN;
+    constexpr int FM = TM / 16, FN = TN / 16;
+    constexpr int A_CPR = BK / 4;            // 16-byte chunks per A slab row (8)
+    constexpr int B_CPR = BN / 4;
+    constexpr int BLD = BN + 4;              // padded B slab row, floats
+    constexpr int CA = BM * A_CPR / T;
+    constexpr int CB = BK * B_CPR / T;
+    constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BLD;
+    static_assert((BM * A_CPR) % T == 0 && (BK * B_CPR) % T == 0, "slab chunks must divide threads");
+    __shared__ __attribute__((aligned(16))) float smem[2 * (A_ELEMS + B_ELEMS)];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int g = lane >> 4, li = lane & 15;
+
+    const TileCoord tc = tile_map(blockIdx.x, p.batch, p.tiles_m, p.tiles_n, p.group_m);
+    const int64_t m0 = tc.tm * BM, n0 = tc.tn * BN;
+    const int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const float *Ab = (const float *)p.A + tc.b * p.sA + m0 * lda;
+    const float *Bb = (const float *)p.B + tc.b * p.sB + n0;
+
+    int a_row[CA], a_c[CA], b_row[CB], b_c[CB];
+#pragma unroll
+    for (int i = 0; i < CA; ++i) {
+        const int q = tid + T * i;
+        a_row[i] = q / A_CPR;
+        a_c[i] = q % A_CPR;
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+        const int q = tid + T * i;
+        b_row[i] = q / B_CPR;
+        b_c[i] = q % B_CPR;
+    }
+
+    u32x4 ra[CA], rb[CB];
+    auto load_slab = [&](int kt) {
+        const int64_t k0 = (int64_t)kt * BK;
+#pragma unroll
+        for (int i = 0; i < CA; ++i) {
+            const float *row = Ab + (int64_t)a_row[i] * lda;
+            if (EVEN) ra[i] = *(const u32x4 *)(row + k0 + a_c[i] * 4);
+            else ra[i] = load_chunk4_f32(row, k0 + a_c[i] * 4, K, m0 + a_row[i] < M, p.align_a);
+        }
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            const int64_t k = k0 + b_row[i];
+            const float *row = Bb + k * ldb;
+            if (EVEN) rb[i] = *(const u32x4 *)(row + b_c[i] * 4);
+            else rb[i] = load_chunk4_f32(row, b_c[i] * 4, N - n0, k < K, p.align_b);
+        }
+    };
+    auto store_slab = [&](int buf) {
+        float *As = smem + buf * (A_ELEMS + B_ELEMS);
+        float *Bs = As + A_ELEMS;
+#pragma unroll
+        for (int i = 0; i < CA; ++i)
+            *(u32x4 *)(As + a_row[i] * BK + ((a_c[i] ^ swz_a(a_row[i])) * 4)) = ra[i];
+#pragma unroll
+        for (int i = 0; i < CB; ++i) *(u32x4 *)(Bs + b_row[i] * BLD + b_c[i] * 4) = rb[i];
+    };
+
+    f32x4 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int KT = (int)((K + BK - 1) / BK);
+    load_slab(0);
+    store_slab(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < KT) load_slab(kt + 1);
+        const float *As = smem + cur * (A_ELEMS + B_ELEMS);
+        const float *Bs = As + A_ELEMS;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            f32x4 af[FM];
+            float bfr[FN][4];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int row = wm * TM + fm * 16 + li;
+                const int c = ks * 4 + g;
+                af[fm] = *(const f32x4 *)(As + row * BK + ((c ^ swz_a(row)) * 4));
+            }
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    bfr[fn][q] = Bs[(ks * 16 + g * 4 + q) * BLD + wn * TN + fn * 16 + li];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm)
+                        acc[fn][fm] = __builtin_amdgcn_mfma_f32_16x16x4f32(bfr[fn][q], af[fm][q], acc[fn][fm], 0, 0, 0);
+        }
+        if (kt + 1 < KT) store_slab(cur ^ 1);
+        __syncthreads();
+    }
+
+    float *Cb = (float *)p.C + tc.b * p.sC;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int64_t m = m0 + wm * TM + fm * 16 + li;
+            const int64_t n = n0 + wn * TN + fn * 16 + g * 4;
+            if (!EVEN && (m >= M || n >= N)) continue;
+            const bool full = EVEN || (m < M && n + 4 <= N);
+            store4(Cb, true, p.ldc, m, n, acc[fn][fm], full, M, N, p.align_c);
+        }
+}
+
+// ========================================================= small-M (decode)
+//
+// C[M,N] = X[M,K] . W[K,N] for M <= 16 is bound by streaming W once from HBM
+// (arithmetic intensity about M FLOP per byte; MUSA lesson m11-l5, case 2
+// GEMV; "Operator & Runtime" §5.2.4 on splitting a single decode row's
+// reduction to occupy the device).  Design:
+//  * a workgroup owns 64 columns of W and all of K; its NW waves split K in a
+//    fixed partition that does not depend on M, and their partial sums are
+//    added in wave order through LDS (no atomics: bitwise reproducible and
+//    independent of how many rows the call has; "Operator & Runtime" §5.2.4);
+//  * lane (g, r) streams 8 rows x 8 bytes of W straight into registers --
+//    each load instruction reads 4 rows x 128 contiguous bytes -- and a
+//    4x8 transpose of 16-bit halves in registers turns them into the
+//    K-contiguous operands of 4 matrix-core blocks, whose logical column r
+//    maps to physical column 4r + b;
+//  * X rows (zero beyond M) are the other MFMA operand; the 16-row MFMA
+//    covers any M <= 16 at no extra memory traffic.
+template <int NW>
+__global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
+{
+    constexpr int NC = 64;                   // columns per workgroup
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, li = lane & 15;
+    const int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const int64_t n0 = (int64_t)blockIdx.x * NC;
+    const int64_t bidx = blockIdx.y;
+    const uint16_t *X = (const uint16_t *)p.A + bidx * p.sA;
+    const uint16_t *W = (const uint16_t *)p.B + bidx * p.sB;
+
+    const int64_t steps = (K + 31) / 32;
+    const int64_t s_begin = steps * wave / NW, s_end = steps * (wave + 1) / NW;
+    const bool fast = (p.align_b >= 8) && (n0 + NC <= N);
+    const bool xfast = (p.align_a >= 16);
+    const int64_t ncol = n0 + 4 * li;        // first of this lane's 4 columns
+    const bool m_ok = li < M;
+
+    f32x4 acc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int64_t s = s_begin; s < s_end; ++s) {
+        const int64_t kb = s * 32 + g * 8;
+        u32x2 w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t k = kb + j;
+            u32x2 v = {0u, 0u};
+            if (k < K) {
+                const uint16_t *src = W + k * ldb + ncol;
+                if (fast) {
+                    v = *(const u32x2 *)src;
+                } else {
+                    uint32_t e[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) e[c] = (ncol + c < N) ? (uint32_t)src[c] : 0u;
+                    v[0] = e[0] | (e[1] << 16);
+                    v[1] = e[2] | (e[3] << 16);
+                }
+            }
+            w[j] = v;
+        }
+        u32x4 xv = {0u, 0u, 0u, 0u};
+        if (m_ok) {
+            const uint16_t *xr = X + (int64_t)li * lda;
+            if (xfast && kb + 8 <= K) xv = *(const u32x4 *)(xr + kb);
+            else xv = load_chunk8_bf16(xr, kb, K, true, 2);
+        }
+        const bf16x8 xf = __builtin_bit_cast(bf16x8, xv);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            u32x4 a;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t lo = w[2 * q][b >> 1], hi = w[2 * q + 1][b >> 1];
+                a[q] = (b & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+            }
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), xf, acc[b], 0, 0, 0);
+        }
+    }
+
+    // acc[b][q] of lane (g, li) is the partial C[li][n0 + 16 g + 4 q + b].
+    __shared__ float red[NW * 64 * 16];
+    float *mine = red + (wave * 64 + lane) * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) mine[q * 4 + b] = acc[b][q];
+    __syncthreads();
+    for (int t = tid; t < 64 * 16; t += NW * 64) {
+        float s = 0.f;
+        for (int w2 = 0; w2 < NW; ++w2) s += red[w2 * 64 * 16 + t];
+        const int L = t >> 4, v = t & 15;
+        const int64_t m = L & 15;
+        const int64_t n = n0 + 16 * (L >> 4) + v;
+        if (m < M && n < N) {
+            if (p.out_f32) ((float *)p.C + bidx * p.sC)[m * p.ldc + n] = s;
+            else ((uint16_t *)p.C + bidx * p.sC)[m * p.ldc + n] = (uint16_t)bf16_rne(s);
+        }
+    }
+}
+
+// ============================================================ generic path
+//
+// Any shape, stride and alignment: 16x16 output tile per workgroup, element
+// loads staged through LDS, FP32 FMA on the vector ALU in k order.
+template <typename TIn>
+__device__ __forceinline__ float widen(TIn v);
+template <>
+__device__ __forceinline__ float widen<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ float widen<uint16_t>(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+template <typename TIn>
+__global__ void __launch_bounds__(256) k_generic(GemmArgs p)
+{
+    __shared__ float As[16][17], Bs[16][17];
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    const TileCoord tc = tile_map(blockIdx.x, p.batch, p.tiles_m, p.tiles_n, 1);
+    const int64_t m = tc.tm * 16 + ty, n = tc.tn * 16 + tx;
+    const TIn *A = (const TIn *)p.A + tc.b * p.sA;
+    const TIn *B = (const TIn *)p.B + tc.b * p.sB;
+    float acc = 0.f;
+    for (int64_t k0 = 0; k0 < p.K; k0 += 16) {
+        const int64_t ka = k0 + tx, kb = k0 + ty;
+        As[ty][tx] = (m < p.M && ka < p.K) ? widen<TIn>(A[m * p.lda + ka]) : 0.f;
+        Bs[ty][tx] = (kb < p.K && n < p.N) ? widen<TIn>(B[kb * p.ldb + n]) : 0.f;
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) acc = __builtin_fmaf(As[ty][kk], Bs[kk][tx], acc);
+        __syncthreads();
+    }
+    if (m < p.M && n < p.N) {
+        if (p.out_f32) ((float *)p.C + tc.b * p.sC)[m * p.ldc + n] = acc;
+        else ((uint16_t *)p.C + tc.b * p.sC)[m * p.ldc + n] = (uint16_t)bf16_rne(acc);
+    }
+}
+
+// K == 0: C := 0 over batch x M x N (grid-stride).
+__global__ void __launch_bounds__(256) k_zero(GemmArgs p)
+{
+    const int64_t total = p.batch * p.M * p.N;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int64_t b = i / (p.M * p.N), r = i % (p.M * p.N);
+        const int64_t m = r / p.N, n = r % p.N;
+        if (p.out_f32) ((float *)p.C + b * p.sC)[m * p.ldc + n] = 0.f;
+        else ((uint16_t *)p.C + b * p.sC)[m * p.ldc + n] = 0;
+    }
+}
+
+// ================================================================ launchers
+
+template <int BM, int BN, int WGM, int WGN>
+static hipError_t launch_bf16(const GemmArgs &a, bool even, int64_t grid, hipStream_t s)
+{
+    if (even) hipLaunchKernelGGL((k_bf16_mfma<BM, BN, WGM, WGN, true>), dim3((unsigned)grid), dim3(WGM * WGN * 64), 0, s, a);
+    else hipLaunchKernelGGL((k_bf16_mfma<BM, BN, WGM, WGN, false>), dim3((unsigned)grid), dim3(WGM * WGN * 64), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN>
+static hipError_t launch_f32(const GemmArgs &a, bool even, int64_t grid, hipStream_t s)
+{
+    if (even) hipLaunchKernelGGL((k_f32_mfma<BM, BN, WGM, WGN, true>), dim3((unsigned)grid), dim3(WGM * WGN * 64), 0, s, a);
+    else hipLaunchKernelGGL((k_f32_mfma<BM, BN, WGM, WGN, false>), dim3((unsigned)grid), dim3(WGM * WGN * 64), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, bool even, int64_t grid,
+                         hipStream_t s)
+{
+    switch (config_id) {
+    case CFG_ZERO:
+        hipLaunchKernelGGL(k_zero, dim3((unsigned)grid), dim3(256), 0, s, a);
+        return hipGetLastError();
+    case CFG_BF16_256x192: return launch_bf16<256, 192, 2, 2>(a, even, grid, s);
+    case CFG_BF16_256x256: return launch_bf16<256, 256, 2, 2>(a, even, grid, s);
+    case CFG_BF16_128x128: return launch_bf16<128, 128, 2, 2>(a, even, grid, s);
+    case CFG_BF16_256x128: return launch_bf16<256, 128, 2, 2>(a, even, grid, s);
+    case CFG_F32_128x128: return launch_f32<128, 128, 2, 2>(a, even, grid, s);
+    case CFG_F32_64x64: return launch_f32<64, 64, 2, 2>(a, even, grid, s);
+    case CFG_DECODE_64:
+        hipLaunchKernelGGL(k_decode<16>, dim3((unsigned)grid, (unsigned)a.batch), dim3(16 * 64), 0, s, a);
+        return hipGetLastError();
+    case CFG_GENERIC:
+        if (f32_inputs) hipLaunchKernelGGL(k_generic<float>, dim3((unsigned)grid), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(k_generic<uint16_t>, dim3((unsigned)grid), dim3(256), 0, s, a);
+        return hipGetLastError();
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace g5

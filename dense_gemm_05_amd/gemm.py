@@ -1,0 +1,136 @@
+"""Thin Python binding of the C ABI in include/gemm05.h.
+
+Argument marshalling only: the functions read sizes, row strides and data
+pointers from torch tensors (device memory owned by the caller), pass the
+current HIP stream, and raise on a nonzero status.  All arithmetic runs in
+the gfx950 kernels of libgemm05.so.
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import GemmError, GemmPlan, lib
+
+__all__ = ["gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "plan_query", "GemmError"]
+
+
+def _ld(t, inner):
+    """Row stride of a 2-D (or trailing 2-D) operand; columns must be unit stride."""
+    rows, cols = t.shape[-2], t.shape[-1]
+    if cols > 1 and t.stride(-1) != 1:
+        raise ValueError("operands must be row-major with unit column stride")
+    ld = t.stride(-2)
+    if rows <= 1 or ld < cols:
+        ld = max(cols, 1) if rows <= 1 else ld
+    return ld
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check_dev(*ts):
+    dev = ts[0].device
+    if dev.type != "cuda":
+        raise ValueError("operands must be GPU tensors")
+    for t in ts[1:]:
+        if t.device != dev:
+            raise ValueError("operands must be on one device")
+    return dev
+
+
+def gemm_sgemm(A, B, C=None):
+    """C[M,N] = A[M,K] . B[K,N] for float32 tensors (gemm_sgemm)."""
+    if A.dtype != torch.float32 or B.dtype != torch.float32:
+        raise TypeError("gemm_sgemm takes float32 operands")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    dev = _check_dev(A, B)
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    if C.shape != (M, N) or C.dtype != torch.float32:
+        raise ValueError("C must be float32 [M, N]")
+    with torch.cuda.device(dev):
+        st = lib().gemm_sgemm(M, N, K, A.data_ptr(), _ld(A, K), B.data_ptr(), _ld(B, N),
+                              C.data_ptr(), _ld(C, N), _stream(dev))
+    if st != 0:
+        raise GemmError(st, "gemm_sgemm")
+    return C
+
+
+def _out_code(dtype):
+    if dtype == torch.bfloat16:
+        return _lib.GEMM_OUT_BF16
+    if dtype == torch.float32:
+        return _lib.GEMM_OUT_F32
+    raise TypeError("output dtype must be bfloat16 or float32")
+
+
+def gemm_bf16(A, B, C=None, out_dtype=torch.bfloat16):
+    """C[M,N] = A[M,K] . B[K,N] for bfloat16 operands, FP32 accumulation,
+    bf16 (round to nearest even) or float32 output (gemm_bf16)."""
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("gemm_bf16 takes bfloat16 operands")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    dev = _check_dev(A, B)
+    if C is None:
+        C = torch.empty((M, N), dtype=out_dtype, device=dev)
+    if C.shape != (M, N):
+        raise ValueError("C must be [M, N]")
+    code = _out_code(C.dtype)
+    with torch.cuda.device(dev):
+        st = lib().gemm_bf16(M, N, K, A.data_ptr(), _ld(A, K), B.data_ptr(), _ld(B, N),
+                             C.data_ptr(), _ld(C, N), code, _stream(dev))
+    if st != 0:
+        raise GemmError(st, "gemm_bf16")
+    return C
+
+
+def _bstride(t):
+    return t.stride(0) if t.shape[0] > 1 else 0
+
+
+def gemm_bf16_batched(A, B, C=None, out_dtype=torch.bfloat16):
+    """C[b] = A[b] . B[b] for bfloat16 stacks [batch, M, K] and [batch, K, N]
+    (gemm_bf16_batched).  A batch stride of 0 (an expanded operand)
+    broadcasts it."""
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("gemm_bf16_batched takes bfloat16 operands")
+    batch, M, K = A.shape
+    b2, K2, N = B.shape
+    if batch != b2 or K != K2:
+        raise ValueError("shape mismatch")
+    dev = _check_dev(A, B)
+    if C is None:
+        C = torch.empty((batch, M, N), dtype=out_dtype, device=dev)
+    if tuple(C.shape) != (batch, M, N):
+        raise ValueError("C must be [batch, M, N]")
+    code = _out_code(C.dtype)
+    with torch.cuda.device(dev):
+        st = lib().gemm_bf16_batched(batch, M, N, K, A.data_ptr(), _ld(A, K), _bstride(A),
+                                     B.data_ptr(), _ld(B, N), _bstride(B),
+                                     C.data_ptr(), _ld(C, N), _bstride(C), code, _stream(dev))
+    if st != 0:
+        raise GemmError(st, "gemm_bf16_batched")
+    return C
+
+
+def plan_query(op, M, N, K, batch=1, lda=None, ldb=None, ldc=None, a_addr=0x10000, b_addr=0x20000000,
+               c_addr=0x40000000, sA=None, sB=None, sC=None, c_type=_lib.GEMM_OUT_BF16):
+    """Host-only: the status and plan a call would produce (no GPU work)."""
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    sA = M * lda if sA is None else sA
+    sB = K * ldb if sB is None else sB
+    sC = M * ldc if sC is None else sC
+    out = GemmPlan()
+    st = lib().gemm_plan_query(op, batch, M, N, K, a_addr, lda, sA, b_addr, ldb, sB, c_addr, ldc, sC,
+                               c_type, ctypes.byref(out))
+    return st, out

@@ -1,0 +1,161 @@
+/*
+ * gemm05.h -- dense GEMM for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The operation is the plain matrix product
+ *
+ *     C[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j],   0 <= i < M, 0 <= j < N
+ *
+ * with 2*M*N*K floating-point operations, as stated by page "4.1 Tối ưu hiệu
+ * năng toán tử GEMM trên CUDA" (§1.1, and the naive kernel of §3.1), by the
+ * MUSA learning-center lesson m11-l5 (case 4, problem statement) and by page
+ * "Operator & Runtime" (§5.2.1).  Batched GEMM for multi-head attention is
+ * named in §1.2 of the first page.  For BF16 operands the products are
+ * accumulated in FP32 and, for a BF16 output, the finished FP32 sum is rounded
+ * once to BF16, round to nearest, ties to even ("Operator & Runtime", the
+ * FFN projection at the start of the chapter, §5.2.2 and §5.4.3).
+ *
+ * Layout.  Every matrix is row-major.  lda, ldb, ldc are row strides counted
+ * in ELEMENTS: A[i][k] is at A + i*lda + k, B[k][j] at B + k*ldb + j, C[i][j]
+ * at C + i*ldc + j.  C is overwritten (there is no alpha/beta).
+ *
+ * Ownership.  The caller owns every buffer.  A, B and C are device pointers
+ * on the current HIP device.  The library never allocates, frees, copies or
+ * synchronises: each call validates its arguments on the host, enqueues its
+ * kernel(s) on `stream` (a hipStream_t; NULL means the null stream) and
+ * returns.  Completion is observed through the stream.  Calls are thread-safe.
+ * No alignment is required; aligned operands (16-byte rows and pointers)
+ * select the faster kernel variants.
+ *
+ * Edge semantics.  M == 0, N == 0 or batch == 0: nothing to do, GEMM_OK.
+ * K == 0: C := 0 (the empty sum).  Results are deterministic: the same call
+ * on the same inputs gives the same bits (no atomics, fixed reduction order),
+ * and the small-M path splits K the same way for every M, so a row's result
+ * does not depend on how many rows are in the call.
+ *
+ * Errors.  A negative status is returned and nothing is enqueued when the
+ * arguments are invalid (GEMM_ERR_INVALID_ARG): a negative size or batch;
+ * lda < K, ldb < N or ldc < N for a non-empty operand; a NULL pointer for an
+ * operand that is read or written; a c_type outside gemm_out_type; a negative
+ * batch stride; batch > 1 with strideC < (M-1)*ldc + N (C entries would
+ * overlap); or C's byte range overlapping A's or B's.  GEMM_ERR_UNSUPPORTED:
+ * a kernel configuration forced through the GEMM_FORCE_CONFIG environment
+ * variable cannot run this problem.  GEMM_ERR_NO_DEVICE: no usable HIP device
+ * is current.  GEMM_ERR_LAUNCH: the kernel launch failed (hipGetLastError).
+ */
+#ifndef GEMM05_H
+#define GEMM05_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_ARG = -1,
+    GEMM_ERR_UNSUPPORTED = -2,
+    GEMM_ERR_LAUNCH = -3,
+    GEMM_ERR_NO_DEVICE = -4
+} gemm_status;
+
+/* Output element type of the BF16 entry points. */
+typedef enum {
+    GEMM_OUT_BF16 = 0, /* C holds bf16 bit patterns (uint16_t), RNE of the FP32 sum */
+    GEMM_OUT_F32 = 1   /* C holds float, the FP32 sum */
+} gemm_out_type;
+
+/* FP32 GEMM: A [M,K] float, B [K,N] float, C [M,N] float (FP32 products and
+ * FP32 accumulation on the matrix cores). */
+int gemm_sgemm(int64_t M, int64_t N, int64_t K,
+               const float *A, int64_t lda,
+               const float *B, int64_t ldb,
+               float *C, int64_t ldc,
+               void *stream);
+
+/* BF16 GEMM with FP32 accumulation: A [M,K] and B [K,N] hold bf16 bit
+ * patterns; C [M,N] is bf16 (c_type GEMM_OUT_BF16) or float (GEMM_OUT_F32).
+ * M <= 16 uses the memory-bound small-M (decode) path. */
+int gemm_bf16(int64_t M, int64_t N, int64_t K,
+              const uint16_t *A, int64_t lda,
+              const uint16_t *B, int64_t ldb,
+              void *C, int64_t ldc, int c_type,
+              void *stream);
+
+/* Batched BF16 GEMM: for b in [0, batch), entry b computes
+ * C + b*strideC := (A + b*strideA) . (B + b*strideB), each as gemm_bf16.
+ * Strides are in elements and >= 0; strideA or strideB of 0 broadcasts that
+ * operand to every entry. */
+int gemm_bf16_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                      const uint16_t *A, int64_t lda, int64_t strideA,
+                      const uint16_t *B, int64_t ldb, int64_t strideB,
+                      void *C, int64_t ldc, int64_t strideC, int c_type,
+                      void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *gemm_status_string(int status);
+
+/* ---- host-only queries (no GPU work, usable without a device) ------------ */
+
+/* Kernel families the selector chooses between. */
+typedef enum {
+    GEMM_FAMILY_NONE = 0,      /* nothing to launch (empty problem) */
+    GEMM_FAMILY_ZERO = 1,      /* K == 0: fill C with zeros */
+    GEMM_FAMILY_BF16_MFMA = 2, /* tiled bf16 MFMA kernel */
+    GEMM_FAMILY_F32_MFMA = 3,  /* tiled f32 MFMA kernel */
+    GEMM_FAMILY_DECODE = 4,    /* small-M bf16 path (M <= 16) */
+    GEMM_FAMILY_GENERIC = 5    /* any shape/alignment, LDS-tiled vector ALU */
+} gemm_family;
+
+/* What a call would launch.  Filled by gemm_plan_query. */
+typedef struct {
+    int family;        /* gemm_family */
+    int config_id;     /* index of the compiled kernel configuration */
+    int tile_m, tile_n, tile_k;
+    int threads;       /* per workgroup */
+    int vec_a, vec_b;  /* bytes per global load of A and of B rows */
+    int even;          /* 1 when no edge masking is compiled in */
+    int64_t grid;      /* workgroups launched */
+    int64_t lds_bytes; /* LDS per workgroup */
+    double model_bytes;/* traffic model of "Operator & Runtime" §5.2.2 for the chosen tile */
+    char name[48];     /* configuration name, as accepted by GEMM_FORCE_CONFIG */
+} gemm_plan;
+
+/* Operation selector for gemm_plan_query. */
+typedef enum { GEMM_OP_SGEMM = 0, GEMM_OP_BF16 = 1 } gemm_op;
+
+/* Validate the arguments of a call and report the plan it would launch,
+ * without touching the GPU.  Pointers are passed as integers (their values
+ * only decide alignment and overlap).  Returns the status the entry point
+ * would return from validation (GEMM_OK, GEMM_ERR_INVALID_ARG or
+ * GEMM_ERR_UNSUPPORTED); `out` may be NULL. */
+int gemm_plan_query(int op, int64_t batch, int64_t M, int64_t N, int64_t K,
+                    uint64_t a_addr, int64_t lda, int64_t strideA,
+                    uint64_t b_addr, int64_t ldb, int64_t strideB,
+                    uint64_t c_addr, int64_t ldc, int64_t strideC,
+                    int c_type, gemm_plan *out);
+
+/* Tile traffic model of "Operator & Runtime" §5.2.2 (Example 5-3): for an
+ * m x n output tile with reduction slab k and element size e bytes (FP32
+ * accumulator of 4 bytes), local memory S = e*m*k + e*k*n + 4*m*n bytes and
+ * interface traffic V = e*M*K*ceil(N/n) + e*K*N*ceil(M/m) + e*M*N bytes. */
+int64_t gemm_model_local_bytes(int64_t m, int64_t n, int64_t k, int64_t elem_bytes);
+double gemm_model_traffic_bytes(int64_t M, int64_t N, int64_t K, int64_t m, int64_t n,
+                                int64_t elem_bytes);
+
+/* The workgroup -> output-tile map used by the tiled kernels: workgroup id
+ * `wg` of a launch covering `batch` x tiles_m x tiles_n tiles is assigned
+ * (b, tm, tn).  Workgroups are dispatched round-robin over the chip's 8
+ * accelerator complex dies (XCDs); the map gives each XCD a contiguous run
+ * of tiles, ordered in column bands `group_m` tiles tall, so that the tiles
+ * resident on one XCD share rows of A and columns of B in that die's L2.
+ * The map is a bijection on [0, batch*tiles_m*tiles_n).  Returns 0, or -1
+ * for out-of-range arguments. */
+int gemm_tile_map(int64_t wg, int64_t batch, int64_t tiles_m, int64_t tiles_n,
+                  int64_t group_m, int64_t *b, int64_t *tm, int64_t *tn);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM05_H */

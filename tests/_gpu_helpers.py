@@ -1,0 +1,60 @@
+"""Helpers shared by the GPU test modules: host <-> device marshalling of
+bf16 bit patterns and the parity tolerances.  No GEMM arithmetic here."""
+import math
+
+import numpy as np
+import torch
+
+import gemm_inputs as gi
+
+
+def dev_bf16(bits):
+    """uint16 bf16 bit patterns (numpy) -> torch.bfloat16 on cuda:0."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def dev_f32(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def host_bits(t):
+    """torch.bfloat16 tensor -> uint16 numpy bit patterns."""
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host_values(t):
+    """GPU result (bf16 or f32) -> float64 numpy values."""
+    if t.dtype == torch.bfloat16:
+        return gi.bf16_bits_to_f32(host_bits(t)).astype(np.float64)
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def tol_f32(K, amax, bmax):
+    """FP32 bar: max |C - C_ref| <= 1e-5 * K * max|a| * max|b|."""
+    return 1e-5 * max(K, 1) * amax * bmax
+
+
+def check_f32(C, ref, K, amax, bmax, what=""):
+    err = np.abs(C - ref)
+    bound = tol_f32(K, amax, bmax)
+    worst = float(err.max()) if err.size else 0.0
+    assert np.all(np.isfinite(C)), f"{what}: non-finite output"
+    assert worst <= bound, f"{what}: max err {worst:.3e} > bound {bound:.3e}"
+    return worst / bound if bound > 0 else 0.0
+
+
+def check_bf16(C, ref, K, what=""):
+    """BF16-output bar: |C - C_ref| <= 2^-8 |C_ref| + 1e-3 sqrt(K), per element."""
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-3 * math.sqrt(max(K, 1))
+    err = np.abs(C - ref)
+    assert np.all(np.isfinite(C)), f"{what}: non-finite output"
+    bad = err > bound
+    if bad.any():
+        idx = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {int(bad.sum())} elements out of bound, first at {tuple(idx)}: "
+                             f"got {C[tuple(idx)]!r} want {ref[tuple(idx)]!r}")
+    return float((err / bound).max()) if err.size else 0.0
+
+
+def amax_bf16(bits):
+    return float(np.abs(gi.bf16_bits_to_f32(bits)).max()) if bits.size else 0.0

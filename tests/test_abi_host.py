@@ -1,0 +1,185 @@
+"""Host-side checks of the C-ABI library (no GPU work is enqueued).
+
+The library loads without a GPU; these tests cover the exported symbols,
+argument validation (which returns before any HIP call), the selector's plan,
+the tile-traffic model against the table printed by page "Operator &
+Runtime" §5.2.2, and the workgroup -> tile map (a bijection).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_gemm_05_amd as g5
+from dense_gemm_05_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(g5.LIB_PATH):
+        from dense_gemm_05_amd.build import build_library
+        build_library()
+    return g5.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    with open(os.path.join(ROOT, "include", "gemm05.h")) as fh:
+        text = fh.read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(gemm_[a-z_0-9]+)\s*\(", text, re.M))
+    assert declared == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for st in (0, -1, -2, -3, -4):
+        assert g5.status_string(st).startswith("GEMM_")
+    assert "unknown" in g5.status_string(7)
+
+
+P = 0x7F0000000000  # fake, well-aligned, non-overlapping addresses (never dereferenced)
+A_ADDR, B_ADDR, C_ADDR = P, P + (1 << 34), P + (2 << 34)
+
+
+def call_bf16(L, M, N, K, a=A_ADDR, lda=None, b=B_ADDR, ldb=None, c=C_ADDR, ldc=None, ct=0):
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return L.gemm_bf16(M, N, K, a, lda, b, ldb, c, ldc, ct, None)
+
+
+@pytest.mark.parametrize("args", [
+    dict(M=-1, N=4, K=4), dict(M=4, N=-1, K=4), dict(M=4, N=4, K=-2),
+    dict(M=4, N=4, K=8, lda=7), dict(M=4, N=8, K=4, ldb=7), dict(M=4, N=8, K=4, ldc=7),
+    dict(M=4, N=4, K=4, a=0), dict(M=4, N=4, K=4, b=0), dict(M=4, N=4, K=4, c=0),
+    dict(M=4, N=4, K=4, ct=2), dict(M=4, N=4, K=4, ct=-1),
+    dict(M=4, N=4, K=4, c=A_ADDR + 8),            # C overlaps A
+    dict(M=4, N=4, K=4, c=B_ADDR),                # C overlaps B
+])
+def test_invalid_arguments_rejected_before_launch(L, args):
+    assert call_bf16(L, **args) == g5.GEMM_ERR_INVALID_ARG
+
+
+def test_invalid_sgemm_and_batched(L):
+    assert L.gemm_sgemm(4, 4, 4, 0, 4, B_ADDR, 4, C_ADDR, 4, None) == g5.GEMM_ERR_INVALID_ARG
+    assert L.gemm_sgemm(4, 4, 4, A_ADDR, 3, B_ADDR, 4, C_ADDR, 4, None) == g5.GEMM_ERR_INVALID_ARG
+    # batch entries of C overlap: strideC < (M-1)*ldc + N
+    assert L.gemm_bf16_batched(2, 4, 4, 4, A_ADDR, 4, 16, B_ADDR, 4, 16, C_ADDR, 4, 15, 0, None) == \
+        g5.GEMM_ERR_INVALID_ARG
+    assert L.gemm_bf16_batched(-1, 4, 4, 4, A_ADDR, 4, 16, B_ADDR, 4, 16, C_ADDR, 4, 16, 0, None) == \
+        g5.GEMM_ERR_INVALID_ARG
+    assert L.gemm_bf16_batched(2, 4, 4, 4, A_ADDR, 4, -16, B_ADDR, 4, 16, C_ADDR, 4, 16, 0, None) == \
+        g5.GEMM_ERR_INVALID_ARG
+
+
+def test_empty_problems_are_noops_without_device(L):
+    # M, N or batch of zero: nothing is enqueued, even with NULL pointers.
+    assert L.gemm_bf16(0, 5, 5, None, 5, None, 5, None, 5, 0, None) == g5.GEMM_OK
+    assert L.gemm_bf16(5, 0, 5, None, 5, None, 0, None, 0, 0, None) == g5.GEMM_OK
+    assert L.gemm_sgemm(0, 0, 0, None, 0, None, 0, None, 0, None) == g5.GEMM_OK
+    assert L.gemm_bf16_batched(0, 4, 4, 4, None, 4, 0, None, 4, 0, None, 4, 0, 0, None) == g5.GEMM_OK
+
+
+def test_k_zero_plans_a_fill(L):
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 3, 5, 0)
+    assert st == 0 and p.name == b"zero"
+
+
+def test_force_config_unsupported(L, monkeypatch):
+    monkeypatch.setenv("GEMM_FORCE_CONFIG", "f32_128x128")
+    st, _ = g5.plan_query(g5.GEMM_OP_BF16, 64, 64, 64)
+    assert st == g5.GEMM_ERR_UNSUPPORTED
+    monkeypatch.setenv("GEMM_FORCE_CONFIG", "no_such_config")
+    st, _ = g5.plan_query(g5.GEMM_OP_BF16, 64, 64, 64)
+    assert st == g5.GEMM_ERR_UNSUPPORTED
+    monkeypatch.setenv("GEMM_FORCE_CONFIG", "decode_64")
+    st, _ = g5.plan_query(g5.GEMM_OP_BF16, 64, 64, 64)   # M > 16
+    assert st == g5.GEMM_ERR_UNSUPPORTED
+    monkeypatch.setenv("GEMM_FORCE_CONFIG", "generic")
+    st, p = g5.plan_query(g5.GEMM_OP_SGEMM, 64, 64, 64)
+    assert st == 0 and p.name == b"generic"
+
+
+def test_selector_choices_for_the_workloads(L):
+    # FFN projection: 256x192 tiles give 4 x 64 = 256 workgroups, one per CU.
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 1024, 12288, 4096)
+    assert st == 0 and p.name == b"bf16_256x192" and p.grid == 256 and p.even == 1
+    # decode rows go to the small-M path, whatever M <= 16 is
+    for M in (1, 4, 16):
+        st, p = g5.plan_query(g5.GEMM_OP_BF16, M, 12288, 4096)
+        assert st == 0 and p.family == 4 and p.grid == 12288 // 64
+    st, p = g5.plan_query(g5.GEMM_OP_SGEMM, 4096, 4096, 4096)
+    assert st == 0 and p.family == 3 and p.even == 1
+    # ragged: K=4100 bf16 rows are only 8-byte aligned -> masked variant
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 1000, 12280, 4100, c_type=1)
+    assert st == 0 and p.family == 2 and p.even == 0 and p.vec_a == 8 and p.vec_b == 16
+    # every plan fits the 160 KiB LDS of a gfx950 CU
+    for args in [(1024, 12288, 4096), (1000, 12280, 4100), (17, 33, 65)]:
+        st, p = g5.plan_query(g5.GEMM_OP_BF16, *args)
+        assert p.lds_bytes <= 160 * 1024
+
+
+def _golden_rows():
+    rows, extra = [], {}
+    with open(os.path.join(GOLDEN, "op_runtime_5_2_2_tile_traffic.txt")) as fh:
+        for line in fh:
+            if not line.strip() or line.startswith("#"):
+                continue
+            parts = line.split()
+            if parts[0] in ("flops", "once_MiB"):
+                extra[parts[0]] = int(parts[1])
+            else:
+                rows.append((int(parts[0]), int(parts[1]), int(parts[2]), int(parts[3]), float(parts[4])))
+    return rows, extra
+
+
+def test_traffic_model_reproduces_op_runtime_table(L):
+    M, K, N = 1024, 4096, 12288
+    rows, extra = _golden_rows()
+    flops = 2 * M * K * N
+    assert flops == extra["flops"]
+    once = (2 * (M * K + K * N + M * N)) / 2 ** 20
+    assert once == extra["once_MiB"]
+    for m, n, kib, mib, fpb in rows:
+        assert L.gemm_model_local_bytes(m, n, 32, 2) == kib * 1024
+        v = L.gemm_model_traffic_bytes(M, N, K, m, n, 2)
+        assert v == mib * 2 ** 20
+        # The page's intensity column is 103e9 FLOP (its rounded figure) over V,
+        # to one decimal; the exact 2MKN gives the same within 0.06.
+        assert round(103e9 / v, 1) == fpb
+        assert abs(flops / v - fpb) < 0.06
+
+
+def test_tile_map_is_a_bijection(L):
+    i64 = ctypes.c_int64
+    b, tm, tn = i64(), i64(), i64()
+    for batch, tiles_m, tiles_n, group in [(1, 4, 64, 4), (1, 7, 5, 3), (3, 3, 11, 8), (2, 13, 9, 8),
+                                           (1, 1, 1, 1), (32, 4, 6, 4), (1, 16, 16, 8), (5, 1, 13, 1)]:
+        seen = set()
+        total = batch * tiles_m * tiles_n
+        for w in range(total):
+            assert L.gemm_tile_map(w, batch, tiles_m, tiles_n, group, ctypes.byref(b), ctypes.byref(tm),
+                                   ctypes.byref(tn)) == 0
+            assert 0 <= b.value < batch and 0 <= tm.value < tiles_m and 0 <= tn.value < tiles_n
+            seen.add((b.value, tm.value, tn.value))
+        assert len(seen) == total
+        assert L.gemm_tile_map(total, batch, tiles_m, tiles_n, group, ctypes.byref(b), ctypes.byref(tm),
+                               ctypes.byref(tn)) == -1
+
+
+def test_tile_map_gives_each_xcd_a_compact_block(L):
+    """FFN grid (4 x 64 tiles of 256x192): the 32 workgroups on XCD x
+    (ids x, x+8, ...) cover all 4 row tiles of 8 adjacent column tiles."""
+    i64 = ctypes.c_int64
+    b, tm, tn = i64(), i64(), i64()
+    for x in range(8):
+        cols, rowset = set(), set()
+        for w in range(x, 256, 8):
+            L.gemm_tile_map(w, 1, 4, 64, 4, ctypes.byref(b), ctypes.byref(tm), ctypes.byref(tn))
+            cols.add(tn.value)
+            rowset.add(tm.value)
+        assert rowset == {0, 1, 2, 3} and cols == set(range(8 * x, 8 * x + 8))

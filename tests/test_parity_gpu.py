@@ -1,0 +1,294 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the FP64
+CPU oracle on the same seeded inputs.
+
+Bars (written here, per element):
+  FP32:                     max |C - C_ref| <= 1e-5 * K * max|a| * max|b|
+  BF16 output:              |C - C_ref| <= 2^-8 |C_ref| + 1e-3 sqrt(K)
+  FP32 output, bf16 inputs: the FP32 bar with max|a|, max|b| of that entry's
+                            bf16 inputs
+C_ref is the oracle's unrounded double result.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gemm_inputs as gi
+from _gpu_helpers import (amax_bf16, check_bf16, check_f32, dev_bf16, dev_f32, host_bits,
+                                host_values)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import dense_gemm_05_amd as g5
+
+
+def _say(msg):
+    print(f"[parity] {msg}", flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _no_forced_config(monkeypatch):
+    monkeypatch.delenv("GEMM_FORCE_CONFIG", raising=False)
+
+
+# ---------------------------------------------------------------- FP32
+
+def test_sgemm_256_cube(oracle_mod):
+    _say("sgemm 256^3")
+    A, B = gi.sgemm_inputs(256)
+    C = g5.gemm_sgemm(dev_f32(A), dev_f32(B))
+    torch.cuda.synchronize()
+    ref = oracle_mod.gemm_f32(A, B)
+    check_f32(host_values(C), ref, 256, np.abs(A).max(), np.abs(B).max(), "sgemm 256^3")
+
+
+SHAPES = [(1, 1, 1), (7, 9, 5), (16, 16, 16), (17, 33, 65), (64, 64, 64), (65, 127, 129),
+          (127, 65, 33), (129, 257, 255), (255, 129, 31), (300, 200, 100), (3, 500, 1000)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_sgemm_ragged(oracle_mod, M, N, K):
+    _say(f"sgemm {M}x{N}x{K}")
+    A, B = gi.small_case("f32", M, N, K)
+    C = g5.gemm_sgemm(dev_f32(A), dev_f32(B))
+    ref = oracle_mod.gemm_f32(A, B)
+    check_f32(host_values(C), ref, K, np.abs(A).max(), np.abs(B).max(), f"sgemm {M}x{N}x{K}")
+
+
+def test_sgemm_padded_strides(oracle_mod):
+    """lda > K, ldb > N, ldc > N (views into wider buffers)."""
+    M, N, K = 70, 90, 110
+    g = np.random.default_rng(31)
+    Aw = gi.uniform_pm1(g, (M, K + 10))
+    Bw = gi.uniform_pm1(g, (K, N + 7))
+    dA, dB = dev_f32(Aw), dev_f32(Bw)
+    Cfull = torch.full((M, N + 13), float("nan"), device="cuda")
+    g5.gemm_sgemm(dA[:, :K], dB[:, :N], Cfull[:, :N])
+    ref = oracle_mod.gemm_f32(Aw[:, :K], Bw[:, :N])
+    host = host_values(Cfull)
+    check_f32(host[:, :N], ref, K, np.abs(Aw[:, :K]).max(), np.abs(Bw[:, :N]).max(), "sgemm padded")
+    assert np.all(np.isnan(host[:, N:])), "ldc padding was written"
+
+
+def test_sgemm_4096_sampled(oracle_mod):
+    """The 4096^3 workload at full size, in the launch configuration the
+    benchmark times; rows spread over the tile grid are checked in full."""
+    _say("sgemm 4096^3 (sampled rows)")
+    A, B = gi.sgemm_inputs(4096, workload=gi.W_SGEMM_LARGE)
+    C = g5.gemm_sgemm(dev_f32(A), dev_f32(B))
+    rows = np.array([0, 1, 127, 128, 129, 1000, 2047, 2048, 3071, 4094, 4095])
+    ref = oracle_mod.gemm_f32(np.ascontiguousarray(A[rows]), B)
+    got = host_values(C)[rows]
+    check_f32(got, ref, 4096, np.abs(A).max(), np.abs(B).max(), "sgemm 4096 rows")
+
+
+# ---------------------------------------------------------------- BF16
+
+BF16_SHAPES = [(17, 33, 65), (20, 8, 3), (33, 190, 7), (64, 64, 64), (129, 257, 255), (256, 192, 64),
+               (257, 193, 130), (300, 385, 129), (512, 384, 128), (100, 1000, 77), (1, 300, 100),
+               (5, 77, 1000), (16, 129, 64), (16, 64, 4100)]
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", BF16_SHAPES)
+def test_bf16_ragged(oracle_mod, M, N, K, out):
+    _say(f"bf16 {M}x{N}x{K} -> {out}")
+    A, B = gi.small_case("bf16", M, N, K, seed=1, scale_b=0.125)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    C = g5.gemm_bf16(dev_bf16(A), dev_bf16(B), out_dtype=od)
+    ref = oracle_mod.gemm_bf16(A, B)
+    if out == "bf16":
+        check_bf16(host_values(C), ref, K, f"bf16 {M}x{N}x{K}")
+    else:
+        check_f32(host_values(C), ref, K, amax_bf16(A), amax_bf16(B), f"bf16->f32 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("cfg", ["bf16_256x192", "bf16_128x128", "bf16_256x128", "bf16_256x256", "generic",
+                                 "decode_64"])
+def test_bf16_every_config(oracle_mod, monkeypatch, cfg):
+    """Each compiled configuration, forced, on a ragged problem with padded
+    strides and odd K (misaligned rows)."""
+    M = 16 if cfg == "decode_64" else 300
+    N, K = 390, 261
+    _say(f"bf16 forced {cfg} {M}x{N}x{K}")
+    A, B = gi.small_case("bf16", M, N + 5, K + 3, seed=6, scale_b=0.125)
+    dA, dB = dev_bf16(A), dev_bf16(B)
+    monkeypatch.setenv("GEMM_FORCE_CONFIG", cfg)
+    for od in (torch.bfloat16, torch.float32):
+        Cfull = torch.full((M, N + 7), float("nan"), device="cuda", dtype=od)
+        g5.gemm_bf16(dA[:, :K], dB[:K, :N], Cfull[:, :N])
+        ref = oracle_mod.gemm_bf16(np.ascontiguousarray(A[:, :K]), np.ascontiguousarray(B[:K, :N]))
+        host = host_values(Cfull)
+        if od == torch.bfloat16:
+            check_bf16(host[:, :N], ref, K, f"{cfg} bf16")
+        else:
+            check_f32(host[:, :N], ref, K, amax_bf16(A[:, :K]), amax_bf16(B[:K, :N]), f"{cfg} f32")
+        assert np.all(np.isnan(host[:, N:])), f"{cfg}: ldc padding was written"
+
+
+@pytest.mark.parametrize("cfg", ["f32_128x128", "f32_64x64", "generic"])
+def test_sgemm_every_config(oracle_mod, monkeypatch, cfg):
+    M, N, K = 150, 170, 190
+    A, B = gi.small_case("f32", M, N, K, seed=8)
+    monkeypatch.setenv("GEMM_FORCE_CONFIG", cfg)
+    C = g5.gemm_sgemm(dev_f32(A), dev_f32(B))
+    ref = oracle_mod.gemm_f32(A, B)
+    check_f32(host_values(C), ref, K, np.abs(A).max(), np.abs(B).max(), cfg)
+
+
+def test_ffn_projection_full_size(oracle_mod):
+    """X[1024,4096] . W[4096,12288] -> bf16, the benchmarked launch; 48 rows
+    spread across every row tile and all 12288 columns are checked in full."""
+    _say("FFN 1024x12288x4096")
+    X, W = gi.ffn_inputs()
+    C = g5.gemm_bf16(dev_bf16(X), dev_bf16(W))
+    st, plan = g5.plan_query(g5.GEMM_OP_BF16, 1024, 12288, 4096)
+    assert plan.name == b"bf16_256x192"
+    rows = np.unique(np.concatenate([np.arange(0, 1024, 32), np.arange(1, 1024, 97), [255, 256, 767, 1023]]))
+    ref = oracle_mod.gemm_bf16(np.ascontiguousarray(X[rows]), W)
+    got = host_values(C)[rows]
+    check_bf16(got, ref, 4096, "FFN rows")
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_decode_full_size(oracle_mod, M):
+    _say(f"decode M={M}")
+    X, W = gi.decode_inputs(M)
+    C = g5.gemm_bf16(dev_bf16(X), dev_bf16(W))
+    ref = oracle_mod.gemm_bf16(X, W)
+    check_bf16(host_values(C), ref, 4096, f"decode M={M}")
+
+
+def test_decode_batch_invariance():
+    """Rows of the M=1 and M=4 results equal the matching rows of M=16 bit for
+    bit: the K split does not depend on M ("Operator & Runtime" §5.2.4)."""
+    X16, W = gi.decode_inputs(16)
+    dW = dev_bf16(W)
+    C16 = host_bits(g5.gemm_bf16(dev_bf16(X16), dW))
+    for M in (1, 4, 9):
+        CM = host_bits(g5.gemm_bf16(dev_bf16(np.ascontiguousarray(X16[:M])), dW))
+        assert np.array_equal(CM, C16[:M]), f"M={M} rows differ from M=16"
+
+
+def test_batched_attention_scores(oracle_mod):
+    """32 x Q[1024,128] . K^T[128,1024] -> f32; 4 entries in full, the rest
+    on sampled rows."""
+    _say("batched 32x1024x1024x128")
+    Q, KT = gi.batched_inputs()
+    C = g5.gemm_bf16_batched(dev_bf16(Q), dev_bf16(KT), out_dtype=torch.float32)
+    host = host_values(C)
+    for b in (0, 1, 17, 31):
+        ref = oracle_mod.gemm_bf16(Q[b], KT[b])
+        check_f32(host[b], ref, 128, amax_bf16(Q[b]), amax_bf16(KT[b]), f"batch entry {b}")
+    rows = np.array([0, 255, 256, 511, 777, 1023])
+    for b in range(32):
+        ref = oracle_mod.gemm_bf16(np.ascontiguousarray(Q[b][rows]), KT[b])
+        check_f32(host[b][rows], ref, 128, amax_bf16(Q[b]), amax_bf16(KT[b]), f"batch {b} rows")
+
+
+def test_ragged_single_gemm(oracle_mod):
+    """M=1000, N=12280, K=4100 bf16 -> f32 (edge tiles in M and N, a K tail
+    of 4, 8-byte aligned rows of A); also with bf16 output."""
+    _say("ragged 1000x12280x4100")
+    A, B = gi.ragged_inputs()
+    dA, dB = dev_bf16(A), dev_bf16(B)
+    rows = np.unique(np.concatenate([np.arange(0, 1000, 41), [255, 256, 767, 768, 998, 999]]))
+    refr = oracle_mod.gemm_bf16(np.ascontiguousarray(A[rows]), B)
+    C = g5.gemm_bf16(dA, dB, out_dtype=torch.float32)
+    check_f32(host_values(C)[rows], refr, 4100, amax_bf16(A), amax_bf16(B), "ragged f32")
+    Cb = g5.gemm_bf16(dA, dB, out_dtype=torch.bfloat16)
+    check_bf16(host_values(Cb)[rows], refr, 4100, "ragged bf16")
+
+
+def test_batched_strides_broadcast_and_single(oracle_mod):
+    g = np.random.default_rng(21)
+    A = gi.to_bf16_bits(gi.normal(g, (3, 40, 50)))
+    B = gi.to_bf16_bits(gi.normal(g, (1, 50, 70), 0.125))
+    dA, dB = dev_bf16(A), dev_bf16(B)
+    C = g5.gemm_bf16_batched(dA, dB.expand(3, 50, 70), out_dtype=torch.float32)  # strideB = 0
+    host = host_values(C)
+    for b in range(3):
+        check_f32(host[b], oracle_mod.gemm_bf16(A[b], B[0]), 50, amax_bf16(A[b]), amax_bf16(B), f"bcast {b}")
+    # batch of one equals the single GEMM bit for bit
+    C1 = g5.gemm_bf16_batched(dA[:1], dB, out_dtype=torch.float32)
+    Cs = g5.gemm_bf16(dA[0], dB[0], out_dtype=torch.float32)
+    assert torch.equal(C1[0], Cs)
+
+
+# ---------------------------------------------------------- edge semantics
+
+def test_k_zero_writes_zeros():
+    A = torch.empty((5, 0), dtype=torch.bfloat16, device="cuda")
+    B = torch.empty((0, 7), dtype=torch.bfloat16, device="cuda")
+    C = torch.full((5, 7), 3.0, dtype=torch.bfloat16, device="cuda")
+    g5.gemm_bf16(A, B, C)
+    assert torch.count_nonzero(C).item() == 0
+    Cf = torch.full((5, 7), 3.0, device="cuda")
+    g5.gemm_sgemm(A.float(), B.float(), Cf)
+    assert torch.count_nonzero(Cf).item() == 0
+
+
+def test_empty_m_leaves_c_untouched():
+    A = torch.empty((0, 9), dtype=torch.bfloat16, device="cuda")
+    B = torch.ones((9, 4), dtype=torch.bfloat16, device="cuda")
+    C = torch.empty((0, 4), dtype=torch.bfloat16, device="cuda")
+    assert g5.gemm_bf16(A, B, C).shape == (0, 4)
+
+
+@pytest.mark.parametrize("M", [1, 40])   # decode path and tiled path
+def test_bf16_round_to_nearest_even_ties(M):
+    """K=2: 1*1 + 1*2^-8 = 1 + 2^-8 exactly in FP32 -> tie -> 1.0;
+    (1+2^-7) + 2^-8 = 1 + 3*2^-8 -> tie -> 1 + 2^-6."""
+    a = np.ones((M, 2), np.float32)
+    b = np.array([[1.0, 1.0 + 2 ** -7], [2 ** -8, 2 ** -8]], np.float32)
+    C = g5.gemm_bf16(dev_bf16(gi.to_bf16_bits(a)), dev_bf16(gi.to_bf16_bits(b)))
+    bits = host_bits(C)
+    assert np.all(bits[:, 0] == 0x3F80) and np.all(bits[:, 1] == 0x3F82), bits[:2]
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (16, 100, 300), (1024, 1152, 4100), (300, 300, 300)])
+def test_identity_and_all_ones(M, N, K):
+    """All-ones: every entry is exactly K (bf16 output: RNE(K)); identity
+    A = I gives C = B exactly."""
+    ones_a = torch.ones((M, K), dtype=torch.bfloat16, device="cuda")
+    ones_b = torch.ones((K, N), dtype=torch.bfloat16, device="cuda")
+    Cf = g5.gemm_bf16(ones_a, ones_b, out_dtype=torch.float32)
+    assert torch.all(Cf == K)
+    Cb = g5.gemm_bf16(ones_a, ones_b)
+    want = gi.bf16_bits_to_f32(gi.to_bf16_bits(np.array([K], np.float32)))[0]
+    assert torch.all(Cb.float() == float(want))
+    Cs = g5.gemm_sgemm(ones_a.float(), ones_b.float())
+    assert torch.all(Cs == K)
+    if M == K:
+        eye = torch.eye(K, dtype=torch.bfloat16, device="cuda")
+        B = torch.randn((K, N), device="cuda").to(torch.bfloat16)
+        assert torch.equal(g5.gemm_bf16(eye, B), B)
+        assert torch.equal(g5.gemm_sgemm(eye.float(), B.float()), B.float())
+
+
+def test_deterministic_bitwise():
+    X, W = gi.ffn_inputs(M=512, K=1024, N=3072)
+    dX, dW = dev_bf16(X), dev_bf16(W)
+    c1 = host_bits(g5.gemm_bf16(dX, dW))
+    c2 = host_bits(g5.gemm_bf16(dX, dW))
+    assert np.array_equal(c1, c2)
+    A, B = gi.small_case("f32", 300, 300, 300)
+    s1 = g5.gemm_sgemm(dev_f32(A), dev_f32(B))
+    s2 = g5.gemm_sgemm(dev_f32(A), dev_f32(B))
+    assert torch.equal(s1, s2)
+
+
+def test_nan_sentinel_every_element_written_once():
+    """C pre-filled with NaN inside a guard band: afterwards every logical
+    element is finite and the padding columns and the rows after the last are
+    still NaN."""
+    for (M, N, K) in [(257, 193, 70), (1000, 1000, 64), (5, 300, 40)]:
+        A, B = gi.small_case("bf16", M, N, K, seed=3)
+        buf = torch.full((M + 3, N + 9), float("nan"), device="cuda")
+        g5.gemm_bf16(dev_bf16(A), dev_bf16(B), buf[:M, :N])
+        h = buf.cpu().numpy()
+        assert np.all(np.isfinite(h[:M, :N]))
+        assert np.all(np.isnan(h[:M, N:])) and np.all(np.isnan(h[M:, :]))
