@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of the dense-GEMM library on one MI355X.
+
+Headline: TFLOPS and fraction of the dense BF16 matrix-core peak for the FFN
+projection C[1024,12288] = X[1024,4096] . W[4096,12288] (bf16 in, FP32
+accumulation, bf16 out), and HBM GB/s of the M=1 decode shape.  The other
+workloads (decode M=4/16, FP32 256^3 and 4096^3, batched attention scores,
+the ragged 1000x12280x4100 GEMM) are reported in "workloads".
+
+Timing: inputs are generated on the host from fixed seeds, copied to HBM, and
+rotated over R buffer sets (R x working set >= 512 MiB) so that successive
+calls cannot be served from the 256 MiB Infinity Cache.  After W warmup calls,
+K back-to-back calls are bracketed by HIP events recorded on the stream the
+kernels run on; the time per call is the event interval / K.
+
+One JSON line is printed on stdout.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6    # 256 CUs x 4096 FLOP/clk x 2.4 GHz, dense
+PEAK_F32_TFLOPS = 157.3      # FP32 matrix
+PEAK_HBM_GBPS = 8000.0
+METRIC = "TFLOPS & % MFMA peak, BF16 1024x4096x12288; GB/s at M=1 decode"
+KERNEL_SRC = os.path.join(ROOT, "dense_gemm_05_amd", "csrc", "g5_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_bf16_256x192_traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "sgemm", "batched", "ragged", "copy"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        msg = ("bench.py measures one GPU only: this library has no multi-GPU path "
+               "(each GPU would run its own shard of the GEMM; see the sharding notes). Use --gpus 1.")
+        print(json.dumps({"error": msg, "n_gpus": args.gpus}))
+        print(msg, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gemm_inputs as gi
+    from __graft_entry__ import _ensure_built
+    _ensure_built()
+    import dense_gemm_05_amd as g5
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def to_dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def timed(fn_list, steps, warmup):
+        """fn_list: one closure per buffer set.  Returns ms per call."""
+        R = len(fn_list)
+        for i in range(warmup):
+            fn_list[i % R]()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(steps):
+            fn_list[i % R]()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    def rotations(set_bytes):
+        return min(64, max(1, -(-512 * 2 ** 20 // set_bytes)))
+
+    out = {"metric": METRIC, "value": None, "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded; N(0,1) X, N(0,1/64) W)",
+           "config": {"workload": "bf16 FFN projection X[1024,4096] . W[4096,12288] -> C bf16, FP32 accumulate",
+                      "M": 1024, "N": 12288, "K": 4096, "global_batch": 1024, "parallelism": "single GPU"}}
+    workloads = []
+    ffn_rows_gpu = None
+
+    if args.only == "copy":
+        # Calibration for HBM byte counters: a plain device-to-device copy of
+        # 1 GiB (torch's copy kernel) reads and writes exactly 1 GiB.
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy: 3 x 1 GiB device copies done")
+        print(json.dumps({"copy_bytes_per_launch": 4 * n, "launches": 3}))
+        return
+
+    # ------------------------------------------------------------ FFN (headline)
+    if args.only in ("all", "ffn"):
+        M, N, K = 1024, 12288, 4096
+        log("FFN: generating inputs")
+        X, W = gi.ffn_inputs(M, K, N)
+        R = rotations(2 * (M * K + K * N + M * N))
+        dX = [to_dev_bf16(X) for _ in range(R)]
+        dW = [to_dev_bf16(W) for _ in range(R)]
+        dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        fns = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i])) for i in range(R)]
+        st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
+        ms = timed(fns, args.steps, args.warmup)
+        flops = 2.0 * M * N * K
+        tflops = flops / (ms * 1e-3) / 1e12
+        log(f"FFN: {ms * 1e3:.2f} us/call, {tflops:.1f} TFLOPS ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak), "
+            f"config {plan.name.decode()}, R={R}")
+        out["value"] = round(tflops, 2)
+        out["ms_per_step"] = round(ms, 5)
+        traffic = None
+        if os.path.exists(TRAFFIC_FILE):
+            with open(TRAFFIC_FILE) as fh:
+                tr = json.load(fh)
+            if tr.get("kernel_sha256_16") == kernel_hash():
+                traffic = tr.get("hbm_bytes_per_launch")
+        out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                           "kernel": f"k_bf16_mfma<256,192,2,2,even> ({plan.name.decode()}, grid {plan.grid})",
+                           "flops_per_launch": flops}
+        workloads.append({"name": "ffn_bf16_1024x12288x4096", "us": round(ms * 1e3, 3),
+                          "tflops": round(tflops, 2), "frac_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+                          "config": plan.name.decode(), "rotations": R})
+        ffn_rows_gpu = (X, W, dC[(args.steps - 1) % R])
+
+    # ------------------------------------------------------------ decode
+    if args.only in ("all", "decode"):
+        N, K = 12288, 4096
+        for M in (1, 4, 16):
+            X, W = gi.decode_inputs(M, K, N)
+            alg_bytes = 2 * (M * K + K * N + M * N)
+            R = rotations(alg_bytes)
+            dX = [to_dev_bf16(X) for _ in range(R)]
+            dW = [to_dev_bf16(W) for _ in range(R)]
+            dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+            fns = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i])) for i in range(R)]
+            ms = timed(fns, max(200, args.steps), args.warmup)
+            gbps = alg_bytes / (ms * 1e-3) / 1e9
+            log(f"decode M={M}: {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM)")
+            rec = {"name": f"decode_bf16_m{M}_12288x4096", "us": round(ms * 1e3, 3), "GBps": round(gbps, 1),
+                   "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "alg_bytes": alg_bytes, "rotations": R}
+            workloads.append(rec)
+            if M == 1:
+                out["decode_m1"] = {"GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
+                                    "us": round(ms * 1e3, 3), "alg_bytes": alg_bytes}
+            del dX, dW, dC
+
+    # ------------------------------------------------------------ FP32
+    if args.only in ("all", "sgemm"):
+        for n, wl, steps in ((256, gi.W_SGEMM_SMALL, 500), (4096, gi.W_SGEMM_LARGE, 20)):
+            A, B = gi.sgemm_inputs(n, workload=wl)
+            R = rotations(4 * 3 * n * n)
+            dA = [torch.from_numpy(A).to(dev) for _ in range(R)]
+            dB = [torch.from_numpy(B).to(dev) for _ in range(R)]
+            dC = [torch.empty((n, n), device=dev) for _ in range(R)]
+            fns = [(lambda i=i: g5.gemm_sgemm(dA[i], dB[i], dC[i])) for i in range(R)]
+            ms = timed(fns, steps, 5)
+            tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+            log(f"sgemm {n}^3: {ms * 1e3:.2f} us/call, {tf:.1f} TFLOPS ({100 * tf / PEAK_F32_TFLOPS:.1f}% of fp32 peak)")
+            workloads.append({"name": f"sgemm_f32_{n}^3", "us": round(ms * 1e3, 3), "tflops": round(tf, 2),
+                              "frac_peak": round(tf / PEAK_F32_TFLOPS, 4), "rotations": R})
+            del dA, dB, dC
+
+    # ------------------------------------------------------------ batched
+    if args.only in ("all", "batched"):
+        Q, KT = gi.batched_inputs()
+        bt, M, K = Q.shape
+        N = KT.shape[2]
+        alg_bytes = 2 * Q.size + 2 * KT.size + 4 * bt * M * N
+        R = rotations(alg_bytes)
+        dQ = [to_dev_bf16(Q) for _ in range(R)]
+        dK = [to_dev_bf16(KT) for _ in range(R)]
+        dC = [torch.empty((bt, M, N), device=dev) for _ in range(R)]
+        fns = [(lambda i=i: g5.gemm_bf16_batched(dQ[i], dK[i], dC[i])) for i in range(R)]
+        ms = timed(fns, 100, 10)
+        flops = 2.0 * bt * M * N * K
+        t_roof = max(flops / (PEAK_BF16_TFLOPS * 1e12), alg_bytes / (PEAK_HBM_GBPS * 1e9))
+        gbps = alg_bytes / (ms * 1e-3) / 1e9
+        log(f"batched 32x1024x1024x128: {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s, roofline frac {t_roof / (ms * 1e-3):.3f}")
+        workloads.append({"name": "batched_bf16_32x1024x1024x128_f32out", "us": round(ms * 1e3, 3),
+                          "GBps": round(gbps, 1), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                          "frac_roofline": round(t_roof / (ms * 1e-3), 4), "alg_bytes": alg_bytes, "rotations": R})
+        del dQ, dK, dC
+
+    # ------------------------------------------------------------ ragged
+    if args.only in ("all", "ragged"):
+        A, B = gi.ragged_inputs()
+        M, K = A.shape
+        N = B.shape[1]
+        R = rotations(2 * (M * K + K * N) + 4 * M * N)
+        dA = [to_dev_bf16(A) for _ in range(R)]
+        dB = [to_dev_bf16(B) for _ in range(R)]
+        dC = [torch.empty((M, N), device=dev) for _ in range(R)]
+        fns = [(lambda i=i: g5.gemm_bf16(dA[i], dB[i], dC[i])) for i in range(R)]
+        ms = timed(fns, 30, 5)
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        log(f"ragged 1000x12280x4100: {ms * 1e3:.2f} us/call, {tf:.1f} TFLOPS ({100 * tf / PEAK_BF16_TFLOPS:.1f}%)")
+        workloads.append({"name": "ragged_bf16_1000x12280x4100_f32out", "us": round(ms * 1e3, 3),
+                          "tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "rotations": R})
+        del dA, dB, dC
+
+    out["workloads"] = workloads
+
+    # ------------------------------------------------------------ CPU oracle
+    if not args.no_cpu and ffn_rows_gpu is not None:
+        import oracle
+        X, W, dCl = ffn_rows_gpu
+        Cg = dCl.view(torch.int16).cpu().numpy().view(np.uint16)
+        t = time.time()
+        oracle.gemm_bf16(np.ascontiguousarray(X[:8]), W)       # calibration, 8 rows
+        per_row = (time.time() - t) / 8
+        rows = int(max(8, min(1024, args.cpu_seconds / max(per_row, 1e-6))))
+        t = time.time()
+        ref = oracle.gemm_bf16(np.ascontiguousarray(X[:rows]), W)
+        secs = time.time() - t
+        cpu_tflops = 2.0 * rows * 12288 * 4096 / secs / 1e12
+        got = gi.bf16_bits_to_f32(Cg[:rows]).astype(np.float64)
+        bound = 2.0 ** -8 * np.abs(ref) + 1e-3 * 64.0
+        worst = float((np.abs(got - ref) / bound).max())
+        log(f"oracle: {rows} rows in {secs:.1f} s on {oracle.num_threads()} threads -> {cpu_tflops * 1e3:.2f} GFLOPS; "
+            f"GPU rows within bar, worst err/bound {worst:.3f}")
+        out["cpu_baseline"] = {"value": round(cpu_tflops, 6), "unit": "TFLOPS", "cores": oracle.num_threads(),
+                               "kind": "oracle",
+                               "sample": f"first {rows} of 1024 rows of the FFN projection (x 12288 cols, K=4096), "
+                                         f"FP64 triple loop, {secs:.1f} s",
+                               "gpu_rows_worst_err_over_bound": round(worst, 4)}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -24,7 +24,6 @@ const ConfigInfo kConfigs[CFG_COUNT] = {
     {CFG_NONE, GEMM_FAMILY_NONE, 0, 0, 0, 0, 0, "none"},
     {CFG_ZERO, GEMM_FAMILY_ZERO, 0, 0, 0, 256, 0, "zero"},
     {CFG_BF16_256x192, GEMM_FAMILY_BF16_MFMA, 256, 192, 64, 256, 2 * (256 * 64 + 64 * 192) * 2, "bf16_256x192"},
-    {CFG_BF16_256x256, GEMM_FAMILY_BF16_MFMA, 256, 256, 64, 256, 2 * (256 * 64 + 64 * 256) * 2, "bf16_256x256"},
     {CFG_BF16_128x128, GEMM_FAMILY_BF16_MFMA, 128, 128, 64, 256, 2 * (128 * 64 + 64 * 128) * 2, "bf16_128x128"},
     {CFG_BF16_256x128, GEMM_FAMILY_BF16_MFMA, 256, 128, 64, 256, 2 * (256 * 64 + 64 * 128) * 2, "bf16_256x128"},
     {CFG_F32_128x128, GEMM_FAMILY_F32_MFMA, 128, 128, 32, 256, 2 * (128 * 32 + 32 * 132) * 4, "f32_128x128"},

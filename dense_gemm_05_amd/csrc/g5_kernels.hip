@@ -135,11 +135,48 @@ __device__ __forceinline__ void store4(void *Cbase, bool out_f32, int64_t ldc, i
     }
 }
 
+// One wave-wide direct-to-LDS copy: lane i's 16 bytes at byte offset
+// voff + soff of the buffer based at `base` land at lds + 16 i (bytes).
+// The buffer base must be the same for every lane; num_records is set to the
+// largest positive value, the aligned kernels' offsets stay far below it.
+__device__ __forceinline__ void buffer_load_lds16(const void *base, uint32_t voff, uint32_t soff, void *lds)
+{
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, G5_LDS(void, lds), 16, voff, soff, 0, 0);
+}
+
+// The same copy issued as an instruction the compiler does not look into.
+// Its waitcnt pass would otherwise treat every later LDS read as possibly
+// aliasing the copy's destination and wait for all copies in flight
+// (vmcnt(0)), which would serialise a multi-stage ring; the ring kernel
+// accounts for its copies itself with explicit vmcnt waits.  M0 carries the
+// LDS destination; one wait state separates its write from the load.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t make_rsrc(const void *base)
+{
+    const uint64_t b = (uint64_t)base;
+    i32x4_t r;
+    r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)b);
+    r[1] = __builtin_amdgcn_readfirstlane((int32_t)((b >> 32) & 0xffffu));
+    r[2] = 0x7fffffff;
+    r[3] = 0x00020000;
+    return r;
+}
+__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t soff, const void *lds)
+{
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)G5_LDS(const void, lds));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
 // XOR swizzles of 16-byte chunk indices.
 //  A slab rows hold 8 chunks (64 bf16 or 32 fp32): the chunk index is XORed
-//  with a function of the row that is distinct over any 8 consecutive rows
-//  and, paired with the row's parity, over any 16 consecutive rows.
-__device__ __forceinline__ int swz_a(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+//  with row & 7, so the 16 rows that one fragment read touches (16 lanes,
+//  same logical chunk) land on 8 distinct chunk positions -- measured
+//  conflict-free for ds_read_b128 on gfx950 (4 LDS cycles per wave read).
+__device__ __forceinline__ int swz_a(int row) { return row & 7; }
 //  bf16 B slab rows (k) are read 4 rows x 32 bytes per 16 lanes by the
 //  transposing read; XORing chunk bits 1..2 (a 32-byte segment inside an
 //  aligned group of 4 segments) with this function of k spreads the 8 rows
@@ -290,6 +327,191 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 1) k_bf16_mfma(GemmArgs p)
             const bool full = EVEN || (m < M && n + 4 <= N);
             if (!EVEN && (m >= M || n >= N)) continue;
             store4(Cb, p.out_f32 != 0, p.ldc, m, n, acc[fn][fm], full, M, N, p.align_c);
+        }
+}
+
+// ============================================ bf16 MFMA kernel, aligned case
+//
+// For problems whose dimensions are whole tiles and whose rows are 16-byte
+// aligned.  Tile BM x BN, 8 waves (two per SIMD, so one wave's MFMAs run
+// while the other waits), wave tile (BM/WGM) x (BN/WGN).
+//
+// K is walked in stages of 32 through a ring of NS LDS slots, so the copies
+// of stage k+NS-1 are in flight while stage k is multiplied: the slab copies
+// from L2 (and, on first touch, HBM) get NS-1 stages of compute to land
+// ("4.1 Tối ưu hiệu năng toán tử GEMM trên CUDA" §9-§10 and "Operator &
+// Runtime" §5.3.2 double buffering, deepened for gfx950's latency; three or
+// four stages in the CUTLASS sense the first page cites).
+//  * Copies are buffer loads that write LDS directly
+//    (buffer_load_dwordx4 ... lds): one wave instruction moves 64 x 16 bytes
+//    into 1 KiB of LDS, lane i at byte 16 i, with no registers or ds_write
+//    instructions spent on staging.  The slot's XOR swizzle is applied by
+//    choosing, per lane, which global chunk lands in its position.  Waves
+//    0..A_W-1 copy A, the next B_W waves copy B.
+//  * A slot rows are 32 bf16 = 64 bytes (4 chunks), swizzled chunk ^
+//    ((row >> 1) & 3), measured conflict-free for the fragment reads; B slot
+//    rows are BN bf16, swizzled with swz_b, read with ds_read_b64_tr_b16.
+//  * Each wave waits for its own copies of the next stage (vmcnt counts
+//    the copies still allowed in flight), then one barrier per stage.  After
+//    the barrier the next stage's fragments are read into the second
+//    register set while the last TAIL MFMAs of the current stage run.
+template <int BM, int BN, int WGM, int WGN, int NS>
+__global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
+{
+    constexpr int NWAVE = WGM * WGN;
+    constexpr int BK = 32;
+    constexpr int TM = BM / WGM, TN = BN / WGN;
+    constexpr int FM = TM / 16, FN = TN / 16;
+    constexpr int NMFMA = FM * FN;
+    constexpr int TAIL = NMFMA / 2;                           // MFMAs run after the barrier
+    constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN;
+    constexpr int SLOT = A_ELEMS + B_ELEMS;                   // elements per ring slot
+    constexpr int A_REG = A_ELEMS * 2 / 1024, B_REG = B_ELEMS * 2 / 1024;
+    constexpr int A_W = NWAVE / 2, B_W = NWAVE / 2;           // copying waves per operand
+    constexpr int LA = A_REG / A_W, LB = B_REG / B_W;         // copies per wave per stage
+    static_assert(NWAVE == 8, "two waves per SIMD");
+    static_assert(A_REG % A_W == 0 && B_REG % B_W == 0, "slab split");
+    static_assert((BN / 8) % 8 == 0, "B slot rows must be whole swizzle groups");
+    static_assert(LA <= 7 && LB <= 7 && NS >= 3, "vmcnt accounting");
+    static_assert(TAIL > 0 && TAIL < NMFMA, "tail");
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * SLOT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int g = lane >> 4, li = lane & 15;
+
+    const TileCoord tc = tile_map(blockIdx.x, p.batch, p.tiles_m, p.tiles_n, p.group_m);
+    const int64_t m0 = tc.tm * BM, n0 = tc.tn * BN;
+    const int64_t lda = p.lda, ldb = p.ldb;
+    const uint16_t *Ab = (const uint16_t *)p.A + tc.b * p.sA + m0 * lda;
+    const uint16_t *Bb = (const uint16_t *)p.B + tc.b * p.sB + n0;
+
+    // Copy sources (byte offsets from the stage's buffer base).  A region r
+    // holds slot rows 16r..16r+15: lane l lands in row 16r + l/4, position
+    // l%4, which holds logical chunk (l%4) ^ ((row >> 1) & 3) -- the same for
+    // every r.  B region r is bytes [1024 r, 1024 r + 1024) of the [32][BN]
+    // slot: lane l lands at row k, position pc, holding chunk pc ^ swz_b(k).
+    const bool a_wave = wave < A_W;
+    const int a_r0 = a_wave ? wave * LA : 0;
+    const int a_row = 16 * a_r0 + (lane >> 2);
+    const uint32_t a_voff = (uint32_t)(a_row * lda * 2 + (((lane & 3) ^ ((a_row >> 1) & 3)) * 16));
+    const uint32_t a_rstride = (uint32_t)(16 * lda * 2);
+    const int b_r0 = a_wave ? 0 : (wave - A_W) * LB;
+    uint32_t b_voff[LB];
+#pragma unroll
+    for (int j = 0; j < LB; ++j) {
+        const int q = 1024 * (b_r0 + j) + 16 * lane;
+        const int k = q / (BN * 2), pc = (q % (BN * 2)) / 16;
+        b_voff[j] = (uint32_t)((k * ldb + ((pc ^ swz_b(k)) * 8)) * 2);
+    }
+    auto issue = [&](int kt, int slot) {
+        uint16_t *sl = smem + slot * SLOT;
+        if (a_wave) {
+            const i32x4_t r = make_rsrc(Ab + (int64_t)kt * BK);
+#pragma unroll
+            for (int j = 0; j < LA; ++j) dma16(r, a_voff, a_rstride * j, sl + (a_r0 + j) * 512);
+        } else {
+            const i32x4_t r = make_rsrc(Bb + (int64_t)kt * BK * ldb);
+#pragma unroll
+            for (int j = 0; j < LB; ++j) dma16(r, b_voff[j], 0, sl + A_ELEMS + (b_r0 + j) * 512);
+        }
+    };
+
+    // Fragment read offsets within a slot (elements).
+    int a_rd[FM], b_rd[FN], b_rd4[FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+        const int row = wm * TM + fm * 16 + li;
+        a_rd[fm] = row * BK + ((g ^ ((row >> 1) & 3)) * 8);
+    }
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+        const int k = g * 8 + (li >> 2);
+        const int ncol = wn * TN + fn * 16 + (li & 3) * 4;
+        const int c = ncol >> 3, half = (ncol >> 2) & 1;
+        b_rd[fn] = A_ELEMS + k * BN + ((c ^ swz_b(k)) * 8) + half * 4;
+        b_rd4[fn] = A_ELEMS + (k + 4) * BN + ((c ^ swz_b(k + 4)) * 8) + half * 4;
+    }
+    struct Frags {
+        bf16x8 a[FM];
+        bf16x8 b[FN];
+    };
+    auto read_frags = [&](Frags &f, int slot) {
+        const uint16_t *sl = smem + slot * SLOT;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) f.a[fm] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(sl + a_rd[fm]));
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G5_LDS(i16x4, sl + b_rd[fn]));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G5_LDS(i16x4, sl + b_rd4[fn]));
+            f.b[fn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    };
+
+    f32x4 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto mfma_range = [&](const Frags &f, int first, int count) {
+#pragma unroll
+        for (int t = 0; t < NMFMA; ++t) {
+            if (t < first || t >= first + count) continue;
+            const int fn = t / FM, fm = t % FM;
+            acc[fn][fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[fn], f.a[fm], acc[fn][fm], 0, 0, 0);
+        }
+    };
+
+    // Wait until this wave's copies of the next stage have landed -- at most
+    // (NS-2) stages of its copies may still be in flight -- and its LDS reads
+    // are done, then the workgroup barrier.  gfx9 s_waitcnt encoding:
+    // vmcnt[3:0] (values < 16), expcnt[6:4] = 7 (no wait), lgkmcnt[11:8] = 0.
+    auto stage_barrier = [&]() {
+        if (a_wave) __builtin_amdgcn_s_waitcnt(0x0070 | (LA * (NS - 2)));
+        else __builtin_amdgcn_s_waitcnt(0x0070 | (LB * (NS - 2)));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");   // no LDS access moves across the barrier
+    };
+
+    const int KT = (int)(p.K / BK);
+#pragma unroll
+    for (int s2 = 0; s2 < NS - 1; ++s2) issue(s2 < KT ? s2 : KT - 1, s2);
+    stage_barrier();
+    Frags f0, f1;
+    read_frags(f0, 0);
+
+    // One stage: copies for stage kt+NS-1 (clamped: the last NS-1 stages
+    // reload the final stage into slots nobody reads again, which keeps the
+    // in-flight counts uniform), MFMAs, barrier, next fragments, tail.
+    auto step = [&](int kt, Frags &fc, Frags &fnx) {
+        const int ks = kt + NS - 1;
+        issue(ks < KT ? ks : KT - 1, ks % NS);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_range(fc, 0, NMFMA - TAIL);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_barrier();
+        read_frags(fnx, (kt + 1) % NS);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_range(fc, NMFMA - TAIL, TAIL);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = 0;
+    for (; kt + 1 < KT; kt += 2) {
+        step(kt, f0, f1);
+        step(kt + 1, f1, f0);
+    }
+    if (kt < KT) step(kt, f0, f1);
+    __builtin_amdgcn_s_waitcnt(0);
+
+    void *Cb = (char *)p.C + tc.b * p.sC * (p.out_f32 ? 4 : 2);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int64_t m = m0 + wm * TM + fm * 16 + li;
+            const int64_t n = n0 + wn * TN + fn * 16 + g * 4;
+            store4(Cb, p.out_f32 != 0, p.ldc, m, n, acc[fn][fm], true, p.M, p.N, p.align_c);
         }
 }
 
@@ -574,10 +796,10 @@ __global__ void __launch_bounds__(256) k_zero(GemmArgs p)
 
 // ================================================================ launchers
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, int DWGM, int DWGN>
 static hipError_t launch_bf16(const GemmArgs &a, bool even, int64_t grid, hipStream_t s)
 {
-    if (even) hipLaunchKernelGGL((k_bf16_mfma<BM, BN, WGM, WGN, true>), dim3((unsigned)grid), dim3(WGM * WGN * 64), 0, s, a);
+    if (even) hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, 4>), dim3((unsigned)grid), dim3(DWGM * DWGN * 64), 0, s, a);
     else hipLaunchKernelGGL((k_bf16_mfma<BM, BN, WGM, WGN, false>), dim3((unsigned)grid), dim3(WGM * WGN * 64), 0, s, a);
     return hipGetLastError();
 }
@@ -597,10 +819,9 @@ hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, bool
     case CFG_ZERO:
         hipLaunchKernelGGL(k_zero, dim3((unsigned)grid), dim3(256), 0, s, a);
         return hipGetLastError();
-    case CFG_BF16_256x192: return launch_bf16<256, 192, 2, 2>(a, even, grid, s);
-    case CFG_BF16_256x256: return launch_bf16<256, 256, 2, 2>(a, even, grid, s);
-    case CFG_BF16_128x128: return launch_bf16<128, 128, 2, 2>(a, even, grid, s);
-    case CFG_BF16_256x128: return launch_bf16<256, 128, 2, 2>(a, even, grid, s);
+    case CFG_BF16_256x192: return launch_bf16<256, 192, 2, 2, 4, 2>(a, even, grid, s);
+    case CFG_BF16_128x128: return launch_bf16<128, 128, 2, 2, 4, 2>(a, even, grid, s);
+    case CFG_BF16_256x128: return launch_bf16<256, 128, 2, 2, 4, 2>(a, even, grid, s);
     case CFG_F32_128x128: return launch_f32<128, 128, 2, 2>(a, even, grid, s);
     case CFG_F32_64x64: return launch_f32<64, 64, 2, 2>(a, even, grid, s);
     case CFG_DECODE_64:
