@@ -33,7 +33,7 @@ class GemmPlan(ctypes.Structure):
     _fields_ = [("family", ctypes.c_int), ("config_id", ctypes.c_int),
                 ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("tile_k", ctypes.c_int),
                 ("threads", ctypes.c_int), ("vec_a", ctypes.c_int), ("vec_b", ctypes.c_int),
-                ("even", ctypes.c_int), ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int64),
+                ("even", ctypes.c_int), ("variant", ctypes.c_int), ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int64),
                 ("model_bytes", ctypes.c_double), ("name", ctypes.c_char * 48)]
 
 

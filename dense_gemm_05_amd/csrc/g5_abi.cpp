@@ -49,7 +49,8 @@ struct Problem {
 
 struct Plan {
     int config = CFG_NONE;
-    bool even = false;
+    bool even = false;       // no edge masking
+    int variant = 0;         // kernel variant passed to launch_config
     int64_t grid = 0;
     int64_t tiles_m = 0, tiles_n = 0, group_m = 1;
     int align_a = 2, align_b = 2, align_c = 2;
@@ -184,14 +185,30 @@ void fill_grid(const Problem &p, Plan &pl)
                          : 0.0;
 }
 
-bool even_ok(const Problem &p, const Plan &pl)
+// Tiled kernel variant for a config (see launch_config): the aligned ring
+// kernel when the problem is whole tiles with 16-byte rows, the masked ring
+// kernel when B rows are 16-byte and A rows at least 4-byte aligned and each
+// operand's byte extent fits 31 bits (32-bit buffer offsets), else the fully
+// general kernel.
+int pick_variant(const Problem &p, const Plan &pl, bool *even)
 {
     const ConfigInfo &c = kConfigs[pl.config];
-    if (c.family != GEMM_FAMILY_BF16_MFMA && c.family != GEMM_FAMILY_F32_MFMA) return false;
-    if (p.M % c.tile_m || p.N % c.tile_n || p.K % c.tile_k) return false;
-    if (pl.align_a < 16 || pl.align_b < 16) return false;
-    if (pl.align_c < (elem_c(p) == 4 ? 16 : 8)) return false;
-    return true;
+    *even = false;
+    if (c.family == GEMM_FAMILY_F32_MFMA) {
+        *even = !(p.M % c.tile_m || p.N % c.tile_n || p.K % c.tile_k) && pl.align_a >= 16 && pl.align_b >= 16 &&
+                pl.align_c >= 16;
+        return *even ? 1 : 0;
+    }
+    if (c.family != GEMM_FAMILY_BF16_MFMA) return 0;
+    const __int128 a_bytes = ((__int128)(p.M - 1) * p.lda + p.K) * 2;
+    const __int128 b_bytes = ((__int128)(p.K - 1) * p.ldb + p.N) * 2;
+    const bool fits = a_bytes < ((__int128)1 << 31) && b_bytes < ((__int128)1 << 31);
+    if (!fits || pl.align_b < 16 || pl.align_a < 4) return 0;
+    const int ring_k = 32;
+    *even = !(p.M % c.tile_m || p.N % c.tile_n || p.K % ring_k) && pl.align_a >= 16 &&
+            pl.align_c >= (elem_c(p) == 4 ? 16 : 8);
+    if (*even) return 1;
+    return pl.align_a >= 16 ? 2 : 3;
 }
 
 // Returns GEMM_OK or GEMM_ERR_UNSUPPORTED.
@@ -235,7 +252,13 @@ int select_plan(const Problem &p, Plan &pl)
         const int nc = p.op == GEMM_OP_BF16 ? 3 : 2;
         double best = 0.0;
         for (int i = 0; i < nc; ++i) {
-            const double t = model_time(p, kConfigs[cands[i].id], cands[i].eff);
+            Plan trial = pl;
+            trial.config = cands[i].id;
+            bool ev = false;
+            const int var = pick_variant(p, trial, &ev);
+            // measured relative speed of the kernel variants
+            const double veff = var == 1 ? 1.0 : (var == 2 || var == 3) ? 0.85 : 0.3;
+            const double t = model_time(p, kConfigs[cands[i].id], cands[i].eff * veff);
             if (pl.config == CFG_NONE || t < best) {
                 best = t;
                 pl.config = cands[i].id;
@@ -244,7 +267,7 @@ int select_plan(const Problem &p, Plan &pl)
     }
     fill_grid(p, pl);
     if (pl.grid <= 0 || pl.grid > (int64_t)1 << 24) return GEMM_ERR_UNSUPPORTED;
-    pl.even = even_ok(p, pl);
+    pl.variant = pick_variant(p, pl, &pl.even);
     return GEMM_OK;
 }
 
@@ -262,6 +285,7 @@ void fill_public_plan(const Problem &p, const Plan &pl, gemm_plan *out)
     out->vec_a = pl.align_a;
     out->vec_b = pl.align_b;
     out->even = pl.even ? 1 : 0;
+    out->variant = pl.variant;
     out->grid = pl.grid * (c.family == GEMM_FAMILY_DECODE ? p.batch : 1);
     out->lds_bytes = c.lds_bytes;
     out->model_bytes = pl.model_bytes;
@@ -307,9 +331,9 @@ int run(const Problem &p, void *stream)
     st = check_device();
     if (st != GEMM_OK) return st;
     if (log_enabled())
-        std::fprintf(stderr, "[gemm05] op=%d batch=%lld M=%lld N=%lld K=%lld -> %s even=%d grid=%lld align=(%d,%d,%d)\n",
+        std::fprintf(stderr, "[gemm05] op=%d batch=%lld M=%lld N=%lld K=%lld -> %s variant=%d grid=%lld align=(%d,%d,%d)\n",
                      p.op, (long long)p.batch, (long long)p.M, (long long)p.N, (long long)p.K,
-                     kConfigs[pl.config].name, pl.even ? 1 : 0, (long long)pl.grid, pl.align_a, pl.align_b,
+                     kConfigs[pl.config].name, pl.variant, (long long)pl.grid, pl.align_a, pl.align_b,
                      pl.align_c);
     GemmArgs a;
     a.A = (const void *)p.a;
@@ -332,7 +356,7 @@ int run(const Problem &p, void *stream)
     a.align_b = pl.align_b;
     a.align_c = pl.align_c;
     a.out_f32 = elem_c(p) == 4 ? 1 : 0;
-    const hipError_t e = launch_config(pl.config, p.op == GEMM_OP_SGEMM, a, pl.even, pl.grid, (hipStream_t)stream);
+    const hipError_t e = launch_config(pl.config, p.op == GEMM_OP_SGEMM, a, pl.variant, pl.grid, (hipStream_t)stream);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 

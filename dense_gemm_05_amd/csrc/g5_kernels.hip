@@ -152,23 +152,39 @@ __device__ __forceinline__ void buffer_load_lds16(const void *base, uint32_t vof
 // accounts for its copies itself with explicit vmcnt waits.  M0 carries the
 // LDS destination; one wait state separates its write from the load.
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4_t make_rsrc(const void *base)
+__device__ __forceinline__ i32x4_t make_rsrc(const void *base, uint32_t num_records = 0x7fffffffu)
 {
     const uint64_t b = (uint64_t)base;
     i32x4_t r;
     r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)b);
     r[1] = __builtin_amdgcn_readfirstlane((int32_t)((b >> 32) & 0xffffu));
-    r[2] = 0x7fffffff;
+    r[2] = __builtin_amdgcn_readfirstlane((int32_t)num_records);
     r[3] = 0x00020000;
     return r;
 }
-__device__ __forceinline__ void dma16(i32x4_t rsrc, uint32_t voff, uint32_t soff, const void *lds)
+// BYTES is 16 (dwordx4) or 4 (dword): the LDS-writing buffer loads that
+// gfx950 provides for these widths.
+template <int BYTES>
+__device__ __forceinline__ void dma(i32x4_t rsrc, uint32_t voff, uint32_t soff, const void *lds)
 {
     const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)G5_LDS(const void, lds));
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
-                 : "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff)
-                 : "memory", "m0");
+    if (BYTES == 16)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :
+                     : "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                     :
+                     : "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff)
+                     : "memory", "m0");
+}
+
+// s_waitcnt immediate (gfx9 layout): vmcnt in bits [3:0] and [15:14],
+// expcnt [6:4] (7 = no wait), lgkmcnt [11:8].
+constexpr int waitcnt_imm(int vmcnt, int lgkmcnt)
+{
+    return (vmcnt & 0xf) | ((vmcnt >> 4) << 14) | (7 << 4) | ((lgkmcnt & 0xf) << 8);
 }
 
 // XOR swizzles of 16-byte chunk indices.
@@ -330,24 +346,22 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 1) k_bf16_mfma(GemmArgs p)
         }
 }
 
-// ============================================ bf16 MFMA kernel, aligned case
+// ================================================= bf16 MFMA ring kernel
 //
-// For problems whose dimensions are whole tiles and whose rows are 16-byte
-// aligned.  Tile BM x BN, 8 waves (two per SIMD, so one wave's MFMAs run
-// while the other waits), wave tile (BM/WGM) x (BN/WGN).
+// Tile BM x BN, 8 waves (two per SIMD, so one wave's MFMAs run while the
+// other waits), wave tile (BM/WGM) x (BN/WGN).
 //
 // K is walked in stages of 32 through a ring of NS LDS slots, so the copies
 // of stage k+NS-1 are in flight while stage k is multiplied: the slab copies
 // from L2 (and, on first touch, HBM) get NS-1 stages of compute to land
 // ("4.1 Tối ưu hiệu năng toán tử GEMM trên CUDA" §9-§10 and "Operator &
-// Runtime" §5.3.2 double buffering, deepened for gfx950's latency; three or
-// four stages in the CUTLASS sense the first page cites).
-//  * Copies are buffer loads that write LDS directly
-//    (buffer_load_dwordx4 ... lds): one wave instruction moves 64 x 16 bytes
-//    into 1 KiB of LDS, lane i at byte 16 i, with no registers or ds_write
-//    instructions spent on staging.  The slot's XOR swizzle is applied by
-//    choosing, per lane, which global chunk lands in its position.  Waves
-//    0..A_W-1 copy A, the next B_W waves copy B.
+// Runtime" §5.3.2 double buffering, deepened for gfx950's latency).
+//  * Copies are buffer loads that write LDS directly (buffer_load ... lds):
+//    one wave instruction moves 64 lanes x AV bytes of A (AV = 16, or 4 for
+//    rows that are only 4- or 8-byte aligned) or 64 x 16 bytes of B into LDS, lane
+//    i at byte AV*i, with no registers or ds_write instructions spent on
+//    staging.  The slot's XOR swizzle is applied by choosing, per lane, which
+//    global chunk lands in its position.  Waves 0..3 copy A, 4..7 copy B.
 //  * A slot rows are 32 bf16 = 64 bytes (4 chunks), swizzled chunk ^
 //    ((row >> 1) & 3), measured conflict-free for the fragment reads; B slot
 //    rows are BN bf16, swizzled with swz_b, read with ds_read_b64_tr_b16.
@@ -355,7 +369,13 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 1) k_bf16_mfma(GemmArgs p)
 //    the copies still allowed in flight), then one barrier per stage.  After
 //    the barrier the next stage's fragments are read into the second
 //    register set while the last TAIL MFMAs of the current stage run.
-template <int BM, int BN, int WGM, int WGN, int NS>
+//  * MASKED: the buffer descriptors carry each operand's byte extent, so
+//    reads past it return zero instead of faulting; rows of A at or beyond M
+//    are sent out of range.  Columns of B beyond N and rows of A beyond M
+//    only feed outputs that are never stored.  A K remainder (K % 32) is a
+//    final stage loaded element by element with zero fill ("4.1" §4.5 and
+//    "Operator & Runtime" §5.4.2: out-of-range elements contribute zero).
+template <int BM, int BN, int WGM, int WGN, int NS, int AV, bool MASKED>
 __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
 {
     constexpr int NWAVE = WGM * WGN;
@@ -366,13 +386,15 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     constexpr int TAIL = NMFMA / 2;                           // MFMAs run after the barrier
     constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN;
     constexpr int SLOT = A_ELEMS + B_ELEMS;                   // elements per ring slot
-    constexpr int A_REG = A_ELEMS * 2 / 1024, B_REG = B_ELEMS * 2 / 1024;
+    constexpr int A_INS = A_ELEMS * 2 / (64 * AV), B_INS = B_ELEMS * 2 / 1024;   // copy instructions
     constexpr int A_W = NWAVE / 2, B_W = NWAVE / 2;           // copying waves per operand
-    constexpr int LA = A_REG / A_W, LB = B_REG / B_W;         // copies per wave per stage
+    constexpr int LA = A_INS / A_W, LB = B_INS / B_W;         // copies per wave per stage
+    constexpr int ROWS_PER_A = 64 * AV / 64;                  // A rows per copy instruction
     static_assert(NWAVE == 8, "two waves per SIMD");
-    static_assert(A_REG % A_W == 0 && B_REG % B_W == 0, "slab split");
+    static_assert(AV == 16 || AV == 4, "A copy width");
+    static_assert(A_INS % A_W == 0 && B_INS % B_W == 0, "slab split");
     static_assert((BN / 8) % 8 == 0, "B slot rows must be whole swizzle groups");
-    static_assert(LA <= 7 && LB <= 7 && NS >= 3, "vmcnt accounting");
+    static_assert(NS >= 3 && LA * (NS - 2) < 64 && LB * (NS - 2) < 64, "vmcnt accounting");
     static_assert(TAIL > 0 && TAIL < NMFMA, "tail");
     __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * SLOT];
 
@@ -383,38 +405,52 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
 
     const TileCoord tc = tile_map(blockIdx.x, p.batch, p.tiles_m, p.tiles_n, p.group_m);
     const int64_t m0 = tc.tm * BM, n0 = tc.tn * BN;
-    const int64_t lda = p.lda, ldb = p.ldb;
-    const uint16_t *Ab = (const uint16_t *)p.A + tc.b * p.sA + m0 * lda;
-    const uint16_t *Bb = (const uint16_t *)p.B + tc.b * p.sB + n0;
+    const int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const uint16_t *Abat = (const uint16_t *)p.A + tc.b * p.sA;
+    const uint16_t *Bbat = (const uint16_t *)p.B + tc.b * p.sB;
+    // Byte extents of this batch entry's operands (reads past them return 0).
+    const uint32_t a_bytes = MASKED ? (uint32_t)(((M - 1) * lda + K) * 2) : 0x7fffffffu;
+    const uint32_t b_bytes = MASKED ? (uint32_t)(((K - 1) * ldb + N) * 2) : 0x7fffffffu;
 
-    // Copy sources (byte offsets from the stage's buffer base).  A region r
-    // holds slot rows 16r..16r+15: lane l lands in row 16r + l/4, position
-    // l%4, which holds logical chunk (l%4) ^ ((row >> 1) & 3) -- the same for
-    // every r.  B region r is bytes [1024 r, 1024 r + 1024) of the [32][BN]
-    // slot: lane l lands at row k, position pc, holding chunk pc ^ swz_b(k).
+    // Copy sources.  Offsets are bytes from the batch entry's base; the stage
+    // adds k0 (A) or k0 rows (B) through the scalar offset.  A instruction r
+    // covers slot rows ROWS_PER_A*r.. ; lane l lands in row ROWS_PER_A*r +
+    // l/(64/ROWS_PER_A) at byte (l % (64/ROWS_PER_A))*AV of the row, and
+    // holds the matching bytes of logical chunk (position ^ ((row>>1)&3)).
     const bool a_wave = wave < A_W;
-    const int a_r0 = a_wave ? wave * LA : 0;
-    const int a_row = 16 * a_r0 + (lane >> 2);
-    const uint32_t a_voff = (uint32_t)(a_row * lda * 2 + (((lane & 3) ^ ((a_row >> 1) & 3)) * 16));
-    const uint32_t a_rstride = (uint32_t)(16 * lda * 2);
-    const int b_r0 = a_wave ? 0 : (wave - A_W) * LB;
+    const int a_i0 = a_wave ? wave * LA : 0;
+    uint32_t a_voff[LA];
+#pragma unroll
+    for (int j = 0; j < LA; ++j) {
+        constexpr int LPR = 64 / ROWS_PER_A;                  // lanes per 64-byte row
+        const int row = ROWS_PER_A * (a_i0 + j) + lane / LPR;
+        const int byte = (lane % LPR) * AV;                   // byte within the slot row
+        const int chunk = (byte >> 4) ^ ((row >> 1) & 3);
+        const uint32_t off = (uint32_t)((m0 + row) * lda * 2 + chunk * 16 + (byte & 15));
+        a_voff[j] = (MASKED && m0 + row >= M) ? 0x80000000u : off;
+    }
+    const int b_i0 = a_wave ? 0 : (wave - A_W) * LB;
     uint32_t b_voff[LB];
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
-        const int q = 1024 * (b_r0 + j) + 16 * lane;
+        const int q = 1024 * (b_i0 + j) + 16 * lane;
         const int k = q / (BN * 2), pc = (q % (BN * 2)) / 16;
-        b_voff[j] = (uint32_t)((k * ldb + ((pc ^ swz_b(k)) * 8)) * 2);
+        b_voff[j] = (uint32_t)((k * ldb + n0 + ((pc ^ swz_b(k)) * 8)) * 2);
     }
+    // The stage's offset moves the descriptor base (scalar arithmetic) and
+    // shrinks its extent to match, so the scalar offset stays 0.
     auto issue = [&](int kt, int slot) {
         uint16_t *sl = smem + slot * SLOT;
         if (a_wave) {
-            const i32x4_t r = make_rsrc(Ab + (int64_t)kt * BK);
+            const uint32_t adv = (uint32_t)(kt * BK * 2);
+            const i32x4_t r = make_rsrc(Abat + (int64_t)kt * BK, a_bytes - adv);
 #pragma unroll
-            for (int j = 0; j < LA; ++j) dma16(r, a_voff, a_rstride * j, sl + (a_r0 + j) * 512);
+            for (int j = 0; j < LA; ++j) dma<AV>(r, a_voff[j], 0, sl + (a_i0 + j) * (32 * AV));
         } else {
-            const i32x4_t r = make_rsrc(Bb + (int64_t)kt * BK * ldb);
+            const uint32_t adv = (uint32_t)((int64_t)kt * BK * ldb * 2);
+            const i32x4_t r = make_rsrc(Bbat + (int64_t)kt * BK * ldb, b_bytes - adv);
 #pragma unroll
-            for (int j = 0; j < LB; ++j) dma16(r, b_voff[j], 0, sl + A_ELEMS + (b_r0 + j) * 512);
+            for (int j = 0; j < LB; ++j) dma<16>(r, b_voff[j], 0, sl + A_ELEMS + (b_i0 + j) * 512);
         }
     };
 
@@ -465,43 +501,66 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
 
     // Wait until this wave's copies of the next stage have landed -- at most
     // (NS-2) stages of its copies may still be in flight -- and its LDS reads
-    // are done, then the workgroup barrier.  gfx9 s_waitcnt encoding:
-    // vmcnt[3:0] (values < 16), expcnt[6:4] = 7 (no wait), lgkmcnt[11:8] = 0.
+    // are done, then the workgroup barrier.
     auto stage_barrier = [&]() {
-        if (a_wave) __builtin_amdgcn_s_waitcnt(0x0070 | (LA * (NS - 2)));
-        else __builtin_amdgcn_s_waitcnt(0x0070 | (LB * (NS - 2)));
+        if (a_wave) __builtin_amdgcn_s_waitcnt(waitcnt_imm(LA * (NS - 2), 0));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_imm(LB * (NS - 2), 0));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");   // no LDS access moves across the barrier
     };
 
-    const int KT = (int)(p.K / BK);
-#pragma unroll
-    for (int s2 = 0; s2 < NS - 1; ++s2) issue(s2 < KT ? s2 : KT - 1, s2);
-    stage_barrier();
+    const int KT = (int)(K / BK);                             // whole stages
     Frags f0, f1;
-    read_frags(f0, 0);
-
-    // One stage: copies for stage kt+NS-1 (clamped: the last NS-1 stages
-    // reload the final stage into slots nobody reads again, which keeps the
-    // in-flight counts uniform), MFMAs, barrier, next fragments, tail.
-    auto step = [&](int kt, Frags &fc, Frags &fnx) {
-        const int ks = kt + NS - 1;
-        issue(ks < KT ? ks : KT - 1, ks % NS);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_range(fc, 0, NMFMA - TAIL);
-        __builtin_amdgcn_sched_barrier(0);
+    if (KT > 0) {
+#pragma unroll
+        for (int s2 = 0; s2 < NS - 1; ++s2) issue(s2 < KT ? s2 : KT - 1, s2);
         stage_barrier();
-        read_frags(fnx, (kt + 1) % NS);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_range(fc, NMFMA - TAIL, TAIL);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    int kt = 0;
-    for (; kt + 1 < KT; kt += 2) {
-        step(kt, f0, f1);
-        step(kt + 1, f1, f0);
+        read_frags(f0, 0);
+
+        // One stage: copies for stage kt+NS-1 (clamped: the last NS-1 stages
+        // reload the final stage into slots nobody reads again, which keeps
+        // the in-flight counts uniform), MFMAs, barrier, next fragments, tail.
+        auto step = [&](int kt, Frags &fc, Frags &fnx) {
+            const int ks = kt + NS - 1;
+            issue(ks < KT ? ks : KT - 1, ks % NS);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_range(fc, 0, NMFMA - TAIL);
+            __builtin_amdgcn_sched_barrier(0);
+            stage_barrier();
+            read_frags(fnx, (kt + 1) % NS);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_range(fc, NMFMA - TAIL, TAIL);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        int kt = 0;
+        for (; kt + 1 < KT; kt += 2) {
+            step(kt, f0, f1);
+            step(kt + 1, f1, f0);
+        }
+        if (kt < KT) step(kt, f0, f1);
     }
-    if (kt < KT) step(kt, f0, f1);
+    if (MASKED && K % BK != 0) {
+        // K remainder: every copy in flight lands first, then the last stage
+        // is loaded element by element with zero fill into slot 0.
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const int64_t k0 = (int64_t)KT * BK;
+        uint16_t *sA = smem, *sB = smem + A_ELEMS;
+        for (int q = tid; q < BM * 4; q += NWAVE * 64) {
+            const int row = q >> 2, c = q & 3;
+            const u32x4 v = load_chunk8_bf16(Abat + (m0 + row) * lda, k0 + 8 * c, K, m0 + row < M, p.align_a);
+            *(u32x4 *)(sA + row * BK + ((c ^ ((row >> 1) & 3)) * 8)) = v;
+        }
+        for (int q = tid; q < BK * (BN / 8); q += NWAVE * 64) {
+            const int k = q / (BN / 8), c = q % (BN / 8);
+            const u32x4 v = load_chunk8_bf16(Bbat + (k0 + k) * ldb + n0, 8 * c, N - n0, k0 + k < K, p.align_b);
+            *(u32x4 *)(sB + k * BN + ((c ^ swz_b(k)) * 8)) = v;
+        }
+        __syncthreads();
+        read_frags(f0, 0);
+        mfma_range(f0, 0, NMFMA);
+    }
     __builtin_amdgcn_s_waitcnt(0);
 
     void *Cb = (char *)p.C + tc.b * p.sC * (p.out_f32 ? 4 : 2);
@@ -511,7 +570,9 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         for (int fm = 0; fm < FM; ++fm) {
             const int64_t m = m0 + wm * TM + fm * 16 + li;
             const int64_t n = n0 + wn * TN + fn * 16 + g * 4;
-            store4(Cb, p.out_f32 != 0, p.ldc, m, n, acc[fn][fm], true, p.M, p.N, p.align_c);
+            if (MASKED && (m >= M || n >= N)) continue;
+            const bool full = !MASKED || (n + 4 <= N);
+            store4(Cb, p.out_f32 != 0, p.ldc, m, n, acc[fn][fm], full, M, N, p.align_c);
         }
 }
 
@@ -796,11 +857,18 @@ __global__ void __launch_bounds__(256) k_zero(GemmArgs p)
 
 // ================================================================ launchers
 
+// variant: 0 general (k_bf16_mfma), 1 ring kernel aligned, 2 ring kernel
+// masked with 16-byte A rows, 3 ring kernel masked with 4-byte A copies.
 template <int BM, int BN, int WGM, int WGN, int DWGM, int DWGN>
-static hipError_t launch_bf16(const GemmArgs &a, bool even, int64_t grid, hipStream_t s)
+static hipError_t launch_bf16(const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
 {
-    if (even) hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, 4>), dim3((unsigned)grid), dim3(DWGM * DWGN * 64), 0, s, a);
-    else hipLaunchKernelGGL((k_bf16_mfma<BM, BN, WGM, WGN, false>), dim3((unsigned)grid), dim3(WGM * WGN * 64), 0, s, a);
+    const dim3 g((unsigned)grid), b8(DWGM * DWGN * 64);
+    switch (variant) {
+    case 1: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, 4, 16, false>), g, b8, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, 4, 16, true>), g, b8, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, 4, 4, true>), g, b8, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_bf16_mfma<BM, BN, WGM, WGN, false>), g, dim3(WGM * WGN * 64), 0, s, a); break;
+    }
     return hipGetLastError();
 }
 
@@ -812,18 +880,18 @@ static hipError_t launch_f32(const GemmArgs &a, bool even, int64_t grid, hipStre
     return hipGetLastError();
 }
 
-hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, bool even, int64_t grid,
+hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, int variant, int64_t grid,
                          hipStream_t s)
 {
     switch (config_id) {
     case CFG_ZERO:
         hipLaunchKernelGGL(k_zero, dim3((unsigned)grid), dim3(256), 0, s, a);
         return hipGetLastError();
-    case CFG_BF16_256x192: return launch_bf16<256, 192, 2, 2, 4, 2>(a, even, grid, s);
-    case CFG_BF16_128x128: return launch_bf16<128, 128, 2, 2, 4, 2>(a, even, grid, s);
-    case CFG_BF16_256x128: return launch_bf16<256, 128, 2, 2, 4, 2>(a, even, grid, s);
-    case CFG_F32_128x128: return launch_f32<128, 128, 2, 2>(a, even, grid, s);
-    case CFG_F32_64x64: return launch_f32<64, 64, 2, 2>(a, even, grid, s);
+    case CFG_BF16_256x192: return launch_bf16<256, 192, 2, 2, 4, 2>(a, variant, grid, s);
+    case CFG_BF16_128x128: return launch_bf16<128, 128, 2, 2, 4, 2>(a, variant, grid, s);
+    case CFG_BF16_256x128: return launch_bf16<256, 128, 2, 2, 4, 2>(a, variant, grid, s);
+    case CFG_F32_128x128: return launch_f32<128, 128, 2, 2>(a, variant == 1, grid, s);
+    case CFG_F32_64x64: return launch_f32<64, 64, 2, 2>(a, variant == 1, grid, s);
     case CFG_DECODE_64:
         hipLaunchKernelGGL(k_decode<16>, dim3((unsigned)grid, (unsigned)a.batch), dim3(16 * 64), 0, s, a);
         return hipGetLastError();

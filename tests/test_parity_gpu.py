@@ -292,3 +292,42 @@ def test_nan_sentinel_every_element_written_once():
         h = buf.cpu().numpy()
         assert np.all(np.isfinite(h[:M, :N]))
         assert np.all(np.isnan(h[:M, N:])) and np.all(np.isnan(h[M:, :]))
+
+
+# Each tiled-kernel variant on a shape chosen to select it (asserted through
+# the host plan).  Padding columns of A and B and the ldc padding of C hold
+# NaN: a kernel that read A beyond K, or let columns of B beyond N reach a
+# stored output, or wrote outside the logical C, fails.
+VARIANT_CASES = [
+    # M, N, K, A row pad, B row pad, expected variant
+    (512, 384, 128, 0, 0, 1),      # aligned ring kernel
+    (300, 392, 264, 0, 0, 2),      # masked ring kernel, K tail of 8
+    (300, 392, 262, 0, 0, 3),      # 4-byte A copies (rows 4-byte aligned)
+    (300, 392, 20, 4, 0, 2),       # K < 32: only the element-loaded tail stage
+    (257, 200, 96, 8, 8, 2),       # edge tiles in M and N, padded rows
+    (70, 392, 1000, 2, 0, 3),      # long K with a tail, few rows
+]
+
+
+@pytest.mark.parametrize("M,N,K,pa,pb,variant", VARIANT_CASES)
+def test_bf16_kernel_variants(oracle_mod, M, N, K, pa, pb, variant):
+    _say(f"variant {variant} {M}x{N}x{K} pads ({pa},{pb})")
+    g = np.random.default_rng([M, N, K, pa, pb])
+    A = gi.to_bf16_bits(gi.normal(g, (M, K + pa)))
+    B = gi.to_bf16_bits(gi.normal(g, (K, N + pb), 0.125))
+    A[:, K:] = 0x7FC0    # NaN in the padding
+    B[:, N:] = 0x7FC0
+    dA, dB = dev_bf16(A), dev_bf16(B)
+    for od, ct in ((torch.bfloat16, 0), (torch.float32, 1)):
+        Cfull = torch.full((M, N + 8), float("nan"), device="cuda", dtype=od)
+        st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K, lda=K + pa, ldb=N + pb, ldc=N + 8,
+                                 a_addr=dA.data_ptr(), b_addr=dB.data_ptr(), c_addr=Cfull.data_ptr(), c_type=ct)
+        assert st == 0 and plan.family == 2 and plan.variant == variant, (plan.name, plan.variant)
+        g5.gemm_bf16(dA[:, :K], dB[:, :N], Cfull[:, :N])
+        ref = oracle_mod.gemm_bf16(np.ascontiguousarray(A[:, :K]), np.ascontiguousarray(B[:, :N]))
+        host = host_values(Cfull)
+        if od == torch.bfloat16:
+            check_bf16(host[:, :N], ref, K, f"variant {variant} bf16")
+        else:
+            check_f32(host[:, :N], ref, K, amax_bf16(A[:, :K]), amax_bf16(B[:, :N]), f"variant {variant} f32")
+        assert np.all(np.isnan(host[:, N:])), "ldc padding was written"
