@@ -199,11 +199,17 @@ int pick_variant(const Problem &p, const Plan &pl, bool *even)
                 pl.align_c >= 16;
         return *even ? 1 : 0;
     }
+    if (c.family == GEMM_FAMILY_DECODE) {
+        *even = (p.N % c.tile_n == 0) && pl.align_b >= 8 && pl.align_a >= 16;
+        return *even ? 1 : 0;
+    }
     if (c.family != GEMM_FAMILY_BF16_MFMA) return 0;
     const __int128 a_bytes = ((__int128)(p.M - 1) * p.lda + p.K) * 2;
     const __int128 b_bytes = ((__int128)(p.K - 1) * p.ldb + p.N) * 2;
     const bool fits = a_bytes < ((__int128)1 << 31) && b_bytes < ((__int128)1 << 31);
-    if (!fits || pl.align_b < 16 || pl.align_a < 4) return 0;
+    // N % 8: every 16-byte chunk of B lies wholly inside or wholly past the
+    // descriptor extent (no partially out-of-range copies).
+    if (!fits || pl.align_b < 16 || pl.align_a < 4 || p.N % 8 != 0) return 0;
     const int ring_k = 32;
     *even = !(p.M % c.tile_m || p.N % c.tile_n || p.K % ring_k) && pl.align_a >= 16 &&
             pl.align_c >= (elem_c(p) == 4 ? 16 : 8);

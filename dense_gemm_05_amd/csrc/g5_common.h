@@ -78,7 +78,7 @@ enum ConfigId {
     CFG_BF16_256x128,      // 4 waves (2x2), wave tile 128x64
     CFG_F32_128x128,       // 4 waves (2x2), wave tile 64x64
     CFG_F32_64x64,         // 4 waves (2x2), wave tile 32x32
-    CFG_DECODE_64,         // small M, 64 columns per workgroup, 16 waves
+    CFG_DECODE_64,         // small M, 64 columns per workgroup, 16 waves, K split in-workgroup
     CFG_GENERIC,
     CFG_COUNT
 };

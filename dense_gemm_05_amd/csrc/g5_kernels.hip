@@ -722,7 +722,7 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_f32_mfma(GemmArgs p)
 //    maps to physical column 4r + b;
 //  * X rows (zero beyond M) are the other MFMA operand; the 16-row MFMA
 //    covers any M <= 16 at no extra memory traffic.
-template <int NW>
+template <int NW, bool FAST>
 __global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
 {
     constexpr int NC = 64;                   // columns per workgroup
@@ -735,44 +735,43 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
     const uint16_t *X = (const uint16_t *)p.A + bidx * p.sA;
     const uint16_t *W = (const uint16_t *)p.B + bidx * p.sB;
 
-    const int64_t steps = (K + 31) / 32;
+    // Fixed partition of the 32-row K steps over the waves (independent of M).
+    const int64_t steps = (K + 31) / 32, full = K / 32;
     const int64_t s_begin = steps * wave / NW, s_end = steps * (wave + 1) / NW;
-    const bool fast = (p.align_b >= 8) && (n0 + NC <= N);
-    const bool xfast = (p.align_a >= 16);
+    const int64_t s_full_end = s_end < full ? s_end : full;
     const int64_t ncol = n0 + 4 * li;        // first of this lane's 4 columns
     const bool m_ok = li < M;
+    // This lane's X row (row 0 stands in for rows beyond M; zeroed below).
+    const uint16_t *xr = X + (int64_t)(m_ok ? li : 0) * lda;
+    const uint16_t *wcol = W + ncol;
 
     f32x4 acc[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t s = s_begin; s < s_end; ++s) {
-        const int64_t kb = s * 32 + g * 8;
-        u32x2 w[8];
+    // W rows kb + j (j = 0..7) for this lane's 4 columns, whole step in range.
+    auto load_w = [&](int64_t s, u32x2 *w) {
+        const uint16_t *src = wcol + (s * 32 + g * 8) * ldb;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int64_t k = kb + j;
-            u32x2 v = {0u, 0u};
-            if (k < K) {
-                const uint16_t *src = W + k * ldb + ncol;
-                if (fast) {
-                    v = *(const u32x2 *)src;
-                } else {
-                    uint32_t e[4];
+            if (FAST) {
+                w[j] = *(const u32x2 *)(src + j * ldb);
+            } else {
+                uint32_t e[4];
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) e[c] = (ncol + c < N) ? (uint32_t)src[c] : 0u;
-                    v[0] = e[0] | (e[1] << 16);
-                    v[1] = e[2] | (e[3] << 16);
-                }
+                for (int c = 0; c < 4; ++c) e[c] = (ncol + c < N) ? (uint32_t)src[j * ldb + c] : 0u;
+                w[j] = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
             }
-            w[j] = v;
         }
-        u32x4 xv = {0u, 0u, 0u, 0u};
-        if (m_ok) {
-            const uint16_t *xr = X + (int64_t)li * lda;
-            if (xfast && kb + 8 <= K) xv = *(const u32x4 *)(xr + kb);
-            else xv = load_chunk8_bf16(xr, kb, K, true, 2);
-        }
+    };
+    auto load_x = [&](int64_t s) -> u32x4 {
+        const int64_t kb = s * 32 + g * 8;
+        u32x4 v = FAST ? *(const u32x4 *)(xr + kb) : load_chunk8_bf16(xr, kb, K, true, 2);
+        if (!m_ok) v = u32x4{0u, 0u, 0u, 0u};
+        return v;
+    };
+    // 4x8 transpose of 16-bit halves: block b takes column b of the 8 rows.
+    auto mma = [&](const u32x2 *w, u32x4 xv) {
         const bf16x8 xf = __builtin_bit_cast(bf16x8, xv);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -784,6 +783,47 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
             }
             acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), xf, acc[b], 0, 0, 0);
         }
+    };
+
+    // Whole steps, software pipelined: the next step's loads are issued
+    // before the current step's transpose and MFMAs.
+    if (s_begin < s_full_end) {
+        u32x2 w0[8], w1[8];
+        u32x4 x0 = load_x(s_begin), x1;
+        load_w(s_begin, w0);
+        int64_t s = s_begin;
+        for (; s + 2 <= s_full_end; s += 2) {
+            x1 = load_x(s + 1 < s_full_end ? s + 1 : s);
+            load_w(s + 1 < s_full_end ? s + 1 : s, w1);
+            mma(w0, x0);
+            if (s + 1 < s_full_end) {
+                if (s + 2 < s_full_end) {
+                    x0 = load_x(s + 2);
+                    load_w(s + 2, w0);
+                }
+                mma(w1, x1);
+            }
+        }
+        if (s < s_full_end) mma(w0, x0);
+    }
+    // A partial last step (K % 32), rows beyond K read as zero.
+    for (int64_t s = s_full_end > s_begin ? s_full_end : s_begin; s < s_end; ++s) {
+        const int64_t kb = s * 32 + g * 8;
+        u32x2 w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t k = kb + j;
+            uint32_t e[4] = {0u, 0u, 0u, 0u};
+            if (k < K) {
+                const uint16_t *src = wcol + k * ldb;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) e[c] = (ncol + c < N) ? (uint32_t)src[c] : 0u;
+            }
+            w[j] = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+        }
+        u32x4 xv = load_chunk8_bf16(xr, kb, K, true, 2);
+        if (!m_ok) xv = u32x4{0u, 0u, 0u, 0u};
+        mma(w, xv);
     }
 
     // acc[b][q] of lane (g, li) is the partial C[li][n0 + 16 g + 4 q + b].
@@ -795,14 +835,14 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
         for (int b = 0; b < 4; ++b) mine[q * 4 + b] = acc[b][q];
     __syncthreads();
     for (int t = tid; t < 64 * 16; t += NW * 64) {
-        float s = 0.f;
-        for (int w2 = 0; w2 < NW; ++w2) s += red[w2 * 64 * 16 + t];
+        float sum = 0.f;
+        for (int w2 = 0; w2 < NW; ++w2) sum += red[w2 * 64 * 16 + t];
         const int L = t >> 4, v = t & 15;
         const int64_t m = L & 15;
         const int64_t n = n0 + 16 * (L >> 4) + v;
         if (m < M && n < N) {
-            if (p.out_f32) ((float *)p.C + bidx * p.sC)[m * p.ldc + n] = s;
-            else ((uint16_t *)p.C + bidx * p.sC)[m * p.ldc + n] = (uint16_t)bf16_rne(s);
+            if (p.out_f32) ((float *)p.C + bidx * p.sC)[m * p.ldc + n] = sum;
+            else ((uint16_t *)p.C + bidx * p.sC)[m * p.ldc + n] = (uint16_t)bf16_rne(sum);
         }
     }
 }
@@ -893,7 +933,12 @@ hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, int 
     case CFG_F32_128x128: return launch_f32<128, 128, 2, 2>(a, variant == 1, grid, s);
     case CFG_F32_64x64: return launch_f32<64, 64, 2, 2>(a, variant == 1, grid, s);
     case CFG_DECODE_64:
-        hipLaunchKernelGGL(k_decode<16>, dim3((unsigned)grid, (unsigned)a.batch), dim3(16 * 64), 0, s, a);
+        // variant 1: every column chunk in range, 8-byte aligned W rows and
+        // 16-byte aligned X rows
+        if (variant == 1)
+            hipLaunchKernelGGL((k_decode<16, true>), dim3((unsigned)grid, (unsigned)a.batch), dim3(16 * 64), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_decode<16, false>), dim3((unsigned)grid, (unsigned)a.batch), dim3(16 * 64), 0, s, a);
         return hipGetLastError();
     case CFG_GENERIC:
         if (f32_inputs) hipLaunchKernelGGL(k_generic<float>, dim3((unsigned)grid), dim3(256), 0, s, a);

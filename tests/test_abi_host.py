@@ -108,10 +108,14 @@ def test_selector_choices_for_the_workloads(L):
     # FFN projection: 256x192 tiles give 4 x 64 = 256 workgroups, one per CU.
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 1024, 12288, 4096)
     assert st == 0 and p.name == b"bf16_256x192" and p.grid == 256 and p.even == 1
-    # decode rows go to the small-M path, whatever M <= 16 is
+    # decode rows go to the small-M path, whatever M <= 16 is: 64 columns per
+    # workgroup; its fast variant needs whole column chunks and aligned rows
     for M in (1, 4, 16):
         st, p = g5.plan_query(g5.GEMM_OP_BF16, M, 12288, 4096)
-        assert st == 0 and p.family == 4 and p.grid == 12288 // 64
+        assert st == 0 and p.family == 4 and p.name == b"decode_64" and p.grid == 12288 // 64
+        assert p.variant == 1
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 4, 12290, 4096)
+    assert st == 0 and p.name == b"decode_64" and p.variant == 0
     st, p = g5.plan_query(g5.GEMM_OP_SGEMM, 4096, 4096, 4096)
     assert st == 0 and p.family == 3 and p.even == 1
     # ragged: K=4100 bf16 rows are only 8-byte aligned -> masked variant

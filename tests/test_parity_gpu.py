@@ -162,6 +162,30 @@ def test_decode_full_size(oracle_mod, M):
     check_bf16(host_values(C), ref, 4096, f"decode M={M}")
 
 
+@pytest.mark.parametrize("cfg", ["decode_64"])
+@pytest.mark.parametrize("M,N,K,batch", [(7, 1000, 1000, 1), (1, 512, 4096, 1), (16, 1536, 520, 1),
+                                         (4, 1000, 264, 3), (3, 2048, 24, 1), (5, 130, 31, 2)])
+def test_decode_paths_ragged(oracle_mod, monkeypatch, cfg, M, N, K, batch):
+    """The small-M kernel on N that is not a whole number of column chunks,
+    K with a remainder (and K < 32), odd strides, and a batch."""
+    _say(f"{cfg} batch={batch} {M}x{N}x{K}")
+    g = np.random.default_rng([M, N, K, batch])
+    A = gi.to_bf16_bits(gi.normal(g, (batch, M, K)))
+    B = gi.to_bf16_bits(gi.normal(g, (batch, K, N), 0.125))
+    monkeypatch.setenv("GEMM_FORCE_CONFIG", cfg)
+    st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K, batch=batch)
+    assert st == 0 and plan.name.decode() == cfg
+    for od in (torch.bfloat16, torch.float32):
+        C = g5.gemm_bf16_batched(dev_bf16(A), dev_bf16(B), out_dtype=od)
+        host = host_values(C)
+        for b in range(batch):
+            ref = oracle_mod.gemm_bf16(A[b], B[b])
+            if od == torch.bfloat16:
+                check_bf16(host[b], ref, K, f"{cfg} bf16 batch {b}")
+            else:
+                check_f32(host[b], ref, K, amax_bf16(A[b]), amax_bf16(B[b]), f"{cfg} f32 batch {b}")
+
+
 def test_decode_batch_invariance():
     """Rows of the M=1 and M=4 results equal the matching rows of M=16 bit for
     bit: the K split does not depend on M ("Operator & Runtime" §5.2.4)."""
