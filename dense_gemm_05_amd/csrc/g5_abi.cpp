@@ -294,6 +294,12 @@ void fill_public_plan(const Problem &p, const Plan &pl, gemm_plan *out)
     out->variant = pl.variant;
     out->grid = pl.grid * (c.family == GEMM_FAMILY_DECODE ? p.batch : 1);
     out->lds_bytes = c.lds_bytes;
+    if (c.family == GEMM_FAMILY_BF16_MFMA && pl.variant >= 1) {
+        // LDS-ring kernels: 8 waves, 4 slots of a 32-deep K slab of A and B
+        out->threads = 512;
+        out->tile_k = 32;
+        out->lds_bytes = 4 * (c.tile_m * 32 + 32 * c.tile_n) * 2;
+    }
     out->model_bytes = pl.model_bytes;
     std::snprintf(out->name, sizeof out->name, "%s", c.name);
 }
