@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "sgemm", "batched", "ragged", "copy"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--prewarm-seconds", type=float, default=1.0,
+                    help="untimed calls before each workload's warmup, so that GPU clocks settle")
     return ap.parse_args()
 
 
@@ -87,9 +89,21 @@ def main():
     def to_dev_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
-    def timed(fn_list, steps, warmup):
-        """fn_list: one closure per buffer set.  Returns ms per call."""
+    def timed(fn_list, steps, warmup, prewarm=None):
+        """fn_list: one closure per buffer set.  Returns ms per call.
+
+        Before the W warmup calls, the workload runs untimed for about
+        `prewarm` seconds: the GPU's clocks take a fraction of a second of
+        sustained load to settle, and the first hundreds of microseconds of
+        calls otherwise run measurably slower than the steady state."""
         R = len(fn_list)
+        t_end = time.time() + (args.prewarm_seconds if prewarm is None else prewarm)
+        i = 0
+        while time.time() < t_end:
+            for _ in range(20):
+                fn_list[i % R]()
+                i += 1
+            torch.cuda.synchronize()
         for i in range(warmup):
             fn_list[i % R]()
         torch.cuda.synchronize()

@@ -12,8 +12,13 @@ SOURCES = ["g5_kernels.hip", "g5_abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: keep the compiler from emitting packed FP32 VALU
 # instructions (v_pk_*_f32); the hot loops here are matrix-core bound anyway.
+# -amdgpu-mfma-vgpr-form=1: select the MFMA forms whose accumulators live in
+# the unified VGPR file.  With the default heuristic the one-wave-per-SIMD
+# kernels (192 accumulator registers per lane) got their accumulators split
+# between AGPRs and VGPRs, with hundreds of copies per K slab and spills.
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-Wall", "-Wno-unused-function"]
 
 

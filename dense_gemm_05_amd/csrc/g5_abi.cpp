@@ -211,8 +211,8 @@ int pick_variant(const Problem &p, const Plan &pl, bool *even)
     // descriptor extent (no partially out-of-range copies).
     if (!fits || pl.align_b < 16 || pl.align_a < 4 || p.N % 8 != 0) return 0;
     const int ring_k = 32;
-    *even = !(p.M % c.tile_m || p.N % c.tile_n || p.K % ring_k) && pl.align_a >= 16 &&
-            pl.align_c >= (elem_c(p) == 4 ? 16 : 8);
+    const bool c_ok = pl.align_c >= (elem_c(p) == 4 ? 16 : 8);
+    *even = !(p.M % c.tile_m || p.N % c.tile_n || p.K % ring_k) && pl.align_a >= 16 && c_ok;
     if (*even) return 1;
     return pl.align_a >= 16 ? 2 : 3;
 }
@@ -294,7 +294,7 @@ void fill_public_plan(const Problem &p, const Plan &pl, gemm_plan *out)
     out->variant = pl.variant;
     out->grid = pl.grid * (c.family == GEMM_FAMILY_DECODE ? p.batch : 1);
     out->lds_bytes = c.lds_bytes;
-    if (c.family == GEMM_FAMILY_BF16_MFMA && pl.variant >= 1) {
+    if (c.family == GEMM_FAMILY_BF16_MFMA && pl.variant >= 1 && pl.variant <= 3) {
         // LDS-ring kernels: 8 waves, 4 slots of a 32-deep K slab of A and B
         out->threads = 512;
         out->tile_k = 32;

@@ -899,14 +899,16 @@ __global__ void __launch_bounds__(256) k_zero(GemmArgs p)
 
 // variant: 0 general (k_bf16_mfma), 1 ring kernel aligned, 2 ring kernel
 // masked with 16-byte A rows, 3 ring kernel masked with 4-byte A copies.
-template <int BM, int BN, int WGM, int WGN, int DWGM, int DWGN>
+// NS: slots of the LDS ring (ring kernels); as many as fit in LDS, so that
+// NS-2 slabs of copies are in flight while one is consumed.
+template <int BM, int BN, int WGM, int WGN, int DWGM, int DWGN, int NS>
 static hipError_t launch_bf16(const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
 {
     const dim3 g((unsigned)grid), b8(DWGM * DWGN * 64);
     switch (variant) {
-    case 1: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, 4, 16, false>), g, b8, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, 4, 16, true>), g, b8, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, 4, 4, true>), g, b8, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NS, 16, false>), g, b8, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NS, 16, true>), g, b8, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NS, 4, true>), g, b8, 0, s, a); break;
     default: hipLaunchKernelGGL((k_bf16_mfma<BM, BN, WGM, WGN, false>), g, dim3(WGM * WGN * 64), 0, s, a); break;
     }
     return hipGetLastError();
@@ -927,9 +929,9 @@ hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, int 
     case CFG_ZERO:
         hipLaunchKernelGGL(k_zero, dim3((unsigned)grid), dim3(256), 0, s, a);
         return hipGetLastError();
-    case CFG_BF16_256x192: return launch_bf16<256, 192, 2, 2, 4, 2>(a, variant, grid, s);
-    case CFG_BF16_128x128: return launch_bf16<128, 128, 2, 2, 4, 2>(a, variant, grid, s);
-    case CFG_BF16_256x128: return launch_bf16<256, 128, 2, 2, 4, 2>(a, variant, grid, s);
+    case CFG_BF16_256x192: return launch_bf16<256, 192, 2, 2, 4, 2, 4>(a, variant, grid, s);
+    case CFG_BF16_128x128: return launch_bf16<128, 128, 2, 2, 4, 2, 4>(a, variant, grid, s);
+    case CFG_BF16_256x128: return launch_bf16<256, 128, 2, 2, 4, 2, 4>(a, variant, grid, s);
     case CFG_F32_128x128: return launch_f32<128, 128, 2, 2>(a, variant == 1, grid, s);
     case CFG_F32_64x64: return launch_f32<64, 64, 2, 2>(a, variant == 1, grid, s);
     case CFG_DECODE_64:

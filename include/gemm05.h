@@ -117,7 +117,9 @@ typedef struct {
     int even;          /* 1 when no edge masking is compiled in */
     int variant;       /* tiled kernels: 0 fully general (register-staged copies),
                           1 aligned LDS-ring kernel, 2/3 masked LDS-ring kernel
-                          copying A in 16-/4-byte pieces; other families: 0 */
+                          copying A in 16-/4-byte pieces; the small-M
+                          family: 1 for whole aligned column chunks, else 0;
+                          other families: 0 */
     int64_t grid;      /* workgroups launched */
     int64_t lds_bytes; /* LDS per workgroup */
     double model_bytes;/* traffic model of "Operator & Runtime" §5.2.2 for the chosen tile */

@@ -323,19 +323,24 @@ def test_nan_sentinel_every_element_written_once():
 # NaN: a kernel that read A beyond K, or let columns of B beyond N reach a
 # stored output, or wrote outside the logical C, fails.
 VARIANT_CASES = [
-    # M, N, K, A row pad, B row pad, expected variant
-    (512, 384, 128, 0, 0, 1),      # aligned ring kernel
-    (300, 392, 264, 0, 0, 2),      # masked ring kernel, K tail of 8
-    (300, 392, 262, 0, 0, 3),      # 4-byte A copies (rows 4-byte aligned)
-    (300, 392, 20, 4, 0, 2),       # K < 32: only the element-loaded tail stage
-    (257, 200, 96, 8, 8, 2),       # edge tiles in M and N, padded rows
-    (70, 392, 1000, 2, 0, 3),      # long K with a tail, few rows
+    # M, N, K, A row pad, B row pad, forced config (None: selector), expected variant
+    (512, 384, 128, 0, 0, None, 1),              # aligned ring kernel
+    (512, 384, 128, 0, 0, "bf16_256x192", 1),    # the same with 192-column tiles
+    (300, 392, 264, 0, 0, None, 2),              # masked ring kernel, K tail of 8
+    (300, 392, 264, 0, 0, "bf16_256x192", 2),
+    (300, 392, 262, 0, 0, None, 3),              # 4-byte A copies (rows 4-byte aligned)
+    (300, 392, 20, 4, 0, None, 2),               # K < 32: only the element-loaded tail stage
+    (257, 200, 96, 8, 8, None, 2),               # edge tiles in M and N, padded rows
+    (300, 392, 48, 0, 0, "bf16_128x128", 2),     # one whole and one partial slab
+    (70, 392, 1000, 2, 0, None, 3),              # long K with a tail, few rows
 ]
 
 
-@pytest.mark.parametrize("M,N,K,pa,pb,variant", VARIANT_CASES)
-def test_bf16_kernel_variants(oracle_mod, M, N, K, pa, pb, variant):
-    _say(f"variant {variant} {M}x{N}x{K} pads ({pa},{pb})")
+@pytest.mark.parametrize("M,N,K,pa,pb,cfg,variant", VARIANT_CASES)
+def test_bf16_kernel_variants(oracle_mod, monkeypatch, M, N, K, pa, pb, cfg, variant):
+    _say(f"variant {variant} {M}x{N}x{K} pads ({pa},{pb}) config {cfg}")
+    if cfg:
+        monkeypatch.setenv("GEMM_FORCE_CONFIG", cfg)
     g = np.random.default_rng([M, N, K, pa, pb])
     A = gi.to_bf16_bits(gi.normal(g, (M, K + pa)))
     B = gi.to_bf16_bits(gi.normal(g, (K, N + pb), 0.125))
