@@ -346,6 +346,58 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 1) k_bf16_mfma(GemmArgs p)
         }
 }
 
+// Epilogue of whole tiles: the BM x BN results, held as acc[fn][fm] with
+// lane (g, li) of wave (wm, wn) owning row wm*TM + 16 fm + li, columns
+// wn*TN + 16 fn + 4 g .. +3, are written to LDS in row-major order (rows
+// padded by 16 bytes against bank conflicts), then copied to C in 16-byte
+// chunks with consecutive lanes on consecutive chunks of a row.  Tiles that
+// do not fit in LDS at once go in passes of whole wave rows.  `lds` holds
+// LDS_BYTES; every wave must have finished with it.
+template <int BM, int BN, int WGM, int WGN, int LDS_BYTES, typename TOut, int NFN, int NFM>
+__device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM], uint16_t *lds, void *Cb,
+                                                   int64_t ldc, int64_t m0, int64_t n0)
+{
+    constexpr int TM = BM / WGM, TN = BN / WGN;
+    constexpr int ESZ = (int)sizeof(TOut);
+    constexpr int PITCH = BN * ESZ + 16;                     // bytes per staged row
+    constexpr int CPR = BN * ESZ / 16;                       // 16-byte chunks per row
+    constexpr int NT = WGM * WGN * 64;
+    constexpr int FITS = LDS_BYTES / PITCH;                  // rows that fit
+    constexpr int RP = FITS >= BM ? BM : (FITS >= BM / 2 ? BM / 2 : BM / 4);
+    static_assert(RP % TM == 0 && RP * PITCH <= LDS_BYTES, "staging passes");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int g = lane >> 4, li = lane & 15;
+    char *L = (char *)lds;
+#pragma unroll
+    for (int pass = 0; pass < BM / RP; ++pass) {
+        if (wm * TM / RP == pass) {
+#pragma unroll
+            for (int fn = 0; fn < NFN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < NFM; ++fm) {
+                    const int r = wm * TM + fm * 16 + li - pass * RP;
+                    const int c = wn * TN + fn * 16 + g * 4;
+                    const f32x4 v = acc[fn][fm];
+                    if (ESZ == 4) {
+                        *(f32x4 *)(L + r * PITCH + c * 4) = v;
+                    } else {
+                        u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                        *(u32x2 *)(L + r * PITCH + c * 2) = w;
+                    }
+                }
+        }
+        __syncthreads();
+        for (int q = tid; q < RP * CPR; q += NT) {
+            const int r = q / CPR, c = q % CPR;
+            const u32x4 v = *(const u32x4 *)(L + r * PITCH + c * 16);
+            char *dst = (char *)Cb + ((m0 + pass * RP + r) * ldc + n0) * ESZ + c * 16;
+            *(u32x4 *)dst = v;
+        }
+        __syncthreads();
+    }
+}
+
 // ================================================= bf16 MFMA ring kernel
 //
 // Tile BM x BN, 8 waves (two per SIMD, so one wave's MFMAs run while the
@@ -564,6 +616,17 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     __builtin_amdgcn_s_waitcnt(0);
 
     void *Cb = (char *)p.C + tc.b * p.sC * (p.out_f32 ? 4 : 2);
+    if (!MASKED && p.align_c >= 16) {
+        // Whole tile, 16-byte aligned rows of C: stage the results through
+        // LDS (free once every wave's copies and reads are done) and write
+        // whole 16-byte chunks, consecutive lanes on consecutive chunks of a
+        // row, so that every 128-byte line of C is written by one store.
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (p.out_f32) store_tile_via_lds<BM, BN, WGM, WGN, NS * SLOT * 2, float>(acc, smem, Cb, p.ldc, m0, n0);
+        else store_tile_via_lds<BM, BN, WGM, WGN, NS * SLOT * 2, uint16_t>(acc, smem, Cb, p.ldc, m0, n0);
+        return;
+    }
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
