@@ -56,7 +56,8 @@ def kernel_label(plan):
     tm, tn = plan.tile_m, plan.tile_n
     if plan.family == 2 and plan.variant in (1, 2, 3):
         av, masked = {1: (16, "false"), 2: (16, "true"), 3: (4, "true")}[plan.variant]
-        return f"k_bf16_ms<{tm},{tn},4,2,4,{av},{masked}> ({name}, grid {plan.grid}, {plan.threads} threads)"
+        wg = "2,4" if (tm, tn) == (256, 192) else "4,2"
+        return f"k_bf16_ms<{tm},{tn},{wg},4,{av},{masked}> ({name}, grid {plan.grid}, {plan.threads} threads)"
     return f"{name} variant {plan.variant} (grid {plan.grid}, {plan.threads} threads)"
 
 

@@ -73,7 +73,7 @@ struct GemmArgs {
 enum ConfigId {
     CFG_NONE = 0,
     CFG_ZERO,
-    CFG_BF16_256x192,      // masked: 4 waves (2x2); aligned: 8 waves (4x2)
+    CFG_BF16_256x192,      // general kernel: 4 waves (2x2); ring kernels: 8 waves (2x4, wave tile 128x48)
     CFG_BF16_128x128,      // 4 waves (2x2), wave tile 64x64
     CFG_BF16_256x128,      // 4 waves (2x2), wave tile 128x64
     CFG_F32_128x128,       // 4 waves (2x2), wave tile 64x64

@@ -403,11 +403,13 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
 // Tile BM x BN, 8 waves (two per SIMD, so one wave's MFMAs run while the
 // other waits), wave tile (BM/WGM) x (BN/WGN).
 //
-// K is walked in stages of 32 through a ring of NS LDS slots, so the copies
-// of stage k+NS-1 are in flight while stage k is multiplied: the slab copies
-// from L2 (and, on first touch, HBM) get NS-1 stages of compute to land
-// ("4.1 Tối ưu hiệu năng toán tử GEMM trên CUDA" §9-§10 and "Operator &
-// Runtime" §5.3.2 double buffering, deepened for gfx950's latency).
+// K is walked in stages of 32 through rings of LDS slots, NSA for A and NSB
+// for B, so the copies of A stage k+NSA-1 and B stage k+NSB-1 are in flight
+// while stage k is multiplied: the slab copies from L2 (and, on first touch,
+// HBM) get several stages of compute to land ("4.1 Tối ưu hiệu năng toán tử
+// GEMM trên CUDA" §9-§10 and "Operator & Runtime" §5.3.2 double buffering,
+// deepened for gfx950's latency).  The two depths are independent because
+// A and B are copied by different waves, each with its own vmcnt.
 //  * Copies are buffer loads that write LDS directly (buffer_load ... lds):
 //    one wave instruction moves 64 lanes x AV bytes of A (AV = 16, or 4 for
 //    rows that are only 4- or 8-byte aligned) or 64 x 16 bytes of B into LDS, lane
@@ -418,7 +420,9 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
 //    ((row >> 1) & 3), measured conflict-free for the fragment reads; B slot
 //    rows are BN bf16, swizzled with swz_b, read with ds_read_b64_tr_b16.
 //  * Each wave waits for its own copies of the next stage (vmcnt counts
-//    the copies still allowed in flight), then one barrier per stage.  After
+//    the copies still allowed in flight), then one barrier per stage.  The
+//    loop is bounded by LDS traffic (copy writes plus fragment reads) and by
+//    the copy path, not by copy latency: deeper rings measured no faster.  After
 //    the barrier the next stage's fragments are read into the second
 //    register set while the last TAIL MFMAs of the current stage run.
 //  * MASKED: the buffer descriptors carry each operand's byte extent, so
@@ -427,7 +431,7 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
 //    only feed outputs that are never stored.  A K remainder (K % 32) is a
 //    final stage loaded element by element with zero fill ("4.1" §4.5 and
 //    "Operator & Runtime" §5.4.2: out-of-range elements contribute zero).
-template <int BM, int BN, int WGM, int WGN, int NS, int AV, bool MASKED>
+template <int BM, int BN, int WGM, int WGN, int NSA, int NSB, int AV, bool MASKED>
 __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
 {
     constexpr int NWAVE = WGM * WGN;
@@ -437,7 +441,8 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     constexpr int NMFMA = FM * FN;
     constexpr int TAIL = NMFMA / 2;                           // MFMAs run after the barrier
     constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN;
-    constexpr int SLOT = A_ELEMS + B_ELEMS;                   // elements per ring slot
+    constexpr int B_BASE = NSA * A_ELEMS;                     // B ring after the A ring (elements)
+    constexpr int LDS_BYTES = (NSA * A_ELEMS + NSB * B_ELEMS) * 2;
     constexpr int A_INS = A_ELEMS * 2 / (64 * AV), B_INS = B_ELEMS * 2 / 1024;   // copy instructions
     constexpr int A_W = NWAVE / 2, B_W = NWAVE / 2;           // copying waves per operand
     constexpr int LA = A_INS / A_W, LB = B_INS / B_W;         // copies per wave per stage
@@ -446,9 +451,9 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     static_assert(AV == 16 || AV == 4, "A copy width");
     static_assert(A_INS % A_W == 0 && B_INS % B_W == 0, "slab split");
     static_assert((BN / 8) % 8 == 0, "B slot rows must be whole swizzle groups");
-    static_assert(NS >= 3 && LA * (NS - 2) < 64 && LB * (NS - 2) < 64, "vmcnt accounting");
+    static_assert(NSA >= 3 && NSB >= 3 && LA * (NSA - 2) < 64 && LB * (NSB - 2) < 64, "vmcnt accounting");
     static_assert(TAIL > 0 && TAIL < NMFMA, "tail");
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[NS * SLOT];
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[LDS_BYTES / 2];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -491,18 +496,21 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     }
     // The stage's offset moves the descriptor base (scalar arithmetic) and
     // shrinks its extent to match, so the scalar offset stays 0.
-    auto issue = [&](int kt, int slot) {
-        uint16_t *sl = smem + slot * SLOT;
+    // Each copying wave issues only its operand: A waves copy stage kt into
+    // the A slot of stage ks (ks % NSA), B waves into B slot ks % NSB.
+    auto issue = [&](int kt, int ks) {
         if (a_wave) {
+            uint16_t *sl = smem + (ks % NSA) * A_ELEMS;
             const uint32_t adv = (uint32_t)(kt * BK * 2);
             const i32x4_t r = make_rsrc(Abat + (int64_t)kt * BK, a_bytes - adv);
 #pragma unroll
             for (int j = 0; j < LA; ++j) dma<AV>(r, a_voff[j], 0, sl + (a_i0 + j) * (32 * AV));
         } else {
+            uint16_t *sl = smem + B_BASE + (ks % NSB) * B_ELEMS;
             const uint32_t adv = (uint32_t)((int64_t)kt * BK * ldb * 2);
             const i32x4_t r = make_rsrc(Bbat + (int64_t)kt * BK * ldb, b_bytes - adv);
 #pragma unroll
-            for (int j = 0; j < LB; ++j) dma<16>(r, b_voff[j], 0, sl + A_ELEMS + (b_i0 + j) * 512);
+            for (int j = 0; j < LB; ++j) dma<16>(r, b_voff[j], 0, sl + (b_i0 + j) * 512);
         }
     };
 
@@ -518,21 +526,23 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         const int k = g * 8 + (li >> 2);
         const int ncol = wn * TN + fn * 16 + (li & 3) * 4;
         const int c = ncol >> 3, half = (ncol >> 2) & 1;
-        b_rd[fn] = A_ELEMS + k * BN + ((c ^ swz_b(k)) * 8) + half * 4;
-        b_rd4[fn] = A_ELEMS + (k + 4) * BN + ((c ^ swz_b(k + 4)) * 8) + half * 4;
+        b_rd[fn] = k * BN + ((c ^ swz_b(k)) * 8) + half * 4;
+        b_rd4[fn] = (k + 4) * BN + ((c ^ swz_b(k + 4)) * 8) + half * 4;
     }
     struct Frags {
         bf16x8 a[FM];
         bf16x8 b[FN];
     };
-    auto read_frags = [&](Frags &f, int slot) {
-        const uint16_t *sl = smem + slot * SLOT;
+    // Fragments of stage kt (A slot kt % NSA, B slot kt % NSB).
+    auto read_frags = [&](Frags &f, int kt) {
+        const uint16_t *sa = smem + (kt % NSA) * A_ELEMS;
+        const uint16_t *sb = smem + B_BASE + (kt % NSB) * B_ELEMS;
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) f.a[fm] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(sl + a_rd[fm]));
+        for (int fm = 0; fm < FM; ++fm) f.a[fm] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(sa + a_rd[fm]));
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G5_LDS(i16x4, sl + b_rd[fn]));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G5_LDS(i16x4, sl + b_rd4[fn]));
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G5_LDS(i16x4, sb + b_rd[fn]));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G5_LDS(i16x4, sb + b_rd4[fn]));
             f.b[fn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
     };
@@ -552,34 +562,39 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     };
 
     // Wait until this wave's copies of the next stage have landed -- at most
-    // (NS-2) stages of its copies may still be in flight -- and its LDS reads
-    // are done, then the workgroup barrier.
+    // NSA-2 (A waves) or NSB-2 (B waves) stages of its copies may still be in
+    // flight -- and its LDS reads are done, then the workgroup barrier.
     auto stage_barrier = [&]() {
-        if (a_wave) __builtin_amdgcn_s_waitcnt(waitcnt_imm(LA * (NS - 2), 0));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_imm(LB * (NS - 2), 0));
+        if (a_wave) __builtin_amdgcn_s_waitcnt(waitcnt_imm(LA * (NSA - 2), 0));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_imm(LB * (NSB - 2), 0));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");   // no LDS access moves across the barrier
     };
 
     const int KT = (int)(K / BK);                             // whole stages
+    // A stage past the last reloads the last one, into the slot of the stage
+    // it stands for, which is never read again.
+    auto issue_clamped = [&](int ks) { issue(ks < KT ? ks : KT - 1, ks); };
     Frags f0, f1;
     if (KT > 0) {
-#pragma unroll
-        for (int s2 = 0; s2 < NS - 1; ++s2) issue(s2 < KT ? s2 : KT - 1, s2);
+        // Prologue: A stages 0..NSA-2 and B stages 0..NSB-2 (clamped, see
+        // below), stage 0 complete.
+        const int NPRO = a_wave ? NSA - 1 : NSB - 1;
+        for (int s2 = 0; s2 < NPRO; ++s2) issue_clamped(s2);
         stage_barrier();
         read_frags(f0, 0);
 
-        // One stage: copies for stage kt+NS-1 (clamped: the last NS-1 stages
-        // reload the final stage into slots nobody reads again, which keeps
-        // the in-flight counts uniform), MFMAs, barrier, next fragments, tail.
+        // One stage: copies for stage kt+NSA-1 (A waves) or kt+NSB-1 (B
+        // waves), MFMAs, barrier, next fragments, tail.  Stages past the last
+        // one reload the final stage into a slot nobody reads again, which
+        // keeps the in-flight counts uniform.
         auto step = [&](int kt, Frags &fc, Frags &fnx) {
-            const int ks = kt + NS - 1;
-            issue(ks < KT ? ks : KT - 1, ks % NS);
+            issue_clamped(kt + (a_wave ? NSA : NSB) - 1);
             __builtin_amdgcn_sched_barrier(0);
             mfma_range(fc, 0, NMFMA - TAIL);
             __builtin_amdgcn_sched_barrier(0);
             stage_barrier();
-            read_frags(fnx, (kt + 1) % NS);
+            read_frags(fnx, kt + 1);
             __builtin_amdgcn_sched_barrier(0);
             mfma_range(fc, NMFMA - TAIL, TAIL);
             __builtin_amdgcn_sched_barrier(0);
@@ -598,7 +613,7 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         const int64_t k0 = (int64_t)KT * BK;
-        uint16_t *sA = smem, *sB = smem + A_ELEMS;
+        uint16_t *sA = smem, *sB = smem + B_BASE;
         for (int q = tid; q < BM * 4; q += NWAVE * 64) {
             const int row = q >> 2, c = q & 3;
             const u32x4 v = load_chunk8_bf16(Abat + (m0 + row) * lda, k0 + 8 * c, K, m0 + row < M, p.align_a);
@@ -623,8 +638,8 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         // row, so that every 128-byte line of C is written by one store.
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (p.out_f32) store_tile_via_lds<BM, BN, WGM, WGN, NS * SLOT * 2, float>(acc, smem, Cb, p.ldc, m0, n0);
-        else store_tile_via_lds<BM, BN, WGM, WGN, NS * SLOT * 2, uint16_t>(acc, smem, Cb, p.ldc, m0, n0);
+        if (p.out_f32) store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, float>(acc, smem, Cb, p.ldc, m0, n0);
+        else store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, uint16_t>(acc, smem, Cb, p.ldc, m0, n0);
         return;
     }
 #pragma unroll
@@ -962,16 +977,16 @@ __global__ void __launch_bounds__(256) k_zero(GemmArgs p)
 
 // variant: 0 general (k_bf16_mfma), 1 ring kernel aligned, 2 ring kernel
 // masked with 16-byte A rows, 3 ring kernel masked with 4-byte A copies.
-// NS: slots of the LDS ring (ring kernels); as many as fit in LDS, so that
-// NS-2 slabs of copies are in flight while one is consumed.
-template <int BM, int BN, int WGM, int WGN, int DWGM, int DWGN, int NS>
+// NSA, NSB: slots of the A and B rings of the ring kernels (NSA-2 and NSB-2
+// slabs of copies in flight while one is consumed).
+template <int BM, int BN, int WGM, int WGN, int DWGM, int DWGN, int NSA, int NSB>
 static hipError_t launch_bf16(const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
 {
     const dim3 g((unsigned)grid), b8(DWGM * DWGN * 64);
     switch (variant) {
-    case 1: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NS, 16, false>), g, b8, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NS, 16, true>), g, b8, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NS, 4, true>), g, b8, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NSA, NSB, 16, false>), g, b8, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NSA, NSB, 16, true>), g, b8, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NSA, NSB, 4, true>), g, b8, 0, s, a); break;
     default: hipLaunchKernelGGL((k_bf16_mfma<BM, BN, WGM, WGN, false>), g, dim3(WGM * WGN * 64), 0, s, a); break;
     }
     return hipGetLastError();
@@ -992,9 +1007,9 @@ hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, int 
     case CFG_ZERO:
         hipLaunchKernelGGL(k_zero, dim3((unsigned)grid), dim3(256), 0, s, a);
         return hipGetLastError();
-    case CFG_BF16_256x192: return launch_bf16<256, 192, 2, 2, 4, 2, 4>(a, variant, grid, s);
-    case CFG_BF16_128x128: return launch_bf16<128, 128, 2, 2, 4, 2, 4>(a, variant, grid, s);
-    case CFG_BF16_256x128: return launch_bf16<256, 128, 2, 2, 4, 2, 4>(a, variant, grid, s);
+    case CFG_BF16_256x192: return launch_bf16<256, 192, 2, 2, 2, 4, 4, 4>(a, variant, grid, s);
+    case CFG_BF16_128x128: return launch_bf16<128, 128, 2, 2, 4, 2, 4, 4>(a, variant, grid, s);
+    case CFG_BF16_256x128: return launch_bf16<256, 128, 2, 2, 4, 2, 4, 4>(a, variant, grid, s);
     case CFG_F32_128x128: return launch_f32<128, 128, 2, 2>(a, variant == 1, grid, s);
     case CFG_F32_64x64: return launch_f32<64, 64, 2, 2>(a, variant == 1, grid, s);
     case CFG_DECODE_64:
