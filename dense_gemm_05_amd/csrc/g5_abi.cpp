@@ -10,7 +10,9 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
+#include <utility>
 
 #include "../../include/gemm05.h"
 #include "g5_common.h"
@@ -29,6 +31,7 @@ const ConfigInfo kConfigs[CFG_COUNT] = {
     {CFG_F32_128x128, GEMM_FAMILY_F32_MFMA, 128, 128, 32, 256, 2 * (128 * 32 + 32 * 132) * 4, "f32_128x128"},
     {CFG_F32_64x64, GEMM_FAMILY_F32_MFMA, 64, 64, 32, 256, 2 * (64 * 32 + 32 * 68) * 4, "f32_64x64"},
     {CFG_DECODE_64, GEMM_FAMILY_DECODE, 16, 64, 32, 1024, 16 * 64 * 16 * 4, "decode_64"},
+    {CFG_DECODE_SPLIT, GEMM_FAMILY_DECODE, 16, 128, 32, 1024, 16 * 64 * 32 * 4 + 4, "decode_splitk"},
     {CFG_GENERIC, GEMM_FAMILY_GENERIC, 16, 16, 16, 256, 2 * 16 * 17 * 4, "generic"},
 };
 
@@ -54,8 +57,20 @@ struct Plan {
     int64_t grid = 0;
     int64_t tiles_m = 0, tiles_n = 0, group_m = 1;
     int align_a = 2, align_b = 2, align_c = 2;
+    int ks = 1;              // K slices of the split small-M path
     double model_bytes = 0.0;
 };
+
+// K slices per strip of the split small-M path: enough workgroups for the
+// 256 CUs (at most 8 slices, each at least 16 steps of 32 rows).
+int decode_slices(int64_t strips, int64_t K)
+{
+    int64_t ks = 256 / (strips > 0 ? strips : 1);
+    const int64_t by_k = K / (32 * 16);
+    if (ks > by_k) ks = by_k;
+    if (ks > 8) ks = 8;
+    return ks < 1 ? 1 : (int)ks;
+}
 
 int elem_a(const Problem &p) { return p.op == GEMM_OP_SGEMM ? 4 : 2; }
 int elem_c(const Problem &p) { return (p.op == GEMM_OP_SGEMM || p.c_type == GEMM_OUT_F32) ? 4 : 2; }
@@ -170,6 +185,10 @@ void fill_grid(const Problem &p, Plan &pl)
         pl.tiles_m = 1;
         pl.tiles_n = cdiv(p.N, c.tile_n);
         pl.grid = pl.tiles_n;  // x; batch goes to grid y
+        if (pl.config == CFG_DECODE_SPLIT) {
+            pl.ks = decode_slices(pl.tiles_n * p.batch, p.K);
+            pl.grid = pl.tiles_n * pl.ks;
+        }
         break;
     default:
         pl.tiles_m = cdiv(p.M, c.tile_m);
@@ -201,6 +220,8 @@ int pick_variant(const Problem &p, const Plan &pl, bool *even)
     }
     if (c.family == GEMM_FAMILY_DECODE) {
         *even = (p.N % c.tile_n == 0) && pl.align_b >= 8 && pl.align_a >= 16;
+        if (pl.config == CFG_DECODE_SPLIT)     // 16-byte loads of whole steps only
+            return (*even && pl.align_b >= 16 && p.K % 32 == 0) ? 1 : -1;
         return *even ? 1 : 0;
     }
     if (c.family != GEMM_FAMILY_BF16_MFMA) return 0;
@@ -243,7 +264,12 @@ int select_plan(const Problem &p, Plan &pl)
             return GEMM_ERR_UNSUPPORTED;
         pl.config = id;
     } else if (p.op == GEMM_OP_BF16 && p.M <= 16 && p.batch <= 65535) {
-        pl.config = CFG_DECODE_64;
+        // The split path when its preconditions hold and it would use more
+        // than one slice; else whole-K strips of 64 columns.
+        pl.config = CFG_DECODE_SPLIT;
+        bool ev = false;
+        if (pick_variant(p, pl, &ev) < 0 || decode_slices(cdiv(p.N, 128) * p.batch, p.K) < 2)
+            pl.config = CFG_DECODE_64;
     } else {
         // Candidates with their measured relative efficiency; the model
         // picks the fastest (page "Operator & Runtime" §5.4.5: feasibility,
@@ -274,6 +300,7 @@ int select_plan(const Problem &p, Plan &pl)
     fill_grid(p, pl);
     if (pl.grid <= 0 || pl.grid > (int64_t)1 << 24) return GEMM_ERR_UNSUPPORTED;
     pl.variant = pick_variant(p, pl, &pl.even);
+    if (pl.variant < 0) return GEMM_ERR_UNSUPPORTED;   // forced split path without its preconditions
     return GEMM_OK;
 }
 
@@ -332,6 +359,57 @@ bool log_enabled()
     return v == 1;
 }
 
+// ------------------------------------------------------------ workspace
+// The split small-M path keeps per-strip counters and partial sums in two
+// buffers owned by the library: one pair per (device, stream), allocated on
+// first use and grown when a call needs more, never freed before exit.  The
+// counter buffer is zeroed when it is allocated and every kernel leaves the
+// counters it used at zero; the partial sums need no initial value.
+struct Buffer {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+struct Workspace {
+    Buffer cnt, part;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, void *>, Workspace> g_ws;
+
+// Make `b` at least `need` bytes (zeroed when `zero`); false on failure.
+bool grow(Buffer &b, size_t need, bool zero, void *stream)
+{
+    if (b.bytes >= need) return true;
+    if (b.ptr) {
+        if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return false;
+        (void)hipFree(b.ptr);
+        b.ptr = nullptr;
+        b.bytes = 0;
+    }
+    const size_t bytes = (need + (2u << 20) - 1) & ~(size_t)((2u << 20) - 1);
+    void *ptr = nullptr;
+    if (hipMalloc(&ptr, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    if (zero && hipMemsetAsync(ptr, 0, bytes, (hipStream_t)stream) != hipSuccess) {
+        (void)hipFree(ptr);
+        return false;
+    }
+    b.ptr = ptr;
+    b.bytes = bytes;
+    return true;
+}
+
+bool get_workspace(int dev, void *stream, size_t cnt_bytes, size_t part_bytes, unsigned **cnt, float **part)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace &w = g_ws[std::make_pair(dev, stream)];
+    if (!grow(w.cnt, cnt_bytes, true, stream) || !grow(w.part, part_bytes, false, stream)) return false;
+    *cnt = (unsigned *)w.cnt.ptr;
+    *part = (float *)w.part.ptr;
+    return true;
+}
+
 int run(const Problem &p, void *stream)
 {
     int st = validate(p);
@@ -368,6 +446,23 @@ int run(const Problem &p, void *stream)
     a.align_b = pl.align_b;
     a.align_c = pl.align_c;
     a.out_f32 = elem_c(p) == 4 ? 1 : 0;
+    if (pl.config == CFG_DECODE_SPLIT) {
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        const size_t cnt_bytes = (size_t)p.batch * pl.tiles_n * sizeof(unsigned);
+        const size_t part_bytes = (size_t)p.batch * pl.tiles_n * pl.ks * 16 * 128 * sizeof(float);
+        unsigned *cnt = nullptr;
+        float *part = nullptr;
+        if (get_workspace(dev, stream, cnt_bytes, part_bytes, &cnt, &part)) {
+            const hipError_t e = launch_decode_split(a, part, cnt, pl.ks, (hipStream_t)stream);
+            return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+        }
+        // No workspace: whole-K strips of 64 columns.
+        pl.config = CFG_DECODE_64;
+        fill_grid(p, pl);
+        pl.variant = pick_variant(p, pl, &pl.even);
+        a.tiles_n = pl.tiles_n;
+    }
     const hipError_t e = launch_config(pl.config, p.op == GEMM_OP_SGEMM, a, pl.variant, pl.grid, (hipStream_t)stream);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }

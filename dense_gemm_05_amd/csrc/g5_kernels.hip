@@ -928,6 +928,165 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
     }
 }
 
+// ============================================= small-M path, K split over workgroups
+//
+// Streaming W from HBM is capped per CU, and at the same workgroup count it
+// runs faster with 256-byte row pieces than with 128-byte ones (measured:
+// 192 workgroups, 128-byte strips 4.4 TB/s, 256-byte strips with K halved
+// 5.1 TB/s).  This kernel gives a workgroup 128 columns (256 bytes of each W
+// row) and one of KS contiguous slices of the K steps, so N = 12288 becomes
+// 96 strips x 2 slices.  Within the workgroup the NW waves split the slice
+// and add their partial sums through LDS in wave order, as in k_decode.
+//  * Lane (g, r) loads 16 bytes (8 columns) of 8 rows per 32-row step, each
+//    load instruction covering 4 rows x 256 contiguous bytes; an 8x8
+//    transpose of 16-bit halves in registers feeds 8 matrix-core blocks
+//    whose logical column r is physical column 8r + c.
+//  * Slices are combined without atomics on data: every workgroup writes
+//    its partial sums to the workspace with device-scope stores, waits until
+//    they have completed, and then one thread adds 1 to the strip's counter
+//    (device-scope atomic).  The workgroup that brings the counter to KS
+//    reads the KS partials with device-scope loads and adds them in slice
+//    order -- the same order whichever workgroup arrives last, so the result
+//    is deterministic and, the partition being independent of M, the same
+//    for every row count -- then writes C and resets the counter for the
+//    next call.  Device-scope loads and stores are coherent across the
+//    XCDs' L2s on their own, so no L2 write-back or invalidation (a full
+//    fence) is needed; with fences the path measured twice as slow.
+//  * W is read once: its loads are non-temporal.
+// Requires N % 128 == 0, K % 32 == 0, 16-byte aligned rows of X and W.
+// DB: double-buffer the W rows of two steps in registers.
+template <int NW, bool DB>
+__global__ void __launch_bounds__(NW * 64, 1) k_decode_sk(GemmArgs p, float *ws, unsigned *cnt, int KS)
+{
+    constexpr int NC = 128;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, li = lane & 15;
+    const int64_t M = p.M, K = p.K, lda = p.lda, ldb = p.ldb;
+    const int64_t nstrip = p.tiles_n;
+    const int64_t strip = (int64_t)blockIdx.x / KS, slice = (int64_t)blockIdx.x % KS;
+    const int64_t n0 = strip * NC;
+    const int64_t bidx = blockIdx.y;
+    const uint16_t *X = (const uint16_t *)p.A + bidx * p.sA;
+    const uint16_t *W = (const uint16_t *)p.B + bidx * p.sB;
+
+    // Fixed partition of the 32-row steps: over slices, then over waves.
+    const int64_t steps = K / 32;
+    const int64_t sl0 = steps * slice / KS, sl1 = steps * (slice + 1) / KS;
+    const int64_t s_begin = sl0 + (sl1 - sl0) * wave / NW, s_end = sl0 + (sl1 - sl0) * (wave + 1) / NW;
+    const bool m_ok = li < M;
+    const uint16_t *xr = X + (int64_t)(m_ok ? li : 0) * lda;
+    const uint16_t *wcol = W + n0 + 8 * li;
+
+    f32x4 acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto load_w = [&](int64_t s, u32x4 *w) {
+        const uint16_t *src = wcol + (s * 32 + g * 8) * ldb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = __builtin_nontemporal_load((const u32x4 *)(src + j * ldb));
+    };
+    auto load_x = [&](int64_t s) -> u32x4 {
+        u32x4 v = *(const u32x4 *)(xr + s * 32 + g * 8);
+        if (!m_ok) v = u32x4{0u, 0u, 0u, 0u};
+        return v;
+    };
+    // 8x8 transpose of 16-bit halves: block c takes column c of the 8 rows.
+    auto mma = [&](const u32x4 *w, u32x4 xv) {
+        const bf16x8 xf = __builtin_bit_cast(bf16x8, xv);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            u32x4 a;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t lo = w[2 * q][c >> 1], hi = w[2 * q + 1][c >> 1];
+                a[q] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+            }
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), xf, acc[c], 0, 0, 0);
+        }
+    };
+    if (!DB) {
+        for (int64_t s = s_begin; s < s_end; ++s) {
+            u32x4 w[8];
+            const u32x4 xv = load_x(s);
+            load_w(s, w);
+            mma(w, xv);
+        }
+    } else if (s_begin < s_end) {
+        u32x4 w0[8], w1[8];
+        u32x4 x0 = load_x(s_begin), x1;
+        load_w(s_begin, w0);
+        int64_t s = s_begin;
+        for (; s + 2 <= s_end; s += 2) {
+            x1 = load_x(s + 1);
+            load_w(s + 1, w1);
+            mma(w0, x0);
+            if (s + 2 < s_end) {
+                x0 = load_x(s + 2);
+                load_w(s + 2, w0);
+            }
+            mma(w1, x1);
+        }
+        if (s < s_end) mma(w0, x0);
+    }
+
+    // acc[c][q] of lane (g, li) is the partial C[li][n0 + 32 g + 8 q + c].
+    __shared__ float red[NW * 64 * 32];
+    __shared__ unsigned arrived;
+    float *mine = red + (wave * 64 + lane) * 32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) mine[q * 8 + c] = acc[c][q];
+    __syncthreads();
+    float *part = ws + ((bidx * nstrip + strip) * KS + slice) * (16 * NC);
+    // Entry t: lane L = t / 32, q = (t / 8) % 4, c = t % 8 -> row L % 16,
+    // column 32 (L / 16) + 8 q + c of the strip.
+    for (int t = tid; t < 64 * 32; t += NW * 64) {
+        float sum = 0.f;
+        for (int w2 = 0; w2 < NW; ++w2) sum += red[w2 * 64 * 32 + t];
+        const int L = t >> 5, q = (t >> 3) & 3, c = t & 7;
+        const int m = L & 15, n = 32 * (L >> 4) + 8 * q + c;
+        if (KS == 1) {
+            if (m < M) {
+                if (p.out_f32) ((float *)p.C + bidx * p.sC)[m * p.ldc + n0 + n] = sum;
+                else ((uint16_t *)p.C + bidx * p.sC)[m * p.ldc + n0 + n] = (uint16_t)bf16_rne(sum);
+            }
+        } else {
+            __hip_atomic_store(part + m * NC + n, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (KS == 1) return;
+    // Publish this slice; the last of the KS workgroups of the strip sums.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    unsigned *c_strip = cnt + bidx * nstrip + strip;
+    if (tid == 0) arrived = __hip_atomic_fetch_add(c_strip, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrived != (unsigned)(KS - 1)) return;
+    const float *parts = ws + (bidx * nstrip + strip) * KS * (16 * NC);
+    for (int t = tid; t < 16 * NC; t += NW * 64) {
+        const int m = t / NC, n = t % NC;
+        if (m >= M) continue;
+        float sum = 0.f;
+        for (int k2 = 0; k2 < KS; ++k2)
+            sum += __hip_atomic_load(parts + k2 * (16 * NC) + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (p.out_f32) ((float *)p.C + bidx * p.sC)[m * p.ldc + n0 + n] = sum;
+        else ((uint16_t *)p.C + bidx * p.sC)[m * p.ldc + n0 + n] = (uint16_t)bf16_rne(sum);
+    }
+    if (tid == 0) __hip_atomic_store(c_strip, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_decode_split(const GemmArgs &a, float *ws, unsigned *cnt, int ks, hipStream_t s)
+{
+    // 16 waves, one 32-row step in registers at a time (two would spill at
+    // 16 waves per CU; the waves themselves keep enough loads in flight).
+    hipLaunchKernelGGL((k_decode_sk<16, false>), dim3((unsigned)(a.tiles_n * ks), (unsigned)a.batch), dim3(16 * 64), 0,
+                       s, a, ws, cnt, ks);
+    return hipGetLastError();
+}
+
 // ============================================================ generic path
 //
 // Any shape, stride and alignment: 16x16 output tile per workgroup, element

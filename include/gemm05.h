@@ -18,19 +18,24 @@
  * in ELEMENTS: A[i][k] is at A + i*lda + k, B[k][j] at B + k*ldb + j, C[i][j]
  * at C + i*ldc + j.  C is overwritten (there is no alpha/beta).
  *
- * Ownership.  The caller owns every buffer.  A, B and C are device pointers
- * on the current HIP device.  The library never allocates, frees, copies or
- * synchronises: each call validates its arguments on the host, enqueues its
+ * Ownership.  The caller owns A, B and C: device pointers on the current
+ * HIP device.  Each call validates its arguments on the host, enqueues its
  * kernel(s) on `stream` (a hipStream_t; NULL means the null stream) and
- * returns.  Completion is observed through the stream.  Calls are thread-safe.
+ * returns; completion is observed through the stream.  Calls are
+ * thread-safe.  The one exception to "no allocation": the small-M path with
+ * K split over workgroups keeps a workspace of partial sums and counters per
+ * (device, stream), allocated with hipMalloc on that stream's first such
+ * call (or when a larger call needs more; the stream is synchronised before
+ * an old workspace is freed) and kept until the process exits.  If the
+ * allocation fails the call falls back to the whole-K small-M kernel.
  * No alignment is required; aligned operands (16-byte rows and pointers)
  * select the faster kernel variants.
  *
  * Edge semantics.  M == 0, N == 0 or batch == 0: nothing to do, GEMM_OK.
  * K == 0: C := 0 (the empty sum).  Results are deterministic: the same call
- * on the same inputs gives the same bits (no atomics, fixed reduction order),
- * and the small-M path splits K the same way for every M, so a row's result
- * does not depend on how many rows are in the call.
+ * on the same inputs gives the same bits (no atomics on data, fixed
+ * reduction order), and the small-M path splits K the same way for every M,
+ * so a row's result does not depend on how many rows are in the call.
  *
  * Errors.  A negative status is returned and nothing is enqueued when the
  * arguments are invalid (GEMM_ERR_INVALID_ARG): a negative size or batch;
@@ -75,7 +80,8 @@ int gemm_sgemm(int64_t M, int64_t N, int64_t K,
 
 /* BF16 GEMM with FP32 accumulation: A [M,K] and B [K,N] hold bf16 bit
  * patterns; C [M,N] is bf16 (c_type GEMM_OUT_BF16) or float (GEMM_OUT_F32).
- * M <= 16 uses the memory-bound small-M (decode) path. */
+ * M <= 16 uses the memory-bound small-M (decode) path (see Ownership for
+ * its workspace). */
 int gemm_bf16(int64_t M, int64_t N, int64_t K,
               const uint16_t *A, int64_t lda,
               const uint16_t *B, int64_t ldb,

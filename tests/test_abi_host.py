@@ -102,20 +102,31 @@ def test_force_config_unsupported(L, monkeypatch):
     monkeypatch.setenv("GEMM_FORCE_CONFIG", "generic")
     st, p = g5.plan_query(g5.GEMM_OP_SGEMM, 64, 64, 64)
     assert st == 0 and p.name == b"generic"
+    monkeypatch.setenv("GEMM_FORCE_CONFIG", "decode_splitk")
+    for (M, N, K) in ((4, 256, 31), (4, 250, 64)):            # K % 32, N % 128
+        st, _ = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
+        assert st == g5.GEMM_ERR_UNSUPPORTED
+    st, _ = g5.plan_query(g5.GEMM_OP_BF16, 4, 256, 64, lda=72)  # X rows 144 bytes apart: 16-byte aligned
+    assert st == 0
+    st, _ = g5.plan_query(g5.GEMM_OP_BF16, 4, 256, 64, lda=68)  # 136 bytes: not 16-byte aligned
+    assert st == g5.GEMM_ERR_UNSUPPORTED
 
 
 def test_selector_choices_for_the_workloads(L):
     # FFN projection: 256x192 tiles give 4 x 64 = 256 workgroups, one per CU.
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 1024, 12288, 4096)
     assert st == 0 and p.name == b"bf16_256x192" and p.grid == 256 and p.even == 1
-    # decode rows go to the small-M path, whatever M <= 16 is: 64 columns per
-    # workgroup; its fast variant needs whole column chunks and aligned rows
+    # decode rows go to the small-M path, whatever M <= 16 is: 128-column
+    # strips with K split in 2 (96 x 2 workgroups) when N % 128 == 0 and the
+    # rows are 16-byte aligned; else whole-K strips of 64 columns
     for M in (1, 4, 16):
         st, p = g5.plan_query(g5.GEMM_OP_BF16, M, 12288, 4096)
-        assert st == 0 and p.family == 4 and p.name == b"decode_64" and p.grid == 12288 // 64
+        assert st == 0 and p.family == 4 and p.name == b"decode_splitk" and p.grid == 96 * 2
         assert p.variant == 1
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 4, 12290, 4096)
     assert st == 0 and p.name == b"decode_64" and p.variant == 0
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 1, 32768, 4096)     # 256 strips: one slice, whole-K path
+    assert st == 0 and p.name == b"decode_64"
     st, p = g5.plan_query(g5.GEMM_OP_SGEMM, 4096, 4096, 4096)
     assert st == 0 and p.family == 3 and p.even == 1
     # ragged: K=4100 bf16 rows are only 8-byte aligned -> masked variant

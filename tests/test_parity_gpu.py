@@ -186,6 +186,46 @@ def test_decode_paths_ragged(oracle_mod, monkeypatch, cfg, M, N, K, batch):
                 check_f32(host[b], ref, K, amax_bf16(A[b]), amax_bf16(B[b]), f"{cfg} f32 batch {b}")
 
 
+@pytest.mark.parametrize("M,N,K,batch", [(1, 512, 4096, 1), (7, 1280, 1024, 1), (16, 384, 96, 3),
+                                         (4, 256, 8192, 1), (3, 12288, 4096, 1)])
+def test_decode_split_k(oracle_mod, monkeypatch, M, N, K, batch):
+    """The split small-M path: 1, 2 and 8 K slices per strip, a batch; two
+    calls in a row, so the second runs on the counters the first left."""
+    _say(f"decode_splitk {M}x{N}x{K} batch {batch}")
+    monkeypatch.setenv("GEMM_FORCE_CONFIG", "decode_splitk")
+    g = np.random.default_rng([M, N, K, batch, 5])
+    X = gi.to_bf16_bits(gi.normal(g, (batch, M, K)))
+    W = gi.to_bf16_bits(gi.normal(g, (batch, K, N), 0.125))
+    dX, dW = dev_bf16(X), dev_bf16(W)
+    for rep in range(2):
+        C = g5.gemm_bf16_batched(dX, dW, out_dtype=torch.float32 if rep else torch.bfloat16)
+        host = host_values(C)
+        for b in range(batch):
+            ref = oracle_mod.gemm_bf16(X[b], W[b])
+            if rep:
+                check_f32(host[b], ref, K, amax_bf16(X[b]), amax_bf16(W[b]), f"splitk f32 b{b}")
+            else:
+                check_bf16(host[b], ref, K, f"splitk bf16 b{b}")
+
+
+def test_decode_split_k_back_to_back(oracle_mod):
+    """Twenty consecutive calls of the split path with fresh inputs each time,
+    queued without synchronisation: every result must come from its own
+    call's partial sums (a stale partial would show as a mismatch)."""
+    _say("decode_splitk x20 back to back")
+    M, N, K = 2, 2048, 2048
+    g = np.random.default_rng(77)
+    Xs = [gi.to_bf16_bits(gi.normal(g, (M, K))) for _ in range(20)]
+    W = gi.to_bf16_bits(gi.normal(g, (K, N), 0.125))
+    dW = dev_bf16(W)
+    st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
+    assert plan.name == b"decode_splitk" and plan.grid == 16 * 4
+    outs = [g5.gemm_bf16(dev_bf16(X), dW, out_dtype=torch.float32) for X in Xs]
+    for i, (X, C) in enumerate(zip(Xs, outs)):
+        ref = oracle_mod.gemm_bf16(X, W)
+        check_f32(host_values(C), ref, K, amax_bf16(X), amax_bf16(W), f"call {i}")
+
+
 def test_decode_batch_invariance():
     """Rows of the M=1 and M=4 results equal the matching rows of M=16 bit for
     bit: the K split does not depend on M ("Operator & Runtime" §5.2.4)."""
