@@ -57,7 +57,7 @@ def kernel_label(plan):
     if plan.family == 2 and plan.variant in (1, 2, 3):
         av, masked = {1: (16, "false"), 2: (16, "true"), 3: (4, "true")}[plan.variant]
         wg = "2,4" if (tm, tn) == (256, 192) else "4,2"
-        return f"k_bf16_ms<{tm},{tn},{wg},4,{av},{masked}> ({name}, grid {plan.grid}, {plan.threads} threads)"
+        return f"k_bf16_ms<{tm},{tn},{wg},4,4,{av},{masked}> ({name}, grid {plan.grid}, {plan.threads} threads)"
     return f"{name} variant {plan.variant} (grid {plan.grid}, {plan.threads} threads)"
 
 

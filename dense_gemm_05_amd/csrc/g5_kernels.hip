@@ -1053,7 +1053,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode_sk(GemmArgs p, float *ws,
                 if (p.out_f32) ((float *)p.C + bidx * p.sC)[m * p.ldc + n0 + n] = sum;
                 else ((uint16_t *)p.C + bidx * p.sC)[m * p.ldc + n0 + n] = (uint16_t)bf16_rne(sum);
             }
-        } else {
+        } else if (m < M) {                  // rows past M are never read back
             __hip_atomic_store(part + m * NC + n, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
