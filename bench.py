@@ -62,8 +62,19 @@ def kernel_label(plan):
 
 
 def kernel_hash():
-    with open(KERNEL_SRC, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    """Hash of the source the FFN kernel is built from: the shared helpers
+    and the LDS-ring kernel with its epilogue (edits elsewhere in the file,
+    e.g. to the small-M kernels, leave stored counter readings valid)."""
+    with open(KERNEL_SRC, encoding="utf-8") as fh:
+        src = fh.read()
+    parts = []
+    for start, end in (("// ---------------------------------------------------------------- helpers",
+                        "// ===================================================== bf16 tiled MFMA kernel"),
+                       ("// Epilogue of whole tiles:",
+                        "// ===================================================== fp32 tiled MFMA kernel")):
+        a = src.index(start)
+        parts.append(src[a:src.index(end, a)])
+    return hashlib.sha256("".join(parts).encode()).hexdigest()[:16]
 
 
 def main():
