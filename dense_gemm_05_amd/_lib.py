@@ -34,7 +34,8 @@ class GemmPlan(ctypes.Structure):
                 ("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("tile_k", ctypes.c_int),
                 ("threads", ctypes.c_int), ("vec_a", ctypes.c_int), ("vec_b", ctypes.c_int),
                 ("even", ctypes.c_int), ("variant", ctypes.c_int), ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int64),
-                ("model_bytes", ctypes.c_double), ("name", ctypes.c_char * 48)]
+                ("model_bytes", ctypes.c_double), ("name", ctypes.c_char * 48),
+                ("workspace_bytes", ctypes.c_int64)]
 
 
 class GemmError(RuntimeError):

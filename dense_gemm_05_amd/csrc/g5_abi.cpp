@@ -279,8 +279,14 @@ int select_plan(const Problem &p, Plan &pl)
             double eff;
         };
         static const Cand bf16c[] = {{CFG_BF16_256x192, 1.0}, {CFG_BF16_256x128, 0.95}, {CFG_BF16_128x128, 0.85}};
+        // With only a few 32-deep stages per tile, a tile's time is mostly
+        // its first-load latency and its epilogue, which a second resident
+        // workgroup per CU hides: the 128x128 ring kernel (64 KiB of LDS,
+        // two per CU) measured 1.12x faster than 256x128 (96 KiB, one per
+        // CU) on 32 x 1024x1024x128 with FP32 output.
+        static const Cand bf16_short_k[] = {{CFG_BF16_256x192, 0.7}, {CFG_BF16_256x128, 0.75}, {CFG_BF16_128x128, 1.0}};
         static const Cand f32c[] = {{CFG_F32_128x128, 1.0}, {CFG_F32_64x64, 0.8}};
-        const Cand *cands = p.op == GEMM_OP_BF16 ? bf16c : f32c;
+        const Cand *cands = p.op == GEMM_OP_BF16 ? (p.K <= 8 * 32 ? bf16_short_k : bf16c) : f32c;
         const int nc = p.op == GEMM_OP_BF16 ? 3 : 2;
         double best = 0.0;
         for (int i = 0; i < nc; ++i) {
@@ -303,6 +309,14 @@ int select_plan(const Problem &p, Plan &pl)
     if (pl.variant < 0) return GEMM_ERR_UNSUPPORTED;   // forced split path without its preconditions
     return GEMM_OK;
 }
+
+// Workspace of the split small-M path: one slot of 16 x 128 partial sums
+// per (batch entry, strip, K slice), one arrival counter per strip.
+size_t split_part_bytes(const Problem &p, const Plan &pl)
+{
+    return (size_t)p.batch * pl.tiles_n * pl.ks * 16 * 128 * sizeof(float);
+}
+size_t split_cnt_bytes(const Problem &p, const Plan &pl) { return (size_t)p.batch * pl.tiles_n * sizeof(unsigned); }
 
 void fill_public_plan(const Problem &p, const Plan &pl, gemm_plan *out)
 {
@@ -329,6 +343,7 @@ void fill_public_plan(const Problem &p, const Plan &pl, gemm_plan *out)
     }
     out->model_bytes = pl.model_bytes;
     std::snprintf(out->name, sizeof out->name, "%s", c.name);
+    if (pl.config == CFG_DECODE_SPLIT) out->workspace_bytes = split_part_bytes(p, pl) + split_cnt_bytes(p, pl);
 }
 
 // ------------------------------------------------------------ device check
@@ -449,8 +464,8 @@ int run(const Problem &p, void *stream)
     if (pl.config == CFG_DECODE_SPLIT) {
         int dev = 0;
         (void)hipGetDevice(&dev);
-        const size_t cnt_bytes = (size_t)p.batch * pl.tiles_n * sizeof(unsigned);
-        const size_t part_bytes = (size_t)p.batch * pl.tiles_n * pl.ks * 16 * 128 * sizeof(float);
+        const size_t cnt_bytes = split_cnt_bytes(p, pl);
+        const size_t part_bytes = split_part_bytes(p, pl);
         unsigned *cnt = nullptr;
         float *part = nullptr;
         if (get_workspace(dev, stream, cnt_bytes, part_bytes, &cnt, &part)) {

@@ -354,10 +354,12 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 1) k_bf16_mfma(GemmArgs p)
 // padded by 16 bytes against bank conflicts), then copied to C in 16-byte
 // chunks with consecutive lanes on consecutive chunks of a row.  Tiles that
 // do not fit in LDS at once go in passes of whole wave rows.  `lds` holds
-// LDS_BYTES; every wave must have finished with it.
-template <int BM, int BN, int WGM, int WGN, int LDS_BYTES, typename TOut, int NFN, int NFM>
+// LDS_BYTES; every wave must have finished with it.  MASKED: only chunks of
+// rows < M that end at or before column N are stored (N must be a multiple
+// of the chunk's 16 / sizeof(TOut) elements, so no chunk straddles it).
+template <int BM, int BN, int WGM, int WGN, int LDS_BYTES, typename TOut, bool MASKED, int NFN, int NFM>
 __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM], uint16_t *lds, void *Cb,
-                                                   int64_t ldc, int64_t m0, int64_t n0)
+                                                   int64_t ldc, int64_t m0, int64_t n0, int64_t M, int64_t N)
 {
     constexpr int TM = BM / WGM, TN = BN / WGN;
     constexpr int ESZ = (int)sizeof(TOut);
@@ -392,6 +394,7 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
         __syncthreads();
         for (int q = tid; q < RP * CPR; q += NT) {
             const int r = q / CPR, c = q % CPR;
+            if (MASKED && (m0 + pass * RP + r >= M || n0 + (int64_t)(c + 1) * (16 / ESZ) > N)) continue;
             const u32x4 v = *(const u32x4 *)(L + r * PITCH + c * 16);
             char *dst = (char *)Cb + ((m0 + pass * RP + r) * ldc + n0) * ESZ + c * 16;
             __builtin_nontemporal_store(v, (u32x4 *)dst);     // C is written once
@@ -633,15 +636,17 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     __builtin_amdgcn_s_waitcnt(0);
 
     void *Cb = (char *)p.C + tc.b * p.sC * (p.out_f32 ? 4 : 2);
-    if (!MASKED && p.align_c >= 16) {
-        // Whole tile, 16-byte aligned rows of C: stage the results through
-        // LDS (free once every wave's copies and reads are done) and write
-        // whole 16-byte chunks, consecutive lanes on consecutive chunks of a
-        // row, so that every 128-byte line of C is written by one store.
+    if (p.align_c >= 16 && (!MASKED || N % (p.out_f32 ? 4 : 8) == 0)) {
+        // 16-byte aligned rows of C: stage the results through LDS (free
+        // once every wave's copies and reads are done) and write whole
+        // 16-byte chunks, consecutive lanes on consecutive chunks of a row,
+        // so that every 128-byte line of C is written by one store.  Edge
+        // tiles store only the chunks inside C, which needs N to be a whole
+        // number of chunks.
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (p.out_f32) store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, float>(acc, smem, Cb, p.ldc, m0, n0);
-        else store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, uint16_t>(acc, smem, Cb, p.ldc, m0, n0);
+        if (p.out_f32) store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, float, MASKED>(acc, smem, Cb, p.ldc, m0, n0, M, N);
+        else store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, uint16_t, MASKED>(acc, smem, Cb, p.ldc, m0, n0, M, N);
         return;
     }
 #pragma unroll

@@ -130,6 +130,9 @@ typedef struct {
     int64_t lds_bytes; /* LDS per workgroup */
     double model_bytes;/* traffic model of "Operator & Runtime" §5.2.2 for the chosen tile */
     char name[48];     /* configuration name, as accepted by GEMM_FORCE_CONFIG */
+    int64_t workspace_bytes; /* library-owned workspace the call needs: partial
+                                sums and arrival counters of the split small-M
+                                path; 0 for every other plan */
 } gemm_plan;
 
 /* Operation selector for gemm_plan_query. */

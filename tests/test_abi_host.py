@@ -122,13 +122,16 @@ def test_selector_choices_for_the_workloads(L):
     for M in (1, 4, 16):
         st, p = g5.plan_query(g5.GEMM_OP_BF16, M, 12288, 4096)
         assert st == 0 and p.family == 4 and p.name == b"decode_splitk" and p.grid == 96 * 2
-        assert p.variant == 1
+        assert p.variant == 1 and p.workspace_bytes == 96 * 2 * 16 * 128 * 4 + 96 * 4
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 4, 12290, 4096)
-    assert st == 0 and p.name == b"decode_64" and p.variant == 0
+    assert st == 0 and p.name == b"decode_64" and p.variant == 0 and p.workspace_bytes == 0
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 1, 32768, 4096)     # 256 strips: one slice, whole-K path
     assert st == 0 and p.name == b"decode_64"
     st, p = g5.plan_query(g5.GEMM_OP_SGEMM, 4096, 4096, 4096)
     assert st == 0 and p.family == 3 and p.even == 1
+    # batched scores, K = 128 (4 stages): 128x128 tiles, two workgroups per CU
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 1024, 1024, 128, batch=32, c_type=1)
+    assert st == 0 and p.name == b"bf16_128x128" and p.grid == 32 * 8 * 8 and p.variant == 1
     # ragged: K=4100 bf16 rows are only 8-byte aligned -> masked variant
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 1000, 12280, 4100, c_type=1)
     assert st == 0 and p.family == 2 and p.even == 0 and p.vec_a == 8 and p.vec_b == 16
@@ -198,3 +201,20 @@ def test_tile_map_gives_each_xcd_a_compact_block(L):
             cols.add(tn.value)
             rowset.add(tm.value)
         assert rowset == {0, 1, 2, 3} and cols == set(range(8 * x, 8 * x + 8))
+
+
+@pytest.mark.parametrize("M,N,K,batch", [(1, 12288, 4096, 1), (5, 1664, 4160, 1), (16, 384, 1024, 3),
+                                         (9, 1024, 1024, 5), (1, 256, 8192, 1)])
+def test_split_small_m_workspace_covers_every_slot(M, N, K, batch):
+    """The split small-M kernel's workgroup (strip, slice) of batch entry b
+    writes partial-sum slot (b*strips + strip)*KS + slice of 16 x 128 floats
+    and counter b*strips + strip; the workspace the plan reports must hold
+    the largest of each, for the KS the launch uses (grid = strips*KS*batch)."""
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, M, N, K, batch=batch)
+    assert st == 0 and p.name == b"decode_splitk", p.name
+    strips = N // 128
+    ks = p.grid // (strips * batch)
+    assert p.grid == strips * ks * batch and 2 <= ks <= 8
+    top_slot = ((batch - 1) * strips + strips - 1) * ks + ks - 1
+    top_cnt = (batch - 1) * strips + strips - 1
+    assert (top_slot + 1) * 16 * 128 * 4 + (top_cnt + 1) * 4 <= p.workspace_bytes

@@ -187,10 +187,12 @@ def test_decode_paths_ragged(oracle_mod, monkeypatch, cfg, M, N, K, batch):
 
 
 @pytest.mark.parametrize("M,N,K,batch", [(1, 512, 4096, 1), (7, 1280, 1024, 1), (16, 384, 96, 3),
-                                         (4, 256, 8192, 1), (3, 12288, 4096, 1)])
+                                         (4, 256, 8192, 1), (3, 12288, 4096, 1), (5, 1664, 4160, 1),
+                                         (9, 1024, 1024, 5)])
 def test_decode_split_k(oracle_mod, monkeypatch, M, N, K, batch):
-    """The split small-M path: 1, 2 and 8 K slices per strip, a batch; two
-    calls in a row, so the second runs on the counters the first left."""
+    """The split small-M path: 1, 2 and 8 K slices per strip, slices of
+    unequal length, batches; two calls in a row, so the second runs on the
+    counters the first left."""
     _say(f"decode_splitk {M}x{N}x{K} batch {batch}")
     monkeypatch.setenv("GEMM_FORCE_CONFIG", "decode_splitk")
     g = np.random.default_rng([M, N, K, batch, 5])
