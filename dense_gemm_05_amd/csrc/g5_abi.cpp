@@ -30,6 +30,7 @@ const ConfigInfo kConfigs[CFG_COUNT] = {
     {CFG_BF16_256x128, GEMM_FAMILY_BF16_MFMA, 256, 128, 64, 256, 2 * (256 * 64 + 64 * 128) * 2, "bf16_256x128"},
     {CFG_F32_128x128, GEMM_FAMILY_F32_MFMA, 128, 128, 32, 256, 2 * (128 * 32 + 32 * 132) * 4, "f32_128x128"},
     {CFG_F32_64x64, GEMM_FAMILY_F32_MFMA, 64, 64, 32, 256, 2 * (64 * 32 + 32 * 68) * 4, "f32_64x64"},
+    {CFG_F32_32x32_WK, GEMM_FAMILY_F32_MFMA, 32, 32, 256, 256, 8 * (32 * 32 + 32 * 36) * 4, "f32_32x32_wholek"},
     {CFG_DECODE_64, GEMM_FAMILY_DECODE, 16, 64, 32, 1024, 16 * 64 * 16 * 4, "decode_64"},
     {CFG_DECODE_SPLIT, GEMM_FAMILY_DECODE, 16, 128, 32, 1024, 16 * 64 * 32 * 4 + 4, "decode_splitk"},
     {CFG_GENERIC, GEMM_FAMILY_GENERIC, 16, 16, 16, 256, 2 * 16 * 17 * 4, "generic"},
@@ -213,6 +214,11 @@ int pick_variant(const Problem &p, const Plan &pl, bool *even)
 {
     const ConfigInfo &c = kConfigs[pl.config];
     *even = false;
+    if (pl.config == CFG_F32_32x32_WK) {     // all of K at once: whole tiles and slabs only
+        *even = !(p.M % 32 || p.N % 32 || p.K % 32) && p.K <= 256 && pl.align_a >= 16 && pl.align_b >= 16 &&
+                pl.align_c >= 16;
+        return *even ? 1 : -1;
+    }
     if (c.family == GEMM_FAMILY_F32_MFMA) {
         *even = !(p.M % c.tile_m || p.N % c.tile_n || p.K % c.tile_k) && pl.align_a >= 16 && pl.align_b >= 16 &&
                 pl.align_c >= 16;
@@ -263,6 +269,12 @@ int select_plan(const Problem &p, Plan &pl)
             kConfigs[id].family == GEMM_FAMILY_NONE)
             return GEMM_ERR_UNSUPPORTED;
         pl.config = id;
+    } else if (p.op == GEMM_OP_SGEMM && p.K <= 256 && cdiv(p.M, 64) * cdiv(p.N, 64) * p.batch < kNumCU &&
+               [&] { Plan t = pl; t.config = CFG_F32_32x32_WK; bool ev; return pick_variant(p, t, &ev) == 1; }()) {
+        // A small FP32 problem with few slabs: 32x32 tiles with all of K
+        // staged at once (one load latency per tile instead of one per slab;
+        // 256^3 measured 9.4 us with the double-buffered 64x64 kernel).
+        pl.config = CFG_F32_32x32_WK;
     } else if (p.op == GEMM_OP_BF16 && p.M <= 16 && p.batch <= 65535) {
         // The split path when its preconditions hold and it would use more
         // than one slice; else whole-K strips of 64 columns.

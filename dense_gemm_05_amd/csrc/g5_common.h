@@ -78,6 +78,7 @@ enum ConfigId {
     CFG_BF16_256x128,      // 4 waves (2x2), wave tile 128x64
     CFG_F32_128x128,       // 4 waves (2x2), wave tile 64x64
     CFG_F32_64x64,         // 4 waves (2x2), wave tile 32x32
+    CFG_F32_32x32_WK,      // 4 waves (2x2), wave tile 16x16, all of K (<= 256) staged at once
     CFG_DECODE_64,         // small M, 64 columns per workgroup, 16 waves, K split in-workgroup
     CFG_DECODE_SPLIT,      // small M, 128-column strips, K split over workgroups too
     CFG_GENERIC,

@@ -790,6 +790,117 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_f32_mfma(GemmArgs p)
         }
 }
 
+// FP32, all of K staged at once (K <= KMAX, whole tiles, 16-byte aligned
+// rows).  A small problem gives each CU only a few slabs to multiply, so the
+// double-buffered kernel above spends its time on one global-load latency per
+// slab in sequence.  Here every thread issues the loads of every slab of its
+// tile before the first is stored to LDS, so the tile waits for one latency,
+// then multiplies all slabs from LDS with a single barrier.  Slab layout and
+// fragment reads are those of k_f32_mfma.
+template <int BM, int BN, int WGM, int WGN, int KMAX>
+__global__ void __launch_bounds__(WGM *WGN * 64, 2) k_f32_wholek(GemmArgs p)
+{
+    constexpr int T = WGM * WGN * 64;
+    constexpr int BK = 32;
+    constexpr int NS = KMAX / BK;
+    constexpr int TM = BM / WGM, TN = BN / WGN;
+    constexpr int FM = TM / 16, FN = TN / 16;
+    constexpr int A_CPR = BK / 4;
+    constexpr int B_CPR = BN / 4;
+    constexpr int BLD = BN + 4;
+    constexpr int CA = BM * A_CPR / T;
+    constexpr int CB = BK * B_CPR / T;
+    constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BLD;
+    static_assert((BM * A_CPR) % T == 0 && (BK * B_CPR) % T == 0 && CA >= 1 && CB >= 1, "slab chunks must divide threads");
+    __shared__ __attribute__((aligned(16))) float smem[NS * (A_ELEMS + B_ELEMS)];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int g = lane >> 4, li = lane & 15;
+    const TileCoord tc = tile_map(blockIdx.x, p.batch, p.tiles_m, p.tiles_n, p.group_m);
+    const int64_t m0 = tc.tm * BM, n0 = tc.tn * BN;
+    const int64_t lda = p.lda, ldb = p.ldb;
+    const float *Ab = (const float *)p.A + tc.b * p.sA + m0 * lda;
+    const float *Bb = (const float *)p.B + tc.b * p.sB + n0;
+    const int KT = (int)(p.K / BK);                  // 1 <= KT <= NS (host checked)
+
+    u32x4 ra[NS][CA], rb[NS][CB];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        if (s >= KT) break;
+#pragma unroll
+        for (int i = 0; i < CA; ++i) {
+            const int q = tid + T * i, row = q / A_CPR, c = q % A_CPR;
+            ra[s][i] = *(const u32x4 *)(Ab + (int64_t)row * lda + s * BK + c * 4);
+        }
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            const int q = tid + T * i, k = q / B_CPR, c = q % B_CPR;
+            rb[s][i] = *(const u32x4 *)(Bb + (int64_t)(s * BK + k) * ldb + c * 4);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        if (s >= KT) break;
+        float *As = smem + s * (A_ELEMS + B_ELEMS);
+        float *Bs = As + A_ELEMS;
+#pragma unroll
+        for (int i = 0; i < CA; ++i) {
+            const int q = tid + T * i, row = q / A_CPR, c = q % A_CPR;
+            *(u32x4 *)(As + row * BK + ((c ^ swz_a(row)) * 4)) = ra[s][i];
+        }
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+            const int q = tid + T * i, k = q / B_CPR, c = q % B_CPR;
+            *(u32x4 *)(Bs + k * BLD + c * 4) = rb[s][i];
+        }
+    }
+    __syncthreads();
+
+    f32x4 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < KT; ++kt) {
+        const float *As = smem + kt * (A_ELEMS + B_ELEMS);
+        const float *Bs = As + A_ELEMS;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            f32x4 af[FM];
+            float bfr[FN][4];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int row = wm * TM + fm * 16 + li;
+                const int c = ks * 4 + g;
+                af[fm] = *(const f32x4 *)(As + row * BK + ((c ^ swz_a(row)) * 4));
+            }
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) bfr[fn][q] = Bs[(ks * 16 + g * 4 + q) * BLD + wn * TN + fn * 16 + li];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm)
+                        acc[fn][fm] = __builtin_amdgcn_mfma_f32_16x16x4f32(bfr[fn][q], af[fm][q], acc[fn][fm], 0, 0, 0);
+        }
+    }
+
+    float *Cb = (float *)p.C + tc.b * p.sC;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int64_t m = m0 + wm * TM + fm * 16 + li;
+            const int64_t n = n0 + wn * TN + fn * 16 + g * 4;
+            store4(Cb, true, p.ldc, m, n, acc[fn][fm], true, p.M, p.N, p.align_c);
+        }
+}
+
 // ========================================================= small-M (decode)
 //
 // C[M,N] = X[M,K] . W[K,N] for M <= 16 is bound by streaming W once from HBM
@@ -1179,6 +1290,11 @@ hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, int 
     case CFG_BF16_256x128: return launch_bf16<256, 128, 2, 2, 4, 2, 4, 4>(a, variant, grid, s);
     case CFG_F32_128x128: return launch_f32<128, 128, 2, 2>(a, variant == 1, grid, s);
     case CFG_F32_64x64: return launch_f32<64, 64, 2, 2>(a, variant == 1, grid, s);
+    case CFG_F32_32x32_WK:
+        // variant 1 only: whole tiles, K % 32 == 0, K <= 256, 16-byte aligned rows
+        if (variant != 1) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((k_f32_wholek<32, 32, 2, 2, 256>), dim3((unsigned)grid), dim3(256), 0, s, a);
+        return hipGetLastError();
     case CFG_DECODE_64:
         // variant 1: every column chunk in range, 8-byte aligned W rows and
         // 16-byte aligned X rows

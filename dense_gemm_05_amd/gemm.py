@@ -26,8 +26,16 @@ def _ld(t, inner):
     return ld
 
 
-def _stream(dev):
-    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+# The raw handle of a device's current stream, without building a Stream
+# object (a few microseconds per call otherwise, which is the whole kernel
+# time of a small product).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(idx):
+    if _raw_stream is not None:
+        return _raw_stream(idx)
+    return torch.cuda.current_stream(idx).cuda_stream
 
 
 def _check_dev(*ts):
@@ -38,6 +46,15 @@ def _check_dev(*ts):
         if t.device != dev:
             raise ValueError("operands must be on one device")
     return dev
+
+
+def _launch(fn, dev, *args):
+    """Call `fn(*args, stream)` with `dev` current, on its current stream."""
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    if idx == torch.cuda.current_device():
+        return fn(*args, _stream(idx))
+    with torch.cuda.device(idx):
+        return fn(*args, _stream(idx))
 
 
 def gemm_sgemm(A, B, C=None):
@@ -53,9 +70,8 @@ def gemm_sgemm(A, B, C=None):
         C = torch.empty((M, N), dtype=torch.float32, device=dev)
     if C.shape != (M, N) or C.dtype != torch.float32:
         raise ValueError("C must be float32 [M, N]")
-    with torch.cuda.device(dev):
-        st = lib().gemm_sgemm(M, N, K, A.data_ptr(), _ld(A, K), B.data_ptr(), _ld(B, N),
-                              C.data_ptr(), _ld(C, N), _stream(dev))
+    st = _launch(lib().gemm_sgemm, dev, M, N, K, A.data_ptr(), _ld(A, K), B.data_ptr(), _ld(B, N),
+                 C.data_ptr(), _ld(C, N))
     if st != 0:
         raise GemmError(st, "gemm_sgemm")
     return C
@@ -84,9 +100,8 @@ def gemm_bf16(A, B, C=None, out_dtype=torch.bfloat16):
     if C.shape != (M, N):
         raise ValueError("C must be [M, N]")
     code = _out_code(C.dtype)
-    with torch.cuda.device(dev):
-        st = lib().gemm_bf16(M, N, K, A.data_ptr(), _ld(A, K), B.data_ptr(), _ld(B, N),
-                             C.data_ptr(), _ld(C, N), code, _stream(dev))
+    st = _launch(lib().gemm_bf16, dev, M, N, K, A.data_ptr(), _ld(A, K), B.data_ptr(), _ld(B, N),
+                 C.data_ptr(), _ld(C, N), code)
     if st != 0:
         raise GemmError(st, "gemm_bf16")
     return C
@@ -112,10 +127,8 @@ def gemm_bf16_batched(A, B, C=None, out_dtype=torch.bfloat16):
     if tuple(C.shape) != (batch, M, N):
         raise ValueError("C must be [batch, M, N]")
     code = _out_code(C.dtype)
-    with torch.cuda.device(dev):
-        st = lib().gemm_bf16_batched(batch, M, N, K, A.data_ptr(), _ld(A, K), _bstride(A),
-                                     B.data_ptr(), _ld(B, N), _bstride(B),
-                                     C.data_ptr(), _ld(C, N), _bstride(C), code, _stream(dev))
+    st = _launch(lib().gemm_bf16_batched, dev, batch, M, N, K, A.data_ptr(), _ld(A, K), _bstride(A),
+                 B.data_ptr(), _ld(B, N), _bstride(B), C.data_ptr(), _ld(C, N), _bstride(C), code)
     if st != 0:
         raise GemmError(st, "gemm_bf16_batched")
     return C

@@ -102,6 +102,12 @@ def test_force_config_unsupported(L, monkeypatch):
     monkeypatch.setenv("GEMM_FORCE_CONFIG", "generic")
     st, p = g5.plan_query(g5.GEMM_OP_SGEMM, 64, 64, 64)
     assert st == 0 and p.name == b"generic"
+    monkeypatch.setenv("GEMM_FORCE_CONFIG", "f32_32x32_wholek")
+    for (M, N, K) in ((100, 256, 256), (256, 256, 288), (256, 250, 256)):   # M % 32, K > 256, N % 32
+        st, _ = g5.plan_query(g5.GEMM_OP_SGEMM, M, N, K)
+        assert st == g5.GEMM_ERR_UNSUPPORTED
+    st, _ = g5.plan_query(g5.GEMM_OP_SGEMM, 256, 256, 256, lda=258)   # A rows 8-byte aligned
+    assert st == g5.GEMM_ERR_UNSUPPORTED
     monkeypatch.setenv("GEMM_FORCE_CONFIG", "decode_splitk")
     for (M, N, K) in ((4, 256, 31), (4, 250, 64)):            # K % 32, N % 128
         st, _ = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
@@ -129,6 +135,12 @@ def test_selector_choices_for_the_workloads(L):
     assert st == 0 and p.name == b"decode_64"
     st, p = g5.plan_query(g5.GEMM_OP_SGEMM, 4096, 4096, 4096)
     assert st == 0 and p.family == 3 and p.even == 1
+    # FP32 256^3: 32x32 tiles with all of K staged at once; K = 288 (9 slabs)
+    # or a 4096^3 problem go to the double-buffered kernels
+    st, p = g5.plan_query(g5.GEMM_OP_SGEMM, 256, 256, 256)
+    assert st == 0 and p.name == b"f32_32x32_wholek" and p.grid == 64 and p.variant == 1
+    st, p = g5.plan_query(g5.GEMM_OP_SGEMM, 256, 256, 288)
+    assert st == 0 and p.name == b"f32_64x64"
     # batched scores, K = 128 (4 stages): 128x128 tiles, two workgroups per CU
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 1024, 1024, 128, batch=32, c_type=1)
     assert st == 0 and p.name == b"bf16_128x128" and p.grid == 32 * 8 * 8 and p.variant == 1

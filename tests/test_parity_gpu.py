@@ -139,6 +139,28 @@ def test_sgemm_every_config(oracle_mod, monkeypatch, cfg):
     check_f32(host_values(C), ref, K, np.abs(A).max(), np.abs(B).max(), cfg)
 
 
+@pytest.mark.parametrize("M,N,K,pad", [(256, 256, 256, 0), (64, 96, 32, 0), (96, 32, 224, 4), (320, 128, 160, 8)])
+def test_sgemm_whole_k(oracle_mod, M, N, K, pad):
+    """The whole-K FP32 kernel (all slabs staged before the first MFMA) on
+    1 to 8 slabs; padded rows of A, B and C hold NaN, so a read past K or N
+    or a write past N shows."""
+    _say(f"sgemm whole-K {M}x{N}x{K} pad {pad}")
+    A, B = gi.small_case("f32", M, N, K, seed=K + pad)
+    Aw = np.full((M, K + pad), np.nan, np.float32)
+    Bw = np.full((K, N + pad), np.nan, np.float32)
+    Aw[:, :K], Bw[:, :N] = A, B
+    dA, dB = dev_f32(Aw), dev_f32(Bw)
+    Cfull = torch.full((M, N + pad), float("nan"), device="cuda", dtype=torch.float32)
+    st, plan = g5.plan_query(g5.GEMM_OP_SGEMM, M, N, K, lda=K + pad, ldb=N + pad, ldc=N + pad,
+                             a_addr=dA.data_ptr(), b_addr=dB.data_ptr(), c_addr=Cfull.data_ptr())
+    assert st == 0 and plan.name == b"f32_32x32_wholek", plan.name
+    g5.gemm_sgemm(dA[:, :K], dB[:, :N], Cfull[:, :N])
+    host = host_values(Cfull)
+    check_f32(host[:, :N], oracle_mod.gemm_f32(A, B), K, np.abs(A).max(), np.abs(B).max(), "sgemm whole-K")
+    if pad:
+        assert np.all(np.isnan(host[:, N:])), "ldc padding was written"
+
+
 def test_ffn_projection_full_size(oracle_mod):
     """X[1024,4096] . W[4096,12288] -> bf16, the benchmarked launch; 48 rows
     spread across every row tile and all 12288 columns are checked in full."""
