@@ -59,6 +59,8 @@ struct Plan {
     int64_t tiles_m = 0, tiles_n = 0, group_m = 1;
     int align_a = 2, align_b = 2, align_c = 2;
     int ks = 1;              // K slices of the split small-M path
+    bool realign_a = false;  // copy A's rows to 16-byte aligned ones first
+    int64_t lda2 = 0;        // row stride of that copy (elements)
     double model_bytes = 0.0;
 };
 
@@ -319,7 +321,33 @@ int select_plan(const Problem &p, Plan &pl)
     if (pl.grid <= 0 || pl.grid > (int64_t)1 << 24) return GEMM_ERR_UNSUPPORTED;
     pl.variant = pick_variant(p, pl, &pl.even);
     if (pl.variant < 0) return GEMM_ERR_UNSUPPORTED;   // forced split path without its preconditions
+    // A large bf16 product whose A rows are not 16-byte aligned: multiply
+    // from a copy of A with aligned rows when that lets the ring kernel copy
+    // A 16 bytes per lane (the copy costs 2 x M x K x 2 bytes of traffic,
+    // small next to the product from 2^30 multiply-adds on).
+    if (kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && pl.align_a < 16 &&
+        (double)p.batch * p.M * p.N * p.K >= (double)(1 << 30)) {
+        Problem q = p;
+        q.lda = (p.K + 7) / 8 * 8;
+        q.sA = p.M * q.lda;
+        Plan t = pl;
+        t.align_a = 16;
+        bool ev = false;
+        const int v = pick_variant(q, t, &ev);
+        if (v == 1 || v == 2) {
+            pl.realign_a = true;
+            pl.lda2 = q.lda;
+            pl.align_a = 16;
+            pl.variant = v;
+            pl.even = ev;
+        }
+    }
     return GEMM_OK;
+}
+
+size_t realign_bytes(const Problem &p, const Plan &pl)
+{
+    return pl.realign_a ? (size_t)p.batch * p.M * pl.lda2 * 2 : 0;
 }
 
 // Workspace of the split small-M path: one slot of 16 x 128 partial sums
@@ -356,6 +384,7 @@ void fill_public_plan(const Problem &p, const Plan &pl, gemm_plan *out)
     out->model_bytes = pl.model_bytes;
     std::snprintf(out->name, sizeof out->name, "%s", c.name);
     if (pl.config == CFG_DECODE_SPLIT) out->workspace_bytes = split_part_bytes(p, pl) + split_cnt_bytes(p, pl);
+    out->workspace_bytes += realign_bytes(p, pl);
 }
 
 // ------------------------------------------------------------ device check
@@ -397,7 +426,8 @@ struct Buffer {
     size_t bytes = 0;
 };
 struct Workspace {
-    Buffer cnt, part;
+    Buffer cnt, part;  // split small-M path
+    Buffer rows;       // realigned copy of A
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, void *>, Workspace> g_ws;
@@ -437,6 +467,14 @@ bool get_workspace(int dev, void *stream, size_t cnt_bytes, size_t part_bytes, u
     return true;
 }
 
+uint16_t *get_row_buffer(int dev, void *stream, size_t bytes)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace &w = g_ws[std::make_pair(dev, stream)];
+    if (!grow(w.rows, bytes, false, stream)) return nullptr;
+    return (uint16_t *)w.rows.ptr;
+}
+
 int run(const Problem &p, void *stream)
 {
     int st = validate(p);
@@ -473,6 +511,27 @@ int run(const Problem &p, void *stream)
     a.align_b = pl.align_b;
     a.align_c = pl.align_c;
     a.out_f32 = elem_c(p) == 4 ? 1 : 0;
+    if (pl.realign_a) {
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        uint16_t *A2 = get_row_buffer(dev, stream, realign_bytes(p, pl));
+        if (A2) {
+            const hipError_t e = launch_realign_rows((const uint16_t *)p.a, p.lda, p.sA, p.batch, p.M, p.K,
+                                                     row_alignment(p.a, p.lda, p.sA, p.batch, 2), A2, pl.lda2,
+                                                     (hipStream_t)stream);
+            if (e != hipSuccess) return GEMM_ERR_LAUNCH;
+            a.A = A2;
+            a.lda = pl.lda2;
+            a.sA = p.M * pl.lda2;
+            a.align_a = 16;
+        } else {
+            // No buffer: multiply from A as it is.
+            pl.realign_a = false;
+            pl.align_a = row_alignment(p.a, p.lda, p.sA, p.batch, 2);
+            pl.variant = pick_variant(p, pl, &pl.even);
+            a.align_a = pl.align_a;
+        }
+    }
     if (pl.config == CFG_DECODE_SPLIT) {
         int dev = 0;
         (void)hipGetDevice(&dev);

@@ -20,6 +20,12 @@ hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, int 
 // partial sums, `cnt` batch x strips counters that are zero on entry and
 // left zero on exit.  Requires N % 128 == 0, K % 32 == 0, 16-byte aligned
 // rows of X and W.
+// Copy batch x M rows of K bf16 elements (row stride lda, batch stride sA,
+// rows `align`-byte aligned) into A2 with row stride lda2 (a multiple of 8,
+// >= K) and batch stride M x lda2, zero-filling columns K..lda2-1.
+hipError_t launch_realign_rows(const uint16_t *A, int64_t lda, int64_t sA, int64_t batch, int64_t M, int64_t K,
+                               int align, uint16_t *A2, int64_t lda2, hipStream_t s);
+
 hipError_t launch_decode_split(const GemmArgs &a, float *ws, unsigned *cnt, int ks, hipStream_t s);
 
 }  // namespace g5

@@ -1203,6 +1203,39 @@ hipError_t launch_decode_split(const GemmArgs &a, float *ws, unsigned *cnt, int 
     return hipGetLastError();
 }
 
+// ===================================================== row realignment
+//
+// A bf16 operand whose rows are not 16-byte aligned can only be copied into
+// LDS 4 bytes per lane, four times the copy instructions of the 16-byte
+// copies (measured on 1000x12280x4100: 142 against 125 us for the same
+// product with aligned rows).  For a large product the library first copies
+// the rows into a buffer with a row length of lda2 elements (K rounded up to
+// a multiple of 8; columns K..lda2-1 hold zeros) and multiplies from there.
+// One thread per 16-byte chunk of the destination, grid-stride.
+__global__ void __launch_bounds__(256) k_realign_rows(const uint16_t *A, int64_t lda, int64_t sA, int64_t batch,
+                                                      int64_t M, int64_t K, int align, uint16_t *A2, int64_t lda2)
+{
+    const int64_t cpr = lda2 / 8;                      // chunks per row
+    const int64_t total = batch * M * cpr;
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total; q += (int64_t)gridDim.x * 256) {
+        const int64_t r = q / cpr, c = q % cpr;
+        const int64_t b = r / M, m = r % M;
+        const u32x4 v = load_chunk8_bf16(A + b * sA + m * lda, 8 * c, K, true, align);
+        *(u32x4 *)(A2 + r * lda2 + 8 * c) = v;
+    }
+}
+
+hipError_t launch_realign_rows(const uint16_t *A, int64_t lda, int64_t sA, int64_t batch, int64_t M, int64_t K,
+                               int align, uint16_t *A2, int64_t lda2, hipStream_t s)
+{
+    const int64_t total = batch * M * (lda2 / 8);
+    int64_t grid = (total + 255) / 256;
+    if (grid > 4096) grid = 4096;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(k_realign_rows, dim3((unsigned)grid), dim3(256), 0, s, A, lda, sA, batch, M, K, align, A2, lda2);
+    return hipGetLastError();
+}
+
 // ============================================================ generic path
 //
 // Any shape, stride and alignment: 16x16 output tile per workgroup, element

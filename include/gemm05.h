@@ -22,12 +22,15 @@
  * HIP device.  Each call validates its arguments on the host, enqueues its
  * kernel(s) on `stream` (a hipStream_t; NULL means the null stream) and
  * returns; completion is observed through the stream.  Calls are
- * thread-safe.  The one exception to "no allocation": the small-M path with
- * K split over workgroups keeps a workspace of partial sums and counters per
- * (device, stream), allocated with hipMalloc on that stream's first such
- * call (or when a larger call needs more; the stream is synchronised before
- * an old workspace is freed) and kept until the process exits.  If the
- * allocation fails the call falls back to the whole-K small-M kernel.
+ * thread-safe.  The exceptions to "no allocation" are two workspaces kept
+ * per (device, stream): the small-M path with K split over workgroups keeps
+ * partial sums and counters there, and a large bf16 product (from 2^30
+ * multiply-adds) whose A rows are not 16-byte aligned first copies A's rows
+ * there with 16-byte aligned starts.  Each is allocated with hipMalloc on
+ * that stream's first such call (or when a larger call needs more; the
+ * stream is synchronised before an old buffer is freed) and kept until the
+ * process exits.  If an allocation fails the call runs without it: the
+ * whole-K small-M kernel, or the tiled kernel copying A's rows as they are.
  * No alignment is required; aligned operands (16-byte rows and pointers)
  * select the faster kernel variants.
  *
@@ -119,7 +122,8 @@ typedef struct {
     int config_id;     /* index of the compiled kernel configuration */
     int tile_m, tile_n, tile_k;
     int threads;       /* per workgroup */
-    int vec_a, vec_b;  /* bytes per global load of A and of B rows */
+    int vec_a, vec_b;  /* bytes per global load of A and of B rows (16 for A
+                          when its rows are realigned first) */
     int even;          /* 1 when no edge masking is compiled in */
     int variant;       /* tiled kernels: 0 fully general (register-staged copies),
                           1 aligned LDS-ring kernel, 2/3 masked LDS-ring kernel
@@ -132,7 +136,8 @@ typedef struct {
     char name[48];     /* configuration name, as accepted by GEMM_FORCE_CONFIG */
     int64_t workspace_bytes; /* library-owned workspace the call needs: partial
                                 sums and arrival counters of the split small-M
-                                path; 0 for every other plan */
+                                path, or the realigned copy of A (batch x M
+                                rows of K rounded up to 8 bf16); else 0 */
 } gemm_plan;
 
 /* Operation selector for gemm_plan_query. */

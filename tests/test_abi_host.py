@@ -144,9 +144,15 @@ def test_selector_choices_for_the_workloads(L):
     # batched scores, K = 128 (4 stages): 128x128 tiles, two workgroups per CU
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 1024, 1024, 128, batch=32, c_type=1)
     assert st == 0 and p.name == b"bf16_128x128" and p.grid == 32 * 8 * 8 and p.variant == 1
-    # ragged: K=4100 bf16 rows are only 8-byte aligned -> masked variant
+    # ragged: K=4100 bf16 rows are only 8-byte aligned; the product is large,
+    # so A's rows are first copied to 4104-element (16-byte aligned) rows
+    # and the masked ring kernel copies A 16 bytes per lane (variant 2)
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 1000, 12280, 4100, c_type=1)
-    assert st == 0 and p.family == 2 and p.even == 0 and p.vec_a == 8 and p.vec_b == 16
+    assert st == 0 and p.family == 2 and p.even == 0 and p.vec_a == 16 and p.vec_b == 16
+    assert p.variant == 2 and p.workspace_bytes == 1000 * 4104 * 2
+    # a small product keeps A as it is (4-byte copies, variant 3)
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 300, 392, 262)
+    assert st == 0 and p.variant == 3 and p.vec_a == 4 and p.workspace_bytes == 0
     # every plan fits the 160 KiB LDS of a gfx950 CU
     for args in [(1024, 12288, 4096), (1000, 12280, 4100), (17, 33, 65)]:
         st, p = g5.plan_query(g5.GEMM_OP_BF16, *args)

@@ -277,6 +277,32 @@ def test_batched_attention_scores(oracle_mod):
         check_f32(host[b][rows], ref, 128, amax_bf16(Q[b]), amax_bf16(KT[b]), f"batch {b} rows")
 
 
+@pytest.mark.parametrize("M,N,K,pa,batch", [(520, 1024, 2050, 1, 1), (520, 1024, 2050, 2, 1),
+                                            (300, 1024, 2052, 2, 3), (512, 1024, 2048, 2, 1)])
+def test_bf16_realigned_rows(oracle_mod, M, N, K, pa, batch):
+    """Large products whose A rows are 2-, 4- or 8-byte aligned multiply
+    from a copy of A with 16-byte aligned rows (asserted through the plan).
+    A's padding holds NaN: a copy that read past K would poison C."""
+    _say(f"realigned A {batch}x{M}x{N}x{K} pad {pa}")
+    g = np.random.default_rng([M, N, K, pa, batch, 3])
+    A = gi.to_bf16_bits(gi.normal(g, (batch, M, K + pa)))
+    B = gi.to_bf16_bits(gi.normal(g, (batch, K, N), 0.125))
+    A[:, :, K:] = 0x7FC0
+    dA, dB = dev_bf16(A), dev_bf16(B)
+    C = torch.empty((batch, M, N), device="cuda", dtype=torch.float32)
+    st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K, batch=batch, lda=K + pa, a_addr=dA.data_ptr(),
+                             b_addr=dB.data_ptr(), c_addr=C.data_ptr(), sA=M * (K + pa), sB=K * N, sC=M * N,
+                             c_type=1)
+    assert st == 0 and plan.family == 2 and plan.vec_a == 16 and plan.variant in (1, 2), (plan.name, plan.variant)
+    assert plan.workspace_bytes == batch * M * ((K + 7) // 8 * 8) * 2
+    g5.gemm_bf16_batched(dA[:, :, :K], dB, C)
+    host = host_values(C)
+    for b in range(batch):
+        rows = np.arange(0, M, 7)
+        ref = oracle_mod.gemm_bf16(np.ascontiguousarray(A[b][rows, :K]), B[b])
+        check_f32(host[b][rows], ref, K, amax_bf16(A[b][:, :K]), amax_bf16(B[b]), f"realigned batch {b}")
+
+
 def test_ragged_single_gemm(oracle_mod):
     """M=1000, N=12280, K=4100 bf16 -> f32 (edge tiles in M and N, a K tail
     of 4, 8-byte aligned rows of A); also with bf16 output."""
