@@ -31,8 +31,8 @@ const ConfigInfo kConfigs[CFG_COUNT] = {
     {CFG_F32_128x128, GEMM_FAMILY_F32_MFMA, 128, 128, 32, 256, 2 * (128 * 32 + 32 * 132) * 4, "f32_128x128"},
     {CFG_F32_64x64, GEMM_FAMILY_F32_MFMA, 64, 64, 32, 256, 2 * (64 * 32 + 32 * 68) * 4, "f32_64x64"},
     {CFG_F32_32x32_WK, GEMM_FAMILY_F32_MFMA, 32, 32, 256, 256, 8 * (32 * 32 + 32 * 36) * 4, "f32_32x32_wholek"},
-    {CFG_DECODE_64, GEMM_FAMILY_DECODE, 16, 64, 32, 1024, 16 * 64 * 16 * 4, "decode_64"},
-    {CFG_DECODE_SPLIT, GEMM_FAMILY_DECODE, 16, 128, 32, 1024, 16 * 64 * 32 * 4 + 4, "decode_splitk"},
+    {CFG_DECODE_64, GEMM_FAMILY_DECODE, 16, 64, 32, 1024, 16 * 64 * 17 * 4, "decode_64"},
+    {CFG_DECODE_SPLIT, GEMM_FAMILY_DECODE, 16, 128, 32, 1024, 16 * 64 * 33 * 4 + 4, "decode_splitk"},
     {CFG_GENERIC, GEMM_FAMILY_GENERIC, 16, 16, 16, 256, 2 * 16 * 17 * 4, "generic"},
 };
 

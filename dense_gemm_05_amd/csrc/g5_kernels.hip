@@ -200,6 +200,19 @@ __device__ __forceinline__ int swz_a(int row) { return row & 7; }
 //  aligned group of 4 segments) with this function of k spreads the 8 rows
 //  {k0..k0+3, k0+8..k0+11} that 32 lanes read over distinct banks.
 __device__ __forceinline__ int swz_b(int k) { return ((((k >> 1) & 1) | (((k >> 3) & 1) << 1))) << 1; }
+//  The ring kernel's B slots: with BN = 192 the row pitch (384 bytes) puts
+//  consecutive rows half the banks apart, so swz_b suffices.  When the row
+//  pitch is a multiple of 256 bytes (BN % 128 == 0) every row starts on the
+//  same bank, so the 8 rows read together get 8 distinct 32-byte segments:
+//  chunk bits 1..3 are XORed with (k & 3) | ((k >> 3) & 1) << 2 (measured
+//  bank conflicts, as a share of LDS cycles, with 128x128 tiles: batched
+//  32 x 1024x1024x128 27% -> 0%, the FFN shape 40% -> 1.5%).
+template <int BN>
+__device__ __forceinline__ int swz_bn(int k)
+{
+    if constexpr (BN % 128 == 0) return ((k & 3) | (((k >> 3) & 1) << 2)) << 1;
+    else return swz_b(k);
+}
 
 // ===================================================== bf16 tiled MFMA kernel
 //
@@ -423,7 +436,7 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
 //    global chunk lands in its position.  Waves 0..3 copy A, 4..7 copy B.
 //  * A slot rows are 32 bf16 = 64 bytes (4 chunks), swizzled chunk ^
 //    ((row >> 1) & 3), measured conflict-free for the fragment reads; B slot
-//    rows are BN bf16, swizzled with swz_b, read with ds_read_b64_tr_b16.
+//    rows are BN bf16, swizzled with swz_bn, read with ds_read_b64_tr_b16.
 //  * Each wave waits for its own copies of the next stage (vmcnt counts
 //    the copies still allowed in flight), then one barrier per stage.  The
 //    loop is bounded by LDS traffic (copy writes plus fragment reads) and by
@@ -455,7 +468,7 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     static_assert(NWAVE == 8, "two waves per SIMD");
     static_assert(AV == 16 || AV == 4, "A copy width");
     static_assert(A_INS % A_W == 0 && B_INS % B_W == 0, "slab split");
-    static_assert((BN / 8) % 8 == 0, "B slot rows must be whole swizzle groups");
+    static_assert((BN / 8) % 8 == 0 && (BN % 128 != 0 || (BN / 8) % 16 == 0), "B slot rows must be whole swizzle groups");
     static_assert(NSA >= 3 && NSB >= 3 && LA * (NSA - 2) < 64 && LB * (NSB - 2) < 64, "vmcnt accounting");
     static_assert(TAIL > 0 && TAIL < NMFMA, "tail");
     __shared__ __attribute__((aligned(1024))) uint16_t smem[LDS_BYTES / 2];
@@ -497,7 +510,7 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     for (int j = 0; j < LB; ++j) {
         const int q = 1024 * (b_i0 + j) + 16 * lane;
         const int k = q / (BN * 2), pc = (q % (BN * 2)) / 16;
-        b_voff[j] = (uint32_t)((k * ldb + n0 + ((pc ^ swz_b(k)) * 8)) * 2);
+        b_voff[j] = (uint32_t)((k * ldb + n0 + ((pc ^ swz_bn<BN>(k)) * 8)) * 2);
     }
     // The stage's offset moves the descriptor base (scalar arithmetic) and
     // shrinks its extent to match, so the scalar offset stays 0.
@@ -531,8 +544,8 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         const int k = g * 8 + (li >> 2);
         const int ncol = wn * TN + fn * 16 + (li & 3) * 4;
         const int c = ncol >> 3, half = (ncol >> 2) & 1;
-        b_rd[fn] = k * BN + ((c ^ swz_b(k)) * 8) + half * 4;
-        b_rd4[fn] = (k + 4) * BN + ((c ^ swz_b(k + 4)) * 8) + half * 4;
+        b_rd[fn] = k * BN + ((c ^ swz_bn<BN>(k)) * 8) + half * 4;
+        b_rd4[fn] = (k + 4) * BN + ((c ^ swz_bn<BN>(k + 4)) * 8) + half * 4;
     }
     struct Frags {
         bf16x8 a[FM];
@@ -627,7 +640,7 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         for (int q = tid; q < BK * (BN / 8); q += NWAVE * 64) {
             const int k = q / (BN / 8), c = q % (BN / 8);
             const u32x4 v = load_chunk8_bf16(Bbat + (k0 + k) * ldb + n0, 8 * c, N - n0, k0 + k < K, p.align_b);
-            *(u32x4 *)(sB + k * BN + ((c ^ swz_b(k)) * 8)) = v;
+            *(u32x4 *)(sB + k * BN + ((c ^ swz_bn<BN>(k)) * 8)) = v;
         }
         __syncthreads();
         read_frags(f0, 0);
@@ -1024,17 +1037,20 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
     }
 
     // acc[b][q] of lane (g, li) is the partial C[li][n0 + 16 g + 4 q + b].
-    __shared__ float red[NW * 64 * 16];
-    float *mine = red + (wave * 64 + lane) * 16;
+    // Each lane's 16 partials go to LDS at a stride of 17 floats, so the 64
+    // lanes of one write instruction fall on 64 different banks.
+    constexpr int RS = 17;
+    __shared__ float red[NW * 64 * RS];
+    float *mine = red + (wave * 64 + lane) * RS;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int b = 0; b < 4; ++b) mine[q * 4 + b] = acc[b][q];
     __syncthreads();
     for (int t = tid; t < 64 * 16; t += NW * 64) {
-        float sum = 0.f;
-        for (int w2 = 0; w2 < NW; ++w2) sum += red[w2 * 64 * 16 + t];
         const int L = t >> 4, v = t & 15;
+        float sum = 0.f;
+        for (int w2 = 0; w2 < NW; ++w2) sum += red[(w2 * 64 + L) * RS + v];
         const int64_t m = L & 15;
         const int64_t n = n0 + 16 * (L >> 4) + v;
         if (m < M && n < N) {
@@ -1148,9 +1164,12 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode_sk(GemmArgs p, float *ws,
     }
 
     // acc[c][q] of lane (g, li) is the partial C[li][n0 + 32 g + 8 q + c].
-    __shared__ float red[NW * 64 * 32];
+    // Each lane's 32 partials go to LDS at a stride of 33 floats, so the 64
+    // lanes of one write instruction fall on 64 different banks.
+    constexpr int RS = 33;
+    __shared__ float red[NW * 64 * RS];
     __shared__ unsigned arrived;
-    float *mine = red + (wave * 64 + lane) * 32;
+    float *mine = red + (wave * 64 + lane) * RS;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -1160,9 +1179,9 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode_sk(GemmArgs p, float *ws,
     // Entry t: lane L = t / 32, q = (t / 8) % 4, c = t % 8 -> row L % 16,
     // column 32 (L / 16) + 8 q + c of the strip.
     for (int t = tid; t < 64 * 32; t += NW * 64) {
-        float sum = 0.f;
-        for (int w2 = 0; w2 < NW; ++w2) sum += red[w2 * 64 * 32 + t];
         const int L = t >> 5, q = (t >> 3) & 3, c = t & 7;
+        float sum = 0.f;
+        for (int w2 = 0; w2 < NW; ++w2) sum += red[(w2 * 64 + L) * RS + (t & 31)];
         const int m = L & 15, n = 32 * (L >> 4) + 8 * q + c;
         if (KS == 1) {
             if (m < M) {
