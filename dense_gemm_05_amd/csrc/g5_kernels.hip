@@ -1292,15 +1292,32 @@ __global__ void __launch_bounds__(256) k_generic(GemmArgs p)
 }
 
 // K == 0: C := 0 over batch x M x N (grid-stride).
+// Rows whose starts are 16-byte aligned are written in 16-byte chunks,
+// non-temporal (C is written once), with the columns past the last whole
+// chunk element by element; other rows element by element.
 __global__ void __launch_bounds__(256) k_zero(GemmArgs p)
 {
-    const int64_t total = p.batch * p.M * p.N;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-        const int64_t b = i / (p.M * p.N), r = i % (p.M * p.N);
-        const int64_t m = r / p.N, n = r % p.N;
+    const int esz = p.out_f32 ? 4 : 2;
+    const int64_t rows = p.batch * p.M;
+    const int64_t stride = (int64_t)gridDim.x * 256, first = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    auto elem = [&](int64_t r, int64_t n) {
+        const int64_t b = r / p.M, m = r % p.M;
         if (p.out_f32) ((float *)p.C + b * p.sC)[m * p.ldc + n] = 0.f;
         else ((uint16_t *)p.C + b * p.sC)[m * p.ldc + n] = 0;
+    };
+    int64_t done_cols = 0;                              // columns written as chunks
+    if (p.align_c >= 16) {
+        const int64_t per = 16 / esz, cpr = p.N / per;
+        done_cols = cpr * per;
+        for (int64_t q = first; q < rows * cpr; q += stride) {
+            const int64_t r = q / cpr, c = q % cpr;
+            const int64_t b = r / p.M, m = r % p.M;
+            char *dst = (char *)p.C + ((b * p.sC + m * p.ldc) * esz) + c * 16;
+            __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, (u32x4 *)dst);
+        }
     }
+    const int64_t rest = p.N - done_cols;
+    for (int64_t q = first; q < rows * rest; q += stride) elem(q / rest, done_cols + q % rest);
 }
 
 // ================================================================ launchers

@@ -345,6 +345,22 @@ def test_k_zero_writes_zeros():
     assert torch.count_nonzero(Cf).item() == 0
 
 
+@pytest.mark.parametrize("M,N,pad,batch,od", [(64, 1000, 8, 1, torch.float32), (64, 1000, 8, 1, torch.bfloat16),
+                                              (33, 37, 3, 2, torch.float32), (17, 129, 7, 3, torch.bfloat16),
+                                              (1024, 1024, 0, 4, torch.float32)])
+def test_k_zero_fill_shapes(M, N, pad, batch, od):
+    """K = 0 over aligned rows (16-byte chunks plus a column tail) and
+    unaligned rows (element stores): C[:, :N] becomes 0, the ldc padding
+    keeps its NaN."""
+    A = torch.empty((batch, M, 0), dtype=torch.bfloat16, device="cuda")
+    B = torch.empty((batch, 0, N), dtype=torch.bfloat16, device="cuda")
+    Cfull = torch.full((batch, M, N + pad), float("nan"), dtype=od, device="cuda")
+    g5.gemm_bf16_batched(A, B, Cfull[:, :, :N])
+    host = Cfull.float().cpu().numpy()
+    assert np.all(host[:, :, :N] == 0)
+    assert np.all(np.isnan(host[:, :, N:]))
+
+
 def test_empty_m_leaves_c_untouched():
     A = torch.empty((0, 9), dtype=torch.bfloat16, device="cuda")
     B = torch.ones((9, 4), dtype=torch.bfloat16, device="cuda")
