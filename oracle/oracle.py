@@ -23,7 +23,7 @@ def lib_path():
 def build(verbose=False):
     """Compile the oracle with gcc (-O2, OpenMP, no FP contraction)."""
     cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-           "-shared", "-fPIC", "-std=c11", "-Wall", "-o", _LIB + ".tmp", _SRC]
+           "-shared", "-fPIC", "-std=c11", "-Wall", "-o", _LIB + ".tmp", _SRC, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
@@ -48,6 +48,10 @@ def _load():
     lib.oracle_dot_f64_from_f32.argtypes = [i64, p, p, i64, i64]
     lib.oracle_dot_f64_from_f32.restype = ctypes.c_double
     lib.oracle_round_bf16_array.argtypes = [i64, p, p]
+    lib.oracle_round_bf16_d_array.argtypes = [i64, p, p]
+    lib.oracle_silu_array.argtypes = [i64, p, p]
+    lib.oracle_gemm_bf16_silu.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64]
+    lib.oracle_swiglu_bf16.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, p, p, i64]
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -138,6 +142,51 @@ def round_bf16(x):
     out = np.empty(x.shape, np.uint16)
     _load().oracle_round_bf16_array(x.size, x.ctypes.data, out.ctypes.data)
     return out
+
+
+def round_bf16_value(x):
+    """Nearest bf16 value (ties to even) of each double, as doubles."""
+    x = np.ascontiguousarray(np.asarray(x, np.float64))
+    out = np.empty(x.shape, np.float64)
+    _load().oracle_round_bf16_d_array(x.size, x.ctypes.data, out.ctypes.data)
+    return out
+
+
+def silu(x):
+    """SiLU(x) = x / (1 + e^-x), elementwise in double."""
+    x = np.ascontiguousarray(np.asarray(x, np.float64))
+    out = np.empty(x.shape, np.float64)
+    _load().oracle_silu_array(x.size, x.ctypes.data, out.ctypes.data)
+    return out
+
+
+def gemm_bf16_silu(A, B):
+    """Y = SiLU(round_bf16(A.B)) in double from bf16 bit patterns."""
+    A, lda = _rows(A, np.uint16)
+    B, ldb = _rows(B, np.uint16)
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    Y = np.empty((M, N), np.float64)
+    _load().oracle_gemm_bf16_silu(M, N, K, A.ctypes.data, lda, B.ctypes.data, ldb, Y.ctypes.data, max(N, 1))
+    return Y
+
+
+def swiglu_bf16(X, Wgu):
+    """SwiGLU on a merged [K, 2N] gate/up weight (gate in the first N
+    columns): returns (Z, g, u, t) in double, Z = t * u unrounded."""
+    X, ldx = _rows(X, np.uint16)
+    Wgu, ldw = _rows(Wgu, np.uint16)
+    M, K = X.shape
+    K2, N2 = Wgu.shape
+    if K != K2 or N2 % 2:
+        raise ValueError("expected X [M,K] and Wgu [K,2N]")
+    N = N2 // 2
+    Z, g, u, t = (np.empty((M, N), np.float64) for _ in range(4))
+    _load().oracle_swiglu_bf16(M, N, K, X.ctypes.data, ldx, Wgu.ctypes.data, ldw, Z.ctypes.data,
+                               g.ctypes.data, u.ctypes.data, t.ctypes.data, max(N, 1))
+    return Z, g, u, t
 
 
 def num_threads():

@@ -32,6 +32,7 @@
  * FP32 accumulator ("Operator & Runtime", §5.2.2 and §5.4.3); it is
  * written from the bit-level definition of that rounding.
  */
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 #include <stdlib.h>
@@ -139,6 +140,89 @@ uint16_t oracle_round_bf16(float x)
 void oracle_round_bf16_array(int64_t n, const float *x, uint16_t *out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_round_bf16(x[i]);
+}
+
+/* ---------------------------------------------------------------------
+ * Fused epilogues of page "Operator & Runtime": the activation of §5.4.2
+ * (Y = SiLU(A.W)) and the SwiGLU product of §5.3.1 (Z = SiLU(G) (.) U with
+ * G = X.W_g, U = X.W_u).  §5.4.3 requires the rounding of the unfused
+ * program to survive fusion: the FP32 product is rounded to bf16 before the
+ * activation.  For SwiGLU the unfused program keeps G, U and T = SiLU(G) as
+ * bf16 tensors, so each of them is rounded to bf16 once; the final output is
+ * returned unrounded (double), like every other reference here.
+ */
+
+/* Nearest bf16 value to a double, ties to even, returned as a double (no
+ * detour through binary32, which would round twice).  bf16 keeps 8
+ * significant bits with binary32's exponent range: normal numbers are
+ * rounded at 2^(e-7) for |x| in [2^e, 2^(e+1)); below 2^-126 the step is the
+ * fixed subnormal quantum 2^-133.  Values that round beyond the largest
+ * finite bf16, (2 - 2^-7) * 2^127, become infinities. */
+static double round_bf16_d(double x)
+{
+    if (x != x || x == 0.0) return x;
+    const double ax = fabs(x);
+    if (ax == INFINITY) return x;
+    double step;
+    if (ax < ldexp(1.0, -126)) {
+        step = ldexp(1.0, -133);
+    } else {
+        int e;
+        (void)frexp(ax, &e);            /* ax in [2^(e-1), 2^e) */
+        step = ldexp(1.0, e - 1 - 7);
+    }
+    const double r = nearbyint(x / step) * step;   /* exact scaling; ties to even */
+    if (fabs(r) > ldexp(2.0 - ldexp(1.0, -7), 127)) return x > 0 ? INFINITY : -INFINITY;
+    return r;
+}
+
+double oracle_round_bf16_d(double x) { return round_bf16_d(x); }
+
+/* SiLU(x) = x * sigmoid(x) = x / (1 + e^-x). */
+static double silu(double x) { return x / (1.0 + exp(-x)); }
+
+double oracle_silu(double x) { return silu(x); }
+
+void oracle_round_bf16_d_array(int64_t n, const double *x, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = round_bf16_d(x[i]);
+}
+
+void oracle_silu_array(int64_t n, const double *x, double *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = silu(x[i]);
+}
+
+/* Y[i][j] = SiLU(round_bf16(sum_k A[i][k] B[k][j])), bf16 inputs, double out. */
+void oracle_gemm_bf16_silu(int64_t M, int64_t N, int64_t K,
+                           const uint16_t *A, int64_t lda,
+                           const uint16_t *B, int64_t ldb,
+                           double *Y, int64_t ldy)
+{
+    oracle_gemm_f64_from_bf16(M, N, K, A, lda, B, ldb, Y, ldy);
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) Y[i * ldy + j] = silu(round_bf16_d(Y[i * ldy + j]));
+}
+
+/* SwiGLU on a merged gate/up weight: Wgu is [K][2N] with W_g in columns
+ * 0..N-1 and W_u in columns N..2N-1.  With G and U the double products,
+ * g = round_bf16(G), u = round_bf16(U), t = round_bf16(SiLU(g)) and
+ * Z = t * u (unrounded).  g, u and t are returned too ([M][N], ldz). */
+void oracle_swiglu_bf16(int64_t M, int64_t N, int64_t K,
+                        const uint16_t *X, int64_t ldx,
+                        const uint16_t *Wgu, int64_t ldw,
+                        double *Z, double *g, double *u, double *t, int64_t ldz)
+{
+    oracle_gemm_f64_from_bf16(M, N, K, X, ldx, Wgu, ldw, g, ldz);
+    oracle_gemm_f64_from_bf16(M, N, K, X, ldx, Wgu + N, ldw, u, ldz);
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            const int64_t o = i * ldz + j;
+            g[o] = round_bf16_d(g[o]);
+            u[o] = round_bf16_d(u[o]);
+            t[o] = round_bf16_d(silu(g[o]));
+            Z[o] = t[o] * u[o];
+        }
 }
 
 int oracle_num_threads(void)

@@ -1,0 +1,164 @@
+"""Pins for the oracle's fused-epilogue references (no GPU).
+
+Page "Operator & Runtime" fuses an activation into the GEMM's output tile
+(section 5.4.2, Y = SiLU(A.W)) and the SwiGLU product into the two
+projections that share X (section 5.3.1, Z = SiLU(G) (.) U), and requires
+the unfused program's rounding to survive: the FP32 product is rounded to
+bf16 before the activation (section 5.4.3).  Each pin below checks the
+oracle against something other than its own code: the value the page
+prints, identities of SiLU, exact integer products, the bit-level bf16
+rounding already pinned in test_oracle.py, and hand-worked bf16 values.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import gemm_inputs as gi
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bits(x):
+    return gi.to_bf16_bits(np.asarray(x, np.float32))
+
+
+# ---------------------------------------------------------------- SiLU
+
+def test_silu_page_example(oracle_mod):
+    """The page's pair of partial sums 1 and -1 (section 5.4.3)."""
+    with open(os.path.join(GOLDEN, "op_runtime_5_4_3_silu_partial_sums.txt")) as fh:
+        rows = [l for l in fh if l.strip() and not l.startswith("#")]
+    parts, full, page_value, decimals = [c.split() for c in rows[0].split(";")]
+    parts = [float(x) for x in parts]
+    assert oracle_mod.silu([sum(parts)])[0] == float(full[0])
+    s = float(oracle_mod.silu(parts).sum())
+    assert round(s, int(decimals[0])) == float(page_value[0])
+    # closed form: SiLU(1) + SiLU(-1) = sigmoid(1) - sigmoid(-1) = tanh(1/2)
+    assert abs(s - math.tanh(0.5)) < 1e-15
+
+
+def test_silu_identities(oracle_mod):
+    x = np.array([0.0, 0.25, 1.0, 3.5, 10.0, 37.0])
+    s_pos, s_neg = oracle_mod.silu(x), oracle_mod.silu(-x)
+    # SiLU(x) - SiLU(-x) = x sigmoid(x) + x sigmoid(-x) = x
+    assert np.allclose(s_pos - s_neg, x, rtol=0, atol=1e-14)
+    # SiLU(x) / x = sigmoid(x) = 1 / (1 + e^-x), which is 1/2 at 0 and tends to 1
+    assert oracle_mod.silu([0.0])[0] == 0.0
+    assert oracle_mod.silu([40.0])[0] == 40.0
+    assert -1e-15 < oracle_mod.silu([-40.0])[0] < 0
+    # the minimum of SiLU is about -0.2785 at x ~ -1.2785 (W(1/e) + 1)
+    xs = np.linspace(-3, 0, 30001)
+    m = oracle_mod.silu(xs)
+    assert abs(m.min() + 0.27846454) < 1e-7 and abs(xs[m.argmin()] + 1.2784645) < 1e-3
+
+
+# ---------------------------------------------------------------- bf16 of a double
+
+ROUND_D_CASES = [
+    (1 + 2 ** -8, 1.0, "tie rounds to the even neighbour (down)"),
+    (1 + 3 * 2 ** -8, 1 + 2 ** -6, "tie rounds to the even neighbour (up)"),
+    (1 + 2 ** -8 + 2 ** -40, 1 + 2 ** -7, "just above a tie rounds up (binary32 first would round twice)"),
+    (257.0, 256.0, "257 is a tie between 256 and 258"),
+    (-259.0, -260.0, "ties to even for negatives"),
+    (1.5 * 2 ** -130, 1.5 * 2 ** -130, "subnormal, exact"),
+    (2 ** -134, 0.0, "half the smallest subnormal rounds to zero (even)"),
+    (3 * 2 ** -134, 2 ** -132, "tie between 2^-133 and 2^-132 rounds to the even one"),
+    ((2 - 2 ** -8) * 2 ** 127, math.inf, "half an ulp above the largest finite value overflows"),
+    ((2 - 2 ** -7) * 2 ** 127, (2 - 2 ** -7) * 2 ** 127, "largest finite value"),
+]
+
+
+@pytest.mark.parametrize("x,want,why", ROUND_D_CASES, ids=[c[2] for c in ROUND_D_CASES])
+def test_round_bf16_value(oracle_mod, x, want, why):
+    assert oracle_mod.round_bf16_value([x])[0] == want, why
+
+
+def test_round_bf16_value_agrees_with_binary32_rounding(oracle_mod):
+    """For values that are exact in binary32, rounding the double must give
+    the bf16 that the (separately pinned) binary32 rounding gives."""
+    g = np.random.default_rng(11)
+    x = np.concatenate([g.standard_normal(20000) * 10.0 ** g.integers(-30, 30, 20000),
+                        [0.0, -0.0, 1e-40, -3e38]]).astype(np.float32)
+    want = (oracle_mod.round_bf16(x).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    got = oracle_mod.round_bf16_value(x.astype(np.float64))
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- Y = SiLU(A.W)
+
+def test_gemm_silu_exact_integers(oracle_mod):
+    """Small-integer operands: A.W is an exact integer product (checked with
+    numpy int64), bf16-representable here, so Y = SiLU(A.W) in double."""
+    g = np.random.default_rng(5)
+    A = g.integers(-3, 4, (7, 9)); W = g.integers(-3, 4, (9, 6))
+    C = A @ W                                     # int64, |C| <= 81
+    Y = oracle_mod.gemm_bf16_silu(bits(A), bits(W))
+    Cf = C.astype(np.float64)
+    assert np.allclose(Y, Cf / (1.0 + np.exp(-Cf)), rtol=1e-15, atol=0)
+
+
+def test_gemm_silu_rounds_before_the_activation(oracle_mod):
+    """A.W = 257 is not a bf16 value; the product is rounded (to 256) before
+    SiLU, as section 5.4.3 requires, so Y = SiLU(256) = 256, not 257."""
+    A = bits(np.ones((1, 257))); W = bits(np.ones((257, 1)))
+    assert oracle_mod.gemm_bf16_silu(A, W)[0, 0] == 256.0
+
+
+# ---------------------------------------------------------------- SwiGLU
+
+def _merged(Wg, Wu):
+    return np.ascontiguousarray(np.concatenate([Wg, Wu], axis=1))
+
+
+def test_swiglu_gate_and_up_halves(oracle_mod):
+    """X = [1, 1], gate column sums to 64 and up column to 2: SiLU(64) is 64
+    in bf16, so Z = 128.  Swapping gate and up would give
+    bf16(SiLU(2)) * 64 = 1.7578125 * 64 = 112.5."""
+    X = bits([[1.0, 1.0]])
+    Wg = bits([[32.0], [32.0]]); Wu = bits([[1.0], [1.0]])
+    Z, g, u, t = oracle_mod.swiglu_bf16(X, _merged(Wg, Wu))
+    assert (g[0, 0], u[0, 0], t[0, 0], Z[0, 0]) == (64.0, 2.0, 64.0, 128.0)
+    Zs, *_ = oracle_mod.swiglu_bf16(X, _merged(Wu, Wg))
+    assert Zs[0, 0] == 112.5
+
+
+def test_swiglu_rounds_the_activation(oracle_mod):
+    """g = 1, u = 3: SiLU(1) = 0.7310585... rounds to the bf16 value
+    0.73046875 (187 * 2^-8) before the product, so Z = 2.19140625 exactly
+    (without that rounding it would be 2.1931757...)."""
+    X = bits([[1.0]])
+    Z, g, u, t = oracle_mod.swiglu_bf16(X, _merged(bits([[1.0]]), bits([[3.0]])))
+    assert t[0, 0] == 187 * 2.0 ** -8 and Z[0, 0] == 2.19140625
+
+
+def test_swiglu_zero_gate_and_strided_weights(oracle_mod):
+    """A zero gate gives Z = 0 whatever U is; a merged weight with padded
+    rows (ldw > 2N) gives the same result as the unpadded one."""
+    g = np.random.default_rng(9)
+    X = bits(g.standard_normal((5, 16)))
+    Wg = bits(np.zeros((16, 4))); Wu = bits(g.standard_normal((16, 4)))
+    Z, *_ = oracle_mod.swiglu_bf16(X, _merged(Wg, Wu))
+    assert np.all(Z == 0)
+    Wg = bits(g.standard_normal((16, 4)))
+    W = _merged(Wg, Wu)
+    Wpad = np.zeros((16, 11), np.uint16); Wpad[:, :8] = W
+    Z1, *_ = oracle_mod.swiglu_bf16(X, W)
+    Z2, *_ = oracle_mod.swiglu_bf16(X, Wpad[:, :8])
+    assert np.array_equal(Z1, Z2)
+
+
+def test_swiglu_matches_its_parts(oracle_mod):
+    """Z equals the plain products of the two halves, each rounded to bf16,
+    through SiLU, rounded, and multiplied: assembled here from the separately
+    pinned product and rounding functions."""
+    g = np.random.default_rng(12)
+    X = bits(g.standard_normal((6, 40)))
+    Wg = bits(g.standard_normal((40, 5)) * 0.125); Wu = bits(g.standard_normal((40, 5)) * 0.125)
+    Z, gg, uu, tt = oracle_mod.swiglu_bf16(X, _merged(Wg, Wu))
+    G = oracle_mod.round_bf16_value(oracle_mod.gemm_bf16(X, Wg))
+    U = oracle_mod.round_bf16_value(oracle_mod.gemm_bf16(X, Wu))
+    T = oracle_mod.round_bf16_value(oracle_mod.silu(G))
+    assert np.array_equal(gg, G) and np.array_equal(uu, U) and np.array_equal(tt, T)
+    assert np.array_equal(Z, T * U)
