@@ -28,6 +28,7 @@ const ConfigInfo kConfigs[CFG_COUNT] = {
     {CFG_BF16_256x192, GEMM_FAMILY_BF16_MFMA, 256, 192, 64, 256, 2 * (256 * 64 + 64 * 192) * 2, "bf16_256x192"},
     {CFG_BF16_128x128, GEMM_FAMILY_BF16_MFMA, 128, 128, 64, 256, 2 * (128 * 64 + 64 * 128) * 2, "bf16_128x128"},
     {CFG_BF16_256x128, GEMM_FAMILY_BF16_MFMA, 256, 128, 64, 256, 2 * (256 * 64 + 64 * 128) * 2, "bf16_256x128"},
+    {CFG_BF16_256x256, GEMM_FAMILY_BF16_MFMA, 256, 256, 64, 256, 2 * (256 * 64 + 64 * 256) * 2, "bf16_256x256"},
     {CFG_F32_128x128, GEMM_FAMILY_F32_MFMA, 128, 128, 32, 256, 2 * (128 * 32 + 32 * 132) * 4, "f32_128x128"},
     {CFG_F32_64x64, GEMM_FAMILY_F32_MFMA, 64, 64, 32, 256, 2 * (64 * 32 + 32 * 68) * 4, "f32_64x64"},
     {CFG_F32_32x32_WK, GEMM_FAMILY_F32_MFMA, 32, 32, 256, 256, 8 * (32 * 32 + 32 * 36) * 4, "f32_32x32_wholek"},
@@ -40,6 +41,7 @@ const ConfigInfo kConfigs[CFG_COUNT] = {
 constexpr int kNumCU = 256;
 constexpr int64_t kLdsPerCU = 160 * 1024;
 constexpr double kHbmBytesPerS = 8.0e12;
+constexpr double kCopyBytesPerCUperS = 40.8e9;   // measured, LDS-ring kernels (see model_time)
 constexpr double kBf16FlopsPerCUperS = 2.5166e15 / kNumCU;
 constexpr double kF32FlopsPerCUperS = 157.3e12 / kNumCU;
 
@@ -123,35 +125,31 @@ int validate(const Problem &p)
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Workgroups of a config that fit on one CU at once (LDS-limited; every
-// tiled config here runs 4 waves per workgroup).
-int wg_per_cu(const ConfigInfo &c)
-{
-    if (c.lds_bytes <= 0) return 8;
-    int64_t n = kLdsPerCU / c.lds_bytes;
-    if (n < 1) n = 1;
-    if (c.family == GEMM_FAMILY_BF16_MFMA && c.tile_m * c.tile_n > 128 * 128) n = 1;  // 1 wave/SIMD (registers)
-    if (n > 2) n = 2;
-    return (int)n;
-}
-
-// Cost model of a tiled config (seconds): the slower of the matrix-core time
-// -- whole waves of tiles over the CUs, each tile padded to full size -- and
-// the interface traffic of "Operator & Runtime" §5.2.2 over HBM bandwidth,
-// divided by a relative efficiency measured per tile shape.
+// Cost model of a tiled config (seconds), page "Operator & Runtime" §5.4.5
+// (estimate first, then correct by measurement).  The interface traffic of
+// §5.2.2 -- every tile reads its A row panel and B column panel and writes
+// its C block -- is on gfx950 served mostly by the L2 and the Infinity Cache,
+// and what it limits is each CU's copy path: a tile's operand bytes pass
+// through one CU at the measured copy rate of the LDS-ring kernels (about
+// 41 GB/s per CU: 3.77 MB per 256x192 tile of the FFN projection in a
+// ~92 us main loop).  A CU that runs n tiles pays n times the slower of its
+// matrix-core time and its copy time; the whole call is never faster than
+// reading the operands and writing C once from HBM.  The result is divided
+// by a relative efficiency measured per tile shape.
 double model_time(const Problem &p, const ConfigInfo &c, double eff)
 {
     const int64_t tm = cdiv(p.M, c.tile_m), tn = cdiv(p.N, c.tile_n);
     const int64_t tiles = p.batch * tm * tn;
-    const int occ = wg_per_cu(c);
-    const int64_t waves = cdiv(tiles, (int64_t)kNumCU * occ);
+    const int64_t per_cu = cdiv(tiles, (int64_t)kNumCU);
     const double rate = (p.op == GEMM_OP_SGEMM ? kF32FlopsPerCUperS : kBf16FlopsPerCUperS);
     const double kpad = (double)cdiv(p.K, c.tile_k) * c.tile_k;
-    const double t_compute = (double)waves * occ * (2.0 * c.tile_m * c.tile_n * kpad) / rate;
-    const double bytes = p.batch * gemm_model_traffic_bytes(p.M, p.N, p.K, c.tile_m, c.tile_n, elem_a(p)) +
-                         (double)p.batch * p.M * p.N * (elem_c(p) - elem_a(p));
-    const double t_mem = bytes / kHbmBytesPerS;
-    return (t_compute > t_mem ? t_compute : t_mem) / eff;
+    const double t_mfma = (2.0 * c.tile_m * c.tile_n * kpad) / rate;
+    const double tile_bytes = (double)(c.tile_m + c.tile_n) * kpad * elem_a(p) + (double)c.tile_m * c.tile_n * elem_c(p);
+    const double t_copy = tile_bytes / kCopyBytesPerCUperS;
+    const double t_tiles = (double)per_cu * (t_mfma > t_copy ? t_mfma : t_copy);
+    const double once = (double)p.batch * ((double)elem_a(p) * (p.M * p.K + p.K * p.N) + (double)elem_c(p) * p.M * p.N);
+    const double t_hbm = once / kHbmBytesPerS;
+    return (t_tiles > t_hbm ? t_tiles : t_hbm) / eff;
 }
 
 int find_config_by_name(const char *name)
@@ -292,16 +290,23 @@ int select_plan(const Problem &p, Plan &pl)
             int id;
             double eff;
         };
-        static const Cand bf16c[] = {{CFG_BF16_256x192, 1.0}, {CFG_BF16_256x128, 0.95}, {CFG_BF16_128x128, 0.85}};
+        // 256x256 tiles move the fewest bytes per flop through the copy
+        // path and LDS, and carry the same measured per-flop rate as 256x192
+        // when the tile count fills whole waves: bf16 4096^3 116.6 us
+        // against 164.9 us for 256x192 (352 tiles, 2 waves); the FFN shape
+        // (192 tiles of 256x256, a 0.75 wave) 115.7 against 97.9 us.
+        static const Cand bf16c[] = {{CFG_BF16_256x192, 1.0}, {CFG_BF16_256x256, 1.0}, {CFG_BF16_256x128, 0.95},
+                                     {CFG_BF16_128x128, 0.85}};
         // With only a few 32-deep stages per tile, a tile's time is mostly
         // its first-load latency and its epilogue, which a second resident
         // workgroup per CU hides: the 128x128 ring kernel (64 KiB of LDS,
         // two per CU) measured 1.12x faster than 256x128 (96 KiB, one per
         // CU) on 32 x 1024x1024x128 with FP32 output.
-        static const Cand bf16_short_k[] = {{CFG_BF16_256x192, 0.7}, {CFG_BF16_256x128, 0.75}, {CFG_BF16_128x128, 1.0}};
+        static const Cand bf16_short_k[] = {{CFG_BF16_256x192, 0.7}, {CFG_BF16_256x256, 0.65}, {CFG_BF16_256x128, 0.75},
+                                            {CFG_BF16_128x128, 1.0}};
         static const Cand f32c[] = {{CFG_F32_128x128, 1.0}, {CFG_F32_64x64, 0.8}};
         const Cand *cands = p.op == GEMM_OP_BF16 ? (p.K <= 8 * 32 ? bf16_short_k : bf16c) : f32c;
-        const int nc = p.op == GEMM_OP_BF16 ? 3 : 2;
+        const int nc = p.op == GEMM_OP_BF16 ? 4 : 2;
         double best = 0.0;
         for (int i = 0; i < nc; ++i) {
             Plan trial = pl;

@@ -76,6 +76,7 @@ enum ConfigId {
     CFG_BF16_256x192,      // general kernel: 4 waves (2x2); ring kernels: 8 waves (2x4, wave tile 128x48)
     CFG_BF16_128x128,      // 4 waves (2x2), wave tile 64x64
     CFG_BF16_256x128,      // 4 waves (2x2), wave tile 128x64
+    CFG_BF16_256x256,      // general kernel: 4 waves (2x2); ring kernels: 8 waves (2x4, wave tile 128x64)
     CFG_F32_128x128,       // 4 waves (2x2), wave tile 64x64
     CFG_F32_64x64,         // 4 waves (2x2), wave tile 32x32
     CFG_F32_32x32_WK,      // 4 waves (2x2), wave tile 16x16, all of K (<= 256) staged at once

@@ -381,18 +381,22 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
     constexpr int NT = WGM * WGN * 64;
     constexpr int FITS = LDS_BYTES / PITCH;                  // rows that fit
     constexpr int RP = FITS >= BM ? BM : (FITS >= BM / 2 ? BM / 2 : BM / 4);
-    static_assert(RP % TM == 0 && RP * PITCH <= LDS_BYTES, "staging passes");
+    static_assert(RP % 16 == 0 && RP * PITCH <= LDS_BYTES, "staging passes");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
     const int g = lane >> 4, li = lane & 15;
     char *L = (char *)lds;
 #pragma unroll
     for (int pass = 0; pass < BM / RP; ++pass) {
-        if (wm * TM / RP == pass) {
+        // Each pass stages the 16-row accumulator blocks whose rows fall in
+        // it (a wave's rows span several passes when a pass is shorter than
+        // the wave tile).
+        if (wm * TM / RP <= pass && (wm * TM + TM - 1) / RP >= pass) {
 #pragma unroll
             for (int fn = 0; fn < NFN; ++fn)
 #pragma unroll
                 for (int fm = 0; fm < NFM; ++fm) {
+                    if ((wm * TM + fm * 16) / RP != pass) continue;
                     const int r = wm * TM + fm * 16 + li - pass * RP;
                     const int c = wn * TN + fn * 16 + g * 4;
                     const f32x4 v = acc[fn][fm];
@@ -1357,6 +1361,7 @@ hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, int 
     case CFG_BF16_256x192: return launch_bf16<256, 192, 2, 2, 2, 4, 4, 4>(a, variant, grid, s);
     case CFG_BF16_128x128: return launch_bf16<128, 128, 2, 2, 4, 2, 4, 4>(a, variant, grid, s);
     case CFG_BF16_256x128: return launch_bf16<256, 128, 2, 2, 4, 2, 4, 4>(a, variant, grid, s);
+    case CFG_BF16_256x256: return launch_bf16<256, 256, 2, 2, 2, 4, 4, 4>(a, variant, grid, s);
     case CFG_F32_128x128: return launch_f32<128, 128, 2, 2>(a, variant == 1, grid, s);
     case CFG_F32_64x64: return launch_f32<64, 64, 2, 2>(a, variant == 1, grid, s);
     case CFG_F32_32x32_WK:

@@ -133,6 +133,20 @@ def test_selector_choices_for_the_workloads(L):
     assert st == 0 and p.name == b"decode_64" and p.variant == 0 and p.workspace_bytes == 0
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 1, 32768, 4096)     # 256 strips: one slice, whole-K path
     assert st == 0 and p.name == b"decode_64"
+    # a bf16 4096^3 product: 256x256 tiles fill the 256 CUs exactly once
+    # (256x192 would need 352 tiles, two waves; measured 116.6 against
+    # 164.9 us); an output with too few large tiles for the 256 CUs takes
+    # 128x128 tiles, the least operand bytes per CU (2048x2048x8192: 93.7
+    # against 149.7 us with 256x192; the 1024x1536x4096 shard of an 8-way
+    # split FFN: 45.4 against 78.5 us)
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 4096, 4096, 4096)
+    assert st == 0 and p.name == b"bf16_256x256" and p.grid == 256 and p.variant == 1
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 8192, 4096, 2048)
+    assert st == 0 and p.name == b"bf16_256x256" and p.grid == 512
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 2048, 2048, 8192)
+    assert st == 0 and p.name == b"bf16_128x128" and p.grid == 256
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 1024, 1536, 4096)
+    assert st == 0 and p.name == b"bf16_128x128" and p.grid == 96
     st, p = g5.plan_query(g5.GEMM_OP_SGEMM, 4096, 4096, 4096)
     assert st == 0 and p.family == 3 and p.even == 1
     # FP32 256^3: 32x32 tiles with all of K staged at once; K = 288 (9 slabs)

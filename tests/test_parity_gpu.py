@@ -106,7 +106,7 @@ def test_bf16_ragged(oracle_mod, M, N, K, out):
         check_f32(host_values(C), ref, K, amax_bf16(A), amax_bf16(B), f"bf16->f32 {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("cfg", ["bf16_256x192", "bf16_128x128", "bf16_256x128", "generic",
+@pytest.mark.parametrize("cfg", ["bf16_256x192", "bf16_128x128", "bf16_256x128", "bf16_256x256", "generic",
                                  "decode_64"])
 def test_bf16_every_config(oracle_mod, monkeypatch, cfg):
     """Each compiled configuration, forced, on a ragged problem with padded
@@ -173,6 +173,25 @@ def test_ffn_projection_full_size(oracle_mod):
     ref = oracle_mod.gemm_bf16(np.ascontiguousarray(X[rows]), W)
     got = host_values(C)[rows]
     check_bf16(got, ref, 4096, "FFN rows")
+
+
+@pytest.mark.parametrize("M,N,K,cfg", [(4096, 4096, 4096, b"bf16_256x256"), (2048, 2048, 8192, b"bf16_128x128")])
+def test_large_bf16_products_sampled(oracle_mod, M, N, K, cfg):
+    """Large bf16 products on the tile shapes the selector gives them
+    (256x256 tiles for a 4096^3 product, 128x128 tiles for an output too
+    small to fill the CUs with large tiles); rows from every row tile,
+    both edges of each, all columns."""
+    _say(f"bf16 {M}x{N}x{K} sampled rows ({cfg.decode()})")
+    st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
+    assert st == 0 and plan.name == cfg, plan.name
+    g = np.random.default_rng(M + N + K)
+    A = gi.to_bf16_bits(gi.normal(g, (M, K)))
+    B = gi.to_bf16_bits(gi.normal(g, (K, N), 0.125))
+    C = g5.gemm_bf16(dev_bf16(A), dev_bf16(B))
+    tile = plan.tile_m
+    rows = np.unique(np.concatenate([np.arange(0, M, tile), np.arange(tile - 1, M, tile), np.arange(7, M, 301)]))
+    ref = oracle_mod.gemm_bf16(np.ascontiguousarray(A[rows]), B)
+    check_bf16(host_values(C)[rows], ref, K, f"bf16 {M}x{N}x{K} rows")
 
 
 @pytest.mark.parametrize("M", [1, 4, 16])
