@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "sgemm", "batched", "ragged", "copy"])
+    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "sgemm", "batched", "ragged", "swiglu", "copy"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--prewarm-seconds", type=float, default=1.0,
@@ -260,6 +260,34 @@ def main():
         workloads.append({"name": "ragged_bf16_1000x12280x4100_f32out", "us": round(ms * 1e3, 3),
                           "tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "rotations": R})
         del dA, dB, dC
+
+    # ------------------------------------------------------------ fused SwiGLU FFN
+    if args.only in ("all", "swiglu"):
+        # The FFN's gate and up projections of X with one merged weight
+        # [4096, 2 x 12288] and the SwiGLU product in the epilogue, next to
+        # the same two projections as plain calls (bf16 g and u written out).
+        M, N, K = 1024, 12288, 4096
+        X, Wgu = gi.swiglu_inputs(M, K, N)
+        alg_bytes = 2 * (M * K + K * 2 * N + M * N)
+        R = rotations(alg_bytes)
+        dX = [to_dev_bf16(X) for _ in range(R)]
+        dW = [to_dev_bf16(Wgu) for _ in range(R)]
+        dZ = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        dG = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        dU = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        fused = [(lambda i=i: g5.gemm_bf16_swiglu(dX[i], dW[i], dZ[i])) for i in range(R)]
+        plain = [(lambda i=i: (g5.gemm_bf16(dX[i], dW[i][:, :N], dG[i]), g5.gemm_bf16(dX[i], dW[i][:, N:], dU[i])))
+                 for i in range(R)]
+        ms = timed(fused, 30, 5)
+        ms_plain = timed(plain, 30, 5)
+        flops = 2.0 * 2 * M * N * K
+        tf = flops / (ms * 1e-3) / 1e12
+        log(f"swiglu FFN 1024x(2x12288)x4096: fused {ms * 1e3:.2f} us ({tf:.1f} TFLOPS); "
+            f"two plain projections {ms_plain * 1e3:.2f} us")
+        workloads.append({"name": "swiglu_ffn_bf16_1024x2x12288x4096", "us": round(ms * 1e3, 3),
+                          "tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                          "two_plain_projections_us": round(ms_plain * 1e3, 3), "rotations": R})
+        del dX, dW, dZ, dG, dU
 
     out["workloads"] = workloads
 

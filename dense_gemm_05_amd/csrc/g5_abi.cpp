@@ -78,6 +78,18 @@ int decode_slices(int64_t strips, int64_t K)
 }
 
 int elem_a(const Problem &p) { return p.op == GEMM_OP_SGEMM ? 4 : 2; }
+// Fused epilogue of an operation (EPI_NONE for the plain products).
+int epi_of(const Problem &p)
+{
+    return p.op == GEMM_OP_BF16_SILU ? EPI_SILU : p.op == GEMM_OP_BF16_SWIGLU ? EPI_SWIGLU : EPI_NONE;
+}
+// Columns of B: the merged gate|up weight of SwiGLU has 2N.
+int64_t b_cols(const Problem &p) { return p.op == GEMM_OP_BF16_SWIGLU ? 2 * p.N : p.N; }
+// Output columns per tile of a tiled config (SwiGLU: half the B columns).
+int64_t out_tile_n(const Problem &p, const ConfigInfo &c)
+{
+    return p.op == GEMM_OP_BF16_SWIGLU ? c.tile_n / 2 : c.tile_n;
+}
 int elem_c(const Problem &p) { return (p.op == GEMM_OP_SGEMM || p.c_type == GEMM_OUT_F32) ? 4 : 2; }
 
 // Largest power of two <= 16 dividing the address of every row start of an
@@ -104,10 +116,12 @@ bool overlap(const Range &x, const Range &y) { return x.lo < y.hi && y.lo < x.hi
 
 int validate(const Problem &p)
 {
-    if (p.op != GEMM_OP_SGEMM && p.op != GEMM_OP_BF16) return GEMM_ERR_INVALID_ARG;
+    if (p.op != GEMM_OP_SGEMM && p.op != GEMM_OP_BF16 && p.op != GEMM_OP_BF16_SILU && p.op != GEMM_OP_BF16_SWIGLU)
+        return GEMM_ERR_INVALID_ARG;
     if (p.batch < 0 || p.M < 0 || p.N < 0 || p.K < 0) return GEMM_ERR_INVALID_ARG;
     if (p.op == GEMM_OP_BF16 && p.c_type != GEMM_OUT_BF16 && p.c_type != GEMM_OUT_F32)
         return GEMM_ERR_INVALID_ARG;
+    if (epi_of(p) != EPI_NONE && (p.c_type != GEMM_OUT_BF16 || p.batch > 1)) return GEMM_ERR_INVALID_ARG;
     if (p.sA < 0 || p.sB < 0 || p.sC < 0) return GEMM_ERR_INVALID_ARG;
     if (p.batch == 0 || p.M == 0 || p.N == 0) return GEMM_OK;  // nothing to do
     if (p.ldc < p.N || p.c == 0) return GEMM_ERR_INVALID_ARG;
@@ -115,9 +129,9 @@ int validate(const Problem &p)
     const Range rc = extent(p.c, p.batch, p.M, p.N, p.ldc, p.sC, elem_c(p));
     if (rc.hi > ((__int128)1 << 63)) return GEMM_ERR_INVALID_ARG;
     if (p.K == 0) return GEMM_OK;
-    if (p.lda < p.K || p.ldb < p.N || p.a == 0 || p.b == 0) return GEMM_ERR_INVALID_ARG;
+    if (p.lda < p.K || p.ldb < b_cols(p) || p.a == 0 || p.b == 0) return GEMM_ERR_INVALID_ARG;
     const Range ra = extent(p.a, p.batch, p.M, p.K, p.lda, p.sA, elem_a(p));
-    const Range rb = extent(p.b, p.batch, p.K, p.N, p.ldb, p.sB, elem_a(p));
+    const Range rb = extent(p.b, p.batch, p.K, b_cols(p), p.ldb, p.sB, elem_a(p));
     if (ra.hi > ((__int128)1 << 63) || rb.hi > ((__int128)1 << 63)) return GEMM_ERR_INVALID_ARG;
     if (overlap(rc, ra) || overlap(rc, rb)) return GEMM_ERR_INVALID_ARG;
     return GEMM_OK;
@@ -138,16 +152,18 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // by a relative efficiency measured per tile shape.
 double model_time(const Problem &p, const ConfigInfo &c, double eff)
 {
-    const int64_t tm = cdiv(p.M, c.tile_m), tn = cdiv(p.N, c.tile_n);
+    const int64_t tm = cdiv(p.M, c.tile_m), tn = cdiv(p.N, out_tile_n(p, c));
     const int64_t tiles = p.batch * tm * tn;
     const int64_t per_cu = cdiv(tiles, (int64_t)kNumCU);
     const double rate = (p.op == GEMM_OP_SGEMM ? kF32FlopsPerCUperS : kBf16FlopsPerCUperS);
     const double kpad = (double)cdiv(p.K, c.tile_k) * c.tile_k;
     const double t_mfma = (2.0 * c.tile_m * c.tile_n * kpad) / rate;
-    const double tile_bytes = (double)(c.tile_m + c.tile_n) * kpad * elem_a(p) + (double)c.tile_m * c.tile_n * elem_c(p);
+    const double tile_bytes =
+        (double)(c.tile_m + c.tile_n) * kpad * elem_a(p) + (double)c.tile_m * out_tile_n(p, c) * elem_c(p);
     const double t_copy = tile_bytes / kCopyBytesPerCUperS;
     const double t_tiles = (double)per_cu * (t_mfma > t_copy ? t_mfma : t_copy);
-    const double once = (double)p.batch * ((double)elem_a(p) * (p.M * p.K + p.K * p.N) + (double)elem_c(p) * p.M * p.N);
+    const double once =
+        (double)p.batch * ((double)elem_a(p) * (p.M * p.K + p.K * b_cols(p)) + (double)elem_c(p) * p.M * p.N);
     const double t_hbm = once / kHbmBytesPerS;
     return (t_tiles > t_hbm ? t_tiles : t_hbm) / eff;
 }
@@ -159,9 +175,13 @@ int find_config_by_name(const char *name)
     return -1;
 }
 
+// Configurations compiled with the fused epilogues.
+bool has_epilogues(int id) { return id == CFG_BF16_256x192 || id == CFG_BF16_256x256 || id == CFG_BF16_128x128; }
+
 bool config_fits(const Problem &p, int id)
 {
     const ConfigInfo &c = kConfigs[id];
+    if (epi_of(p) != EPI_NONE) return has_epilogues(id);
     switch (c.family) {
     case GEMM_FAMILY_BF16_MFMA: return p.op == GEMM_OP_BF16;
     case GEMM_FAMILY_F32_MFMA: return p.op == GEMM_OP_SGEMM;
@@ -193,7 +213,7 @@ void fill_grid(const Problem &p, Plan &pl)
         break;
     default:
         pl.tiles_m = cdiv(p.M, c.tile_m);
-        pl.tiles_n = cdiv(p.N, c.tile_n);
+        pl.tiles_n = cdiv(p.N, out_tile_n(p, c));
         pl.grid = p.batch * pl.tiles_m * pl.tiles_n;
         break;
     }
@@ -232,14 +252,14 @@ int pick_variant(const Problem &p, const Plan &pl, bool *even)
     }
     if (c.family != GEMM_FAMILY_BF16_MFMA) return 0;
     const __int128 a_bytes = ((__int128)(p.M - 1) * p.lda + p.K) * 2;
-    const __int128 b_bytes = ((__int128)(p.K - 1) * p.ldb + p.N) * 2;
+    const __int128 b_bytes = ((__int128)(p.K - 1) * p.ldb + b_cols(p)) * 2;
     const bool fits = a_bytes < ((__int128)1 << 31) && b_bytes < ((__int128)1 << 31);
     // N % 8: every 16-byte chunk of B lies wholly inside or wholly past the
     // descriptor extent (no partially out-of-range copies).
     if (!fits || pl.align_b < 16 || pl.align_a < 4 || p.N % 8 != 0) return 0;
     const int ring_k = 32;
     const bool c_ok = pl.align_c >= (elem_c(p) == 4 ? 16 : 8);
-    *even = !(p.M % c.tile_m || p.N % c.tile_n || p.K % ring_k) && pl.align_a >= 16 && c_ok;
+    *even = !(p.M % c.tile_m || p.N % out_tile_n(p, c) || p.K % ring_k) && pl.align_a >= 16 && c_ok;
     if (*even) return 1;
     return pl.align_a >= 16 ? 2 : 3;
 }
@@ -262,6 +282,9 @@ int select_plan(const Problem &p, Plan &pl)
         return GEMM_OK;
     }
 
+    // The fused epilogues run in the LDS-staged store of the ring kernels:
+    // 16-byte aligned output rows and whole 16-byte output chunks.
+    if (epi_of(p) != EPI_NONE && (pl.align_c < 16 || p.N % 8 != 0)) return GEMM_ERR_UNSUPPORTED;
     const char *force = std::getenv("GEMM_FORCE_CONFIG");
     if (force && *force) {
         const int id = find_config_by_name(force);
@@ -305,10 +328,12 @@ int select_plan(const Problem &p, Plan &pl)
         static const Cand bf16_short_k[] = {{CFG_BF16_256x192, 0.7}, {CFG_BF16_256x256, 0.65}, {CFG_BF16_256x128, 0.75},
                                             {CFG_BF16_128x128, 1.0}};
         static const Cand f32c[] = {{CFG_F32_128x128, 1.0}, {CFG_F32_64x64, 0.8}};
-        const Cand *cands = p.op == GEMM_OP_BF16 ? (p.K <= 8 * 32 ? bf16_short_k : bf16c) : f32c;
-        const int nc = p.op == GEMM_OP_BF16 ? 4 : 2;
+        const bool bf16 = p.op != GEMM_OP_SGEMM;
+        const Cand *cands = bf16 ? (p.K <= 8 * 32 ? bf16_short_k : bf16c) : f32c;
+        const int nc = bf16 ? 4 : 2;
         double best = 0.0;
         for (int i = 0; i < nc; ++i) {
+            if (!config_fits(p, cands[i].id)) continue;
             Plan trial = pl;
             trial.config = cands[i].id;
             bool ev = false;
@@ -330,8 +355,10 @@ int select_plan(const Problem &p, Plan &pl)
     // from a copy of A with aligned rows when that lets the ring kernel copy
     // A 16 bytes per lane (the copy costs 2 x M x K x 2 bytes of traffic,
     // small next to the product from 2^30 multiply-adds on).
+    // The fused epilogues exist only in the ring kernels, so a fused call
+    // whose A rows no ring variant takes is realigned at any size.
     if (kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && pl.align_a < 16 &&
-        (double)p.batch * p.M * p.N * p.K >= (double)(1 << 30)) {
+        ((double)p.batch * p.M * p.N * p.K >= (double)(1 << 30) || (epi_of(p) != EPI_NONE && pl.variant == 0))) {
         Problem q = p;
         q.lda = (p.K + 7) / 8 * 8;
         q.sA = p.M * q.lda;
@@ -347,6 +374,8 @@ int select_plan(const Problem &p, Plan &pl)
             pl.even = ev;
         }
     }
+    // fused epilogues exist in the ring kernels only (variants 1-3)
+    if (epi_of(p) != EPI_NONE && pl.config != CFG_ZERO && pl.variant == 0) return GEMM_ERR_UNSUPPORTED;
     return GEMM_OK;
 }
 
@@ -535,6 +564,7 @@ int run(const Problem &p, void *stream)
             pl.align_a = row_alignment(p.a, p.lda, p.sA, p.batch, 2);
             pl.variant = pick_variant(p, pl, &pl.even);
             a.align_a = pl.align_a;
+            if (epi_of(p) != EPI_NONE && pl.variant == 0) return GEMM_ERR_UNSUPPORTED;
         }
     }
     if (pl.config == CFG_DECODE_SPLIT) {
@@ -554,7 +584,9 @@ int run(const Problem &p, void *stream)
         pl.variant = pick_variant(p, pl, &pl.even);
         a.tiles_n = pl.tiles_n;
     }
-    const hipError_t e = launch_config(pl.config, p.op == GEMM_OP_SGEMM, a, pl.variant, pl.grid, (hipStream_t)stream);
+    const hipError_t e = pl.config == CFG_ZERO || epi_of(p) == EPI_NONE
+                             ? launch_config(pl.config, p.op == GEMM_OP_SGEMM, a, pl.variant, pl.grid, (hipStream_t)stream)
+                             : launch_fused(pl.config, epi_of(p), a, pl.variant, pl.grid, (hipStream_t)stream);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
@@ -590,6 +622,22 @@ int gemm_bf16_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const uint
     return g5::run(p, stream);
 }
 
+int gemm_bf16_silu(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                   uint16_t *C, int64_t ldc, void *stream)
+{
+    const Problem p{GEMM_OP_BF16_SILU, 1, M, N, K, (uint64_t)A, (uint64_t)B, (uint64_t)C, lda, ldb, ldc, 0, 0, 0,
+                    GEMM_OUT_BF16};
+    return g5::run(p, stream);
+}
+
+int gemm_bf16_swiglu(int64_t M, int64_t N, int64_t K, const uint16_t *X, int64_t ldx, const uint16_t *Wgu,
+                     int64_t ldw, uint16_t *Z, int64_t ldz, void *stream)
+{
+    const Problem p{GEMM_OP_BF16_SWIGLU, 1, M, N, K, (uint64_t)X, (uint64_t)Wgu, (uint64_t)Z, ldx, ldw, ldz, 0, 0,
+                    0, GEMM_OUT_BF16};
+    return g5::run(p, stream);
+}
+
 const char *gemm_status_string(int status)
 {
     switch (status) {
@@ -607,7 +655,9 @@ int gemm_plan_query(int op, int64_t batch, int64_t M, int64_t N, int64_t K, uint
                     int64_t strideC, int c_type, gemm_plan *out)
 {
     const Problem p{op, batch, M, N, K, a_addr, b_addr, c_addr, lda, ldb, ldc, strideA, strideB, strideC,
-                    op == GEMM_OP_SGEMM ? (int)GEMM_OUT_F32 : c_type};
+                    op == GEMM_OP_SGEMM ? (int)GEMM_OUT_F32
+                    : (op == GEMM_OP_BF16_SILU || op == GEMM_OP_BF16_SWIGLU) ? (int)GEMM_OUT_BF16
+                                                                              : c_type};
     int st = g5::validate(p);
     if (st != GEMM_OK) return st;
     g5::Plan pl;

@@ -68,6 +68,9 @@ struct GemmArgs {
     int32_t out_f32;         // 1: C is float, 0: C is bf16 bits
 };
 
+// Fused epilogues of the bf16 ring kernels.
+enum Epilogue { EPI_NONE = 0, EPI_SILU = 1, EPI_SWIGLU = 2 };
+
 // Compiled configurations.  The selector picks one; GEMM_FORCE_CONFIG may
 // name one explicitly.
 enum ConfigId {

@@ -15,6 +15,12 @@ namespace g5 {
 hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, int variant, int64_t grid,
                          hipStream_t s);
 
+// The same for a bf16 product with a fused epilogue (EPI_SILU or
+// EPI_SWIGLU; ring kernel variants 1-3 of the configs 256x192, 256x256 and
+// 128x128, with a.tiles_n counting output tiles of tile_n / 2 columns for
+// EPI_SWIGLU).
+hipError_t launch_fused(int config_id, int epi, const GemmArgs &a, int variant, int64_t grid, hipStream_t s);
+
 // Small-M path with K split over `ks` workgroups per 128-column strip
 // (a.tiles_n strips): `ws` holds batch x strips x ks x 16 x 128 floats of
 // partial sums, `cnt` batch x strips counters that are zero on entry and

@@ -54,6 +54,36 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return bf16_rne(lo) | (bf16_rne(hi) << 16);
 }
 
+// SiLU(x) = x * sigmoid(x) = x / (1 + e^-x), in FP32 ("Operator & Runtime"
+// §5.4.2 fuses it into the output tile), with the hardware reciprocal (about
+// 1 ulp, far below the bf16 rounding that follows).  Large negative x gives
+// e^-x = inf and a result of -0.
+__device__ __forceinline__ float silu_f32(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Fused epilogues of a bf16 output chunk (8 values, already rounded once to
+// bf16 from the FP32 sums: the rounding of the unfused program survives,
+// §5.4.3).  SiLU: y = bf16(SiLU(g)).  SwiGLU (§5.3.1): z = bf16(t * u) with
+// t = bf16(SiLU(g)); t and u are bf16, so t * u is exact in FP32 and z is
+// rounded once.
+__device__ __forceinline__ u32x4 epi_silu8(u32x4 g)
+{
+    u32x4 y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = pack_bf16x2(silu_f32(bf16_lo(g[i])), silu_f32(bf16_hi(g[i])));
+    return y;
+}
+__device__ __forceinline__ u32x4 epi_swiglu8(u32x4 g, u32x4 u)
+{
+    const u32x4 t = epi_silu8(g);
+    u32x4 z;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        z[i] = pack_bf16x2(bf16_lo(t[i]) * bf16_lo(u[i]), bf16_hi(t[i]) * bf16_hi(u[i]));
+    return z;
+}
+
 // Load 8 consecutive bf16 elements (one 16-byte chunk) starting at element
 // `col` of a row, zero for elements at or beyond `limit` or when the row is
 // out of range.  `align` is the byte alignment of the row start (16/8/4/2);
@@ -370,10 +400,12 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 1) k_bf16_mfma(GemmArgs p)
 // LDS_BYTES; every wave must have finished with it.  MASKED: only chunks of
 // rows < M that end at or before column N are stored (N must be a multiple
 // of the chunk's 16 / sizeof(TOut) elements, so no chunk straddles it).
-template <int BM, int BN, int WGM, int WGN, int LDS_BYTES, typename TOut, bool MASKED, int NFN, int NFM>
+template <int BM, int BN, int WGM, int WGN, int LDS_BYTES, typename TOut, bool MASKED, int EPI = EPI_NONE, int NFN,
+          int NFM>
 __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM], uint16_t *lds, void *Cb,
                                                    int64_t ldc, int64_t m0, int64_t n0, int64_t M, int64_t N)
 {
+    static_assert(EPI == EPI_NONE || sizeof(TOut) == 2, "fused epilogues write bf16");
     constexpr int TM = BM / WGM, TN = BN / WGN;
     constexpr int ESZ = (int)sizeof(TOut);
     constexpr int PITCH = BN * ESZ + 16;                     // bytes per staged row
@@ -409,12 +441,27 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
                 }
         }
         __syncthreads();
-        for (int q = tid; q < RP * CPR; q += NT) {
-            const int r = q / CPR, c = q % CPR;
-            if (MASKED && (m0 + pass * RP + r >= M || n0 + (int64_t)(c + 1) * (16 / ESZ) > N)) continue;
-            const u32x4 v = *(const u32x4 *)(L + r * PITCH + c * 16);
-            char *dst = (char *)Cb + ((m0 + pass * RP + r) * ldc + n0) * ESZ + c * 16;
-            __builtin_nontemporal_store(v, (u32x4 *)dst);     // C is written once
+        if constexpr (EPI == EPI_SWIGLU) {
+            // Tile columns [0, BN/2) hold the gate product g, [BN/2, BN) the
+            // up product u of the same BN/2 output columns starting at n0.
+            constexpr int OPR = CPR / 2;                     // output chunks per row
+            for (int q = tid; q < RP * OPR; q += NT) {
+                const int r = q / OPR, c = q % OPR;
+                if (MASKED && (m0 + pass * RP + r >= M || n0 + (int64_t)(c + 1) * 8 > N)) continue;
+                const u32x4 g = *(const u32x4 *)(L + r * PITCH + c * 16);
+                const u32x4 u = *(const u32x4 *)(L + r * PITCH + (c + OPR) * 16);
+                char *dst = (char *)Cb + ((m0 + pass * RP + r) * ldc + n0) * 2 + c * 16;
+                __builtin_nontemporal_store(epi_swiglu8(g, u), (u32x4 *)dst);
+            }
+        } else {
+            for (int q = tid; q < RP * CPR; q += NT) {
+                const int r = q / CPR, c = q % CPR;
+                if (MASKED && (m0 + pass * RP + r >= M || n0 + (int64_t)(c + 1) * (16 / ESZ) > N)) continue;
+                u32x4 v = *(const u32x4 *)(L + r * PITCH + c * 16);
+                if constexpr (EPI == EPI_SILU) v = epi_silu8(v);
+                char *dst = (char *)Cb + ((m0 + pass * RP + r) * ldc + n0) * ESZ + c * 16;
+                __builtin_nontemporal_store(v, (u32x4 *)dst);     // C is written once
+            }
         }
         __syncthreads();
     }
@@ -453,7 +500,13 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
 //    only feed outputs that are never stored.  A K remainder (K % 32) is a
 //    final stage loaded element by element with zero fill ("4.1" §4.5 and
 //    "Operator & Runtime" §5.4.2: out-of-range elements contribute zero).
-template <int BM, int BN, int WGM, int WGN, int NSA, int NSB, int AV, bool MASKED>
+//  * EPI: EPI_SILU applies SiLU to each bf16-rounded output; EPI_SWIGLU
+//    multiplies a merged gate|up weight B = [W_g | W_u] ([K, 2N]): the
+//    tile's B slab takes its first BN/2 columns from W_g and the last BN/2
+//    from the same columns of W_u, and the epilogue combines the two halves
+//    into BN/2 columns of Z = bf16(bf16(SiLU(g)) * u).  Both need the
+//    LDS-staged epilogue (16-byte aligned output rows, N % 8 == 0).
+template <int BM, int BN, int WGM, int WGN, int NSA, int NSB, int AV, bool MASKED, int EPI = EPI_NONE>
 __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
 {
     constexpr int NWAVE = WGM * WGN;
@@ -482,14 +535,20 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     const int wm = wave / WGN, wn = wave % WGN;
     const int g = lane >> 4, li = lane & 15;
 
+    constexpr bool GLU = EPI == EPI_SWIGLU;
+    constexpr int HALF = BN / 2;                              // GLU: columns per weight half
+    static_assert(!GLU || HALF % 8 == 0, "GLU halves must be whole chunks");
     const TileCoord tc = tile_map(blockIdx.x, p.batch, p.tiles_m, p.tiles_n, p.group_m);
-    const int64_t m0 = tc.tm * BM, n0 = tc.tn * BN;
+    // n0: first output column (GLU: first column of each weight half)
+    const int64_t m0 = tc.tm * BM, n0 = tc.tn * (GLU ? HALF : BN);
     const int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
     const uint16_t *Abat = (const uint16_t *)p.A + tc.b * p.sA;
     const uint16_t *Bbat = (const uint16_t *)p.B + tc.b * p.sB;
     // Byte extents of this batch entry's operands (reads past them return 0).
     const uint32_t a_bytes = MASKED ? (uint32_t)(((M - 1) * lda + K) * 2) : 0x7fffffffu;
-    const uint32_t b_bytes = MASKED ? (uint32_t)(((K - 1) * ldb + N) * 2) : 0x7fffffffu;
+    const uint32_t b_bytes = MASKED ? (uint32_t)(((K - 1) * ldb + (GLU ? 2 * N : N)) * 2) : 0x7fffffffu;
+    // Global column of slot column c (a multiple of 8) of the B slab.
+    auto b_col = [&](int c) -> int64_t { return GLU ? (c < HALF ? n0 + c : N + n0 + (c - HALF)) : n0 + c; };
 
     // Copy sources.  Offsets are bytes from the batch entry's base; the stage
     // adds k0 (A) or k0 rows (B) through the scalar offset.  A instruction r
@@ -514,7 +573,7 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     for (int j = 0; j < LB; ++j) {
         const int q = 1024 * (b_i0 + j) + 16 * lane;
         const int k = q / (BN * 2), pc = (q % (BN * 2)) / 16;
-        b_voff[j] = (uint32_t)((k * ldb + n0 + ((pc ^ swz_bn<BN>(k)) * 8)) * 2);
+        b_voff[j] = (uint32_t)((k * ldb + b_col((pc ^ swz_bn<BN>(k)) * 8)) * 2);
     }
     // The stage's offset moves the descriptor base (scalar arithmetic) and
     // shrinks its extent to match, so the scalar offset stays 0.
@@ -643,7 +702,12 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         }
         for (int q = tid; q < BK * (BN / 8); q += NWAVE * 64) {
             const int k = q / (BN / 8), c = q % (BN / 8);
-            const u32x4 v = load_chunk8_bf16(Bbat + (k0 + k) * ldb + n0, 8 * c, N - n0, k0 + k < K, p.align_b);
+            // GLU: chunk c of the up half is column n0 + 8c - HALF of W_u,
+            // which lies at N + n0 + 8c - HALF of the merged row
+            const bool up = GLU && 8 * c >= HALF;
+            const int64_t base = up ? N + n0 - HALF : n0;
+            const u32x4 v = load_chunk8_bf16(Bbat + (k0 + k) * ldb + base, 8 * c, up ? N - n0 + HALF : N - n0,
+                                             k0 + k < K, p.align_b);
             *(u32x4 *)(sB + k * BN + ((c ^ swz_bn<BN>(k)) * 8)) = v;
         }
         __syncthreads();
@@ -662,10 +726,15 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         // number of chunks.
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (p.out_f32) store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, float, MASKED>(acc, smem, Cb, p.ldc, m0, n0, M, N);
-        else store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, uint16_t, MASKED>(acc, smem, Cb, p.ldc, m0, n0, M, N);
+        if constexpr (EPI != EPI_NONE) {
+            store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, uint16_t, MASKED, EPI>(acc, smem, Cb, p.ldc, m0, n0, M, N);
+        } else {
+            if (p.out_f32) store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, float, MASKED>(acc, smem, Cb, p.ldc, m0, n0, M, N);
+            else store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, uint16_t, MASKED>(acc, smem, Cb, p.ldc, m0, n0, M, N);
+        }
         return;
     }
+    if constexpr (EPI != EPI_NONE) return;   // the host never launches a fused epilogue without the staged store
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
@@ -1341,6 +1410,37 @@ static hipError_t launch_bf16(const GemmArgs &a, int variant, int64_t grid, hipS
     default: hipLaunchKernelGGL((k_bf16_mfma<BM, BN, WGM, WGN, false>), g, dim3(WGM * WGN * 64), 0, s, a); break;
     }
     return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN, int NSA, int NSB, int EPI>
+static hipError_t launch_bf16_epi(const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
+{
+    const dim3 g((unsigned)grid), b8(WGM * WGN * 64);
+    switch (variant) {
+    case 1: hipLaunchKernelGGL((k_bf16_ms<BM, BN, WGM, WGN, NSA, NSB, 16, false, EPI>), g, b8, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_bf16_ms<BM, BN, WGM, WGN, NSA, NSB, 16, true, EPI>), g, b8, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_bf16_ms<BM, BN, WGM, WGN, NSA, NSB, 4, true, EPI>), g, b8, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int EPI>
+static hipError_t launch_fused_epi(int config_id, const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
+{
+    switch (config_id) {
+    case CFG_BF16_256x192: return launch_bf16_epi<256, 192, 2, 4, 4, 4, EPI>(a, variant, grid, s);
+    case CFG_BF16_256x256: return launch_bf16_epi<256, 256, 2, 4, 4, 4, EPI>(a, variant, grid, s);
+    case CFG_BF16_128x128: return launch_bf16_epi<128, 128, 4, 2, 4, 4, EPI>(a, variant, grid, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_fused(int config_id, int epi, const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
+{
+    if (epi == EPI_SILU) return launch_fused_epi<EPI_SILU>(config_id, a, variant, grid, s);
+    if (epi == EPI_SWIGLU) return launch_fused_epi<EPI_SWIGLU>(config_id, a, variant, grid, s);
+    return hipErrorInvalidValue;
 }
 
 template <int BM, int BN, int WGM, int WGN>

@@ -12,7 +12,8 @@ import torch
 from . import _lib
 from ._lib import GemmError, GemmPlan, lib
 
-__all__ = ["gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "plan_query", "GemmError"]
+__all__ = ["gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_silu", "gemm_bf16_swiglu", "plan_query",
+           "GemmError"]
 
 
 def _ld(t, inner):
@@ -134,11 +135,53 @@ def gemm_bf16_batched(A, B, C=None, out_dtype=torch.bfloat16):
     return C
 
 
+def gemm_bf16_silu(A, B, C=None):
+    """C[M,N] = bf16(SiLU(bf16(A . B))) for bfloat16 operands (gemm_bf16_silu)."""
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("gemm_bf16_silu takes bfloat16 operands")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    dev = _check_dev(A, B)
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if C.shape != (M, N) or C.dtype != torch.bfloat16:
+        raise ValueError("C must be bfloat16 [M, N]")
+    st = _launch(lib().gemm_bf16_silu, dev, M, N, K, A.data_ptr(), _ld(A, K), B.data_ptr(), _ld(B, N),
+                 C.data_ptr(), _ld(C, N))
+    if st != 0:
+        raise GemmError(st, "gemm_bf16_silu")
+    return C
+
+
+def gemm_bf16_swiglu(X, Wgu, Z=None):
+    """Z[M,N] = bf16(bf16(SiLU(bf16(X . W_g))) * bf16(X . W_u)) for a merged
+    bfloat16 weight Wgu[K, 2N] = [W_g | W_u] (gemm_bf16_swiglu)."""
+    if X.dtype != torch.bfloat16 or Wgu.dtype != torch.bfloat16:
+        raise TypeError("gemm_bf16_swiglu takes bfloat16 operands")
+    M, K = X.shape
+    K2, N2 = Wgu.shape
+    if K != K2 or N2 % 2:
+        raise ValueError("expected X [M, K] and Wgu [K, 2N]")
+    N = N2 // 2
+    dev = _check_dev(X, Wgu)
+    if Z is None:
+        Z = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if Z.shape != (M, N) or Z.dtype != torch.bfloat16:
+        raise ValueError("Z must be bfloat16 [M, N]")
+    st = _launch(lib().gemm_bf16_swiglu, dev, M, N, K, X.data_ptr(), _ld(X, K), Wgu.data_ptr(), _ld(Wgu, N2),
+                 Z.data_ptr(), _ld(Z, N))
+    if st != 0:
+        raise GemmError(st, "gemm_bf16_swiglu")
+    return Z
+
+
 def plan_query(op, M, N, K, batch=1, lda=None, ldb=None, ldc=None, a_addr=0x10000, b_addr=0x20000000,
                c_addr=0x40000000, sA=None, sB=None, sC=None, c_type=_lib.GEMM_OUT_BF16):
     """Host-only: the status and plan a call would produce (no GPU work)."""
     lda = K if lda is None else lda
-    ldb = N if ldb is None else ldb
+    ldb = (2 * N if op == _lib.GEMM_OP_BF16_SWIGLU else N) if ldb is None else ldb
     ldc = N if ldc is None else ldc
     sA = M * lda if sA is None else sA
     sB = K * ldb if sB is None else sB

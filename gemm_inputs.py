@@ -88,6 +88,16 @@ def decode_inputs(M, K=4096, N=12288, workload=W_DECODE):
     return np.ascontiguousarray(X16[:M]), W
 
 
+def swiglu_inputs(M=1024, K=4096, N=12288, workload=W_FFN):
+    """The FFN's two projections that share X, with a merged weight:
+    X ~ N(0,1) [M,K] (the FFN projection's X), Wgu [K,2N] = [W_g | W_u] with
+    W_g the FFN projection's weight and W_u a second N(0,1/64) draw (tensor
+    id 4); bf16 bit patterns."""
+    X, Wg = ffn_inputs(M, K, N, workload)
+    Wu = to_bf16_bits(normal(rng(workload, 4), (K, N), 0.125))
+    return X, np.ascontiguousarray(np.concatenate([Wg, Wu], axis=1))
+
+
 def batched_inputs(batch=32, M=1024, N=1024, K=128, workload=W_BATCHED):
     """Q ~ N(0,1) [batch,M,K] and Kmat ~ N(0,1) [batch,N,K] in bf16; the B
     operand is the materialised row-major transpose Kmat^T [batch,K,N]."""

@@ -101,6 +101,45 @@ int gemm_bf16_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
                       void *C, int64_t ldc, int64_t strideC, int c_type,
                       void *stream);
 
+/* ---- fused epilogues ------------------------------------------------------
+ *
+ * Page "Operator & Runtime" fuses the element-wise step after a projection
+ * into the GEMM's output tile, so that the intermediate never travels to HBM
+ * and back: an activation applied to the finished output tile (§5.4.2,
+ * Y = SiLU(A.W)), and the SwiGLU product of the two projections that share
+ * the input X (§5.3.1, Z = SiLU(X.W_g) (.) (X.W_u)).  §5.4.3 requires the
+ * fused program to keep the rounding of the unfused one: each product is
+ * accumulated in FP32 and rounded once to bf16 before the activation, and
+ * every intermediate the unfused program would store as bf16 is rounded to
+ * bf16.  SiLU(x) = x / (1 + e^-x), evaluated in FP32.
+ *
+ * Both calls take bf16 operands (bit patterns), write a bf16 result and
+ * follow gemm_bf16 for layout, ownership, streams, determinism and errors,
+ * with these additions.  GEMM_ERR_UNSUPPORTED: the output rows are not
+ * 16-byte aligned (C or Z pointer and ldc/ldz), N is not a multiple of 8,
+ * or no LDS-ring kernel can run the call (B rows not 16-byte aligned, or an
+ * operand spanning 2 GiB or more).  A's rows, when not 16-byte aligned, are
+ * first copied to aligned rows in the workspace described under Ownership,
+ * at any size of the product.  K == 0 writes zeros (SiLU(0) = 0).
+ */
+
+/* C [M,N] := bf16(SiLU(bf16(A.B))): A [M,K], B [K,N] as in gemm_bf16. */
+int gemm_bf16_silu(int64_t M, int64_t N, int64_t K,
+                   const uint16_t *A, int64_t lda,
+                   const uint16_t *B, int64_t ldb,
+                   uint16_t *C, int64_t ldc,
+                   void *stream);
+
+/* SwiGLU with a merged gate|up weight: X [M,K]; Wgu [K,2N] (ldw >= 2N)
+ * holds W_g in columns 0..N-1 and W_u in columns N..2N-1.  With
+ * g = bf16(X.W_g), u = bf16(X.W_u) and t = bf16(SiLU(g)), elementwise,
+ * Z [M,N] := bf16(t * u). */
+int gemm_bf16_swiglu(int64_t M, int64_t N, int64_t K,
+                     const uint16_t *X, int64_t ldx,
+                     const uint16_t *Wgu, int64_t ldw,
+                     uint16_t *Z, int64_t ldz,
+                     void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *gemm_status_string(int status);
 
@@ -141,7 +180,12 @@ typedef struct {
 } gemm_plan;
 
 /* Operation selector for gemm_plan_query. */
-typedef enum { GEMM_OP_SGEMM = 0, GEMM_OP_BF16 = 1 } gemm_op;
+typedef enum {
+    GEMM_OP_SGEMM = 0,       /* gemm_sgemm */
+    GEMM_OP_BF16 = 1,        /* gemm_bf16, gemm_bf16_batched */
+    GEMM_OP_BF16_SILU = 2,   /* gemm_bf16_silu (batch 1, c_type ignored) */
+    GEMM_OP_BF16_SWIGLU = 3  /* gemm_bf16_swiglu (batch 1, b = Wgu, c_type ignored) */
+} gemm_op;
 
 /* Validate the arguments of a call and report the plan it would launch,
  * without touching the GPU.  Pointers are passed as integers (their values

@@ -58,3 +58,43 @@ def check_bf16(C, ref, K, what=""):
 
 def amax_bf16(bits):
     return float(np.abs(gi.bf16_bits_to_f32(bits)).max()) if bits.size else 0.0
+
+
+# Fused epilogues.  The kernel rounds its FP32 product g_k to bf16, the
+# oracle rounds the exact product G; within the bf16 GEMM bar the two
+# rounded values differ by at most
+#     dg = 3 * 2^-9 |G| + 1e-3 sqrt(K)
+# (the kernel's bf16 output is within 2^-8 |G| + 1e-3 sqrt(K) of G, the
+# oracle's within 2^-9 |G|).  SiLU is Lipschitz with constant max|SiLU'| =
+# 1.0998 < 1.1, and every further rounding to bf16 adds at most 2^-9 of the
+# value (2^-8 is used to cover the FP32 evaluation of SiLU as well).
+
+def _dg(G, K):
+    return 3 * 2.0 ** -9 * np.abs(G) + 1e-3 * math.sqrt(max(K, 1))
+
+
+def check_silu(Y, G, Yref, K, what=""):
+    """|y - Y_ref| <= 1.1 dg (1 + 2^-9) + 2^-8 |Y_ref|, with G the exact product."""
+    bound = 1.1 * _dg(G, K) * (1 + 2.0 ** -9) + 2.0 ** -8 * np.abs(Yref)
+    return _check(Y, Yref, bound, what)
+
+
+def check_swiglu(Z, G, U, t, u, Zref, K, what=""):
+    """t = bf16(SiLU(g)) differs by dt = 1.1 dg (1 + 2^-9) + 2^-8 |t| and u by
+    du = dg(U); the product by dt (|u| + du) + |t| du; the final rounding
+    adds 2^-8 |Z_ref|."""
+    dt = 1.1 * _dg(G, K) * (1 + 2.0 ** -9) + 2.0 ** -8 * np.abs(t)
+    du = _dg(U, K)
+    bound = (dt * (np.abs(u) + du) + np.abs(t) * du) * (1 + 2.0 ** -9) + 2.0 ** -8 * np.abs(Zref)
+    return _check(Z, Zref, bound, what)
+
+
+def _check(C, ref, bound, what):
+    err = np.abs(C - ref)
+    assert np.all(np.isfinite(C)), f"{what}: non-finite output"
+    bad = err > bound
+    if bad.any():
+        idx = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} elements out of bound, first at {idx}: "
+                             f"got {C[idx]!r} want {ref[idx]!r} (bound {bound[idx]!r})")
+    return float((err / bound).max()) if err.size else 0.0

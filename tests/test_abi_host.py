@@ -250,3 +250,52 @@ def test_split_small_m_workspace_covers_every_slot(M, N, K, batch):
     top_slot = ((batch - 1) * strips + strips - 1) * ks + ks - 1
     top_cnt = (batch - 1) * strips + strips - 1
     assert (top_slot + 1) * 16 * 128 * 4 + (top_cnt + 1) * 4 <= p.workspace_bytes
+
+
+def call_fused(L, op, M, N, K, a=A_ADDR, lda=None, b=B_ADDR, ldb=None, c=C_ADDR, ldc=None):
+    lda = K if lda is None else lda
+    ldb = (N if op == "silu" else 2 * N) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    fn = L.gemm_bf16_silu if op == "silu" else L.gemm_bf16_swiglu
+    return fn(M, N, K, a, lda, b, ldb, c, ldc, None)
+
+
+@pytest.mark.parametrize("op", ["silu", "swiglu"])
+def test_fused_arguments(L, op):
+    """Fused epilogues: the same validation as gemm_bf16 with B spanning 2N
+    columns for SwiGLU; unaligned output rows or N % 8 are unsupported."""
+    nb = 1 if op == "silu" else 2
+    assert call_fused(L, op, -1, 8, 4) == g5.GEMM_ERR_INVALID_ARG
+    assert call_fused(L, op, 4, 8, 4, ldb=nb * 8 - 1) == g5.GEMM_ERR_INVALID_ARG
+    assert call_fused(L, op, 4, 8, 4, lda=3) == g5.GEMM_ERR_INVALID_ARG
+    assert call_fused(L, op, 4, 8, 4, ldc=7) == g5.GEMM_ERR_INVALID_ARG
+    assert call_fused(L, op, 4, 8, 4, b=0) == g5.GEMM_ERR_INVALID_ARG
+    # C starting inside B's last row: overlaps only if B spans nb*N columns
+    assert call_fused(L, op, 4, 8, 4, c=B_ADDR + (3 * nb * 8 + nb * 8 - 4) * 2) == g5.GEMM_ERR_INVALID_ARG
+    assert call_fused(L, op, 4, 12, 4) == g5.GEMM_ERR_UNSUPPORTED          # N % 8
+    assert call_fused(L, op, 4, 8, 4, c=C_ADDR + 2) == g5.GEMM_ERR_UNSUPPORTED  # C rows 2-byte aligned
+    assert call_fused(L, op, 0, 8, 4) == g5.GEMM_OK                          # empty: nothing to do
+    opc = g5.GEMM_OP_BF16_SILU if op == "silu" else g5.GEMM_OP_BF16_SWIGLU
+    st, p = g5.plan_query(opc, 4, 8, 0)
+    assert st == 0 and p.family == 1                                         # K = 0: fill with zeros
+    st, _ = g5.plan_query(opc, 4, 8, 4, batch=2)
+    assert st == g5.GEMM_ERR_INVALID_ARG                                     # no batched fused call
+
+
+def test_fused_plans(L):
+    """Ring-kernel variants of the fused calls (the epilogues exist in the
+    ring kernels only): 4-byte A copies for 4-byte aligned rows, 16-byte for
+    aligned ones, and 2-byte aligned A rows realigned first at any size;
+    SwiGLU output tiles of half the B tile's columns."""
+    for op in (g5.GEMM_OP_BF16_SILU, g5.GEMM_OP_BF16_SWIGLU):
+        nb = 392 if op == g5.GEMM_OP_BF16_SILU else 784
+        st, p = g5.plan_query(op, 300, 392, 261, lda=266, ldb=nb + 8, ldc=400)
+        assert st == 0 and p.variant == 3 and p.workspace_bytes == 0
+        st, p = g5.plan_query(op, 300, 392, 264, lda=272, ldb=nb + 8, ldc=400)
+        assert st == 0 and p.variant == 2
+        st, p = g5.plan_query(op, 257, 96, 33)
+        assert st == 0 and p.variant == 2 and p.workspace_bytes == 257 * 40 * 2
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_SWIGLU, 1024, 12288, 4096)
+    assert st == 0 and p.name == b"bf16_256x192" and p.grid == 4 * 128 and p.variant == 1
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_SILU, 1024, 12288, 4096)
+    assert st == 0 and p.name == b"bf16_256x192" and p.grid == 256
