@@ -61,6 +61,7 @@ struct Plan {
     int64_t tiles_m = 0, tiles_n = 0, group_m = 1;
     int align_a = 2, align_b = 2, align_c = 2;
     int ks = 1;              // K slices of the split small-M path
+    int ksplit = 1;          // K slices of a tiled bf16 call (128x128 ring kernel)
     bool realign_a = false;  // copy A's rows to 16-byte aligned ones first
     int64_t lda2 = 0;        // row stride of that copy (elements)
     double model_bytes = 0.0;
@@ -168,6 +169,18 @@ double model_time(const Problem &p, const ConfigInfo &c, double eff)
     return (t_tiles > t_hbm ? t_tiles : t_hbm) / eff;
 }
 
+// The same for the 128x128 ring kernel with K split into S slices: each
+// tile's S workgroups run 1/S of the stages, each publishes its FP32 tile
+// and the last reads the other S-1 back (both through the CU's copy path).
+double model_time_split(const Problem &p, const ConfigInfo &c, int S, double eff)
+{
+    Problem q = p;
+    q.K = cdiv(cdiv(p.K, 32), S) * 32;
+    q.batch = p.batch * S;
+    const double combine = (double)S * c.tile_m * c.tile_n * 4 / kCopyBytesPerCUperS;
+    return model_time(q, c, eff) + combine / eff;
+}
+
 int find_config_by_name(const char *name)
 {
     for (int i = 0; i < CFG_COUNT; ++i)
@@ -214,7 +227,7 @@ void fill_grid(const Problem &p, Plan &pl)
     default:
         pl.tiles_m = cdiv(p.M, c.tile_m);
         pl.tiles_n = cdiv(p.N, out_tile_n(p, c));
-        pl.grid = p.batch * pl.tiles_m * pl.tiles_n;
+        pl.grid = p.batch * pl.tiles_m * pl.tiles_n * pl.ksplit;
         break;
     }
     // Column bands as tall as the whole M extent when it is only a few tiles
@@ -263,6 +276,17 @@ int pick_variant(const Problem &p, const Plan &pl, bool *even)
     if (*even) return 1;
     return pl.align_a >= 16 ? 2 : 3;
 }
+
+// A K split into S slices of whole 32-deep stages, each at least 4 stages,
+// with partial tiles addressable by 32-bit buffer offsets per tile.
+bool split_ok(const Problem &p, int S)
+{
+    const int64_t kt = p.K / 32;
+    return S >= 2 && S <= 8 && kt >= 4 * S && p.batch * cdiv(p.M, 128) * cdiv(p.N, 128) * S <= ((int64_t)1 << 24);
+}
+
+// Stages per slice of a K split (the last slice also takes the rest of K).
+int split_kt_per(const Problem &p, int S) { return (int)((p.K / 32) / S); }
 
 // Returns GEMM_OK or GEMM_ERR_UNSUPPORTED.
 int select_plan(const Problem &p, Plan &pl)
@@ -346,6 +370,34 @@ int select_plan(const Problem &p, Plan &pl)
                 pl.config = cands[i].id;
             }
         }
+        // An output with fewer tiles than CUs: K split over workgroups of
+        // 128x128 tiles when the model gives it the shortest time
+        // (page "Operator & Runtime" §5.2.4 splits the reduction dimension
+        // to occupy the device).
+        if (bf16 && epi_of(p) == EPI_NONE) {
+            Plan t = pl;
+            t.config = CFG_BF16_128x128;
+            bool ev = false;
+            const int var = pick_variant(p, t, &ev);
+            for (int S = 2; S <= 8 && var >= 1; ++S) {
+                if (!split_ok(p, S)) continue;
+                const double eff = (p.K <= 8 * 32 ? 1.0 : 0.85) * (var == 1 ? 1.0 : 0.85);
+                const double tm = model_time_split(p, kConfigs[CFG_BF16_128x128], S, eff);
+                if (tm < best) {
+                    best = tm;
+                    pl.config = CFG_BF16_128x128;
+                    pl.ksplit = S;
+                }
+            }
+        }
+    }
+    if (const char *fk = std::getenv("GEMM_FORCE_KSPLIT")) {
+        // diagnostic: force the K split of the 128x128 ring kernel (1 = none)
+        const int S = std::atoi(fk);
+        if (S >= 1 && pl.config == CFG_BF16_128x128 && epi_of(p) == EPI_NONE) {
+            if (S > 1 && !split_ok(p, S)) return GEMM_ERR_UNSUPPORTED;
+            pl.ksplit = S;
+        }
     }
     fill_grid(p, pl);
     if (pl.grid <= 0 || pl.grid > (int64_t)1 << 24) return GEMM_ERR_UNSUPPORTED;
@@ -392,6 +444,18 @@ size_t split_part_bytes(const Problem &p, const Plan &pl)
 }
 size_t split_cnt_bytes(const Problem &p, const Plan &pl) { return (size_t)p.batch * pl.tiles_n * sizeof(unsigned); }
 
+// Workspace of a K-split tiled call: ksplit FP32 partial tiles per tile,
+// one arrival counter per tile.
+size_t ksplit_part_bytes(const Problem &p, const Plan &pl)
+{
+    const ConfigInfo &c = kConfigs[pl.config];
+    return pl.ksplit > 1 ? (size_t)p.batch * pl.tiles_m * pl.tiles_n * pl.ksplit * c.tile_m * c.tile_n * 4 : 0;
+}
+size_t ksplit_cnt_bytes(const Problem &p, const Plan &pl)
+{
+    return pl.ksplit > 1 ? (size_t)p.batch * pl.tiles_m * pl.tiles_n * sizeof(unsigned) : 0;
+}
+
 void fill_public_plan(const Problem &p, const Plan &pl, gemm_plan *out)
 {
     if (!out) return;
@@ -418,7 +482,9 @@ void fill_public_plan(const Problem &p, const Plan &pl, gemm_plan *out)
     out->model_bytes = pl.model_bytes;
     std::snprintf(out->name, sizeof out->name, "%s", c.name);
     if (pl.config == CFG_DECODE_SPLIT) out->workspace_bytes = split_part_bytes(p, pl) + split_cnt_bytes(p, pl);
+    out->workspace_bytes += ksplit_part_bytes(p, pl) + ksplit_cnt_bytes(p, pl);
     out->workspace_bytes += realign_bytes(p, pl);
+    out->ksplit = pl.ksplit;
 }
 
 // ------------------------------------------------------------ device check
@@ -545,6 +611,26 @@ int run(const Problem &p, void *stream)
     a.align_b = pl.align_b;
     a.align_c = pl.align_c;
     a.out_f32 = elem_c(p) == 4 ? 1 : 0;
+    a.ksplit = 1;
+    a.kt_per = 0;
+    a.ws_part = nullptr;
+    a.ws_cnt = nullptr;
+    if (pl.ksplit > 1) {
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        unsigned *cnt = nullptr;
+        float *part = nullptr;
+        if (get_workspace(dev, stream, ksplit_cnt_bytes(p, pl), ksplit_part_bytes(p, pl), &cnt, &part)) {
+            a.ksplit = pl.ksplit;
+            a.kt_per = split_kt_per(p, pl.ksplit);
+            a.ws_part = part;
+            a.ws_cnt = cnt;
+        } else {
+            // No workspace: one workgroup per tile over all of K.
+            pl.ksplit = 1;
+            fill_grid(p, pl);
+        }
+    }
     if (pl.realign_a) {
         int dev = 0;
         (void)hipGetDevice(&dev);

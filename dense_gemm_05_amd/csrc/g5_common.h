@@ -66,6 +66,15 @@ struct GemmArgs {
     int32_t align_b;
     int32_t align_c;
     int32_t out_f32;         // 1: C is float, 0: C is bf16 bits
+    // K split over workgroups (LDS-ring kernels with ksplit > 1): workgroup
+    // w computes slice w / (batch*tiles_m*tiles_n) of the 32-deep stages of
+    // tile w % (batch*tiles_m*tiles_n), kt_per stages (the last slice also
+    // the rest of K); FP32 partial tiles and per-tile arrival counters live
+    // in ws_part and ws_cnt.
+    int32_t ksplit;
+    int32_t kt_per;
+    float *ws_part;
+    unsigned *ws_cnt;
 };
 
 // Fused epilogues of the bf16 ring kernels.

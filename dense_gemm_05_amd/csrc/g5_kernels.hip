@@ -506,7 +506,13 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
 //    from the same columns of W_u, and the epilogue combines the two halves
 //    into BN/2 columns of Z = bf16(bf16(SiLU(g)) * u).  Both need the
 //    LDS-staged epilogue (16-byte aligned output rows, N % 8 == 0).
-template <int BM, int BN, int WGM, int WGN, int NSA, int NSB, int AV, bool MASKED, int EPI = EPI_NONE>
+//  * SK: K is split over p.ksplit workgroups per tile (see GemmArgs); each
+//    publishes its FP32 accumulators and the last to arrive adds the
+//    partial tiles in slice order, so the result does not depend on which
+//    workgroup finishes last ("Operator & Runtime" §5.2.4: partial sums over
+//    split K, combined in a fixed order).
+template <int BM, int BN, int WGM, int WGN, int NSA, int NSB, int AV, bool MASKED, int EPI = EPI_NONE,
+          bool SK = false>
 __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
 {
     constexpr int NWAVE = WGM * WGN;
@@ -538,15 +544,24 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     constexpr bool GLU = EPI == EPI_SWIGLU;
     constexpr int HALF = BN / 2;                              // GLU: columns per weight half
     static_assert(!GLU || HALF % 8 == 0, "GLU halves must be whole chunks");
-    const TileCoord tc = tile_map(blockIdx.x, p.batch, p.tiles_m, p.tiles_n, p.group_m);
+    const int64_t ntiles = p.batch * p.tiles_m * p.tiles_n;
+    const int64_t wg = SK ? (int64_t)blockIdx.x % ntiles : (int64_t)blockIdx.x;
+    const int slice = SK ? (int)((int64_t)blockIdx.x / ntiles) : 0;
+    const TileCoord tc = tile_map(wg, p.batch, p.tiles_m, p.tiles_n, p.group_m);
     // n0: first output column (GLU: first column of each weight half)
     const int64_t m0 = tc.tm * BM, n0 = tc.tn * (GLU ? HALF : BN);
-    const int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
-    const uint16_t *Abat = (const uint16_t *)p.A + tc.b * p.sA;
-    const uint16_t *Bbat = (const uint16_t *)p.B + tc.b * p.sB;
-    // Byte extents of this batch entry's operands (reads past them return 0).
-    const uint32_t a_bytes = MASKED ? (uint32_t)(((M - 1) * lda + K) * 2) : 0x7fffffffu;
-    const uint32_t b_bytes = MASKED ? (uint32_t)(((K - 1) * ldb + (GLU ? 2 * N : N)) * 2) : 0x7fffffffu;
+    const int64_t M = p.M, N = p.N, lda = p.lda, ldb = p.ldb;
+    // This workgroup's part of K starts at kbase; the operand bases below are
+    // moved there, so everything after this works on K columns from them.
+    const int64_t kbase = SK ? (int64_t)slice * p.kt_per * BK : 0;
+    const int64_t K = SK && slice < p.ksplit - 1 ? (int64_t)p.kt_per * BK : p.K - kbase;
+    const uint16_t *Abat = (const uint16_t *)p.A + tc.b * p.sA + kbase;
+    const uint16_t *Bbat = (const uint16_t *)p.B + tc.b * p.sB + kbase * ldb;
+    // Byte extents of this batch entry's operands from those bases (reads
+    // past them return 0).
+    const uint32_t a_bytes = MASKED ? (uint32_t)(((M - 1) * lda + (p.K - kbase)) * 2) : 0x7fffffffu;
+    const uint32_t b_bytes =
+        MASKED ? (uint32_t)(((p.K - kbase - 1) * ldb + (GLU ? 2 * N : N)) * 2) : 0x7fffffffu;
     // Global column of slot column c (a multiple of 8) of the B slab.
     auto b_col = [&](int c) -> int64_t { return GLU ? (c < HALF ? n0 + c : N + n0 + (c - HALF)) : n0 + c; };
 
@@ -715,6 +730,51 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         mfma_range(f0, 0, NMFMA);
     }
     __builtin_amdgcn_s_waitcnt(0);
+
+    if constexpr (SK) {
+        // Publish this slice's FP32 tile in register order (block, wave,
+        // lane: each wave writes 1 KiB runs) with device-scope (sc1) stores,
+        // wait for them, then count the arrival.  The workgroup that brings
+        // the tile's counter to ksplit adds the slices 0, 1, ... in order
+        // (its own from registers, bit-identical to what it stored), resets
+        // the counter for the next call and stores the tile.
+        __shared__ unsigned sk_arrived;
+        constexpr int TILE_F = BM * BN;
+        float *tile_ws = p.ws_part + wg * p.ksplit * (int64_t)TILE_F;
+        const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+            tile_ws + (int64_t)slice * TILE_F, 0, TILE_F * 4, 0x00020000);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int off = (((fn * FM + fm) * NWAVE + wave) * 64 + lane) * 16;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[fn][fm]), wr, off, 0, 16);
+            }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) sk_arrived = __hip_atomic_fetch_add(p.ws_cnt + wg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (sk_arrived != (unsigned)(p.ksplit - 1)) return;
+        f32x4 tot[FN][FM];
+        for (int s2 = 0; s2 < p.ksplit; ++s2) {
+            const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+                tile_ws + (int64_t)s2 * TILE_F, 0, TILE_F * 4, 0x00020000);
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    const int off = (((fn * FM + fm) * NWAVE + wave) * 64 + lane) * 16;
+                    const f32x4 v = s2 == slice ? acc[fn][fm]
+                                                : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, 16));
+                    tot[fn][fm] = s2 == 0 ? v : tot[fn][fm] + v;
+                }
+        }
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = tot[fn][fm];
+        if (tid == 0) __hip_atomic_store(p.ws_cnt + wg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     void *Cb = (char *)p.C + tc.b * p.sC * (p.out_f32 ? 4 : 2);
     if (p.align_c >= 16 && (!MASKED || N % (p.out_f32 ? 4 : 8) == 0)) {
@@ -1403,6 +1463,18 @@ template <int BM, int BN, int WGM, int WGN, int DWGM, int DWGN, int NSA, int NSB
 static hipError_t launch_bf16(const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
 {
     const dim3 g((unsigned)grid), b8(DWGM * DWGN * 64);
+    if constexpr (BM == 128 && BN == 128) {
+        // K split over workgroups (128x128 tiles only: the smallest partial tiles)
+        if (a.ksplit > 1) {
+            switch (variant) {
+            case 1: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NSA, NSB, 16, false, EPI_NONE, true>), g, b8, 0, s, a); break;
+            case 2: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NSA, NSB, 16, true, EPI_NONE, true>), g, b8, 0, s, a); break;
+            case 3: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NSA, NSB, 4, true, EPI_NONE, true>), g, b8, 0, s, a); break;
+            default: return hipErrorInvalidValue;
+            }
+            return hipGetLastError();
+        }
+    }
     switch (variant) {
     case 1: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NSA, NSB, 16, false>), g, b8, 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NSA, NSB, 16, true>), g, b8, 0, s, a); break;

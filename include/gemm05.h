@@ -23,14 +23,21 @@
  * kernel(s) on `stream` (a hipStream_t; NULL means the null stream) and
  * returns; completion is observed through the stream.  Calls are
  * thread-safe.  The exceptions to "no allocation" are two workspaces kept
- * per (device, stream): the small-M path with K split over workgroups keeps
- * partial sums and counters there, and a large bf16 product (from 2^30
- * multiply-adds) whose A rows are not 16-byte aligned first copies A's rows
- * there with 16-byte aligned starts.  Each is allocated with hipMalloc on
- * that stream's first such call (or when a larger call needs more; the
- * stream is synchronised before an old buffer is freed) and kept until the
- * process exits.  If an allocation fails the call runs without it: the
- * whole-K small-M kernel, or the tiled kernel copying A's rows as they are.
+ * per (device, stream): the small-M path and a tiled bf16 call with K split
+ * over workgroups (an output with too few tiles to fill the GPU) keep FP32
+ * partial sums and arrival counters in the first, and a large bf16 product
+ * (from 2^30 multiply-adds) whose A rows are not 16-byte aligned first
+ * copies A's rows into the second with 16-byte aligned starts.  Each is
+ * allocated with hipMalloc on that stream's first such call (or when a
+ * larger call needs more; the stream is synchronised before an old buffer
+ * is freed) and kept until the process exits; the counters are zero between
+ * calls.  Calls on one stream are ordered, so they never share a workspace
+ * at the same time.  If an allocation fails the call runs without it: the
+ * whole-K small-M kernel, one workgroup per tile over all of K, or the tiled
+ * kernel copying A's rows as they are.  The environment variable
+ * GEMM_FORCE_KSPLIT=S (diagnostics and tests) forces a split of S slices on
+ * calls that use 128x128 tiles (1 = none; GEMM_ERR_UNSUPPORTED when S
+ * slices of at least 4 32-deep stages do not fit K).
  * No alignment is required; aligned operands (16-byte rows and pointers)
  * select the faster kernel variants.
  *
@@ -175,8 +182,11 @@ typedef struct {
     char name[48];     /* configuration name, as accepted by GEMM_FORCE_CONFIG */
     int64_t workspace_bytes; /* library-owned workspace the call needs: partial
                                 sums and arrival counters of the split small-M
-                                path, or the realigned copy of A (batch x M
-                                rows of K rounded up to 8 bf16); else 0 */
+                                path or of a K-split tiled call, and the
+                                realigned copy of A (batch x M rows of K
+                                rounded up to 8 bf16); else 0 */
+    int ksplit;        /* tiled bf16 calls: workgroups sharing each output
+                          tile's K range (1: no split); grid counts them all */
 } gemm_plan;
 
 /* Operation selector for gemm_plan_query. */

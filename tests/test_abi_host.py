@@ -145,8 +145,11 @@ def test_selector_choices_for_the_workloads(L):
     assert st == 0 and p.name == b"bf16_256x256" and p.grid == 512
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 2048, 2048, 8192)
     assert st == 0 and p.name == b"bf16_128x128" and p.grid == 256
+    # ... and with K split in 2 over workgroups (96 tiles -> 192 workgroups;
+    # the slices' FP32 tiles and a counter per tile in the workspace)
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 1024, 1536, 4096)
-    assert st == 0 and p.name == b"bf16_128x128" and p.grid == 96
+    assert st == 0 and p.name == b"bf16_128x128" and p.ksplit == 2 and p.grid == 192
+    assert p.workspace_bytes == 96 * 2 * 128 * 128 * 4 + 96 * 4
     st, p = g5.plan_query(g5.GEMM_OP_SGEMM, 4096, 4096, 4096)
     assert st == 0 and p.family == 3 and p.even == 1
     # FP32 256^3: 32x32 tiles with all of K staged at once; K = 288 (9 slabs)
@@ -299,3 +302,27 @@ def test_fused_plans(L):
     assert st == 0 and p.name == b"bf16_256x192" and p.grid == 4 * 128 and p.variant == 1
     st, p = g5.plan_query(g5.GEMM_OP_BF16_SILU, 1024, 12288, 4096)
     assert st == 0 and p.name == b"bf16_256x192" and p.grid == 256
+
+
+def test_ksplit_plans(L, monkeypatch):
+    """K split over workgroups: only for outputs with fewer tiles than CUs,
+    each slice at least 4 stages of 32; forcing follows the same rule."""
+    for args, ks in [((1024, 12288, 4096), 1), ((4096, 4096, 4096), 1), ((2048, 2048, 8192), 1),
+                     ((512, 512, 4096), 5), ((256, 256, 16384), 8), ((1000, 1000, 1000), 3)]:
+        st, p = g5.plan_query(g5.GEMM_OP_BF16, *args)
+        assert st == 0 and p.ksplit == ks, (args, p.ksplit)
+        tiles = -(-args[0] // p.tile_m) * -(-args[1] // p.tile_n)
+        assert p.grid == tiles * ks
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 1024, 1024, 128, batch=32, c_type=1)
+    assert st == 0 and p.ksplit == 1
+    # fused epilogues and FP32 never split
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_SILU, 512, 512, 4096)
+    assert st == 0 and p.ksplit == 1
+    st, p = g5.plan_query(g5.GEMM_OP_SGEMM, 512, 512, 4096)
+    assert st == 0 and p.ksplit == 1
+    monkeypatch.setenv("GEMM_FORCE_CONFIG", "bf16_128x128")
+    monkeypatch.setenv("GEMM_FORCE_KSPLIT", "3")
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 300, 392, 400)      # 12 stages: 3 slices of 4
+    assert st == 0 and p.ksplit == 3 and p.grid == 3 * 12
+    st, _ = g5.plan_query(g5.GEMM_OP_BF16, 300, 392, 380)      # 11 stages: too few for 3
+    assert st == g5.GEMM_ERR_UNSUPPORTED

@@ -136,13 +136,16 @@ def test_fused_deterministic_and_k_zero():
     assert torch.all(Y == 0)
 
 
-def test_swiglu_matches_separate_products():
+def test_swiglu_matches_separate_products(monkeypatch):
     """Z from the fused call equals bf16(bf16(SiLU(g)) * u) computed from the
     library's own bf16 gate and up products, bit for bit: both take the same
-    FP32 sums (same kernel, same summation order) and round them once."""
+    FP32 sums (same kernel, same summation order; the plain products are
+    kept from splitting K, which the fused call never does) and round them
+    once."""
     X, Wgu = _swiglu_case(512, 384, 640, 4)
     dX, dW = dev_bf16(X), dev_bf16(Wgu)
     Z = g5.gemm_bf16_swiglu(dX, dW)
+    monkeypatch.setenv("GEMM_FORCE_KSPLIT", "1")
     g = g5.gemm_bf16(dX, dW[:, :384])
     u = g5.gemm_bf16(dX, dW[:, 384:])
     # the elementwise step on the host in float32, from the GPU's bf16 g and u

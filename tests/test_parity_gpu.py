@@ -313,7 +313,11 @@ def test_bf16_realigned_rows(oracle_mod, M, N, K, pa, batch):
                              b_addr=dB.data_ptr(), c_addr=C.data_ptr(), sA=M * (K + pa), sB=K * N, sC=M * N,
                              c_type=1)
     assert st == 0 and plan.family == 2 and plan.vec_a == 16 and plan.variant in (1, 2), (plan.name, plan.variant)
-    assert plan.workspace_bytes == batch * M * ((K + 7) // 8 * 8) * 2
+    split = 0
+    if plan.ksplit > 1:       # few tiles: K also split over workgroups (partial tiles, counters)
+        tiles = batch * -(-M // plan.tile_m) * -(-N // plan.tile_n)
+        split = tiles * plan.ksplit * plan.tile_m * plan.tile_n * 4 + tiles * 4
+    assert plan.workspace_bytes == batch * M * ((K + 7) // 8 * 8) * 2 + split
     g5.gemm_bf16_batched(dA[:, :, :K], dB, C)
     host = host_values(C)
     for b in range(batch):
@@ -485,3 +489,72 @@ def test_bf16_kernel_variants(oracle_mod, monkeypatch, M, N, K, pa, pb, cfg, var
         else:
             check_f32(host[:, :N], ref, K, amax_bf16(A[:, :K]), amax_bf16(B[:, :N]), f"variant {variant} f32")
         assert np.all(np.isnan(host[:, N:])), "ldc padding was written"
+
+
+@pytest.mark.parametrize("M,N,K,S,lda_pad,batch", [
+    (300, 392, 262, 2, 0, 1),      # 4-byte A copies, K tail of 6
+    (512, 512, 4096, 5, 0, 1),     # aligned whole tiles, uneven slices (25, 25, 25, 25, 28 stages)
+    (257, 200, 1000, 7, 0, 1),     # ragged edges, K tail of 8 in the last slice
+    (129, 136, 640, 4, 8, 3),      # batched, padded A rows
+    (64, 128, 256, 2, 0, 2),       # one tile per batch entry
+])
+def test_bf16_ksplit(oracle_mod, monkeypatch, M, N, K, S, lda_pad, batch):
+    """K split over S workgroups per tile (forced), every ring variant the
+    shape selects, FP32 and bf16 output; NaN in the ldc padding shows any
+    stray write; a second call gives the same bits (the per-tile counters
+    are back at zero and the slice order is fixed)."""
+    _say(f"bf16 ksplit {S} batch {batch} {M}x{N}x{K} lda pad {lda_pad}")
+    g = np.random.default_rng([gi.SEED_BASE + 5000, M, N, K, S])
+    A = gi.to_bf16_bits(gi.normal(g, (batch, M, K + lda_pad)))
+    B = gi.to_bf16_bits(gi.normal(g, (batch, K, N), 0.125))
+    dA, dB = dev_bf16(A), dev_bf16(B)
+    monkeypatch.setenv("GEMM_FORCE_CONFIG", "bf16_128x128")
+    monkeypatch.setenv("GEMM_FORCE_KSPLIT", str(S))
+    for od in (torch.float32, torch.bfloat16):
+        Cfull = torch.full((batch, M, N + 8), float("nan"), device="cuda", dtype=od)
+        outs = []
+        for _ in range(2):
+            if batch == 1:
+                g5.gemm_bf16(dA[0, :, :K], dB[0], Cfull[0, :, :N])
+            else:
+                g5.gemm_bf16_batched(dA[:, :, :K], dB, Cfull[:, :, :N])
+            outs.append(Cfull.clone())
+        assert torch.equal(outs[0].view(torch.int16 if od == torch.bfloat16 else torch.int32),
+                           outs[1].view(torch.int16 if od == torch.bfloat16 else torch.int32)), "not deterministic"
+        host = host_values(Cfull)
+        for b in range(batch):
+            Ab = np.ascontiguousarray(A[b, :, :K])
+            ref = oracle_mod.gemm_bf16(Ab, B[b])
+            if od == torch.bfloat16:
+                check_bf16(host[b, :, :N], ref, K, f"ksplit {S} bf16 entry {b}")
+            else:
+                check_f32(host[b, :, :N], ref, K, amax_bf16(Ab), amax_bf16(B[b]), f"ksplit {S} f32 entry {b}")
+        assert np.all(np.isnan(host[:, :, N:])), "ldc padding was written"
+
+
+def test_ksplit_back_to_back_changing_split(oracle_mod, monkeypatch):
+    """Calls with different splits and shapes on one stream, without
+    synchronising in between: each sees zeroed counters."""
+    monkeypatch.setenv("GEMM_FORCE_CONFIG", "bf16_128x128")
+    cases = [(256, 384, 1024, 4), (256, 384, 1024, 2), (384, 256, 768, 6), (256, 384, 1024, 8)]
+    res = []
+    for M, N, K, S in cases:
+        A, B = gi.small_case("bf16", M, N, K, seed=S, scale_b=0.125)
+        monkeypatch.setenv("GEMM_FORCE_KSPLIT", str(S))
+        res.append((A, B, g5.gemm_bf16(dev_bf16(A), dev_bf16(B), out_dtype=torch.float32)))
+    for (A, B, C), (M, N, K, S) in zip(res, cases):
+        check_f32(host_values(C), oracle_mod.gemm_bf16(A, B), K, amax_bf16(A), amax_bf16(B), f"split {S}")
+
+
+def test_ksplit_shard_full_size(oracle_mod):
+    """The 1024x1536x4096 shard of an 8-way column split of the FFN
+    projection: 96 tiles of 128x128, K split in 2 by the selector."""
+    _say("bf16 1024x1536x4096 split")
+    X, W = gi.ffn_inputs()
+    W = np.ascontiguousarray(W[:, :1536])
+    st, plan = g5.plan_query(g5.GEMM_OP_BF16, 1024, 1536, 4096)
+    assert st == 0 and plan.ksplit == 2
+    C = g5.gemm_bf16(dev_bf16(X), dev_bf16(W))
+    rows = np.unique(np.concatenate([np.arange(0, 1024, 64), np.arange(127, 1024, 128), [1, 1000]]))
+    ref = oracle_mod.gemm_bf16(np.ascontiguousarray(X[rows]), W)
+    check_bf16(host_values(C)[rows], ref, 4096, "shard rows")
