@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "sgemm", "batched", "ragged", "swiglu", "copy"])
+    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "sgemm", "batched", "ragged", "swiglu", "shard", "copy"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--prewarm-seconds", type=float, default=1.0,
@@ -56,8 +56,10 @@ def kernel_label(plan):
     tm, tn = plan.tile_m, plan.tile_n
     if plan.family == 2 and plan.variant in (1, 2, 3):
         av, masked = {1: (16, "false"), 2: (16, "true"), 3: (4, "true")}[plan.variant]
-        wg = "2,4" if (tm, tn) == (256, 192) else "4,2"
-        return f"k_bf16_ms<{tm},{tn},{wg},4,4,{av},{masked}> ({name}, grid {plan.grid}, {plan.threads} threads)"
+        wg = "2,4" if tm == 256 and tn in (192, 256) else "4,2"
+        sk = "true" if plan.ksplit > 1 else "false"
+        return (f"k_bf16_ms<{tm},{tn},{wg},4,4,{av},{masked},0,{sk}> ({name}, grid {plan.grid}, "
+                f"{plan.threads} threads)")
     return f"{name} variant {plan.variant} (grid {plan.grid}, {plan.threads} threads)"
 
 
@@ -288,6 +290,28 @@ def main():
                           "tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                           "two_plain_projections_us": round(ms_plain * 1e3, 3), "rotations": R})
         del dX, dW, dZ, dG, dU
+
+    # ------------------------------------------------------------ column shard (split K)
+    if args.only in ("all", "shard"):
+        # The 1024x1536x4096 shard of an 8-way column split of the FFN
+        # projection: 96 tiles of 128x128 for 256 CUs, so K is split over
+        # workgroups.
+        M, N, K = 1024, 1536, 4096
+        X, W = gi.ffn_inputs()
+        W = np.ascontiguousarray(W[:, :N])
+        R = rotations(2 * (M * K + K * N + M * N))
+        dX = [to_dev_bf16(X) for _ in range(R)]
+        dW = [to_dev_bf16(W) for _ in range(R)]
+        dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        fns = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i])) for i in range(R)]
+        st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
+        ms = timed(fns, 100, 10)
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        log(f"shard 1024x1536x4096: {ms * 1e3:.2f} us/call, {tf:.1f} TFLOPS, {plan.name.decode()} ksplit {plan.ksplit}")
+        workloads.append({"name": "shard_bf16_1024x1536x4096", "us": round(ms * 1e3, 3), "tflops": round(tf, 2),
+                          "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "config": plan.name.decode(),
+                          "ksplit": plan.ksplit, "rotations": R})
+        del dX, dW, dC
 
     out["workloads"] = workloads
 
