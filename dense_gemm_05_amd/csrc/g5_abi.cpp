@@ -64,6 +64,8 @@ struct Plan {
     int ksplit = 1;          // K slices of a tiled bf16 call (128x128 ring kernel)
     bool realign_a = false;  // copy A's rows to 16-byte aligned ones first
     int64_t lda2 = 0;        // row stride of that copy (elements)
+    bool realign_b = false;  // the same for the rows of a transposed B (Bt [N, K])
+    int64_t ldb2 = 0;
     double model_bytes = 0.0;
 };
 
@@ -84,8 +86,14 @@ int epi_of(const Problem &p)
 {
     return p.op == GEMM_OP_BF16_SILU ? EPI_SILU : p.op == GEMM_OP_BF16_SWIGLU ? EPI_SWIGLU : EPI_NONE;
 }
-// Columns of B: the merged gate|up weight of SwiGLU has 2N.
-int64_t b_cols(const Problem &p) { return p.op == GEMM_OP_BF16_SWIGLU ? 2 * p.N : p.N; }
+// B is given transposed, Bt [N, K].
+bool b_trans(const Problem &p) { return p.op == GEMM_OP_BF16_NT; }
+// Rows and columns of the B operand as stored: [K, N], Bt [N, K], or the
+// merged gate|up weight [K, 2N] of SwiGLU.
+int64_t b_rows(const Problem &p) { return b_trans(p) ? p.N : p.K; }
+int64_t b_cols(const Problem &p) { return b_trans(p) ? p.K : p.op == GEMM_OP_BF16_SWIGLU ? 2 * p.N : p.N; }
+// Calls only the LDS-ring kernels can run (variants 1-3).
+bool ring_only(const Problem &p) { return epi_of(p) != EPI_NONE || b_trans(p); }
 // Output columns per tile of a tiled config (SwiGLU: half the B columns).
 int64_t out_tile_n(const Problem &p, const ConfigInfo &c)
 {
@@ -117,10 +125,11 @@ bool overlap(const Range &x, const Range &y) { return x.lo < y.hi && y.lo < x.hi
 
 int validate(const Problem &p)
 {
-    if (p.op != GEMM_OP_SGEMM && p.op != GEMM_OP_BF16 && p.op != GEMM_OP_BF16_SILU && p.op != GEMM_OP_BF16_SWIGLU)
+    if (p.op != GEMM_OP_SGEMM && p.op != GEMM_OP_BF16 && p.op != GEMM_OP_BF16_SILU && p.op != GEMM_OP_BF16_SWIGLU &&
+        p.op != GEMM_OP_BF16_NT)
         return GEMM_ERR_INVALID_ARG;
     if (p.batch < 0 || p.M < 0 || p.N < 0 || p.K < 0) return GEMM_ERR_INVALID_ARG;
-    if (p.op == GEMM_OP_BF16 && p.c_type != GEMM_OUT_BF16 && p.c_type != GEMM_OUT_F32)
+    if ((p.op == GEMM_OP_BF16 || p.op == GEMM_OP_BF16_NT) && p.c_type != GEMM_OUT_BF16 && p.c_type != GEMM_OUT_F32)
         return GEMM_ERR_INVALID_ARG;
     if (epi_of(p) != EPI_NONE && (p.c_type != GEMM_OUT_BF16 || p.batch > 1)) return GEMM_ERR_INVALID_ARG;
     if (p.sA < 0 || p.sB < 0 || p.sC < 0) return GEMM_ERR_INVALID_ARG;
@@ -132,7 +141,7 @@ int validate(const Problem &p)
     if (p.K == 0) return GEMM_OK;
     if (p.lda < p.K || p.ldb < b_cols(p) || p.a == 0 || p.b == 0) return GEMM_ERR_INVALID_ARG;
     const Range ra = extent(p.a, p.batch, p.M, p.K, p.lda, p.sA, elem_a(p));
-    const Range rb = extent(p.b, p.batch, p.K, b_cols(p), p.ldb, p.sB, elem_a(p));
+    const Range rb = extent(p.b, p.batch, b_rows(p), b_cols(p), p.ldb, p.sB, elem_a(p));
     if (ra.hi > ((__int128)1 << 63) || rb.hi > ((__int128)1 << 63)) return GEMM_ERR_INVALID_ARG;
     if (overlap(rc, ra) || overlap(rc, rb)) return GEMM_ERR_INVALID_ARG;
     return GEMM_OK;
@@ -195,6 +204,7 @@ bool config_fits(const Problem &p, int id)
 {
     const ConfigInfo &c = kConfigs[id];
     if (epi_of(p) != EPI_NONE) return has_epilogues(id);
+    if (b_trans(p)) return c.family == GEMM_FAMILY_BF16_MFMA;   // the ring kernels of every bf16 tile config
     switch (c.family) {
     case GEMM_FAMILY_BF16_MFMA: return p.op == GEMM_OP_BF16;
     case GEMM_FAMILY_F32_MFMA: return p.op == GEMM_OP_SGEMM;
@@ -265,11 +275,12 @@ int pick_variant(const Problem &p, const Plan &pl, bool *even)
     }
     if (c.family != GEMM_FAMILY_BF16_MFMA) return 0;
     const __int128 a_bytes = ((__int128)(p.M - 1) * p.lda + p.K) * 2;
-    const __int128 b_bytes = ((__int128)(p.K - 1) * p.ldb + b_cols(p)) * 2;
+    const __int128 b_bytes = ((__int128)(b_rows(p) - 1) * p.ldb + b_cols(p)) * 2;
     const bool fits = a_bytes < ((__int128)1 << 31) && b_bytes < ((__int128)1 << 31);
     // N % 8: every 16-byte chunk of B lies wholly inside or wholly past the
     // descriptor extent (no partially out-of-range copies).
-    if (!fits || pl.align_b < 16 || pl.align_a < 4 || p.N % 8 != 0) return 0;
+    // (Bt's chunks run along K like A's: no condition on N.)
+    if (!fits || pl.align_b < 16 || pl.align_a < 4 || (!b_trans(p) && p.N % 8 != 0)) return 0;
     const int ring_k = 32;
     const bool c_ok = pl.align_c >= (elem_c(p) == 4 ? 16 : 8);
     *even = !(p.M % c.tile_m || p.N % out_tile_n(p, c) || p.K % ring_k) && pl.align_a >= 16 && c_ok;
@@ -322,7 +333,7 @@ int select_plan(const Problem &p, Plan &pl)
         // staged at once (one load latency per tile instead of one per slab;
         // 256^3 measured 9.4 us with the double-buffered 64x64 kernel).
         pl.config = CFG_F32_32x32_WK;
-    } else if (p.op == GEMM_OP_BF16 && p.M <= 16 && p.batch <= 65535) {
+    } else if (p.op == GEMM_OP_BF16 && p.M <= 16 && p.batch <= 65535) {   // (Bt: the tiled kernels)
         // The split path when its preconditions hold and it would use more
         // than one slice; else whole-K strips of 64 columns.
         pl.config = CFG_DECODE_SPLIT;
@@ -378,7 +389,8 @@ int select_plan(const Problem &p, Plan &pl)
             Plan t = pl;
             t.config = CFG_BF16_128x128;
             bool ev = false;
-            const int var = pick_variant(p, t, &ev);
+            int var = pick_variant(p, t, &ev);
+            if (b_trans(p) && var == 0 && pl.align_b < 16) var = 2;   // Bt rows realigned below
             for (int S = 2; S <= 8 && var >= 1; ++S) {
                 if (!split_ok(p, S)) continue;
                 const double eff = (p.K <= 8 * 32 ? 1.0 : 0.85) * (var == 1 ? 1.0 : 0.85);
@@ -407,11 +419,25 @@ int select_plan(const Problem &p, Plan &pl)
     // from a copy of A with aligned rows when that lets the ring kernel copy
     // A 16 bytes per lane (the copy costs 2 x M x K x 2 bytes of traffic,
     // small next to the product from 2^30 multiply-adds on).
-    // The fused epilogues exist only in the ring kernels, so a fused call
-    // whose A rows no ring variant takes is realigned at any size.
-    if (kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && pl.align_a < 16 &&
-        ((double)p.batch * p.M * p.N * p.K >= (double)(1 << 30) || (epi_of(p) != EPI_NONE && pl.variant == 0))) {
+    // The fused epilogues and a transposed B exist only in the ring kernels,
+    // so such a call whose rows no ring variant takes is realigned at any
+    // size: Bt's rows first, then A's.
+    if (kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && b_trans(p) && pl.align_b < 16) {
+        pl.realign_b = true;
+        pl.ldb2 = (p.K + 7) / 8 * 8;
+        pl.align_b = 16;
         Problem q = p;
+        q.ldb = pl.ldb2;
+        q.sB = p.N * pl.ldb2;
+        pl.variant = pick_variant(q, pl, &pl.even);
+    }
+    if (kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && pl.align_a < 16 &&
+        ((double)p.batch * p.M * p.N * p.K >= (double)(1 << 30) || (ring_only(p) && pl.variant == 0))) {
+        Problem q = p;
+        if (pl.realign_b) {
+            q.ldb = pl.ldb2;
+            q.sB = p.N * pl.ldb2;
+        }
         q.lda = (p.K + 7) / 8 * 8;
         q.sA = p.M * q.lda;
         Plan t = pl;
@@ -426,14 +452,18 @@ int select_plan(const Problem &p, Plan &pl)
             pl.even = ev;
         }
     }
-    // fused epilogues exist in the ring kernels only (variants 1-3)
-    if (epi_of(p) != EPI_NONE && pl.config != CFG_ZERO && pl.variant == 0) return GEMM_ERR_UNSUPPORTED;
+    // fused epilogues and a transposed B exist in the ring kernels only (variants 1-3)
+    if (ring_only(p) && pl.config != CFG_ZERO && pl.variant == 0) return GEMM_ERR_UNSUPPORTED;
     return GEMM_OK;
 }
 
 size_t realign_bytes(const Problem &p, const Plan &pl)
 {
     return pl.realign_a ? (size_t)p.batch * p.M * pl.lda2 * 2 : 0;
+}
+size_t realign_b_bytes(const Problem &p, const Plan &pl)
+{
+    return pl.realign_b ? (size_t)p.batch * p.N * pl.ldb2 * 2 : 0;
 }
 
 // Workspace of the split small-M path: one slot of 16 x 128 partial sums
@@ -483,7 +513,7 @@ void fill_public_plan(const Problem &p, const Plan &pl, gemm_plan *out)
     std::snprintf(out->name, sizeof out->name, "%s", c.name);
     if (pl.config == CFG_DECODE_SPLIT) out->workspace_bytes = split_part_bytes(p, pl) + split_cnt_bytes(p, pl);
     out->workspace_bytes += ksplit_part_bytes(p, pl) + ksplit_cnt_bytes(p, pl);
-    out->workspace_bytes += realign_bytes(p, pl);
+    out->workspace_bytes += realign_bytes(p, pl) + realign_b_bytes(p, pl);
     out->ksplit = pl.ksplit;
 }
 
@@ -528,6 +558,7 @@ struct Buffer {
 struct Workspace {
     Buffer cnt, part;  // split small-M path
     Buffer rows;       // realigned copy of A
+    Buffer rows_b;     // realigned copy of a transposed B
 };
 std::mutex g_ws_mutex;
 std::map<std::pair<int, void *>, Workspace> g_ws;
@@ -567,12 +598,13 @@ bool get_workspace(int dev, void *stream, size_t cnt_bytes, size_t part_bytes, u
     return true;
 }
 
-uint16_t *get_row_buffer(int dev, void *stream, size_t bytes)
+uint16_t *get_row_buffer(int dev, void *stream, size_t bytes, bool second = false)
 {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace &w = g_ws[std::make_pair(dev, stream)];
-    if (!grow(w.rows, bytes, false, stream)) return nullptr;
-    return (uint16_t *)w.rows.ptr;
+    Buffer &b = second ? w.rows_b : w.rows;
+    if (!grow(b, bytes, false, stream)) return nullptr;
+    return (uint16_t *)b.ptr;
 }
 
 int run(const Problem &p, void *stream)
@@ -613,6 +645,21 @@ int run(const Problem &p, void *stream)
     a.out_f32 = elem_c(p) == 4 ? 1 : 0;
     a.ksplit = 1;
     a.kt_per = 0;
+    a.b_trans = b_trans(p) ? 1 : 0;
+    if (pl.realign_b) {
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        uint16_t *B2 = get_row_buffer(dev, stream, realign_b_bytes(p, pl), true);
+        if (!B2) return GEMM_ERR_UNSUPPORTED;   // no ring kernel takes these Bt rows as they are
+        const hipError_t e = launch_realign_rows((const uint16_t *)p.b, p.ldb, p.sB, p.batch, p.N, p.K,
+                                                 row_alignment(p.b, p.ldb, p.sB, p.batch, 2), B2, pl.ldb2,
+                                                 (hipStream_t)stream);
+        if (e != hipSuccess) return GEMM_ERR_LAUNCH;
+        a.B = B2;
+        a.ldb = pl.ldb2;
+        a.sB = p.N * pl.ldb2;
+        a.align_b = 16;
+    }
     a.ws_part = nullptr;
     a.ws_cnt = nullptr;
     if (pl.ksplit > 1) {
@@ -650,7 +697,13 @@ int run(const Problem &p, void *stream)
             pl.align_a = row_alignment(p.a, p.lda, p.sA, p.batch, 2);
             pl.variant = pick_variant(p, pl, &pl.even);
             a.align_a = pl.align_a;
-            if (epi_of(p) != EPI_NONE && pl.variant == 0) return GEMM_ERR_UNSUPPORTED;
+            if (pl.realign_b) {   // the variant for the realigned Bt rows
+                Problem q = p;
+                q.ldb = pl.ldb2;
+                q.sB = p.N * pl.ldb2;
+                pl.variant = pick_variant(q, pl, &pl.even);
+            }
+            if (ring_only(p) && pl.variant == 0) return GEMM_ERR_UNSUPPORTED;
         }
     }
     if (pl.config == CFG_DECODE_SPLIT) {
@@ -705,6 +758,23 @@ int gemm_bf16_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const uint
 {
     const Problem p{GEMM_OP_BF16, batch, M, N, K, (uint64_t)A, (uint64_t)B, (uint64_t)C, lda, ldb, ldc,
                     strideA, strideB, strideC, c_type};
+    return g5::run(p, stream);
+}
+
+int gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda, const uint16_t *Bt, int64_t ldbt,
+                 void *C, int64_t ldc, int c_type, void *stream)
+{
+    const Problem p{GEMM_OP_BF16_NT, 1, M, N, K, (uint64_t)A, (uint64_t)Bt, (uint64_t)C, lda, ldbt, ldc, 0, 0, 0,
+                    c_type};
+    return g5::run(p, stream);
+}
+
+int gemm_bf16_nt_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                         int64_t strideA, const uint16_t *Bt, int64_t ldbt, int64_t strideBt, void *C, int64_t ldc,
+                         int64_t strideC, int c_type, void *stream)
+{
+    const Problem p{GEMM_OP_BF16_NT, batch, M, N, K, (uint64_t)A, (uint64_t)Bt, (uint64_t)C, lda, ldbt, ldc,
+                    strideA, strideBt, strideC, c_type};
     return g5::run(p, stream);
 }
 

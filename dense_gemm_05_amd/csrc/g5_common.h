@@ -73,6 +73,7 @@ struct GemmArgs {
     // in ws_part and ws_cnt.
     int32_t ksplit;
     int32_t kt_per;
+    int32_t b_trans;         // 1: B is given as Bt [N, K] (element (k, n) at B + n*ldb + k)
     float *ws_part;
     unsigned *ws_cnt;
 };

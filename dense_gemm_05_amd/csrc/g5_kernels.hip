@@ -511,8 +511,13 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
 //    partial tiles in slice order, so the result does not depend on which
 //    workgroup finishes last ("Operator & Runtime" §5.2.4: partial sums over
 //    split K, combined in a fixed order).
+//  * BT: B is given transposed, Bt [N, K] row-major (element (k, n) at
+//    Bt + n*ldb + k), the layout of a linear layer's weight and of the keys
+//    of attention scores.  Its slab is then K-contiguous like A's: copied
+//    and swizzled like A's, and read with ds_read_b128 instead of the
+//    transposing read.
 template <int BM, int BN, int WGM, int WGN, int NSA, int NSB, int AV, bool MASKED, int EPI = EPI_NONE,
-          bool SK = false>
+          bool SK = false, bool BT = false>
 __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
 {
     constexpr int NWAVE = WGM * WGN;
@@ -544,6 +549,7 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     constexpr bool GLU = EPI == EPI_SWIGLU;
     constexpr int HALF = BN / 2;                              // GLU: columns per weight half
     static_assert(!GLU || HALF % 8 == 0, "GLU halves must be whole chunks");
+    static_assert(!(GLU && BT), "SwiGLU takes B as [K, 2N]");
     const int64_t ntiles = p.batch * p.tiles_m * p.tiles_n;
     const int64_t wg = SK ? (int64_t)blockIdx.x % ntiles : (int64_t)blockIdx.x;
     const int slice = SK ? (int)((int64_t)blockIdx.x / ntiles) : 0;
@@ -556,12 +562,14 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     const int64_t kbase = SK ? (int64_t)slice * p.kt_per * BK : 0;
     const int64_t K = SK && slice < p.ksplit - 1 ? (int64_t)p.kt_per * BK : p.K - kbase;
     const uint16_t *Abat = (const uint16_t *)p.A + tc.b * p.sA + kbase;
-    const uint16_t *Bbat = (const uint16_t *)p.B + tc.b * p.sB + kbase * ldb;
+    const uint16_t *Bbat = (const uint16_t *)p.B + tc.b * p.sB + (BT ? kbase : kbase * ldb);
     // Byte extents of this batch entry's operands from those bases (reads
     // past them return 0).
     const uint32_t a_bytes = MASKED ? (uint32_t)(((M - 1) * lda + (p.K - kbase)) * 2) : 0x7fffffffu;
     const uint32_t b_bytes =
-        MASKED ? (uint32_t)(((p.K - kbase - 1) * ldb + (GLU ? 2 * N : N)) * 2) : 0x7fffffffu;
+        !MASKED ? 0x7fffffffu
+        : BT    ? (uint32_t)(((N - 1) * ldb + (p.K - kbase)) * 2)
+                : (uint32_t)(((p.K - kbase - 1) * ldb + (GLU ? 2 * N : N)) * 2);
     // Global column of slot column c (a multiple of 8) of the B slab.
     auto b_col = [&](int c) -> int64_t { return GLU ? (c < HALF ? n0 + c : N + n0 + (c - HALF)) : n0 + c; };
 
@@ -586,9 +594,17 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     uint32_t b_voff[LB];
 #pragma unroll
     for (int j = 0; j < LB; ++j) {
-        const int q = 1024 * (b_i0 + j) + 16 * lane;
-        const int k = q / (BN * 2), pc = (q % (BN * 2)) / 16;
-        b_voff[j] = (uint32_t)((k * ldb + b_col((pc ^ swz_bn<BN>(k)) * 8)) * 2);
+        if constexpr (BT) {
+            // as A: 16 slot rows (columns n) of 64 bytes per instruction
+            const int row = 16 * (b_i0 + j) + lane / 4;
+            const int chunk = (lane % 4) ^ ((row >> 1) & 3);
+            const uint32_t off = (uint32_t)((n0 + row) * ldb * 2 + chunk * 16);
+            b_voff[j] = (MASKED && n0 + row >= N) ? 0x80000000u : off;
+        } else {
+            const int q = 1024 * (b_i0 + j) + 16 * lane;
+            const int k = q / (BN * 2), pc = (q % (BN * 2)) / 16;
+            b_voff[j] = (uint32_t)((k * ldb + b_col((pc ^ swz_bn<BN>(k)) * 8)) * 2);
+        }
     }
     // The stage's offset moves the descriptor base (scalar arithmetic) and
     // shrinks its extent to match, so the scalar offset stays 0.
@@ -603,8 +619,9 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
             for (int j = 0; j < LA; ++j) dma<AV>(r, a_voff[j], 0, sl + (a_i0 + j) * (32 * AV));
         } else {
             uint16_t *sl = smem + B_BASE + (ks % NSB) * B_ELEMS;
-            const uint32_t adv = (uint32_t)((int64_t)kt * BK * ldb * 2);
-            const i32x4_t r = make_rsrc(Bbat + (int64_t)kt * BK * ldb, b_bytes - adv);
+            const int64_t kstep = BT ? (int64_t)kt * BK : (int64_t)kt * BK * ldb;   // elements
+            const uint32_t adv = (uint32_t)(kstep * 2);
+            const i32x4_t r = make_rsrc(Bbat + kstep, b_bytes - adv);
 #pragma unroll
             for (int j = 0; j < LB; ++j) dma<16>(r, b_voff[j], 0, sl + (b_i0 + j) * 512);
         }
@@ -619,11 +636,17 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     }
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
-        const int k = g * 8 + (li >> 2);
-        const int ncol = wn * TN + fn * 16 + (li & 3) * 4;
-        const int c = ncol >> 3, half = (ncol >> 2) & 1;
-        b_rd[fn] = k * BN + ((c ^ swz_bn<BN>(k)) * 8) + half * 4;
-        b_rd4[fn] = (k + 4) * BN + ((c ^ swz_bn<BN>(k + 4)) * 8) + half * 4;
+        if constexpr (BT) {
+            const int row = wn * TN + fn * 16 + li;
+            b_rd[fn] = row * BK + ((g ^ ((row >> 1) & 3)) * 8);
+            b_rd4[fn] = 0;
+        } else {
+            const int k = g * 8 + (li >> 2);
+            const int ncol = wn * TN + fn * 16 + (li & 3) * 4;
+            const int c = ncol >> 3, half = (ncol >> 2) & 1;
+            b_rd[fn] = k * BN + ((c ^ swz_bn<BN>(k)) * 8) + half * 4;
+            b_rd4[fn] = (k + 4) * BN + ((c ^ swz_bn<BN>(k + 4)) * 8) + half * 4;
+        }
     }
     struct Frags {
         bf16x8 a[FM];
@@ -637,9 +660,13 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         for (int fm = 0; fm < FM; ++fm) f.a[fm] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(sa + a_rd[fm]));
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G5_LDS(i16x4, sb + b_rd[fn]));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G5_LDS(i16x4, sb + b_rd4[fn]));
-            f.b[fn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            if constexpr (BT) {
+                f.b[fn] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(sb + b_rd[fn]));
+            } else {
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G5_LDS(i16x4, sb + b_rd[fn]));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G5_LDS(i16x4, sb + b_rd4[fn]));
+                f.b[fn] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
         }
     };
 
@@ -715,6 +742,13 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
             const u32x4 v = load_chunk8_bf16(Abat + (m0 + row) * lda, k0 + 8 * c, K, m0 + row < M, p.align_a);
             *(u32x4 *)(sA + row * BK + ((c ^ ((row >> 1) & 3)) * 8)) = v;
         }
+        if constexpr (BT) {
+            for (int q = tid; q < BN * 4; q += NWAVE * 64) {
+                const int row = q >> 2, c = q & 3;
+                const u32x4 v = load_chunk8_bf16(Bbat + (n0 + row) * ldb, k0 + 8 * c, K, n0 + row < N, p.align_b);
+                *(u32x4 *)(sB + row * BK + ((c ^ ((row >> 1) & 3)) * 8)) = v;
+            }
+        } else
         for (int q = tid; q < BK * (BN / 8); q += NWAVE * 64) {
             const int k = q / (BN / 8), c = q % (BN / 8);
             // GLU: chunk c of the up half is column n0 + 8c - HALF of W_u,
@@ -1459,6 +1493,19 @@ __global__ void __launch_bounds__(256) k_zero(GemmArgs p)
 // masked with 16-byte A rows, 3 ring kernel masked with 4-byte A copies.
 // NSA, NSB: slots of the A and B rings of the ring kernels (NSA-2 and NSB-2
 // slabs of copies in flight while one is consumed).
+// Ring kernel variants 1-3 (16-byte A copies aligned / masked, 4-byte A copies masked).
+template <int BM, int BN, int WGM, int WGN, int NSA, int NSB, int EPI, bool SK, bool BT>
+static hipError_t launch_ring(const GemmArgs &a, int variant, dim3 g, dim3 b, hipStream_t s)
+{
+    switch (variant) {
+    case 1: hipLaunchKernelGGL((k_bf16_ms<BM, BN, WGM, WGN, NSA, NSB, 16, false, EPI, SK, BT>), g, b, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_bf16_ms<BM, BN, WGM, WGN, NSA, NSB, 16, true, EPI, SK, BT>), g, b, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_bf16_ms<BM, BN, WGM, WGN, NSA, NSB, 4, true, EPI, SK, BT>), g, b, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int WGM, int WGN, int DWGM, int DWGN, int NSA, int NSB>
 static hipError_t launch_bf16(const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
 {
@@ -1466,15 +1513,11 @@ static hipError_t launch_bf16(const GemmArgs &a, int variant, int64_t grid, hipS
     if constexpr (BM == 128 && BN == 128) {
         // K split over workgroups (128x128 tiles only: the smallest partial tiles)
         if (a.ksplit > 1) {
-            switch (variant) {
-            case 1: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NSA, NSB, 16, false, EPI_NONE, true>), g, b8, 0, s, a); break;
-            case 2: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NSA, NSB, 16, true, EPI_NONE, true>), g, b8, 0, s, a); break;
-            case 3: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NSA, NSB, 4, true, EPI_NONE, true>), g, b8, 0, s, a); break;
-            default: return hipErrorInvalidValue;
-            }
-            return hipGetLastError();
+            if (a.b_trans) return launch_ring<BM, BN, DWGM, DWGN, NSA, NSB, EPI_NONE, true, true>(a, variant, g, b8, s);
+            return launch_ring<BM, BN, DWGM, DWGN, NSA, NSB, EPI_NONE, true, false>(a, variant, g, b8, s);
         }
     }
+    if (a.b_trans) return launch_ring<BM, BN, DWGM, DWGN, NSA, NSB, EPI_NONE, false, true>(a, variant, g, b8, s);
     switch (variant) {
     case 1: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NSA, NSB, 16, false>), g, b8, 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_bf16_ms<BM, BN, DWGM, DWGN, NSA, NSB, 16, true>), g, b8, 0, s, a); break;

@@ -12,8 +12,8 @@ import torch
 from . import _lib
 from ._lib import GemmError, GemmPlan, lib
 
-__all__ = ["gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_silu", "gemm_bf16_swiglu", "plan_query",
-           "GemmError"]
+__all__ = ["gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm_bf16_nt_batched",
+           "gemm_bf16_silu", "gemm_bf16_swiglu", "plan_query", "GemmError"]
 
 
 def _ld(t, inner):
@@ -135,6 +135,49 @@ def gemm_bf16_batched(A, B, C=None, out_dtype=torch.bfloat16):
     return C
 
 
+def gemm_bf16_nt(A, Bt, C=None, out_dtype=torch.bfloat16):
+    """C[M,N] = A[M,K] . Bt[N,K]^T for bfloat16 operands (gemm_bf16_nt): B
+    given transposed, as a linear layer's weight or attention's keys."""
+    if A.dtype != torch.bfloat16 or Bt.dtype != torch.bfloat16:
+        raise TypeError("gemm_bf16_nt takes bfloat16 operands")
+    M, K = A.shape
+    N, K2 = Bt.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    dev = _check_dev(A, Bt)
+    if C is None:
+        C = torch.empty((M, N), dtype=out_dtype, device=dev)
+    if C.shape != (M, N):
+        raise ValueError("C must be [M, N]")
+    st = _launch(lib().gemm_bf16_nt, dev, M, N, K, A.data_ptr(), _ld(A, K), Bt.data_ptr(), _ld(Bt, K),
+                 C.data_ptr(), _ld(C, N), _out_code(C.dtype))
+    if st != 0:
+        raise GemmError(st, "gemm_bf16_nt")
+    return C
+
+
+def gemm_bf16_nt_batched(A, Bt, C=None, out_dtype=torch.bfloat16):
+    """C[b] = A[b] . Bt[b]^T for bfloat16 stacks [batch, M, K] and [batch, N, K]
+    (gemm_bf16_nt_batched), e.g. attention scores Q . K^T; a batch stride of
+    0 broadcasts an operand."""
+    if A.dtype != torch.bfloat16 or Bt.dtype != torch.bfloat16:
+        raise TypeError("gemm_bf16_nt_batched takes bfloat16 operands")
+    batch, M, K = A.shape
+    b2, N, K2 = Bt.shape
+    if batch != b2 or K != K2:
+        raise ValueError("shape mismatch")
+    dev = _check_dev(A, Bt)
+    if C is None:
+        C = torch.empty((batch, M, N), dtype=out_dtype, device=dev)
+    if tuple(C.shape) != (batch, M, N):
+        raise ValueError("C must be [batch, M, N]")
+    st = _launch(lib().gemm_bf16_nt_batched, dev, batch, M, N, K, A.data_ptr(), _ld(A, K), _bstride(A),
+                 Bt.data_ptr(), _ld(Bt, K), _bstride(Bt), C.data_ptr(), _ld(C, N), _bstride(C), _out_code(C.dtype))
+    if st != 0:
+        raise GemmError(st, "gemm_bf16_nt_batched")
+    return C
+
+
 def gemm_bf16_silu(A, B, C=None):
     """C[M,N] = bf16(SiLU(bf16(A . B))) for bfloat16 operands (gemm_bf16_silu)."""
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
@@ -181,10 +224,10 @@ def plan_query(op, M, N, K, batch=1, lda=None, ldb=None, ldc=None, a_addr=0x1000
                c_addr=0x40000000, sA=None, sB=None, sC=None, c_type=_lib.GEMM_OUT_BF16):
     """Host-only: the status and plan a call would produce (no GPU work)."""
     lda = K if lda is None else lda
-    ldb = (2 * N if op == _lib.GEMM_OP_BF16_SWIGLU else N) if ldb is None else ldb
+    ldb = (2 * N if op == _lib.GEMM_OP_BF16_SWIGLU else K if op == _lib.GEMM_OP_BF16_NT else N) if ldb is None else ldb
     ldc = N if ldc is None else ldc
     sA = M * lda if sA is None else sA
-    sB = K * ldb if sB is None else sB
+    sB = (N if op == _lib.GEMM_OP_BF16_NT else K) * ldb if sB is None else sB
     sC = M * ldc if sC is None else sC
     out = GemmPlan()
     st = lib().gemm_plan_query(op, batch, M, N, K, a_addr, lda, sA, b_addr, ldb, sB, c_addr, ldc, sC,

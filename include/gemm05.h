@@ -108,6 +108,27 @@ int gemm_bf16_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
                       void *C, int64_t ldc, int64_t strideC, int c_type,
                       void *stream);
 
+/* BF16 GEMM with B given transposed ("NT"): C [M,N] := A [M,K] . Bt^T, where
+ * Bt [N,K] is row-major with row stride ldbt >= K, so B's element (k, n) is
+ * Bt[n*ldbt + k].  This is the layout of a linear layer's weight ([out, in])
+ * and of the keys in attention scores Q.K^T (the batched GEMM for multi-head
+ * attention named in §1.2 of page "4.1 Tối ưu hiệu năng toán tử GEMM trên
+ * CUDA"): no transposed copy of B is needed.  Everything else follows
+ * gemm_bf16 / gemm_bf16_batched (strideBt is the batch stride of Bt), except
+ * that small M runs on the tiled kernels, and Bt rows that are not 16-byte
+ * aligned are first copied to aligned rows in the workspace described under
+ * Ownership (GEMM_ERR_UNSUPPORTED if that allocation fails). */
+int gemm_bf16_nt(int64_t M, int64_t N, int64_t K,
+                 const uint16_t *A, int64_t lda,
+                 const uint16_t *Bt, int64_t ldbt,
+                 void *C, int64_t ldc, int c_type,
+                 void *stream);
+int gemm_bf16_nt_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                         const uint16_t *A, int64_t lda, int64_t strideA,
+                         const uint16_t *Bt, int64_t ldbt, int64_t strideBt,
+                         void *C, int64_t ldc, int64_t strideC, int c_type,
+                         void *stream);
+
 /* ---- fused epilogues ------------------------------------------------------
  *
  * Page "Operator & Runtime" fuses the element-wise step after a projection
@@ -194,7 +215,8 @@ typedef enum {
     GEMM_OP_SGEMM = 0,       /* gemm_sgemm */
     GEMM_OP_BF16 = 1,        /* gemm_bf16, gemm_bf16_batched */
     GEMM_OP_BF16_SILU = 2,   /* gemm_bf16_silu (batch 1, c_type ignored) */
-    GEMM_OP_BF16_SWIGLU = 3  /* gemm_bf16_swiglu (batch 1, b = Wgu, c_type ignored) */
+    GEMM_OP_BF16_SWIGLU = 3, /* gemm_bf16_swiglu (batch 1, b = Wgu, c_type ignored) */
+    GEMM_OP_BF16_NT = 4      /* gemm_bf16_nt, gemm_bf16_nt_batched (b = Bt, ldb = ldbt) */
 } gemm_op;
 
 /* Validate the arguments of a call and report the plan it would launch,

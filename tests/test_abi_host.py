@@ -326,3 +326,26 @@ def test_ksplit_plans(L, monkeypatch):
     assert st == 0 and p.ksplit == 3 and p.grid == 3 * 12
     st, _ = g5.plan_query(g5.GEMM_OP_BF16, 300, 392, 380)      # 11 stages: too few for 3
     assert st == g5.GEMM_ERR_UNSUPPORTED
+
+
+def test_nt_arguments_and_plans(L):
+    """Transposed B: ldbt >= K, Bt spans N rows of K; every bf16 tile config
+    runs it on its ring kernel; Bt rows that are not 16-byte aligned are
+    realigned first (the general kernel takes no transposed B); small M stays
+    on the tiled kernels."""
+    def nt(M, N, K, lda=None, ldb=None, ldc=None, c=C_ADDR, b=B_ADDR):
+        return L.gemm_bf16_nt(M, N, K, A_ADDR, K if lda is None else lda, b, K if ldb is None else ldb, c,
+                              N if ldc is None else ldc, 0, None)
+    assert nt(4, 8, 16, ldb=15) == g5.GEMM_ERR_INVALID_ARG
+    assert nt(4, 8, 16, b=0) == g5.GEMM_ERR_INVALID_ARG
+    assert nt(4, 8, 16, c=B_ADDR + (7 * 16 + 15) * 2) == g5.GEMM_ERR_INVALID_ARG   # C inside Bt's last row
+    assert nt(0, 8, 16) == g5.GEMM_OK
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_NT, 1024, 12288, 4096)
+    assert st == 0 and p.name == b"bf16_256x192" and p.variant == 1 and p.grid == 256
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_NT, 16, 12288, 4096)
+    assert st == 0 and p.family == 2
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_NT, 300, 392, 264, ldb=265)
+    assert st == 0 and p.variant >= 1 and p.vec_b == 16
+    assert p.workspace_bytes >= 392 * 264 * 2
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_NT, 1024, 1024, 128, batch=32, c_type=1)
+    assert st == 0 and p.name == b"bf16_128x128" and p.variant == 1 and p.workspace_bytes == 0
