@@ -29,7 +29,7 @@ PEAK_BF16_TFLOPS = 2516.6    # 256 CUs x 4096 FLOP/clk x 2.4 GHz, dense
 PEAK_F32_TFLOPS = 157.3      # FP32 matrix
 PEAK_HBM_GBPS = 8000.0
 METRIC = "TFLOPS & % MFMA peak, BF16 1024x4096x12288; GB/s at M=1 decode"
-KERNEL_SRC = os.path.join(ROOT, "dense_gemm_05_amd", "csrc", "g5_kernels.hip")
+KERNEL_SRC = os.path.join(ROOT, "dense_gemm_05_amd", "csrc", "g5_device.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_bf16_ms_256x192_ffn_1024x12288x4096_traffic.json")
 
 
@@ -64,19 +64,11 @@ def kernel_label(plan):
 
 
 def kernel_hash():
-    """Hash of the source the FFN kernel is built from: the shared helpers
-    and the LDS-ring kernel with its epilogue (edits elsewhere in the file,
-    e.g. to the small-M kernels, leave stored counter readings valid)."""
+    """Hash of the source the FFN kernel is built from: the device header
+    holding the shared helpers and the LDS-ring kernel with its epilogue
+    (edits to the other kernels leave stored counter readings valid)."""
     with open(KERNEL_SRC, encoding="utf-8") as fh:
-        src = fh.read()
-    parts = []
-    for start, end in (("// ---------------------------------------------------------------- helpers",
-                        "// ===================================================== bf16 tiled MFMA kernel"),
-                       ("// Epilogue of whole tiles:",
-                        "// ===================================================== fp32 tiled MFMA kernel")):
-        a = src.index(start)
-        parts.append(src[a:src.index(end, a)])
-    return hashlib.sha256("".join(parts).encode()).hexdigest()[:16]
+        return hashlib.sha256(fh.read().encode()).hexdigest()[:16]
 
 
 def main():

@@ -8,7 +8,9 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgemm05.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["g5_kernels.hip", "g5_abi.cpp"]
+# Compiled in parallel: the ring kernel's instantiations are spread over
+# several translation units.
+SOURCES = ["g5_kernels.hip", "g5_ring_bt.hip", "g5_ring_epi.hip", "g5_abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: keep the compiler from emitting packed FP32 VALU
 # instructions (v_pk_*_f32); the hot loops here are matrix-core bound anyway.

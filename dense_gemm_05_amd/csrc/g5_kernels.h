@@ -15,6 +15,11 @@ namespace g5 {
 hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, int variant, int64_t grid,
                          hipStream_t s);
 
+// The bf16 ring kernels with B given transposed (a.b_trans): variants 1-3
+// of the configs 256x192, 256x256, 256x128 and 128x128, the last also with
+// K split (a.ksplit > 1).
+hipError_t launch_ring_bt(int config_id, const GemmArgs &a, int variant, int64_t grid, hipStream_t s);
+
 // The same for a bf16 product with a fused epilogue (EPI_SILU or
 // EPI_SWIGLU; ring kernel variants 1-3 of the configs 256x192, 256x256 and
 // 128x128, with a.tiles_n counting output tiles of tile_n / 2 columns for
