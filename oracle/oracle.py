@@ -52,6 +52,13 @@ def _load():
     lib.oracle_silu_array.argtypes = [i64, p, p]
     lib.oracle_gemm_bf16_silu.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64]
     lib.oracle_swiglu_bf16.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, p, p, i64]
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_decode.restype = ctypes.c_double
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_e4m3_encode_array.argtypes = [i64, p, p]
+    lib.oracle_quantize_rows_e4m3.argtypes = [i64, i64, p, i64, p, i64, p]
+    lib.oracle_gemm_fp8_nt.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, p, i64]
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -187,6 +194,50 @@ def swiglu_bf16(X, Wgu):
     _load().oracle_swiglu_bf16(M, N, K, X.ctypes.data, ldx, Wgu.ctypes.data, ldw, Z.ctypes.data,
                                g.ctypes.data, u.ctypes.data, t.ctypes.data, max(N, 1))
     return Z, g, u, t
+
+
+def e4m3_decode(codes):
+    """Values of E4M3FN codes (uint8), as doubles."""
+    codes = np.asarray(codes, np.uint8)
+    L = _load()
+    return np.array([L.oracle_e4m3_decode(int(c)) for c in codes.ravel()], np.float64).reshape(codes.shape)
+
+
+def e4m3_encode(x):
+    """Nearest E4M3FN codes (ties to even, saturating at 448) of doubles."""
+    x = np.ascontiguousarray(np.asarray(x, np.float64))
+    out = np.empty(x.shape, np.uint8)
+    _load().oracle_e4m3_encode_array(x.size, x.ctypes.data, out.ctypes.data)
+    return out
+
+
+def quantize_rows_e4m3(X):
+    """Per-row E4M3FN quantization of bf16 bit patterns X [rows, cols]:
+    returns (codes uint8 [rows, cols], dequantization factors float32 [rows])."""
+    X, ldx = _rows(X, np.uint16)
+    rows, cols = X.shape
+    Q = np.empty((rows, cols), np.uint8)
+    s = np.empty(rows, np.float32)
+    _load().oracle_quantize_rows_e4m3(rows, cols, X.ctypes.data, ldx, Q.ctypes.data, max(cols, 1), s.ctypes.data)
+    return Q, s
+
+
+def gemm_fp8_nt(A, sa, Bt, sb):
+    """C = diag(sa) (dec(A) . dec(Bt)^T) diag(sb) in double; A [M,K], Bt [N,K]
+    E4M3FN codes; sa [M], sb [N] float32 or None."""
+    A, lda = _rows(A, np.uint8)
+    Bt, ldb = _rows(Bt, np.uint8)
+    M, K = A.shape
+    N, K2 = Bt.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    sa_p = np.ascontiguousarray(sa, np.float32) if sa is not None else None
+    sb_p = np.ascontiguousarray(sb, np.float32) if sb is not None else None
+    C = np.empty((M, N), np.float64)
+    _load().oracle_gemm_fp8_nt(M, N, K, A.ctypes.data, lda, None if sa_p is None else sa_p.ctypes.data,
+                               Bt.ctypes.data, ldb, None if sb_p is None else sb_p.ctypes.data,
+                               C.ctypes.data, max(N, 1))
+    return C
 
 
 def num_threads():

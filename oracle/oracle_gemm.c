@@ -225,6 +225,124 @@ void oracle_swiglu_bf16(int64_t M, int64_t N, int64_t K,
         }
 }
 
+/* ---------------------------------------------------------------------
+ * FP8 quantization and the scaled FP8 product ("Operator & Runtime", §5.4.3,
+ * Example 5-7 and Example 5-8).
+ *
+ * E4M3FN, as the page states it: an 8-bit float with 1 sign bit, 4 exponent
+ * bits and 3 mantissa bits, largest finite value 448.  With exponent bias 7
+ * a code s eeee mmm is (-1)^s (1 + m/8) 2^(e-7) for e >= 1; e = 0 holds the
+ * subnormals (-1)^s m 2^-9; there are no infinities, and e = 15 with m = 7
+ * is NaN (so 448 = 1.75 * 2^8 is the largest finite value).
+ *
+ * Per-row quantization with a scale from the whole row's maximum (Example
+ * 5-7: the row is read first, then quantized): for a row x with
+ * amax = max |x|, each element becomes the nearest E4M3FN value of
+ * x * 448 / amax and dequantizes by the factor amax / 448.  The decision
+ * that picks a code is taken in binary32, the kernel's precision:
+ * inv = fl(448 / amax), y = fl(x * inv), y clamped to [-448, 448], then
+ * rounded to the nearest E4M3FN value, ties to the code with the even
+ * mantissa.  The dequantization factor is fl(amax / 448).  A row of zeros
+ * has amax = 0, inv = 0, codes 0 and factor 0.
+ */
+static double e4m3_decode(uint8_t c)
+{
+    const int e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double v = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+    return (c & 0x80) ? -v : v;
+}
+
+/* Nearest E4M3FN code to x (NaN -> 0x7f, |x| > 448 saturates to +-448). */
+static uint8_t e4m3_encode(double x)
+{
+    if (x != x) return 0x7f;
+    const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    double a = fabs(x);
+    if (a > 448.0) a = 448.0;
+    /* spacing of representable values around a: 2^-9 below 2^-6 (the
+     * subnormals and the first binade share it), else 2^(E-3) for a in
+     * [2^E, 2^(E+1)) */
+    double step;
+    if (a < ldexp(1.0, -6)) {
+        step = ldexp(1.0, -9);
+    } else {
+        int ex;
+        (void)frexp(a, &ex);               /* a in [2^(ex-1), 2^ex) */
+        step = ldexp(1.0, ex - 1 - 3);
+    }
+    /* a / step is exact (power-of-two scaling); nearbyint rounds half to
+     * even, and an even multiple of the step is an even mantissa */
+    const double q = nearbyint(a / step) * step;
+    if (q == 0.0) return sign;
+    if (q < ldexp(1.0, -6)) return (uint8_t)(sign | (uint8_t)(q / ldexp(1.0, -9)));
+    int ex;
+    const double f = frexp(q, &ex);          /* q = f 2^ex, f in [0.5, 1) */
+    const int e = ex - 1 + 7;
+    const int m = (int)((2.0 * f - 1.0) * 8.0);
+    return (uint8_t)(sign | (e << 3) | m);
+}
+
+double oracle_e4m3_decode(uint8_t c) { return e4m3_decode(c); }
+uint8_t oracle_e4m3_encode(double x) { return e4m3_encode(x); }
+
+void oracle_e4m3_encode_array(int64_t n, const double *x, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = e4m3_encode(x[i]);
+}
+
+static float widen_bf16_f(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Per-row E4M3FN quantization of bf16 rows X [rows, cols] into codes Q
+ * (row stride ldq) and dequantization factors scale[rows]. */
+void oracle_quantize_rows_e4m3(int64_t rows, int64_t cols, const uint16_t *X, int64_t ldx,
+                               uint8_t *Q, int64_t ldq, float *scale)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t *x = X + r * ldx;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < cols; ++k) {
+            const float v = fabsf(widen_bf16_f(x[k]));
+            if (v > amax) amax = v;
+        }
+        const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+        scale[r] = amax / 448.0f;
+        for (int64_t k = 0; k < cols; ++k) {
+            float y = widen_bf16_f(x[k]) * inv;
+            if (y > 448.0f) y = 448.0f;
+            if (y < -448.0f) y = -448.0f;
+            Q[r * ldq + k] = e4m3_encode((double)y);
+        }
+    }
+}
+
+/* The scaled FP8 product with B given transposed (Bt [N, K]):
+ * C[i][j] = (sum_k dec(A[i][k]) dec(Bt[j][k])) * sa[i] * sb[j], in double,
+ * k ascending; a NULL scale vector means factors of 1.  The products of two
+ * E4M3FN values (4 significant bits each) and their sums are exact in
+ * double at these sizes. */
+void oracle_gemm_fp8_nt(int64_t M, int64_t N, int64_t K,
+                        const uint8_t *A, int64_t lda, const float *sa,
+                        const uint8_t *Bt, int64_t ldb, const float *sb,
+                        double *C, int64_t ldc)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += e4m3_decode(A[i * lda + k]) * e4m3_decode(Bt[j * ldb + k]);
+            if (sa) acc *= (double)sa[i];
+            if (sb) acc *= (double)sb[j];
+            C[i * ldc + j] = acc;
+        }
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -1,0 +1,151 @@
+"""Pins for the oracle's FP8 (E4M3FN) quantization and scaled product (no GPU).
+
+Page "Operator & Runtime" (section 5.4.3) quantizes to E4M3FN -- one sign,
+four exponent and three mantissa bits, largest finite value 448 -- with a
+scale from the whole row's maximum (Example 5-7), and compares quantizing
+before the GEMM with quantizing inside it (Example 5-8).  Each pin checks
+the oracle against something other than its own code: the page's printed
+values, the format's fixed points, exact small-integer products and
+brute-force rational arithmetic.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import gemm_inputs as gi
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_rows(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return [l.split() for l in fh if l.strip() and not l.startswith("#")]
+
+
+def test_page_example_row_scale(oracle_mod):
+    """Example 5-7: whole-row max 10 turns the first element into code 44
+    (dequantized 55/56); the first block alone (max 1) keeps it exact."""
+    (n, blk, v1, v2, fmax), (scaled, rounded, num, den), (scaled1, deq1, dn, dd, pct) = _golden_rows(
+        "op_runtime_5_4_3_e4m3_row_scale.txt")
+    n, blk, v1, v2 = int(n), int(blk), float(v1), float(v2)
+    x = np.zeros((1, n), np.float32)
+    x[0, 0], x[0, blk] = v1, v2
+    Q, s = oracle_mod.quantize_rows_e4m3(gi.to_bf16_bits(x))
+    assert oracle_mod.e4m3_decode([Q[0, 0]])[0] == float(rounded)
+    assert oracle_mod.e4m3_decode([Q[0, blk]])[0] == float(fmax)
+    assert np.all(Q[0, 1:blk] == 0) and np.all(Q[0, blk + 1:] == 0)
+    deq = float(oracle_mod.e4m3_decode([Q[0, 0]])[0]) * float(s[0])
+    assert abs(deq - int(num) / int(den)) < 1e-6                  # 55/56, up to the binary32 factor
+    assert abs(float(s[0]) - v2 / float(fmax)) <= 2.0 ** -24 * v2 / float(fmax)   # binary32 rounding
+    # the first block alone: scaled value exactly 448, dequantized exactly 1
+    Q1, s1 = oracle_mod.quantize_rows_e4m3(gi.to_bf16_bits(x[:, :blk]))
+    assert oracle_mod.e4m3_decode([Q1[0, 0]])[0] == float(scaled1)
+    # exact in rationals: 448 * (1 / 448); the stored factor is 1/448 in binary32
+    assert abs(oracle_mod.e4m3_decode([Q1[0, 0]])[0] * float(s1[0]) - float(deq1)) <= 2.0 ** -24
+    assert Fraction(int(oracle_mod.e4m3_decode([Q1[0, 0]])[0])) * Fraction(1, 448) == Fraction(deq1)
+    diff = float(deq1) - int(num) / int(den)
+    assert Fraction(diff).limit_denominator(1000) == Fraction(int(dn), int(dd))
+    assert round(100 * diff, 1) == float(pct)
+    assert abs(float(scaled) - v1 * float(fmax) / v2) < 1e-12
+
+
+def test_e4m3fn_fixed_points(oracle_mod):
+    """Values the format's definition fixes: 1 = 0 0111 000, the largest
+    finite 448 = 1.75 * 2^8, NaN at exponent 15 mantissa 7, the smallest
+    subnormal 2^-9 and normal 2^-6, the sign bit."""
+    d = lambda c: float(oracle_mod.e4m3_decode([c])[0])
+    assert d(0b0_0111_000) == 1.0
+    assert d(0b0_1111_110) == 448.0 and d(0b1_1111_110) == -448.0
+    assert math.isnan(d(0x7F)) and math.isnan(d(0xFF))
+    assert d(0b0_1111_101) == 416.0                                # 1.625 * 256
+    assert d(0x01) == 2.0 ** -9 and d(0x07) == 7 * 2.0 ** -9 and d(0x08) == 2.0 ** -6
+    assert d(0x00) == 0.0 and d(0x80) == 0.0 and math.copysign(1, d(0x80)) < 0
+    vals = oracle_mod.e4m3_decode(np.arange(256, dtype=np.uint8))
+    fin = vals[np.isfinite(vals)]
+    assert len(fin) == 254 and fin.max() == 448.0 and fin.min() == -448.0
+    # 127 distinct non-negative values, strictly increasing with the code
+    pos = vals[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+
+
+def test_e4m3fn_encode_round_trip_and_ties(oracle_mod):
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    vals = oracle_mod.e4m3_decode(codes)
+    assert np.array_equal(oracle_mod.e4m3_encode(vals), codes)
+    # midpoints between neighbours go to the neighbour with the even mantissa
+    pos = oracle_mod.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (pos[:-1] + pos[1:]) / 2
+    got = oracle_mod.e4m3_encode(mids)
+    lo = np.arange(0x7E, dtype=np.uint8)
+    want = np.where(lo % 2 == 0, lo, lo + 1).astype(np.uint8)
+    assert np.array_equal(got, want)
+    # hand-picked: 44.8 -> 44, 46 (tie 44/48) -> 48, 2^-10 (tie 0 / 2^-9) -> 0,
+    # 3 * 2^-10 (tie 2^-9 / 2^-8) -> 2^-8, above 448 saturates, NaN -> 0x7f
+    enc = lambda x: int(oracle_mod.e4m3_encode([x])[0])
+    assert oracle_mod.e4m3_decode([enc(44.8)])[0] == 44.0
+    assert oracle_mod.e4m3_decode([enc(46.0)])[0] == 48.0
+    assert enc(2.0 ** -10) == 0x00 and enc(3 * 2.0 ** -10) == 0x02
+    assert enc(460.0) == 0x7E and enc(1e6) == 0x7E and enc(-1e6) == 0xFE
+    assert enc(float("nan")) == 0x7F
+    # nearest: on a fine grid, no finite code is closer than the chosen one
+    xs = np.linspace(-450, 450, 20001)
+    ch = oracle_mod.e4m3_decode(oracle_mod.e4m3_encode(xs))
+    allv = np.sort(oracle_mod.e4m3_decode(np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)))
+    best = np.min(np.abs(xs[:, None] - allv[None, :]), axis=1)
+    inrange = np.abs(xs) <= 448
+    assert np.all(np.abs(xs - ch)[inrange] <= best[inrange] + 1e-12)
+
+
+def test_quantize_rows_properties(oracle_mod):
+    g = np.random.default_rng(7)
+    X = gi.to_bf16_bits(gi.normal(g, (6, 300)))
+    X[3] = 0                                                       # a zero row
+    Q, s = oracle_mod.quantize_rows_e4m3(X)
+    xf = gi.bf16_bits_to_f32(X).astype(np.float64)
+    for r in range(6):
+        amax = np.abs(xf[r]).max()
+        if amax == 0:
+            assert np.all(Q[r] == 0) and s[r] == 0
+            continue
+        assert s[r] == np.float32(np.float32(amax) / np.float32(448))
+        k = np.argmax(np.abs(xf[r]))
+        assert oracle_mod.e4m3_decode([Q[r, k]])[0] == math.copysign(448.0, xf[r, k])
+        # every dequantized value is within half a step of its exact value
+        deq = oracle_mod.e4m3_decode(Q[r]) * float(s[r])
+        rel = np.abs(deq - xf[r]) / np.maximum(np.abs(xf[r]), amax * 2.0 ** -6)
+        assert rel.max() <= 2.0 ** -4 * 1.0001
+
+
+def test_fp8_product_brute_force(oracle_mod):
+    """Tiny scaled products against exact rational arithmetic; scales and
+    codes arbitrary (finite), including subnormals and negative values."""
+    g = np.random.default_rng(11)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    for M, N, K in [(1, 1, 1), (3, 4, 5), (5, 2, 7)]:
+        A = g.choice(finite, (M, K))
+        Bt = g.choice(finite, (N, K))
+        sa = (g.random(M) * 4).astype(np.float32)
+        sb = (g.random(N) * 4).astype(np.float32)
+        C = oracle_mod.gemm_fp8_nt(A, sa, Bt, sb)
+        dec = lambda c: Fraction(float(oracle_mod.e4m3_decode([c])[0]))
+        for i in range(M):
+            for j in range(N):
+                exact = sum(dec(A[i, k]) * dec(Bt[j, k]) for k in range(K)) * Fraction(float(sa[i])) * Fraction(float(sb[j]))
+                assert abs(Fraction(C[i, j]) - exact) <= abs(exact) * Fraction(1, 2 ** 52)
+        C1 = oracle_mod.gemm_fp8_nt(A, None, Bt, None)              # no scales: factors of 1
+        assert C1[0, 0] == float(sum(dec(A[0, k]) * dec(Bt[0, k]) for k in range(K)))
+
+
+def test_fp8_product_small_integers(oracle_mod):
+    """Codes of small integers (exact in E4M3FN) give integer products."""
+    enc = lambda v: oracle_mod.e4m3_encode(np.asarray(v, np.float64))
+    A = enc([[1, 2, -3], [4, 0, 5]])
+    Bt = enc([[1, 1, 1], [2, -1, 0.5]])
+    C = oracle_mod.gemm_fp8_nt(A, None, Bt, None)
+    # [1, 2, -3].[2, -1, 0.5] = 2 - 2 - 1.5; [4, 0, 5].[2, -1, 0.5] = 8 + 2.5
+    assert np.array_equal(C, np.array([[0.0, -1.5], [9.0, 10.5]]))
+    C2 = oracle_mod.gemm_fp8_nt(A, np.array([2, 0.5], np.float32), Bt, np.array([1, 4], np.float32))
+    assert np.array_equal(C2, np.array([[0.0, -12.0], [4.5, 21.0]]))
