@@ -51,6 +51,7 @@ struct Problem {
     uint64_t a, b, c;
     int64_t lda, ldb, ldc, sA, sB, sC;
     int c_type;
+    uint64_t scale_a = 0, scale_b = 0;   // fp8: dequantization factors (float), 0 = none
 };
 
 struct Plan {
@@ -80,14 +81,16 @@ int decode_slices(int64_t strips, int64_t K)
     return ks < 1 ? 1 : (int)ks;
 }
 
-int elem_a(const Problem &p) { return p.op == GEMM_OP_SGEMM ? 4 : 2; }
+int elem_a(const Problem &p) { return p.op == GEMM_OP_SGEMM ? 4 : p.op == GEMM_OP_FP8_NT ? 1 : 2; }
+// K per stage of the LDS-ring kernels: 64-byte slot rows of bf16 or fp8.
+int stage_k(const Problem &p) { return p.op == GEMM_OP_FP8_NT ? 64 : 32; }
 // Fused epilogue of an operation (EPI_NONE for the plain products).
 int epi_of(const Problem &p)
 {
     return p.op == GEMM_OP_BF16_SILU ? EPI_SILU : p.op == GEMM_OP_BF16_SWIGLU ? EPI_SWIGLU : EPI_NONE;
 }
 // B is given transposed, Bt [N, K].
-bool b_trans(const Problem &p) { return p.op == GEMM_OP_BF16_NT; }
+bool b_trans(const Problem &p) { return p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_FP8_NT; }
 // Rows and columns of the B operand as stored: [K, N], Bt [N, K], or the
 // merged gate|up weight [K, 2N] of SwiGLU.
 int64_t b_rows(const Problem &p) { return b_trans(p) ? p.N : p.K; }
@@ -126,11 +129,13 @@ bool overlap(const Range &x, const Range &y) { return x.lo < y.hi && y.lo < x.hi
 int validate(const Problem &p)
 {
     if (p.op != GEMM_OP_SGEMM && p.op != GEMM_OP_BF16 && p.op != GEMM_OP_BF16_SILU && p.op != GEMM_OP_BF16_SWIGLU &&
-        p.op != GEMM_OP_BF16_NT)
+        p.op != GEMM_OP_BF16_NT && p.op != GEMM_OP_FP8_NT)
         return GEMM_ERR_INVALID_ARG;
     if (p.batch < 0 || p.M < 0 || p.N < 0 || p.K < 0) return GEMM_ERR_INVALID_ARG;
-    if ((p.op == GEMM_OP_BF16 || p.op == GEMM_OP_BF16_NT) && p.c_type != GEMM_OUT_BF16 && p.c_type != GEMM_OUT_F32)
+    if ((p.op == GEMM_OP_BF16 || p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_FP8_NT) && p.c_type != GEMM_OUT_BF16 &&
+        p.c_type != GEMM_OUT_F32)
         return GEMM_ERR_INVALID_ARG;
+    if (p.op == GEMM_OP_FP8_NT && (p.batch > 1 || (p.scale_a % 4) || (p.scale_b % 4))) return GEMM_ERR_INVALID_ARG;
     if (epi_of(p) != EPI_NONE && (p.c_type != GEMM_OUT_BF16 || p.batch > 1)) return GEMM_ERR_INVALID_ARG;
     if (p.sA < 0 || p.sB < 0 || p.sC < 0) return GEMM_ERR_INVALID_ARG;
     if (p.batch == 0 || p.M == 0 || p.N == 0) return GEMM_OK;  // nothing to do
@@ -144,6 +149,10 @@ int validate(const Problem &p)
     const Range rb = extent(p.b, p.batch, b_rows(p), b_cols(p), p.ldb, p.sB, elem_a(p));
     if (ra.hi > ((__int128)1 << 63) || rb.hi > ((__int128)1 << 63)) return GEMM_ERR_INVALID_ARG;
     if (overlap(rc, ra) || overlap(rc, rb)) return GEMM_ERR_INVALID_ARG;
+    if (p.scale_a && overlap(rc, Range{(__int128)p.scale_a, (__int128)p.scale_a + 4 * (__int128)p.M}))
+        return GEMM_ERR_INVALID_ARG;
+    if (p.scale_b && overlap(rc, Range{(__int128)p.scale_b, (__int128)p.scale_b + 4 * (__int128)p.N}))
+        return GEMM_ERR_INVALID_ARG;
     return GEMM_OK;
 }
 
@@ -184,7 +193,7 @@ double model_time(const Problem &p, const ConfigInfo &c, double eff)
 double model_time_split(const Problem &p, const ConfigInfo &c, int S, double eff)
 {
     Problem q = p;
-    q.K = cdiv(cdiv(p.K, 32), S) * 32;
+    q.K = cdiv(cdiv(p.K, stage_k(p)), S) * stage_k(p);
     q.batch = p.batch * S;
     const double combine = (double)S * c.tile_m * c.tile_n * 4 / kCopyBytesPerCUperS;
     return model_time(q, c, eff) + combine / eff;
@@ -197,13 +206,14 @@ int find_config_by_name(const char *name)
     return -1;
 }
 
-// Configurations compiled with the fused epilogues.
+// Configurations compiled with the fused epilogues (and with fp8 operands).
 bool has_epilogues(int id) { return id == CFG_BF16_256x192 || id == CFG_BF16_256x256 || id == CFG_BF16_128x128; }
 
 bool config_fits(const Problem &p, int id)
 {
     const ConfigInfo &c = kConfigs[id];
     if (epi_of(p) != EPI_NONE) return has_epilogues(id);
+    if (p.op == GEMM_OP_FP8_NT) return has_epilogues(id);         // fp8 ring kernels: 256x192, 256x256, 128x128
     if (b_trans(p)) return c.family == GEMM_FAMILY_BF16_MFMA;   // the ring kernels of every bf16 tile config
     switch (c.family) {
     case GEMM_FAMILY_BF16_MFMA: return p.op == GEMM_OP_BF16;
@@ -281,7 +291,7 @@ int pick_variant(const Problem &p, const Plan &pl, bool *even)
     // descriptor extent (no partially out-of-range copies).
     // (Bt's chunks run along K like A's: no condition on N.)
     if (!fits || pl.align_b < 16 || pl.align_a < 4 || (!b_trans(p) && p.N % 8 != 0)) return 0;
-    const int ring_k = 32;
+    const int ring_k = stage_k(p);
     const bool c_ok = pl.align_c >= (elem_c(p) == 4 ? 16 : 8);
     *even = !(p.M % c.tile_m || p.N % out_tile_n(p, c) || p.K % ring_k) && pl.align_a >= 16 && c_ok;
     if (*even) return 1;
@@ -292,12 +302,12 @@ int pick_variant(const Problem &p, const Plan &pl, bool *even)
 // with partial tiles addressable by 32-bit buffer offsets per tile.
 bool split_ok(const Problem &p, int S)
 {
-    const int64_t kt = p.K / 32;
+    const int64_t kt = p.K / stage_k(p);
     return S >= 2 && S <= 8 && kt >= 4 * S && p.batch * cdiv(p.M, 128) * cdiv(p.N, 128) * S <= ((int64_t)1 << 24);
 }
 
 // Stages per slice of a K split (the last slice also takes the rest of K).
-int split_kt_per(const Problem &p, int S) { return (int)((p.K / 32) / S); }
+int split_kt_per(const Problem &p, int S) { return (int)((p.K / stage_k(p)) / S); }
 
 // Returns GEMM_OK or GEMM_ERR_UNSUPPORTED.
 int select_plan(const Problem &p, Plan &pl)
@@ -422,7 +432,7 @@ int select_plan(const Problem &p, Plan &pl)
     // The fused epilogues and a transposed B exist only in the ring kernels,
     // so such a call whose rows no ring variant takes is realigned at any
     // size: Bt's rows first, then A's.
-    if (kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && b_trans(p) && pl.align_b < 16) {
+    if (kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && p.op == GEMM_OP_BF16_NT && pl.align_b < 16) {
         pl.realign_b = true;
         pl.ldb2 = (p.K + 7) / 8 * 8;
         pl.align_b = 16;
@@ -431,7 +441,7 @@ int select_plan(const Problem &p, Plan &pl)
         q.sB = p.N * pl.ldb2;
         pl.variant = pick_variant(q, pl, &pl.even);
     }
-    if (kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && pl.align_a < 16 &&
+    if (kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && p.op != GEMM_OP_FP8_NT && pl.align_a < 16 &&
         ((double)p.batch * p.M * p.N * p.K >= (double)(1 << 30) || (ring_only(p) && pl.variant == 0))) {
         Problem q = p;
         if (pl.realign_b) {
@@ -646,6 +656,9 @@ int run(const Problem &p, void *stream)
     a.ksplit = 1;
     a.kt_per = 0;
     a.b_trans = b_trans(p) ? 1 : 0;
+    a.fp8 = p.op == GEMM_OP_FP8_NT ? 1 : 0;
+    a.scale_a = (const float *)p.scale_a;
+    a.scale_b = (const float *)p.scale_b;
     if (pl.realign_b) {
         int dev = 0;
         (void)hipGetDevice(&dev);
@@ -776,6 +789,36 @@ int gemm_bf16_nt_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const u
     const Problem p{GEMM_OP_BF16_NT, batch, M, N, K, (uint64_t)A, (uint64_t)Bt, (uint64_t)C, lda, ldbt, ldc,
                     strideA, strideBt, strideC, c_type};
     return g5::run(p, stream);
+}
+
+int gemm_fp8_nt(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda, const float *scale_a,
+                const uint8_t *Bt, int64_t ldbt, const float *scale_b, void *C, int64_t ldc, int c_type, void *stream)
+{
+    Problem p{GEMM_OP_FP8_NT, 1, M, N, K, (uint64_t)A, (uint64_t)Bt, (uint64_t)C, lda, ldbt, ldc, 0, 0, 0, c_type};
+    p.scale_a = (uint64_t)scale_a;
+    p.scale_b = (uint64_t)scale_b;
+    return g5::run(p, stream);
+}
+
+int gemm_fp8_quantize_rows(int64_t rows, int64_t cols, const uint16_t *X, int64_t ldx, uint8_t *Q, int64_t ldq,
+                           float *scale, void *stream)
+{
+    if (rows < 0 || cols < 0 || rows > 0x7fffffff) return GEMM_ERR_INVALID_ARG;
+    if (rows == 0) return GEMM_OK;
+    if (!scale || ((uint64_t)scale % 4)) return GEMM_ERR_INVALID_ARG;
+    if (cols > 0 && (!X || !Q || ldx < cols || ldq < cols)) return GEMM_ERR_INVALID_ARG;
+    const g5::Range rs{(__int128)(uint64_t)scale, (__int128)(uint64_t)scale + 4 * (__int128)rows};
+    if (cols > 0) {
+        const g5::Range rx = g5::extent((uint64_t)X, 1, rows, cols, ldx, 0, 2);
+        const g5::Range rq = g5::extent((uint64_t)Q, 1, rows, cols, ldq, 0, 1);
+        if (g5::overlap(rx, rq) || g5::overlap(rs, rx) || g5::overlap(rs, rq)) return GEMM_ERR_INVALID_ARG;
+    }
+    int st = g5::check_device();
+    if (st != GEMM_OK) return st;
+    const hipError_t e = g5::launch_quant_rows_e4m3(X, ldx, rows, cols, g5::row_alignment((uint64_t)X, ldx, 0, 1, 2),
+                                                    Q, ldq, g5::row_alignment((uint64_t)Q, ldq, 0, 1, 1), scale,
+                                                    (hipStream_t)stream);
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
 int gemm_bf16_silu(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,

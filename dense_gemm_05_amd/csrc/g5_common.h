@@ -74,6 +74,9 @@ struct GemmArgs {
     int32_t ksplit;
     int32_t kt_per;
     int32_t b_trans;         // 1: B is given as Bt [N, K] (element (k, n) at B + n*ldb + k)
+    int32_t fp8;             // 1: A and Bt hold E4M3FN codes (with b_trans)
+    const float *scale_a;    // fp8: factor of each row of A (M floats) or NULL
+    const float *scale_b;    // fp8: factor of each row of Bt (N floats) or NULL
     float *ws_part;
     unsigned *ws_cnt;
 };

@@ -18,6 +18,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef long i64x2 __attribute__((ext_vector_type(2)));
 
 #define G5_LDS(T, p) ((__attribute__((address_space(3))) T *)(p))
 
@@ -100,6 +101,32 @@ __device__ __forceinline__ u32x4 load_chunk8_bf16(const uint16_t *row, int64_t c
 }
 
 // Same for 4 consecutive floats (one 16-byte chunk of an fp32 row).
+// Load 16 consecutive bytes (16 fp8 codes) starting at element `col` of a
+// row, zero for elements at or beyond `limit` or when the row is out of
+// range; `align` is the byte alignment of the row start (col is a multiple
+// of 16).
+__device__ __forceinline__ u32x4 load_chunk16_u8(const uint8_t *row, int64_t col, int64_t limit, bool row_ok,
+                                                 int align)
+{
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (!row_ok) return v;
+    const uint8_t *p = row + col;
+    if (col + 16 <= limit) {
+        if (align >= 16) return *(const u32x4 *)p;
+        if (align >= 4) {
+            const uint32_t *q = (const uint32_t *)p;
+            v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
+            return v;
+        }
+    }
+    uint32_t e[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) e[i] = (col + i < limit) ? (uint32_t)p[i] : 0u;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v[w] = e[4 * w] | (e[4 * w + 1] << 8) | (e[4 * w + 2] << 16) | (e[4 * w + 3] << 24);
+    return v;
+}
+
 __device__ __forceinline__ u32x4 load_chunk4_f32(const float *row, int64_t col, int64_t limit,
                                                  bool row_ok, int align)
 {
@@ -353,12 +380,22 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
 //    of attention scores.  Its slab is then K-contiguous like A's: copied
 //    and swizzled like A's, and read with ds_read_b128 instead of the
 //    transposing read.
+//  * F8: A and Bt hold E4M3FN codes (with BT): the same 64-byte slot rows
+//    then carry 64 values of K per stage, each 16-byte fragment feeds two
+//    v_mfma_f32_16x16x32_fp8_fp8 (the first takes bytes 0-7 of every lane,
+//    the second bytes 8-15: one permutation of K, the same for both
+//    operands), and the FP32 sums are multiplied by p.scale_a[row] and
+//    p.scale_b[column] before the epilogue ("Operator & Runtime" §5.4.3,
+//    Example 5-7: dequantization by the row's factor).
 template <int BM, int BN, int WGM, int WGN, int NSA, int NSB, int AV, bool MASKED, int EPI = EPI_NONE,
-          bool SK = false, bool BT = false>
+          bool SK = false, bool BT = false, bool F8 = false>
 __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
 {
     constexpr int NWAVE = WGM * WGN;
-    constexpr int BK = 32;
+    constexpr int BK = 32;                                    // slot row: 32 bf16 = 64 bytes
+    constexpr int EB = F8 ? 1 : 2;                            // bytes per operand element
+    constexpr int KS = 64 / EB;                               // K per stage
+    static_assert(!F8 || (BT && EPI == EPI_NONE), "fp8 operands: A and Bt, no fused epilogue");
     constexpr int TM = BM / WGM, TN = BN / WGN;
     constexpr int FM = TM / 16, FN = TN / 16;
     constexpr int NMFMA = FM * FN;
@@ -396,16 +433,16 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     const int64_t M = p.M, N = p.N, lda = p.lda, ldb = p.ldb;
     // This workgroup's part of K starts at kbase; the operand bases below are
     // moved there, so everything after this works on K columns from them.
-    const int64_t kbase = SK ? (int64_t)slice * p.kt_per * BK : 0;
-    const int64_t K = SK && slice < p.ksplit - 1 ? (int64_t)p.kt_per * BK : p.K - kbase;
-    const uint16_t *Abat = (const uint16_t *)p.A + tc.b * p.sA + kbase;
-    const uint16_t *Bbat = (const uint16_t *)p.B + tc.b * p.sB + (BT ? kbase : kbase * ldb);
+    const int64_t kbase = SK ? (int64_t)slice * p.kt_per * KS : 0;
+    const int64_t K = SK && slice < p.ksplit - 1 ? (int64_t)p.kt_per * KS : p.K - kbase;
+    const char *Abat = (const char *)p.A + (tc.b * p.sA + kbase) * EB;
+    const char *Bbat = (const char *)p.B + (tc.b * p.sB + (BT ? kbase : kbase * ldb)) * EB;
     // Byte extents of this batch entry's operands from those bases (reads
     // past them return 0).
-    const uint32_t a_bytes = MASKED ? (uint32_t)(((M - 1) * lda + (p.K - kbase)) * 2) : 0x7fffffffu;
+    const uint32_t a_bytes = MASKED ? (uint32_t)(((M - 1) * lda + (p.K - kbase)) * EB) : 0x7fffffffu;
     const uint32_t b_bytes =
         !MASKED ? 0x7fffffffu
-        : BT    ? (uint32_t)(((N - 1) * ldb + (p.K - kbase)) * 2)
+        : BT    ? (uint32_t)(((N - 1) * ldb + (p.K - kbase)) * EB)
                 : (uint32_t)(((p.K - kbase - 1) * ldb + (GLU ? 2 * N : N)) * 2);
     // Global column of slot column c (a multiple of 8) of the B slab.
     auto b_col = [&](int c) -> int64_t { return GLU ? (c < HALF ? n0 + c : N + n0 + (c - HALF)) : n0 + c; };
@@ -424,7 +461,7 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         const int row = ROWS_PER_A * (a_i0 + j) + lane / LPR;
         const int byte = (lane % LPR) * AV;                   // byte within the slot row
         const int chunk = (byte >> 4) ^ ((row >> 1) & 3);
-        const uint32_t off = (uint32_t)((m0 + row) * lda * 2 + chunk * 16 + (byte & 15));
+        const uint32_t off = (uint32_t)((m0 + row) * lda * EB + chunk * 16 + (byte & 15));
         a_voff[j] = (MASKED && m0 + row >= M) ? 0x80000000u : off;
     }
     const int b_i0 = a_wave ? 0 : (wave - A_W) * LB;
@@ -435,7 +472,7 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
             // as A: 16 slot rows (columns n) of 64 bytes per instruction
             const int row = 16 * (b_i0 + j) + lane / 4;
             const int chunk = (lane % 4) ^ ((row >> 1) & 3);
-            const uint32_t off = (uint32_t)((n0 + row) * ldb * 2 + chunk * 16);
+            const uint32_t off = (uint32_t)((n0 + row) * ldb * EB + chunk * 16);
             b_voff[j] = (MASKED && n0 + row >= N) ? 0x80000000u : off;
         } else {
             const int q = 1024 * (b_i0 + j) + 16 * lane;
@@ -450,14 +487,15 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     auto issue = [&](int kt, int ks) {
         if (a_wave) {
             uint16_t *sl = smem + (ks % NSA) * A_ELEMS;
-            const uint32_t adv = (uint32_t)(kt * BK * 2);
-            const i32x4_t r = make_rsrc(Abat + (int64_t)kt * BK, a_bytes - adv);
+            const uint32_t adv = (uint32_t)(kt * 64);         // 64 bytes of each A row per stage
+            const i32x4_t r = make_rsrc(Abat + adv, a_bytes - adv);
 #pragma unroll
             for (int j = 0; j < LA; ++j) dma<AV>(r, a_voff[j], 0, sl + (a_i0 + j) * (32 * AV));
         } else {
             uint16_t *sl = smem + B_BASE + (ks % NSB) * B_ELEMS;
-            const int64_t kstep = BT ? (int64_t)kt * BK : (int64_t)kt * BK * ldb;   // elements
-            const uint32_t adv = (uint32_t)(kstep * 2);
+            // bytes: 64 of each Bt row, or BK rows of B
+            const int64_t kstep = BT ? (int64_t)kt * 64 : (int64_t)kt * BK * ldb * 2;
+            const uint32_t adv = (uint32_t)kstep;
             const i32x4_t r = make_rsrc(Bbat + kstep, b_bytes - adv);
 #pragma unroll
             for (int j = 0; j < LB; ++j) dma<16>(r, b_voff[j], 0, sl + (b_i0 + j) * 512);
@@ -517,7 +555,13 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         for (int t = 0; t < NMFMA; ++t) {
             if (t < first || t >= first + count) continue;
             const int fn = t / FM, fm = t % FM;
-            acc[fn][fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[fn], f.a[fm], acc[fn][fm], 0, 0, 0);
+            if constexpr (F8) {
+                const i64x2 a2 = __builtin_bit_cast(i64x2, f.a[fm]), b2 = __builtin_bit_cast(i64x2, f.b[fn]);
+                acc[fn][fm] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(b2[0], a2[0], acc[fn][fm], 0, 0, 0);
+                acc[fn][fm] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(b2[1], a2[1], acc[fn][fm], 0, 0, 0);
+            } else {
+                acc[fn][fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[fn], f.a[fm], acc[fn][fm], 0, 0, 0);
+            }
         }
     };
 
@@ -531,7 +575,7 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         asm volatile("" ::: "memory");   // no LDS access moves across the barrier
     };
 
-    const int KT = (int)(K / BK);                             // whole stages
+    const int KT = (int)(K / KS);                             // whole stages
     // A stage past the last reloads the last one, into the slot of the stage
     // it stands for, which is never read again.
     auto issue_clamped = [&](int ks) { issue(ks < KT ? ks : KT - 1, ks); };
@@ -566,23 +610,29 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         }
         if (kt < KT) step(kt, f0, f1);
     }
-    if (MASKED && K % BK != 0) {
+    if (MASKED && K % KS != 0) {
         // K remainder: every copy in flight lands first, then the last stage
         // is loaded element by element with zero fill into slot 0.
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        const int64_t k0 = (int64_t)KT * BK;
+        const int64_t k0 = (int64_t)KT * KS;
         uint16_t *sA = smem, *sB = smem + B_BASE;
         for (int q = tid; q < BM * 4; q += NWAVE * 64) {
             const int row = q >> 2, c = q & 3;
-            const u32x4 v = load_chunk8_bf16(Abat + (m0 + row) * lda, k0 + 8 * c, K, m0 + row < M, p.align_a);
+            const u32x4 v = F8 ? load_chunk16_u8((const uint8_t *)Abat + (m0 + row) * lda, k0 + 16 * c, K,
+                                                 m0 + row < M, p.align_a)
+                               : load_chunk8_bf16((const uint16_t *)Abat + (m0 + row) * lda, k0 + 8 * c, K,
+                                                  m0 + row < M, p.align_a);
             *(u32x4 *)(sA + row * BK + ((c ^ ((row >> 1) & 3)) * 8)) = v;
         }
         if constexpr (BT) {
             for (int q = tid; q < BN * 4; q += NWAVE * 64) {
                 const int row = q >> 2, c = q & 3;
-                const u32x4 v = load_chunk8_bf16(Bbat + (n0 + row) * ldb, k0 + 8 * c, K, n0 + row < N, p.align_b);
+                const u32x4 v = F8 ? load_chunk16_u8((const uint8_t *)Bbat + (n0 + row) * ldb, k0 + 16 * c, K,
+                                                     n0 + row < N, p.align_b)
+                                   : load_chunk8_bf16((const uint16_t *)Bbat + (n0 + row) * ldb, k0 + 8 * c, K,
+                                                      n0 + row < N, p.align_b);
                 *(u32x4 *)(sB + row * BK + ((c ^ ((row >> 1) & 3)) * 8)) = v;
             }
         } else
@@ -592,8 +642,8 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
             // which lies at N + n0 + 8c - HALF of the merged row
             const bool up = GLU && 8 * c >= HALF;
             const int64_t base = up ? N + n0 - HALF : n0;
-            const u32x4 v = load_chunk8_bf16(Bbat + (k0 + k) * ldb + base, 8 * c, up ? N - n0 + HALF : N - n0,
-                                             k0 + k < K, p.align_b);
+            const u32x4 v = load_chunk8_bf16((const uint16_t *)Bbat + (k0 + k) * ldb + base, 8 * c,
+                                             up ? N - n0 + HALF : N - n0, k0 + k < K, p.align_b);
             *(u32x4 *)(sB + k * BN + ((c ^ swz_bn<BN>(k)) * 8)) = v;
         }
         __syncthreads();
@@ -647,6 +697,26 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         if (tid == 0) __hip_atomic_store(p.ws_cnt + wg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
+    if constexpr (F8) {
+        // Dequantization: the row's factor, then the column's, in FP32.
+        if (p.scale_a || p.scale_b) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int64_t m = m0 + wm * TM + fm * 16 + li;
+                const float sa = (p.scale_a && m < M) ? p.scale_a[m] : 1.0f;
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    const int64_t n = n0 + wn * TN + fn * 16 + g * 4;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float sb = (p.scale_b && n + i < N) ? p.scale_b[n + i] : 1.0f;
+                        acc[fn][fm][i] = acc[fn][fm][i] * sa * sb;
+                    }
+                }
+            }
+        }
+    }
+
     void *Cb = (char *)p.C + tc.b * p.sC * (p.out_f32 ? 4 : 2);
     if (p.align_c >= 16 && (!MASKED || N % (p.out_f32 ? 4 : 8) == 0)) {
         // 16-byte aligned rows of C: stage the results through LDS (free
@@ -679,13 +749,13 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
 }
 
 // Ring kernel variants 1-3 (16-byte A copies aligned / masked, 4-byte A copies masked).
-template <int BM, int BN, int WGM, int WGN, int NSA, int NSB, int EPI, bool SK, bool BT>
+template <int BM, int BN, int WGM, int WGN, int NSA, int NSB, int EPI, bool SK, bool BT, bool F8 = false>
 static hipError_t launch_ring(const GemmArgs &a, int variant, dim3 g, dim3 b, hipStream_t s)
 {
     switch (variant) {
-    case 1: hipLaunchKernelGGL((k_bf16_ms<BM, BN, WGM, WGN, NSA, NSB, 16, false, EPI, SK, BT>), g, b, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_bf16_ms<BM, BN, WGM, WGN, NSA, NSB, 16, true, EPI, SK, BT>), g, b, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_bf16_ms<BM, BN, WGM, WGN, NSA, NSB, 4, true, EPI, SK, BT>), g, b, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_bf16_ms<BM, BN, WGM, WGN, NSA, NSB, 16, false, EPI, SK, BT, F8>), g, b, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_bf16_ms<BM, BN, WGM, WGN, NSA, NSB, 16, true, EPI, SK, BT, F8>), g, b, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_bf16_ms<BM, BN, WGM, WGN, NSA, NSB, 4, true, EPI, SK, BT, F8>), g, b, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

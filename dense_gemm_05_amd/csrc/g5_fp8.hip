@@ -1,0 +1,115 @@
+// g5_fp8.hip -- FP8 (E4M3FN) path: per-row quantization of bf16 rows and the
+// launchers of the LDS-ring kernel on E4M3FN operands (page "Operator &
+// Runtime" §5.4.3, Examples 5-7 and 5-8: quantize each row with a factor from
+// the whole row's maximum, before the GEMM, then multiply the codes and
+// dequantize the FP32 sums by the row and column factors).
+#include <hip/hip_runtime.h>
+
+#include "g5_common.h"
+#include "g5_device.h"
+#include "g5_kernels.h"
+
+namespace g5 {
+
+// One workgroup per row.  Pass 1 finds the row's largest magnitude (each
+// thread over its 16-byte chunks, then across the wave by butterfly
+// exchanges, then across the 4 waves in LDS: the tree reduction of the
+// reduce page, "3.1 Tối ưu toán tử CUDA Reduce").  Pass 2 writes the codes:
+// inv = 448 / amax and y = x * inv in binary32, y clamped to [-448, 448]
+// (NaN passes), then the hardware conversion, which rounds to the nearest
+// E4M3FN value, ties to even.  The row's dequantization factor is
+// amax / 448; a row of zeros gets codes 0 and factor 0.  Rows of up to
+// NCH * 2048 elements stay in registers between the passes; longer rows
+// are read again in pass 2.
+template <int NCH>
+__global__ void __launch_bounds__(256) k_quant_rows_e4m3(const uint16_t *X, int64_t ldx, int64_t cols, int align_x,
+                                                         uint8_t *Q, int64_t ldq, int align_q, float *scale)
+{
+    const int64_t r = blockIdx.x;
+    const uint16_t *x = X + r * ldx;
+    uint8_t *q = Q + r * ldq;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool held = cols <= (int64_t)NCH * 2048;
+    u32x4 v[NCH];
+    float m = 0.0f;
+    auto absmax8 = [](float m, const u32x4 &c) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(c[i])), fabsf(bf16_hi(c[i]))));
+        return m;
+    };
+    if (held) {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const int64_t c = (int64_t)tid * 8 + (int64_t)j * 2048;
+            v[j] = c < cols ? load_chunk8_bf16(x, c, cols, true, align_x) : u32x4{0u, 0u, 0u, 0u};
+            m = absmax8(m, v[j]);
+        }
+    } else {
+        for (int64_t c = (int64_t)tid * 8; c < cols; c += 2048) m = absmax8(m, load_chunk8_bf16(x, c, cols, true, align_x));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    __shared__ float red[4];
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
+    if (tid == 0) scale[r] = amax / 448.0f;
+    auto clamp448 = [](float y) { return y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y); };
+    auto emit = [&](int64_t c, const u32x4 &cv) {
+        uint32_t w[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float y0 = clamp448(bf16_lo(cv[2 * h]) * inv), y1 = clamp448(bf16_hi(cv[2 * h]) * inv);
+            const float y2 = clamp448(bf16_lo(cv[2 * h + 1]) * inv), y3 = clamp448(bf16_hi(cv[2 * h + 1]) * inv);
+            int packed = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+            packed = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, packed, true);
+            w[h] = (uint32_t)packed;
+        }
+        if (c + 8 <= cols && align_q >= 8) {
+            u32x2 st = {w[0], w[1]};
+            *(u32x2 *)(q + c) = st;
+        } else {
+            for (int i = 0; i < 8 && c + i < cols; ++i) q[c + i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+        }
+    };
+    if (held) {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const int64_t c = (int64_t)tid * 8 + (int64_t)j * 2048;
+            if (c < cols) emit(c, v[j]);
+        }
+    } else {
+        for (int64_t c = (int64_t)tid * 8; c < cols; c += 2048) emit(c, load_chunk8_bf16(x, c, cols, true, align_x));
+    }
+}
+
+hipError_t launch_quant_rows_e4m3(const uint16_t *X, int64_t ldx, int64_t rows, int64_t cols, int align_x,
+                                  uint8_t *Q, int64_t ldq, int align_q, float *scale, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_quant_rows_e4m3<4>, dim3((unsigned)rows), dim3(256), 0, s, X, ldx, cols, align_x, Q, ldq,
+                       align_q, scale);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN>
+static hipError_t launch_f8(const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
+{
+    const dim3 g((unsigned)grid), b8(WGM * WGN * 64);
+    if constexpr (BM == 128 && BN == 128) {
+        if (a.ksplit > 1) return launch_ring<BM, BN, WGM, WGN, 4, 4, EPI_NONE, true, true, true>(a, variant, g, b8, s);
+    }
+    return launch_ring<BM, BN, WGM, WGN, 4, 4, EPI_NONE, false, true, true>(a, variant, g, b8, s);
+}
+
+hipError_t launch_ring_fp8(int config_id, const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
+{
+    switch (config_id) {
+    case CFG_BF16_256x192: return launch_f8<256, 192, 2, 4>(a, variant, grid, s);
+    case CFG_BF16_256x256: return launch_f8<256, 256, 2, 4>(a, variant, grid, s);
+    case CFG_BF16_128x128: return launch_f8<128, 128, 4, 2>(a, variant, grid, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace g5

@@ -20,6 +20,16 @@ hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, int 
 // K split (a.ksplit > 1).
 hipError_t launch_ring_bt(int config_id, const GemmArgs &a, int variant, int64_t grid, hipStream_t s);
 
+// The ring kernels on E4M3FN operands (a.fp8, a.b_trans): variants 1-3 of
+// the configs 256x192, 256x256 and 128x128, the last also with K split.
+hipError_t launch_ring_fp8(int config_id, const GemmArgs &a, int variant, int64_t grid, hipStream_t s);
+
+// Per-row E4M3FN quantization of `rows` bf16 rows of `cols` elements (row
+// strides ldx, ldq; align_x, align_q the byte alignments of the row starts)
+// into codes Q and dequantization factors scale[rows].
+hipError_t launch_quant_rows_e4m3(const uint16_t *X, int64_t ldx, int64_t rows, int64_t cols, int align_x,
+                                  uint8_t *Q, int64_t ldq, int align_q, float *scale, hipStream_t s);
+
 // The same for a bf16 product with a fused epilogue (EPI_SILU or
 // EPI_SWIGLU; ring kernel variants 1-3 of the configs 256x192, 256x256 and
 // 128x128, with a.tiles_n counting output tiles of tile_n / 2 columns for

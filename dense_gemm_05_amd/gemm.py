@@ -13,7 +13,7 @@ from . import _lib
 from ._lib import GemmError, GemmPlan, lib
 
 __all__ = ["gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm_bf16_nt_batched",
-           "gemm_bf16_silu", "gemm_bf16_swiglu", "plan_query", "GemmError"]
+           "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_fp8_quantize_rows", "gemm_fp8_nt", "plan_query", "GemmError"]
 
 
 def _ld(t, inner):
@@ -178,6 +178,63 @@ def gemm_bf16_nt_batched(A, Bt, C=None, out_dtype=torch.bfloat16):
     return C
 
 
+def _codes(t):
+    """E4M3FN codes: a uint8 tensor or a float8_e4m3fn tensor viewed as bytes."""
+    if t.dtype == torch.uint8:
+        return t
+    if str(t.dtype) == "torch.float8_e4m3fn":
+        return t.view(torch.uint8)
+    raise TypeError("fp8 operands are uint8 codes or float8_e4m3fn tensors")
+
+
+def gemm_fp8_quantize_rows(X, Q=None, scale=None):
+    """Per-row E4M3FN quantization of a bfloat16 [rows, cols] tensor
+    (gemm_fp8_quantize_rows): returns (codes uint8 [rows, cols], float32
+    dequantization factors [rows])."""
+    if X.dtype != torch.bfloat16 or X.dim() != 2:
+        raise TypeError("gemm_fp8_quantize_rows takes a 2-D bfloat16 tensor")
+    rows, cols = X.shape
+    dev = _check_dev(X)
+    if Q is None:
+        Q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty((rows,), dtype=torch.float32, device=dev)
+    Q = _codes(Q)
+    if tuple(Q.shape) != (rows, cols) or tuple(scale.shape) != (rows,) or scale.dtype != torch.float32:
+        raise ValueError("Q must be [rows, cols] codes and scale float32 [rows]")
+    if rows > 1 and scale.stride(0) != 1:
+        raise ValueError("scale must be contiguous")
+    st = _launch(lib().gemm_fp8_quantize_rows, dev, rows, cols, X.data_ptr(), _ld(X, cols), Q.data_ptr(),
+                 _ld(Q, cols), scale.data_ptr())
+    if st != 0:
+        raise GemmError(st, "gemm_fp8_quantize_rows")
+    return Q, scale
+
+
+def gemm_fp8_nt(A, scale_a, Bt, scale_b, C=None, out_dtype=torch.bfloat16):
+    """C[M,N] = (dec(A) . dec(Bt)^T) * scale_a[:, None] * scale_b[None, :] for
+    E4M3FN codes A [M,K] and Bt [N,K] (gemm_fp8_nt); a scale may be None."""
+    A, Bt = _codes(A), _codes(Bt)
+    M, K = A.shape
+    N, K2 = Bt.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    dev = _check_dev(A, Bt)
+    for sc, n, what in ((scale_a, M, "scale_a"), (scale_b, N, "scale_b")):
+        if sc is not None and (sc.dtype != torch.float32 or tuple(sc.shape) != (n,) or (n > 1 and sc.stride(0) != 1)):
+            raise ValueError(f"{what} must be a contiguous float32 vector of {n}")
+    if C is None:
+        C = torch.empty((M, N), dtype=out_dtype, device=dev)
+    if C.shape != (M, N):
+        raise ValueError("C must be [M, N]")
+    st = _launch(lib().gemm_fp8_nt, dev, M, N, K, A.data_ptr(), _ld(A, K),
+                 None if scale_a is None else scale_a.data_ptr(), Bt.data_ptr(), _ld(Bt, K),
+                 None if scale_b is None else scale_b.data_ptr(), C.data_ptr(), _ld(C, N), _out_code(C.dtype))
+    if st != 0:
+        raise GemmError(st, "gemm_fp8_nt")
+    return C
+
+
 def gemm_bf16_silu(A, B, C=None):
     """C[M,N] = bf16(SiLU(bf16(A . B))) for bfloat16 operands (gemm_bf16_silu)."""
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
@@ -224,10 +281,11 @@ def plan_query(op, M, N, K, batch=1, lda=None, ldb=None, ldc=None, a_addr=0x1000
                c_addr=0x40000000, sA=None, sB=None, sC=None, c_type=_lib.GEMM_OUT_BF16):
     """Host-only: the status and plan a call would produce (no GPU work)."""
     lda = K if lda is None else lda
-    ldb = (2 * N if op == _lib.GEMM_OP_BF16_SWIGLU else K if op == _lib.GEMM_OP_BF16_NT else N) if ldb is None else ldb
+    ldb = (2 * N if op == _lib.GEMM_OP_BF16_SWIGLU else K if op in (_lib.GEMM_OP_BF16_NT, _lib.GEMM_OP_FP8_NT)
+           else N) if ldb is None else ldb
     ldc = N if ldc is None else ldc
     sA = M * lda if sA is None else sA
-    sB = (N if op == _lib.GEMM_OP_BF16_NT else K) * ldb if sB is None else sB
+    sB = (N if op in (_lib.GEMM_OP_BF16_NT, _lib.GEMM_OP_FP8_NT) else K) * ldb if sB is None else sB
     sC = M * ldc if sC is None else sC
     out = GemmPlan()
     st = lib().gemm_plan_query(op, batch, M, N, K, a_addr, lda, sA, b_addr, ldb, sB, c_addr, ldc, sC,

@@ -129,6 +129,46 @@ int gemm_bf16_nt_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
                          void *C, int64_t ldc, int64_t strideC, int c_type,
                          void *stream);
 
+/* ---- FP8 (E4M3FN) ---------------------------------------------------------
+ *
+ * Page "Operator & Runtime" (§5.4.3) quantizes to E4M3FN -- 1 sign, 4
+ * exponent and 3 mantissa bits, largest finite value 448 -- with a factor
+ * from the whole row's maximum (Example 5-7), and prefers quantizing the
+ * input once, before the GEMM, to quantizing inside every output tile
+ * (Example 5-8).  Codes are the OCP E4M3FN encoding (exponent bias 7, no
+ * infinities, 0x7f/0xff NaN), which is what gfx950's fp8 matrix cores read.
+ */
+
+/* Per-row quantization of bf16 rows X [rows, cols] (row stride ldx) into
+ * E4M3FN codes Q (row stride ldq, bytes) and dequantization factors
+ * scale[rows] (float, 4-byte aligned): with amax the row's largest
+ * magnitude, inv = 448 / amax and y = x * inv in binary32, y clamped to
+ * [-448, 448], the code is the nearest E4M3FN value to y (ties to the even
+ * mantissa) and scale = amax / 448.  A row of zeros gives codes 0 and
+ * factor 0.  Inputs are expected finite (a NaN element becomes a NaN code).
+ * GEMM_ERR_INVALID_ARG: negative sizes, ldx or ldq < cols, NULL or
+ * unaligned pointers, or overlapping X, Q and scale. */
+int gemm_fp8_quantize_rows(int64_t rows, int64_t cols,
+                           const uint16_t *X, int64_t ldx,
+                           uint8_t *Q, int64_t ldq, float *scale,
+                           void *stream);
+
+/* Scaled FP8 GEMM with B given transposed:
+ *     C[i][j] = (sum_k dec(A[i][k]) * dec(Bt[j][k])) * scale_a[i] * scale_b[j]
+ * A [M,K] and Bt [N,K] E4M3FN codes (row strides lda, ldbt >= K, bytes);
+ * the products are exact in FP32 and summed in FP32; the sum is multiplied
+ * by the row's factor, then the column's (NULL: factors of 1); C is bf16
+ * (rounded once, to nearest even) or float by c_type.  Layout and errors as
+ * gemm_bf16_nt, with: GEMM_ERR_INVALID_ARG for unaligned scale pointers or C
+ * overlapping a scale vector; GEMM_ERR_UNSUPPORTED when Bt's rows are not
+ * 16-byte aligned or A's rows not 4-byte aligned.  Small M runs on the
+ * tiled kernels. */
+int gemm_fp8_nt(int64_t M, int64_t N, int64_t K,
+                const uint8_t *A, int64_t lda, const float *scale_a,
+                const uint8_t *Bt, int64_t ldbt, const float *scale_b,
+                void *C, int64_t ldc, int c_type,
+                void *stream);
+
 /* ---- fused epilogues ------------------------------------------------------
  *
  * Page "Operator & Runtime" fuses the element-wise step after a projection
@@ -216,7 +256,8 @@ typedef enum {
     GEMM_OP_BF16 = 1,        /* gemm_bf16, gemm_bf16_batched */
     GEMM_OP_BF16_SILU = 2,   /* gemm_bf16_silu (batch 1, c_type ignored) */
     GEMM_OP_BF16_SWIGLU = 3, /* gemm_bf16_swiglu (batch 1, b = Wgu, c_type ignored) */
-    GEMM_OP_BF16_NT = 4      /* gemm_bf16_nt, gemm_bf16_nt_batched (b = Bt, ldb = ldbt) */
+    GEMM_OP_BF16_NT = 4,     /* gemm_bf16_nt, gemm_bf16_nt_batched (b = Bt, ldb = ldbt) */
+    GEMM_OP_FP8_NT = 5       /* gemm_fp8_nt (batch 1, b = Bt; scales do not change the plan) */
 } gemm_op;
 
 /* Validate the arguments of a call and report the plan it would launch,

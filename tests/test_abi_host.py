@@ -349,3 +349,32 @@ def test_nt_arguments_and_plans(L):
     assert p.workspace_bytes >= 392 * 264 * 2
     st, p = g5.plan_query(g5.GEMM_OP_BF16_NT, 1024, 1024, 128, batch=32, c_type=1)
     assert st == 0 and p.name == b"bf16_128x128" and p.variant == 1 and p.workspace_bytes == 0
+
+
+def test_fp8_arguments_and_plans(L):
+    """FP8: factors 4-byte aligned and not overlapping C; Bt rows 16-byte
+    aligned and A rows 4-byte aligned (the ring kernels only); 64 K values
+    per stage; quantization arguments."""
+    def f8(M, N, K, lda=None, ldb=None, sa=0, sb=0, c=C_ADDR):
+        return L.gemm_fp8_nt(M, N, K, A_ADDR, K if lda is None else lda, sa, B_ADDR, K if ldb is None else ldb, sb,
+                             c, N, 0, None)
+    assert f8(4, 8, 16, ldb=15) == g5.GEMM_ERR_INVALID_ARG
+    assert f8(4, 8, 16, sa=C_ADDR + 2) == g5.GEMM_ERR_INVALID_ARG             # misaligned factor vector
+    assert f8(4, 8, 16, sb=C_ADDR + 8) == g5.GEMM_ERR_INVALID_ARG             # factors inside C
+    assert f8(4, 8, 20) == g5.GEMM_ERR_UNSUPPORTED                            # Bt rows 4-byte aligned
+    assert f8(4, 8, 20, lda=22, ldb=32) == g5.GEMM_ERR_UNSUPPORTED            # A rows 2-byte aligned
+    assert f8(0, 8, 16) == g5.GEMM_OK
+    st, p = g5.plan_query(g5.GEMM_OP_FP8_NT, 1024, 12288, 4096)
+    assert st == 0 and p.name == b"bf16_256x192" and p.variant == 1 and p.even == 1
+    st, p = g5.plan_query(g5.GEMM_OP_FP8_NT, 1024, 12288, 4128)              # K % 64 = 32: masked
+    assert st == 0 and p.variant == 2
+    st, p = g5.plan_query(g5.GEMM_OP_FP8_NT, 300, 392, 260, ldb=272)
+    assert st == 0 and p.variant == 3
+    st, p = g5.plan_query(g5.GEMM_OP_FP8_NT, 1024, 1536, 4096)
+    assert st == 0 and p.name == b"bf16_128x128" and p.ksplit == 2
+    q = L.gemm_fp8_quantize_rows
+    assert q(-1, 8, A_ADDR, 8, B_ADDR, 8, C_ADDR, None) == g5.GEMM_ERR_INVALID_ARG
+    assert q(4, 8, A_ADDR, 7, B_ADDR, 8, C_ADDR, None) == g5.GEMM_ERR_INVALID_ARG
+    assert q(4, 8, A_ADDR, 8, A_ADDR + 8, 8, C_ADDR, None) == g5.GEMM_ERR_INVALID_ARG   # Q inside X
+    assert q(4, 8, A_ADDR, 8, B_ADDR, 8, C_ADDR + 1, None) == g5.GEMM_ERR_INVALID_ARG   # misaligned factors
+    assert q(0, 8, A_ADDR, 8, B_ADDR, 8, C_ADDR, None) == g5.GEMM_OK

@@ -1,0 +1,166 @@
+"""GPU parity of the FP8 (E4M3FN) path against the oracle, through the C ABI:
+per-row quantization (gemm_fp8_quantize_rows, codes and factors bit for
+bit) and the scaled FP8 product (gemm_fp8_nt).
+
+Page "Operator & Runtime" (section 5.4.3, Examples 5-7 and 5-8): the whole
+row's maximum sets the factor, the input is quantized once before the GEMM,
+and the FP32 sums are dequantized by the row and column factors.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gemm_inputs as gi
+from _gpu_helpers import dev_bf16, host_values
+
+import dense_gemm_05_amd as g5
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[fp8] {msg}", flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _no_forced_config(monkeypatch):
+    monkeypatch.delenv("GEMM_FORCE_CONFIG", raising=False)
+    monkeypatch.delenv("GEMM_FORCE_KSPLIT", raising=False)
+
+
+def dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def check_fp8(C, ref, K, amax_a, amax_b, out, what):
+    """FP32 accumulation of exact products: the FP32 bar over the
+    dequantized operands; a bf16 output adds one rounding (2^-8 |C_ref|)."""
+    bound = 1e-5 * max(K, 1) * amax_a * amax_b + (2.0 ** -8 * np.abs(ref) if out == "bf16" else 0.0)
+    err = np.abs(C - ref)
+    assert np.all(np.isfinite(C)), f"{what}: non-finite output"
+    bad = err > bound
+    if np.any(bad):
+        idx = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} out of bound, first at {idx}: got {C[idx]!r} want {ref[idx]!r}")
+
+
+@pytest.mark.parametrize("rows,cols,ldx_pad,ldq_pad", [
+    (7, 300, 0, 0), (64, 4096, 0, 0), (33, 1000, 5, 3), (5, 8, 0, 1), (3, 13, 2, 0), (300, 264, 8, 8),
+    (4, 8192, 0, 0), (3, 9000, 4, 2),         # rows held in registers up to 8192; longer rows are read twice
+])
+def test_quantize_rows_bit_exact(oracle_mod, rows, cols, ldx_pad, ldq_pad):
+    """Codes and factors equal the oracle's bit for bit: normal rows of
+    several magnitudes, a zero row, a row whose maximum is negative, a row
+    with one nonzero, padded and odd row strides."""
+    _say(f"quantize {rows}x{cols} pads {ldx_pad},{ldq_pad}")
+    g = np.random.default_rng([gi.SEED_BASE + 7000, rows, cols])
+    x = gi.normal(g, (rows, cols + ldx_pad))
+    x *= np.float32(2.0) ** g.integers(-12, 12, (rows, 1)).astype(np.float32)
+    x[0] = 0
+    if rows > 1:
+        x[1, :] = np.abs(x[1, :]) * 0.5
+        x[1, cols // 2] = -np.float32(3.0)
+    if rows > 2:
+        x[2, :] = 0
+        x[2, cols - 1] = np.float32(10.0)
+    X = gi.to_bf16_bits(x)
+    Qref, sref = oracle_mod.quantize_rows_e4m3(np.ascontiguousarray(X[:, :cols]))
+    dX = dev_bf16(X)
+    Qfull = torch.full((rows, cols + ldq_pad), 0xAB, dtype=torch.uint8, device="cuda")
+    scale = torch.full((rows,), float("nan"), dtype=torch.float32, device="cuda")
+    g5.gemm_fp8_quantize_rows(dX[:, :cols], Qfull[:, :cols], scale)
+    Q = Qfull.cpu().numpy()
+    assert np.array_equal(Q[:, :cols], Qref), f"{int((Q[:, :cols] != Qref).sum())} codes differ"
+    assert np.array_equal(scale.cpu().numpy().view(np.uint32), sref.view(np.uint32)), "factors differ"
+    assert np.all(Q[:, cols:] == 0xAB), "row padding of Q was written"
+
+
+def _fp8_case(M, N, K, seed, pa=0, pb=0, scales=True):
+    g = np.random.default_rng([gi.SEED_BASE + 7100 + seed, M, N, K, pa, pb])
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    # codes spread over the whole range, weighted to moderate magnitudes
+    A = g.choice(finite, (M, K + pa))
+    Bt = g.choice(finite, (N, K + pb))
+    sa = (2.0 ** g.uniform(-8, -4, M)).astype(np.float32) if scales else None
+    sb = (2.0 ** g.uniform(-8, -4, N)).astype(np.float32) if scales else None
+    return A, Bt, sa, sb
+
+
+def _amax(oracle_mod, codes, s):
+    d = np.abs(oracle_mod.e4m3_decode(np.unique(codes)))
+    return float(d.max()) * (float(np.abs(s).max()) if s is not None else 1.0)
+
+
+@pytest.mark.parametrize("cfg", [None, "bf16_256x192", "bf16_256x256", "bf16_128x128"])
+@pytest.mark.parametrize("M,N,K,pa,pb,scales", [
+    (300, 392, 256, 0, 0, True),     # 16-byte rows, ragged M and N
+    (300, 392, 260, 0, 12, True),    # A rows 4-byte aligned (4-byte copies), K tail of 4
+    (257, 190, 1000, 8, 8, False),   # no factors, K tail of 40
+    (512, 384, 128, 0, 0, True),     # whole tiles for 128x128
+])
+def test_fp8_nt_parity(oracle_mod, monkeypatch, cfg, M, N, K, pa, pb, scales):
+    _say(f"fp8 {cfg} {M}x{N}x{K} pads {pa},{pb} scales {scales}")
+    A, Bt, sa, sb = _fp8_case(M, N, K, 1, pa, pb, scales)
+    ref = oracle_mod.gemm_fp8_nt(np.ascontiguousarray(A[:, :K]), sa, np.ascontiguousarray(Bt[:, :K]), sb)
+    dA, dB = dev_u8(A), dev_u8(Bt)
+    dsa = None if sa is None else torch.from_numpy(sa).cuda()
+    dsb = None if sb is None else torch.from_numpy(sb).cuda()
+    if cfg:
+        monkeypatch.setenv("GEMM_FORCE_CONFIG", cfg)
+    am, bm = _amax(oracle_mod, A[:, :K], sa), _amax(oracle_mod, Bt[:, :K], sb)
+    for out, od in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+        Cfull = torch.full((M, N + 4), float("nan"), device="cuda", dtype=od)
+        g5.gemm_fp8_nt(dA[:, :K], dsa, dB[:, :K], dsb, Cfull[:, :N])
+        host = host_values(Cfull)
+        check_fp8(host[:, :N], ref, K, am, bm, out, f"fp8 {cfg} {out}")
+        assert np.all(np.isnan(host[:, N:])), "ldc padding was written"
+
+
+@pytest.mark.parametrize("S", [2, 3])
+def test_fp8_nt_ksplit(oracle_mod, monkeypatch, S):
+    M, N, K = 200, 264, 1024
+    A, Bt, sa, sb = _fp8_case(M, N, K, 2)
+    monkeypatch.setenv("GEMM_FORCE_CONFIG", "bf16_128x128")
+    monkeypatch.setenv("GEMM_FORCE_KSPLIT", str(S))
+    C = g5.gemm_fp8_nt(dev_u8(A), torch.from_numpy(sa).cuda(), dev_u8(Bt), torch.from_numpy(sb).cuda(),
+                       out_dtype=torch.float32)
+    ref = oracle_mod.gemm_fp8_nt(A, sa, Bt, sb)
+    check_fp8(host_values(C), ref, K, _amax(oracle_mod, A, sa), _amax(oracle_mod, Bt, sb), "f32", f"fp8 split {S}")
+
+
+def test_fp8_small_integers_exact(oracle_mod):
+    """Codes of small integers and power-of-two factors: every partial sum is
+    an integer below 2^24, so the FP32 result is exact, bit for bit."""
+    g = np.random.default_rng(5)
+    M, N, K = 260, 200, 512
+    vals = np.arange(-6, 7, dtype=np.float64)
+    A = oracle_mod.e4m3_encode(g.choice(vals, (M, K)))
+    Bt = oracle_mod.e4m3_encode(g.choice(vals, (N, K)))
+    sa = (2.0 ** g.integers(-3, 3, M)).astype(np.float32)
+    sb = (2.0 ** g.integers(-3, 3, N)).astype(np.float32)
+    C = g5.gemm_fp8_nt(dev_u8(A), torch.from_numpy(sa).cuda(), dev_u8(Bt), torch.from_numpy(sb).cuda(),
+                       out_dtype=torch.float32)
+    assert np.array_equal(host_values(C), oracle_mod.gemm_fp8_nt(A, sa, Bt, sb))
+
+
+def test_fp8_ffn_end_to_end(oracle_mod):
+    """The FFN projection in FP8: X [1024,4096] quantized per row (tokens),
+    W^T [12288,4096] quantized per row (output channels), both on the GPU
+    (codes bit-exact with the oracle's), then the scaled product against
+    the oracle on sampled rows."""
+    _say("fp8 FFN 1024x12288x4096")
+    X, W = gi.ffn_inputs()
+    Wt = np.ascontiguousarray(W.T)
+    qX, sX = g5.gemm_fp8_quantize_rows(dev_bf16(X))
+    qW, sW = g5.gemm_fp8_quantize_rows(dev_bf16(Wt))
+    rX, rsX = oracle_mod.quantize_rows_e4m3(X)
+    rows = np.array([0, 1, 255, 256, 511, 777, 1023])
+    assert np.array_equal(qX.cpu().numpy(), rX) and np.array_equal(sX.cpu().numpy(), rsX)
+    rW, rsW = oracle_mod.quantize_rows_e4m3(Wt)
+    assert np.array_equal(qW.cpu().numpy(), rW) and np.array_equal(sW.cpu().numpy(), rsW)
+    st, plan = g5.plan_query(g5.GEMM_OP_FP8_NT, 1024, 12288, 4096)
+    assert st == 0 and plan.name == b"bf16_256x192" and plan.variant == 1
+    C = g5.gemm_fp8_nt(qX, sX, qW, sW)
+    ref = oracle_mod.gemm_fp8_nt(np.ascontiguousarray(rX[rows]), rsX[rows], rW, rsW)
+    check_fp8(host_values(C)[rows], ref, 4096, _amax(oracle_mod, rX, rsX), _amax(oracle_mod, rW, rsW), "bf16",
+              "fp8 FFN rows")
