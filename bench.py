@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6    # 256 CUs x 4096 FLOP/clk x 2.4 GHz, dense
 PEAK_F32_TFLOPS = 157.3      # FP32 matrix
 PEAK_HBM_GBPS = 8000.0
+PEAK_FP8_TFLOPS = 5033.2     # dense E4M3 matrix-core peak (2x bf16)
 METRIC = "TFLOPS & % MFMA peak, BF16 1024x4096x12288; GB/s at M=1 decode"
 KERNEL_SRC = os.path.join(ROOT, "dense_gemm_05_amd", "csrc", "g5_device.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_bf16_ms_256x192_ffn_1024x12288x4096_traffic.json")
@@ -42,7 +43,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "sgemm", "batched", "ragged", "swiglu", "shard", "copy"])
+    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "sgemm", "batched", "ragged", "swiglu", "shard", "fp8", "scores_nt", "copy"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--prewarm-seconds", type=float, default=1.0,
@@ -304,6 +305,56 @@ def main():
                           "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "config": plan.name.decode(),
                           "ksplit": plan.ksplit, "rotations": R})
         del dX, dW, dC
+
+    # ------------------------------------------------------------ FP8 FFN
+    if args.only in ("all", "fp8"):
+        # The FFN projection in E4M3FN: W^T [12288,4096] quantized per output
+        # channel once (weights), X quantized per token on every call, then
+        # the scaled FP8 product into bf16.
+        M, N, K = 1024, 12288, 4096
+        X, W = gi.ffn_inputs()
+        Wt = np.ascontiguousarray(W.T)
+        R = rotations(M * K * 3 + N * K + 2 * M * N)
+        dX = [to_dev_bf16(X) for _ in range(R)]
+        qW = [g5.gemm_fp8_quantize_rows(to_dev_bf16(Wt)) for _ in range(R)]
+        qX = [g5.gemm_fp8_quantize_rows(dX[i]) for i in range(R)]
+        dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        gemm = [(lambda i=i: g5.gemm_fp8_nt(qX[i][0], qX[i][1], qW[i][0], qW[i][1], dC[i])) for i in range(R)]
+        quant = [(lambda i=i: g5.gemm_fp8_quantize_rows(dX[i], qX[i][0], qX[i][1])) for i in range(R)]
+        both = [(lambda i=i: (g5.gemm_fp8_quantize_rows(dX[i], qX[i][0], qX[i][1]),
+                              g5.gemm_fp8_nt(qX[i][0], qX[i][1], qW[i][0], qW[i][1], dC[i]))) for i in range(R)]
+        ms_g = timed(gemm, 50, 10)
+        ms_q = timed(quant, 100, 10)
+        ms_b = timed(both, 50, 10)
+        fl = 2.0 * M * N * K
+        tf = fl / (ms_g * 1e-3) / 1e12
+        log(f"fp8 FFN: GEMM {ms_g * 1e3:.2f} us ({tf:.1f} TFLOPS, {tf / PEAK_FP8_TFLOPS:.3f} of fp8 peak); "
+            f"quantize X {ms_q * 1e3:.2f} us; both {ms_b * 1e3:.2f} us")
+        workloads.append({"name": "fp8_ffn_e4m3_1024x12288x4096", "us": round(ms_g * 1e3, 3), "tflops": round(tf, 2),
+                          "frac_peak": round(tf / PEAK_FP8_TFLOPS, 4), "peak": PEAK_FP8_TFLOPS,
+                          "quantize_x_us": round(ms_q * 1e3, 3), "quantize_and_gemm_us": round(ms_b * 1e3, 3),
+                          "rotations": R})
+        del dX, qW, qX, dC
+
+    # ------------------------------------------------------------ attention scores from row-major K
+    if args.only in ("all", "scores_nt"):
+        Q, KT = gi.batched_inputs()
+        Km = np.ascontiguousarray(np.transpose(KT, (0, 2, 1)))
+        bt, M, K = Q.shape
+        N = Km.shape[1]
+        alg_bytes = 2 * Q.size + 2 * Km.size + 4 * bt * M * N
+        R = rotations(alg_bytes)
+        dQ = [to_dev_bf16(Q) for _ in range(R)]
+        dK = [to_dev_bf16(Km) for _ in range(R)]
+        dC = [torch.empty((bt, M, N), device=dev) for _ in range(R)]
+        fns = [(lambda i=i: g5.gemm_bf16_nt_batched(dQ[i], dK[i], dC[i])) for i in range(R)]
+        ms = timed(fns, 100, 10)
+        gbps = alg_bytes / (ms * 1e-3) / 1e9
+        log(f"scores Q.K^T from row-major K (NT): {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s")
+        workloads.append({"name": "scores_nt_bf16_32x1024x1024x128_f32out", "us": round(ms * 1e3, 3),
+                          "GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "alg_bytes": alg_bytes,
+                          "rotations": R})
+        del dQ, dK, dC
 
     out["workloads"] = workloads
 

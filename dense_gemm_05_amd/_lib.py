@@ -31,7 +31,7 @@ GEMM_FAMILY = {0: "none", 1: "zero", 2: "bf16_mfma", 3: "f32_mfma", 4: "decode",
 EXPORTS = ("gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm_bf16_nt_batched",
            "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_fp8_quantize_rows", "gemm_fp8_nt",
            "gemm_status_string",
-           "gemm_plan_query", "gemm_model_local_bytes", "gemm_model_traffic_bytes",
+           "gemm_plan_query", "gemm_model_local_bytes", "gemm_model_traffic_bytes", "gemm_model_quant_traffic",
            "gemm_tile_map")
 
 
@@ -89,6 +89,8 @@ def lib():
     L.gemm_model_local_bytes.restype = i64
     L.gemm_model_traffic_bytes.argtypes = [i64, i64, i64, i64, i64, i64]
     L.gemm_model_traffic_bytes.restype = ctypes.c_double
+    L.gemm_model_quant_traffic.argtypes = [i64] * 9 + [ctypes.POINTER(ctypes.c_double)] * 2
+    L.gemm_model_quant_traffic.restype = None
     L.gemm_tile_map.argtypes = [i64, i64, i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64),
                                 ctypes.POINTER(i64)]
     L.gemm_tile_map.restype = i32

@@ -878,6 +878,21 @@ double gemm_model_traffic_bytes(int64_t M, int64_t N, int64_t K, int64_t m, int6
     return e * M * K * (double)((N + n - 1) / n) + e * K * N * (double)((M + m - 1) / m) + e * M * N;
 }
 
+void gemm_model_quant_traffic(int64_t M, int64_t N, int64_t K, int64_t m, int64_t n, int64_t in_bytes,
+                              int64_t q_bytes, int64_t w_bytes, int64_t out_bytes, double *separate, double *fused)
+{
+    double sep = 0.0, fus = 0.0;
+    if (m > 0 && n > 0 && M >= 0 && N >= 0 && K >= 0) {
+        const double in = (double)in_bytes * M * K, q = (double)q_bytes * M * K;
+        const double col_blocks = (double)((N + n - 1) / n), row_blocks = (double)((M + m - 1) / m);
+        const double common = row_blocks * w_bytes * (double)K * N + (double)out_bytes * M * N;
+        sep = in + q + col_blocks * q + common;     // read once, write the codes, each column block reads them
+        fus = in + col_blocks * in + common;        // read once for the factors, each column block re-reads it
+    }
+    if (separate) *separate = sep;
+    if (fused) *fused = fus;
+}
+
 int gemm_tile_map(int64_t wg, int64_t batch, int64_t tiles_m, int64_t tiles_n, int64_t group_m, int64_t *b,
                   int64_t *tm, int64_t *tn)
 {

@@ -279,6 +279,19 @@ int64_t gemm_model_local_bytes(int64_t m, int64_t n, int64_t k, int64_t elem_byt
 double gemm_model_traffic_bytes(int64_t M, int64_t N, int64_t K, int64_t m, int64_t n,
                                 int64_t elem_bytes);
 
+/* Traffic of quantizing a GEMM input per row, "Operator & Runtime" §5.4.3
+ * Example 5-8: input A [M,K] of in_bytes per element quantized to q_bytes,
+ * weights [K,N] of w_bytes, output [M,N] of out_bytes, m x n output tiles,
+ * factors from each row's maximum.  Quantizing separately reads A once,
+ * writes the codes and has each of the ceil(N/n) column blocks read the
+ * codes; quantizing inside the GEMM reads A once for the factors and has
+ * every column block read A again.  Both add ceil(M/m) reads of the weights
+ * and one write of the output.  Writes the two byte counts (either pointer
+ * may be NULL). */
+void gemm_model_quant_traffic(int64_t M, int64_t N, int64_t K, int64_t m, int64_t n, int64_t in_bytes,
+                              int64_t q_bytes, int64_t w_bytes, int64_t out_bytes, double *separate,
+                              double *fused);
+
 /* The workgroup -> output-tile map used by the tiled kernels: workgroup id
  * `wg` of a launch covering `batch` x tiles_m x tiles_n tiles is assigned
  * (b, tm, tn).  Workgroups are dispatched round-robin over the chip's 8

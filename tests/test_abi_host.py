@@ -378,3 +378,28 @@ def test_fp8_arguments_and_plans(L):
     assert q(4, 8, A_ADDR, 8, A_ADDR + 8, 8, C_ADDR, None) == g5.GEMM_ERR_INVALID_ARG   # Q inside X
     assert q(4, 8, A_ADDR, 8, B_ADDR, 8, C_ADDR + 1, None) == g5.GEMM_ERR_INVALID_ARG   # misaligned factors
     assert q(0, 8, A_ADDR, 8, B_ADDR, 8, C_ADDR, None) == g5.GEMM_OK
+
+
+def test_quant_traffic_model_reproduces_example_5_8(L):
+    """gemm_model_quant_traffic against the page's Example 5-8: 444 MiB when
+    the input is quantized before the GEMM, 620 MiB when inside it."""
+    import ctypes
+    rows = {}
+    vals = None
+    with open(os.path.join(GOLDEN, "op_runtime_5_4_3_quant_traffic.txt")) as fh:
+        for line in fh:
+            if not line.strip() or line.startswith("#"):
+                continue
+            parts = line.split()
+            if vals is None:
+                vals = [int(v) for v in parts]
+            else:
+                rows[parts[0]] = int(parts[1])
+    M, K, N, m, n, inb, qb, wb, ob = vals
+    sep, fus = ctypes.c_double(), ctypes.c_double()
+    L.gemm_model_quant_traffic(M, N, K, m, n, inb, qb, wb, ob, ctypes.byref(sep), ctypes.byref(fus))
+    MiB = 2.0 ** 20
+    assert sep.value / MiB == rows["total_separate"] and fus.value / MiB == rows["total_fused"]
+    common = (-(-M // m)) * wb * K * N + ob * M * N
+    assert common / MiB == rows["common"]
+    assert (sep.value - common) / MiB == rows["input_separate"] and (fus.value - common) / MiB == rows["input_fused"]
