@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "sgemm", "batched", "ragged", "swiglu", "shard", "fp8", "scores_nt", "copy"])
+    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "sgemm", "batched", "ragged", "swiglu", "shard", "fp8", "scores_nt", "decode_nt", "copy"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--prewarm-seconds", type=float, default=1.0,
@@ -200,6 +200,28 @@ def main():
             if M == 1:
                 out["decode_m1"] = {"GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
                                     "us": round(ms * 1e3, 3), "alg_bytes": alg_bytes}
+            del dX, dW, dC
+
+    # ------------------------------------------------------------ decode with a linear layer's weight
+    if args.only in ("all", "decode_nt"):
+        # The same decode rows against W stored as a linear layer's weight,
+        # Wt [12288, 4096]: a GEMV over the contiguous rows of Wt.
+        N, K = 12288, 4096
+        for M in (1, 4, 16):
+            X, W = gi.decode_inputs(M, K, N)
+            Wt = np.ascontiguousarray(W.T)
+            alg_bytes = 2 * (M * K + K * N + M * N)
+            R = rotations(alg_bytes)
+            dX = [to_dev_bf16(X) for _ in range(R)]
+            dW = [to_dev_bf16(Wt) for _ in range(R)]
+            dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+            fns = [(lambda i=i: g5.gemm_bf16_nt(dX[i], dW[i], dC[i])) for i in range(R)]
+            ms = timed(fns, max(200, args.steps), args.warmup)
+            gbps = alg_bytes / (ms * 1e-3) / 1e9
+            log(f"decode NT M={M}: {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM)")
+            workloads.append({"name": f"decode_nt_bf16_m{M}_12288x4096", "us": round(ms * 1e3, 3),
+                              "GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
+                              "alg_bytes": alg_bytes, "rotations": R})
             del dX, dW, dC
 
     # ------------------------------------------------------------ FP32

@@ -34,6 +34,7 @@ const ConfigInfo kConfigs[CFG_COUNT] = {
     {CFG_F32_32x32_WK, GEMM_FAMILY_F32_MFMA, 32, 32, 256, 256, 8 * (32 * 32 + 32 * 36) * 4, "f32_32x32_wholek"},
     {CFG_DECODE_64, GEMM_FAMILY_DECODE, 16, 64, 32, 1024, 16 * 64 * 17 * 4, "decode_64"},
     {CFG_DECODE_SPLIT, GEMM_FAMILY_DECODE, 16, 128, 32, 1024, 16 * 64 * 33 * 4 + 4, "decode_splitk"},
+    {CFG_DECODE_NT, GEMM_FAMILY_DECODE, 16, 16, 32, 512, 8 * 64 * 16, "decode_nt"},
     {CFG_GENERIC, GEMM_FAMILY_GENERIC, 16, 16, 16, 256, 2 * 16 * 17 * 4, "generic"},
 };
 
@@ -218,7 +219,9 @@ bool config_fits(const Problem &p, int id)
     switch (c.family) {
     case GEMM_FAMILY_BF16_MFMA: return p.op == GEMM_OP_BF16;
     case GEMM_FAMILY_F32_MFMA: return p.op == GEMM_OP_SGEMM;
-    case GEMM_FAMILY_DECODE: return p.op == GEMM_OP_BF16 && p.M <= 16 && p.batch <= 65535;
+    case GEMM_FAMILY_DECODE:
+        if (id == CFG_DECODE_NT) return p.op == GEMM_OP_BF16_NT && p.M <= 16 && p.batch <= 65535;
+        return p.op == GEMM_OP_BF16 && p.M <= 16 && p.batch <= 65535;
     case GEMM_FAMILY_GENERIC: return true;
     default: return false;
     }
@@ -237,7 +240,8 @@ void fill_grid(const Problem &p, Plan &pl)
     }
     case GEMM_FAMILY_DECODE:
         pl.tiles_m = 1;
-        pl.tiles_n = cdiv(p.N, c.tile_n);
+        // (decode_nt: three 16-row blocks per workgroup when M > 1)
+        pl.tiles_n = cdiv(p.N, c.tile_n * (pl.config == CFG_DECODE_NT && p.M > 1 ? 3 : 1));
         pl.grid = pl.tiles_n;  // x; batch goes to grid y
         if (pl.config == CFG_DECODE_SPLIT) {
             pl.ks = decode_slices(pl.tiles_n * p.batch, p.K);
@@ -276,6 +280,10 @@ int pick_variant(const Problem &p, const Plan &pl, bool *even)
         *even = !(p.M % c.tile_m || p.N % c.tile_n || p.K % c.tile_k) && pl.align_a >= 16 && pl.align_b >= 16 &&
                 pl.align_c >= 16;
         return *even ? 1 : 0;
+    }
+    if (pl.config == CFG_DECODE_NT) {      // 16-byte loads of Bt rows; 3 row blocks per workgroup for M > 1
+        *even = pl.align_b >= 16;
+        return *even ? (p.M > 1 ? 2 : 1) : -1;
     }
     if (c.family == GEMM_FAMILY_DECODE) {
         *even = (p.N % c.tile_n == 0) && pl.align_b >= 8 && pl.align_a >= 16;
@@ -343,7 +351,10 @@ int select_plan(const Problem &p, Plan &pl)
         // staged at once (one load latency per tile instead of one per slab;
         // 256^3 measured 9.4 us with the double-buffered 64x64 kernel).
         pl.config = CFG_F32_32x32_WK;
-    } else if (p.op == GEMM_OP_BF16 && p.M <= 16 && p.batch <= 65535) {   // (Bt: the tiled kernels)
+    } else if (p.op == GEMM_OP_BF16_NT && p.M <= 16 && p.batch <= 65535 && pl.align_b >= 16) {
+        // Small M with B transposed: a GEMV over the contiguous rows of Bt.
+        pl.config = CFG_DECODE_NT;
+    } else if (p.op == GEMM_OP_BF16 && p.M <= 16 && p.batch <= 65535) {
         // The split path when its preconditions hold and it would use more
         // than one slice; else whole-K strips of 64 columns.
         pl.config = CFG_DECODE_SPLIT;

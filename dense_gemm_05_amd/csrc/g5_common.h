@@ -98,6 +98,7 @@ enum ConfigId {
     CFG_F32_32x32_WK,      // 4 waves (2x2), wave tile 16x16, all of K (<= 256) staged at once
     CFG_DECODE_64,         // small M, 64 columns per workgroup, 16 waves, K split in-workgroup
     CFG_DECODE_SPLIT,      // small M, 128-column strips, K split over workgroups too
+    CFG_DECODE_NT,         // small M, B given transposed: 16 rows of Bt per workgroup, K split over 8 waves
     CFG_GENERIC,
     CFG_COUNT
 };

@@ -725,6 +725,111 @@ hipError_t launch_decode_split(const GemmArgs &a, float *ws, unsigned *cnt, int 
     return hipGetLastError();
 }
 
+// ============================================= small-M path, B given transposed
+//
+// C[M, N] = X[M, K] . Bt[N, K]^T for M <= 16: every output is a dot product
+// along a contiguous row of Bt, the GEMV case of MUSA lesson m11-l5 (rows of
+// the matrix reduced against one vector, here up to 16 vectors at once).
+// A workgroup owns 16 rows of Bt (16 output columns); its NW waves split K
+// into contiguous ranges, so each wave streams 16 row pieces of about
+// K / NW elements, 64 bytes of each row per 32-deep step and the next 64
+// bytes in the next step: every 128-byte line is read whole, by one wave,
+// back to back.  The rows go straight from HBM into the matrix core as the
+// 16-row operand (lane (g, r): row r, 8 consecutive K values; no transpose
+// is needed), X rows as the other operand (rows past M are zero).  The
+// waves' 16x16 partial sums are added in LDS in wave order: the K partition
+// is independent of M, so a row's result does not depend on how many rows
+// the call has.  A K remainder (K % 32) is a final step loaded element by
+// element with zero fill.  RB blocks of 16 rows per workgroup share each X
+// fragment (X is re-read once per block otherwise: as many bytes as Bt when
+// M = 16).  Requires 16-byte aligned rows of Bt.
+template <int NW, int RB>
+__global__ void __launch_bounds__(NW * 64) k_decode_nt(GemmArgs p)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, li = lane & 15;
+    const int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * RB;
+    const int64_t bidx = blockIdx.y;
+    const uint16_t *X = (const uint16_t *)p.A + bidx * p.sA;
+    const uint16_t *Bt = (const uint16_t *)p.B + bidx * p.sB;
+    const bool m_ok = li < M;
+    bool n_ok[RB];
+    const uint16_t *brow[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        n_ok[r] = n0 + 16 * r + li < N;
+        brow[r] = Bt + (n_ok[r] ? n0 + 16 * r + li : 0) * ldb;
+    }
+    const uint16_t *xrow = X + (m_ok ? li : 0) * lda;
+
+    const int64_t whole = K / 32;                          // whole 32-deep steps
+    const int64_t s_begin = whole * wave / NW, s_end = whole * (wave + 1) / NW;
+    f32x4 acc[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto load_b = [&](int r, int64_t s) -> u32x4 {
+        return n_ok[r] ? __builtin_nontemporal_load((const u32x4 *)(brow[r] + s * 32 + g * 8)) : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto load_x = [&](int64_t s) -> u32x4 {
+        return load_chunk8_bf16(xrow, s * 32 + g * 8, K, m_ok, p.align_a);
+    };
+    auto mma = [&](int r, u32x4 b, u32x4 x) {
+        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b), __builtin_bit_cast(bf16x8, x),
+                                                         acc[r], 0, 0, 0);
+    };
+    // D steps of Bt in flight ahead of the matrix core.
+    constexpr int D = RB == 1 ? 4 : 2;
+    int64_t s = s_begin;
+    for (; s + D <= s_end; s += D) {
+        u32x4 b[D][RB], x[D];
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+#pragma unroll
+            for (int r = 0; r < RB; ++r) b[j][r] = load_b(r, s + j);
+#pragma unroll
+        for (int j = 0; j < D; ++j) x[j] = load_x(s + j);
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+#pragma unroll
+            for (int r = 0; r < RB; ++r) mma(r, b[j][r], x[j]);
+    }
+    for (; s < s_end; ++s) {
+        const u32x4 x = load_x(s);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) mma(r, load_b(r, s), x);
+    }
+    if (wave == NW - 1 && K % 32 != 0) {
+        // the K remainder, zero-filled past K
+        const u32x4 x = load_x(whole);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) mma(r, load_chunk8_bf16(brow[r], whole * 32 + g * 8, K, n_ok[r], p.align_b), x);
+    }
+
+    // acc[r][q] of lane (g, li) is the partial sum for column
+    // n0 + 16 r + 4 g + q, row li.
+    __shared__ f32x4 red[NW][RB][64];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) red[wave][r][lane] = acc[r];
+    __syncthreads();
+    if (tid < 64 * RB) {
+        const int r = tid >> 6, t = tid & 63;
+        f32x4 sum = red[0][r][t];
+#pragma unroll
+        for (int w2 = 1; w2 < NW; ++w2) sum += red[w2][r][t];
+        const int m = t & 15, gg = t >> 4;
+        if (m < M) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = n0 + 16 * r + 4 * gg + q;
+                if (n >= N) continue;
+                if (p.out_f32) ((float *)p.C + bidx * p.sC)[m * p.ldc + n] = sum[q];
+                else ((uint16_t *)p.C + bidx * p.sC)[m * p.ldc + n] = (uint16_t)bf16_rne(sum[q]);
+            }
+        }
+    }
+}
+
 // ===================================================== row realignment
 //
 // A bf16 operand whose rows are not 16-byte aligned can only be copied into
@@ -889,6 +994,15 @@ hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, int 
             hipLaunchKernelGGL((k_decode<16, true>), dim3((unsigned)grid, (unsigned)a.batch), dim3(16 * 64), 0, s, a);
         else
             hipLaunchKernelGGL((k_decode<16, false>), dim3((unsigned)grid, (unsigned)a.batch), dim3(16 * 64), 0, s, a);
+        return hipGetLastError();
+    case CFG_DECODE_NT:
+        // variant 1: one 16-row block per workgroup (M = 1); 2: three, which
+        // share each X fragment (for M = 16 the fragments would otherwise
+        // cost as much traffic as Bt: 29.2 against 23.9 us at N = 12288)
+        if (variant == 2)
+            hipLaunchKernelGGL((k_decode_nt<8, 3>), dim3((unsigned)grid, (unsigned)a.batch), dim3(8 * 64), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_decode_nt<8, 1>), dim3((unsigned)grid, (unsigned)a.batch), dim3(8 * 64), 0, s, a);
         return hipGetLastError();
     case CFG_GENERIC:
         if (f32_inputs) hipLaunchKernelGGL(k_generic<float>, dim3((unsigned)grid), dim3(256), 0, s, a);

@@ -342,7 +342,13 @@ def test_nt_arguments_and_plans(L):
     assert nt(0, 8, 16) == g5.GEMM_OK
     st, p = g5.plan_query(g5.GEMM_OP_BF16_NT, 1024, 12288, 4096)
     assert st == 0 and p.name == b"bf16_256x192" and p.variant == 1 and p.grid == 256
+    # small M: a GEMV over the rows of Bt (decode_nt), 16 rows per workgroup,
+    # 48 (three blocks sharing X) when M > 1; unaligned Bt rows: tiled kernels
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_NT, 1, 12288, 4096)
+    assert st == 0 and p.name == b"decode_nt" and p.grid == 768 and p.variant == 1
     st, p = g5.plan_query(g5.GEMM_OP_BF16_NT, 16, 12288, 4096)
+    assert st == 0 and p.name == b"decode_nt" and p.grid == 256 and p.variant == 2
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_NT, 16, 12288, 4100)
     assert st == 0 and p.family == 2
     st, p = g5.plan_query(g5.GEMM_OP_BF16_NT, 300, 392, 264, ldb=265)
     assert st == 0 and p.variant >= 1 and p.vec_b == 16

@@ -121,3 +121,42 @@ def test_nt_linear_weight_full_size(oracle_mod):
     rows = np.array([0, 255, 256, 511, 700, 1023])
     ref = oracle_mod.gemm_bf16(np.ascontiguousarray(X[rows]), W)
     check_bf16(host_values(C)[rows], ref, 4096, "FFN NT rows")
+
+
+@pytest.mark.parametrize("M,N,K,batch", [(1, 12288, 4096, 1), (4, 1000, 1000, 1), (16, 264, 4104, 1), (7, 100, 72, 3),
+                                         (3, 40, 8, 1)])
+def test_nt_small_m(oracle_mod, M, N, K, batch):
+    """Small M with B transposed runs as a GEMV over the rows of Bt
+    (decode_nt): ragged N, K tails (K % 32 != 0), batched, both outputs."""
+    _say(f"nt small-M {batch}x{M}x{N}x{K}")
+    st, plan = g5.plan_query(g5.GEMM_OP_BF16_NT, M, N, K, batch=batch)
+    assert st == 0 and plan.name == b"decode_nt"
+    g = np.random.default_rng([gi.SEED_BASE + 6100, M, N, K, batch])
+    A = gi.to_bf16_bits(gi.normal(g, (batch, M, K)))
+    Bt = gi.to_bf16_bits(gi.normal(g, (batch, N, K), 0.125))
+    for od in (torch.float32, torch.bfloat16):
+        Cfull = torch.full((batch, M, N + 3), float("nan"), device="cuda", dtype=od)
+        if batch == 1:
+            g5.gemm_bf16_nt(dev_bf16(A[0]), dev_bf16(Bt[0]), Cfull[0, :, :N])
+        else:
+            g5.gemm_bf16_nt_batched(dev_bf16(A), dev_bf16(Bt), Cfull[:, :, :N])
+        host = host_values(Cfull)
+        for b in range(batch):
+            ref = oracle_mod.gemm_bf16(A[b], np.ascontiguousarray(Bt[b].T))
+            if od == torch.bfloat16:
+                check_bf16(host[b, :, :N], ref, K, f"nt small-M bf16 {b}")
+            else:
+                check_f32(host[b, :, :N], ref, K, amax_bf16(A[b]), amax_bf16(Bt[b]), f"nt small-M f32 {b}")
+        assert np.all(np.isnan(host[:, :, N:])), "ldc padding was written"
+
+
+def test_nt_small_m_batch_invariance():
+    """Rows of an M = 1, 4, 9 call equal the same rows of an M = 16 call bit
+    for bit (the K partition does not depend on M)."""
+    X, W = gi.decode_inputs(16)
+    dW = dev_bf16(np.ascontiguousarray(W.T))
+    dX = dev_bf16(X)
+    c16 = g5.gemm_bf16_nt(dX, dW).view(torch.int16)
+    for M in (1, 4, 9):
+        cm = g5.gemm_bf16_nt(dX[:M], dW).view(torch.int16)
+        assert torch.equal(cm, c16[:M]), f"M={M} differs from the M=16 rows"
