@@ -52,6 +52,8 @@ def _load():
     lib.oracle_silu_array.argtypes = [i64, p, p]
     lib.oracle_gemm_bf16_silu.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64]
     lib.oracle_swiglu_bf16.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, p, p, i64]
+    lib.oracle_gemm_bf16_affine.argtypes = [i64, i64, i64, p, i64, p, i64, ctypes.c_double, p, ctypes.c_double,
+                                            p, i64, ctypes.c_int, p, i64]
     lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3_decode.restype = ctypes.c_double
     lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
@@ -194,6 +196,29 @@ def swiglu_bf16(X, Wgu):
     _load().oracle_swiglu_bf16(M, N, K, X.ctypes.data, ldx, Wgu.ctypes.data, ldw, Z.ctypes.data,
                                g.ctypes.data, u.ctypes.data, t.ctypes.data, max(N, 1))
     return Z, g, u, t
+
+
+def gemm_bf16_affine(A, B, alpha=1.0, bias=None, beta=0.0, C_old=None):
+    """alpha * (A.B) + bias[j] + beta * C_old[i][j] in double; A, B, bias and a
+    bf16 C_old as bf16 bit patterns (uint16), or a float32 C_old."""
+    A, lda = _rows(A, np.uint16)
+    B, ldb = _rows(B, np.uint16)
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    bias_p = None if bias is None else np.ascontiguousarray(bias, np.uint16)
+    if beta != 0.0:
+        old_f32 = C_old.dtype == np.float32
+        C_old, ldo = _rows(C_old, np.float32 if old_f32 else np.uint16)
+        old_p = C_old.ctypes.data
+    else:
+        old_f32, ldo, old_p = False, 1, None
+    C = np.empty((M, N), np.float64)
+    _load().oracle_gemm_bf16_affine(M, N, K, A.ctypes.data, lda, B.ctypes.data, ldb, float(alpha),
+                                    None if bias_p is None else bias_p.ctypes.data, float(beta), old_p, ldo,
+                                    int(old_f32), C.ctypes.data, max(N, 1))
+    return C
 
 
 def e4m3_decode(codes):

@@ -226,6 +226,33 @@ void oracle_swiglu_bf16(int64_t M, int64_t N, int64_t K,
 }
 
 /* ---------------------------------------------------------------------
+ * The affine epilogue of a bf16 product: C := alpha * (A.B) + bias[j] +
+ * beta * C_old[i][j], the product accumulated exactly (double), every term
+ * widened exactly to double (bias and a bf16 C_old from their bf16 bit
+ * patterns), returned unrounded.  bias may be NULL (no bias); C_old is read
+ * only when beta != 0.  c_old_f32 selects float (1) or bf16 (0) C_old.
+ */
+void oracle_gemm_bf16_affine(int64_t M, int64_t N, int64_t K,
+                             const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                             double alpha, const uint16_t *bias, double beta,
+                             const void *C_old, int64_t ldc_old, int c_old_f32,
+                             double *C, int64_t ldc)
+{
+    oracle_gemm_f64_from_bf16(M, N, K, A, lda, B, ldb, C, ldc);
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            double v = alpha * C[i * ldc + j];
+            if (bias) v += widen_bf16(bias[j]);
+            if (beta != 0.0) {
+                const double old = c_old_f32 ? (double)((const float *)C_old)[i * ldc_old + j]
+                                             : widen_bf16(((const uint16_t *)C_old)[i * ldc_old + j]);
+                v += beta * old;
+            }
+            C[i * ldc + j] = v;
+        }
+}
+
+/* ---------------------------------------------------------------------
  * FP8 quantization and the scaled FP8 product ("Operator & Runtime", §5.4.3,
  * Example 5-7 and Example 5-8).
  *

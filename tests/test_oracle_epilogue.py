@@ -162,3 +162,39 @@ def test_swiglu_matches_its_parts(oracle_mod):
     T = oracle_mod.round_bf16_value(oracle_mod.silu(G))
     assert np.array_equal(gg, G) and np.array_equal(uu, U) and np.array_equal(tt, T)
     assert np.array_equal(Z, T * U)
+
+
+# ---------------------------------------------------------------- affine epilogue
+
+def test_affine_reduces_to_product(oracle_mod):
+    """alpha = 1, no bias, beta = 0 is the plain product; alpha scales it."""
+    A, B = gi.small_case("bf16", 5, 6, 7, seed=3)
+    P = oracle_mod.gemm_bf16(A, B)
+    assert np.array_equal(oracle_mod.gemm_bf16_affine(A, B), P)
+    assert np.array_equal(oracle_mod.gemm_bf16_affine(A, B, alpha=-2.5), -2.5 * P)
+
+
+def test_affine_bias_and_old_c_closed_forms(oracle_mod):
+    """With A = 0 the result is bias[j] + beta * C_old[i][j] exactly (both
+    bf16 and float C_old); with identity A it is alpha * B + bias + beta * C_old."""
+    M, N = 4, 6
+    A0 = np.zeros((M, 3), np.uint16)
+    B = bits(np.arange(3 * N, dtype=np.float32).reshape(3, N))
+    bias = bits(np.array([1, -2, 0.5, 4, -0.25, 8], np.float32))
+    old = np.arange(M * N, dtype=np.float32).reshape(M, N) - 7
+    got = oracle_mod.gemm_bf16_affine(A0, B, alpha=3.0, bias=bias, beta=0.5, C_old=bits(old))
+    want = gi.bf16_bits_to_f32(bias)[None, :].astype(np.float64) + 0.5 * gi.bf16_bits_to_f32(bits(old))
+    assert np.array_equal(got, want)
+    got32 = oracle_mod.gemm_bf16_affine(A0, B, alpha=3.0, bias=None, beta=-1.0, C_old=old)
+    assert np.array_equal(got32, -old.astype(np.float64))
+    I = bits(np.eye(3, dtype=np.float32))
+    got_i = oracle_mod.gemm_bf16_affine(I, B, alpha=2.0, bias=bias, beta=1.0, C_old=old[:3])
+    want_i = 2.0 * gi.bf16_bits_to_f32(B) + gi.bf16_bits_to_f32(bias)[None, :] + old[:3]
+    assert np.array_equal(got_i, want_i.astype(np.float64))
+
+
+def test_affine_ignores_old_c_when_beta_is_zero(oracle_mod):
+    """beta = 0 never reads C_old (NaN there does not propagate)."""
+    A, B = gi.small_case("bf16", 3, 4, 5, seed=4)
+    old = np.full((3, 4), np.nan, np.float32)
+    assert np.all(np.isfinite(oracle_mod.gemm_bf16_affine(A, B, beta=0.0, C_old=old)))
