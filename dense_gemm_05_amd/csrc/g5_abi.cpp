@@ -53,6 +53,9 @@ struct Problem {
     int64_t lda, ldb, ldc, sA, sB, sC;
     int c_type;
     uint64_t scale_a = 0, scale_b = 0;   // fp8: dequantization factors (float), 0 = none
+    // affine epilogue: C := alpha * (A.B) + bias[n] + beta * C
+    float alpha = 1.0f, beta = 0.0f;
+    uint64_t bias = 0;                   // bf16 [N], 0 = none
 };
 
 struct Plan {
@@ -88,8 +91,13 @@ int stage_k(const Problem &p) { return p.op == GEMM_OP_FP8_NT ? 64 : 32; }
 // Fused epilogue of an operation (EPI_NONE for the plain products).
 int epi_of(const Problem &p)
 {
-    return p.op == GEMM_OP_BF16_SILU ? EPI_SILU : p.op == GEMM_OP_BF16_SWIGLU ? EPI_SWIGLU : EPI_NONE;
+    return p.op == GEMM_OP_BF16_SILU     ? EPI_SILU
+           : p.op == GEMM_OP_BF16_SWIGLU ? EPI_SWIGLU
+           : p.op == GEMM_OP_BF16_AFFINE ? EPI_AFFINE
+                                         : EPI_NONE;
 }
+// An affine call with no product to form (alpha == 0: A and B are not read).
+bool no_product(const Problem &p) { return p.op == GEMM_OP_BF16_AFFINE && p.alpha == 0.0f; }
 // B is given transposed, Bt [N, K].
 bool b_trans(const Problem &p) { return p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_FP8_NT; }
 // Rows and columns of the B operand as stored: [K, N], Bt [N, K], or the
@@ -130,21 +138,25 @@ bool overlap(const Range &x, const Range &y) { return x.lo < y.hi && y.lo < x.hi
 int validate(const Problem &p)
 {
     if (p.op != GEMM_OP_SGEMM && p.op != GEMM_OP_BF16 && p.op != GEMM_OP_BF16_SILU && p.op != GEMM_OP_BF16_SWIGLU &&
-        p.op != GEMM_OP_BF16_NT && p.op != GEMM_OP_FP8_NT)
+        p.op != GEMM_OP_BF16_NT && p.op != GEMM_OP_FP8_NT && p.op != GEMM_OP_BF16_AFFINE)
         return GEMM_ERR_INVALID_ARG;
     if (p.batch < 0 || p.M < 0 || p.N < 0 || p.K < 0) return GEMM_ERR_INVALID_ARG;
-    if ((p.op == GEMM_OP_BF16 || p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_FP8_NT) && p.c_type != GEMM_OUT_BF16 &&
-        p.c_type != GEMM_OUT_F32)
+    if ((p.op == GEMM_OP_BF16 || p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_FP8_NT || p.op == GEMM_OP_BF16_AFFINE) &&
+        p.c_type != GEMM_OUT_BF16 && p.c_type != GEMM_OUT_F32)
         return GEMM_ERR_INVALID_ARG;
     if (p.op == GEMM_OP_FP8_NT && (p.batch > 1 || (p.scale_a % 4) || (p.scale_b % 4))) return GEMM_ERR_INVALID_ARG;
-    if (epi_of(p) != EPI_NONE && (p.c_type != GEMM_OUT_BF16 || p.batch > 1)) return GEMM_ERR_INVALID_ARG;
+    if ((p.op == GEMM_OP_BF16_SILU || p.op == GEMM_OP_BF16_SWIGLU) && (p.c_type != GEMM_OUT_BF16 || p.batch > 1))
+        return GEMM_ERR_INVALID_ARG;
+    if (p.op == GEMM_OP_BF16_AFFINE && (!std::isfinite(p.alpha) || !std::isfinite(p.beta) || (p.bias % 2)))
+        return GEMM_ERR_INVALID_ARG;
     if (p.sA < 0 || p.sB < 0 || p.sC < 0) return GEMM_ERR_INVALID_ARG;
     if (p.batch == 0 || p.M == 0 || p.N == 0) return GEMM_OK;  // nothing to do
     if (p.ldc < p.N || p.c == 0) return GEMM_ERR_INVALID_ARG;
     if (p.batch > 1 && (__int128)p.sC < (__int128)(p.M - 1) * p.ldc + p.N) return GEMM_ERR_INVALID_ARG;
     const Range rc = extent(p.c, p.batch, p.M, p.N, p.ldc, p.sC, elem_c(p));
     if (rc.hi > ((__int128)1 << 63)) return GEMM_ERR_INVALID_ARG;
-    if (p.K == 0) return GEMM_OK;
+    if (p.bias && overlap(rc, Range{(__int128)p.bias, (__int128)p.bias + 2 * (__int128)p.N})) return GEMM_ERR_INVALID_ARG;
+    if (p.K == 0 || no_product(p)) return GEMM_OK;
     if (p.lda < p.K || p.ldb < b_cols(p) || p.a == 0 || p.b == 0) return GEMM_ERR_INVALID_ARG;
     const Range ra = extent(p.a, p.batch, p.M, p.K, p.lda, p.sA, elem_a(p));
     const Range rb = extent(p.b, p.batch, b_rows(p), b_cols(p), p.ldb, p.sB, elem_a(p));
@@ -329,7 +341,7 @@ int select_plan(const Problem &p, Plan &pl)
     pl.align_a = row_alignment(p.a, p.lda, p.sA, p.batch, ea);
     pl.align_b = row_alignment(p.b, p.ldb, p.sB, p.batch, ea);
     pl.align_c = row_alignment(p.c, p.ldc, p.sC, p.batch, ec);
-    if (p.K == 0) {
+    if (p.K == 0 || no_product(p)) {
         pl.config = CFG_ZERO;
         fill_grid(p, pl);
         return GEMM_OK;
@@ -406,7 +418,7 @@ int select_plan(const Problem &p, Plan &pl)
         // 128x128 tiles when the model gives it the shortest time
         // (page "Operator & Runtime" §5.2.4 splits the reduction dimension
         // to occupy the device).
-        if (bf16 && epi_of(p) == EPI_NONE) {
+        if (bf16 && (epi_of(p) == EPI_NONE || epi_of(p) == EPI_AFFINE)) {
             Plan t = pl;
             t.config = CFG_BF16_128x128;
             bool ev = false;
@@ -427,7 +439,7 @@ int select_plan(const Problem &p, Plan &pl)
     if (const char *fk = std::getenv("GEMM_FORCE_KSPLIT")) {
         // diagnostic: force the K split of the 128x128 ring kernel (1 = none)
         const int S = std::atoi(fk);
-        if (S >= 1 && pl.config == CFG_BF16_128x128 && epi_of(p) == EPI_NONE) {
+        if (S >= 1 && pl.config == CFG_BF16_128x128 && (epi_of(p) == EPI_NONE || epi_of(p) == EPI_AFFINE)) {
             if (S > 1 && !split_ok(p, S)) return GEMM_ERR_UNSUPPORTED;
             pl.ksplit = S;
         }
@@ -670,6 +682,10 @@ int run(const Problem &p, void *stream)
     a.fp8 = p.op == GEMM_OP_FP8_NT ? 1 : 0;
     a.scale_a = (const float *)p.scale_a;
     a.scale_b = (const float *)p.scale_b;
+    a.alpha = p.alpha;
+    a.beta = p.beta;
+    a.bias = (const uint16_t *)p.bias;
+    a.align_bias = row_alignment(p.bias, 0, 0, 1, 2);
     if (pl.realign_b) {
         int dev = 0;
         (void)hipGetDevice(&dev);
@@ -747,9 +763,11 @@ int run(const Problem &p, void *stream)
         pl.variant = pick_variant(p, pl, &pl.even);
         a.tiles_n = pl.tiles_n;
     }
-    const hipError_t e = pl.config == CFG_ZERO || epi_of(p) == EPI_NONE
-                             ? launch_config(pl.config, p.op == GEMM_OP_SGEMM, a, pl.variant, pl.grid, (hipStream_t)stream)
-                             : launch_fused(pl.config, epi_of(p), a, pl.variant, pl.grid, (hipStream_t)stream);
+    const hipError_t e =
+        pl.config == CFG_ZERO ? (p.op == GEMM_OP_BF16_AFFINE ? launch_affine_no_product(a, pl.grid, (hipStream_t)stream)
+                                                             : launch_config(pl.config, false, a, 0, pl.grid, (hipStream_t)stream))
+        : epi_of(p) == EPI_NONE ? launch_config(pl.config, p.op == GEMM_OP_SGEMM, a, pl.variant, pl.grid, (hipStream_t)stream)
+                                : launch_fused(pl.config, epi_of(p), a, pl.variant, pl.grid, (hipStream_t)stream);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
@@ -845,6 +863,18 @@ int gemm_bf16_swiglu(int64_t M, int64_t N, int64_t K, const uint16_t *X, int64_t
 {
     const Problem p{GEMM_OP_BF16_SWIGLU, 1, M, N, K, (uint64_t)X, (uint64_t)Wgu, (uint64_t)Z, ldx, ldw, ldz, 0, 0,
                     0, GEMM_OUT_BF16};
+    return g5::run(p, stream);
+}
+
+int gemm_bf16_affine(int64_t batch, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda, int64_t strideA,
+                     const uint16_t *B, int64_t ldb, int64_t strideB, float alpha, const uint16_t *bias, float beta,
+                     void *C, int64_t ldc, int64_t strideC, int c_type, void *stream)
+{
+    Problem p{GEMM_OP_BF16_AFFINE, batch, M, N, K, (uint64_t)A, (uint64_t)B, (uint64_t)C, lda, ldb, ldc,
+              strideA, strideB, strideC, c_type};
+    p.alpha = alpha;
+    p.beta = beta;
+    p.bias = (uint64_t)bias;
     return g5::run(p, stream);
 }
 

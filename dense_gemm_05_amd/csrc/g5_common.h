@@ -79,10 +79,15 @@ struct GemmArgs {
     const float *scale_b;    // fp8: factor of each row of Bt (N floats) or NULL
     float *ws_part;
     unsigned *ws_cnt;
+    // EPI_AFFINE: C := alpha * (A.B) + bias[n] + beta * C (C read only when
+    // beta != 0; bias bf16 [N] or NULL, its start `align_bias`-byte aligned).
+    float alpha, beta;
+    const uint16_t *bias;
+    int32_t align_bias;
 };
 
 // Fused epilogues of the bf16 ring kernels.
-enum Epilogue { EPI_NONE = 0, EPI_SILU = 1, EPI_SWIGLU = 2 };
+enum Epilogue { EPI_NONE = 0, EPI_SILU = 1, EPI_SWIGLU = 2, EPI_AFFINE = 3 };
 
 // Compiled configurations.  The selector picks one; GEMM_FORCE_CONFIG may
 // name one explicitly.

@@ -267,9 +267,11 @@ __device__ __forceinline__ int swz_bn(int k)
 template <int BM, int BN, int WGM, int WGN, int LDS_BYTES, typename TOut, bool MASKED, int EPI = EPI_NONE, int NFN,
           int NFM>
 __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM], uint16_t *lds, void *Cb,
-                                                   int64_t ldc, int64_t m0, int64_t n0, int64_t M, int64_t N)
+                                                   int64_t ldc, int64_t m0, int64_t n0, int64_t M, int64_t N,
+                                                   const GemmArgs *pa = nullptr)
 {
-    static_assert(EPI == EPI_NONE || sizeof(TOut) == 2, "fused epilogues write bf16");
+    static_assert(EPI == EPI_NONE || (EPI == EPI_AFFINE ? sizeof(TOut) == 4 : sizeof(TOut) == 2),
+                  "SiLU and SwiGLU stage bf16; the affine epilogue stages the FP32 sums");
     constexpr int TM = BM / WGM, TN = BN / WGN;
     constexpr int ESZ = (int)sizeof(TOut);
     constexpr int PITCH = BN * ESZ + 16;                     // bytes per staged row
@@ -316,6 +318,60 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
                 const u32x4 u = *(const u32x4 *)(L + r * PITCH + (c + OPR) * 16);
                 char *dst = (char *)Cb + ((m0 + pass * RP + r) * ldc + n0) * 2 + c * 16;
                 __builtin_nontemporal_store(epi_swiglu8(g, u), (u32x4 *)dst);
+            }
+        } else if constexpr (EPI == EPI_AFFINE) {
+            // 8 columns per step: v = alpha * sum + (bias[n] + beta * C[m][n])
+            // in FP32, rounded once to C's type (bf16 or float).
+            constexpr int OPR = BN / 8;
+            const float alpha = pa->alpha, beta = pa->beta;
+            const bool f32o = pa->out_f32 != 0;
+            for (int q = tid; q < RP * OPR; q += NT) {
+                const int r = q / OPR, c = q % OPR;
+                const int64_t m = m0 + pass * RP + r, n = n0 + (int64_t)c * 8;
+                if (MASKED && (m >= M || n + 8 > N)) continue;
+                const f32x4 s0 = *(const f32x4 *)(L + r * PITCH + c * 32);
+                const f32x4 s1 = *(const f32x4 *)(L + r * PITCH + c * 32 + 16);
+                float t[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                if (pa->bias) {
+                    const u32x4 bb = load_chunk8_bf16(pa->bias, n, N, true, pa->align_bias);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        t[2 * i] = bf16_lo(bb[i]);
+                        t[2 * i + 1] = bf16_hi(bb[i]);
+                    }
+                }
+                char *dst = (char *)Cb + (m * ldc + n) * (f32o ? 4 : 2);
+                if (beta != 0.f) {
+                    if (f32o) {
+                        const f32x4 o0 = *(const f32x4 *)dst, o1 = *(const f32x4 *)(dst + 16);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            t[i] = __builtin_fmaf(beta, o0[i], t[i]);
+                            t[4 + i] = __builtin_fmaf(beta, o1[i], t[4 + i]);
+                        }
+                    } else {
+                        const u32x4 o = *(const u32x4 *)dst;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            t[2 * i] = __builtin_fmaf(beta, bf16_lo(o[i]), t[2 * i]);
+                            t[2 * i + 1] = __builtin_fmaf(beta, bf16_hi(o[i]), t[2 * i + 1]);
+                        }
+                    }
+                }
+                f32x4 v0, v1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v0[i] = __builtin_fmaf(alpha, s0[i], t[i]);
+                    v1[i] = __builtin_fmaf(alpha, s1[i], t[4 + i]);
+                }
+                if (f32o) {
+                    __builtin_nontemporal_store(v0, (f32x4 *)dst);
+                    __builtin_nontemporal_store(v1, (f32x4 *)(dst + 16));
+                } else {
+                    const u32x4 w = {pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
+                                     pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
+                    __builtin_nontemporal_store(w, (u32x4 *)dst);
+                }
             }
         } else {
             for (int q = tid; q < RP * CPR; q += NT) {
@@ -370,6 +426,8 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
 //    from the same columns of W_u, and the epilogue combines the two halves
 //    into BN/2 columns of Z = bf16(bf16(SiLU(g)) * u).  Both need the
 //    LDS-staged epilogue (16-byte aligned output rows, N % 8 == 0).
+//  * EPI_AFFINE: C := alpha * sum + bias[n] + beta * C, from the FP32 sums
+//    staged in LDS, rounded once to C's type (bf16 or float).
 //  * SK: K is split over p.ksplit workgroups per tile (see GemmArgs); each
 //    publishes its FP32 accumulators and the last to arrive adds the
 //    partial tiles in slice order, so the result does not depend on which
@@ -727,7 +785,9 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         // number of chunks.
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if constexpr (EPI != EPI_NONE) {
+        if constexpr (EPI == EPI_AFFINE) {
+            store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, float, MASKED, EPI>(acc, smem, Cb, p.ldc, m0, n0, M, N, &p);
+        } else if constexpr (EPI != EPI_NONE) {
             store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, uint16_t, MASKED, EPI>(acc, smem, Cb, p.ldc, m0, n0, M, N);
         } else {
             if (p.out_f32) store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, float, MASKED>(acc, smem, Cb, p.ldc, m0, n0, M, N);

@@ -30,11 +30,15 @@ hipError_t launch_ring_fp8(int config_id, const GemmArgs &a, int variant, int64_
 hipError_t launch_quant_rows_e4m3(const uint16_t *X, int64_t ldx, int64_t rows, int64_t cols, int align_x,
                                   uint8_t *Q, int64_t ldq, int align_q, float *scale, hipStream_t s);
 
-// The same for a bf16 product with a fused epilogue (EPI_SILU or
-// EPI_SWIGLU; ring kernel variants 1-3 of the configs 256x192, 256x256 and
-// 128x128, with a.tiles_n counting output tiles of tile_n / 2 columns for
-// EPI_SWIGLU).
+// The same for a bf16 product with a fused epilogue (EPI_SILU, EPI_SWIGLU
+// or EPI_AFFINE; ring kernel variants 1-3 of the configs 256x192, 256x256
+// and 128x128, the last also with K split for EPI_AFFINE, with a.tiles_n
+// counting output tiles of tile_n / 2 columns for EPI_SWIGLU).
 hipError_t launch_fused(int config_id, int epi, const GemmArgs &a, int variant, int64_t grid, hipStream_t s);
+
+// The affine epilogue alone (K == 0 or alpha == 0): C := bias[n] + beta * C
+// over a.batch x a.M x a.N, reading C only when a.beta != 0.
+hipError_t launch_affine_no_product(const GemmArgs &a, int64_t grid, hipStream_t s);
 
 // Small-M path with K split over `ks` workgroups per 128-column strip
 // (a.tiles_n strips): `ws` holds batch x strips x ks x 16 x 128 floats of

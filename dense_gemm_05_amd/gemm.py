@@ -13,7 +13,8 @@ from . import _lib
 from ._lib import GemmError, GemmPlan, lib
 
 __all__ = ["gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm_bf16_nt_batched",
-           "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_fp8_quantize_rows", "gemm_fp8_nt", "plan_query", "GemmError"]
+           "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_fp8_quantize_rows", "gemm_fp8_nt", "gemm_bf16_affine",
+           "plan_query", "GemmError"]
 
 
 def _ld(t, inner):
@@ -275,6 +276,33 @@ def gemm_bf16_swiglu(X, Wgu, Z=None):
     if st != 0:
         raise GemmError(st, "gemm_bf16_swiglu")
     return Z
+
+
+def gemm_bf16_affine(A, B, C, alpha=1.0, bias=None, beta=0.0):
+    """C := alpha * (A . B) + bias + beta * C in place (gemm_bf16_affine):
+    bfloat16 A [M,K] / B [K,N] or stacks [batch, M, K] / [batch, K, N], C of
+    the matching shape in bfloat16 or float32 (read when beta != 0), bias a
+    bfloat16 vector of N elements or None.  Returns C."""
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("gemm_bf16_affine takes bfloat16 operands")
+    if A.dim() != B.dim() or A.dim() not in (2, 3):
+        raise ValueError("A and B must both be 2-D or both be 3-D")
+    A3, B3, C3 = (A, B, C) if A.dim() == 3 else (A.unsqueeze(0), B.unsqueeze(0), C.unsqueeze(0))
+    batch, M, K = A3.shape
+    b2, K2, N = B3.shape
+    if batch != b2 or K != K2 or tuple(C3.shape) != (batch, M, N):
+        raise ValueError("shape mismatch")
+    dev = _check_dev(A, B, C) if bias is None else _check_dev(A, B, C, bias)
+    if bias is not None and (bias.dtype != torch.bfloat16 or tuple(bias.shape) != (N,) or
+                             (N > 1 and bias.stride(0) != 1)):
+        raise ValueError("bias must be a contiguous bfloat16 vector of N elements")
+    code = _out_code(C.dtype)
+    st = _launch(lib().gemm_bf16_affine, dev, batch, M, N, K, A3.data_ptr(), _ld(A3, K), _bstride(A3),
+                 B3.data_ptr(), _ld(B3, N), _bstride(B3), float(alpha), None if bias is None else bias.data_ptr(),
+                 float(beta), C3.data_ptr(), _ld(C3, N), _bstride(C3), code)
+    if st != 0:
+        raise GemmError(st, "gemm_bf16_affine")
+    return C
 
 
 def plan_query(op, M, N, K, batch=1, lda=None, ldb=None, ldc=None, a_addr=0x10000, b_addr=0x20000000,

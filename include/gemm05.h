@@ -16,7 +16,8 @@
  *
  * Layout.  Every matrix is row-major.  lda, ldb, ldc are row strides counted
  * in ELEMENTS: A[i][k] is at A + i*lda + k, B[k][j] at B + k*ldb + j, C[i][j]
- * at C + i*ldc + j.  C is overwritten (there is no alpha/beta).
+ * at C + i*ldc + j.  C is overwritten (alpha, beta and a bias are the
+ * affine epilogue's, gemm_bf16_affine).
  *
  * Ownership.  The caller owns A, B and C: device pointers on the current
  * HIP device.  Each call validates its arguments on the host, enqueues its
@@ -208,6 +209,38 @@ int gemm_bf16_swiglu(int64_t M, int64_t N, int64_t K,
                      uint16_t *Z, int64_t ldz,
                      void *stream);
 
+/* ---- affine epilogue -------------------------------------------------------
+ *
+ * C := alpha * (A.B) + bias + beta * C, the scaling and accumulation of the
+ * BLAS GEMM and the bias of a linear layer, applied to the finished output
+ * tile like the activations above.  The pages fix no formula for it; the
+ * reading here keeps the rounding rule of "Operator & Runtime" §5.4.3: the
+ * product is accumulated in FP32 and
+ *
+ *     C[i][j] := round(fma(alpha, S[i][j], fma(beta, C_old[i][j], bias[j])))
+ *
+ * is evaluated in FP32 and rounded once to C's type (bf16 RNE, or float).
+ * bias is a bf16 vector of N elements (bit patterns, any 2-byte alignment)
+ * shared by every row and batch entry, or NULL for none.  C is read only
+ * when beta != 0 (so with beta == 0 its old contents, NaN included, do not
+ * matter), and A and B only when alpha != 0 and K > 0; otherwise the call
+ * computes bias[j] + beta * C_old[i][j] element by element.
+ *
+ * Arguments follow gemm_bf16_batched (batch 1 for a single product), plus:
+ * GEMM_ERR_INVALID_ARG when alpha or beta is not finite, bias is not 2-byte
+ * aligned, or bias overlaps C; GEMM_ERR_UNSUPPORTED as for the fused
+ * epilogues above (16-byte aligned rows of C, N % 8 == 0, B rows 16-byte
+ * aligned) when a product is formed.  Small outputs split K over
+ * workgroups as gemm_bf16 does (the workgroup that completes a tile applies
+ * the epilogue).
+ */
+int gemm_bf16_affine(int64_t batch, int64_t M, int64_t N, int64_t K,
+                     const uint16_t *A, int64_t lda, int64_t strideA,
+                     const uint16_t *B, int64_t ldb, int64_t strideB,
+                     float alpha, const uint16_t *bias, float beta,
+                     void *C, int64_t ldc, int64_t strideC, int c_type,
+                     void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *gemm_status_string(int status);
 
@@ -257,7 +290,9 @@ typedef enum {
     GEMM_OP_BF16_SILU = 2,   /* gemm_bf16_silu (batch 1, c_type ignored) */
     GEMM_OP_BF16_SWIGLU = 3, /* gemm_bf16_swiglu (batch 1, b = Wgu, c_type ignored) */
     GEMM_OP_BF16_NT = 4,     /* gemm_bf16_nt, gemm_bf16_nt_batched (b = Bt, ldb = ldbt) */
-    GEMM_OP_FP8_NT = 5       /* gemm_fp8_nt (batch 1, b = Bt; scales do not change the plan) */
+    GEMM_OP_FP8_NT = 5,      /* gemm_fp8_nt (batch 1, b = Bt; scales do not change the plan) */
+    GEMM_OP_BF16_AFFINE = 6  /* gemm_bf16_affine with alpha = 1 (alpha, beta and bias do not change the
+                                plan; alpha == 0 plans the element-wise pass of K == 0) */
 } gemm_op;
 
 /* Validate the arguments of a call and report the plan it would launch,

@@ -98,3 +98,22 @@ def _check(C, ref, bound, what):
         raise AssertionError(f"{what}: {int(bad.sum())} elements out of bound, first at {idx}: "
                              f"got {C[idx]!r} want {ref[idx]!r} (bound {bound[idx]!r})")
     return float((err / bound).max()) if err.size else 0.0
+
+
+# Affine epilogue C = alpha * S + bias + beta * C_old, evaluated by the kernel
+# in FP32 from its FP32 sum S and rounded once.  S is within the accumulation
+# part of the bf16 bar of the exact product P (2^-9 |P| + 1e-3 sqrt(K); the
+# other 2^-9 |P| of that bar is the output rounding), scaled by |alpha|; the
+# two FP32 fused multiply-adds add at most 2^-23 of the magnitudes they
+# combine (2^-20 is used); the final rounding to bf16 at most 2^-9 |C_ref|
+# (2^-8 is used), to float nothing beyond the FP32 bar.
+
+def check_affine(C, ref, P, K, alpha, bias_vals, beta, old_vals, out_f32, amax=0.0, bmax=0.0, what=""):
+    mags = np.abs(alpha * P) + np.abs(bias_vals)[None, :] + np.abs(beta * old_vals)
+    if out_f32:
+        acc = abs(alpha) * tol_f32(K, amax, bmax)
+        bound = acc + 2.0 ** -20 * mags
+    else:
+        acc = abs(alpha) * (2.0 ** -9 * np.abs(P) + 1e-3 * math.sqrt(max(K, 1)))
+        bound = 2.0 ** -8 * np.abs(ref) + acc + 2.0 ** -20 * mags
+    return _check(C, ref, np.broadcast_to(bound, ref.shape), what)

@@ -315,7 +315,7 @@ def test_ksplit_plans(L, monkeypatch):
         assert p.grid == tiles * ks
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 1024, 1024, 128, batch=32, c_type=1)
     assert st == 0 and p.ksplit == 1
-    # fused epilogues and FP32 never split
+    # SiLU, SwiGLU and FP32 never split
     st, p = g5.plan_query(g5.GEMM_OP_BF16_SILU, 512, 512, 4096)
     assert st == 0 and p.ksplit == 1
     st, p = g5.plan_query(g5.GEMM_OP_SGEMM, 512, 512, 4096)
@@ -409,3 +409,55 @@ def test_quant_traffic_model_reproduces_example_5_8(L):
     common = (-(-M // m)) * wb * K * N + ob * M * N
     assert common / MiB == rows["common"]
     assert (sep.value - common) / MiB == rows["input_separate"] and (fus.value - common) / MiB == rows["input_fused"]
+
+
+def call_affine(L, M, N, K, batch=1, a=A_ADDR, lda=None, b=B_ADDR, ldb=None, c=C_ADDR, ldc=None, alpha=1.0,
+                bias=0, beta=0.0, c_type=0, sA=None, sB=None, sC=None):
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    sA = M * lda if sA is None else sA
+    sB = K * ldb if sB is None else sB
+    sC = M * ldc if sC is None else sC
+    return L.gemm_bf16_affine(batch, M, N, K, a, lda, sA, b, ldb, sB, alpha, bias or None, beta, c, ldc, sC,
+                              c_type, None)
+
+
+def test_affine_arguments(L):
+    """Affine epilogue: gemm_bf16_batched's validation plus finite alpha and
+    beta and a 2-byte aligned bias outside C; the fused-epilogue store's
+    preconditions when a product is formed (not for alpha == 0 or K == 0,
+    which read neither A nor B)."""
+    assert call_affine(L, -1, 8, 4) == g5.GEMM_ERR_INVALID_ARG
+    assert call_affine(L, 4, 8, 4, alpha=float("nan")) == g5.GEMM_ERR_INVALID_ARG
+    assert call_affine(L, 4, 8, 4, beta=float("inf")) == g5.GEMM_ERR_INVALID_ARG
+    assert call_affine(L, 4, 8, 4, bias=0x7000001) == g5.GEMM_ERR_INVALID_ARG      # odd address
+    assert call_affine(L, 4, 8, 4, bias=C_ADDR + 6) == g5.GEMM_ERR_INVALID_ARG     # inside C
+    assert call_affine(L, 4, 8, 4, c_type=2) == g5.GEMM_ERR_INVALID_ARG
+    assert call_affine(L, 4, 8, 4, b=0) == g5.GEMM_ERR_INVALID_ARG
+    assert call_affine(L, 2, 8, 4, batch=2, sC=8) == g5.GEMM_ERR_INVALID_ARG       # C entries overlap
+    assert call_affine(L, 4, 12, 4) == g5.GEMM_ERR_UNSUPPORTED                     # N % 8
+    assert call_affine(L, 4, 8, 4, c=C_ADDR + 2) == g5.GEMM_ERR_UNSUPPORTED        # C rows 2-byte aligned
+    assert call_affine(L, 0, 8, 4) == g5.GEMM_OK                                    # empty: nothing to do
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_AFFINE, 4, 8, 0)
+    assert st == 0 and p.family == 1                                                # K = 0: element-wise pass
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_AFFINE, 4, 12, 0, c_addr=C_ADDR + 2)
+    assert st == 0 and p.family == 1                                                # ... at any alignment
+
+
+def test_affine_plans(L):
+    """The affine epilogue runs on the fused-epilogue ring kernels, batched,
+    with either output type, and splits K for small outputs like gemm_bf16."""
+    op = g5.GEMM_OP_BF16_AFFINE
+    for ct in (0, 1):
+        st, p = g5.plan_query(op, 1024, 12288, 4096, c_type=ct)
+        assert st == 0 and p.family == 2 and p.variant == 1 and p.ksplit == 1
+        assert p.name in (b"bf16_256x192", b"bf16_256x256", b"bf16_128x128")
+    st, p = g5.plan_query(op, 512, 512, 4096)
+    assert st == 0 and p.name == b"bf16_128x128" and p.ksplit == 5
+    st, p = g5.plan_query(op, 1, 4096, 4096)
+    assert st == 0 and p.name == b"bf16_128x128" and p.ksplit > 1                 # small M: a ring kernel
+    st, p = g5.plan_query(op, 300, 392, 261, lda=266, ldb=400, ldc=400, batch=3)
+    assert st == 0 and p.variant == 3
+    st, p = g5.plan_query(op, 257, 96, 33)
+    assert st == 0 and p.variant == 2 and p.workspace_bytes == 257 * 40 * 2        # A realigned
