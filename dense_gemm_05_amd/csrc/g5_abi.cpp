@@ -104,8 +104,10 @@ bool b_trans(const Problem &p) { return p.op == GEMM_OP_BF16_NT || p.op == GEMM_
 // merged gate|up weight [K, 2N] of SwiGLU.
 int64_t b_rows(const Problem &p) { return b_trans(p) ? p.N : p.K; }
 int64_t b_cols(const Problem &p) { return b_trans(p) ? p.K : p.op == GEMM_OP_BF16_SWIGLU ? 2 * p.N : p.N; }
-// Calls only the LDS-ring kernels can run (variants 1-3).
+// Calls only the LDS-ring kernels can run (variants 1-3) when they take a
+// tiled config (the affine epilogue also runs in the small-M kernels).
 bool ring_only(const Problem &p) { return epi_of(p) != EPI_NONE || b_trans(p); }
+bool tiled(int config) { return kConfigs[config].family == GEMM_FAMILY_BF16_MFMA; }
 // Output columns per tile of a tiled config (SwiGLU: half the B columns).
 int64_t out_tile_n(const Problem &p, const ConfigInfo &c)
 {
@@ -225,6 +227,8 @@ bool has_epilogues(int id) { return id == CFG_BF16_256x192 || id == CFG_BF16_256
 bool config_fits(const Problem &p, int id)
 {
     const ConfigInfo &c = kConfigs[id];
+    if (epi_of(p) == EPI_AFFINE && (id == CFG_DECODE_64 || id == CFG_DECODE_SPLIT))
+        return p.M <= 16 && p.batch <= 65535;                     // the small-M kernels apply it too
     if (epi_of(p) != EPI_NONE) return has_epilogues(id);
     if (p.op == GEMM_OP_FP8_NT) return has_epilogues(id);         // fp8 ring kernels: 256x192, 256x256, 128x128
     if (b_trans(p)) return c.family == GEMM_FAMILY_BF16_MFMA;   // the ring kernels of every bf16 tile config
@@ -366,7 +370,7 @@ int select_plan(const Problem &p, Plan &pl)
     } else if (p.op == GEMM_OP_BF16_NT && p.M <= 16 && p.batch <= 65535 && pl.align_b >= 16) {
         // Small M with B transposed: a GEMV over the contiguous rows of Bt.
         pl.config = CFG_DECODE_NT;
-    } else if (p.op == GEMM_OP_BF16 && p.M <= 16 && p.batch <= 65535) {
+    } else if ((p.op == GEMM_OP_BF16 || p.op == GEMM_OP_BF16_AFFINE) && p.M <= 16 && p.batch <= 65535) {
         // The split path when its preconditions hold and it would use more
         // than one slice; else whole-K strips of 64 columns.
         pl.config = CFG_DECODE_SPLIT;
@@ -486,7 +490,7 @@ int select_plan(const Problem &p, Plan &pl)
         }
     }
     // fused epilogues and a transposed B exist in the ring kernels only (variants 1-3)
-    if (ring_only(p) && pl.config != CFG_ZERO && pl.variant == 0) return GEMM_ERR_UNSUPPORTED;
+    if (ring_only(p) && tiled(pl.config) && pl.variant == 0) return GEMM_ERR_UNSUPPORTED;
     return GEMM_OK;
 }
 
@@ -686,6 +690,7 @@ int run(const Problem &p, void *stream)
     a.beta = p.beta;
     a.bias = (const uint16_t *)p.bias;
     a.align_bias = row_alignment(p.bias, 0, 0, 1, 2);
+    a.affine = p.op == GEMM_OP_BF16_AFFINE ? 1 : 0;
     if (pl.realign_b) {
         int dev = 0;
         (void)hipGetDevice(&dev);
@@ -743,7 +748,7 @@ int run(const Problem &p, void *stream)
                 q.sB = p.N * pl.ldb2;
                 pl.variant = pick_variant(q, pl, &pl.even);
             }
-            if (ring_only(p) && pl.variant == 0) return GEMM_ERR_UNSUPPORTED;
+            if (ring_only(p) && tiled(pl.config) && pl.variant == 0) return GEMM_ERR_UNSUPPORTED;
         }
     }
     if (pl.config == CFG_DECODE_SPLIT) {
@@ -766,7 +771,8 @@ int run(const Problem &p, void *stream)
     const hipError_t e =
         pl.config == CFG_ZERO ? (p.op == GEMM_OP_BF16_AFFINE ? launch_affine_no_product(a, pl.grid, (hipStream_t)stream)
                                                              : launch_config(pl.config, false, a, 0, pl.grid, (hipStream_t)stream))
-        : epi_of(p) == EPI_NONE ? launch_config(pl.config, p.op == GEMM_OP_SGEMM, a, pl.variant, pl.grid, (hipStream_t)stream)
+        : epi_of(p) == EPI_NONE || !tiled(pl.config)
+            ? launch_config(pl.config, p.op == GEMM_OP_SGEMM, a, pl.variant, pl.grid, (hipStream_t)stream)
                                 : launch_fused(pl.config, epi_of(p), a, pl.variant, pl.grid, (hipStream_t)stream);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }

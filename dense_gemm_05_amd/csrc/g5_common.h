@@ -84,6 +84,7 @@ struct GemmArgs {
     float alpha, beta;
     const uint16_t *bias;
     int32_t align_bias;
+    int32_t affine;          // 1: the small-M kernels apply the affine epilogue
 };
 
 // Fused epilogues of the bf16 ring kernels.

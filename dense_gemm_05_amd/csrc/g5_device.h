@@ -284,8 +284,30 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
     const int wm = wave / WGN, wn = wave % WGN;
     const int g = lane >> 4, li = lane & 15;
     char *L = (char *)lds;
+    // Affine epilogue: 8-column steps, APER per thread and pass.
+    constexpr int AOPR = BN / 8;
+    constexpr int APER = EPI == EPI_AFFINE ? (RP * AOPR + NT - 1) / NT : 1;
+    u32x4 old0[APER], old1[APER];
 #pragma unroll
     for (int pass = 0; pass < BM / RP; ++pass) {
+        if constexpr (EPI == EPI_AFFINE) {
+            // Load this pass's old C chunks first (beta != 0), so that their
+            // latency overlaps the staging below.
+            if (pa->beta != 0.f) {
+                const bool f32o = pa->out_f32 != 0;
+#pragma unroll
+                for (int i = 0; i < APER; ++i) {
+                    const int q = tid + i * NT;
+                    if (APER * NT != RP * AOPR && q >= RP * AOPR) break;
+                    const int r = q / AOPR, c = q % AOPR;
+                    const int64_t m = m0 + pass * RP + r, n = n0 + (int64_t)c * 8;
+                    if (MASKED && (m >= M || n + 8 > N)) continue;
+                    const char *src = (const char *)Cb + (m * ldc + n) * (f32o ? 4 : 2);
+                    old0[i] = *(const u32x4 *)src;
+                    if (f32o) old1[i] = *(const u32x4 *)(src + 16);
+                }
+            }
+        }
         // Each pass stages the 16-row accumulator blocks whose rows fall in
         // it (a wave's rows span several passes when a pass is shorter than
         // the wave tile).
@@ -321,12 +343,15 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
             }
         } else if constexpr (EPI == EPI_AFFINE) {
             // 8 columns per step: v = alpha * sum + (bias[n] + beta * C[m][n])
-            // in FP32, rounded once to C's type (bf16 or float).
-            constexpr int OPR = BN / 8;
+            // in FP32, rounded once to C's type (bf16 or float); the old C
+            // chunks of this pass were loaded before the staging.
             const float alpha = pa->alpha, beta = pa->beta;
             const bool f32o = pa->out_f32 != 0;
-            for (int q = tid; q < RP * OPR; q += NT) {
-                const int r = q / OPR, c = q % OPR;
+#pragma unroll
+            for (int i = 0; i < APER; ++i) {
+                const int q = tid + i * NT;
+                if (APER * NT != RP * AOPR && q >= RP * AOPR) break;
+                const int r = q / AOPR, c = q % AOPR;
                 const int64_t m = m0 + pass * RP + r, n = n0 + (int64_t)c * 8;
                 if (MASKED && (m >= M || n + 8 > N)) continue;
                 const f32x4 s0 = *(const f32x4 *)(L + r * PITCH + c * 32);
@@ -335,35 +360,34 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
                 if (pa->bias) {
                     const u32x4 bb = load_chunk8_bf16(pa->bias, n, N, true, pa->align_bias);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        t[2 * i] = bf16_lo(bb[i]);
-                        t[2 * i + 1] = bf16_hi(bb[i]);
+                    for (int j = 0; j < 4; ++j) {
+                        t[2 * j] = bf16_lo(bb[j]);
+                        t[2 * j + 1] = bf16_hi(bb[j]);
                     }
                 }
-                char *dst = (char *)Cb + (m * ldc + n) * (f32o ? 4 : 2);
                 if (beta != 0.f) {
                     if (f32o) {
-                        const f32x4 o0 = *(const f32x4 *)dst, o1 = *(const f32x4 *)(dst + 16);
+                        const f32x4 o0 = __builtin_bit_cast(f32x4, old0[i]), o1 = __builtin_bit_cast(f32x4, old1[i]);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            t[i] = __builtin_fmaf(beta, o0[i], t[i]);
-                            t[4 + i] = __builtin_fmaf(beta, o1[i], t[4 + i]);
+                        for (int j = 0; j < 4; ++j) {
+                            t[j] = __builtin_fmaf(beta, o0[j], t[j]);
+                            t[4 + j] = __builtin_fmaf(beta, o1[j], t[4 + j]);
                         }
                     } else {
-                        const u32x4 o = *(const u32x4 *)dst;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            t[2 * i] = __builtin_fmaf(beta, bf16_lo(o[i]), t[2 * i]);
-                            t[2 * i + 1] = __builtin_fmaf(beta, bf16_hi(o[i]), t[2 * i + 1]);
+                        for (int j = 0; j < 4; ++j) {
+                            t[2 * j] = __builtin_fmaf(beta, bf16_lo(old0[i][j]), t[2 * j]);
+                            t[2 * j + 1] = __builtin_fmaf(beta, bf16_hi(old0[i][j]), t[2 * j + 1]);
                         }
                     }
                 }
                 f32x4 v0, v1;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v0[i] = __builtin_fmaf(alpha, s0[i], t[i]);
-                    v1[i] = __builtin_fmaf(alpha, s1[i], t[4 + i]);
+                for (int j = 0; j < 4; ++j) {
+                    v0[j] = __builtin_fmaf(alpha, s0[j], t[j]);
+                    v1[j] = __builtin_fmaf(alpha, s1[j], t[4 + j]);
                 }
+                char *dst = (char *)Cb + (m * ldc + n) * (f32o ? 4 : 2);
                 if (f32o) {
                     __builtin_nontemporal_store(v0, (f32x4 *)dst);
                     __builtin_nontemporal_store(v1, (f32x4 *)(dst + 16));

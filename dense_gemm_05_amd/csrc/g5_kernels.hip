@@ -435,6 +435,25 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_f32_wholek(GemmArgs p)
 //    maps to physical column 4r + b;
 //  * X rows (zero beyond M) are the other MFMA operand; the 16-row MFMA
 //    covers any M <= 16 at no extra memory traffic.
+// One output element of the small-M kernels: the FP32 sum of batch entry
+// b, or with the affine epilogue alpha * sum + bias[n] + beta * C[m][n]
+// (C read only when beta != 0), rounded once to C's type.
+__device__ __forceinline__ void store_out(const GemmArgs &p, int64_t b, int64_t m, int64_t n, float sum)
+{
+    const int64_t off = b * p.sC + m * p.ldc + n;
+    if (p.affine) {
+        float t = p.bias ? __uint_as_float((uint32_t)p.bias[n] << 16) : 0.f;
+        if (p.beta != 0.f) {
+            const float old = p.out_f32 ? ((const float *)p.C)[off]
+                                        : __uint_as_float((uint32_t)((const uint16_t *)p.C)[off] << 16);
+            t = __builtin_fmaf(p.beta, old, t);
+        }
+        sum = __builtin_fmaf(p.alpha, sum, t);
+    }
+    if (p.out_f32) ((float *)p.C)[off] = sum;
+    else ((uint16_t *)p.C)[off] = (uint16_t)bf16_rne(sum);
+}
+
 template <int NW, bool FAST>
 __global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
 {
@@ -556,10 +575,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
         for (int w2 = 0; w2 < NW; ++w2) sum += red[(w2 * 64 + L) * RS + v];
         const int64_t m = L & 15;
         const int64_t n = n0 + 16 * (L >> 4) + v;
-        if (m < M && n < N) {
-            if (p.out_f32) ((float *)p.C + bidx * p.sC)[m * p.ldc + n] = sum;
-            else ((uint16_t *)p.C + bidx * p.sC)[m * p.ldc + n] = (uint16_t)bf16_rne(sum);
-        }
+        if (m < M && n < N) store_out(p, bidx, m, n, sum);
     }
 }
 
@@ -687,10 +703,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode_sk(GemmArgs p, float *ws,
         for (int w2 = 0; w2 < NW; ++w2) sum += red[(w2 * 64 + L) * RS + (t & 31)];
         const int m = L & 15, n = 32 * (L >> 4) + 8 * q + c;
         if (KS == 1) {
-            if (m < M) {
-                if (p.out_f32) ((float *)p.C + bidx * p.sC)[m * p.ldc + n0 + n] = sum;
-                else ((uint16_t *)p.C + bidx * p.sC)[m * p.ldc + n0 + n] = (uint16_t)bf16_rne(sum);
-            }
+            if (m < M) store_out(p, bidx, m, n0 + n, sum);
         } else if (m < M) {                  // rows past M are never read back
             __hip_atomic_store(part + m * NC + n, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -710,8 +723,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode_sk(GemmArgs p, float *ws,
         float sum = 0.f;
         for (int k2 = 0; k2 < KS; ++k2)
             sum += __hip_atomic_load(parts + k2 * (16 * NC) + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (p.out_f32) ((float *)p.C + bidx * p.sC)[m * p.ldc + n0 + n] = sum;
-        else ((uint16_t *)p.C + bidx * p.sC)[m * p.ldc + n0 + n] = (uint16_t)bf16_rne(sum);
+        store_out(p, bidx, m, n0 + n, sum);
     }
     if (tid == 0) __hip_atomic_store(c_strip, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

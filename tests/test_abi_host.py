@@ -447,7 +447,8 @@ def test_affine_arguments(L):
 
 def test_affine_plans(L):
     """The affine epilogue runs on the fused-epilogue ring kernels, batched,
-    with either output type, and splits K for small outputs like gemm_bf16."""
+    with either output type, and splits K for small outputs like gemm_bf16;
+    M <= 16 takes the small-M kernels."""
     op = g5.GEMM_OP_BF16_AFFINE
     for ct in (0, 1):
         st, p = g5.plan_query(op, 1024, 12288, 4096, c_type=ct)
@@ -456,7 +457,11 @@ def test_affine_plans(L):
     st, p = g5.plan_query(op, 512, 512, 4096)
     assert st == 0 and p.name == b"bf16_128x128" and p.ksplit == 5
     st, p = g5.plan_query(op, 1, 4096, 4096)
-    assert st == 0 and p.name == b"bf16_128x128" and p.ksplit > 1                 # small M: a ring kernel
+    assert st == 0 and p.name == b"decode_splitk"                                  # small M: the small-M kernels
+    st, p = g5.plan_query(op, 5, 200, 64, batch=2)
+    assert st == 0 and p.name == b"decode_64" and p.variant == 0
+    st, p = g5.plan_query(op, 17, 4096, 4096)
+    assert st == 0 and p.family == 2
     st, p = g5.plan_query(op, 300, 392, 261, lda=266, ldb=400, ldc=400, batch=3)
     assert st == 0 and p.variant == 3
     st, p = g5.plan_query(op, 257, 96, 33)

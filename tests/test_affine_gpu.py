@@ -186,6 +186,30 @@ def test_affine_identity_matches_plain_product(monkeypatch, S):
         assert torch.equal(C.float(), plain.float()), out
 
 
+@pytest.mark.parametrize("M,N,K,batch", [(1, 12288, 4096, 1), (4, 12288, 4096, 1), (16, 12288, 4096, 1),
+                                         (5, 200, 64, 2), (3, 1024, 1000, 1), (16, 384, 1024, 3)])
+def test_affine_small_m(oracle_mod, M, N, K, batch):
+    """M <= 16 on the small-M kernels (the K-split one for N % 128 == 0 and
+    K % 32 == 0, else the whole-K one), bias and beta * C in both output
+    types; the decode shape of the FFN at full size."""
+    for out_f32 in (False, True):
+        _say(f"small M {batch}x{M}x{N}x{K} out_f32={out_f32}")
+        A, B, bias, old32, old16 = _case(M, N, K, 7, batch=batch)
+        _run_and_check(oracle_mod, A, B, bias, old32, old16, 1.25, -1.0, out_f32, f"small M {M}x{N}x{K}")
+
+
+def test_affine_small_m_rows_do_not_depend_on_m():
+    """The small-M K partition does not depend on M: row 0 of an M = 1 call
+    equals row 0 of an M = 16 call bit for bit, epilogue included."""
+    A, B, bias, _, old16 = _case(16, 12288, 4096, 8)
+    dA, dB, db = dev_bf16(A[0]), dev_bf16(B[0]), dev_bf16(bias)
+    C16 = dev_bf16(old16[0])
+    C1 = dev_bf16(old16[0][:1])
+    g5.gemm_bf16_affine(dA, dB, C16, alpha=0.5, bias=db, beta=1.0)
+    g5.gemm_bf16_affine(dA[:1], dB, C1, alpha=0.5, bias=db, beta=1.0)
+    assert torch.equal(C1.view(torch.int16), C16[:1].view(torch.int16))
+
+
 def test_affine_ffn_full_size(oracle_mod):
     """The FFN projection X[1024,4096] . W[4096,12288] with a bias and a
     residual add (beta = 1) into a bf16 C: rows from every row tile, all
