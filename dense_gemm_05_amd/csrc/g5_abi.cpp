@@ -100,13 +100,18 @@ int epi_of(const Problem &p)
 bool no_product(const Problem &p) { return p.op == GEMM_OP_BF16_AFFINE && p.alpha == 0.0f; }
 // B is given transposed, Bt [N, K].
 bool b_trans(const Problem &p) { return p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_FP8_NT; }
+// A is given transposed, At [K, M].
+bool a_trans(const Problem &p) { return p.op == GEMM_OP_BF16_TN; }
+// Rows and columns of the A operand as stored: [M, K] or At [K, M].
+int64_t a_rows(const Problem &p) { return a_trans(p) ? p.K : p.M; }
+int64_t a_cols(const Problem &p) { return a_trans(p) ? p.M : p.K; }
 // Rows and columns of the B operand as stored: [K, N], Bt [N, K], or the
 // merged gate|up weight [K, 2N] of SwiGLU.
 int64_t b_rows(const Problem &p) { return b_trans(p) ? p.N : p.K; }
 int64_t b_cols(const Problem &p) { return b_trans(p) ? p.K : p.op == GEMM_OP_BF16_SWIGLU ? 2 * p.N : p.N; }
 // Calls only the LDS-ring kernels can run (variants 1-3) when they take a
 // tiled config (the affine epilogue also runs in the small-M kernels).
-bool ring_only(const Problem &p) { return epi_of(p) != EPI_NONE || b_trans(p); }
+bool ring_only(const Problem &p) { return epi_of(p) != EPI_NONE || b_trans(p) || a_trans(p); }
 bool tiled(int config) { return kConfigs[config].family == GEMM_FAMILY_BF16_MFMA; }
 // Output columns per tile of a tiled config (SwiGLU: half the B columns).
 int64_t out_tile_n(const Problem &p, const ConfigInfo &c)
@@ -140,10 +145,11 @@ bool overlap(const Range &x, const Range &y) { return x.lo < y.hi && y.lo < x.hi
 int validate(const Problem &p)
 {
     if (p.op != GEMM_OP_SGEMM && p.op != GEMM_OP_BF16 && p.op != GEMM_OP_BF16_SILU && p.op != GEMM_OP_BF16_SWIGLU &&
-        p.op != GEMM_OP_BF16_NT && p.op != GEMM_OP_FP8_NT && p.op != GEMM_OP_BF16_AFFINE)
+        p.op != GEMM_OP_BF16_NT && p.op != GEMM_OP_FP8_NT && p.op != GEMM_OP_BF16_AFFINE && p.op != GEMM_OP_BF16_TN)
         return GEMM_ERR_INVALID_ARG;
     if (p.batch < 0 || p.M < 0 || p.N < 0 || p.K < 0) return GEMM_ERR_INVALID_ARG;
-    if ((p.op == GEMM_OP_BF16 || p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_FP8_NT || p.op == GEMM_OP_BF16_AFFINE) &&
+    if ((p.op == GEMM_OP_BF16 || p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_FP8_NT || p.op == GEMM_OP_BF16_AFFINE ||
+         p.op == GEMM_OP_BF16_TN) &&
         p.c_type != GEMM_OUT_BF16 && p.c_type != GEMM_OUT_F32)
         return GEMM_ERR_INVALID_ARG;
     if (p.op == GEMM_OP_FP8_NT && (p.batch > 1 || (p.scale_a % 4) || (p.scale_b % 4))) return GEMM_ERR_INVALID_ARG;
@@ -159,8 +165,8 @@ int validate(const Problem &p)
     if (rc.hi > ((__int128)1 << 63)) return GEMM_ERR_INVALID_ARG;
     if (p.bias && overlap(rc, Range{(__int128)p.bias, (__int128)p.bias + 2 * (__int128)p.N})) return GEMM_ERR_INVALID_ARG;
     if (p.K == 0 || no_product(p)) return GEMM_OK;
-    if (p.lda < p.K || p.ldb < b_cols(p) || p.a == 0 || p.b == 0) return GEMM_ERR_INVALID_ARG;
-    const Range ra = extent(p.a, p.batch, p.M, p.K, p.lda, p.sA, elem_a(p));
+    if (p.lda < a_cols(p) || p.ldb < b_cols(p) || p.a == 0 || p.b == 0) return GEMM_ERR_INVALID_ARG;
+    const Range ra = extent(p.a, p.batch, a_rows(p), a_cols(p), p.lda, p.sA, elem_a(p));
     const Range rb = extent(p.b, p.batch, b_rows(p), b_cols(p), p.ldb, p.sB, elem_a(p));
     if (ra.hi > ((__int128)1 << 63) || rb.hi > ((__int128)1 << 63)) return GEMM_ERR_INVALID_ARG;
     if (overlap(rc, ra) || overlap(rc, rb)) return GEMM_ERR_INVALID_ARG;
@@ -231,6 +237,7 @@ bool config_fits(const Problem &p, int id)
         return p.M <= 16 && p.batch <= 65535;                     // the small-M kernels apply it too
     if (epi_of(p) != EPI_NONE) return has_epilogues(id);
     if (p.op == GEMM_OP_FP8_NT) return has_epilogues(id);         // fp8 ring kernels: 256x192, 256x256, 128x128
+    if (a_trans(p)) return has_epilogues(id);                       // transposed-A ring kernels: the same three
     if (b_trans(p)) return c.family == GEMM_FAMILY_BF16_MFMA;   // the ring kernels of every bf16 tile config
     switch (c.family) {
     case GEMM_FAMILY_BF16_MFMA: return p.op == GEMM_OP_BF16;
@@ -308,13 +315,17 @@ int pick_variant(const Problem &p, const Plan &pl, bool *even)
         return *even ? 1 : 0;
     }
     if (c.family != GEMM_FAMILY_BF16_MFMA) return 0;
-    const __int128 a_bytes = ((__int128)(p.M - 1) * p.lda + p.K) * 2;
+    // (At: the masked copy reads the last row up to M rounded up to 8)
+    const __int128 a_bytes = ((__int128)(a_rows(p) - 1) * p.lda + (a_trans(p) ? (p.M + 7) / 8 * 8 : p.K)) * 2;
     const __int128 b_bytes = ((__int128)(b_rows(p) - 1) * p.ldb + b_cols(p)) * 2;
     const bool fits = a_bytes < ((__int128)1 << 31) && b_bytes < ((__int128)1 << 31);
     // N % 8: every 16-byte chunk of B lies wholly inside or wholly past the
     // descriptor extent (no partially out-of-range copies).
     // (Bt's chunks run along K like A's: no condition on N.)
     if (!fits || pl.align_b < 16 || pl.align_a < 4 || (!b_trans(p) && p.N % 8 != 0)) return 0;
+    // At is copied 16 bytes per lane in whole chunks: aligned rows, and M % 8
+    // == 0 unless the rows are the padded copy.
+    if (a_trans(p) && (pl.align_a < 16 || (p.M % 8 != 0 && !pl.realign_a))) return 0;
     const int ring_k = stage_k(p);
     const bool c_ok = pl.align_c >= (elem_c(p) == 4 ? 16 : 8);
     *even = !(p.M % c.tile_m || p.N % out_tile_n(p, c) || p.K % ring_k) && pl.align_a >= 16 && c_ok;
@@ -428,6 +439,7 @@ int select_plan(const Problem &p, Plan &pl)
             bool ev = false;
             int var = pick_variant(p, t, &ev);
             if (b_trans(p) && var == 0 && pl.align_b < 16) var = 2;   // Bt rows realigned below
+            if (a_trans(p) && var == 0) var = 2;                          // At rows realigned below
             for (int S = 2; S <= 8 && var >= 1; ++S) {
                 if (!split_ok(p, S)) continue;
                 const double eff = (p.K <= 8 * 32 ? 1.0 : 0.85) * (var == 1 ? 1.0 : 0.85);
@@ -468,17 +480,19 @@ int select_plan(const Problem &p, Plan &pl)
         q.sB = p.N * pl.ldb2;
         pl.variant = pick_variant(q, pl, &pl.even);
     }
-    if (kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && p.op != GEMM_OP_FP8_NT && pl.align_a < 16 &&
+    if (kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && p.op != GEMM_OP_FP8_NT &&
+        (pl.align_a < 16 || (a_trans(p) && p.M % 8 != 0)) &&
         ((double)p.batch * p.M * p.N * p.K >= (double)(1 << 30) || (ring_only(p) && pl.variant == 0))) {
         Problem q = p;
         if (pl.realign_b) {
             q.ldb = pl.ldb2;
             q.sB = p.N * pl.ldb2;
         }
-        q.lda = (p.K + 7) / 8 * 8;
-        q.sA = p.M * q.lda;
+        q.lda = (a_cols(p) + 7) / 8 * 8;
+        q.sA = a_rows(p) * q.lda;
         Plan t = pl;
         t.align_a = 16;
+        t.realign_a = true;
         bool ev = false;
         const int v = pick_variant(q, t, &ev);
         if (v == 1 || v == 2) {
@@ -496,7 +510,7 @@ int select_plan(const Problem &p, Plan &pl)
 
 size_t realign_bytes(const Problem &p, const Plan &pl)
 {
-    return pl.realign_a ? (size_t)p.batch * p.M * pl.lda2 * 2 : 0;
+    return pl.realign_a ? (size_t)p.batch * a_rows(p) * pl.lda2 * 2 : 0;
 }
 size_t realign_b_bytes(const Problem &p, const Plan &pl)
 {
@@ -691,6 +705,7 @@ int run(const Problem &p, void *stream)
     a.bias = (const uint16_t *)p.bias;
     a.align_bias = row_alignment(p.bias, 0, 0, 1, 2);
     a.affine = p.op == GEMM_OP_BF16_AFFINE ? 1 : 0;
+    a.a_trans = a_trans(p) ? 1 : 0;
     if (pl.realign_b) {
         int dev = 0;
         (void)hipGetDevice(&dev);
@@ -728,13 +743,13 @@ int run(const Problem &p, void *stream)
         (void)hipGetDevice(&dev);
         uint16_t *A2 = get_row_buffer(dev, stream, realign_bytes(p, pl));
         if (A2) {
-            const hipError_t e = launch_realign_rows((const uint16_t *)p.a, p.lda, p.sA, p.batch, p.M, p.K,
-                                                     row_alignment(p.a, p.lda, p.sA, p.batch, 2), A2, pl.lda2,
-                                                     (hipStream_t)stream);
+            const hipError_t e = launch_realign_rows((const uint16_t *)p.a, p.lda, p.sA, p.batch, a_rows(p),
+                                                     a_cols(p), row_alignment(p.a, p.lda, p.sA, p.batch, 2), A2,
+                                                     pl.lda2, (hipStream_t)stream);
             if (e != hipSuccess) return GEMM_ERR_LAUNCH;
             a.A = A2;
             a.lda = pl.lda2;
-            a.sA = p.M * pl.lda2;
+            a.sA = a_rows(p) * pl.lda2;
             a.align_a = 16;
         } else {
             // No buffer: multiply from A as it is.
@@ -869,6 +884,23 @@ int gemm_bf16_swiglu(int64_t M, int64_t N, int64_t K, const uint16_t *X, int64_t
 {
     const Problem p{GEMM_OP_BF16_SWIGLU, 1, M, N, K, (uint64_t)X, (uint64_t)Wgu, (uint64_t)Z, ldx, ldw, ldz, 0, 0,
                     0, GEMM_OUT_BF16};
+    return g5::run(p, stream);
+}
+
+int gemm_bf16_tn(int64_t M, int64_t N, int64_t K, const uint16_t *At, int64_t ldat, const uint16_t *B, int64_t ldb,
+                 void *C, int64_t ldc, int c_type, void *stream)
+{
+    const Problem p{GEMM_OP_BF16_TN, 1, M, N, K, (uint64_t)At, (uint64_t)B, (uint64_t)C, ldat, ldb, ldc, 0, 0, 0,
+                    c_type};
+    return g5::run(p, stream);
+}
+
+int gemm_bf16_tn_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const uint16_t *At, int64_t ldat,
+                         int64_t strideAt, const uint16_t *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc,
+                         int64_t strideC, int c_type, void *stream)
+{
+    const Problem p{GEMM_OP_BF16_TN, batch, M, N, K, (uint64_t)At, (uint64_t)B, (uint64_t)C, ldat, ldb, ldc,
+                    strideAt, strideB, strideC, c_type};
     return g5::run(p, stream);
 }
 

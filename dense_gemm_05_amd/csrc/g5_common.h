@@ -85,6 +85,7 @@ struct GemmArgs {
     const uint16_t *bias;
     int32_t align_bias;
     int32_t affine;          // 1: the small-M kernels apply the affine epilogue
+    int32_t a_trans;         // 1: A is given as At [K, M] (element (m, k) at A + k*lda + m)
 };
 
 // Fused epilogues of the bf16 ring kernels.

@@ -462,6 +462,12 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
 //    of attention scores.  Its slab is then K-contiguous like A's: copied
 //    and swizzled like A's, and read with ds_read_b128 instead of the
 //    transposing read.
+//  * AT: A is given transposed, At [K, M] row-major (element (m, k) at
+//    At + k*lda + m), the layout of the activations in a weight gradient
+//    X^T.dY.  Its slab (BK rows of BM columns m) is copied, swizzled and
+//    read like B's, with the transposing read giving the K-contiguous A
+//    fragments.  Needs 16-byte aligned rows of At and M % 8 == 0 or rows
+//    padded to a multiple of 8 (the masked copy reads whole 16-byte chunks).
 //  * F8: A and Bt hold E4M3FN codes (with BT): the same 64-byte slot rows
 //    then carry 64 values of K per stage, each 16-byte fragment feeds two
 //    v_mfma_f32_16x16x32_fp8_fp8 (the first takes bytes 0-7 of every lane,
@@ -470,7 +476,7 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
 //    p.scale_b[column] before the epilogue ("Operator & Runtime" §5.4.3,
 //    Example 5-7: dequantization by the row's factor).
 template <int BM, int BN, int WGM, int WGN, int NSA, int NSB, int AV, bool MASKED, int EPI = EPI_NONE,
-          bool SK = false, bool BT = false, bool F8 = false>
+          bool SK = false, bool BT = false, bool F8 = false, bool AT = false>
 __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
 {
     constexpr int NWAVE = WGM * WGN;
@@ -478,6 +484,8 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     constexpr int EB = F8 ? 1 : 2;                            // bytes per operand element
     constexpr int KS = 64 / EB;                               // K per stage
     static_assert(!F8 || (BT && EPI == EPI_NONE), "fp8 operands: A and Bt, no fused epilogue");
+    static_assert(!AT || (!F8 && !BT && AV == 16 && EPI == EPI_NONE), "transposed A: bf16, B as [K, N]");
+    static_assert(!AT || ((BM / 8) % 8 == 0 && (BM % 128 != 0 || (BM / 8) % 16 == 0)), "At slot rows: whole swizzle groups");
     constexpr int TM = BM / WGM, TN = BN / WGN;
     constexpr int FM = TM / 16, FN = TN / 16;
     constexpr int NMFMA = FM * FN;
@@ -517,11 +525,15 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     // moved there, so everything after this works on K columns from them.
     const int64_t kbase = SK ? (int64_t)slice * p.kt_per * KS : 0;
     const int64_t K = SK && slice < p.ksplit - 1 ? (int64_t)p.kt_per * KS : p.K - kbase;
-    const char *Abat = (const char *)p.A + (tc.b * p.sA + kbase) * EB;
+    const char *Abat = (const char *)p.A + (tc.b * p.sA + (AT ? kbase * lda : kbase)) * EB;
     const char *Bbat = (const char *)p.B + (tc.b * p.sB + (BT ? kbase : kbase * ldb)) * EB;
     // Byte extents of this batch entry's operands from those bases (reads
     // past them return 0).
-    const uint32_t a_bytes = MASKED ? (uint32_t)(((M - 1) * lda + (p.K - kbase)) * EB) : 0x7fffffffu;
+    // (At: the last row is read up to M rounded up to 8, which the host
+    // guarantees is inside the allocation: M % 8 == 0 or padded rows.)
+    const uint32_t a_bytes = !MASKED ? 0x7fffffffu
+                             : AT    ? (uint32_t)(((p.K - kbase - 1) * lda + ((M + 7) & ~(int64_t)7)) * 2)
+                                     : (uint32_t)(((M - 1) * lda + (p.K - kbase)) * EB);
     const uint32_t b_bytes =
         !MASKED ? 0x7fffffffu
         : BT    ? (uint32_t)(((N - 1) * ldb + (p.K - kbase)) * EB)
@@ -539,6 +551,13 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     uint32_t a_voff[LA];
 #pragma unroll
     for (int j = 0; j < LA; ++j) {
+        if constexpr (AT) {
+            // as B: 1024 bytes of the BK x BM slab (k rows of BM columns m) per instruction
+            const int q = 1024 * (a_i0 + j) + 16 * lane;
+            const int k = q / (BM * 2), pc = (q % (BM * 2)) / 16;
+            a_voff[j] = (uint32_t)((k * lda + m0 + (pc ^ swz_bn<BM>(k)) * 8) * 2);
+            continue;
+        }
         constexpr int LPR = 64 / ROWS_PER_A;                  // lanes per 64-byte row
         const int row = ROWS_PER_A * (a_i0 + j) + lane / LPR;
         const int byte = (lane % LPR) * AV;                   // byte within the slot row
@@ -569,8 +588,10 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     auto issue = [&](int kt, int ks) {
         if (a_wave) {
             uint16_t *sl = smem + (ks % NSA) * A_ELEMS;
-            const uint32_t adv = (uint32_t)(kt * 64);         // 64 bytes of each A row per stage
-            const i32x4_t r = make_rsrc(Abat + adv, a_bytes - adv);
+            // 64 bytes of each A row, or BK rows of At, per stage
+            const int64_t kstep = AT ? (int64_t)kt * BK * lda * 2 : (int64_t)kt * 64;
+            const uint32_t adv = (uint32_t)kstep;
+            const i32x4_t r = make_rsrc(Abat + kstep, a_bytes - adv);
 #pragma unroll
             for (int j = 0; j < LA; ++j) dma<AV>(r, a_voff[j], 0, sl + (a_i0 + j) * (32 * AV));
         } else {
@@ -585,11 +606,21 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     };
 
     // Fragment read offsets within a slot (elements).
-    int a_rd[FM], b_rd[FN], b_rd4[FN];
+    int a_rd[FM], a_rd4[FM], b_rd[FN], b_rd4[FN];
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
-        const int row = wm * TM + fm * 16 + li;
-        a_rd[fm] = row * BK + ((g ^ ((row >> 1) & 3)) * 8);
+        if constexpr (AT) {
+            // the transposing read of B's slab, with rows m in place of columns n
+            const int k = g * 8 + (li >> 2);
+            const int mcol = wm * TM + fm * 16 + (li & 3) * 4;
+            const int c = mcol >> 3, half = (mcol >> 2) & 1;
+            a_rd[fm] = k * BM + ((c ^ swz_bn<BM>(k)) * 8) + half * 4;
+            a_rd4[fm] = (k + 4) * BM + ((c ^ swz_bn<BM>(k + 4)) * 8) + half * 4;
+        } else {
+            const int row = wm * TM + fm * 16 + li;
+            a_rd[fm] = row * BK + ((g ^ ((row >> 1) & 3)) * 8);
+            a_rd4[fm] = 0;
+        }
     }
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
@@ -614,7 +645,15 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         const uint16_t *sa = smem + (kt % NSA) * A_ELEMS;
         const uint16_t *sb = smem + B_BASE + (kt % NSB) * B_ELEMS;
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) f.a[fm] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(sa + a_rd[fm]));
+        for (int fm = 0; fm < FM; ++fm) {
+            if constexpr (AT) {
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G5_LDS(i16x4, sa + a_rd[fm]));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(G5_LDS(i16x4, sa + a_rd4[fm]));
+                f.a[fm] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            } else {
+                f.a[fm] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(sa + a_rd[fm]));
+            }
+        }
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             if constexpr (BT) {
@@ -700,6 +739,14 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         asm volatile("" ::: "memory");
         const int64_t k0 = (int64_t)KT * KS;
         uint16_t *sA = smem, *sB = smem + B_BASE;
+        if constexpr (AT) {
+            for (int q = tid; q < BK * (BM / 8); q += NWAVE * 64) {
+                const int k = q / (BM / 8), c = q % (BM / 8);
+                const u32x4 v = load_chunk8_bf16((const uint16_t *)Abat + (k0 + k) * lda + m0, 8 * c, M - m0,
+                                                 k0 + k < K, p.align_a);
+                *(u32x4 *)(sA + k * BM + ((c ^ swz_bn<BM>(k)) * 8)) = v;
+            }
+        } else
         for (int q = tid; q < BM * 4; q += NWAVE * 64) {
             const int row = q >> 2, c = q & 3;
             const u32x4 v = F8 ? load_chunk16_u8((const uint8_t *)Abat + (m0 + row) * lda, k0 + 16 * c, K,
@@ -833,13 +880,17 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
 }
 
 // Ring kernel variants 1-3 (16-byte A copies aligned / masked, 4-byte A copies masked).
-template <int BM, int BN, int WGM, int WGN, int NSA, int NSB, int EPI, bool SK, bool BT, bool F8 = false>
+template <int BM, int BN, int WGM, int WGN, int NSA, int NSB, int EPI, bool SK, bool BT, bool F8 = false,
+          bool AT = false>
 static hipError_t launch_ring(const GemmArgs &a, int variant, dim3 g, dim3 b, hipStream_t s)
 {
     switch (variant) {
-    case 1: hipLaunchKernelGGL((k_bf16_ms<BM, BN, WGM, WGN, NSA, NSB, 16, false, EPI, SK, BT, F8>), g, b, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_bf16_ms<BM, BN, WGM, WGN, NSA, NSB, 16, true, EPI, SK, BT, F8>), g, b, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_bf16_ms<BM, BN, WGM, WGN, NSA, NSB, 4, true, EPI, SK, BT, F8>), g, b, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_bf16_ms<BM, BN, WGM, WGN, NSA, NSB, 16, false, EPI, SK, BT, F8, AT>), g, b, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_bf16_ms<BM, BN, WGM, WGN, NSA, NSB, 16, true, EPI, SK, BT, F8, AT>), g, b, 0, s, a); break;
+    case 3:
+        if constexpr (AT) return hipErrorInvalidValue;       // At rows are copied 16 bytes per lane only
+        else hipLaunchKernelGGL((k_bf16_ms<BM, BN, WGM, WGN, NSA, NSB, 4, true, EPI, SK, BT, F8>), g, b, 0, s, a);
+        break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

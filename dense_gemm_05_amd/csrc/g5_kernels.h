@@ -20,6 +20,10 @@ hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, int 
 // K split (a.ksplit > 1).
 hipError_t launch_ring_bt(int config_id, const GemmArgs &a, int variant, int64_t grid, hipStream_t s);
 
+// The bf16 ring kernels with A given transposed (a.a_trans): variants 1 and
+// 2 of the configs 256x192, 256x256 and 128x128, the last also with K split.
+hipError_t launch_ring_at(int config_id, const GemmArgs &a, int variant, int64_t grid, hipStream_t s);
+
 // The ring kernels on E4M3FN operands (a.fp8, a.b_trans): variants 1-3 of
 // the configs 256x192, 256x256 and 128x128, the last also with K split.
 hipError_t launch_ring_fp8(int config_id, const GemmArgs &a, int variant, int64_t grid, hipStream_t s);

@@ -984,6 +984,7 @@ hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, int 
     case CFG_BF16_256x256:
         if (a.fp8) return launch_ring_fp8(config_id, a, variant, grid, s);
         if (a.b_trans) return launch_ring_bt(config_id, a, variant, grid, s);
+        if (a.a_trans) return launch_ring_at(config_id, a, variant, grid, s);
         break;
     default: break;
     }

@@ -13,6 +13,7 @@ from . import _lib
 from ._lib import GemmError, GemmPlan, lib
 
 __all__ = ["gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm_bf16_nt_batched",
+           "gemm_bf16_tn", "gemm_bf16_tn_batched",
            "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_fp8_quantize_rows", "gemm_fp8_nt", "gemm_bf16_affine",
            "plan_query", "GemmError"]
 
@@ -179,6 +180,50 @@ def gemm_bf16_nt_batched(A, Bt, C=None, out_dtype=torch.bfloat16):
     return C
 
 
+def gemm_bf16_tn(At, B, C=None, out_dtype=torch.bfloat16):
+    """C[M,N] = At[K,M]^T . B[K,N] for bfloat16 operands (gemm_bf16_tn): A
+    given transposed, e.g. the activations of a weight gradient X^T . dY."""
+    if At.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("gemm_bf16_tn takes bfloat16 operands")
+    K, M = At.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    dev = _check_dev(At, B)
+    if C is None:
+        C = torch.empty((M, N), dtype=out_dtype, device=dev)
+    if C.shape != (M, N):
+        raise ValueError("C must be [M, N]")
+    code = _out_code(C.dtype)
+    st = _launch(lib().gemm_bf16_tn, dev, M, N, K, At.data_ptr(), _ld(At, M), B.data_ptr(), _ld(B, N),
+                 C.data_ptr(), _ld(C, N), code)
+    if st != 0:
+        raise GemmError(st, "gemm_bf16_tn")
+    return C
+
+
+def gemm_bf16_tn_batched(At, B, C=None, out_dtype=torch.bfloat16):
+    """C[b] = At[b]^T . B[b] for bfloat16 stacks [batch, K, M] and [batch, K, N]
+    (gemm_bf16_tn_batched); a batch stride of 0 broadcasts an operand."""
+    if At.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("gemm_bf16_tn_batched takes bfloat16 operands")
+    batch, K, M = At.shape
+    b2, K2, N = B.shape
+    if batch != b2 or K != K2:
+        raise ValueError("shape mismatch")
+    dev = _check_dev(At, B)
+    if C is None:
+        C = torch.empty((batch, M, N), dtype=out_dtype, device=dev)
+    if tuple(C.shape) != (batch, M, N):
+        raise ValueError("C must be [batch, M, N]")
+    code = _out_code(C.dtype)
+    st = _launch(lib().gemm_bf16_tn_batched, dev, batch, M, N, K, At.data_ptr(), _ld(At, M), _bstride(At),
+                 B.data_ptr(), _ld(B, N), _bstride(B), C.data_ptr(), _ld(C, N), _bstride(C), code)
+    if st != 0:
+        raise GemmError(st, "gemm_bf16_tn_batched")
+    return C
+
+
 def _codes(t):
     """E4M3FN codes: a uint8 tensor or a float8_e4m3fn tensor viewed as bytes."""
     if t.dtype == torch.uint8:
@@ -308,11 +353,11 @@ def gemm_bf16_affine(A, B, C, alpha=1.0, bias=None, beta=0.0):
 def plan_query(op, M, N, K, batch=1, lda=None, ldb=None, ldc=None, a_addr=0x10000, b_addr=0x20000000,
                c_addr=0x40000000, sA=None, sB=None, sC=None, c_type=_lib.GEMM_OUT_BF16):
     """Host-only: the status and plan a call would produce (no GPU work)."""
-    lda = K if lda is None else lda
+    lda = (M if op == _lib.GEMM_OP_BF16_TN else K) if lda is None else lda
     ldb = (2 * N if op == _lib.GEMM_OP_BF16_SWIGLU else K if op in (_lib.GEMM_OP_BF16_NT, _lib.GEMM_OP_FP8_NT)
            else N) if ldb is None else ldb
     ldc = N if ldc is None else ldc
-    sA = M * lda if sA is None else sA
+    sA = (K if op == _lib.GEMM_OP_BF16_TN else M) * lda if sA is None else sA
     sB = (N if op in (_lib.GEMM_OP_BF16_NT, _lib.GEMM_OP_FP8_NT) else K) * ldb if sB is None else sB
     sC = M * ldc if sC is None else sC
     out = GemmPlan()

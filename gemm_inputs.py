@@ -98,6 +98,16 @@ def swiglu_inputs(M=1024, K=4096, N=12288, workload=W_FFN):
     return X, np.ascontiguousarray(np.concatenate([Wg, Wu], axis=1))
 
 
+def wgrad_inputs(tokens=1024, d_in=4096, d_out=12288, workload=W_FFN):
+    """The weight gradient of the FFN projection, dW = X^T . dY: X ~ N(0,1)
+    [tokens, d_in] (the FFN projection's X, given as At [K, M] with
+    K = tokens, M = d_in) and dY ~ N(0, 1/64) [tokens, d_out] (tensor id 5);
+    bf16 bit patterns."""
+    X = to_bf16_bits(normal(rng(workload, 0), (tokens, d_in)))
+    dY = to_bf16_bits(normal(rng(workload, 5), (tokens, d_out), 0.125))
+    return X, dY
+
+
 def batched_inputs(batch=32, M=1024, N=1024, K=128, workload=W_BATCHED):
     """Q ~ N(0,1) [batch,M,K] and Kmat ~ N(0,1) [batch,N,K] in bf16; the B
     operand is the materialised row-major transpose Kmat^T [batch,K,N]."""

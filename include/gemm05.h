@@ -50,7 +50,8 @@
  *
  * Errors.  A negative status is returned and nothing is enqueued when the
  * arguments are invalid (GEMM_ERR_INVALID_ARG): a negative size or batch;
- * lda < K, ldb < N or ldc < N for a non-empty operand; a NULL pointer for an
+ * lda < K, ldb < N or ldc < N for a non-empty operand (for the transposed
+ * layouts: ldat < M, ldbt < K); a NULL pointer for an
  * operand that is read or written; a c_type outside gemm_out_type; a negative
  * batch stride; batch > 1 with strideC < (M-1)*ldc + N (C entries would
  * overlap); or C's byte range overlapping A's or B's.  GEMM_ERR_UNSUPPORTED:
@@ -127,6 +128,27 @@ int gemm_bf16_nt(int64_t M, int64_t N, int64_t K,
 int gemm_bf16_nt_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
                          const uint16_t *A, int64_t lda, int64_t strideA,
                          const uint16_t *Bt, int64_t ldbt, int64_t strideBt,
+                         void *C, int64_t ldc, int64_t strideC, int c_type,
+                         void *stream);
+
+/* BF16 GEMM with A given transposed ("TN"): C [M,N] := At^T . B [K,N],
+ * where At [K,M] is row-major with row stride ldat >= M, so A's element
+ * (m, k) is At[k*ldat + m].  This is the layout of the activations X [K,M]
+ * in a weight gradient X^T . dY, which would otherwise need a transposed
+ * copy.  Everything else follows gemm_bf16 / gemm_bf16_batched (strideAt is
+ * the batch stride of At), except that every size runs on the tiled
+ * kernels, and At rows that are not 16-byte aligned, or M not a multiple
+ * of 8, are first copied to aligned rows of ceil(M/8)*8 elements (zero
+ * padded) in the workspace described under Ownership
+ * (GEMM_ERR_UNSUPPORTED if that allocation fails). */
+int gemm_bf16_tn(int64_t M, int64_t N, int64_t K,
+                 const uint16_t *At, int64_t ldat,
+                 const uint16_t *B, int64_t ldb,
+                 void *C, int64_t ldc, int c_type,
+                 void *stream);
+int gemm_bf16_tn_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                         const uint16_t *At, int64_t ldat, int64_t strideAt,
+                         const uint16_t *B, int64_t ldb, int64_t strideB,
                          void *C, int64_t ldc, int64_t strideC, int c_type,
                          void *stream);
 
@@ -291,8 +313,9 @@ typedef enum {
     GEMM_OP_BF16_SWIGLU = 3, /* gemm_bf16_swiglu (batch 1, b = Wgu, c_type ignored) */
     GEMM_OP_BF16_NT = 4,     /* gemm_bf16_nt, gemm_bf16_nt_batched (b = Bt, ldb = ldbt) */
     GEMM_OP_FP8_NT = 5,      /* gemm_fp8_nt (batch 1, b = Bt; scales do not change the plan) */
-    GEMM_OP_BF16_AFFINE = 6  /* gemm_bf16_affine with alpha = 1 (alpha, beta and bias do not change the
+    GEMM_OP_BF16_AFFINE = 6, /* gemm_bf16_affine with alpha = 1 (alpha, beta and bias do not change the
                                 plan; alpha == 0 plans the element-wise pass of K == 0) */
+    GEMM_OP_BF16_TN = 7      /* gemm_bf16_tn, gemm_bf16_tn_batched (a = At, lda = ldat) */
 } gemm_op;
 
 /* Validate the arguments of a call and report the plan it would launch,

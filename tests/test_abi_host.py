@@ -357,6 +357,38 @@ def test_nt_arguments_and_plans(L):
     assert st == 0 and p.name == b"bf16_128x128" and p.variant == 1 and p.workspace_bytes == 0
 
 
+def test_tn_arguments_and_plans(L, monkeypatch):
+    """Transposed A: ldat >= M, At spans K rows of M; the ring kernels of the
+    256x192, 256x256 and 128x128 configs run it (variants 1 and 2 only); At
+    rows not 16-byte aligned, or M % 8 != 0, are realigned into rows of
+    ceil(M/8)*8 elements first; small M stays on the tiled kernels."""
+    def tn(M, N, K, lda=None, ldb=None, ldc=None, a=A_ADDR, c=C_ADDR):
+        return L.gemm_bf16_tn(M, N, K, a, M if lda is None else lda, B_ADDR, N if ldb is None else ldb, c,
+                              N if ldc is None else ldc, 0, None)
+    assert tn(4, 8, 16, lda=3) == g5.GEMM_ERR_INVALID_ARG
+    assert tn(4, 8, 16, a=0) == g5.GEMM_ERR_INVALID_ARG
+    assert tn(4, 8, 16, c=A_ADDR + (15 * 4 + 2) * 2) == g5.GEMM_ERR_INVALID_ARG    # C inside At's last row
+    assert tn(0, 8, 16) == g5.GEMM_OK
+    op = g5.GEMM_OP_BF16_TN
+    st, p = g5.plan_query(op, 4096, 12288, 1024)
+    assert st == 0 and p.family == 2 and p.variant == 1 and p.workspace_bytes == 0
+    assert p.name in (b"bf16_256x192", b"bf16_256x256", b"bf16_128x128")
+    st, p = g5.plan_query(op, 300, 392, 262)                       # M % 8 != 0
+    assert st == 0 and p.variant == 2 and p.workspace_bytes >= 262 * 304 * 2
+    st, p = g5.plan_query(op, 304, 392, 262, lda=306)              # 4-byte aligned At rows
+    assert st == 0 and p.variant == 2 and p.workspace_bytes >= 262 * 304 * 2
+    st, p = g5.plan_query(op, 304, 392, 264, lda=312, ldb=400)     # aligned: no copy
+    assert st == 0 and p.variant == 2 and p.workspace_bytes == 0
+    st, p = g5.plan_query(op, 1, 4096, 4096, lda=8)
+    assert st == 0 and p.family == 2
+    st, p = g5.plan_query(op, 512, 512, 4096)
+    assert st == 0 and p.name == b"bf16_128x128" and p.ksplit > 1
+    for bad in ("bf16_256x128", "decode_64", "f32_128x128"):
+        monkeypatch.setenv("GEMM_FORCE_CONFIG", bad)
+        st, _ = g5.plan_query(op, 304, 392, 264)
+        assert st == g5.GEMM_ERR_UNSUPPORTED, bad
+
+
 def test_fp8_arguments_and_plans(L):
     """FP8: factors 4-byte aligned and not overlapping C; Bt rows 16-byte
     aligned and A rows 4-byte aligned (the ring kernels only); 64 K values
