@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "sgemm", "batched", "ragged", "swiglu", "shard", "fp8", "scores_nt", "decode_nt", "copy"])
+    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "sgemm", "batched", "ragged", "swiglu", "shard", "fp8", "scores_nt", "decode_nt", "affine", "wgrad_tn", "copy"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--prewarm-seconds", type=float, default=1.0,
@@ -377,6 +377,51 @@ def main():
                           "GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "alg_bytes": alg_bytes,
                           "rotations": R})
         del dQ, dK, dC
+
+    # ------------------------------------------------------------ FFN projection with bias and residual
+    if args.only in ("all", "affine"):
+        # C := X.W + bias + C (beta = 1: a residual add into the bf16 output),
+        # against the plain projection on the same buffers.
+        M, N, K = 1024, 12288, 4096
+        X, W = gi.ffn_inputs()
+        g = np.random.default_rng([gi.SEED_BASE + gi.W_FFN, 6])
+        bias = gi.to_bf16_bits(gi.normal(g, (N,)))
+        R = rotations(2 * (M * K + K * N + 2 * M * N))
+        dX = [to_dev_bf16(X) for _ in range(R)]
+        dW = [to_dev_bf16(W) for _ in range(R)]
+        db = [to_dev_bf16(bias) for _ in range(R)]
+        dC = [torch.zeros((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        fns = [(lambda i=i: g5.gemm_bf16_affine(dX[i], dW[i], dC[i], bias=db[i], beta=1.0)) for i in range(R)]
+        plain = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i])) for i in range(R)]
+        ms = timed(fns, 50, 10)
+        ms_plain = timed(plain, 50, 10)
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        log(f"FFN + bias + residual: {ms * 1e3:.2f} us ({tf:.1f} TFLOPS); plain projection {ms_plain * 1e3:.2f} us")
+        workloads.append({"name": "ffn_bias_residual_bf16_1024x12288x4096", "us": round(ms * 1e3, 3),
+                          "tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                          "plain_projection_us": round(ms_plain * 1e3, 3), "rotations": R})
+        del dX, dW, db, dC
+
+    # ------------------------------------------------------------ weight gradient from row-major X (TN)
+    if args.only in ("all", "wgrad_tn"):
+        # dW [4096, 12288] = X^T . dY with X [1024, 4096] as stored (At) and
+        # dY [1024, 12288]: 103 GFLOP over K = 1024 tokens.
+        X, dY = gi.wgrad_inputs()
+        K, M = X.shape
+        N = dY.shape[1]
+        R = rotations(2 * (M * K + K * N + M * N))
+        dX = [to_dev_bf16(X) for _ in range(R)]
+        dD = [to_dev_bf16(dY) for _ in range(R)]
+        dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        fns = [(lambda i=i: g5.gemm_bf16_tn(dX[i], dD[i], dC[i])) for i in range(R)]
+        st, plan = g5.plan_query(g5.GEMM_OP_BF16_TN, M, N, K)
+        ms = timed(fns, 50, 10)
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        log(f"weight gradient X^T.dY 4096x12288x1024 (TN): {ms * 1e3:.2f} us ({tf:.1f} TFLOPS), {plan.name.decode()}")
+        workloads.append({"name": "wgrad_tn_bf16_4096x12288x1024", "us": round(ms * 1e3, 3), "tflops": round(tf, 2),
+                          "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "config": plan.name.decode(),
+                          "rotations": R})
+        del dX, dD, dC
 
     out["workloads"] = workloads
 
