@@ -59,7 +59,7 @@ def kernel_label(plan):
         av, masked = {1: (16, "false"), 2: (16, "true"), 3: (4, "true")}[plan.variant]
         wg = "2,4" if tm == 256 and tn in (192, 256) else "4,2"
         sk = "true" if plan.ksplit > 1 else "false"
-        return (f"k_bf16_ms<{tm},{tn},{wg},4,4,{av},{masked},0,{sk},false,false> ({name}, grid {plan.grid}, "
+        return (f"k_bf16_ms<{tm},{tn},{wg},4,4,{av},{masked},0,{sk},false,false,false> ({name}, grid {plan.grid}, "
                 f"{plan.threads} threads)")
     return f"{name} variant {plan.variant} (grid {plan.grid}, {plan.threads} threads)"
 
