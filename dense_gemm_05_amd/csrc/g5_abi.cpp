@@ -93,13 +93,17 @@ int epi_of(const Problem &p)
 {
     return p.op == GEMM_OP_BF16_SILU     ? EPI_SILU
            : p.op == GEMM_OP_BF16_SWIGLU ? EPI_SWIGLU
-           : p.op == GEMM_OP_BF16_AFFINE ? EPI_AFFINE
-                                         : EPI_NONE;
+           : p.op == GEMM_OP_BF16_AFFINE || p.op == GEMM_OP_BF16_NT_AFFINE ? EPI_AFFINE
+                                                                            : EPI_NONE;
 }
+bool is_affine(const Problem &p) { return epi_of(p) == EPI_AFFINE; }
 // An affine call with no product to form (alpha == 0: A and B are not read).
-bool no_product(const Problem &p) { return p.op == GEMM_OP_BF16_AFFINE && p.alpha == 0.0f; }
+bool no_product(const Problem &p) { return is_affine(p) && p.alpha == 0.0f; }
 // B is given transposed, Bt [N, K].
-bool b_trans(const Problem &p) { return p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_FP8_NT; }
+bool b_trans(const Problem &p)
+{
+    return p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_FP8_NT || p.op == GEMM_OP_BF16_NT_AFFINE;
+}
 // A is given transposed, At [K, M].
 bool a_trans(const Problem &p) { return p.op == GEMM_OP_BF16_TN; }
 // Rows and columns of the A operand as stored: [M, K] or At [K, M].
@@ -145,17 +149,18 @@ bool overlap(const Range &x, const Range &y) { return x.lo < y.hi && y.lo < x.hi
 int validate(const Problem &p)
 {
     if (p.op != GEMM_OP_SGEMM && p.op != GEMM_OP_BF16 && p.op != GEMM_OP_BF16_SILU && p.op != GEMM_OP_BF16_SWIGLU &&
-        p.op != GEMM_OP_BF16_NT && p.op != GEMM_OP_FP8_NT && p.op != GEMM_OP_BF16_AFFINE && p.op != GEMM_OP_BF16_TN)
+        p.op != GEMM_OP_BF16_NT && p.op != GEMM_OP_FP8_NT && p.op != GEMM_OP_BF16_AFFINE && p.op != GEMM_OP_BF16_TN &&
+        p.op != GEMM_OP_BF16_NT_AFFINE)
         return GEMM_ERR_INVALID_ARG;
     if (p.batch < 0 || p.M < 0 || p.N < 0 || p.K < 0) return GEMM_ERR_INVALID_ARG;
-    if ((p.op == GEMM_OP_BF16 || p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_FP8_NT || p.op == GEMM_OP_BF16_AFFINE ||
+    if ((p.op == GEMM_OP_BF16 || p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_FP8_NT || is_affine(p) ||
          p.op == GEMM_OP_BF16_TN) &&
         p.c_type != GEMM_OUT_BF16 && p.c_type != GEMM_OUT_F32)
         return GEMM_ERR_INVALID_ARG;
     if (p.op == GEMM_OP_FP8_NT && (p.batch > 1 || (p.scale_a % 4) || (p.scale_b % 4))) return GEMM_ERR_INVALID_ARG;
     if ((p.op == GEMM_OP_BF16_SILU || p.op == GEMM_OP_BF16_SWIGLU) && (p.c_type != GEMM_OUT_BF16 || p.batch > 1))
         return GEMM_ERR_INVALID_ARG;
-    if (p.op == GEMM_OP_BF16_AFFINE && (!std::isfinite(p.alpha) || !std::isfinite(p.beta) || (p.bias % 2)))
+    if (is_affine(p) && (!std::isfinite(p.alpha) || !std::isfinite(p.beta) || (p.bias % 2)))
         return GEMM_ERR_INVALID_ARG;
     if (p.sA < 0 || p.sB < 0 || p.sC < 0) return GEMM_ERR_INVALID_ARG;
     if (p.batch == 0 || p.M == 0 || p.N == 0) return GEMM_OK;  // nothing to do
@@ -233,8 +238,10 @@ bool has_epilogues(int id) { return id == CFG_BF16_256x192 || id == CFG_BF16_256
 bool config_fits(const Problem &p, int id)
 {
     const ConfigInfo &c = kConfigs[id];
-    if (epi_of(p) == EPI_AFFINE && (id == CFG_DECODE_64 || id == CFG_DECODE_SPLIT))
-        return p.M <= 16 && p.batch <= 65535;                     // the small-M kernels apply it too
+    if (is_affine(p) && c.family == GEMM_FAMILY_DECODE) {       // the small-M kernels apply it too
+        if (b_trans(p)) return id == CFG_DECODE_NT && p.M <= 16 && p.batch <= 65535;
+        return (id == CFG_DECODE_64 || id == CFG_DECODE_SPLIT) && p.M <= 16 && p.batch <= 65535;
+    }
     if (epi_of(p) != EPI_NONE) return has_epilogues(id);
     if (p.op == GEMM_OP_FP8_NT) return has_epilogues(id);         // fp8 ring kernels: 256x192, 256x256, 128x128
     if (a_trans(p)) return has_epilogues(id);                       // transposed-A ring kernels: the same three
@@ -378,7 +385,8 @@ int select_plan(const Problem &p, Plan &pl)
         // staged at once (one load latency per tile instead of one per slab;
         // 256^3 measured 9.4 us with the double-buffered 64x64 kernel).
         pl.config = CFG_F32_32x32_WK;
-    } else if (p.op == GEMM_OP_BF16_NT && p.M <= 16 && p.batch <= 65535 && pl.align_b >= 16) {
+    } else if ((p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_BF16_NT_AFFINE) && p.M <= 16 && p.batch <= 65535 &&
+               pl.align_b >= 16) {
         // Small M with B transposed: a GEMV over the contiguous rows of Bt.
         pl.config = CFG_DECODE_NT;
     } else if ((p.op == GEMM_OP_BF16 || p.op == GEMM_OP_BF16_AFFINE) && p.M <= 16 && p.batch <= 65535) {
@@ -471,7 +479,8 @@ int select_plan(const Problem &p, Plan &pl)
     // The fused epilogues and a transposed B exist only in the ring kernels,
     // so such a call whose rows no ring variant takes is realigned at any
     // size: Bt's rows first, then A's.
-    if (kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && p.op == GEMM_OP_BF16_NT && pl.align_b < 16) {
+    if (kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && b_trans(p) && p.op != GEMM_OP_FP8_NT &&
+        pl.align_b < 16) {
         pl.realign_b = true;
         pl.ldb2 = (p.K + 7) / 8 * 8;
         pl.align_b = 16;
@@ -704,7 +713,7 @@ int run(const Problem &p, void *stream)
     a.beta = p.beta;
     a.bias = (const uint16_t *)p.bias;
     a.align_bias = row_alignment(p.bias, 0, 0, 1, 2);
-    a.affine = p.op == GEMM_OP_BF16_AFFINE ? 1 : 0;
+    a.affine = is_affine(p) ? 1 : 0;
     a.a_trans = a_trans(p) ? 1 : 0;
     if (pl.realign_b) {
         int dev = 0;
@@ -784,7 +793,7 @@ int run(const Problem &p, void *stream)
         a.tiles_n = pl.tiles_n;
     }
     const hipError_t e =
-        pl.config == CFG_ZERO ? (p.op == GEMM_OP_BF16_AFFINE ? launch_affine_no_product(a, pl.grid, (hipStream_t)stream)
+        pl.config == CFG_ZERO ? (is_affine(p) ? launch_affine_no_product(a, pl.grid, (hipStream_t)stream)
                                                              : launch_config(pl.config, false, a, 0, pl.grid, (hipStream_t)stream))
         : epi_of(p) == EPI_NONE || !tiled(pl.config)
             ? launch_config(pl.config, p.op == GEMM_OP_SGEMM, a, pl.variant, pl.grid, (hipStream_t)stream)
@@ -910,6 +919,19 @@ int gemm_bf16_affine(int64_t batch, int64_t M, int64_t N, int64_t K, const uint1
 {
     Problem p{GEMM_OP_BF16_AFFINE, batch, M, N, K, (uint64_t)A, (uint64_t)B, (uint64_t)C, lda, ldb, ldc,
               strideA, strideB, strideC, c_type};
+    p.alpha = alpha;
+    p.beta = beta;
+    p.bias = (uint64_t)bias;
+    return g5::run(p, stream);
+}
+
+int gemm_bf16_nt_affine(int64_t batch, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                        int64_t strideA, const uint16_t *Bt, int64_t ldbt, int64_t strideBt, float alpha,
+                        const uint16_t *bias, float beta, void *C, int64_t ldc, int64_t strideC, int c_type,
+                        void *stream)
+{
+    Problem p{GEMM_OP_BF16_NT_AFFINE, batch, M, N, K, (uint64_t)A, (uint64_t)Bt, (uint64_t)C, lda, ldbt, ldc,
+              strideA, strideBt, strideC, c_type};
     p.alpha = alpha;
     p.beta = beta;
     p.bias = (uint64_t)bias;

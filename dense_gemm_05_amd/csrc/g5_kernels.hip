@@ -835,8 +835,7 @@ __global__ void __launch_bounds__(NW * 64) k_decode_nt(GemmArgs p)
             for (int q = 0; q < 4; ++q) {
                 const int64_t n = n0 + 16 * r + 4 * gg + q;
                 if (n >= N) continue;
-                if (p.out_f32) ((float *)p.C + bidx * p.sC)[m * p.ldc + n] = sum[q];
-                else ((uint16_t *)p.C + bidx * p.sC)[m * p.ldc + n] = (uint16_t)bf16_rne(sum[q]);
+                store_out(p, bidx, m, n, sum[q]);
             }
         }
     }

@@ -15,7 +15,7 @@ from ._lib import GemmError, GemmPlan, lib
 __all__ = ["gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm_bf16_nt_batched",
            "gemm_bf16_tn", "gemm_bf16_tn_batched",
            "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_fp8_quantize_rows", "gemm_fp8_nt", "gemm_bf16_affine",
-           "plan_query", "GemmError"]
+           "gemm_bf16_nt_affine", "plan_query", "GemmError"]
 
 
 def _ld(t, inner):
@@ -328,13 +328,28 @@ def gemm_bf16_affine(A, B, C, alpha=1.0, bias=None, beta=0.0):
     bfloat16 A [M,K] / B [K,N] or stacks [batch, M, K] / [batch, K, N], C of
     the matching shape in bfloat16 or float32 (read when beta != 0), bias a
     bfloat16 vector of N elements or None.  Returns C."""
+    return _affine(A, B, C, alpha, bias, beta, False)
+
+
+def gemm_bf16_nt_affine(A, Bt, C, alpha=1.0, bias=None, beta=0.0):
+    """C := alpha * (A . Bt^T) + bias + beta * C in place
+    (gemm_bf16_nt_affine): Bt [N,K] (or [batch, N, K]) is a linear layer's
+    [out, in] weight; otherwise as gemm_bf16_affine."""
+    return _affine(A, Bt, C, alpha, bias, beta, True)
+
+
+def _affine(A, B, C, alpha, bias, beta, b_trans):
+    what = "gemm_bf16_nt_affine" if b_trans else "gemm_bf16_affine"
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
-        raise TypeError("gemm_bf16_affine takes bfloat16 operands")
+        raise TypeError(f"{what} takes bfloat16 operands")
     if A.dim() != B.dim() or A.dim() not in (2, 3):
         raise ValueError("A and B must both be 2-D or both be 3-D")
     A3, B3, C3 = (A, B, C) if A.dim() == 3 else (A.unsqueeze(0), B.unsqueeze(0), C.unsqueeze(0))
     batch, M, K = A3.shape
-    b2, K2, N = B3.shape
+    if b_trans:
+        b2, N, K2 = B3.shape
+    else:
+        b2, K2, N = B3.shape
     if batch != b2 or K != K2 or tuple(C3.shape) != (batch, M, N):
         raise ValueError("shape mismatch")
     dev = _check_dev(A, B, C) if bias is None else _check_dev(A, B, C, bias)
@@ -342,11 +357,12 @@ def gemm_bf16_affine(A, B, C, alpha=1.0, bias=None, beta=0.0):
                              (N > 1 and bias.stride(0) != 1)):
         raise ValueError("bias must be a contiguous bfloat16 vector of N elements")
     code = _out_code(C.dtype)
-    st = _launch(lib().gemm_bf16_affine, dev, batch, M, N, K, A3.data_ptr(), _ld(A3, K), _bstride(A3),
-                 B3.data_ptr(), _ld(B3, N), _bstride(B3), float(alpha), None if bias is None else bias.data_ptr(),
-                 float(beta), C3.data_ptr(), _ld(C3, N), _bstride(C3), code)
+    fn = lib().gemm_bf16_nt_affine if b_trans else lib().gemm_bf16_affine
+    st = _launch(fn, dev, batch, M, N, K, A3.data_ptr(), _ld(A3, K), _bstride(A3),
+                 B3.data_ptr(), _ld(B3, K if b_trans else N), _bstride(B3), float(alpha),
+                 None if bias is None else bias.data_ptr(), float(beta), C3.data_ptr(), _ld(C3, N), _bstride(C3), code)
     if st != 0:
-        raise GemmError(st, "gemm_bf16_affine")
+        raise GemmError(st, what)
     return C
 
 
@@ -354,11 +370,11 @@ def plan_query(op, M, N, K, batch=1, lda=None, ldb=None, ldc=None, a_addr=0x1000
                c_addr=0x40000000, sA=None, sB=None, sC=None, c_type=_lib.GEMM_OUT_BF16):
     """Host-only: the status and plan a call would produce (no GPU work)."""
     lda = (M if op == _lib.GEMM_OP_BF16_TN else K) if lda is None else lda
-    ldb = (2 * N if op == _lib.GEMM_OP_BF16_SWIGLU else K if op in (_lib.GEMM_OP_BF16_NT, _lib.GEMM_OP_FP8_NT)
-           else N) if ldb is None else ldb
+    nt = op in (_lib.GEMM_OP_BF16_NT, _lib.GEMM_OP_FP8_NT, _lib.GEMM_OP_BF16_NT_AFFINE)
+    ldb = (2 * N if op == _lib.GEMM_OP_BF16_SWIGLU else K if nt else N) if ldb is None else ldb
     ldc = N if ldc is None else ldc
     sA = (K if op == _lib.GEMM_OP_BF16_TN else M) * lda if sA is None else sA
-    sB = (N if op in (_lib.GEMM_OP_BF16_NT, _lib.GEMM_OP_FP8_NT) else K) * ldb if sB is None else sB
+    sB = (N if nt else K) * ldb if sB is None else sB
     sC = M * ldc if sC is None else sC
     out = GemmPlan()
     st = lib().gemm_plan_query(op, batch, M, N, K, a_addr, lda, sA, b_addr, ldb, sB, c_addr, ldc, sC,

@@ -263,6 +263,20 @@ int gemm_bf16_affine(int64_t batch, int64_t M, int64_t N, int64_t K,
                      void *C, int64_t ldc, int64_t strideC, int c_type,
                      void *stream);
 
+/* The same with B given transposed as in gemm_bf16_nt: Bt [N,K] row-major
+ * (ldbt >= K), the [out, in] weight of a linear layer, so that
+ * C := alpha * (A . Bt^T) + bias + beta * C is the layer's output with its
+ * bias and, with beta = 1, a residual add.  M <= 16 with 16-byte aligned Bt
+ * rows runs the small-M transposed-B kernel, which applies the same
+ * epilogue; other calls follow gemm_bf16_nt for the realignment of Bt
+ * rows. */
+int gemm_bf16_nt_affine(int64_t batch, int64_t M, int64_t N, int64_t K,
+                        const uint16_t *A, int64_t lda, int64_t strideA,
+                        const uint16_t *Bt, int64_t ldbt, int64_t strideBt,
+                        float alpha, const uint16_t *bias, float beta,
+                        void *C, int64_t ldc, int64_t strideC, int c_type,
+                        void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *gemm_status_string(int status);
 
@@ -315,7 +329,8 @@ typedef enum {
     GEMM_OP_FP8_NT = 5,      /* gemm_fp8_nt (batch 1, b = Bt; scales do not change the plan) */
     GEMM_OP_BF16_AFFINE = 6, /* gemm_bf16_affine with alpha = 1 (alpha, beta and bias do not change the
                                 plan; alpha == 0 plans the element-wise pass of K == 0) */
-    GEMM_OP_BF16_TN = 7      /* gemm_bf16_tn, gemm_bf16_tn_batched (a = At, lda = ldat) */
+    GEMM_OP_BF16_TN = 7,     /* gemm_bf16_tn, gemm_bf16_tn_batched (a = At, lda = ldat) */
+    GEMM_OP_BF16_NT_AFFINE = 8 /* gemm_bf16_nt_affine with alpha = 1 (b = Bt, ldb = ldbt) */
 } gemm_op;
 
 /* Validate the arguments of a call and report the plan it would launch,

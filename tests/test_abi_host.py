@@ -498,3 +498,26 @@ def test_affine_plans(L):
     assert st == 0 and p.variant == 3
     st, p = g5.plan_query(op, 257, 96, 33)
     assert st == 0 and p.variant == 2 and p.workspace_bytes == 257 * 40 * 2        # A realigned
+
+
+def test_nt_affine_plans(L):
+    """The affine epilogue with B transposed: the transposed-B ring kernels
+    of the fused configs (with K split for small outputs), the small-M
+    transposed-B kernel for M <= 16, Bt rows realigned when not 16-byte
+    aligned; the affine argument checks apply."""
+    op = g5.GEMM_OP_BF16_NT_AFFINE
+    st, p = g5.plan_query(op, 1024, 12288, 4096)
+    assert st == 0 and p.name == b"bf16_256x192" and p.variant == 1
+    st, p = g5.plan_query(op, 1, 12288, 4096)
+    assert st == 0 and p.name == b"decode_nt"
+    st, p = g5.plan_query(op, 512, 512, 4096)
+    assert st == 0 and p.name == b"bf16_128x128" and p.ksplit > 1
+    st, p = g5.plan_query(op, 300, 392, 264, ldb=265)
+    assert st == 0 and p.variant >= 1 and p.workspace_bytes >= 392 * 264 * 2
+    st, _ = g5.plan_query(op, 4, 12, 16)
+    assert st == g5.GEMM_ERR_UNSUPPORTED                                          # N % 8
+    args = (1, 4, 8, 16, A_ADDR, 16, 64, B_ADDR, 16, 128)
+    assert L.gemm_bf16_nt_affine(*args, float("nan"), None, 0.0, C_ADDR, 8, 32, 0, None) == g5.GEMM_ERR_INVALID_ARG
+    assert L.gemm_bf16_nt_affine(*args, 1.0, C_ADDR + 4, 0.0, C_ADDR, 8, 32, 0, None) == g5.GEMM_ERR_INVALID_ARG
+    assert L.gemm_bf16_nt_affine(1, 4, 8, 16, A_ADDR, 16, 64, B_ADDR, 15, 128, 1.0, None, 0.0, C_ADDR, 8, 32, 0,
+                                 None) == g5.GEMM_ERR_INVALID_ARG                  # ldbt < K

@@ -1,5 +1,6 @@
 """GPU parity of the affine epilogue C := alpha * (A.B) + bias + beta * C
-(gemm_bf16_affine) against the oracle, through the C ABI.
+(gemm_bf16_affine, and gemm_bf16_nt_affine with B given transposed) against
+the oracle, through the C ABI.
 
 The epilogue is applied to the finished output tile like the activations of
 page "Operator & Runtime" §5.4.2, with §5.4.3's rounding rule: the product
@@ -227,3 +228,94 @@ def test_affine_ffn_full_size(oracle_mod):
     check_affine(host_values(C)[rows], ref, oracle_mod.gemm_bf16(Xs, W), 4096, 1.0,
                  gi.bf16_bits_to_f32(bias).astype(np.float64), 1.0,
                  gi.bf16_bits_to_f32(res[rows]).astype(np.float64), False, what="ffn rows")
+
+
+# ------------------------------------------------------------ B given transposed
+
+def _nt_check(oracle_mod, A, Bt, bias, old, alpha, beta, got, out_f32, what):
+    B = np.ascontiguousarray(Bt.T)
+    ref = oracle_mod.gemm_bf16_affine(A, B, alpha, bias, beta, old)
+    old_vals = old.astype(np.float64) if out_f32 else gi.bf16_bits_to_f32(old).astype(np.float64)
+    check_affine(got, ref, oracle_mod.gemm_bf16(A, B), A.shape[1], alpha,
+                 gi.bf16_bits_to_f32(bias).astype(np.float64), beta, old_vals, out_f32,
+                 amax_bf16(A), amax_bf16(Bt), what)
+
+
+@pytest.mark.parametrize("cfg", [None, "bf16_256x192", "bf16_256x256", "bf16_128x128"])
+@pytest.mark.parametrize("M,N,K,pb", [(300, 392, 264, 8), (257, 200, 1000, 0), (300, 392, 262, 0)])
+def test_nt_affine_ragged(oracle_mod, monkeypatch, cfg, M, N, K, pb):
+    """A linear layer's output with its bias and a residual (Bt [N, K]): every
+    ring config with the transposed B and the epilogue, both output types;
+    K = 262 gives 4-byte aligned Bt rows (realigned first)."""
+    g = np.random.default_rng([gi.SEED_BASE + 5400, M, N, K, pb])
+    A = gi.to_bf16_bits(gi.normal(g, (M, K)))
+    Bt = gi.to_bf16_bits(gi.normal(g, (N, K + pb), 0.125))
+    bias = gi.to_bf16_bits(gi.normal(g, (N,)))
+    old32 = gi.normal(g, (M, N))
+    old16 = gi.to_bf16_bits(old32)
+    if cfg:
+        monkeypatch.setenv("GEMM_FORCE_CONFIG", cfg)
+    for out_f32 in (False, True):
+        _say(f"nt affine {cfg} {M}x{N}x{K} out_f32={out_f32}")
+        C = dev_f32(old32) if out_f32 else dev_bf16(old16)
+        g5.gemm_bf16_nt_affine(dev_bf16(A), dev_bf16(Bt)[:, :K], C, alpha=0.75, bias=dev_bf16(bias), beta=1.0)
+        _nt_check(oracle_mod, A, np.ascontiguousarray(Bt[:, :K]), bias, old32 if out_f32 else old16, 0.75, 1.0,
+                  host_values(C), out_f32, f"nt affine {cfg}")
+
+
+@pytest.mark.parametrize("S", [2, 4])
+def test_nt_affine_ksplit(oracle_mod, monkeypatch, S):
+    _say(f"nt affine ksplit {S}")
+    g = np.random.default_rng([gi.SEED_BASE + 5500, S])
+    A = gi.to_bf16_bits(gi.normal(g, (200, 1024)))
+    Bt = gi.to_bf16_bits(gi.normal(g, (264, 1024), 0.125))
+    bias = gi.to_bf16_bits(gi.normal(g, (264,)))
+    old = gi.normal(g, (200, 264))
+    monkeypatch.setenv("GEMM_FORCE_CONFIG", "bf16_128x128")
+    monkeypatch.setenv("GEMM_FORCE_KSPLIT", str(S))
+    C = dev_f32(old)
+    g5.gemm_bf16_nt_affine(dev_bf16(A), dev_bf16(Bt), C, alpha=1.0, bias=dev_bf16(bias), beta=-0.5)
+    _nt_check(oracle_mod, A, Bt, bias, old, 1.0, -0.5, host_values(C), True, f"nt affine split {S}")
+
+
+@pytest.mark.parametrize("M,N,K,batch", [(1, 12288, 4096, 1), (16, 12288, 4096, 1), (5, 200, 72, 2), (3, 1000, 4104, 1)])
+def test_nt_affine_small_m(oracle_mod, M, N, K, batch):
+    """M <= 16 on the small-M transposed-B kernel with the epilogue (K tails,
+    batched, both outputs): a decode step of a linear layer with bias and
+    residual."""
+    g = np.random.default_rng([gi.SEED_BASE + 5600, M, N, K, batch])
+    A = gi.to_bf16_bits(gi.normal(g, (batch, M, K)))
+    Bt = gi.to_bf16_bits(gi.normal(g, (batch, N, K), 0.125))
+    bias = gi.to_bf16_bits(gi.normal(g, (N,)))
+    old32 = gi.normal(g, (batch, M, N))
+    old16 = gi.to_bf16_bits(old32)
+    st, plan = g5.plan_query(g5.GEMM_OP_BF16_NT_AFFINE, M, N, K, batch=batch)
+    assert st == 0 and plan.name == b"decode_nt"
+    for out_f32 in (False, True):
+        _say(f"nt affine small M {batch}x{M}x{N}x{K} out_f32={out_f32}")
+        C = dev_f32(old32) if out_f32 else dev_bf16(old16)
+        dA, dB = dev_bf16(A), dev_bf16(Bt)
+        if batch == 1:
+            g5.gemm_bf16_nt_affine(dA[0], dB[0], C[0], alpha=1.0, bias=dev_bf16(bias), beta=1.0)
+        else:
+            g5.gemm_bf16_nt_affine(dA, dB, C, alpha=1.0, bias=dev_bf16(bias), beta=1.0)
+        got = host_values(C)
+        for b in range(batch):
+            _nt_check(oracle_mod, A[b], Bt[b], bias, (old32 if out_f32 else old16)[b], 1.0, 1.0, got[b], out_f32,
+                      f"nt affine small M entry {b}")
+
+
+def test_nt_affine_linear_layer_full_size(oracle_mod):
+    """The FFN projection as a linear layer (weight [12288, 4096]) with bias
+    and residual, bf16: sampled rows, all columns."""
+    _say("nt affine 1024x12288x4096")
+    X, W = gi.ffn_inputs()
+    Wt = np.ascontiguousarray(W.T)
+    g = np.random.default_rng([gi.SEED_BASE + 5700])
+    bias = gi.to_bf16_bits(gi.normal(g, (12288,)))
+    res = gi.to_bf16_bits(gi.normal(g, (1024, 12288)))
+    C = dev_bf16(res)
+    g5.gemm_bf16_nt_affine(dev_bf16(X), dev_bf16(Wt), C, alpha=1.0, bias=dev_bf16(bias), beta=1.0)
+    rows = np.array([0, 255, 256, 700, 1023])
+    _nt_check(oracle_mod, np.ascontiguousarray(X[rows]), Wt, bias, np.ascontiguousarray(res[rows]), 1.0, 1.0,
+              host_values(C)[rows], False, "nt affine FFN rows")
