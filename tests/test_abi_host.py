@@ -521,3 +521,19 @@ def test_nt_affine_plans(L):
     assert L.gemm_bf16_nt_affine(*args, 1.0, C_ADDR + 4, 0.0, C_ADDR, 8, 32, 0, None) == g5.GEMM_ERR_INVALID_ARG
     assert L.gemm_bf16_nt_affine(1, 4, 8, 16, A_ADDR, 16, 64, B_ADDR, 15, 128, 1.0, None, 0.0, C_ADDR, 8, 32, 0,
                                  None) == g5.GEMM_ERR_INVALID_ARG                  # ldbt < K
+
+
+def test_operands_over_2gib_plans(L):
+    """An operand whose byte extent reaches 2^31 cannot be addressed by the
+    ring kernels' 32-bit buffer offsets: plain products take the general
+    kernel (variant 0); calls that exist only on the ring kernels report
+    GEMM_ERR_UNSUPPORTED instead of launching."""
+    M, N, K = 270000, 128, 4096                     # A: 2.2e9 bytes
+    far = dict(a_addr=A_ADDR, b_addr=B_ADDR, c_addr=C_ADDR)
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, M, N, K, **far)
+    assert st == 0 and p.family == 2 and p.variant == 0
+    for op in (g5.GEMM_OP_BF16_SILU, g5.GEMM_OP_BF16_NT, g5.GEMM_OP_BF16_TN, g5.GEMM_OP_BF16_AFFINE):
+        st, _ = g5.plan_query(op, M, N, K, **far)
+        assert st == g5.GEMM_ERR_UNSUPPORTED, op
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 1, 64, 64, batch=70000, **far)
+    assert st == 0 and p.family == 2                # more entries than the small-M grid takes
