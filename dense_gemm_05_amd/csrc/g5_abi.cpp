@@ -620,7 +620,11 @@ struct Workspace {
     Buffer rows;       // realigned copy of A
     Buffer rows_b;     // realigned copy of a transposed B
 };
-std::mutex g_ws_mutex;
+// Held from the first workspace lookup of a call until its last launch is
+// enqueued: a call on the same stream from another thread could otherwise
+// grow (synchronise, free, reallocate) a buffer between this call's lookup
+// and its launch.  Recursive so the lookups below can take it again.
+std::recursive_mutex g_ws_mutex;
 std::map<std::pair<int, void *>, Workspace> g_ws;
 
 // Make `b` at least `need` bytes (zeroed when `zero`); false on failure.
@@ -650,7 +654,7 @@ bool grow(Buffer &b, size_t need, bool zero, void *stream)
 
 bool get_workspace(int dev, void *stream, size_t cnt_bytes, size_t part_bytes, unsigned **cnt, float **part)
 {
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    std::lock_guard<std::recursive_mutex> lock(g_ws_mutex);
     Workspace &w = g_ws[std::make_pair(dev, stream)];
     if (!grow(w.cnt, cnt_bytes, true, stream) || !grow(w.part, part_bytes, false, stream)) return false;
     *cnt = (unsigned *)w.cnt.ptr;
@@ -660,7 +664,7 @@ bool get_workspace(int dev, void *stream, size_t cnt_bytes, size_t part_bytes, u
 
 uint16_t *get_row_buffer(int dev, void *stream, size_t bytes, bool second = false)
 {
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    std::lock_guard<std::recursive_mutex> lock(g_ws_mutex);
     Workspace &w = g_ws[std::make_pair(dev, stream)];
     Buffer &b = second ? w.rows_b : w.rows;
     if (!grow(b, bytes, false, stream)) return nullptr;
@@ -682,6 +686,10 @@ int run(const Problem &p, void *stream)
                      p.op, (long long)p.batch, (long long)p.M, (long long)p.N, (long long)p.K,
                      kConfigs[pl.config].name, pl.variant, (long long)pl.grid, pl.align_a, pl.align_b,
                      pl.align_c);
+    // Calls that use a workspace keep it locked until their launches are
+    // enqueued (see g_ws_mutex).
+    std::unique_lock<std::recursive_mutex> ws_lock(g_ws_mutex, std::defer_lock);
+    if (pl.realign_a || pl.realign_b || pl.ksplit > 1 || pl.config == CFG_DECODE_SPLIT) ws_lock.lock();
     GemmArgs a;
     a.A = (const void *)p.a;
     a.B = (const void *)p.b;

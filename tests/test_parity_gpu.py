@@ -558,3 +558,49 @@ def test_ksplit_shard_full_size(oracle_mod):
     rows = np.unique(np.concatenate([np.arange(0, 1024, 64), np.arange(127, 1024, 128), [1, 1000]]))
     ref = oracle_mod.gemm_bf16(np.ascontiguousarray(X[rows]), W)
     check_bf16(host_values(C)[rows], ref, 4096, "shard rows")
+
+
+def test_workspace_shared_by_threads_on_one_stream():
+    """Two host threads enqueue K-split calls on the same stream at once
+    while one of them keeps needing larger workspaces (each growth
+    synchronises the stream, frees and reallocates the buffer): every
+    result equals the same call made alone, bit for bit."""
+    import threading
+    shapes_a = [(256, 256, 4096)] * 12
+    shapes_b = [(128 * i, 256, 2048) for i in (1, 2, 3, 4, 2, 5, 6, 3, 7, 8, 4, 8)]
+    cases = {}
+    for (M, N, K) in set(shapes_a + shapes_b):
+        A, B = gi.small_case("bf16", M, N, K, seed=90, scale_b=0.125)
+        dA, dB = dev_bf16(A), dev_bf16(B)
+        cases[(M, N, K)] = (dA, dB, g5.gemm_bf16(dA, dB, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    for key in cases:
+        st, plan = g5.plan_query(g5.GEMM_OP_BF16, *key, c_type=1)
+        assert st == 0 and plan.ksplit > 1, key
+    outs = {0: [], 1: []}
+    errors = []
+    # a new stream (default priority) starts with no workspace, so the
+    # growing sizes of the second thread reallocate it during the run
+    shared = torch.cuda.Stream()
+    shared.wait_stream(torch.cuda.current_stream())
+
+    def worker(idx, shapes):
+        try:
+            with torch.cuda.stream(shared):
+                for key in shapes:
+                    dA, dB, _ = cases[key]
+                    outs[idx].append((key, g5.gemm_bf16(dA, dB, out_dtype=torch.float32)))
+        except Exception as e:          # reported below
+            errors.append(e)
+
+    ts = [threading.Thread(target=worker, args=(0, shapes_a)), threading.Thread(target=worker, args=(1, shapes_b))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    shared.synchronize()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for idx in (0, 1):
+        for key, C in outs[idx]:
+            assert torch.equal(C.view(torch.int32), cases[key][2].view(torch.int32)), (idx, key)
