@@ -252,9 +252,11 @@ int gemm_bf16_swiglu(int64_t M, int64_t N, int64_t K,
  * GEMM_ERR_INVALID_ARG when alpha or beta is not finite, bias is not 2-byte
  * aligned, or bias overlaps C; GEMM_ERR_UNSUPPORTED as for the fused
  * epilogues above (16-byte aligned rows of C, N % 8 == 0, B rows 16-byte
- * aligned) when a product is formed.  Small outputs split K over
+ * aligned) when a product is formed on the tiled kernels.  M <= 16 runs
+ * the small-M kernels of gemm_bf16, whose final store applies the same
+ * formula (there B may have any alignment).  Small outputs split K over
  * workgroups as gemm_bf16 does (the workgroup that completes a tile applies
- * the epilogue).
+ * the epilogue, once).
  */
 int gemm_bf16_affine(int64_t batch, int64_t M, int64_t N, int64_t K,
                      const uint16_t *A, int64_t lda, int64_t strideA,
