@@ -93,8 +93,9 @@ int epi_of(const Problem &p)
 {
     return p.op == GEMM_OP_BF16_SILU     ? EPI_SILU
            : p.op == GEMM_OP_BF16_SWIGLU ? EPI_SWIGLU
-           : p.op == GEMM_OP_BF16_AFFINE || p.op == GEMM_OP_BF16_NT_AFFINE ? EPI_AFFINE
-                                                                            : EPI_NONE;
+           : p.op == GEMM_OP_BF16_AFFINE || p.op == GEMM_OP_BF16_NT_AFFINE || p.op == GEMM_OP_BF16_TN_AFFINE
+               ? EPI_AFFINE
+               : EPI_NONE;
 }
 bool is_affine(const Problem &p) { return epi_of(p) == EPI_AFFINE; }
 // An affine call with no product to form (alpha == 0: A and B are not read).
@@ -105,7 +106,7 @@ bool b_trans(const Problem &p)
     return p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_FP8_NT || p.op == GEMM_OP_BF16_NT_AFFINE;
 }
 // A is given transposed, At [K, M].
-bool a_trans(const Problem &p) { return p.op == GEMM_OP_BF16_TN; }
+bool a_trans(const Problem &p) { return p.op == GEMM_OP_BF16_TN || p.op == GEMM_OP_BF16_TN_AFFINE; }
 // Rows and columns of the A operand as stored: [M, K] or At [K, M].
 int64_t a_rows(const Problem &p) { return a_trans(p) ? p.K : p.M; }
 int64_t a_cols(const Problem &p) { return a_trans(p) ? p.M : p.K; }
@@ -150,7 +151,7 @@ int validate(const Problem &p)
 {
     if (p.op != GEMM_OP_SGEMM && p.op != GEMM_OP_BF16 && p.op != GEMM_OP_BF16_SILU && p.op != GEMM_OP_BF16_SWIGLU &&
         p.op != GEMM_OP_BF16_NT && p.op != GEMM_OP_FP8_NT && p.op != GEMM_OP_BF16_AFFINE && p.op != GEMM_OP_BF16_TN &&
-        p.op != GEMM_OP_BF16_NT_AFFINE)
+        p.op != GEMM_OP_BF16_NT_AFFINE && p.op != GEMM_OP_BF16_TN_AFFINE)
         return GEMM_ERR_INVALID_ARG;
     if (p.batch < 0 || p.M < 0 || p.N < 0 || p.K < 0) return GEMM_ERR_INVALID_ARG;
     if ((p.op == GEMM_OP_BF16 || p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_FP8_NT || is_affine(p) ||
@@ -239,6 +240,7 @@ bool config_fits(const Problem &p, int id)
 {
     const ConfigInfo &c = kConfigs[id];
     if (is_affine(p) && c.family == GEMM_FAMILY_DECODE) {       // the small-M kernels apply it too
+        if (a_trans(p)) return false;
         if (b_trans(p)) return id == CFG_DECODE_NT && p.M <= 16 && p.batch <= 65535;
         return (id == CFG_DECODE_64 || id == CFG_DECODE_SPLIT) && p.M <= 16 && p.batch <= 65535;
     }
@@ -927,6 +929,19 @@ int gemm_bf16_affine(int64_t batch, int64_t M, int64_t N, int64_t K, const uint1
 {
     Problem p{GEMM_OP_BF16_AFFINE, batch, M, N, K, (uint64_t)A, (uint64_t)B, (uint64_t)C, lda, ldb, ldc,
               strideA, strideB, strideC, c_type};
+    p.alpha = alpha;
+    p.beta = beta;
+    p.bias = (uint64_t)bias;
+    return g5::run(p, stream);
+}
+
+int gemm_bf16_tn_affine(int64_t batch, int64_t M, int64_t N, int64_t K, const uint16_t *At, int64_t ldat,
+                        int64_t strideAt, const uint16_t *B, int64_t ldb, int64_t strideB, float alpha,
+                        const uint16_t *bias, float beta, void *C, int64_t ldc, int64_t strideC, int c_type,
+                        void *stream)
+{
+    Problem p{GEMM_OP_BF16_TN_AFFINE, batch, M, N, K, (uint64_t)At, (uint64_t)B, (uint64_t)C, ldat, ldb, ldc,
+              strideAt, strideB, strideC, c_type};
     p.alpha = alpha;
     p.beta = beta;
     p.bias = (uint64_t)bias;

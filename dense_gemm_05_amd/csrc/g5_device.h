@@ -484,7 +484,8 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     constexpr int EB = F8 ? 1 : 2;                            // bytes per operand element
     constexpr int KS = 64 / EB;                               // K per stage
     static_assert(!F8 || (BT && EPI == EPI_NONE), "fp8 operands: A and Bt, no fused epilogue");
-    static_assert(!AT || (!F8 && !BT && AV == 16 && EPI == EPI_NONE), "transposed A: bf16, B as [K, N]");
+    static_assert(!AT || (!F8 && !BT && AV == 16 && (EPI == EPI_NONE || EPI == EPI_AFFINE)),
+                  "transposed A: bf16, B as [K, N], plain or affine epilogue");
     static_assert(!AT || ((BM / 8) % 8 == 0 && (BM % 128 != 0 || (BM / 8) % 16 == 0)), "At slot rows: whole swizzle groups");
     constexpr int TM = BM / WGM, TN = BN / WGN;
     constexpr int FM = TM / 16, FN = TN / 16;

@@ -53,13 +53,29 @@ static hipError_t launch_affine_bt(int config_id, const GemmArgs &a, int variant
     }
 }
 
+// The affine epilogue with A given transposed (At [K, M]): variants 1-2.
+static hipError_t launch_affine_at(int config_id, const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
+{
+    const dim3 g((unsigned)grid), b8(512);
+    switch (config_id) {
+    case CFG_BF16_256x192: return launch_ring<256, 192, 2, 4, 4, 4, EPI_AFFINE, false, false, false, true>(a, variant, g, b8, s);
+    case CFG_BF16_256x256: return launch_ring<256, 256, 2, 4, 4, 4, EPI_AFFINE, false, false, false, true>(a, variant, g, b8, s);
+    case CFG_BF16_128x128:
+        if (a.ksplit > 1)
+            return launch_ring<128, 128, 4, 2, 4, 4, EPI_AFFINE, true, false, false, true>(a, variant, g, b8, s);
+        return launch_ring<128, 128, 4, 2, 4, 4, EPI_AFFINE, false, false, false, true>(a, variant, g, b8, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_fused(int config_id, int epi, const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
 {
     if (epi == EPI_SILU) return launch_fused_epi<EPI_SILU>(config_id, a, variant, grid, s);
     if (epi == EPI_SWIGLU) return launch_fused_epi<EPI_SWIGLU>(config_id, a, variant, grid, s);
     if (epi == EPI_AFFINE)
-        return a.b_trans ? launch_affine_bt(config_id, a, variant, grid, s)
-                         : launch_fused_epi<EPI_AFFINE>(config_id, a, variant, grid, s);
+        return a.b_trans   ? launch_affine_bt(config_id, a, variant, grid, s)
+               : a.a_trans ? launch_affine_at(config_id, a, variant, grid, s)
+                           : launch_fused_epi<EPI_AFFINE>(config_id, a, variant, grid, s);
     return hipErrorInvalidValue;
 }
 

@@ -15,7 +15,7 @@ from ._lib import GemmError, GemmPlan, lib
 __all__ = ["gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm_bf16_nt_batched",
            "gemm_bf16_tn", "gemm_bf16_tn_batched",
            "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_fp8_quantize_rows", "gemm_fp8_nt", "gemm_bf16_affine",
-           "gemm_bf16_nt_affine", "plan_query", "GemmError"]
+           "gemm_bf16_nt_affine", "gemm_bf16_tn_affine", "plan_query", "GemmError"]
 
 
 def _ld(t, inner):
@@ -338,14 +338,25 @@ def gemm_bf16_nt_affine(A, Bt, C, alpha=1.0, bias=None, beta=0.0):
     return _affine(A, Bt, C, alpha, bias, beta, True)
 
 
-def _affine(A, B, C, alpha, bias, beta, b_trans):
-    what = "gemm_bf16_nt_affine" if b_trans else "gemm_bf16_affine"
+def gemm_bf16_tn_affine(At, B, C, alpha=1.0, bias=None, beta=0.0):
+    """C := alpha * (At^T . B) + bias + beta * C in place
+    (gemm_bf16_tn_affine): At [K,M] (or [batch, K, M]), e.g. the activations
+    of a weight gradient accumulated with beta = 1; otherwise as
+    gemm_bf16_affine."""
+    return _affine(At, B, C, alpha, bias, beta, False, a_trans=True)
+
+
+def _affine(A, B, C, alpha, bias, beta, b_trans, a_trans=False):
+    what = "gemm_bf16_nt_affine" if b_trans else "gemm_bf16_tn_affine" if a_trans else "gemm_bf16_affine"
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
         raise TypeError(f"{what} takes bfloat16 operands")
     if A.dim() != B.dim() or A.dim() not in (2, 3):
         raise ValueError("A and B must both be 2-D or both be 3-D")
     A3, B3, C3 = (A, B, C) if A.dim() == 3 else (A.unsqueeze(0), B.unsqueeze(0), C.unsqueeze(0))
-    batch, M, K = A3.shape
+    if a_trans:
+        batch, K, M = A3.shape
+    else:
+        batch, M, K = A3.shape
     if b_trans:
         b2, N, K2 = B3.shape
     else:
@@ -357,8 +368,8 @@ def _affine(A, B, C, alpha, bias, beta, b_trans):
                              (N > 1 and bias.stride(0) != 1)):
         raise ValueError("bias must be a contiguous bfloat16 vector of N elements")
     code = _out_code(C.dtype)
-    fn = lib().gemm_bf16_nt_affine if b_trans else lib().gemm_bf16_affine
-    st = _launch(fn, dev, batch, M, N, K, A3.data_ptr(), _ld(A3, K), _bstride(A3),
+    fn = lib().gemm_bf16_nt_affine if b_trans else lib().gemm_bf16_tn_affine if a_trans else lib().gemm_bf16_affine
+    st = _launch(fn, dev, batch, M, N, K, A3.data_ptr(), _ld(A3, M if a_trans else K), _bstride(A3),
                  B3.data_ptr(), _ld(B3, K if b_trans else N), _bstride(B3), float(alpha),
                  None if bias is None else bias.data_ptr(), float(beta), C3.data_ptr(), _ld(C3, N), _bstride(C3), code)
     if st != 0:
@@ -369,11 +380,12 @@ def _affine(A, B, C, alpha, bias, beta, b_trans):
 def plan_query(op, M, N, K, batch=1, lda=None, ldb=None, ldc=None, a_addr=0x10000, b_addr=0x20000000,
                c_addr=0x40000000, sA=None, sB=None, sC=None, c_type=_lib.GEMM_OUT_BF16):
     """Host-only: the status and plan a call would produce (no GPU work)."""
-    lda = (M if op == _lib.GEMM_OP_BF16_TN else K) if lda is None else lda
+    tn = op in (_lib.GEMM_OP_BF16_TN, _lib.GEMM_OP_BF16_TN_AFFINE)
+    lda = (M if tn else K) if lda is None else lda
     nt = op in (_lib.GEMM_OP_BF16_NT, _lib.GEMM_OP_FP8_NT, _lib.GEMM_OP_BF16_NT_AFFINE)
     ldb = (2 * N if op == _lib.GEMM_OP_BF16_SWIGLU else K if nt else N) if ldb is None else ldb
     ldc = N if ldc is None else ldc
-    sA = (K if op == _lib.GEMM_OP_BF16_TN else M) * lda if sA is None else sA
+    sA = (K if tn else M) * lda if sA is None else sA
     sB = (N if nt else K) * ldb if sB is None else sB
     sC = M * ldc if sC is None else sC
     out = GemmPlan()

@@ -279,6 +279,18 @@ int gemm_bf16_nt_affine(int64_t batch, int64_t M, int64_t N, int64_t K,
                         void *C, int64_t ldc, int64_t strideC, int c_type,
                         void *stream);
 
+/* The same with A given transposed as in gemm_bf16_tn: At [K,M] row-major
+ * (ldat >= M), so that with beta = 1 the call accumulates a weight gradient,
+ * dW := dW + X^T . dY, in place (C in float keeps the accumulation in FP32).
+ * Every size runs on the tiled kernels; At rows are realigned as in
+ * gemm_bf16_tn. */
+int gemm_bf16_tn_affine(int64_t batch, int64_t M, int64_t N, int64_t K,
+                        const uint16_t *At, int64_t ldat, int64_t strideAt,
+                        const uint16_t *B, int64_t ldb, int64_t strideB,
+                        float alpha, const uint16_t *bias, float beta,
+                        void *C, int64_t ldc, int64_t strideC, int c_type,
+                        void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *gemm_status_string(int status);
 
@@ -332,7 +344,8 @@ typedef enum {
     GEMM_OP_BF16_AFFINE = 6, /* gemm_bf16_affine with alpha = 1 (alpha, beta and bias do not change the
                                 plan; alpha == 0 plans the element-wise pass of K == 0) */
     GEMM_OP_BF16_TN = 7,     /* gemm_bf16_tn, gemm_bf16_tn_batched (a = At, lda = ldat) */
-    GEMM_OP_BF16_NT_AFFINE = 8 /* gemm_bf16_nt_affine with alpha = 1 (b = Bt, ldb = ldbt) */
+    GEMM_OP_BF16_NT_AFFINE = 8, /* gemm_bf16_nt_affine with alpha = 1 (b = Bt, ldb = ldbt) */
+    GEMM_OP_BF16_TN_AFFINE = 9  /* gemm_bf16_tn_affine with alpha = 1 (a = At, lda = ldat) */
 } gemm_op;
 
 /* Validate the arguments of a call and report the plan it would launch,

@@ -537,3 +537,22 @@ def test_operands_over_2gib_plans(L):
         assert st == g5.GEMM_ERR_UNSUPPORTED, op
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 1, 64, 64, batch=70000, **far)
     assert st == 0 and p.family == 2                # more entries than the small-M grid takes
+
+
+def test_tn_affine_plans(L):
+    """The affine epilogue with A transposed runs on the transposed-A ring
+    kernels at every M (no small-M path), with K split for small outputs and
+    At rows realigned as for gemm_bf16_tn."""
+    op = g5.GEMM_OP_BF16_TN_AFFINE
+    st, p = g5.plan_query(op, 4096, 12288, 1024, c_type=1)
+    assert st == 0 and p.family == 2 and p.variant == 1
+    st, p = g5.plan_query(op, 8, 4096, 4096)
+    assert st == 0 and p.family == 2
+    st, p = g5.plan_query(op, 512, 512, 4096)
+    assert st == 0 and p.name == b"bf16_128x128" and p.ksplit > 1
+    st, p = g5.plan_query(op, 300, 392, 262)                       # M % 8 != 0: At rows realigned
+    assert st == 0 and p.variant == 2 and p.workspace_bytes >= 262 * 304 * 2
+    args = (1, 8, 8, 16, A_ADDR, 8, 128, B_ADDR, 8, 128)
+    assert L.gemm_bf16_tn_affine(*args, float("inf"), None, 1.0, C_ADDR, 8, 64, 0, None) == g5.GEMM_ERR_INVALID_ARG
+    assert L.gemm_bf16_tn_affine(1, 8, 8, 16, A_ADDR, 7, 128, B_ADDR, 8, 128, 1.0, None, 1.0, C_ADDR, 8, 64, 0,
+                                 None) == g5.GEMM_ERR_INVALID_ARG          # ldat < M

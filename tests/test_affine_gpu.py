@@ -319,3 +319,70 @@ def test_nt_affine_linear_layer_full_size(oracle_mod):
     rows = np.array([0, 255, 256, 700, 1023])
     _nt_check(oracle_mod, np.ascontiguousarray(X[rows]), Wt, bias, np.ascontiguousarray(res[rows]), 1.0, 1.0,
               host_values(C)[rows], False, "nt affine FFN rows")
+
+
+# ------------------------------------------------------------ A given transposed
+
+@pytest.mark.parametrize("cfg", [None, "bf16_256x192", "bf16_256x256", "bf16_128x128"])
+@pytest.mark.parametrize("M,N,K,pa", [(304, 392, 264, 8), (300, 200, 1000, 0)])
+def test_tn_affine_ragged(oracle_mod, monkeypatch, cfg, M, N, K, pa):
+    """At [K, M] with the affine epilogue on every transposed-A config; M = 300
+    (not a multiple of 8) goes through the padded copy of At."""
+    g = np.random.default_rng([gi.SEED_BASE + 5800, M, N, K, pa])
+    At = gi.to_bf16_bits(gi.normal(g, (K, M + pa)))
+    B = gi.to_bf16_bits(gi.normal(g, (K, N), 0.125))
+    bias = gi.to_bf16_bits(gi.normal(g, (N,)))
+    old32 = gi.normal(g, (M, N))
+    old16 = gi.to_bf16_bits(old32)
+    A = np.ascontiguousarray(At[:, :M].T)
+    if cfg:
+        monkeypatch.setenv("GEMM_FORCE_CONFIG", cfg)
+    for out_f32 in (False, True):
+        _say(f"tn affine {cfg} {M}x{N}x{K} out_f32={out_f32}")
+        C = dev_f32(old32) if out_f32 else dev_bf16(old16)
+        g5.gemm_bf16_tn_affine(dev_bf16(At)[:, :M], dev_bf16(B), C, alpha=-1.5, bias=dev_bf16(bias), beta=0.5)
+        old = old32 if out_f32 else old16
+        ref = oracle_mod.gemm_bf16_affine(A, B, -1.5, bias, 0.5, old)
+        old_vals = old.astype(np.float64) if out_f32 else gi.bf16_bits_to_f32(old).astype(np.float64)
+        check_affine(host_values(C), ref, oracle_mod.gemm_bf16(A, B), K, -1.5,
+                     gi.bf16_bits_to_f32(bias).astype(np.float64), 0.5, old_vals, out_f32, amax_bf16(A),
+                     amax_bf16(B), f"tn affine {cfg}")
+
+
+@pytest.mark.parametrize("S", [2, 3])
+def test_tn_affine_ksplit(oracle_mod, monkeypatch, S):
+    g = np.random.default_rng([gi.SEED_BASE + 5900, S])
+    At = gi.to_bf16_bits(gi.normal(g, (1024, 200)))
+    B = gi.to_bf16_bits(gi.normal(g, (1024, 264), 0.125))
+    old = gi.normal(g, (200, 264))
+    A = np.ascontiguousarray(At.T)
+    monkeypatch.setenv("GEMM_FORCE_CONFIG", "bf16_128x128")
+    monkeypatch.setenv("GEMM_FORCE_KSPLIT", str(S))
+    C = dev_f32(old)
+    g5.gemm_bf16_tn_affine(dev_bf16(At), dev_bf16(B), C, alpha=1.0, bias=None, beta=1.0)
+    ref = oracle_mod.gemm_bf16_affine(A, B, 1.0, None, 1.0, old)
+    check_affine(host_values(C), ref, oracle_mod.gemm_bf16(A, B), 1024, 1.0, np.zeros(264), 1.0,
+                 old.astype(np.float64), True, amax_bf16(A), amax_bf16(B), f"tn affine split {S}")
+
+
+def test_tn_affine_gradient_accumulation_full_size(oracle_mod):
+    """dW [4096, 12288] (float) += X^T . dY with X [1024, 4096], dY [1024, 12288]:
+    two accumulation steps from a seeded dW, rows from every row tile."""
+    _say("tn affine wgrad accumulation 4096x12288x1024")
+    X, dY = gi.wgrad_inputs()
+    g = np.random.default_rng([gi.SEED_BASE + 6000])
+    dW0 = gi.normal(g, (4096, 12288))
+    dX, dD = dev_bf16(X), dev_bf16(dY)
+    C = dev_f32(dW0)
+    g5.gemm_bf16_tn_affine(dX, dD, C, alpha=1.0, bias=None, beta=1.0)
+    g5.gemm_bf16_tn_affine(dX, dD, C, alpha=1.0, bias=None, beta=1.0)
+    rows = np.array([0, 255, 256, 2047, 4095])
+    Xs = np.ascontiguousarray(X[:, rows].T)
+    P = oracle_mod.gemm_bf16(Xs, dY)
+    ref = dW0[rows].astype(np.float64) + 2.0 * P
+    # two FP32 accumulations: each adds the FP32 bar of one product and
+    # 2^-20 of the magnitudes combined
+    bound = 2 * (1e-5 * 1024 * amax_bf16(X) * amax_bf16(dY)) + 2.0 ** -19 * (np.abs(ref) + 2 * np.abs(P))
+    got = host_values(C[torch.from_numpy(rows).cuda()])
+    err = np.abs(got - ref)
+    assert np.all(err <= bound), f"max err {err.max()} (bound {bound.min()}..{bound.max()})"
