@@ -34,7 +34,8 @@ GEMM_FAMILY = {0: "none", 1: "zero", 2: "bf16_mfma", 3: "f32_mfma", 4: "decode",
 # Every symbol declared by include/gemm05.h.
 EXPORTS = ("gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm_bf16_nt_batched",
            "gemm_bf16_tn", "gemm_bf16_tn_batched",
-           "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_fp8_quantize_rows", "gemm_fp8_nt", "gemm_bf16_affine", "gemm_bf16_nt_affine",
+           "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_bf16_silu_batched", "gemm_bf16_swiglu_batched",
+           "gemm_fp8_quantize_rows", "gemm_fp8_nt", "gemm_bf16_affine", "gemm_bf16_nt_affine",
            "gemm_bf16_tn_affine",
            "gemm_status_string",
            "gemm_plan_query", "gemm_model_local_bytes", "gemm_model_traffic_bytes", "gemm_model_quant_traffic",
@@ -93,6 +94,10 @@ def lib():
     L.gemm_bf16_nt_affine.restype = i32
     L.gemm_bf16_tn_affine.argtypes = L.gemm_bf16_affine.argtypes
     L.gemm_bf16_tn_affine.restype = i32
+    L.gemm_bf16_silu_batched.argtypes = [i64, i64, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64, p]
+    L.gemm_bf16_silu_batched.restype = i32
+    L.gemm_bf16_swiglu_batched.argtypes = L.gemm_bf16_silu_batched.argtypes
+    L.gemm_bf16_swiglu_batched.restype = i32
     L.gemm_bf16_silu.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
     L.gemm_bf16_silu.restype = i32
     L.gemm_bf16_swiglu.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]

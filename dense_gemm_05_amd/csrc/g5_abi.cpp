@@ -159,7 +159,7 @@ int validate(const Problem &p)
         p.c_type != GEMM_OUT_BF16 && p.c_type != GEMM_OUT_F32)
         return GEMM_ERR_INVALID_ARG;
     if (p.op == GEMM_OP_FP8_NT && (p.batch > 1 || (p.scale_a % 4) || (p.scale_b % 4))) return GEMM_ERR_INVALID_ARG;
-    if ((p.op == GEMM_OP_BF16_SILU || p.op == GEMM_OP_BF16_SWIGLU) && (p.c_type != GEMM_OUT_BF16 || p.batch > 1))
+    if ((p.op == GEMM_OP_BF16_SILU || p.op == GEMM_OP_BF16_SWIGLU) && p.c_type != GEMM_OUT_BF16)
         return GEMM_ERR_INVALID_ARG;
     if (is_affine(p) && (!std::isfinite(p.alpha) || !std::isfinite(p.beta) || (p.bias % 2)))
         return GEMM_ERR_INVALID_ARG;
@@ -903,6 +903,24 @@ int gemm_bf16_swiglu(int64_t M, int64_t N, int64_t K, const uint16_t *X, int64_t
 {
     const Problem p{GEMM_OP_BF16_SWIGLU, 1, M, N, K, (uint64_t)X, (uint64_t)Wgu, (uint64_t)Z, ldx, ldw, ldz, 0, 0,
                     0, GEMM_OUT_BF16};
+    return g5::run(p, stream);
+}
+
+int gemm_bf16_silu_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                           int64_t strideA, const uint16_t *B, int64_t ldb, int64_t strideB, uint16_t *C, int64_t ldc,
+                           int64_t strideC, void *stream)
+{
+    const Problem p{GEMM_OP_BF16_SILU, batch, M, N, K, (uint64_t)A, (uint64_t)B, (uint64_t)C, lda, ldb, ldc,
+                    strideA, strideB, strideC, GEMM_OUT_BF16};
+    return g5::run(p, stream);
+}
+
+int gemm_bf16_swiglu_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const uint16_t *X, int64_t ldx,
+                             int64_t strideX, const uint16_t *Wgu, int64_t ldw, int64_t strideW, uint16_t *Z,
+                             int64_t ldz, int64_t strideZ, void *stream)
+{
+    const Problem p{GEMM_OP_BF16_SWIGLU, batch, M, N, K, (uint64_t)X, (uint64_t)Wgu, (uint64_t)Z, ldx, ldw, ldz,
+                    strideX, strideW, strideZ, GEMM_OUT_BF16};
     return g5::run(p, stream);
 }
 

@@ -14,7 +14,8 @@ from ._lib import GemmError, GemmPlan, lib
 
 __all__ = ["gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm_bf16_nt_batched",
            "gemm_bf16_tn", "gemm_bf16_tn_batched",
-           "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_fp8_quantize_rows", "gemm_fp8_nt", "gemm_bf16_affine",
+           "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_bf16_silu_batched", "gemm_bf16_swiglu_batched",
+           "gemm_fp8_quantize_rows", "gemm_fp8_nt", "gemm_bf16_affine",
            "gemm_bf16_nt_affine", "gemm_bf16_tn_affine", "plan_query", "GemmError"]
 
 
@@ -336,6 +337,51 @@ def gemm_bf16_nt_affine(A, Bt, C, alpha=1.0, bias=None, beta=0.0):
     (gemm_bf16_nt_affine): Bt [N,K] (or [batch, N, K]) is a linear layer's
     [out, in] weight; otherwise as gemm_bf16_affine."""
     return _affine(A, Bt, C, alpha, bias, beta, True)
+
+
+def gemm_bf16_silu_batched(A, B, C=None):
+    """C[b] = bf16(SiLU(bf16(A[b] . B[b]))) for bfloat16 stacks [batch, M, K]
+    and [batch, K, N] (gemm_bf16_silu_batched); a batch stride of 0
+    broadcasts an operand."""
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("gemm_bf16_silu_batched takes bfloat16 operands")
+    batch, M, K = A.shape
+    b2, K2, N = B.shape
+    if batch != b2 or K != K2:
+        raise ValueError("shape mismatch")
+    dev = _check_dev(A, B)
+    if C is None:
+        C = torch.empty((batch, M, N), dtype=torch.bfloat16, device=dev)
+    if tuple(C.shape) != (batch, M, N) or C.dtype != torch.bfloat16:
+        raise ValueError("C must be bfloat16 [batch, M, N]")
+    st = _launch(lib().gemm_bf16_silu_batched, dev, batch, M, N, K, A.data_ptr(), _ld(A, K), _bstride(A),
+                 B.data_ptr(), _ld(B, N), _bstride(B), C.data_ptr(), _ld(C, N), _bstride(C))
+    if st != 0:
+        raise GemmError(st, "gemm_bf16_silu_batched")
+    return C
+
+
+def gemm_bf16_swiglu_batched(X, Wgu, Z=None):
+    """Z[b] = SwiGLU of X[b] with the merged gate|up weight Wgu[b] [K, 2N]
+    (gemm_bf16_swiglu_batched), e.g. the experts of a mixture-of-experts FFN;
+    a batch stride of 0 broadcasts an operand."""
+    if X.dtype != torch.bfloat16 or Wgu.dtype != torch.bfloat16:
+        raise TypeError("gemm_bf16_swiglu_batched takes bfloat16 operands")
+    batch, M, K = X.shape
+    b2, K2, N2 = Wgu.shape
+    if batch != b2 or K != K2 or N2 % 2:
+        raise ValueError("expected X [batch, M, K] and Wgu [batch, K, 2N]")
+    N = N2 // 2
+    dev = _check_dev(X, Wgu)
+    if Z is None:
+        Z = torch.empty((batch, M, N), dtype=torch.bfloat16, device=dev)
+    if tuple(Z.shape) != (batch, M, N) or Z.dtype != torch.bfloat16:
+        raise ValueError("Z must be bfloat16 [batch, M, N]")
+    st = _launch(lib().gemm_bf16_swiglu_batched, dev, batch, M, N, K, X.data_ptr(), _ld(X, K), _bstride(X),
+                 Wgu.data_ptr(), _ld(Wgu, N2), _bstride(Wgu), Z.data_ptr(), _ld(Z, N), _bstride(Z))
+    if st != 0:
+        raise GemmError(st, "gemm_bf16_swiglu_batched")
+    return Z
 
 
 def gemm_bf16_tn_affine(At, B, C, alpha=1.0, bias=None, beta=0.0):

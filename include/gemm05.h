@@ -231,6 +231,20 @@ int gemm_bf16_swiglu(int64_t M, int64_t N, int64_t K,
                      uint16_t *Z, int64_t ldz,
                      void *stream);
 
+/* Batched forms (each entry as the single call, strides in elements as in
+ * gemm_bf16_batched, 0 broadcasting an operand): e.g. the experts of a
+ * mixture-of-experts FFN, each with its own tokens and weights. */
+int gemm_bf16_silu_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                           const uint16_t *A, int64_t lda, int64_t strideA,
+                           const uint16_t *B, int64_t ldb, int64_t strideB,
+                           uint16_t *C, int64_t ldc, int64_t strideC,
+                           void *stream);
+int gemm_bf16_swiglu_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                             const uint16_t *X, int64_t ldx, int64_t strideX,
+                             const uint16_t *Wgu, int64_t ldw, int64_t strideW,
+                             uint16_t *Z, int64_t ldz, int64_t strideZ,
+                             void *stream);
+
 /* ---- affine epilogue -------------------------------------------------------
  *
  * C := alpha * (A.B) + bias + beta * C, the scaling and accumulation of the
@@ -337,8 +351,8 @@ typedef struct {
 typedef enum {
     GEMM_OP_SGEMM = 0,       /* gemm_sgemm */
     GEMM_OP_BF16 = 1,        /* gemm_bf16, gemm_bf16_batched */
-    GEMM_OP_BF16_SILU = 2,   /* gemm_bf16_silu (batch 1, c_type ignored) */
-    GEMM_OP_BF16_SWIGLU = 3, /* gemm_bf16_swiglu (batch 1, b = Wgu, c_type ignored) */
+    GEMM_OP_BF16_SILU = 2,   /* gemm_bf16_silu(_batched) (c_type ignored) */
+    GEMM_OP_BF16_SWIGLU = 3, /* gemm_bf16_swiglu(_batched) (b = Wgu, c_type ignored) */
     GEMM_OP_BF16_NT = 4,     /* gemm_bf16_nt, gemm_bf16_nt_batched (b = Bt, ldb = ldbt) */
     GEMM_OP_FP8_NT = 5,      /* gemm_fp8_nt (batch 1, b = Bt; scales do not change the plan) */
     GEMM_OP_BF16_AFFINE = 6, /* gemm_bf16_affine with alpha = 1 (alpha, beta and bias do not change the

@@ -281,8 +281,10 @@ def test_fused_arguments(L, op):
     opc = g5.GEMM_OP_BF16_SILU if op == "silu" else g5.GEMM_OP_BF16_SWIGLU
     st, p = g5.plan_query(opc, 4, 8, 0)
     assert st == 0 and p.family == 1                                         # K = 0: fill with zeros
-    st, _ = g5.plan_query(opc, 4, 8, 4, batch=2)
-    assert st == g5.GEMM_ERR_INVALID_ARG                                     # no batched fused call
+    st, p = g5.plan_query(opc, 4, 8, 4, batch=2)
+    assert st == 0 and p.family == 2                                         # batched (e.g. MoE experts)
+    st, _ = g5.plan_query(opc, 4, 8, 4, batch=2, sC=8 * 4 - 1)
+    assert st == g5.GEMM_ERR_INVALID_ARG                                     # output entries overlap
 
 
 def test_fused_plans(L):

@@ -161,3 +161,43 @@ def test_swiglu_matches_separate_products(monkeypatch):
     same = got == zf
     assert same.mean() > 0.999, f"only {same.mean():.5f} identical"
     assert np.all(np.abs(got - zf) <= 2.0 ** -6 * np.abs(zf) + 1e-30)
+
+
+@pytest.mark.parametrize("broadcast_x", [False, True])
+def test_swiglu_batched_experts(oracle_mod, broadcast_x):
+    """Batched SwiGLU: each entry (an expert of a mixture-of-experts FFN) has
+    its own merged weight, and its own tokens or (stride 0) the same tokens;
+    ragged tiles in M and N, a K tail."""
+    batch, M, N, K = 4, 150, 200, 264
+    _say(f"swiglu batched {batch}x{M}x{N}x{K} broadcast_x={broadcast_x}")
+    g = np.random.default_rng([gi.SEED_BASE + 4100, int(broadcast_x)])
+    X = gi.to_bf16_bits(gi.normal(g, (1 if broadcast_x else batch, M, K)))
+    Wgu = gi.to_bf16_bits(gi.normal(g, (batch, K, 2 * N), 0.125))
+    dX = dev_bf16(X)
+    if broadcast_x:
+        dX = dX.expand(batch, -1, -1)
+    Z = g5.gemm_bf16_swiglu_batched(dX, dev_bf16(Wgu))
+    got = host_values(Z)
+    for b in range(batch):
+        Xb = X[0 if broadcast_x else b]
+        Zr, G, U, t, u = _swiglu_ref(oracle_mod, Xb, Wgu[b])
+        check_swiglu(got[b], G, U, t, u, Zr, K, f"swiglu expert {b}")
+
+
+def test_silu_batched(oracle_mod, monkeypatch):
+    """Batched SiLU on every fused config, each entry checked, NaN padding
+    between entries untouched."""
+    batch, M, N, K = 3, 130, 136, 200
+    g = np.random.default_rng([gi.SEED_BASE + 4200])
+    A = gi.to_bf16_bits(gi.normal(g, (batch, M, K)))
+    B = gi.to_bf16_bits(gi.normal(g, (batch, K, N), 0.125))
+    for cfg in ("bf16_256x192", "bf16_256x256", "bf16_128x128"):
+        _say(f"silu batched forced {cfg}")
+        monkeypatch.setenv("GEMM_FORCE_CONFIG", cfg)
+        Cfull = torch.full((batch, M + 2, N), float("nan"), device="cuda", dtype=torch.bfloat16)
+        g5.gemm_bf16_silu_batched(dev_bf16(A), dev_bf16(B), Cfull[:, :M])
+        host = host_values(Cfull)
+        for b in range(batch):
+            check_silu(host[b, :M], oracle_mod.gemm_bf16(A[b], B[b]), oracle_mod.gemm_bf16_silu(A[b], B[b]), K,
+                       f"silu {cfg} entry {b}")
+        assert np.all(np.isnan(host[:, M:])), "rows between entries were written"
