@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "sgemm", "batched", "ragged", "swiglu", "shard", "fp8", "scores_nt", "decode_nt", "affine", "wgrad_tn", "copy"])
+    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "sgemm", "batched", "ragged", "swiglu", "shard", "fp8", "scores_nt", "decode_nt", "affine", "linear_nt", "wgrad_tn", "copy"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--prewarm-seconds", type=float, default=1.0,
@@ -400,6 +400,32 @@ def main():
         workloads.append({"name": "ffn_bias_residual_bf16_1024x12288x4096", "us": round(ms * 1e3, 3),
                           "tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                           "plain_projection_us": round(ms_plain * 1e3, 3), "rotations": R})
+        del dX, dW, db, dC
+
+    # ------------------------------------------------------------ linear layer: weight [out, in] and bias (NT)
+    if args.only in ("all", "linear_nt"):
+        # y = X . W^T + b with W stored [12288, 4096] as a linear layer keeps
+        # it, bf16 out, next to the same product without the bias.
+        M, N, K = 1024, 12288, 4096
+        X, W = gi.ffn_inputs()
+        Wt = np.ascontiguousarray(W.T)
+        g = np.random.default_rng([gi.SEED_BASE + gi.W_FFN, 7])
+        bias = gi.to_bf16_bits(gi.normal(g, (N,)))
+        R = rotations(2 * (M * K + K * N + M * N))
+        dX = [to_dev_bf16(X) for _ in range(R)]
+        dW = [to_dev_bf16(Wt) for _ in range(R)]
+        db = [to_dev_bf16(bias) for _ in range(R)]
+        dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        fns = [(lambda i=i: g5.gemm_bf16_nt_affine(dX[i], dW[i], dC[i], bias=db[i])) for i in range(R)]
+        plain = [(lambda i=i: g5.gemm_bf16_nt(dX[i], dW[i], dC[i])) for i in range(R)]
+        ms = timed(fns, 50, 10)
+        ms_plain = timed(plain, 50, 10)
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        log(f"linear layer X.W^T + b (W [12288,4096]): {ms * 1e3:.2f} us ({tf:.1f} TFLOPS); "
+            f"without bias {ms_plain * 1e3:.2f} us")
+        workloads.append({"name": "linear_nt_bias_bf16_1024x12288x4096", "us": round(ms * 1e3, 3),
+                          "tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                          "without_bias_us": round(ms_plain * 1e3, 3), "rotations": R})
         del dX, dW, db, dC
 
     # ------------------------------------------------------------ weight gradient from row-major X (TN)
