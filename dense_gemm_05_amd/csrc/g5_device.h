@@ -195,6 +195,7 @@ __device__ __forceinline__ void buffer_load_lds16(const void *base, uint32_t vof
 // accounts for its copies itself with explicit vmcnt waits.  M0 carries the
 // LDS destination; one wait state separates its write from the load.
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ i32x4_t make_rsrc(const void *base, uint32_t num_records = 0x7fffffffu)
 {
     const uint64_t b = (uint64_t)base;
@@ -469,10 +470,12 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
 //    fragments.  Needs 16-byte aligned rows of At and M % 8 == 0 or rows
 //    padded to a multiple of 8 (the masked copy reads whole 16-byte chunks).
 //  * F8: A and Bt hold E4M3FN codes (with BT): the same 64-byte slot rows
-//    then carry 64 values of K per stage, each 16-byte fragment feeds two
-//    v_mfma_f32_16x16x32_fp8_fp8 (the first takes bytes 0-7 of every lane,
-//    the second bytes 8-15: one permutation of K, the same for both
-//    operands), and the FP32 sums are multiplied by p.scale_a[row] and
+//    then carry 64 values of K per stage.  With an even stage count the
+//    stages go in pairs through the double-rate fp8 instruction (below);
+//    otherwise each 16-byte fragment feeds two v_mfma_f32_16x16x32_fp8_fp8
+//    (the first takes bytes 0-7 of every lane, the second bytes 8-15: one
+//    permutation of K, the same for both operands).  The FP32 sums are
+//    multiplied by p.scale_a[row] and
 //    p.scale_b[column] before the epilogue ("Operator & Runtime" §5.4.3,
 //    Example 5-7: dequantization by the row's factor).
 template <int BM, int BN, int WGM, int WGN, int NSA, int NSB, int AV, bool MASKED, int EPI = EPI_NONE,
@@ -725,12 +728,54 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
             mfma_range(fc, NMFMA - TAIL, TAIL);
             __builtin_amdgcn_sched_barrier(0);
         };
-        int kt = 0;
-        for (; kt + 1 < KT; kt += 2) {
-            step(kt, f0, f1);
-            step(kt + 1, f1, f0);
+        // F8 with an even stage count (not at 256x256, whose registers do
+        // not hold both loops): stages in pairs.  The 16-byte fragments of
+        // stages 2j and 2j+1 make each lane's 32 bytes of K for one
+        // double-rate MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 on both
+        // sides, unit block scales), the same permutation of K for both
+        // operands; even stages only copy, wait and read fragments.
+        constexpr bool F8_PAIRS = F8 && !(BM == 256 && BN == 256);
+        bool paired = false;
+        if constexpr (F8_PAIRS) {
+            if (KT % 2 == 0) {
+                paired = true;
+                auto mfma_pair = [&](const Frags &lo, const Frags &hi) {
+#pragma unroll
+                    for (int t = 0; t < NMFMA; ++t) {
+                        const int fn = t / FM, fm = t % FM;
+                        const i32x4_t al = __builtin_bit_cast(i32x4_t, lo.a[fm]);
+                        const i32x4_t ah = __builtin_bit_cast(i32x4_t, hi.a[fm]);
+                        const i32x4_t bl = __builtin_bit_cast(i32x4_t, lo.b[fn]);
+                        const i32x4_t bh = __builtin_bit_cast(i32x4_t, hi.b[fn]);
+                        const i32x8_t a8 = __builtin_shufflevector(al, ah, 0, 1, 2, 3, 4, 5, 6, 7);
+                        const i32x8_t b8 = __builtin_shufflevector(bl, bh, 0, 1, 2, 3, 4, 5, 6, 7);
+                        acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, acc[fn][fm], 0, 0, 0,
+                                                                                       127, 0, 127);
+                    }
+                };
+                for (int kt = 0; kt < KT; kt += 2) {
+                    issue_clamped(kt + (a_wave ? NSA : NSB) - 1);
+                    stage_barrier();
+                    read_frags(f1, kt + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    issue_clamped(kt + (a_wave ? NSA : NSB));
+                    __builtin_amdgcn_sched_barrier(0);
+                    mfma_pair(f0, f1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    stage_barrier();
+                    read_frags(f0, kt + 2);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
         }
-        if (kt < KT) step(kt, f0, f1);
+        if (!paired) {
+            int kt = 0;
+            for (; kt + 1 < KT; kt += 2) {
+                step(kt, f0, f1);
+                step(kt + 1, f1, f0);
+            }
+            if (kt < KT) step(kt, f0, f1);
+        }
     }
     if (MASKED && K % KS != 0) {
         // K remainder: every copy in flight lands first, then the last stage
