@@ -245,6 +245,7 @@ bool config_fits(const Problem &p, int id)
         return (id == CFG_DECODE_64 || id == CFG_DECODE_SPLIT) && p.M <= 16 && p.batch <= 65535;
     }
     if (epi_of(p) != EPI_NONE) return has_epilogues(id);
+    if (p.op == GEMM_OP_FP8_NT && id == CFG_DECODE_NT) return p.M <= 16 && p.batch <= 65535;   // k_decode_nt_f8
     if (p.op == GEMM_OP_FP8_NT) return has_epilogues(id);         // fp8 ring kernels: 256x192, 256x256, 128x128
     if (a_trans(p)) return has_epilogues(id);                       // transposed-A ring kernels: the same three
     if (b_trans(p)) return c.family == GEMM_FAMILY_BF16_MFMA;   // the ring kernels of every bf16 tile config
@@ -387,8 +388,8 @@ int select_plan(const Problem &p, Plan &pl)
         // staged at once (one load latency per tile instead of one per slab;
         // 256^3 measured 9.4 us with the double-buffered 64x64 kernel).
         pl.config = CFG_F32_32x32_WK;
-    } else if ((p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_BF16_NT_AFFINE) && p.M <= 16 && p.batch <= 65535 &&
-               pl.align_b >= 16) {
+    } else if ((p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_BF16_NT_AFFINE || p.op == GEMM_OP_FP8_NT) && p.M <= 16 &&
+               p.batch <= 65535 && pl.align_b >= 16) {
         // Small M with B transposed: a GEMV over the contiguous rows of Bt.
         pl.config = CFG_DECODE_NT;
     } else if ((p.op == GEMM_OP_BF16 || p.op == GEMM_OP_BF16_AFFINE) && p.M <= 16 && p.batch <= 65535) {

@@ -112,4 +112,111 @@ hipError_t launch_ring_fp8(int config_id, const GemmArgs &a, int variant, int64_
     }
 }
 
+// Small M on E4M3FN operands: C[M, N] = (X[M, K] . Bt[N, K]^T) scaled by
+// the factor of each row of X and of each row of Bt, for M <= 16.  As the
+// bf16 transposed-B GEMV: a workgroup owns 16 x RB rows of Bt, its NW waves
+// split K into contiguous ranges of 64-deep steps, and each lane loads 16
+// bytes (16 K values) of a row per step, which feed two
+// v_mfma_f32_16x16x32_fp8_fp8 (bytes 0-7, then 8-15: the same permutation
+// of K for both operands).  A K remainder (K % 64) is a final step loaded
+// element by element with zero fill.  The waves' partial sums are added in
+// LDS in wave order (so a row's result does not depend on M), then scaled
+// and rounded once.  Requires 16-byte aligned rows of Bt.
+template <int NW, int RB>
+__global__ void __launch_bounds__(NW * 64) k_decode_nt_f8(GemmArgs p)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, li = lane & 15;
+    const int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * RB;
+    const uint8_t *X = (const uint8_t *)p.A;
+    const uint8_t *Bt = (const uint8_t *)p.B;
+    const bool m_ok = li < M;
+    bool n_ok[RB];
+    const uint8_t *brow[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        n_ok[r] = n0 + 16 * r + li < N;
+        brow[r] = Bt + (n_ok[r] ? n0 + 16 * r + li : 0) * ldb;
+    }
+    const uint8_t *xrow = X + (m_ok ? li : 0) * lda;
+
+    const int64_t whole = K / 64;                          // whole 64-deep steps
+    const int64_t s_begin = whole * wave / NW, s_end = whole * (wave + 1) / NW;
+    f32x4 acc[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto load_b = [&](int r, int64_t st) -> u32x4 {
+        return n_ok[r] ? __builtin_nontemporal_load((const u32x4 *)(brow[r] + st * 64 + g * 16))
+                       : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto load_x = [&](int64_t st) -> u32x4 { return load_chunk16_u8(xrow, st * 64 + g * 16, K, m_ok, p.align_a); };
+    auto mma = [&](int r, u32x4 b, u32x4 x) {
+        const i64x2 b2 = __builtin_bit_cast(i64x2, b), x2 = __builtin_bit_cast(i64x2, x);
+        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(b2[0], x2[0], acc[r], 0, 0, 0);
+        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(b2[1], x2[1], acc[r], 0, 0, 0);
+    };
+    // D steps of Bt in flight ahead of the matrix core.
+    constexpr int D = RB == 1 ? 4 : 2;
+    int64_t st = s_begin;
+    for (; st + D <= s_end; st += D) {
+        u32x4 b[D][RB], x[D];
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+#pragma unroll
+            for (int r = 0; r < RB; ++r) b[j][r] = load_b(r, st + j);
+#pragma unroll
+        for (int j = 0; j < D; ++j) x[j] = load_x(st + j);
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+#pragma unroll
+            for (int r = 0; r < RB; ++r) mma(r, b[j][r], x[j]);
+    }
+    for (; st < s_end; ++st) {
+        const u32x4 x = load_x(st);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) mma(r, load_b(r, st), x);
+    }
+    if (wave == NW - 1 && K % 64 != 0) {
+        const u32x4 x = load_x(whole);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) mma(r, load_chunk16_u8(brow[r], whole * 64 + g * 16, K, n_ok[r], p.align_b), x);
+    }
+
+    // acc[r][q] of lane (g, li) is the partial sum for column
+    // n0 + 16 r + 4 g + q, row li.
+    __shared__ f32x4 red[NW][RB][64];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) red[wave][r][lane] = acc[r];
+    __syncthreads();
+    if (tid < 64 * RB) {
+        const int r = tid >> 6, t = tid & 63;
+        f32x4 sum = red[0][r][t];
+#pragma unroll
+        for (int w2 = 1; w2 < NW; ++w2) sum += red[w2][r][t];
+        const int m = t & 15, gg = t >> 4;
+        if (m < M) {
+            const float sa = p.scale_a ? p.scale_a[m] : 1.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = n0 + 16 * r + 4 * gg + q;
+                if (n >= N) continue;
+                const float sb = p.scale_b ? p.scale_b[n] : 1.0f;
+                const float v = sum[q] * sa * sb;
+                if (p.out_f32) ((float *)p.C)[m * p.ldc + n] = v;
+                else ((uint16_t *)p.C)[m * p.ldc + n] = (uint16_t)bf16_rne(v);
+            }
+        }
+    }
+}
+
+hipError_t launch_decode_nt_f8(const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
+{
+    if (variant == 2)
+        hipLaunchKernelGGL((k_decode_nt_f8<8, 3>), dim3((unsigned)grid), dim3(8 * 64), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_decode_nt_f8<8, 1>), dim3((unsigned)grid), dim3(8 * 64), 0, s, a);
+    return hipGetLastError();
+}
+
 }  // namespace g5

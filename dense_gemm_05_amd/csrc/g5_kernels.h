@@ -28,6 +28,10 @@ hipError_t launch_ring_at(int config_id, const GemmArgs &a, int variant, int64_t
 // the configs 256x192, 256x256 and 128x128, the last also with K split.
 hipError_t launch_ring_fp8(int config_id, const GemmArgs &a, int variant, int64_t grid, hipStream_t s);
 
+// Small M (<= 16) on E4M3FN operands with B given transposed: variant 1
+// one 16-row block of Bt per workgroup, 2 three (grid = blocks of Bt rows).
+hipError_t launch_decode_nt_f8(const GemmArgs &a, int variant, int64_t grid, hipStream_t s);
+
 // Per-row E4M3FN quantization of `rows` bf16 rows of `cols` elements (row
 // strides ldx, ldq; align_x, align_q the byte alignments of the row starts)
 // into codes Q and dequantization factors scale[rows].

@@ -1008,6 +1008,7 @@ hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, int 
             hipLaunchKernelGGL((k_decode<16, false>), dim3((unsigned)grid, (unsigned)a.batch), dim3(16 * 64), 0, s, a);
         return hipGetLastError();
     case CFG_DECODE_NT:
+        if (a.fp8) return launch_decode_nt_f8(a, variant, grid, s);
         // variant 1: one 16-row block per workgroup (M = 1); 2: three, which
         // share each X fragment (for M = 16 the fragments would otherwise
         // cost as much traffic as Bt: 29.2 against 23.9 us at N = 12288)

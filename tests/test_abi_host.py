@@ -393,8 +393,8 @@ def test_tn_arguments_and_plans(L, monkeypatch):
 
 def test_fp8_arguments_and_plans(L):
     """FP8: factors 4-byte aligned and not overlapping C; Bt rows 16-byte
-    aligned and A rows 4-byte aligned (the ring kernels only); 64 K values
-    per stage; quantization arguments."""
+    aligned and, on the ring kernels (M > 16), A rows 4-byte aligned; 64 K
+    values per stage; quantization arguments."""
     def f8(M, N, K, lda=None, ldb=None, sa=0, sb=0, c=C_ADDR):
         return L.gemm_fp8_nt(M, N, K, A_ADDR, K if lda is None else lda, sa, B_ADDR, K if ldb is None else ldb, sb,
                              c, N, 0, None)
@@ -402,7 +402,12 @@ def test_fp8_arguments_and_plans(L):
     assert f8(4, 8, 16, sa=C_ADDR + 2) == g5.GEMM_ERR_INVALID_ARG             # misaligned factor vector
     assert f8(4, 8, 16, sb=C_ADDR + 8) == g5.GEMM_ERR_INVALID_ARG             # factors inside C
     assert f8(4, 8, 20) == g5.GEMM_ERR_UNSUPPORTED                            # Bt rows 4-byte aligned
-    assert f8(4, 8, 20, lda=22, ldb=32) == g5.GEMM_ERR_UNSUPPORTED            # A rows 2-byte aligned
+    assert f8(20, 8, 20, lda=22, ldb=32) == g5.GEMM_ERR_UNSUPPORTED           # A rows 2-byte aligned (tiled)
+    # M <= 16 with 16-byte Bt rows: the FP8 GEMV over Bt rows, any A alignment
+    st, p = g5.plan_query(g5.GEMM_OP_FP8_NT, 4, 8, 20, lda=22, ldb=32)
+    assert st == 0 and p.name == b"decode_nt"
+    st, p = g5.plan_query(g5.GEMM_OP_FP8_NT, 1, 12288, 4096)
+    assert st == 0 and p.name == b"decode_nt" and p.variant == 1 and p.grid == 768
     assert f8(0, 8, 16) == g5.GEMM_OK
     st, p = g5.plan_query(g5.GEMM_OP_FP8_NT, 1024, 12288, 4096)
     assert st == 0 and p.name == b"bf16_256x192" and p.variant == 1 and p.even == 1

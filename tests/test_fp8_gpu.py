@@ -164,3 +164,46 @@ def test_fp8_ffn_end_to_end(oracle_mod):
     ref = oracle_mod.gemm_fp8_nt(np.ascontiguousarray(rX[rows]), rsX[rows], rW, rsW)
     check_fp8(host_values(C)[rows], ref, 4096, _amax(oracle_mod, rX, rsX), _amax(oracle_mod, rW, rsW), "bf16",
               "fp8 FFN rows")
+
+
+@pytest.mark.parametrize("M,N,K,pb,scales", [(1, 12288, 4096, 0, True), (4, 1000, 4100, 12, True),
+                                             (16, 392, 256, 0, False), (7, 200, 72, 8, True), (3, 40, 8, 8, True)])
+def test_fp8_nt_small_m(oracle_mod, M, N, K, pb, scales):
+    """M <= 16 with 16-byte aligned Bt rows: the FP8 GEMV over the rows of Bt
+    (decode_nt); ragged N, K tails (K % 64 != 0), with and without factors,
+    both outputs, NaN padding of C untouched."""
+    _say(f"fp8 small M {M}x{N}x{K} pb {pb} scales {scales}")
+    A, Bt, sa, sb = _fp8_case(M, N, K, 3, 0, pb, scales)
+    st, plan = g5.plan_query(g5.GEMM_OP_FP8_NT, M, N, K, ldb=K + pb)
+    assert st == 0 and plan.name == b"decode_nt"
+    ref = oracle_mod.gemm_fp8_nt(A, sa, np.ascontiguousarray(Bt[:, :K]), sb)
+    dA, dB = dev_u8(A), dev_u8(Bt)
+    dsa = None if sa is None else torch.from_numpy(sa).cuda()
+    dsb = None if sb is None else torch.from_numpy(sb).cuda()
+    am, bm = _amax(oracle_mod, A, sa), _amax(oracle_mod, Bt[:, :K], sb)
+    for out, od in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+        Cfull = torch.full((M, N + 4), float("nan"), device="cuda", dtype=od)
+        g5.gemm_fp8_nt(dA, dsa, dB[:, :K], dsb, Cfull[:, :N])
+        host = host_values(Cfull)
+        check_fp8(host[:, :N], ref, K, am, bm, out, f"fp8 small M {out}")
+        assert np.all(np.isnan(host[:, N:])), "ldc padding was written"
+
+
+def test_fp8_small_m_exact_and_row_invariant(oracle_mod):
+    """Small-integer codes with power-of-two factors through the small-M path
+    give the oracle's bits; the rows of an M = 1 and an M = 5 call equal the
+    same rows of an M = 16 call (the K partition does not depend on M)."""
+    g = np.random.default_rng(6)
+    N, K = 392, 1000
+    vals = np.arange(-6, 7, dtype=np.float64)
+    A = oracle_mod.e4m3_encode(g.choice(vals, (16, K)))
+    Bt = oracle_mod.e4m3_encode(g.choice(vals, (N, K + 8)))
+    sa = (2.0 ** g.integers(-3, 3, 16)).astype(np.float32)
+    sb = (2.0 ** g.integers(-3, 3, N)).astype(np.float32)
+    dA, dB = dev_u8(A), dev_u8(Bt)[:, :K]
+    dsa, dsb = torch.from_numpy(sa).cuda(), torch.from_numpy(sb).cuda()
+    c16 = g5.gemm_fp8_nt(dA, dsa, dB, dsb, out_dtype=torch.float32)
+    assert np.array_equal(host_values(c16), oracle_mod.gemm_fp8_nt(A, sa, np.ascontiguousarray(Bt[:, :K]), sb))
+    for M in (1, 5):
+        cm = g5.gemm_fp8_nt(dA[:M], dsa[:M], dB, dsb, out_dtype=torch.float32)
+        assert torch.equal(cm.view(torch.int32), c16[:M].view(torch.int32)), f"M={M}"
