@@ -356,7 +356,23 @@ def main():
                           "frac_peak": round(tf / PEAK_FP8_TFLOPS, 4), "peak": PEAK_FP8_TFLOPS,
                           "quantize_x_us": round(ms_q * 1e3, 3), "quantize_and_gemm_us": round(ms_b * 1e3, 3),
                           "rotations": R})
-        del dX, qW, qX, dC
+        del dX, qX, dC
+        # decode with the FP8 weight: M rows of X quantized, the GEMV over Wt's codes
+        for Md in (1, 16):
+            Xd, _ = gi.decode_inputs(Md, K, N)
+            alg = N * K + Md * K + 4 * Md + 4 * N + 2 * Md * N        # codes, factors, bf16 C
+            Rd = rotations(alg)
+            qW2 = [qW[i % R] for i in range(Rd)]
+            qXd = [g5.gemm_fp8_quantize_rows(to_dev_bf16(Xd)) for _ in range(Rd)]
+            dCd = [torch.empty((Md, N), dtype=torch.bfloat16, device=dev) for _ in range(Rd)]
+            fns = [(lambda i=i: g5.gemm_fp8_nt(qXd[i][0], qXd[i][1], qW2[i][0], qW2[i][1], dCd[i])) for i in range(Rd)]
+            ms_d = timed(fns, 200, 10)
+            gbps = alg / (ms_d * 1e-3) / 1e9
+            log(f"fp8 decode M={Md}: {ms_d * 1e3:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM)")
+            workloads.append({"name": f"fp8_decode_m{Md}_12288x4096", "us": round(ms_d * 1e3, 3), "GBps": round(gbps, 1),
+                              "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "alg_bytes": alg, "rotations": Rd})
+            del qXd, dCd, qW2
+        del qW
 
     # ------------------------------------------------------------ attention scores from row-major K
     if args.only in ("all", "scores_nt"):
