@@ -15,10 +15,11 @@ namespace g5 {
 // thread over its 16-byte chunks, then across the wave by butterfly
 // exchanges, then across the 4 waves in LDS: the tree reduction of the
 // reduce page, "3.1 Tối ưu toán tử CUDA Reduce").  Pass 2 writes the codes:
-// inv = 448 / amax and y = x * inv in binary32, y clamped to [-448, 448]
-// (NaN passes), then the hardware conversion, which rounds to the nearest
-// E4M3FN value, ties to even.  The row's dequantization factor is
-// amax / 448; a row of zeros gets codes 0 and factor 0.  Rows of up to
+// y = (x * 448) / amax in binary32 (one correctly rounded division), then
+// the hardware conversion, which rounds to the nearest E4M3FN value, ties
+// to even -- the code nearest to the exact quotient of Example 5-7 (see
+// quot below).  The row's dequantization factor is amax / 448; a row of
+// zeros gets zero codes and factor 0.  Rows of up to
 // NCH * 2048 elements stay in registers between the passes; longer rows
 // are read again in pass 2.
 template <int NCH>
@@ -53,15 +54,24 @@ __global__ void __launch_bounds__(256) k_quant_rows_e4m3(const uint16_t *X, int6
     if (lane == 0) red[wave] = m;
     __syncthreads();
     const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
     if (tid == 0) scale[r] = amax / 448.0f;
+    // y = x * 448 / amax with one rounding: x * 448 is exact in binary32 (a
+    // bf16 significand times 7 * 64), and the division is correctly rounded.
+    // A quotient that is exactly the midpoint of two E4M3FN values (at most
+    // 5 significant bits) is then exact, and any other lies at least
+    // ~2^-13 of its size away from every midpoint, far beyond the 2^-24 of
+    // the rounding, so the conversion below (round to nearest even) picks
+    // the code nearest to the exact quotient.  |x| <= amax keeps |y| <= 448
+    // (the clamp only guards the conversion, which turns larger values into
+    // NaN).  A row of zeros gives signed zeros.
     auto clamp448 = [](float y) { return y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y); };
+    auto quot = [&](float x) { return amax > 0.0f ? clamp448(__fdiv_rn(x * 448.0f, amax)) : x * 0.0f; };
     auto emit = [&](int64_t c, const u32x4 &cv) {
         uint32_t w[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const float y0 = clamp448(bf16_lo(cv[2 * h]) * inv), y1 = clamp448(bf16_hi(cv[2 * h]) * inv);
-            const float y2 = clamp448(bf16_lo(cv[2 * h + 1]) * inv), y3 = clamp448(bf16_hi(cv[2 * h + 1]) * inv);
+            const float y0 = quot(bf16_lo(cv[2 * h])), y1 = quot(bf16_hi(cv[2 * h]));
+            const float y2 = quot(bf16_lo(cv[2 * h + 1])), y3 = quot(bf16_hi(cv[2 * h + 1]));
             int packed = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
             packed = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, packed, true);
             w[h] = (uint32_t)packed;

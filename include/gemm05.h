@@ -165,10 +165,12 @@ int gemm_bf16_tn_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
 /* Per-row quantization of bf16 rows X [rows, cols] (row stride ldx) into
  * E4M3FN codes Q (row stride ldq, bytes) and dequantization factors
  * scale[rows] (float, 4-byte aligned): with amax the row's largest
- * magnitude, inv = 448 / amax and y = x * inv in binary32, y clamped to
- * [-448, 448], the code is the nearest E4M3FN value to y (ties to the even
- * mantissa) and scale = amax / 448.  A row of zeros gives codes 0 and
- * factor 0.  Inputs are expected finite (a NaN element becomes a NaN code).
+ * magnitude, the code of x is the E4M3FN value nearest to the exact
+ * quotient x * 448 / amax (ties to the even mantissa; Example 5-7), reached
+ * with one correctly rounded binary32 division of x * 448 by amax, and
+ * scale = amax / 448 rounded to binary32.  A row of zeros gives zero codes
+ * (signed) and factor 0.  Inputs are expected finite (a NaN element becomes
+ * a NaN code).
  * GEMM_ERR_INVALID_ARG: negative sizes, ldx or ldq < cols, NULL or
  * unaligned pointers, or overlapping X, Q and scale. */
 int gemm_fp8_quantize_rows(int64_t rows, int64_t cols,

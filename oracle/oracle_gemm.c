@@ -318,33 +318,63 @@ void oracle_e4m3_encode_array(int64_t n, const double *x, uint8_t *out)
     for (int64_t i = 0; i < n; ++i) out[i] = e4m3_encode(x[i]);
 }
 
-static float widen_bf16_f(uint16_t h)
-{
-    uint32_t u = (uint32_t)h << 16;
-    float f;
-    memcpy(&f, &u, sizeof f);
-    return f;
-}
-
 /* Per-row E4M3FN quantization of bf16 rows X [rows, cols] into codes Q
- * (row stride ldq) and dequantization factors scale[rows]. */
+ * (row stride ldq) and dequantization factors scale[rows], as page
+ * "Operator & Runtime" defines it (§5.4.3, Example 5-7): the row's largest
+ * magnitude amax maps to the format's largest finite value 448, so an
+ * element x becomes the E4M3FN value nearest to the exact quotient
+ * x * 448 / amax (ties to the even mantissa), and the factor that undoes it
+ * is amax / 448.
+ *
+ * The code is decided exactly, with no rounded quotient: |x| * 448 and
+ * v * amax, for v an E4M3FN value or the midpoint of two neighbours, are
+ * products of at most 8 and 5 significant bits, exact in binary64, so
+ * "x * 448 / amax < v" is decided by comparing |x| * 448 with v * amax.
+ * The magnitude code is the number of positive E4M3FN values whose midpoint
+ * with their successor lies below the quotient (binary search over the 126
+ * midpoints), with a quotient exactly on a midpoint going to the
+ * neighbour whose code is even.  |x| <= amax keeps the quotient at or
+ * below 448.  The factor is amax / 448 rounded once to binary32 (the
+ * division in binary64 cannot land on a binary32 midpoint: amax / 7 has a
+ * periodic binary expansion).  A row of zeros gives codes 0 and factor 0;
+ * a NaN element gives the NaN code. */
 void oracle_quantize_rows_e4m3(int64_t rows, int64_t cols, const uint16_t *X, int64_t ldx,
                                uint8_t *Q, int64_t ldq, float *scale)
 {
+    /* mid[c] = (value(c) + value(c + 1)) / 2 for the magnitude codes
+     * c = 0 .. 125 (value(126) = 448 is the largest finite) */
+    double mid[126];
+    for (int c = 0; c < 126; ++c) mid[c] = 0.5 * (e4m3_decode((uint8_t)c) + e4m3_decode((uint8_t)(c + 1)));
     for (int64_t r = 0; r < rows; ++r) {
         const uint16_t *x = X + r * ldx;
-        float amax = 0.0f;
+        double amax = 0.0;
         for (int64_t k = 0; k < cols; ++k) {
-            const float v = fabsf(widen_bf16_f(x[k]));
+            const double v = fabs(widen_bf16(x[k]));
             if (v > amax) amax = v;
         }
-        const float inv = amax > 0.0f ? 448.0f / amax : 0.0f;
-        scale[r] = amax / 448.0f;
+        scale[r] = (float)(amax / 448.0);
         for (int64_t k = 0; k < cols; ++k) {
-            float y = widen_bf16_f(x[k]) * inv;
-            if (y > 448.0f) y = 448.0f;
-            if (y < -448.0f) y = -448.0f;
-            Q[r * ldq + k] = e4m3_encode((double)y);
+            const double v = widen_bf16(x[k]);
+            if (v != v) {
+                Q[r * ldq + k] = 0x7f;
+                continue;
+            }
+            const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+            if (amax == 0.0) {
+                Q[r * ldq + k] = sign;
+                continue;
+            }
+            const double num = fabs(v) * 448.0;          /* exact */
+            /* lo = number of midpoints strictly below the quotient */
+            int lo = 0, hi = 126;
+            while (lo < hi) {
+                const int m = (lo + hi) / 2;
+                if (mid[m] * amax < num) lo = m + 1;     /* both sides exact */
+                else hi = m;
+            }
+            int c = lo;                                  /* nearest from above the midpoints below */
+            if (c < 126 && mid[c] * amax == num && (c & 1)) c += 1;   /* tie: even neighbour */
+            Q[r * ldq + k] = (uint8_t)(sign | c);
         }
     }
 }

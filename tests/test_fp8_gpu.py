@@ -75,6 +75,36 @@ def test_quantize_rows_bit_exact(oracle_mod, rows, cols, ldx_pad, ldq_pad):
     assert np.all(Q[:, cols:] == 0xAB), "row padding of Q was written"
 
 
+# (x, amax) pairs of bf16 values whose exact quotient x * 448 / amax lies on
+# the midpoint of two E4M3FN neighbours (200, 84, 336, 1.5625, 0.65625, 184):
+# the exact rule of Example 5-7 takes the even code.
+_TIES = [(0.00133514404296875, 0.00299072265625), (0.001190185546875, 0.00634765625),
+         (0.0047607421875, 0.00634765625), (0.00133514404296875, 0.3828125),
+         (0.001190185546875, 0.8125), (0.00122833251953125, 0.00299072265625)]
+
+
+def test_quantize_rows_exact_ties(oracle_mod):
+    """Quotients exactly on a midpoint, both signs, amax given by a negative
+    element, and a wide row of random multiples of the tie numerators: the
+    kernel's codes equal the oracle's exact ones bit for bit."""
+    _say("quantize exact ties")
+    g = np.random.default_rng([gi.SEED_BASE + 7050])
+    rows = []
+    for x, amax in _TIES:
+        r = np.zeros(64, np.float32)
+        r[0], r[1], r[2] = x, -amax, -x
+        # more exact ties of the same row: x * 2^j stays a bf16 value below amax
+        for j, e in enumerate(range(-6, 0)):
+            r[3 + j] = np.float32(x) * np.float32(2.0 ** e)
+        r[10:] = (g.random(54).astype(np.float32) * 2 - 1) * np.float32(amax)
+        rows.append(r)
+    X = gi.to_bf16_bits(np.stack(rows))
+    Qref, sref = oracle_mod.quantize_rows_e4m3(X)
+    Q, scale = g5.gemm_fp8_quantize_rows(dev_bf16(X))
+    assert np.array_equal(Q.cpu().numpy(), Qref), f"{int((Q.cpu().numpy() != Qref).sum())} codes differ"
+    assert np.array_equal(scale.cpu().numpy().view(np.uint32), sref.view(np.uint32)), "factors differ"
+
+
 def _fp8_case(M, N, K, seed, pa=0, pb=0, scales=True):
     g = np.random.default_rng([gi.SEED_BASE + 7100 + seed, M, N, K, pa, pb])
     finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)

@@ -149,3 +149,72 @@ def test_fp8_product_small_integers(oracle_mod):
     assert np.array_equal(C, np.array([[0.0, -1.5], [9.0, 10.5]]))
     C2 = oracle_mod.gemm_fp8_nt(A, np.array([2, 0.5], np.float32), Bt, np.array([1, 4], np.float32))
     assert np.array_equal(C2, np.array([[0.0, -12.0], [4.5, 21.0]]))
+
+
+def _nearest_code_exact(x, amax, mags):
+    """The E4M3FN code nearest to x * 448 / amax in rational arithmetic,
+    ties to the even code, by brute force over the 127 magnitudes."""
+    if amax == 0:
+        return 0x80 if math.copysign(1.0, x) < 0 else 0x00
+    q = abs(Fraction(x)) * 448 / Fraction(amax)
+    best = min(range(len(mags)), key=lambda c: (abs(q - mags[c]), c % 2))
+    return (0x80 if x < 0 or math.copysign(1.0, x) < 0 else 0x00) | best
+
+
+# (x, amax) pairs, bf16 values, whose quotient x * 448 / amax is exactly the
+# midpoint of two E4M3FN neighbours (200 = (192 + 208) / 2, 84 = (80 + 88) / 2,
+# 336 = (320 + 352) / 2, 1.5625 = (1.5 + 1.625) / 2, 0.65625 = (0.625 + 0.6875) / 2).
+_TIES = [(0.00133514404296875, 0.00299072265625), (0.001190185546875, 0.00634765625),
+         (0.0047607421875, 0.00634765625), (0.00133514404296875, 0.3828125),
+         (0.001190185546875, 0.8125), (0.00122833251953125, 0.00299072265625)]
+
+
+def test_quantize_rows_exact_against_rationals(oracle_mod):
+    """Operator & Runtime §5.4.3, Example 5-7: each code is the E4M3FN value
+    nearest to the exact quotient x * 448 / amax.  Checked element by element
+    against rational arithmetic and a brute-force nearest-value search, on
+    rows of several magnitudes (codes across the subnormal range too) and on
+    rows built so that quotients fall exactly on midpoints."""
+    mags = [Fraction(float(v)) for v in oracle_mod.e4m3_decode(np.arange(127, dtype=np.uint8))]
+    g = np.random.default_rng(5)
+    rows = [gi.normal(g, (1, 160)) * s for s in (1.0, 1e-3, 300.0)]
+    rows.append((g.random((1, 160)) * 2 - 1).astype(np.float32))
+    X = gi.to_bf16_bits(np.concatenate(rows, 0))
+    ties = np.zeros((len(_TIES), 3), np.float32)
+    for i, (x, amax) in enumerate(_TIES):
+        ties[i] = [x, -amax, -x]                    # amax as a negative entry, the tie on both signs
+    Q, s = oracle_mod.quantize_rows_e4m3(X)
+    xf = gi.bf16_bits_to_f32(X).astype(np.float64)
+    for r in range(X.shape[0]):
+        amax = float(np.abs(xf[r]).max())
+        for k in range(X.shape[1]):
+            assert int(Q[r, k]) == _nearest_code_exact(float(xf[r, k]), amax, mags), (r, k)
+    Qt, st = oracle_mod.quantize_rows_e4m3(gi.to_bf16_bits(ties))
+    tf = gi.bf16_bits_to_f32(gi.to_bf16_bits(ties)).astype(np.float64)
+    assert np.array_equal(tf, ties.astype(np.float64))            # the inputs are bf16 values
+    for r in range(len(_TIES)):
+        for k in range(3):
+            assert int(Qt[r, k]) == _nearest_code_exact(float(tf[r, k]), float(np.abs(tf[r]).max()), mags)
+
+
+def test_quantize_rows_exact_ties(oracle_mod):
+    """Quotients exactly on a midpoint go to the even code.  The two-rounding
+    binary32 form fl(x * fl(448 / amax)) moves some of them off the midpoint
+    and to the odd neighbour; the exact rule does not."""
+    flips = 0
+    for x, amax in _TIES:
+        q = Fraction(x) * 448 / Fraction(amax)
+        row = gi.to_bf16_bits(np.array([[x, amax]], np.float32))
+        Q, s = oracle_mod.quantize_rows_e4m3(row)
+        v = Fraction(float(oracle_mod.e4m3_decode([Q[0, 0]])[0]))
+        lo = max(Fraction(float(d)) for d in oracle_mod.e4m3_decode(np.arange(127, dtype=np.uint8))
+                 if Fraction(float(d)) <= q)
+        hi = min(Fraction(float(d)) for d in oracle_mod.e4m3_decode(np.arange(127, dtype=np.uint8))
+                 if Fraction(float(d)) >= q)
+        assert (lo + hi) / 2 == q and lo != hi                  # an exact tie
+        assert int(Q[0, 0]) % 2 == 0 and v in (lo, hi)          # the even neighbour
+        # the binary32 two-rounding form, emulated
+        y32 = float(np.float32(x) * (np.float32(448.0) / np.float32(amax)))
+        alt = lo if abs(Fraction(y32) - lo) < abs(Fraction(y32) - hi) else hi
+        flips += alt != v
+    assert flips >= 1                                            # the pin separates the two rules
