@@ -92,6 +92,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+    # caller-owned scratch for the paths that split K over workgroups or
+    # realign rows (one stream, so one workspace serves every call)
+    ws = g5.Workspace(dev)
 
     def to_dev_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -156,7 +159,7 @@ def main():
         dX = [to_dev_bf16(X) for _ in range(R)]
         dW = [to_dev_bf16(W) for _ in range(R)]
         dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        fns = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i])) for i in range(R)]
+        fns = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
         st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
         ms = timed(fns, args.steps, args.warmup)
         flops = 2.0 * M * N * K
@@ -190,7 +193,7 @@ def main():
             dX = [to_dev_bf16(X) for _ in range(R)]
             dW = [to_dev_bf16(W) for _ in range(R)]
             dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-            fns = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i])) for i in range(R)]
+            fns = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
             ms = timed(fns, max(200, args.steps), args.warmup)
             gbps = alg_bytes / (ms * 1e-3) / 1e9
             log(f"decode M={M}: {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM)")
@@ -215,7 +218,7 @@ def main():
             dX = [to_dev_bf16(X) for _ in range(R)]
             dW = [to_dev_bf16(Wt) for _ in range(R)]
             dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-            fns = [(lambda i=i: g5.gemm_bf16_nt(dX[i], dW[i], dC[i])) for i in range(R)]
+            fns = [(lambda i=i: g5.gemm_bf16_nt(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
             ms = timed(fns, max(200, args.steps), args.warmup)
             gbps = alg_bytes / (ms * 1e-3) / 1e9
             log(f"decode NT M={M}: {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM)")
@@ -250,7 +253,7 @@ def main():
         dQ = [to_dev_bf16(Q) for _ in range(R)]
         dK = [to_dev_bf16(KT) for _ in range(R)]
         dC = [torch.empty((bt, M, N), device=dev) for _ in range(R)]
-        fns = [(lambda i=i: g5.gemm_bf16_batched(dQ[i], dK[i], dC[i])) for i in range(R)]
+        fns = [(lambda i=i: g5.gemm_bf16_batched(dQ[i], dK[i], dC[i], workspace=ws)) for i in range(R)]
         ms = timed(fns, 100, 10)
         flops = 2.0 * bt * M * N * K
         t_roof = max(flops / (PEAK_BF16_TFLOPS * 1e12), alg_bytes / (PEAK_HBM_GBPS * 1e9))
@@ -270,7 +273,7 @@ def main():
         dA = [to_dev_bf16(A) for _ in range(R)]
         dB = [to_dev_bf16(B) for _ in range(R)]
         dC = [torch.empty((M, N), device=dev) for _ in range(R)]
-        fns = [(lambda i=i: g5.gemm_bf16(dA[i], dB[i], dC[i])) for i in range(R)]
+        fns = [(lambda i=i: g5.gemm_bf16(dA[i], dB[i], dC[i], workspace=ws)) for i in range(R)]
         ms = timed(fns, 30, 5)
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
         log(f"ragged 1000x12280x4100: {ms * 1e3:.2f} us/call, {tf:.1f} TFLOPS ({100 * tf / PEAK_BF16_TFLOPS:.1f}%)")
@@ -292,8 +295,8 @@ def main():
         dZ = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
         dG = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
         dU = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        fused = [(lambda i=i: g5.gemm_bf16_swiglu(dX[i], dW[i], dZ[i])) for i in range(R)]
-        plain = [(lambda i=i: (g5.gemm_bf16(dX[i], dW[i][:, :N], dG[i]), g5.gemm_bf16(dX[i], dW[i][:, N:], dU[i])))
+        fused = [(lambda i=i: g5.gemm_bf16_swiglu(dX[i], dW[i], dZ[i], workspace=ws)) for i in range(R)]
+        plain = [(lambda i=i: (g5.gemm_bf16(dX[i], dW[i][:, :N], dG[i], workspace=ws), g5.gemm_bf16(dX[i], dW[i][:, N:], dU[i], workspace=ws)))
                  for i in range(R)]
         ms = timed(fused, 30, 5)
         ms_plain = timed(plain, 30, 5)
@@ -318,7 +321,7 @@ def main():
         dX = [to_dev_bf16(X) for _ in range(R)]
         dW = [to_dev_bf16(W) for _ in range(R)]
         dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        fns = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i])) for i in range(R)]
+        fns = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
         st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
         ms = timed(fns, 100, 10)
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
@@ -341,10 +344,10 @@ def main():
         qW = [g5.gemm_fp8_quantize_rows(to_dev_bf16(Wt)) for _ in range(R)]
         qX = [g5.gemm_fp8_quantize_rows(dX[i]) for i in range(R)]
         dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        gemm = [(lambda i=i: g5.gemm_fp8_nt(qX[i][0], qX[i][1], qW[i][0], qW[i][1], dC[i])) for i in range(R)]
+        gemm = [(lambda i=i: g5.gemm_fp8_nt(qX[i][0], qX[i][1], qW[i][0], qW[i][1], dC[i], workspace=ws)) for i in range(R)]
         quant = [(lambda i=i: g5.gemm_fp8_quantize_rows(dX[i], qX[i][0], qX[i][1])) for i in range(R)]
         both = [(lambda i=i: (g5.gemm_fp8_quantize_rows(dX[i], qX[i][0], qX[i][1]),
-                              g5.gemm_fp8_nt(qX[i][0], qX[i][1], qW[i][0], qW[i][1], dC[i]))) for i in range(R)]
+                              g5.gemm_fp8_nt(qX[i][0], qX[i][1], qW[i][0], qW[i][1], dC[i], workspace=ws))) for i in range(R)]
         ms_g = timed(gemm, 50, 10)
         ms_q = timed(quant, 100, 10)
         ms_b = timed(both, 50, 10)
@@ -365,7 +368,7 @@ def main():
             qW2 = [qW[i % R] for i in range(Rd)]
             qXd = [g5.gemm_fp8_quantize_rows(to_dev_bf16(Xd)) for _ in range(Rd)]
             dCd = [torch.empty((Md, N), dtype=torch.bfloat16, device=dev) for _ in range(Rd)]
-            fns = [(lambda i=i: g5.gemm_fp8_nt(qXd[i][0], qXd[i][1], qW2[i][0], qW2[i][1], dCd[i])) for i in range(Rd)]
+            fns = [(lambda i=i: g5.gemm_fp8_nt(qXd[i][0], qXd[i][1], qW2[i][0], qW2[i][1], dCd[i], workspace=ws)) for i in range(Rd)]
             ms_d = timed(fns, 200, 10)
             gbps = alg / (ms_d * 1e-3) / 1e9
             log(f"fp8 decode M={Md}: {ms_d * 1e3:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM)")
@@ -385,7 +388,7 @@ def main():
         dQ = [to_dev_bf16(Q) for _ in range(R)]
         dK = [to_dev_bf16(Km) for _ in range(R)]
         dC = [torch.empty((bt, M, N), device=dev) for _ in range(R)]
-        fns = [(lambda i=i: g5.gemm_bf16_nt_batched(dQ[i], dK[i], dC[i])) for i in range(R)]
+        fns = [(lambda i=i: g5.gemm_bf16_nt_batched(dQ[i], dK[i], dC[i], workspace=ws)) for i in range(R)]
         ms = timed(fns, 100, 10)
         gbps = alg_bytes / (ms * 1e-3) / 1e9
         log(f"scores Q.K^T from row-major K (NT): {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s")
@@ -407,8 +410,8 @@ def main():
         dW = [to_dev_bf16(W) for _ in range(R)]
         db = [to_dev_bf16(bias) for _ in range(R)]
         dC = [torch.zeros((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        fns = [(lambda i=i: g5.gemm_bf16_affine(dX[i], dW[i], dC[i], bias=db[i], beta=1.0)) for i in range(R)]
-        plain = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i])) for i in range(R)]
+        fns = [(lambda i=i: g5.gemm_bf16_affine(dX[i], dW[i], dC[i], bias=db[i], beta=1.0, workspace=ws)) for i in range(R)]
+        plain = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
         ms = timed(fns, 50, 10)
         ms_plain = timed(plain, 50, 10)
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
@@ -432,8 +435,8 @@ def main():
         dW = [to_dev_bf16(Wt) for _ in range(R)]
         db = [to_dev_bf16(bias) for _ in range(R)]
         dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        fns = [(lambda i=i: g5.gemm_bf16_nt_affine(dX[i], dW[i], dC[i], bias=db[i])) for i in range(R)]
-        plain = [(lambda i=i: g5.gemm_bf16_nt(dX[i], dW[i], dC[i])) for i in range(R)]
+        fns = [(lambda i=i: g5.gemm_bf16_nt_affine(dX[i], dW[i], dC[i], bias=db[i], workspace=ws)) for i in range(R)]
+        plain = [(lambda i=i: g5.gemm_bf16_nt(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
         ms = timed(fns, 50, 10)
         ms_plain = timed(plain, 50, 10)
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
@@ -455,7 +458,7 @@ def main():
         dX = [to_dev_bf16(X) for _ in range(R)]
         dD = [to_dev_bf16(dY) for _ in range(R)]
         dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        fns = [(lambda i=i: g5.gemm_bf16_tn(dX[i], dD[i], dC[i])) for i in range(R)]
+        fns = [(lambda i=i: g5.gemm_bf16_tn(dX[i], dD[i], dC[i], workspace=ws)) for i in range(R)]
         st, plan = g5.plan_query(g5.GEMM_OP_BF16_TN, M, N, K)
         ms = timed(fns, 50, 10)
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12

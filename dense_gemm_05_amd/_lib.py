@@ -14,6 +14,7 @@ GEMM_ERR_INVALID_ARG = -1
 GEMM_ERR_UNSUPPORTED = -2
 GEMM_ERR_LAUNCH = -3
 GEMM_ERR_NO_DEVICE = -4
+GEMM_ERR_WORKSPACE = -5
 
 GEMM_OUT_BF16 = 0
 GEMM_OUT_F32 = 1
@@ -36,9 +37,9 @@ EXPORTS = ("gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm
            "gemm_bf16_tn", "gemm_bf16_tn_batched",
            "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_bf16_silu_batched", "gemm_bf16_swiglu_batched",
            "gemm_fp8_quantize_rows", "gemm_fp8_nt", "gemm_bf16_affine", "gemm_bf16_nt_affine",
-           "gemm_bf16_tn_affine",
+           "gemm_bf16_tn_affine", "gemm_run", "gemm_workspace_size",
            "gemm_status_string",
-           "gemm_plan_query", "gemm_model_local_bytes", "gemm_model_traffic_bytes", "gemm_model_quant_traffic",
+           "gemm_plan_query", "gemm_plan_query_ex", "gemm_model_local_bytes", "gemm_model_traffic_bytes", "gemm_model_quant_traffic",
            "gemm_tile_map")
 
 
@@ -107,6 +108,15 @@ def lib():
     L.gemm_plan_query.argtypes = [i32, i64, i64, i64, i64, u64, i64, i64, u64, i64, i64, u64, i64, i64,
                                   i32, ctypes.POINTER(GemmPlan)]
     L.gemm_plan_query.restype = i32
+    L.gemm_plan_query_ex.argtypes = [i32] + L.gemm_plan_query.argtypes
+    L.gemm_plan_query_ex.restype = i32
+    L.gemm_workspace_size.argtypes = [i32, i64, i64, i64, i64, u64, i64, i64, u64, i64, i64, u64, i64, i64,
+                                      i32, ctypes.POINTER(u64)]
+    L.gemm_workspace_size.restype = i32
+    f32 = ctypes.c_float
+    L.gemm_run.argtypes = [i32, i64, i64, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64, i32,
+                           f32, p, f32, p, p, p, u64, p]
+    L.gemm_run.restype = i32
     L.gemm_model_local_bytes.argtypes = [i64, i64, i64, i64]
     L.gemm_model_local_bytes.restype = i64
     L.gemm_model_traffic_bytes.argtypes = [i64, i64, i64, i64, i64, i64]

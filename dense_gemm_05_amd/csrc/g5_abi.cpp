@@ -5,14 +5,11 @@
 // they are usable (through gemm_plan_query) without a device.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <map>
 #include <mutex>
-#include <utility>
 
 #include "../../include/gemm05.h"
 #include "g5_common.h"
@@ -354,8 +351,16 @@ bool split_ok(const Problem &p, int S)
 // Stages per slice of a K split (the last slice also takes the rest of K).
 int split_kt_per(const Problem &p, int S) { return (int)((p.K / stage_k(p)) / S); }
 
+// Counters live in the first kCounterBytes of a workspace: a split call
+// needs one per output tile (tiled kernels) or per strip (small-M path).
+constexpr size_t kCounterBytes = 64 * 1024;
+constexpr int64_t kMaxCounters = (int64_t)(kCounterBytes / sizeof(unsigned));
+
+// The plan of a call.  `ws`: a caller workspace will be passed, so the
+// paths that need scratch memory (K split over workgroups, the split small-M
+// path, realigned row copies) may be chosen; without one they are not.
 // Returns GEMM_OK or GEMM_ERR_UNSUPPORTED.
-int select_plan(const Problem &p, Plan &pl)
+int select_plan(const Problem &p, Plan &pl, bool ws)
 {
     pl = Plan();
     if (p.batch == 0 || p.M == 0 || p.N == 0) {
@@ -397,7 +402,8 @@ int select_plan(const Problem &p, Plan &pl)
         // than one slice; else whole-K strips of 64 columns.
         pl.config = CFG_DECODE_SPLIT;
         bool ev = false;
-        if (pick_variant(p, pl, &ev) < 0 || decode_slices(cdiv(p.N, 128) * p.batch, p.K) < 2)
+        if (!ws || pick_variant(p, pl, &ev) < 0 || decode_slices(cdiv(p.N, 128) * p.batch, p.K) < 2 ||
+            cdiv(p.N, 128) * p.batch > kMaxCounters)
             pl.config = CFG_DECODE_64;
     } else {
         // Candidates with their measured relative efficiency; the model
@@ -444,7 +450,8 @@ int select_plan(const Problem &p, Plan &pl)
         // 128x128 tiles when the model gives it the shortest time
         // (page "Operator & Runtime" §5.2.4 splits the reduction dimension
         // to occupy the device).
-        if (bf16 && (epi_of(p) == EPI_NONE || epi_of(p) == EPI_AFFINE)) {
+        if (ws && bf16 && (epi_of(p) == EPI_NONE || epi_of(p) == EPI_AFFINE) &&
+            p.batch * cdiv(p.M, 128) * cdiv(p.N, 128) <= kMaxCounters) {
             Plan t = pl;
             t.config = CFG_BF16_128x128;
             bool ev = false;
@@ -467,7 +474,8 @@ int select_plan(const Problem &p, Plan &pl)
         // diagnostic: force the K split of the 128x128 ring kernel (1 = none)
         const int S = std::atoi(fk);
         if (S >= 1 && pl.config == CFG_BF16_128x128 && (epi_of(p) == EPI_NONE || epi_of(p) == EPI_AFFINE)) {
-            if (S > 1 && !split_ok(p, S)) return GEMM_ERR_UNSUPPORTED;
+            if (S > 1 && (!ws || !split_ok(p, S) || p.batch * cdiv(p.M, 128) * cdiv(p.N, 128) > kMaxCounters))
+                return GEMM_ERR_UNSUPPORTED;
             pl.ksplit = S;
         }
     }
@@ -482,7 +490,7 @@ int select_plan(const Problem &p, Plan &pl)
     // The fused epilogues and a transposed B exist only in the ring kernels,
     // so such a call whose rows no ring variant takes is realigned at any
     // size: Bt's rows first, then A's.
-    if (kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && b_trans(p) && p.op != GEMM_OP_FP8_NT &&
+    if (ws && kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && b_trans(p) && p.op != GEMM_OP_FP8_NT &&
         pl.align_b < 16) {
         pl.realign_b = true;
         pl.ldb2 = (p.K + 7) / 8 * 8;
@@ -492,7 +500,7 @@ int select_plan(const Problem &p, Plan &pl)
         q.sB = p.N * pl.ldb2;
         pl.variant = pick_variant(q, pl, &pl.even);
     }
-    if (kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && p.op != GEMM_OP_FP8_NT &&
+    if (ws && kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && p.op != GEMM_OP_FP8_NT &&
         (pl.align_a < 16 || (a_trans(p) && p.M % 8 != 0)) &&
         ((double)p.batch * p.M * p.N * p.K >= (double)(1 << 30) || (ring_only(p) && pl.variant == 0))) {
         Problem q = p;
@@ -529,24 +537,35 @@ size_t realign_b_bytes(const Problem &p, const Plan &pl)
     return pl.realign_b ? (size_t)p.batch * p.N * pl.ldb2 * 2 : 0;
 }
 
-// Workspace of the split small-M path: one slot of 16 x 128 partial sums
-// per (batch entry, strip, K slice), one arrival counter per strip.
-size_t split_part_bytes(const Problem &p, const Plan &pl)
+// Partial sums of the split small-M path: one slot of 16 x 128 FP32 per
+// (batch entry, strip, K slice); of a K-split tiled call: ksplit FP32 tiles
+// per output tile.  The arrival counters (one per strip or tile) are in the
+// workspace's counter region.
+size_t partial_bytes(const Problem &p, const Plan &pl)
 {
-    return (size_t)p.batch * pl.tiles_n * pl.ks * 16 * 128 * sizeof(float);
-}
-size_t split_cnt_bytes(const Problem &p, const Plan &pl) { return (size_t)p.batch * pl.tiles_n * sizeof(unsigned); }
-
-// Workspace of a K-split tiled call: ksplit FP32 partial tiles per tile,
-// one arrival counter per tile.
-size_t ksplit_part_bytes(const Problem &p, const Plan &pl)
-{
+    if (pl.config == CFG_DECODE_SPLIT) return (size_t)p.batch * pl.tiles_n * pl.ks * 16 * 128 * sizeof(float);
     const ConfigInfo &c = kConfigs[pl.config];
     return pl.ksplit > 1 ? (size_t)p.batch * pl.tiles_m * pl.tiles_n * pl.ksplit * c.tile_m * c.tile_n * 4 : 0;
 }
-size_t ksplit_cnt_bytes(const Problem &p, const Plan &pl)
+
+// Workspace layout (byte offsets from its start, each region 256-byte
+// aligned): [0, kCounterBytes) arrival counters, then the partial sums,
+// then the realigned copy of A, then that of Bt.  A plan that needs none of
+// them needs no workspace (0 bytes).
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+struct WsLayout {
+    size_t part = 0, rows_a = 0, rows_b = 0, total = 0;
+};
+WsLayout ws_layout(const Problem &p, const Plan &pl)
 {
-    return pl.ksplit > 1 ? (size_t)p.batch * pl.tiles_m * pl.tiles_n * sizeof(unsigned) : 0;
+    WsLayout L;
+    const size_t pb = partial_bytes(p, pl), ab = realign_bytes(p, pl), bb = realign_b_bytes(p, pl);
+    if (pb == 0 && ab == 0 && bb == 0) return L;
+    L.part = kCounterBytes;
+    L.rows_a = L.part + round256(pb);
+    L.rows_b = L.rows_a + round256(ab);
+    L.total = L.rows_b + round256(bb);
+    return L;
 }
 
 void fill_public_plan(const Problem &p, const Plan &pl, gemm_plan *out)
@@ -574,15 +593,13 @@ void fill_public_plan(const Problem &p, const Plan &pl, gemm_plan *out)
     }
     out->model_bytes = pl.model_bytes;
     std::snprintf(out->name, sizeof out->name, "%s", c.name);
-    if (pl.config == CFG_DECODE_SPLIT) out->workspace_bytes = split_part_bytes(p, pl) + split_cnt_bytes(p, pl);
-    out->workspace_bytes += ksplit_part_bytes(p, pl) + ksplit_cnt_bytes(p, pl);
-    out->workspace_bytes += realign_bytes(p, pl) + realign_b_bytes(p, pl);
+    out->workspace_bytes = (int64_t)ws_layout(p, pl).total;
     out->ksplit = pl.ksplit;
 }
 
 // ------------------------------------------------------------ device check
 std::mutex g_dev_mu;
-int g_dev_state[64];  // 0 unknown, 1 ok, -1 unsupported
+int g_dev_state[64];  // 0 unknown, 1 gfx950, -1 another architecture (no usable device)
 
 int check_device()
 {
@@ -595,7 +612,7 @@ int check_device()
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_NO_DEVICE;
         g_dev_state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
     }
-    return g_dev_state[dev] == 1 ? GEMM_OK : GEMM_ERR_UNSUPPORTED;
+    return g_dev_state[dev] == 1 ? GEMM_OK : GEMM_ERR_NO_DEVICE;
 }
 
 bool log_enabled()
@@ -608,91 +625,38 @@ bool log_enabled()
     return v == 1;
 }
 
-// ------------------------------------------------------------ workspace
-// The split small-M path keeps per-strip counters and partial sums in two
-// buffers owned by the library: one pair per (device, stream), allocated on
-// first use and grown when a call needs more, never freed before exit.  The
-// counter buffer is zeroed when it is allocated and every kernel leaves the
-// counters it used at zero; the partial sums need no initial value.
-struct Buffer {
-    void *ptr = nullptr;
-    size_t bytes = 0;
-};
-struct Workspace {
-    Buffer cnt, part;  // split small-M path
-    Buffer rows;       // realigned copy of A
-    Buffer rows_b;     // realigned copy of a transposed B
-};
-// Held from the first workspace lookup of a call until its last launch is
-// enqueued: a call on the same stream from another thread could otherwise
-// grow (synchronise, free, reallocate) a buffer between this call's lookup
-// and its launch.  Recursive so the lookups below can take it again.
-std::recursive_mutex g_ws_mutex;
-std::map<std::pair<int, void *>, Workspace> g_ws;
-
-// Make `b` at least `need` bytes (zeroed when `zero`); false on failure.
-bool grow(Buffer &b, size_t need, bool zero, void *stream)
+// The plan a call runs: with the workspace paths when the caller passes a
+// workspace (which must then hold what the plan needs), else without.
+int plan_for_call(const Problem &p, const void *ws, size_t ws_bytes, Plan &pl, WsLayout &L)
 {
-    if (b.bytes >= need) return true;
-    if (b.ptr) {
-        if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return false;
-        (void)hipFree(b.ptr);
-        b.ptr = nullptr;
-        b.bytes = 0;
-    }
-    const size_t bytes = (need + (2u << 20) - 1) & ~(size_t)((2u << 20) - 1);
-    void *ptr = nullptr;
-    if (hipMalloc(&ptr, bytes) != hipSuccess) {
-        (void)hipGetLastError();
-        return false;
-    }
-    if (zero && hipMemsetAsync(ptr, 0, bytes, (hipStream_t)stream) != hipSuccess) {
-        (void)hipFree(ptr);
-        return false;
-    }
-    b.ptr = ptr;
-    b.bytes = bytes;
-    return true;
+    int st = select_plan(p, pl, ws != nullptr);
+    if (st != GEMM_OK) return st;
+    L = ws_layout(p, pl);
+    if (ws != nullptr && L.total > ws_bytes) return GEMM_ERR_WORKSPACE;
+    if (ws != nullptr && ((uintptr_t)ws % 256) != 0) return GEMM_ERR_INVALID_ARG;
+    return GEMM_OK;
 }
 
-bool get_workspace(int dev, void *stream, size_t cnt_bytes, size_t part_bytes, unsigned **cnt, float **part)
-{
-    std::lock_guard<std::recursive_mutex> lock(g_ws_mutex);
-    Workspace &w = g_ws[std::make_pair(dev, stream)];
-    if (!grow(w.cnt, cnt_bytes, true, stream) || !grow(w.part, part_bytes, false, stream)) return false;
-    *cnt = (unsigned *)w.cnt.ptr;
-    *part = (float *)w.part.ptr;
-    return true;
-}
-
-uint16_t *get_row_buffer(int dev, void *stream, size_t bytes, bool second = false)
-{
-    std::lock_guard<std::recursive_mutex> lock(g_ws_mutex);
-    Workspace &w = g_ws[std::make_pair(dev, stream)];
-    Buffer &b = second ? w.rows_b : w.rows;
-    if (!grow(b, bytes, false, stream)) return nullptr;
-    return (uint16_t *)b.ptr;
-}
-
-int run(const Problem &p, void *stream)
+// Validate, plan and enqueue one call.  `ws`: the caller's workspace (NULL:
+// none); no memory is allocated, freed, copied or waited for here.
+int run(const Problem &p, void *stream, void *ws = nullptr, size_t ws_bytes = 0)
 {
     int st = validate(p);
     if (st != GEMM_OK) return st;
     Plan pl;
-    st = select_plan(p, pl);
+    WsLayout L;
+    st = plan_for_call(p, ws, ws_bytes, pl, L);
     if (st != GEMM_OK) return st;
     if (pl.config == CFG_NONE) return GEMM_OK;
     st = check_device();
     if (st != GEMM_OK) return st;
+    char *wsb = (char *)ws;
+    unsigned *counters = (unsigned *)wsb;
     if (log_enabled())
         std::fprintf(stderr, "[gemm05] op=%d batch=%lld M=%lld N=%lld K=%lld -> %s variant=%d grid=%lld align=(%d,%d,%d)\n",
                      p.op, (long long)p.batch, (long long)p.M, (long long)p.N, (long long)p.K,
                      kConfigs[pl.config].name, pl.variant, (long long)pl.grid, pl.align_a, pl.align_b,
                      pl.align_c);
-    // Calls that use a workspace keep it locked until their launches are
-    // enqueued (see g_ws_mutex).
-    std::unique_lock<std::recursive_mutex> ws_lock(g_ws_mutex, std::defer_lock);
-    if (pl.realign_a || pl.realign_b || pl.ksplit > 1 || pl.config == CFG_DECODE_SPLIT) ws_lock.lock();
     GemmArgs a;
     a.A = (const void *)p.a;
     a.B = (const void *)p.b;
@@ -727,10 +691,7 @@ int run(const Problem &p, void *stream)
     a.affine = is_affine(p) ? 1 : 0;
     a.a_trans = a_trans(p) ? 1 : 0;
     if (pl.realign_b) {
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        uint16_t *B2 = get_row_buffer(dev, stream, realign_b_bytes(p, pl), true);
-        if (!B2) return GEMM_ERR_UNSUPPORTED;   // no ring kernel takes these Bt rows as they are
+        uint16_t *B2 = (uint16_t *)(wsb + L.rows_b);
         const hipError_t e = launch_realign_rows((const uint16_t *)p.b, p.ldb, p.sB, p.batch, p.N, p.K,
                                                  row_alignment(p.b, p.ldb, p.sB, p.batch, 2), B2, pl.ldb2,
                                                  (hipStream_t)stream);
@@ -743,65 +704,25 @@ int run(const Problem &p, void *stream)
     a.ws_part = nullptr;
     a.ws_cnt = nullptr;
     if (pl.ksplit > 1) {
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        unsigned *cnt = nullptr;
-        float *part = nullptr;
-        if (get_workspace(dev, stream, ksplit_cnt_bytes(p, pl), ksplit_part_bytes(p, pl), &cnt, &part)) {
-            a.ksplit = pl.ksplit;
-            a.kt_per = split_kt_per(p, pl.ksplit);
-            a.ws_part = part;
-            a.ws_cnt = cnt;
-        } else {
-            // No workspace: one workgroup per tile over all of K.
-            pl.ksplit = 1;
-            fill_grid(p, pl);
-        }
+        a.ksplit = pl.ksplit;
+        a.kt_per = split_kt_per(p, pl.ksplit);
+        a.ws_part = (float *)(wsb + L.part);
+        a.ws_cnt = counters;
     }
     if (pl.realign_a) {
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        uint16_t *A2 = get_row_buffer(dev, stream, realign_bytes(p, pl));
-        if (A2) {
-            const hipError_t e = launch_realign_rows((const uint16_t *)p.a, p.lda, p.sA, p.batch, a_rows(p),
-                                                     a_cols(p), row_alignment(p.a, p.lda, p.sA, p.batch, 2), A2,
-                                                     pl.lda2, (hipStream_t)stream);
-            if (e != hipSuccess) return GEMM_ERR_LAUNCH;
-            a.A = A2;
-            a.lda = pl.lda2;
-            a.sA = a_rows(p) * pl.lda2;
-            a.align_a = 16;
-        } else {
-            // No buffer: multiply from A as it is.
-            pl.realign_a = false;
-            pl.align_a = row_alignment(p.a, p.lda, p.sA, p.batch, 2);
-            pl.variant = pick_variant(p, pl, &pl.even);
-            a.align_a = pl.align_a;
-            if (pl.realign_b) {   // the variant for the realigned Bt rows
-                Problem q = p;
-                q.ldb = pl.ldb2;
-                q.sB = p.N * pl.ldb2;
-                pl.variant = pick_variant(q, pl, &pl.even);
-            }
-            if (ring_only(p) && tiled(pl.config) && pl.variant == 0) return GEMM_ERR_UNSUPPORTED;
-        }
+        uint16_t *A2 = (uint16_t *)(wsb + L.rows_a);
+        const hipError_t e = launch_realign_rows((const uint16_t *)p.a, p.lda, p.sA, p.batch, a_rows(p), a_cols(p),
+                                                 row_alignment(p.a, p.lda, p.sA, p.batch, 2), A2, pl.lda2,
+                                                 (hipStream_t)stream);
+        if (e != hipSuccess) return GEMM_ERR_LAUNCH;
+        a.A = A2;
+        a.lda = pl.lda2;
+        a.sA = a_rows(p) * pl.lda2;
+        a.align_a = 16;
     }
     if (pl.config == CFG_DECODE_SPLIT) {
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        const size_t cnt_bytes = split_cnt_bytes(p, pl);
-        const size_t part_bytes = split_part_bytes(p, pl);
-        unsigned *cnt = nullptr;
-        float *part = nullptr;
-        if (get_workspace(dev, stream, cnt_bytes, part_bytes, &cnt, &part)) {
-            const hipError_t e = launch_decode_split(a, part, cnt, pl.ks, (hipStream_t)stream);
-            return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
-        }
-        // No workspace: whole-K strips of 64 columns.
-        pl.config = CFG_DECODE_64;
-        fill_grid(p, pl);
-        pl.variant = pick_variant(p, pl, &pl.even);
-        a.tiles_n = pl.tiles_n;
+        const hipError_t e = launch_decode_split(a, (float *)(wsb + L.part), counters, pl.ks, (hipStream_t)stream);
+        return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
     }
     const hipError_t e =
         pl.config == CFG_ZERO ? (is_affine(p) ? launch_affine_no_product(a, pl.grid, (hipStream_t)stream)
@@ -987,14 +908,17 @@ const char *gemm_status_string(int status)
     case GEMM_ERR_INVALID_ARG: return "GEMM_ERR_INVALID_ARG: invalid size, stride, pointer, output type or overlap";
     case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED: no compiled kernel configuration can run this call";
     case GEMM_ERR_LAUNCH: return "GEMM_ERR_LAUNCH: kernel launch failed";
-    case GEMM_ERR_NO_DEVICE: return "GEMM_ERR_NO_DEVICE: no usable HIP device is current";
+    case GEMM_ERR_NO_DEVICE: return "GEMM_ERR_NO_DEVICE: no usable HIP device is current (none, or not gfx950)";
+    case GEMM_ERR_WORKSPACE:
+        return "GEMM_ERR_WORKSPACE: the workspace passed is smaller than the call needs (gemm_workspace_size)";
     default: return "unknown gemm status";
     }
 }
 
-int gemm_plan_query(int op, int64_t batch, int64_t M, int64_t N, int64_t K, uint64_t a_addr, int64_t lda,
-                    int64_t strideA, uint64_t b_addr, int64_t ldb, int64_t strideB, uint64_t c_addr, int64_t ldc,
-                    int64_t strideC, int c_type, gemm_plan *out)
+static int plan_query_impl(int with_workspace, int op, int64_t batch, int64_t M, int64_t N, int64_t K,
+                           uint64_t a_addr, int64_t lda, int64_t strideA, uint64_t b_addr, int64_t ldb,
+                           int64_t strideB, uint64_t c_addr, int64_t ldc, int64_t strideC, int c_type,
+                           gemm_plan *out)
 {
     const Problem p{op, batch, M, N, K, a_addr, b_addr, c_addr, lda, ldb, ldc, strideA, strideB, strideC,
                     op == GEMM_OP_SGEMM ? (int)GEMM_OUT_F32
@@ -1003,10 +927,60 @@ int gemm_plan_query(int op, int64_t batch, int64_t M, int64_t N, int64_t K, uint
     int st = g5::validate(p);
     if (st != GEMM_OK) return st;
     g5::Plan pl;
-    st = g5::select_plan(p, pl);
+    st = g5::select_plan(p, pl, with_workspace != 0);
     if (st != GEMM_OK) return st;
     g5::fill_public_plan(p, pl, out);
     return GEMM_OK;
+}
+
+int gemm_plan_query(int op, int64_t batch, int64_t M, int64_t N, int64_t K, uint64_t a_addr, int64_t lda,
+                    int64_t strideA, uint64_t b_addr, int64_t ldb, int64_t strideB, uint64_t c_addr, int64_t ldc,
+                    int64_t strideC, int c_type, gemm_plan *out)
+{
+    return plan_query_impl(1, op, batch, M, N, K, a_addr, lda, strideA, b_addr, ldb, strideB, c_addr, ldc, strideC,
+                           c_type, out);
+}
+
+int gemm_plan_query_ex(int with_workspace, int op, int64_t batch, int64_t M, int64_t N, int64_t K, uint64_t a_addr,
+                       int64_t lda, int64_t strideA, uint64_t b_addr, int64_t ldb, int64_t strideB, uint64_t c_addr,
+                       int64_t ldc, int64_t strideC, int c_type, gemm_plan *out)
+{
+    return plan_query_impl(with_workspace, op, batch, M, N, K, a_addr, lda, strideA, b_addr, ldb, strideB, c_addr,
+                           ldc, strideC, c_type, out);
+}
+
+int gemm_workspace_size(int op, int64_t batch, int64_t M, int64_t N, int64_t K, uint64_t a_addr, int64_t lda,
+                        int64_t strideA, uint64_t b_addr, int64_t ldb, int64_t strideB, uint64_t c_addr, int64_t ldc,
+                        int64_t strideC, int c_type, uint64_t *bytes)
+{
+    gemm_plan pl;
+    const int st = plan_query_impl(1, op, batch, M, N, K, a_addr, lda, strideA, b_addr, ldb, strideB, c_addr, ldc,
+                                   strideC, c_type, &pl);
+    if (bytes) *bytes = st == GEMM_OK ? (uint64_t)pl.workspace_bytes : 0;
+    return st;
+}
+
+int gemm_run(int op, int64_t batch, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int64_t strideA,
+             const void *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc, int64_t strideC, int c_type,
+             float alpha, const uint16_t *bias, float beta, const float *scale_a, const float *scale_b,
+             void *workspace, uint64_t workspace_bytes, void *stream)
+{
+    if (op < GEMM_OP_SGEMM || op > GEMM_OP_BF16_TN_AFFINE) return GEMM_ERR_INVALID_ARG;
+    Problem p{op, batch, M, N, K, (uint64_t)A, (uint64_t)B, (uint64_t)C, lda, ldb, ldc, strideA, strideB, strideC,
+              op == GEMM_OP_SGEMM ? (int)GEMM_OUT_F32
+              : (op == GEMM_OP_BF16_SILU || op == GEMM_OP_BF16_SWIGLU) ? (int)GEMM_OUT_BF16
+                                                                        : c_type};
+    if (op == GEMM_OP_SGEMM && batch != 1) return GEMM_ERR_INVALID_ARG;
+    if (op == GEMM_OP_FP8_NT) {
+        p.scale_a = (uint64_t)scale_a;
+        p.scale_b = (uint64_t)scale_b;
+    }
+    if (op == GEMM_OP_BF16_AFFINE || op == GEMM_OP_BF16_NT_AFFINE || op == GEMM_OP_BF16_TN_AFFINE) {
+        p.alpha = alpha;
+        p.beta = beta;
+        p.bias = (uint64_t)bias;
+    }
+    return g5::run(p, stream, workspace, (size_t)workspace_bytes);
 }
 
 int64_t gemm_model_local_bytes(int64_t m, int64_t n, int64_t k, int64_t elem_bytes)

@@ -4,6 +4,13 @@ Argument marshalling only: the functions read sizes, row strides and data
 pointers from torch tensors (device memory owned by the caller), pass the
 current HIP stream, and raise on a nonzero status.  All arithmetic runs in
 the gfx950 kernels of libgemm05.so.
+
+Every bf16 / fp8 product takes an optional ``workspace``: a ``Workspace``
+(caller-owned scratch memory, allocated through torch) or a uint8 device
+tensor.  With one the call goes through ``gemm_run`` and may use the paths
+that need scratch memory (K split over workgroups, the split small-M path,
+realigned row copies); without one it calls the named entry point, which
+takes the paths that need none.
 """
 import ctypes
 
@@ -16,7 +23,8 @@ __all__ = ["gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm
            "gemm_bf16_tn", "gemm_bf16_tn_batched",
            "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_bf16_silu_batched", "gemm_bf16_swiglu_batched",
            "gemm_fp8_quantize_rows", "gemm_fp8_nt", "gemm_bf16_affine",
-           "gemm_bf16_nt_affine", "gemm_bf16_tn_affine", "plan_query", "GemmError"]
+           "gemm_bf16_nt_affine", "gemm_bf16_tn_affine", "plan_query", "workspace_size", "Workspace",
+           "GemmError"]
 
 
 def _ld(t, inner):
@@ -43,12 +51,15 @@ def _stream(idx):
 
 
 def _check_dev(*ts):
+    """Every tensor the kernels read or write (None entries skipped) must be a
+    GPU tensor on one device; checked before anything is launched."""
+    ts = [t for t in ts if t is not None]
     dev = ts[0].device
     if dev.type != "cuda":
         raise ValueError("operands must be GPU tensors")
     for t in ts[1:]:
         if t.device != dev:
-            raise ValueError("operands must be on one device")
+            raise ValueError("every operand, output, scale, bias and workspace must be on one GPU")
     return dev
 
 
@@ -61,6 +72,74 @@ def _launch(fn, dev, *args):
         return fn(*args, _stream(idx))
 
 
+class Workspace:
+    """Caller-owned scratch memory for the workspace paths of gemm_run.
+
+    Device memory from torch (zero-filled when allocated: the first 64 KiB
+    are arrival counters that every call leaves at zero).  ``reserve(n)``
+    replaces the buffer with a larger one when a call needs more; the old
+    one is released to torch's stream-ordered allocator.  One Workspace
+    serves calls on one stream (calls that may overlap in time need separate
+    workspaces)."""
+
+    def __init__(self, device=None, nbytes=0):
+        if device is None:
+            device = torch.device("cuda", torch.cuda.current_device())
+        self.device = torch.device(device)
+        self.buf = None
+        self._need = {}        # call shape -> bytes (the size query is host-only and deterministic)
+        if nbytes:
+            self.reserve(nbytes)
+
+    def reserve(self, nbytes):
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+def workspace_size(op, batch, M, N, K, a_addr, lda, sA, b_addr, ldb, sB, c_addr, ldc, sC, c_type):
+    """Host-only: bytes of workspace gemm_run needs for a call (0: none)."""
+    n = ctypes.c_uint64(0)
+    st = lib().gemm_workspace_size(op, batch, M, N, K, a_addr, lda, sA, b_addr, ldb, sB, c_addr, ldc, sC, c_type,
+                                   ctypes.byref(n))
+    if st != 0:
+        raise GemmError(st, "gemm_workspace_size")
+    return int(n.value)
+
+
+def _gemm(what, named, named_args, workspace, dev, op, batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, code,
+          alpha=1.0, bias=None, beta=0.0, scale_a=None, scale_b=None):
+    """Run one call: the named entry point (`named`, its arguments
+    `named_args`) without a workspace, else gemm_run with the workspace's
+    memory."""
+    if workspace is None:
+        st = _launch(getattr(lib(), named), dev, *named_args)
+    else:
+        if isinstance(workspace, Workspace):
+            if workspace.device != dev:
+                raise ValueError("the workspace must be on the operands' GPU")
+            pa, pb, pc = A.data_ptr(), B.data_ptr(), C.data_ptr()
+            # the size depends on the pointers only through their alignment
+            key = (op, batch, M, N, K, lda, sA, ldb, sB, ldc, sC, code, pa % 256, pb % 256, pc % 256)
+            need = workspace._need.get(key)
+            if need is None:
+                need = workspace_size(op, batch, M, N, K, pa, lda, sA, pb, ldb, sB, pc, ldc, sC, code) if K > 0 else 0
+                workspace._need[key] = need
+            buf = workspace.reserve(need)
+        else:
+            buf = workspace
+            if not isinstance(buf, torch.Tensor) or buf.dtype != torch.uint8 or buf.dim() != 1:
+                raise ValueError("a workspace tensor must be a 1-D uint8 tensor")
+            _check_dev(A, buf)
+        st = _launch(lib().gemm_run, dev, op, batch, M, N, K, A.data_ptr(), lda, sA, B.data_ptr(), ldb, sB,
+                     C.data_ptr(), ldc, sC, code, float(alpha), None if bias is None else bias.data_ptr(),
+                     float(beta), None if scale_a is None else scale_a.data_ptr(),
+                     None if scale_b is None else scale_b.data_ptr(), buf.data_ptr(), buf.numel())
+    if st != 0:
+        raise GemmError(st, what)
+    return C
+
+
 def gemm_sgemm(A, B, C=None):
     """C[M,N] = A[M,K] . B[K,N] for float32 tensors (gemm_sgemm)."""
     if A.dtype != torch.float32 or B.dtype != torch.float32:
@@ -69,7 +148,7 @@ def gemm_sgemm(A, B, C=None):
     K2, N = B.shape
     if K != K2:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
-    dev = _check_dev(A, B)
+    dev = _check_dev(A, B, C)
     if C is None:
         C = torch.empty((M, N), dtype=torch.float32, device=dev)
     if C.shape != (M, N) or C.dtype != torch.float32:
@@ -89,7 +168,11 @@ def _out_code(dtype):
     raise TypeError("output dtype must be bfloat16 or float32")
 
 
-def gemm_bf16(A, B, C=None, out_dtype=torch.bfloat16):
+def _bstride(t):
+    return t.stride(0) if t.shape[0] > 1 else 0
+
+
+def gemm_bf16(A, B, C=None, out_dtype=torch.bfloat16, workspace=None):
     """C[M,N] = A[M,K] . B[K,N] for bfloat16 operands, FP32 accumulation,
     bf16 (round to nearest even) or float32 output (gemm_bf16)."""
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
@@ -98,24 +181,19 @@ def gemm_bf16(A, B, C=None, out_dtype=torch.bfloat16):
     K2, N = B.shape
     if K != K2:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
-    dev = _check_dev(A, B)
+    dev = _check_dev(A, B, C)
     if C is None:
         C = torch.empty((M, N), dtype=out_dtype, device=dev)
     if C.shape != (M, N):
         raise ValueError("C must be [M, N]")
     code = _out_code(C.dtype)
-    st = _launch(lib().gemm_bf16, dev, M, N, K, A.data_ptr(), _ld(A, K), B.data_ptr(), _ld(B, N),
-                 C.data_ptr(), _ld(C, N), code)
-    if st != 0:
-        raise GemmError(st, "gemm_bf16")
-    return C
+    lda, ldb, ldc = _ld(A, K), _ld(B, N), _ld(C, N)
+    return _gemm("gemm_bf16", "gemm_bf16",
+                 (M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, code), workspace, dev,
+                 _lib.GEMM_OP_BF16, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, code)
 
 
-def _bstride(t):
-    return t.stride(0) if t.shape[0] > 1 else 0
-
-
-def gemm_bf16_batched(A, B, C=None, out_dtype=torch.bfloat16):
+def gemm_bf16_batched(A, B, C=None, out_dtype=torch.bfloat16, workspace=None):
     """C[b] = A[b] . B[b] for bfloat16 stacks [batch, M, K] and [batch, K, N]
     (gemm_bf16_batched).  A batch stride of 0 (an expanded operand)
     broadcasts it."""
@@ -125,20 +203,20 @@ def gemm_bf16_batched(A, B, C=None, out_dtype=torch.bfloat16):
     b2, K2, N = B.shape
     if batch != b2 or K != K2:
         raise ValueError("shape mismatch")
-    dev = _check_dev(A, B)
+    dev = _check_dev(A, B, C)
     if C is None:
         C = torch.empty((batch, M, N), dtype=out_dtype, device=dev)
     if tuple(C.shape) != (batch, M, N):
         raise ValueError("C must be [batch, M, N]")
     code = _out_code(C.dtype)
-    st = _launch(lib().gemm_bf16_batched, dev, batch, M, N, K, A.data_ptr(), _ld(A, K), _bstride(A),
-                 B.data_ptr(), _ld(B, N), _bstride(B), C.data_ptr(), _ld(C, N), _bstride(C), code)
-    if st != 0:
-        raise GemmError(st, "gemm_bf16_batched")
-    return C
+    lda, ldb, ldc = _ld(A, K), _ld(B, N), _ld(C, N)
+    sA, sB, sC = _bstride(A), _bstride(B), _bstride(C)
+    return _gemm("gemm_bf16_batched", "gemm_bf16_batched",
+                 (batch, M, N, K, A.data_ptr(), lda, sA, B.data_ptr(), ldb, sB, C.data_ptr(), ldc, sC, code),
+                 workspace, dev, _lib.GEMM_OP_BF16, batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, code)
 
 
-def gemm_bf16_nt(A, Bt, C=None, out_dtype=torch.bfloat16):
+def gemm_bf16_nt(A, Bt, C=None, out_dtype=torch.bfloat16, workspace=None):
     """C[M,N] = A[M,K] . Bt[N,K]^T for bfloat16 operands (gemm_bf16_nt): B
     given transposed, as a linear layer's weight or attention's keys."""
     if A.dtype != torch.bfloat16 or Bt.dtype != torch.bfloat16:
@@ -147,19 +225,19 @@ def gemm_bf16_nt(A, Bt, C=None, out_dtype=torch.bfloat16):
     N, K2 = Bt.shape
     if K != K2:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
-    dev = _check_dev(A, Bt)
+    dev = _check_dev(A, Bt, C)
     if C is None:
         C = torch.empty((M, N), dtype=out_dtype, device=dev)
     if C.shape != (M, N):
         raise ValueError("C must be [M, N]")
-    st = _launch(lib().gemm_bf16_nt, dev, M, N, K, A.data_ptr(), _ld(A, K), Bt.data_ptr(), _ld(Bt, K),
-                 C.data_ptr(), _ld(C, N), _out_code(C.dtype))
-    if st != 0:
-        raise GemmError(st, "gemm_bf16_nt")
-    return C
+    code = _out_code(C.dtype)
+    lda, ldb, ldc = _ld(A, K), _ld(Bt, K), _ld(C, N)
+    return _gemm("gemm_bf16_nt", "gemm_bf16_nt",
+                 (M, N, K, A.data_ptr(), lda, Bt.data_ptr(), ldb, C.data_ptr(), ldc, code), workspace, dev,
+                 _lib.GEMM_OP_BF16_NT, 1, M, N, K, A, lda, 0, Bt, ldb, 0, C, ldc, 0, code)
 
 
-def gemm_bf16_nt_batched(A, Bt, C=None, out_dtype=torch.bfloat16):
+def gemm_bf16_nt_batched(A, Bt, C=None, out_dtype=torch.bfloat16, workspace=None):
     """C[b] = A[b] . Bt[b]^T for bfloat16 stacks [batch, M, K] and [batch, N, K]
     (gemm_bf16_nt_batched), e.g. attention scores Q . K^T; a batch stride of
     0 broadcasts an operand."""
@@ -169,19 +247,20 @@ def gemm_bf16_nt_batched(A, Bt, C=None, out_dtype=torch.bfloat16):
     b2, N, K2 = Bt.shape
     if batch != b2 or K != K2:
         raise ValueError("shape mismatch")
-    dev = _check_dev(A, Bt)
+    dev = _check_dev(A, Bt, C)
     if C is None:
         C = torch.empty((batch, M, N), dtype=out_dtype, device=dev)
     if tuple(C.shape) != (batch, M, N):
         raise ValueError("C must be [batch, M, N]")
-    st = _launch(lib().gemm_bf16_nt_batched, dev, batch, M, N, K, A.data_ptr(), _ld(A, K), _bstride(A),
-                 Bt.data_ptr(), _ld(Bt, K), _bstride(Bt), C.data_ptr(), _ld(C, N), _bstride(C), _out_code(C.dtype))
-    if st != 0:
-        raise GemmError(st, "gemm_bf16_nt_batched")
-    return C
+    code = _out_code(C.dtype)
+    lda, ldb, ldc = _ld(A, K), _ld(Bt, K), _ld(C, N)
+    sA, sB, sC = _bstride(A), _bstride(Bt), _bstride(C)
+    return _gemm("gemm_bf16_nt_batched", "gemm_bf16_nt_batched",
+                 (batch, M, N, K, A.data_ptr(), lda, sA, Bt.data_ptr(), ldb, sB, C.data_ptr(), ldc, sC, code),
+                 workspace, dev, _lib.GEMM_OP_BF16_NT, batch, M, N, K, A, lda, sA, Bt, ldb, sB, C, ldc, sC, code)
 
 
-def gemm_bf16_tn(At, B, C=None, out_dtype=torch.bfloat16):
+def gemm_bf16_tn(At, B, C=None, out_dtype=torch.bfloat16, workspace=None):
     """C[M,N] = At[K,M]^T . B[K,N] for bfloat16 operands (gemm_bf16_tn): A
     given transposed, e.g. the activations of a weight gradient X^T . dY."""
     if At.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
@@ -190,20 +269,19 @@ def gemm_bf16_tn(At, B, C=None, out_dtype=torch.bfloat16):
     K2, N = B.shape
     if K != K2:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
-    dev = _check_dev(At, B)
+    dev = _check_dev(At, B, C)
     if C is None:
         C = torch.empty((M, N), dtype=out_dtype, device=dev)
     if C.shape != (M, N):
         raise ValueError("C must be [M, N]")
     code = _out_code(C.dtype)
-    st = _launch(lib().gemm_bf16_tn, dev, M, N, K, At.data_ptr(), _ld(At, M), B.data_ptr(), _ld(B, N),
-                 C.data_ptr(), _ld(C, N), code)
-    if st != 0:
-        raise GemmError(st, "gemm_bf16_tn")
-    return C
+    lda, ldb, ldc = _ld(At, M), _ld(B, N), _ld(C, N)
+    return _gemm("gemm_bf16_tn", "gemm_bf16_tn",
+                 (M, N, K, At.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, code), workspace, dev,
+                 _lib.GEMM_OP_BF16_TN, 1, M, N, K, At, lda, 0, B, ldb, 0, C, ldc, 0, code)
 
 
-def gemm_bf16_tn_batched(At, B, C=None, out_dtype=torch.bfloat16):
+def gemm_bf16_tn_batched(At, B, C=None, out_dtype=torch.bfloat16, workspace=None):
     """C[b] = At[b]^T . B[b] for bfloat16 stacks [batch, K, M] and [batch, K, N]
     (gemm_bf16_tn_batched); a batch stride of 0 broadcasts an operand."""
     if At.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
@@ -212,17 +290,17 @@ def gemm_bf16_tn_batched(At, B, C=None, out_dtype=torch.bfloat16):
     b2, K2, N = B.shape
     if batch != b2 or K != K2:
         raise ValueError("shape mismatch")
-    dev = _check_dev(At, B)
+    dev = _check_dev(At, B, C)
     if C is None:
         C = torch.empty((batch, M, N), dtype=out_dtype, device=dev)
     if tuple(C.shape) != (batch, M, N):
         raise ValueError("C must be [batch, M, N]")
     code = _out_code(C.dtype)
-    st = _launch(lib().gemm_bf16_tn_batched, dev, batch, M, N, K, At.data_ptr(), _ld(At, M), _bstride(At),
-                 B.data_ptr(), _ld(B, N), _bstride(B), C.data_ptr(), _ld(C, N), _bstride(C), code)
-    if st != 0:
-        raise GemmError(st, "gemm_bf16_tn_batched")
-    return C
+    lda, ldb, ldc = _ld(At, M), _ld(B, N), _ld(C, N)
+    sA, sB, sC = _bstride(At), _bstride(B), _bstride(C)
+    return _gemm("gemm_bf16_tn_batched", "gemm_bf16_tn_batched",
+                 (batch, M, N, K, At.data_ptr(), lda, sA, B.data_ptr(), ldb, sB, C.data_ptr(), ldc, sC, code),
+                 workspace, dev, _lib.GEMM_OP_BF16_TN, batch, M, N, K, At, lda, sA, B, ldb, sB, C, ldc, sC, code)
 
 
 def _codes(t):
@@ -241,7 +319,7 @@ def gemm_fp8_quantize_rows(X, Q=None, scale=None):
     if X.dtype != torch.bfloat16 or X.dim() != 2:
         raise TypeError("gemm_fp8_quantize_rows takes a 2-D bfloat16 tensor")
     rows, cols = X.shape
-    dev = _check_dev(X)
+    dev = _check_dev(X, Q, scale)
     if Q is None:
         Q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
     if scale is None:
@@ -258,7 +336,7 @@ def gemm_fp8_quantize_rows(X, Q=None, scale=None):
     return Q, scale
 
 
-def gemm_fp8_nt(A, scale_a, Bt, scale_b, C=None, out_dtype=torch.bfloat16):
+def gemm_fp8_nt(A, scale_a, Bt, scale_b, C=None, out_dtype=torch.bfloat16, workspace=None):
     """C[M,N] = (dec(A) . dec(Bt)^T) * scale_a[:, None] * scale_b[None, :] for
     E4M3FN codes A [M,K] and Bt [N,K] (gemm_fp8_nt); a scale may be None."""
     A, Bt = _codes(A), _codes(Bt)
@@ -266,7 +344,7 @@ def gemm_fp8_nt(A, scale_a, Bt, scale_b, C=None, out_dtype=torch.bfloat16):
     N, K2 = Bt.shape
     if K != K2:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
-    dev = _check_dev(A, Bt)
+    dev = _check_dev(A, Bt, C, scale_a, scale_b)
     for sc, n, what in ((scale_a, M, "scale_a"), (scale_b, N, "scale_b")):
         if sc is not None and (sc.dtype != torch.float32 or tuple(sc.shape) != (n,) or (n > 1 and sc.stride(0) != 1)):
             raise ValueError(f"{what} must be a contiguous float32 vector of {n}")
@@ -274,15 +352,17 @@ def gemm_fp8_nt(A, scale_a, Bt, scale_b, C=None, out_dtype=torch.bfloat16):
         C = torch.empty((M, N), dtype=out_dtype, device=dev)
     if C.shape != (M, N):
         raise ValueError("C must be [M, N]")
-    st = _launch(lib().gemm_fp8_nt, dev, M, N, K, A.data_ptr(), _ld(A, K),
-                 None if scale_a is None else scale_a.data_ptr(), Bt.data_ptr(), _ld(Bt, K),
-                 None if scale_b is None else scale_b.data_ptr(), C.data_ptr(), _ld(C, N), _out_code(C.dtype))
-    if st != 0:
-        raise GemmError(st, "gemm_fp8_nt")
-    return C
+    code = _out_code(C.dtype)
+    lda, ldb, ldc = _ld(A, K), _ld(Bt, K), _ld(C, N)
+    pa = None if scale_a is None else scale_a.data_ptr()
+    pb = None if scale_b is None else scale_b.data_ptr()
+    return _gemm("gemm_fp8_nt", "gemm_fp8_nt",
+                 (M, N, K, A.data_ptr(), lda, pa, Bt.data_ptr(), ldb, pb, C.data_ptr(), ldc, code), workspace, dev,
+                 _lib.GEMM_OP_FP8_NT, 1, M, N, K, A, lda, 0, Bt, ldb, 0, C, ldc, 0, code,
+                 scale_a=scale_a, scale_b=scale_b)
 
 
-def gemm_bf16_silu(A, B, C=None):
+def gemm_bf16_silu(A, B, C=None, workspace=None):
     """C[M,N] = bf16(SiLU(bf16(A . B))) for bfloat16 operands (gemm_bf16_silu)."""
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
         raise TypeError("gemm_bf16_silu takes bfloat16 operands")
@@ -290,19 +370,18 @@ def gemm_bf16_silu(A, B, C=None):
     K2, N = B.shape
     if K != K2:
         raise ValueError(f"inner dimensions differ: {K} vs {K2}")
-    dev = _check_dev(A, B)
+    dev = _check_dev(A, B, C)
     if C is None:
         C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     if C.shape != (M, N) or C.dtype != torch.bfloat16:
         raise ValueError("C must be bfloat16 [M, N]")
-    st = _launch(lib().gemm_bf16_silu, dev, M, N, K, A.data_ptr(), _ld(A, K), B.data_ptr(), _ld(B, N),
-                 C.data_ptr(), _ld(C, N))
-    if st != 0:
-        raise GemmError(st, "gemm_bf16_silu")
-    return C
+    lda, ldb, ldc = _ld(A, K), _ld(B, N), _ld(C, N)
+    return _gemm("gemm_bf16_silu", "gemm_bf16_silu",
+                 (M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc), workspace, dev,
+                 _lib.GEMM_OP_BF16_SILU, 1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, _lib.GEMM_OUT_BF16)
 
 
-def gemm_bf16_swiglu(X, Wgu, Z=None):
+def gemm_bf16_swiglu(X, Wgu, Z=None, workspace=None):
     """Z[M,N] = bf16(bf16(SiLU(bf16(X . W_g))) * bf16(X . W_u)) for a merged
     bfloat16 weight Wgu[K, 2N] = [W_g | W_u] (gemm_bf16_swiglu)."""
     if X.dtype != torch.bfloat16 or Wgu.dtype != torch.bfloat16:
@@ -312,34 +391,18 @@ def gemm_bf16_swiglu(X, Wgu, Z=None):
     if K != K2 or N2 % 2:
         raise ValueError("expected X [M, K] and Wgu [K, 2N]")
     N = N2 // 2
-    dev = _check_dev(X, Wgu)
+    dev = _check_dev(X, Wgu, Z)
     if Z is None:
         Z = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     if Z.shape != (M, N) or Z.dtype != torch.bfloat16:
         raise ValueError("Z must be bfloat16 [M, N]")
-    st = _launch(lib().gemm_bf16_swiglu, dev, M, N, K, X.data_ptr(), _ld(X, K), Wgu.data_ptr(), _ld(Wgu, N2),
-                 Z.data_ptr(), _ld(Z, N))
-    if st != 0:
-        raise GemmError(st, "gemm_bf16_swiglu")
-    return Z
+    ldx, ldw, ldz = _ld(X, K), _ld(Wgu, N2), _ld(Z, N)
+    return _gemm("gemm_bf16_swiglu", "gemm_bf16_swiglu",
+                 (M, N, K, X.data_ptr(), ldx, Wgu.data_ptr(), ldw, Z.data_ptr(), ldz), workspace, dev,
+                 _lib.GEMM_OP_BF16_SWIGLU, 1, M, N, K, X, ldx, 0, Wgu, ldw, 0, Z, ldz, 0, _lib.GEMM_OUT_BF16)
 
 
-def gemm_bf16_affine(A, B, C, alpha=1.0, bias=None, beta=0.0):
-    """C := alpha * (A . B) + bias + beta * C in place (gemm_bf16_affine):
-    bfloat16 A [M,K] / B [K,N] or stacks [batch, M, K] / [batch, K, N], C of
-    the matching shape in bfloat16 or float32 (read when beta != 0), bias a
-    bfloat16 vector of N elements or None.  Returns C."""
-    return _affine(A, B, C, alpha, bias, beta, False)
-
-
-def gemm_bf16_nt_affine(A, Bt, C, alpha=1.0, bias=None, beta=0.0):
-    """C := alpha * (A . Bt^T) + bias + beta * C in place
-    (gemm_bf16_nt_affine): Bt [N,K] (or [batch, N, K]) is a linear layer's
-    [out, in] weight; otherwise as gemm_bf16_affine."""
-    return _affine(A, Bt, C, alpha, bias, beta, True)
-
-
-def gemm_bf16_silu_batched(A, B, C=None):
+def gemm_bf16_silu_batched(A, B, C=None, workspace=None):
     """C[b] = bf16(SiLU(bf16(A[b] . B[b]))) for bfloat16 stacks [batch, M, K]
     and [batch, K, N] (gemm_bf16_silu_batched); a batch stride of 0
     broadcasts an operand."""
@@ -349,19 +412,19 @@ def gemm_bf16_silu_batched(A, B, C=None):
     b2, K2, N = B.shape
     if batch != b2 or K != K2:
         raise ValueError("shape mismatch")
-    dev = _check_dev(A, B)
+    dev = _check_dev(A, B, C)
     if C is None:
         C = torch.empty((batch, M, N), dtype=torch.bfloat16, device=dev)
     if tuple(C.shape) != (batch, M, N) or C.dtype != torch.bfloat16:
         raise ValueError("C must be bfloat16 [batch, M, N]")
-    st = _launch(lib().gemm_bf16_silu_batched, dev, batch, M, N, K, A.data_ptr(), _ld(A, K), _bstride(A),
-                 B.data_ptr(), _ld(B, N), _bstride(B), C.data_ptr(), _ld(C, N), _bstride(C))
-    if st != 0:
-        raise GemmError(st, "gemm_bf16_silu_batched")
-    return C
+    lda, ldb, ldc = _ld(A, K), _ld(B, N), _ld(C, N)
+    sA, sB, sC = _bstride(A), _bstride(B), _bstride(C)
+    return _gemm("gemm_bf16_silu_batched", "gemm_bf16_silu_batched",
+                 (batch, M, N, K, A.data_ptr(), lda, sA, B.data_ptr(), ldb, sB, C.data_ptr(), ldc, sC), workspace,
+                 dev, _lib.GEMM_OP_BF16_SILU, batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, _lib.GEMM_OUT_BF16)
 
 
-def gemm_bf16_swiglu_batched(X, Wgu, Z=None):
+def gemm_bf16_swiglu_batched(X, Wgu, Z=None, workspace=None):
     """Z[b] = SwiGLU of X[b] with the merged gate|up weight Wgu[b] [K, 2N]
     (gemm_bf16_swiglu_batched), e.g. the experts of a mixture-of-experts FFN;
     a batch stride of 0 broadcasts an operand."""
@@ -372,27 +435,43 @@ def gemm_bf16_swiglu_batched(X, Wgu, Z=None):
     if batch != b2 or K != K2 or N2 % 2:
         raise ValueError("expected X [batch, M, K] and Wgu [batch, K, 2N]")
     N = N2 // 2
-    dev = _check_dev(X, Wgu)
+    dev = _check_dev(X, Wgu, Z)
     if Z is None:
         Z = torch.empty((batch, M, N), dtype=torch.bfloat16, device=dev)
     if tuple(Z.shape) != (batch, M, N) or Z.dtype != torch.bfloat16:
         raise ValueError("Z must be bfloat16 [batch, M, N]")
-    st = _launch(lib().gemm_bf16_swiglu_batched, dev, batch, M, N, K, X.data_ptr(), _ld(X, K), _bstride(X),
-                 Wgu.data_ptr(), _ld(Wgu, N2), _bstride(Wgu), Z.data_ptr(), _ld(Z, N), _bstride(Z))
-    if st != 0:
-        raise GemmError(st, "gemm_bf16_swiglu_batched")
-    return Z
+    ldx, ldw, ldz = _ld(X, K), _ld(Wgu, N2), _ld(Z, N)
+    sA, sB, sC = _bstride(X), _bstride(Wgu), _bstride(Z)
+    return _gemm("gemm_bf16_swiglu_batched", "gemm_bf16_swiglu_batched",
+                 (batch, M, N, K, X.data_ptr(), ldx, sA, Wgu.data_ptr(), ldw, sB, Z.data_ptr(), ldz, sC), workspace,
+                 dev, _lib.GEMM_OP_BF16_SWIGLU, batch, M, N, K, X, ldx, sA, Wgu, ldw, sB, Z, ldz, sC,
+                 _lib.GEMM_OUT_BF16)
 
 
-def gemm_bf16_tn_affine(At, B, C, alpha=1.0, bias=None, beta=0.0):
+def gemm_bf16_affine(A, B, C, alpha=1.0, bias=None, beta=0.0, workspace=None):
+    """C := alpha * (A . B) + bias + beta * C in place (gemm_bf16_affine):
+    bfloat16 A [M,K] / B [K,N] or stacks [batch, M, K] / [batch, K, N], C of
+    the matching shape in bfloat16 or float32 (read when beta != 0), bias a
+    bfloat16 vector of N elements or None.  Returns C."""
+    return _affine(A, B, C, alpha, bias, beta, False, workspace=workspace)
+
+
+def gemm_bf16_nt_affine(A, Bt, C, alpha=1.0, bias=None, beta=0.0, workspace=None):
+    """C := alpha * (A . Bt^T) + bias + beta * C in place
+    (gemm_bf16_nt_affine): Bt [N,K] (or [batch, N, K]) is a linear layer's
+    [out, in] weight; otherwise as gemm_bf16_affine."""
+    return _affine(A, Bt, C, alpha, bias, beta, True, workspace=workspace)
+
+
+def gemm_bf16_tn_affine(At, B, C, alpha=1.0, bias=None, beta=0.0, workspace=None):
     """C := alpha * (At^T . B) + bias + beta * C in place
     (gemm_bf16_tn_affine): At [K,M] (or [batch, K, M]), e.g. the activations
     of a weight gradient accumulated with beta = 1; otherwise as
     gemm_bf16_affine."""
-    return _affine(At, B, C, alpha, bias, beta, False, a_trans=True)
+    return _affine(At, B, C, alpha, bias, beta, False, a_trans=True, workspace=workspace)
 
 
-def _affine(A, B, C, alpha, bias, beta, b_trans, a_trans=False):
+def _affine(A, B, C, alpha, bias, beta, b_trans, a_trans=False, workspace=None):
     what = "gemm_bf16_nt_affine" if b_trans else "gemm_bf16_tn_affine" if a_trans else "gemm_bf16_affine"
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
         raise TypeError(f"{what} takes bfloat16 operands")
@@ -409,23 +488,25 @@ def _affine(A, B, C, alpha, bias, beta, b_trans, a_trans=False):
         b2, K2, N = B3.shape
     if batch != b2 or K != K2 or tuple(C3.shape) != (batch, M, N):
         raise ValueError("shape mismatch")
-    dev = _check_dev(A, B, C) if bias is None else _check_dev(A, B, C, bias)
+    dev = _check_dev(A, B, C, bias)
     if bias is not None and (bias.dtype != torch.bfloat16 or tuple(bias.shape) != (N,) or
                              (N > 1 and bias.stride(0) != 1)):
         raise ValueError("bias must be a contiguous bfloat16 vector of N elements")
     code = _out_code(C.dtype)
-    fn = lib().gemm_bf16_nt_affine if b_trans else lib().gemm_bf16_tn_affine if a_trans else lib().gemm_bf16_affine
-    st = _launch(fn, dev, batch, M, N, K, A3.data_ptr(), _ld(A3, M if a_trans else K), _bstride(A3),
-                 B3.data_ptr(), _ld(B3, K if b_trans else N), _bstride(B3), float(alpha),
-                 None if bias is None else bias.data_ptr(), float(beta), C3.data_ptr(), _ld(C3, N), _bstride(C3), code)
-    if st != 0:
-        raise GemmError(st, what)
+    op = (_lib.GEMM_OP_BF16_NT_AFFINE if b_trans else _lib.GEMM_OP_BF16_TN_AFFINE if a_trans
+          else _lib.GEMM_OP_BF16_AFFINE)
+    fn = "gemm_bf16_nt_affine" if b_trans else "gemm_bf16_tn_affine" if a_trans else "gemm_bf16_affine"
+    lda, ldb, ldc = _ld(A3, M if a_trans else K), _ld(B3, K if b_trans else N), _ld(C3, N)
+    sA, sB, sC = _bstride(A3), _bstride(B3), _bstride(C3)
+    bp = None if bias is None else bias.data_ptr()
+    _gemm(what, fn, (batch, M, N, K, A3.data_ptr(), lda, sA, B3.data_ptr(), ldb, sB, float(alpha), bp, float(beta),
+                     C3.data_ptr(), ldc, sC, code),
+          workspace, dev, op, batch, M, N, K, A3, lda, sA, B3, ldb, sB, C3, ldc, sC, code,
+          alpha=alpha, bias=bias, beta=beta)
     return C
 
 
-def plan_query(op, M, N, K, batch=1, lda=None, ldb=None, ldc=None, a_addr=0x10000, b_addr=0x20000000,
-               c_addr=0x40000000, sA=None, sB=None, sC=None, c_type=_lib.GEMM_OUT_BF16):
-    """Host-only: the status and plan a call would produce (no GPU work)."""
+def _plan_args(op, M, N, K, batch, lda, ldb, ldc, sA, sB, sC):
     tn = op in (_lib.GEMM_OP_BF16_TN, _lib.GEMM_OP_BF16_TN_AFFINE)
     lda = (M if tn else K) if lda is None else lda
     nt = op in (_lib.GEMM_OP_BF16_NT, _lib.GEMM_OP_FP8_NT, _lib.GEMM_OP_BF16_NT_AFFINE)
@@ -434,7 +515,16 @@ def plan_query(op, M, N, K, batch=1, lda=None, ldb=None, ldc=None, a_addr=0x1000
     sA = (K if tn else M) * lda if sA is None else sA
     sB = (N if nt else K) * ldb if sB is None else sB
     sC = M * ldc if sC is None else sC
+    return lda, ldb, ldc, sA, sB, sC
+
+
+def plan_query(op, M, N, K, batch=1, lda=None, ldb=None, ldc=None, a_addr=0x10000, b_addr=0x20000000,
+               c_addr=0x40000000, sA=None, sB=None, sC=None, c_type=_lib.GEMM_OUT_BF16, with_workspace=True):
+    """Host-only: the status and plan a call would produce (no GPU work):
+    through gemm_run with a workspace (default) or without one (the named
+    entry points)."""
+    lda, ldb, ldc, sA, sB, sC = _plan_args(op, M, N, K, batch, lda, ldb, ldc, sA, sB, sC)
     out = GemmPlan()
-    st = lib().gemm_plan_query(op, batch, M, N, K, a_addr, lda, sA, b_addr, ldb, sB, c_addr, ldc, sC,
-                               c_type, ctypes.byref(out))
+    st = lib().gemm_plan_query_ex(1 if with_workspace else 0, op, batch, M, N, K, a_addr, lda, sA, b_addr, ldb, sB,
+                                  c_addr, ldc, sC, c_type, ctypes.byref(out))
     return st, out

@@ -19,26 +19,26 @@
  * at C + i*ldc + j.  C is overwritten (alpha, beta and a bias are the
  * affine epilogue's, gemm_bf16_affine).
  *
- * Ownership.  The caller owns A, B and C: device pointers on the current
- * HIP device.  Each call validates its arguments on the host, enqueues its
- * kernel(s) on `stream` (a hipStream_t; NULL means the null stream) and
- * returns; completion is observed through the stream.  Calls are
- * thread-safe.  The exceptions to "no allocation" are two workspaces kept
- * per (device, stream): the small-M path and a tiled bf16 call with K split
- * over workgroups (an output with too few tiles to fill the GPU) keep FP32
- * partial sums and arrival counters in the first, and a large bf16 product
- * (from 2^30 multiply-adds) whose A rows are not 16-byte aligned first
- * copies A's rows into the second with 16-byte aligned starts.  Each is
- * allocated with hipMalloc on that stream's first such call (or when a
- * larger call needs more; the stream is synchronised before an old buffer
- * is freed) and kept until the process exits; the counters are zero between
- * calls.  Calls on one stream are ordered, so they never share a workspace
- * at the same time.  If an allocation fails the call runs without it: the
- * whole-K small-M kernel, one workgroup per tile over all of K, or the tiled
- * kernel copying A's rows as they are.  The environment variable
+ * Ownership.  The caller owns all device memory: A, B, C and, for
+ * gemm_run, an optional workspace.  Each call validates its arguments on the
+ * host, enqueues its kernel(s) on `stream` (a hipStream_t; NULL means the
+ * null stream) and returns; completion is observed through the stream.  The
+ * library never allocates, frees, copies or waits for device memory, and
+ * keeps no state beyond a thread-safe cache of each device's architecture;
+ * calls are thread-safe.  Three paths need scratch memory and run only when
+ * the caller passes a workspace to gemm_run: K split over workgroups (the
+ * small-M path and tiled bf16 outputs with too few tiles to fill the GPU;
+ * FP32 partial sums and arrival counters) and the copy of operand rows that
+ * are not 16-byte aligned into aligned rows (large bf16 products, and the
+ * transposed and fused layouts whose kernels read 16-byte rows only).  The
+ * named entry points (gemm_bf16, ...) take none: they run the same
+ * arithmetic on the paths that need no scratch (whole K per workgroup;
+ * operands read as they are), or return GEMM_ERR_UNSUPPORTED where only a
+ * realigned copy could run the call.  The environment variable
  * GEMM_FORCE_KSPLIT=S (diagnostics and tests) forces a split of S slices on
- * calls that use 128x128 tiles (1 = none; GEMM_ERR_UNSUPPORTED when S
- * slices of at least 4 32-deep stages do not fit K).
+ * gemm_run calls with a workspace that use 128x128 tiles (1 = none;
+ * GEMM_ERR_UNSUPPORTED when S slices of at least 4 32-deep stages do not
+ * fit K, or without a workspace).
  * No alignment is required; aligned operands (16-byte rows and pointers)
  * select the faster kernel variants.
  *
@@ -56,8 +56,11 @@
  * batch stride; batch > 1 with strideC < (M-1)*ldc + N (C entries would
  * overlap); or C's byte range overlapping A's or B's.  GEMM_ERR_UNSUPPORTED:
  * a kernel configuration forced through the GEMM_FORCE_CONFIG environment
- * variable cannot run this problem.  GEMM_ERR_NO_DEVICE: no usable HIP device
- * is current.  GEMM_ERR_LAUNCH: the kernel launch failed (hipGetLastError).
+ * variable cannot run this problem, or only a workspace path could and none
+ * was passed.  GEMM_ERR_NO_DEVICE: no HIP device is current, or the current
+ * one is not a gfx950.  GEMM_ERR_LAUNCH: the kernel launch failed
+ * (hipGetLastError).  GEMM_ERR_WORKSPACE: gemm_run was passed a workspace
+ * smaller than gemm_workspace_size reports for the call.
  */
 #ifndef GEMM05_H
 #define GEMM05_H
@@ -73,7 +76,8 @@ typedef enum {
     GEMM_ERR_INVALID_ARG = -1,
     GEMM_ERR_UNSUPPORTED = -2,
     GEMM_ERR_LAUNCH = -3,
-    GEMM_ERR_NO_DEVICE = -4
+    GEMM_ERR_NO_DEVICE = -4,
+    GEMM_ERR_WORKSPACE = -5
 } gemm_status;
 
 /* Output element type of the BF16 entry points. */
@@ -92,8 +96,8 @@ int gemm_sgemm(int64_t M, int64_t N, int64_t K,
 
 /* BF16 GEMM with FP32 accumulation: A [M,K] and B [K,N] hold bf16 bit
  * patterns; C [M,N] is bf16 (c_type GEMM_OUT_BF16) or float (GEMM_OUT_F32).
- * M <= 16 uses the memory-bound small-M (decode) path (see Ownership for
- * its workspace). */
+ * M <= 16 uses the memory-bound small-M (decode) path; with a workspace
+ * (gemm_run) its K split over workgroups. */
 int gemm_bf16(int64_t M, int64_t N, int64_t K,
               const uint16_t *A, int64_t lda,
               const uint16_t *B, int64_t ldb,
@@ -117,9 +121,10 @@ int gemm_bf16_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
  * attention named in §1.2 of page "4.1 Tối ưu hiệu năng toán tử GEMM trên
  * CUDA"): no transposed copy of B is needed.  Everything else follows
  * gemm_bf16 / gemm_bf16_batched (strideBt is the batch stride of Bt), except
- * that small M runs on the tiled kernels, and Bt rows that are not 16-byte
- * aligned are first copied to aligned rows in the workspace described under
- * Ownership (GEMM_ERR_UNSUPPORTED if that allocation fails). */
+ * that M <= 16 with 16-byte aligned Bt rows runs a small-M kernel of its
+ * own, and Bt rows that are not 16-byte aligned need a workspace
+ * (gemm_run), into which they are first copied to aligned rows
+ * (GEMM_ERR_UNSUPPORTED without one). */
 int gemm_bf16_nt(int64_t M, int64_t N, int64_t K,
                  const uint16_t *A, int64_t lda,
                  const uint16_t *Bt, int64_t ldbt,
@@ -139,8 +144,7 @@ int gemm_bf16_nt_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
  * the batch stride of At), except that every size runs on the tiled
  * kernels, and At rows that are not 16-byte aligned, or M not a multiple
  * of 8, are first copied to aligned rows of ceil(M/8)*8 elements (zero
- * padded) in the workspace described under Ownership
- * (GEMM_ERR_UNSUPPORTED if that allocation fails). */
+ * padded) in a workspace (gemm_run; GEMM_ERR_UNSUPPORTED without one). */
 int gemm_bf16_tn(int64_t M, int64_t N, int64_t K,
                  const uint16_t *At, int64_t ldat,
                  const uint16_t *B, int64_t ldb,
@@ -211,9 +215,10 @@ int gemm_fp8_nt(int64_t M, int64_t N, int64_t K,
  * with these additions.  GEMM_ERR_UNSUPPORTED: the output rows are not
  * 16-byte aligned (C or Z pointer and ldc/ldz), N is not a multiple of 8,
  * or no LDS-ring kernel can run the call (B rows not 16-byte aligned, or an
- * operand spanning 2 GiB or more).  A's rows, when not 16-byte aligned, are
- * first copied to aligned rows in the workspace described under Ownership,
- * at any size of the product.  K == 0 writes zeros (SiLU(0) = 0).
+ * operand spanning 2 GiB or more, or A rows only 2-byte aligned without a
+ * workspace).  With a workspace (gemm_run) A's rows, when not 16-byte
+ * aligned, are first copied to aligned rows, at any size of the product.
+ * K == 0 writes zeros (SiLU(0) = 0).
  */
 
 /* C [M,N] := bf16(SiLU(bf16(A.B))): A [M,K], B [K,N] as in gemm_bf16. */
@@ -270,9 +275,9 @@ int gemm_bf16_swiglu_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
  * epilogues above (16-byte aligned rows of C, N % 8 == 0, B rows 16-byte
  * aligned) when a product is formed on the tiled kernels.  M <= 16 runs
  * the small-M kernels of gemm_bf16, whose final store applies the same
- * formula (there B may have any alignment).  Small outputs split K over
- * workgroups as gemm_bf16 does (the workgroup that completes a tile applies
- * the epilogue, once).
+ * formula (there B may have any alignment).  With a workspace (gemm_run),
+ * small outputs split K over workgroups as gemm_bf16 does (the workgroup
+ * that completes a tile applies the epilogue, once).
  */
 int gemm_bf16_affine(int64_t batch, int64_t M, int64_t N, int64_t K,
                      const uint16_t *A, int64_t lda, int64_t strideA,
@@ -307,6 +312,44 @@ int gemm_bf16_tn_affine(int64_t batch, int64_t M, int64_t N, int64_t K,
                         void *C, int64_t ldc, int64_t strideC, int c_type,
                         void *stream);
 
+/* ---- one entry point for every operation, with a caller workspace --------
+ *
+ * gemm_run performs the call that the named entry point of `op` (a
+ * gemm_op, below) would, with the same arguments and semantics, and may in
+ * addition use `workspace`: device memory of `workspace_bytes` bytes on the
+ * current device, owned by the caller, 256-byte aligned, holding at least
+ * what gemm_workspace_size reports for the same call (GEMM_ERR_WORKSPACE
+ * otherwise; NULL runs the call without scratch, exactly as the named entry
+ * point).  Its first 64 KiB are arrival counters: they must be zero before a
+ * workspace is first used (e.g. zero-filled at allocation) and every call
+ * leaves them zero when it completes; the rest needs no initial value.
+ * A workspace serves one call at a time: calls that may overlap in time
+ * (on different streams) need different workspaces; calls on one stream
+ * may share one.
+ * Arguments: A, lda, strideA and B, ldb, strideB as the op's entry point
+ * names them (A = At for the TN ops, B = Bt for the NT and FP8 ops, B = Wgu
+ * for SwiGLU), batch 1 for the ops without a batched form (gemm_sgemm,
+ * gemm_fp8_nt); c_type is ignored where the op fixes it (SGEMM: float;
+ * SiLU, SwiGLU: bf16); alpha, bias and beta are read by the affine ops only,
+ * scale_a and scale_b by GEMM_OP_FP8_NT only. */
+int gemm_run(int op, int64_t batch, int64_t M, int64_t N, int64_t K,
+             const void *A, int64_t lda, int64_t strideA,
+             const void *B, int64_t ldb, int64_t strideB,
+             void *C, int64_t ldc, int64_t strideC, int c_type,
+             float alpha, const uint16_t *bias, float beta,
+             const float *scale_a, const float *scale_b,
+             void *workspace, uint64_t workspace_bytes,
+             void *stream);
+
+/* Workspace bytes gemm_run needs for a call (0: none; host only, no GPU
+ * work).  Arguments as gemm_plan_query; writes *bytes and returns the
+ * validation status. */
+int gemm_workspace_size(int op, int64_t batch, int64_t M, int64_t N, int64_t K,
+                        uint64_t a_addr, int64_t lda, int64_t strideA,
+                        uint64_t b_addr, int64_t ldb, int64_t strideB,
+                        uint64_t c_addr, int64_t ldc, int64_t strideC,
+                        int c_type, uint64_t *bytes);
+
 /* Static, NUL-terminated description of a status code. */
 const char *gemm_status_string(int status);
 
@@ -340,11 +383,12 @@ typedef struct {
     int64_t lds_bytes; /* LDS per workgroup */
     double model_bytes;/* traffic model of "Operator & Runtime" §5.2.2 for the chosen tile */
     char name[48];     /* configuration name, as accepted by GEMM_FORCE_CONFIG */
-    int64_t workspace_bytes; /* library-owned workspace the call needs: partial
-                                sums and arrival counters of the split small-M
-                                path or of a K-split tiled call, and the
-                                realigned copy of A (batch x M rows of K
-                                rounded up to 8 bf16); else 0 */
+    int64_t workspace_bytes; /* workspace the planned call needs (gemm_run):
+                                64 KiB of arrival counters plus the partial
+                                sums of the split small-M path or of a
+                                K-split tiled call and the realigned row
+                                copies of A and Bt, each rounded up to 256
+                                bytes; 0 when it needs none */
     int ksplit;        /* tiled bf16 calls: workgroups sharing each output
                           tile's K range (1: no split); grid counts them all */
 } gemm_plan;
@@ -364,16 +408,23 @@ typedef enum {
     GEMM_OP_BF16_TN_AFFINE = 9  /* gemm_bf16_tn_affine with alpha = 1 (a = At, lda = ldat) */
 } gemm_op;
 
-/* Validate the arguments of a call and report the plan it would launch,
- * without touching the GPU.  Pointers are passed as integers (their values
- * only decide alignment and overlap).  Returns the status the entry point
- * would return from validation (GEMM_OK, GEMM_ERR_INVALID_ARG or
- * GEMM_ERR_UNSUPPORTED); `out` may be NULL. */
+/* Validate the arguments of a call and report the plan gemm_run launches
+ * for it with a sufficient workspace, without touching the GPU.  Pointers
+ * are passed as integers (their values only decide alignment and overlap).
+ * Returns the status the call would return from validation (GEMM_OK,
+ * GEMM_ERR_INVALID_ARG or GEMM_ERR_UNSUPPORTED); `out` may be NULL. */
 int gemm_plan_query(int op, int64_t batch, int64_t M, int64_t N, int64_t K,
                     uint64_t a_addr, int64_t lda, int64_t strideA,
                     uint64_t b_addr, int64_t ldb, int64_t strideB,
                     uint64_t c_addr, int64_t ldc, int64_t strideC,
                     int c_type, gemm_plan *out);
+/* The same, for a call with (with_workspace != 0) or without a workspace:
+ * the named entry points run the plan without. */
+int gemm_plan_query_ex(int with_workspace, int op, int64_t batch, int64_t M, int64_t N, int64_t K,
+                       uint64_t a_addr, int64_t lda, int64_t strideA,
+                       uint64_t b_addr, int64_t ldb, int64_t strideB,
+                       uint64_t c_addr, int64_t ldc, int64_t strideC,
+                       int c_type, gemm_plan *out);
 
 /* Tile traffic model of "Operator & Runtime" §5.2.2 (Example 5-3): for an
  * m x n output tile with reduction slab k and element size e bytes (FP32

@@ -117,3 +117,16 @@ def check_affine(C, ref, P, K, alpha, bias_vals, beta, old_vals, out_f32, amax=0
         acc = abs(alpha) * (2.0 ** -9 * np.abs(P) + 1e-3 * math.sqrt(max(K, 1)))
         bound = 2.0 ** -8 * np.abs(ref) + acc + 2.0 ** -20 * mags
     return _check(C, ref, np.broadcast_to(bound, ref.shape), what)
+
+
+_WS = None
+
+
+def ws():
+    """The test process's workspace (caller-owned scratch for gemm_run),
+    created on first use on the current device and grown as calls need."""
+    global _WS
+    if _WS is None:
+        import dense_gemm_05_amd as g5
+        _WS = g5.Workspace()
+    return _WS

@@ -36,9 +36,17 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         assert g5.status_string(st).startswith("GEMM_")
     assert "unknown" in g5.status_string(7)
+
+
+def ws_bytes(part=0, rows_a=0, rows_b=0):
+    """Workspace a plan needs (include/gemm05.h, gemm_run): 64 KiB of arrival
+    counters, then the partial sums and the realigned row copies, each
+    rounded up to 256 bytes; nothing when none of them is needed."""
+    r = lambda b: (b + 255) // 256 * 256
+    return 0 if part == rows_a == rows_b == 0 else 65536 + r(part) + r(rows_a) + r(rows_b)
 
 
 P = 0x7F0000000000  # fake, well-aligned, non-overlapping addresses (never dereferenced)
@@ -128,7 +136,7 @@ def test_selector_choices_for_the_workloads(L):
     for M in (1, 4, 16):
         st, p = g5.plan_query(g5.GEMM_OP_BF16, M, 12288, 4096)
         assert st == 0 and p.family == 4 and p.name == b"decode_splitk" and p.grid == 96 * 2
-        assert p.variant == 1 and p.workspace_bytes == 96 * 2 * 16 * 128 * 4 + 96 * 4
+        assert p.variant == 1 and p.workspace_bytes == ws_bytes(96 * 2 * 16 * 128 * 4)
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 4, 12290, 4096)
     assert st == 0 and p.name == b"decode_64" and p.variant == 0 and p.workspace_bytes == 0
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 1, 32768, 4096)     # 256 strips: one slice, whole-K path
@@ -149,7 +157,7 @@ def test_selector_choices_for_the_workloads(L):
     # the slices' FP32 tiles and a counter per tile in the workspace)
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 1024, 1536, 4096)
     assert st == 0 and p.name == b"bf16_128x128" and p.ksplit == 2 and p.grid == 192
-    assert p.workspace_bytes == 96 * 2 * 128 * 128 * 4 + 96 * 4
+    assert p.workspace_bytes == ws_bytes(96 * 2 * 128 * 128 * 4)
     st, p = g5.plan_query(g5.GEMM_OP_SGEMM, 4096, 4096, 4096)
     assert st == 0 and p.family == 3 and p.even == 1
     # FP32 256^3: 32x32 tiles with all of K staged at once; K = 288 (9 slabs)
@@ -166,7 +174,7 @@ def test_selector_choices_for_the_workloads(L):
     # and the masked ring kernel copies A 16 bytes per lane (variant 2)
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 1000, 12280, 4100, c_type=1)
     assert st == 0 and p.family == 2 and p.even == 0 and p.vec_a == 16 and p.vec_b == 16
-    assert p.variant == 2 and p.workspace_bytes == 1000 * 4104 * 2
+    assert p.variant == 2 and p.workspace_bytes == ws_bytes(0, 1000 * 4104 * 2)
     # a small product keeps A as it is (4-byte copies, variant 3)
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 300, 392, 262)
     assert st == 0 and p.variant == 3 and p.vec_a == 4 and p.workspace_bytes == 0
@@ -252,7 +260,7 @@ def test_split_small_m_workspace_covers_every_slot(M, N, K, batch):
     assert p.grid == strips * ks * batch and 2 <= ks <= 8
     top_slot = ((batch - 1) * strips + strips - 1) * ks + ks - 1
     top_cnt = (batch - 1) * strips + strips - 1
-    assert (top_slot + 1) * 16 * 128 * 4 + (top_cnt + 1) * 4 <= p.workspace_bytes
+    assert (top_cnt + 1) * 4 <= 65536 and 65536 + (top_slot + 1) * 16 * 128 * 4 <= p.workspace_bytes
 
 
 def call_fused(L, op, M, N, K, a=A_ADDR, lda=None, b=B_ADDR, ldb=None, c=C_ADDR, ldc=None):
@@ -299,7 +307,7 @@ def test_fused_plans(L):
         st, p = g5.plan_query(op, 300, 392, 264, lda=272, ldb=nb + 8, ldc=400)
         assert st == 0 and p.variant == 2
         st, p = g5.plan_query(op, 257, 96, 33)
-        assert st == 0 and p.variant == 2 and p.workspace_bytes == 257 * 40 * 2
+        assert st == 0 and p.variant == 2 and p.workspace_bytes == ws_bytes(0, 257 * 40 * 2)
     st, p = g5.plan_query(g5.GEMM_OP_BF16_SWIGLU, 1024, 12288, 4096)
     assert st == 0 and p.name == b"bf16_256x192" and p.grid == 4 * 128 and p.variant == 1
     st, p = g5.plan_query(g5.GEMM_OP_BF16_SILU, 1024, 12288, 4096)
@@ -504,7 +512,7 @@ def test_affine_plans(L):
     st, p = g5.plan_query(op, 300, 392, 261, lda=266, ldb=400, ldc=400, batch=3)
     assert st == 0 and p.variant == 3
     st, p = g5.plan_query(op, 257, 96, 33)
-    assert st == 0 and p.variant == 2 and p.workspace_bytes == 257 * 40 * 2        # A realigned
+    assert st == 0 and p.variant == 2 and p.workspace_bytes == ws_bytes(0, 257 * 40 * 2)        # A realigned
 
 
 def test_nt_affine_plans(L):
@@ -563,3 +571,69 @@ def test_tn_affine_plans(L):
     assert L.gemm_bf16_tn_affine(*args, float("inf"), None, 1.0, C_ADDR, 8, 64, 0, None) == g5.GEMM_ERR_INVALID_ARG
     assert L.gemm_bf16_tn_affine(1, 8, 8, 16, A_ADDR, 7, 128, B_ADDR, 8, 128, 1.0, None, 1.0, C_ADDR, 8, 64, 0,
                                  None) == g5.GEMM_ERR_INVALID_ARG          # ldat < M
+
+
+# ---- the ownership contract: caller workspaces, nothing allocated inside ----
+
+def test_named_calls_plan_without_workspace(L):
+    """The named entry points run the plans of a call without a workspace:
+    whole K per workgroup (no split small-M path, no K split over
+    workgroups) and no realigned row copies."""
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 1, 12288, 4096, with_workspace=False)
+    assert st == 0 and p.name == b"decode_64" and p.workspace_bytes == 0
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 1024, 1536, 4096, with_workspace=False)
+    assert st == 0 and p.ksplit == 1 and p.workspace_bytes == 0
+    # ragged 1000x12280x4100: A rows (8200 bytes) realigned only with a workspace
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 1000, 12280, 4100, c_type=1, with_workspace=False)
+    assert st == 0 and p.variant == 3 and p.workspace_bytes == 0
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 1000, 12280, 4100, c_type=1)
+    assert st == 0 and p.variant == 2 and p.workspace_bytes == ws_bytes(0, 1000 * 4104 * 2)
+    # a fused epilogue with 2-byte aligned A rows runs only from a realigned copy
+    st, _ = g5.plan_query(g5.GEMM_OP_BF16_SILU, 300, 256, 130, lda=131, with_workspace=False)
+    assert st == g5.GEMM_ERR_UNSUPPORTED
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_SILU, 300, 256, 130, lda=131)
+    assert st == 0 and p.workspace_bytes > 0
+    # GEMM_FORCE_KSPLIT needs a workspace
+    for M, N, K in ((1024, 1536, 4096), (4096, 4096, 4096)):
+        st, p = g5.plan_query(g5.GEMM_OP_BF16, M, N, K, with_workspace=False)
+        assert st == 0 and p.ksplit == 1
+
+
+def test_workspace_size_matches_plan(L):
+    for args in ((g5.GEMM_OP_BF16, 1, 1, 12288, 4096), (g5.GEMM_OP_BF16, 1, 1024, 1536, 4096),
+                 (g5.GEMM_OP_BF16, 1, 1024, 12288, 4096), (g5.GEMM_OP_BF16_TN, 1, 300, 392, 262)):
+        op, batch, M, N, K = args
+        st, p = g5.plan_query(op, M, N, K, batch=batch)
+        lda, ldb, ldc, sA, sB, sC = g5.gemm._plan_args(op, M, N, K, batch, None, None, None, None, None, None)
+        n = g5.workspace_size(op, batch, M, N, K, 0x10000, lda, sA, 0x20000000, ldb, sB, 0x40000000, ldc, sC, 0)
+        assert st == 0 and n == p.workspace_bytes
+
+
+def test_run_rejects_small_or_unaligned_workspace(L):
+    """gemm_run checks the workspace on the host, before any GPU call: too
+    small is GEMM_ERR_WORKSPACE, not 256-byte aligned GEMM_ERR_INVALID_ARG
+    (fake device addresses; nothing is enqueued)."""
+    M, N, K = 1, 12288, 4096
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
+    need = p.workspace_bytes
+    assert need > 65536
+    WS = P + (3 << 34)
+    run = lambda ws, n: L.gemm_run(g5.GEMM_OP_BF16, 1, M, N, K, A_ADDR, K, 0, B_ADDR, N, 0, C_ADDR, N, 0, 0,
+                                   1.0, None, 0.0, None, None, ws, n, None)
+    assert run(WS, need - 1) == g5.GEMM_ERR_WORKSPACE
+    assert run(WS + 16, need) == g5.GEMM_ERR_INVALID_ARG
+    assert L.gemm_run(99, 1, M, N, K, A_ADDR, K, 0, B_ADDR, N, 0, C_ADDR, N, 0, 0, 1.0, None, 0.0, None, None,
+                      None, 0, None) == g5.GEMM_ERR_INVALID_ARG
+
+
+def test_library_source_allocates_nothing():
+    """The library's sources name no allocation, free, copy or
+    synchronisation call: the caller owns every byte of device memory."""
+    csrc = os.path.join(ROOT, "dense_gemm_05_amd", "csrc")
+    banned = re.compile(r"\bhip(Malloc|MallocAsync|Free|FreeAsync|HostMalloc|Memcpy\w*|Memset\w*|StreamSynchronize|"
+                        r"DeviceSynchronize|EventSynchronize|ExtMallocWithFlags|MallocManaged)\b")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".cpp", ".hip", ".h")):
+            with open(os.path.join(csrc, name)) as fh:
+                for i, line in enumerate(fh, 1):
+                    assert not banned.search(line), f"{name}:{i}: {line.strip()}"

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import gemm_inputs as gi
-from _gpu_helpers import amax_bf16, check_affine, dev_bf16, dev_f32, host_values
+from _gpu_helpers import amax_bf16, check_affine, dev_bf16, dev_f32, host_values, ws
 
 import dense_gemm_05_amd as g5
 
@@ -48,7 +48,7 @@ def _run_and_check(oracle_mod, A, B, bias, old32, old16, alpha, beta, out_f32, w
     dbias = dev_bf16(bias) if use_bias else None
     C = dev_f32(old32) if out_f32 else dev_bf16(old16)
     g5.gemm_bf16_affine(dA if batch > 1 else dA[0], dB if batch > 1 else dB[0], C if batch > 1 else C[0],
-                        alpha=alpha, bias=dbias, beta=beta)
+                        alpha=alpha, bias=dbias, beta=beta, workspace=ws())
     got = host_values(C)
     bias_vals = gi.bf16_bits_to_f32(bias).astype(np.float64) if use_bias else np.zeros(N)
     worst = 0.0
@@ -102,7 +102,7 @@ def test_affine_every_config(oracle_mod, monkeypatch, cfg):
         Cfull[:, :N] = dev_bf16(old)
         monkeypatch.setenv("GEMM_FORCE_CONFIG", cfg)
         g5.gemm_bf16_affine(dev_bf16(A)[:, :K], dev_bf16(B)[:, :N], Cfull[:, :N], alpha=1.5, bias=dev_bf16(bias),
-                            beta=-0.5)
+                            beta=-0.5, workspace=ws())
         monkeypatch.delenv("GEMM_FORCE_CONFIG")
         host = host_values(Cfull)
         Av, Bv = np.ascontiguousarray(A[:, :K]), np.ascontiguousarray(B[:, :N])
@@ -135,7 +135,7 @@ def test_affine_batched_broadcast(oracle_mod):
     B = np.broadcast_to(B[:1], B.shape).copy()
     dA, dB1 = dev_bf16(A), dev_bf16(B[0])
     C = dev_bf16(old16)
-    g5.gemm_bf16_affine(dA, dB1.unsqueeze(0).expand(3, -1, -1), C, alpha=1.0, bias=dev_bf16(bias), beta=1.0)
+    g5.gemm_bf16_affine(dA, dB1.unsqueeze(0).expand(3, -1, -1), C, alpha=1.0, bias=dev_bf16(bias), beta=1.0, workspace=ws())
     got = host_values(C)
     for b in range(3):
         ref = oracle_mod.gemm_bf16_affine(A[b], B[b], 1.0, bias, 1.0, old16[b])
@@ -157,17 +157,17 @@ def test_affine_without_product():
     nanA = torch.full((M, K), float("nan"), device="cuda", dtype=torch.bfloat16)
     nanB = torch.full((K, N), float("nan"), device="cuda", dtype=torch.bfloat16)
     C = dev_f32(old)
-    g5.gemm_bf16_affine(nanA, nanB, C, alpha=0.0, bias=dev_bf16(bias), beta=-2.0)
+    g5.gemm_bf16_affine(nanA, nanB, C, alpha=0.0, bias=dev_bf16(bias), beta=-2.0, workspace=ws())
     assert np.array_equal(host_values(C).astype(np.float32), want)
     C = dev_f32(old)
-    g5.gemm_bf16_affine(nanA[:, :0], nanB[:0], C, alpha=3.0, bias=dev_bf16(bias), beta=-2.0)
+    g5.gemm_bf16_affine(nanA[:, :0], nanB[:0], C, alpha=3.0, bias=dev_bf16(bias), beta=-2.0, workspace=ws())
     assert np.array_equal(host_values(C).astype(np.float32), want)
     Cb = torch.full((M, N), float("nan"), device="cuda", dtype=torch.bfloat16)
-    g5.gemm_bf16_affine(nanA[:, :0], nanB[:0], Cb, alpha=1.0, bias=dev_bf16(bias), beta=0.0)
+    g5.gemm_bf16_affine(nanA[:, :0], nanB[:0], Cb, alpha=1.0, bias=dev_bf16(bias), beta=0.0, workspace=ws())
     assert np.array_equal(host_values(Cb), np.broadcast_to(bv, (M, N)).astype(np.float64))
     A, B, _, _, _ = _case(M, N, K, 5)
     Cn = torch.full((M, N), float("nan"), device="cuda", dtype=torch.float32)
-    g5.gemm_bf16_affine(dev_bf16(A[0]), dev_bf16(B[0]), Cn, alpha=1.0, bias=None, beta=0.0)
+    g5.gemm_bf16_affine(dev_bf16(A[0]), dev_bf16(B[0]), Cn, alpha=1.0, bias=None, beta=0.0, workspace=ws())
     assert torch.isfinite(Cn).all()
 
 
@@ -181,9 +181,9 @@ def test_affine_identity_matches_plain_product(monkeypatch, S):
     monkeypatch.setenv("GEMM_FORCE_CONFIG", "bf16_128x128")
     monkeypatch.setenv("GEMM_FORCE_KSPLIT", str(S))
     for out in (torch.bfloat16, torch.float32):
-        plain = g5.gemm_bf16(dA, dB, out_dtype=out)
+        plain = g5.gemm_bf16(dA, dB, out_dtype=out, workspace=ws())
         C = torch.empty_like(plain)
-        g5.gemm_bf16_affine(dA, dB, C)
+        g5.gemm_bf16_affine(dA, dB, C, workspace=ws())
         assert torch.equal(C.float(), plain.float()), out
 
 
@@ -206,8 +206,8 @@ def test_affine_small_m_rows_do_not_depend_on_m():
     dA, dB, db = dev_bf16(A[0]), dev_bf16(B[0]), dev_bf16(bias)
     C16 = dev_bf16(old16[0])
     C1 = dev_bf16(old16[0][:1])
-    g5.gemm_bf16_affine(dA, dB, C16, alpha=0.5, bias=db, beta=1.0)
-    g5.gemm_bf16_affine(dA[:1], dB, C1, alpha=0.5, bias=db, beta=1.0)
+    g5.gemm_bf16_affine(dA, dB, C16, alpha=0.5, bias=db, beta=1.0, workspace=ws())
+    g5.gemm_bf16_affine(dA[:1], dB, C1, alpha=0.5, bias=db, beta=1.0, workspace=ws())
     assert torch.equal(C1.view(torch.int16), C16[:1].view(torch.int16))
 
 
@@ -221,7 +221,7 @@ def test_affine_ffn_full_size(oracle_mod):
     bias = gi.to_bf16_bits(gi.normal(g, (12288,)))
     res = gi.to_bf16_bits(gi.normal(g, (1024, 12288)))
     C = dev_bf16(res)
-    g5.gemm_bf16_affine(dev_bf16(X), dev_bf16(W), C, alpha=1.0, bias=dev_bf16(bias), beta=1.0)
+    g5.gemm_bf16_affine(dev_bf16(X), dev_bf16(W), C, alpha=1.0, bias=dev_bf16(bias), beta=1.0, workspace=ws())
     rows = np.array([0, 255, 256, 700, 1023])
     Xs = np.ascontiguousarray(X[rows])
     ref = oracle_mod.gemm_bf16_affine(Xs, W, 1.0, bias, 1.0, np.ascontiguousarray(res[rows]))
@@ -258,7 +258,7 @@ def test_nt_affine_ragged(oracle_mod, monkeypatch, cfg, M, N, K, pb):
     for out_f32 in (False, True):
         _say(f"nt affine {cfg} {M}x{N}x{K} out_f32={out_f32}")
         C = dev_f32(old32) if out_f32 else dev_bf16(old16)
-        g5.gemm_bf16_nt_affine(dev_bf16(A), dev_bf16(Bt)[:, :K], C, alpha=0.75, bias=dev_bf16(bias), beta=1.0)
+        g5.gemm_bf16_nt_affine(dev_bf16(A), dev_bf16(Bt)[:, :K], C, alpha=0.75, bias=dev_bf16(bias), beta=1.0, workspace=ws())
         _nt_check(oracle_mod, A, np.ascontiguousarray(Bt[:, :K]), bias, old32 if out_f32 else old16, 0.75, 1.0,
                   host_values(C), out_f32, f"nt affine {cfg}")
 
@@ -274,7 +274,7 @@ def test_nt_affine_ksplit(oracle_mod, monkeypatch, S):
     monkeypatch.setenv("GEMM_FORCE_CONFIG", "bf16_128x128")
     monkeypatch.setenv("GEMM_FORCE_KSPLIT", str(S))
     C = dev_f32(old)
-    g5.gemm_bf16_nt_affine(dev_bf16(A), dev_bf16(Bt), C, alpha=1.0, bias=dev_bf16(bias), beta=-0.5)
+    g5.gemm_bf16_nt_affine(dev_bf16(A), dev_bf16(Bt), C, alpha=1.0, bias=dev_bf16(bias), beta=-0.5, workspace=ws())
     _nt_check(oracle_mod, A, Bt, bias, old, 1.0, -0.5, host_values(C), True, f"nt affine split {S}")
 
 
@@ -296,9 +296,9 @@ def test_nt_affine_small_m(oracle_mod, M, N, K, batch):
         C = dev_f32(old32) if out_f32 else dev_bf16(old16)
         dA, dB = dev_bf16(A), dev_bf16(Bt)
         if batch == 1:
-            g5.gemm_bf16_nt_affine(dA[0], dB[0], C[0], alpha=1.0, bias=dev_bf16(bias), beta=1.0)
+            g5.gemm_bf16_nt_affine(dA[0], dB[0], C[0], alpha=1.0, bias=dev_bf16(bias), beta=1.0, workspace=ws())
         else:
-            g5.gemm_bf16_nt_affine(dA, dB, C, alpha=1.0, bias=dev_bf16(bias), beta=1.0)
+            g5.gemm_bf16_nt_affine(dA, dB, C, alpha=1.0, bias=dev_bf16(bias), beta=1.0, workspace=ws())
         got = host_values(C)
         for b in range(batch):
             _nt_check(oracle_mod, A[b], Bt[b], bias, (old32 if out_f32 else old16)[b], 1.0, 1.0, got[b], out_f32,
@@ -315,7 +315,7 @@ def test_nt_affine_linear_layer_full_size(oracle_mod):
     bias = gi.to_bf16_bits(gi.normal(g, (12288,)))
     res = gi.to_bf16_bits(gi.normal(g, (1024, 12288)))
     C = dev_bf16(res)
-    g5.gemm_bf16_nt_affine(dev_bf16(X), dev_bf16(Wt), C, alpha=1.0, bias=dev_bf16(bias), beta=1.0)
+    g5.gemm_bf16_nt_affine(dev_bf16(X), dev_bf16(Wt), C, alpha=1.0, bias=dev_bf16(bias), beta=1.0, workspace=ws())
     rows = np.array([0, 255, 256, 700, 1023])
     _nt_check(oracle_mod, np.ascontiguousarray(X[rows]), Wt, bias, np.ascontiguousarray(res[rows]), 1.0, 1.0,
               host_values(C)[rows], False, "nt affine FFN rows")
@@ -340,7 +340,7 @@ def test_tn_affine_ragged(oracle_mod, monkeypatch, cfg, M, N, K, pa):
     for out_f32 in (False, True):
         _say(f"tn affine {cfg} {M}x{N}x{K} out_f32={out_f32}")
         C = dev_f32(old32) if out_f32 else dev_bf16(old16)
-        g5.gemm_bf16_tn_affine(dev_bf16(At)[:, :M], dev_bf16(B), C, alpha=-1.5, bias=dev_bf16(bias), beta=0.5)
+        g5.gemm_bf16_tn_affine(dev_bf16(At)[:, :M], dev_bf16(B), C, alpha=-1.5, bias=dev_bf16(bias), beta=0.5, workspace=ws())
         old = old32 if out_f32 else old16
         ref = oracle_mod.gemm_bf16_affine(A, B, -1.5, bias, 0.5, old)
         old_vals = old.astype(np.float64) if out_f32 else gi.bf16_bits_to_f32(old).astype(np.float64)
@@ -359,7 +359,7 @@ def test_tn_affine_ksplit(oracle_mod, monkeypatch, S):
     monkeypatch.setenv("GEMM_FORCE_CONFIG", "bf16_128x128")
     monkeypatch.setenv("GEMM_FORCE_KSPLIT", str(S))
     C = dev_f32(old)
-    g5.gemm_bf16_tn_affine(dev_bf16(At), dev_bf16(B), C, alpha=1.0, bias=None, beta=1.0)
+    g5.gemm_bf16_tn_affine(dev_bf16(At), dev_bf16(B), C, alpha=1.0, bias=None, beta=1.0, workspace=ws())
     ref = oracle_mod.gemm_bf16_affine(A, B, 1.0, None, 1.0, old)
     check_affine(host_values(C), ref, oracle_mod.gemm_bf16(A, B), 1024, 1.0, np.zeros(264), 1.0,
                  old.astype(np.float64), True, amax_bf16(A), amax_bf16(B), f"tn affine split {S}")
@@ -374,8 +374,8 @@ def test_tn_affine_gradient_accumulation_full_size(oracle_mod):
     dW0 = gi.normal(g, (4096, 12288))
     dX, dD = dev_bf16(X), dev_bf16(dY)
     C = dev_f32(dW0)
-    g5.gemm_bf16_tn_affine(dX, dD, C, alpha=1.0, bias=None, beta=1.0)
-    g5.gemm_bf16_tn_affine(dX, dD, C, alpha=1.0, bias=None, beta=1.0)
+    g5.gemm_bf16_tn_affine(dX, dD, C, alpha=1.0, bias=None, beta=1.0, workspace=ws())
+    g5.gemm_bf16_tn_affine(dX, dD, C, alpha=1.0, bias=None, beta=1.0, workspace=ws())
     rows = np.array([0, 255, 256, 2047, 4095])
     Xs = np.ascontiguousarray(X[:, rows].T)
     P = oracle_mod.gemm_bf16(Xs, dY)

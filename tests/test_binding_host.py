@@ -1,0 +1,89 @@
+"""Host-side checks of the Python binding (no GPU): every tensor a kernel
+reads or writes -- operands, outputs, codes, scales, bias, workspace -- is
+checked to be on the operands' GPU before the library is called."""
+import pytest
+import torch
+
+import dense_gemm_05_amd as g5
+from dense_gemm_05_amd import gemm as gm
+
+
+class FakeGpuTensor:
+    """Just enough of a tensor for the binding's checks, claiming cuda:0."""
+
+    def __init__(self, shape, dtype, device="cuda:0"):
+        self.shape = torch.Size(shape)
+        self.dtype = dtype
+        self.device = torch.device(device)
+
+    def dim(self):
+        return len(self.shape)
+
+    def stride(self, i=None):
+        st, acc = [], 1
+        for n in reversed(self.shape):
+            st.append(acc)
+            acc *= max(n, 1)
+        st = tuple(reversed(st))
+        return st if i is None else st[i]
+
+    def data_ptr(self):
+        return 0x7F0000000000
+
+    def unsqueeze(self, d):
+        s = list(self.shape)
+        s.insert(d, 1)
+        return FakeGpuTensor(s, self.dtype, str(self.device))
+
+    def view(self, dtype):
+        return FakeGpuTensor(self.shape, dtype, str(self.device))
+
+
+@pytest.fixture
+def no_lib(monkeypatch):
+    def boom():
+        raise AssertionError("the library was called")
+    monkeypatch.setattr(gm, "lib", boom)
+
+
+def _bf(*shape):
+    return FakeGpuTensor(shape, torch.bfloat16)
+
+
+def test_host_output_rejected_before_launch(no_lib):
+    A, B = _bf(8, 16), _bf(16, 24)
+    C_cpu = torch.empty((8, 24), dtype=torch.bfloat16)
+    for fn in (g5.gemm_bf16, g5.gemm_bf16_silu):
+        with pytest.raises(ValueError):
+            fn(A, B, C_cpu)
+    with pytest.raises(ValueError):
+        g5.gemm_bf16_nt(A, _bf(24, 16), C_cpu)
+    with pytest.raises(ValueError):
+        g5.gemm_bf16_tn(_bf(16, 8), B, C_cpu)
+    with pytest.raises(ValueError):
+        g5.gemm_bf16_batched(_bf(2, 8, 16), _bf(2, 16, 24), torch.empty((2, 8, 24), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        g5.gemm_bf16_swiglu(A, _bf(16, 48), C_cpu)
+    with pytest.raises(ValueError):
+        g5.gemm_sgemm(FakeGpuTensor((8, 16), torch.float32), FakeGpuTensor((16, 24), torch.float32),
+                      torch.empty((8, 24)))
+
+
+def test_host_bias_scale_codes_and_workspace_rejected(no_lib):
+    A, B, C = _bf(8, 16), _bf(16, 24), _bf(8, 24)
+    with pytest.raises(ValueError):
+        g5.gemm_bf16_affine(A, B, C, bias=torch.zeros(24, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        g5.gemm_bf16(A, B, C, workspace=torch.zeros(1 << 16, dtype=torch.uint8))
+    X = _bf(4, 32)
+    with pytest.raises(ValueError):
+        g5.gemm_fp8_quantize_rows(X, torch.empty((4, 32), dtype=torch.uint8), None)
+    with pytest.raises(ValueError):
+        g5.gemm_fp8_quantize_rows(X, None, torch.empty(4, dtype=torch.float32))
+    qa, qb = FakeGpuTensor((8, 32), torch.uint8), FakeGpuTensor((24, 32), torch.uint8)
+    with pytest.raises(ValueError):
+        g5.gemm_fp8_nt(qa, torch.ones(8), qb, None, C)
+    with pytest.raises(ValueError):
+        g5.gemm_fp8_nt(qa, None, qb, torch.ones(24), C)
+    with pytest.raises(ValueError):
+        g5.gemm_fp8_nt(qa, None, qb, None, torch.empty((8, 24), dtype=torch.bfloat16))

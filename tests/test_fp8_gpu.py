@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import gemm_inputs as gi
-from _gpu_helpers import dev_bf16, host_values
+from _gpu_helpers import dev_bf16, host_values, ws
 
 import dense_gemm_05_amd as g5
 
@@ -140,7 +140,7 @@ def test_fp8_nt_parity(oracle_mod, monkeypatch, cfg, M, N, K, pa, pb, scales):
     am, bm = _amax(oracle_mod, A[:, :K], sa), _amax(oracle_mod, Bt[:, :K], sb)
     for out, od in (("f32", torch.float32), ("bf16", torch.bfloat16)):
         Cfull = torch.full((M, N + 4), float("nan"), device="cuda", dtype=od)
-        g5.gemm_fp8_nt(dA[:, :K], dsa, dB[:, :K], dsb, Cfull[:, :N])
+        g5.gemm_fp8_nt(dA[:, :K], dsa, dB[:, :K], dsb, Cfull[:, :N], workspace=ws())
         host = host_values(Cfull)
         check_fp8(host[:, :N], ref, K, am, bm, out, f"fp8 {cfg} {out}")
         assert np.all(np.isnan(host[:, N:])), "ldc padding was written"
@@ -153,7 +153,7 @@ def test_fp8_nt_ksplit(oracle_mod, monkeypatch, S):
     monkeypatch.setenv("GEMM_FORCE_CONFIG", "bf16_128x128")
     monkeypatch.setenv("GEMM_FORCE_KSPLIT", str(S))
     C = g5.gemm_fp8_nt(dev_u8(A), torch.from_numpy(sa).cuda(), dev_u8(Bt), torch.from_numpy(sb).cuda(),
-                       out_dtype=torch.float32)
+                       out_dtype=torch.float32, workspace=ws())
     ref = oracle_mod.gemm_fp8_nt(A, sa, Bt, sb)
     check_fp8(host_values(C), ref, K, _amax(oracle_mod, A, sa), _amax(oracle_mod, Bt, sb), "f32", f"fp8 split {S}")
 
@@ -169,7 +169,7 @@ def test_fp8_small_integers_exact(oracle_mod):
     sa = (2.0 ** g.integers(-3, 3, M)).astype(np.float32)
     sb = (2.0 ** g.integers(-3, 3, N)).astype(np.float32)
     C = g5.gemm_fp8_nt(dev_u8(A), torch.from_numpy(sa).cuda(), dev_u8(Bt), torch.from_numpy(sb).cuda(),
-                       out_dtype=torch.float32)
+                       out_dtype=torch.float32, workspace=ws())
     assert np.array_equal(host_values(C), oracle_mod.gemm_fp8_nt(A, sa, Bt, sb))
 
 
@@ -190,7 +190,7 @@ def test_fp8_ffn_end_to_end(oracle_mod):
     assert np.array_equal(qW.cpu().numpy(), rW) and np.array_equal(sW.cpu().numpy(), rsW)
     st, plan = g5.plan_query(g5.GEMM_OP_FP8_NT, 1024, 12288, 4096)
     assert st == 0 and plan.name == b"bf16_256x192" and plan.variant == 1
-    C = g5.gemm_fp8_nt(qX, sX, qW, sW)
+    C = g5.gemm_fp8_nt(qX, sX, qW, sW, workspace=ws())
     ref = oracle_mod.gemm_fp8_nt(np.ascontiguousarray(rX[rows]), rsX[rows], rW, rsW)
     check_fp8(host_values(C)[rows], ref, 4096, _amax(oracle_mod, rX, rsX), _amax(oracle_mod, rW, rsW), "bf16",
               "fp8 FFN rows")
@@ -213,7 +213,7 @@ def test_fp8_nt_small_m(oracle_mod, M, N, K, pb, scales):
     am, bm = _amax(oracle_mod, A, sa), _amax(oracle_mod, Bt[:, :K], sb)
     for out, od in (("f32", torch.float32), ("bf16", torch.bfloat16)):
         Cfull = torch.full((M, N + 4), float("nan"), device="cuda", dtype=od)
-        g5.gemm_fp8_nt(dA, dsa, dB[:, :K], dsb, Cfull[:, :N])
+        g5.gemm_fp8_nt(dA, dsa, dB[:, :K], dsb, Cfull[:, :N], workspace=ws())
         host = host_values(Cfull)
         check_fp8(host[:, :N], ref, K, am, bm, out, f"fp8 small M {out}")
         assert np.all(np.isnan(host[:, N:])), "ldc padding was written"
@@ -232,8 +232,8 @@ def test_fp8_small_m_exact_and_row_invariant(oracle_mod):
     sb = (2.0 ** g.integers(-3, 3, N)).astype(np.float32)
     dA, dB = dev_u8(A), dev_u8(Bt)[:, :K]
     dsa, dsb = torch.from_numpy(sa).cuda(), torch.from_numpy(sb).cuda()
-    c16 = g5.gemm_fp8_nt(dA, dsa, dB, dsb, out_dtype=torch.float32)
+    c16 = g5.gemm_fp8_nt(dA, dsa, dB, dsb, out_dtype=torch.float32, workspace=ws())
     assert np.array_equal(host_values(c16), oracle_mod.gemm_fp8_nt(A, sa, np.ascontiguousarray(Bt[:, :K]), sb))
     for M in (1, 5):
-        cm = g5.gemm_fp8_nt(dA[:M], dsa[:M], dB, dsb, out_dtype=torch.float32)
+        cm = g5.gemm_fp8_nt(dA[:M], dsa[:M], dB, dsb, out_dtype=torch.float32, workspace=ws())
         assert torch.equal(cm.view(torch.int32), c16[:M].view(torch.int32)), f"M={M}"

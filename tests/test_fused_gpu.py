@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import gemm_inputs as gi
-from _gpu_helpers import check_silu, check_swiglu, dev_bf16, host_values
+from _gpu_helpers import check_silu, check_swiglu, dev_bf16, host_values, ws
 
 import dense_gemm_05_amd as g5
 
@@ -50,7 +50,7 @@ SHAPES = [(300, 392, 262), (256, 192, 256), (512, 576, 96), (17, 200, 64), (1, 1
 def test_silu_ragged(oracle_mod, M, N, K):
     _say(f"silu {M}x{N}x{K}")
     A, B = gi.small_case("bf16", M, N, K, seed=21, scale_b=0.125)
-    Y = g5.gemm_bf16_silu(dev_bf16(A), dev_bf16(B))
+    Y = g5.gemm_bf16_silu(dev_bf16(A), dev_bf16(B), workspace=ws())
     G = oracle_mod.gemm_bf16(A, B)
     check_silu(host_values(Y), G, oracle_mod.gemm_bf16_silu(A, B), K, f"silu {M}x{N}x{K}")
 
@@ -59,7 +59,7 @@ def test_silu_ragged(oracle_mod, M, N, K):
 def test_swiglu_ragged(oracle_mod, M, N, K):
     _say(f"swiglu {M}x{N}x{K}")
     X, Wgu = _swiglu_case(M, N, K, 1)
-    Z = g5.gemm_bf16_swiglu(dev_bf16(X), dev_bf16(Wgu))
+    Z = g5.gemm_bf16_swiglu(dev_bf16(X), dev_bf16(Wgu), workspace=ws())
     Zr, G, U, t, u = _swiglu_ref(oracle_mod, X, Wgu)
     check_swiglu(host_values(Z), G, U, t, u, Zr, K, f"swiglu {M}x{N}x{K}")
 
@@ -104,7 +104,7 @@ def test_swiglu_ffn_full_size(oracle_mod):
     X, Wgu = gi.swiglu_inputs()
     st, plan = g5.plan_query(g5.GEMM_OP_BF16_SWIGLU, 1024, 12288, 4096)
     assert st == 0 and plan.name == b"bf16_256x192" and plan.grid == 512 and plan.variant == 1
-    Z = g5.gemm_bf16_swiglu(dev_bf16(X), dev_bf16(Wgu))
+    Z = g5.gemm_bf16_swiglu(dev_bf16(X), dev_bf16(Wgu), workspace=ws())
     rows = np.array([0, 1, 255, 256, 511, 600, 767, 768, 1023])
     Xs = np.ascontiguousarray(X[rows])
     Zr, G, U, t, u = _swiglu_ref(oracle_mod, Xs, Wgu)
@@ -114,7 +114,7 @@ def test_swiglu_ffn_full_size(oracle_mod):
 def test_silu_ffn_full_size(oracle_mod):
     _say("silu 1024x12288x4096")
     X, W = gi.ffn_inputs()
-    Y = g5.gemm_bf16_silu(dev_bf16(X), dev_bf16(W))
+    Y = g5.gemm_bf16_silu(dev_bf16(X), dev_bf16(W), workspace=ws())
     rows = np.array([0, 255, 256, 700, 1023])
     Xs = np.ascontiguousarray(X[rows])
     check_silu(host_values(Y)[rows], oracle_mod.gemm_bf16(Xs, W), oracle_mod.gemm_bf16_silu(Xs, W), 4096,
@@ -124,15 +124,15 @@ def test_silu_ffn_full_size(oracle_mod):
 def test_fused_deterministic_and_k_zero():
     X, Wgu = _swiglu_case(300, 200, 520, 3)
     dX, dW = dev_bf16(X), dev_bf16(Wgu)
-    z1 = g5.gemm_bf16_swiglu(dX, dW)
-    z2 = g5.gemm_bf16_swiglu(dX, dW)
+    z1 = g5.gemm_bf16_swiglu(dX, dW, workspace=ws())
+    z2 = g5.gemm_bf16_swiglu(dX, dW, workspace=ws())
     assert torch.equal(z1.view(torch.int16), z2.view(torch.int16))
     # K = 0: g = u = 0, SiLU(0) = 0, Z = 0; Y = SiLU(0) = 0
     Z = torch.full((300, 200), float("nan"), device="cuda", dtype=torch.bfloat16)
-    g5.gemm_bf16_swiglu(dX[:, :0], dW[:0, :], Z)
+    g5.gemm_bf16_swiglu(dX[:, :0], dW[:0, :], Z, workspace=ws())
     assert torch.all(Z == 0)
     Y = torch.full((300, 200), float("nan"), device="cuda", dtype=torch.bfloat16)
-    g5.gemm_bf16_silu(dX[:, :0], dW[:0, :200], Y)
+    g5.gemm_bf16_silu(dX[:, :0], dW[:0, :200], Y, workspace=ws())
     assert torch.all(Y == 0)
 
 
@@ -144,10 +144,10 @@ def test_swiglu_matches_separate_products(monkeypatch):
     once."""
     X, Wgu = _swiglu_case(512, 384, 640, 4)
     dX, dW = dev_bf16(X), dev_bf16(Wgu)
-    Z = g5.gemm_bf16_swiglu(dX, dW)
+    Z = g5.gemm_bf16_swiglu(dX, dW, workspace=ws())
     monkeypatch.setenv("GEMM_FORCE_KSPLIT", "1")
-    g = g5.gemm_bf16(dX, dW[:, :384])
-    u = g5.gemm_bf16(dX, dW[:, 384:])
+    g = g5.gemm_bf16(dX, dW[:, :384], workspace=ws())
+    u = g5.gemm_bf16(dX, dW[:, 384:], workspace=ws())
     # the elementwise step on the host in float32, from the GPU's bf16 g and u
     gf = host_values(g).astype(np.float32)
     sig = (gf / (np.float32(1) + np.exp(-gf, dtype=np.float32))).astype(np.float32)
@@ -176,7 +176,7 @@ def test_swiglu_batched_experts(oracle_mod, broadcast_x):
     dX = dev_bf16(X)
     if broadcast_x:
         dX = dX.expand(batch, -1, -1)
-    Z = g5.gemm_bf16_swiglu_batched(dX, dev_bf16(Wgu))
+    Z = g5.gemm_bf16_swiglu_batched(dX, dev_bf16(Wgu), workspace=ws())
     got = host_values(Z)
     for b in range(batch):
         Xb = X[0 if broadcast_x else b]
@@ -195,7 +195,7 @@ def test_silu_batched(oracle_mod, monkeypatch):
         _say(f"silu batched forced {cfg}")
         monkeypatch.setenv("GEMM_FORCE_CONFIG", cfg)
         Cfull = torch.full((batch, M + 2, N), float("nan"), device="cuda", dtype=torch.bfloat16)
-        g5.gemm_bf16_silu_batched(dev_bf16(A), dev_bf16(B), Cfull[:, :M])
+        g5.gemm_bf16_silu_batched(dev_bf16(A), dev_bf16(B), Cfull[:, :M], workspace=ws())
         host = host_values(Cfull)
         for b in range(batch):
             check_silu(host[b, :M], oracle_mod.gemm_bf16(A[b], B[b]), oracle_mod.gemm_bf16_silu(A[b], B[b]), K,

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import gemm_inputs as gi
-from _gpu_helpers import check_bf16, check_f32, amax_bf16, dev_bf16, host_values
+from _gpu_helpers import check_bf16, check_f32, amax_bf16, dev_bf16, host_values, ws
 
 import dense_gemm_05_amd as g5
 
@@ -35,7 +35,7 @@ def test_operand_over_2gib(oracle_mod):
     assert st == 0 and plan.variant == 0
     dA = dev_bf16(block).repeat(M // P + 1, 1)[:M]
     assert dA.is_contiguous() and dA.shape == (M, K)
-    C = g5.gemm_bf16(dA, dev_bf16(B))
+    C = g5.gemm_bf16(dA, dev_bf16(B), workspace=ws())
     rows = np.array([0, 1, P - 1, P, 131071, 262143, 262144, 262145, 265000, M - 1])
     got = host_values(C[torch.from_numpy(rows).cuda()])
     ref = oracle_mod.gemm_bf16(np.ascontiguousarray(block[rows % P]), B)
@@ -52,7 +52,7 @@ def test_batch_past_small_m_grid(oracle_mod):
     g = np.random.default_rng([gi.SEED_BASE + 8100])
     A = gi.to_bf16_bits(gi.normal(g, (batch, M, K)))
     B = gi.to_bf16_bits(gi.normal(g, (batch, K, N), 0.125))
-    C = g5.gemm_bf16_batched(dev_bf16(A), dev_bf16(B), out_dtype=torch.float32)
+    C = g5.gemm_bf16_batched(dev_bf16(A), dev_bf16(B), out_dtype=torch.float32, workspace=ws())
     host = host_values(C)
     for b in (0, 1, 65534, 65535, 65536, batch - 1):
         ref = oracle_mod.gemm_bf16(A[b], B[b])

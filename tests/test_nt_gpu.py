@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import gemm_inputs as gi
-from _gpu_helpers import amax_bf16, check_bf16, check_f32, dev_bf16, host_values
+from _gpu_helpers import amax_bf16, check_bf16, check_f32, dev_bf16, host_values, ws
 
 import dense_gemm_05_amd as g5
 
@@ -58,7 +58,7 @@ def test_nt_ragged(oracle_mod, monkeypatch, cfg, M, N, K, pa, pb):
     ref = _ref(oracle_mod, A, Bt, K)
     for od in (torch.float32, torch.bfloat16):
         Cfull = torch.full((M, N + 5), float("nan"), device="cuda", dtype=od)
-        g5.gemm_bf16_nt(dA[:, :K], dB[:, :K], Cfull[:, :N])
+        g5.gemm_bf16_nt(dA[:, :K], dB[:, :K], Cfull[:, :N], workspace=ws())
         host = host_values(Cfull)
         if od == torch.bfloat16:
             check_bf16(host[:, :N], ref, K, f"nt {cfg} bf16")
@@ -74,7 +74,7 @@ def test_nt_ksplit(oracle_mod, monkeypatch, S):
     A, Bt = _case(M, N, K, 8, 8, 2)
     monkeypatch.setenv("GEMM_FORCE_CONFIG", "bf16_128x128")
     monkeypatch.setenv("GEMM_FORCE_KSPLIT", str(S))
-    C = g5.gemm_bf16_nt(dev_bf16(A)[:, :K], dev_bf16(Bt)[:, :K], out_dtype=torch.float32)
+    C = g5.gemm_bf16_nt(dev_bf16(A)[:, :K], dev_bf16(Bt)[:, :K], out_dtype=torch.float32, workspace=ws())
     check_f32(host_values(C), _ref(oracle_mod, A, Bt, K), K, amax_bf16(A[:, :K]), amax_bf16(Bt[:, :K]),
               f"nt split {S}")
 
@@ -85,8 +85,8 @@ def test_nt_matches_nn_bitwise():
     A, Bt = _case(512, 576, 640, 0, 0, 3)
     dA, dBt = dev_bf16(A), dev_bf16(Bt)
     dB = dBt.t().contiguous()
-    c1 = g5.gemm_bf16(dA, dB, out_dtype=torch.float32)
-    c2 = g5.gemm_bf16_nt(dA, dBt, out_dtype=torch.float32)
+    c1 = g5.gemm_bf16(dA, dB, out_dtype=torch.float32, workspace=ws())
+    c2 = g5.gemm_bf16_nt(dA, dBt, out_dtype=torch.float32, workspace=ws())
     assert torch.equal(c1.view(torch.int32), c2.view(torch.int32))
 
 
@@ -98,7 +98,7 @@ def test_attention_scores_nt_full_size(oracle_mod):
     Km = np.ascontiguousarray(np.transpose(KT, (0, 2, 1)))      # [32, 1024, 128], as drawn
     st, plan = g5.plan_query(g5.GEMM_OP_BF16_NT, 1024, 1024, 128, batch=32, c_type=1)
     assert st == 0 and plan.name == b"bf16_128x128" and plan.variant == 1 and plan.workspace_bytes == 0
-    C = g5.gemm_bf16_nt_batched(dev_bf16(Q), dev_bf16(Km), out_dtype=torch.float32)
+    C = g5.gemm_bf16_nt_batched(dev_bf16(Q), dev_bf16(Km), out_dtype=torch.float32, workspace=ws())
     host = host_values(C)
     for b in (0, 5, 31):
         ref = oracle_mod.gemm_bf16(Q[b], KT[b])
@@ -117,7 +117,7 @@ def test_nt_linear_weight_full_size(oracle_mod):
     Wt = np.ascontiguousarray(W.T)
     st, plan = g5.plan_query(g5.GEMM_OP_BF16_NT, 1024, 12288, 4096)
     assert st == 0 and plan.name == b"bf16_256x192" and plan.variant == 1
-    C = g5.gemm_bf16_nt(dev_bf16(X), dev_bf16(Wt))
+    C = g5.gemm_bf16_nt(dev_bf16(X), dev_bf16(Wt), workspace=ws())
     rows = np.array([0, 255, 256, 511, 700, 1023])
     ref = oracle_mod.gemm_bf16(np.ascontiguousarray(X[rows]), W)
     check_bf16(host_values(C)[rows], ref, 4096, "FFN NT rows")
@@ -137,9 +137,9 @@ def test_nt_small_m(oracle_mod, M, N, K, batch):
     for od in (torch.float32, torch.bfloat16):
         Cfull = torch.full((batch, M, N + 3), float("nan"), device="cuda", dtype=od)
         if batch == 1:
-            g5.gemm_bf16_nt(dev_bf16(A[0]), dev_bf16(Bt[0]), Cfull[0, :, :N])
+            g5.gemm_bf16_nt(dev_bf16(A[0]), dev_bf16(Bt[0]), Cfull[0, :, :N], workspace=ws())
         else:
-            g5.gemm_bf16_nt_batched(dev_bf16(A), dev_bf16(Bt), Cfull[:, :, :N])
+            g5.gemm_bf16_nt_batched(dev_bf16(A), dev_bf16(Bt), Cfull[:, :, :N], workspace=ws())
         host = host_values(Cfull)
         for b in range(batch):
             ref = oracle_mod.gemm_bf16(A[b], np.ascontiguousarray(Bt[b].T))
@@ -156,7 +156,7 @@ def test_nt_small_m_batch_invariance():
     X, W = gi.decode_inputs(16)
     dW = dev_bf16(np.ascontiguousarray(W.T))
     dX = dev_bf16(X)
-    c16 = g5.gemm_bf16_nt(dX, dW).view(torch.int16)
+    c16 = g5.gemm_bf16_nt(dX, dW, workspace=ws()).view(torch.int16)
     for M in (1, 4, 9):
-        cm = g5.gemm_bf16_nt(dX[:M], dW).view(torch.int16)
+        cm = g5.gemm_bf16_nt(dX[:M], dW, workspace=ws()).view(torch.int16)
         assert torch.equal(cm, c16[:M]), f"M={M} differs from the M=16 rows"

@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import gemm_inputs as gi
-from _gpu_helpers import (amax_bf16, check_bf16, check_f32, dev_bf16, dev_f32, host_bits,
+from _gpu_helpers import (ws, amax_bf16, check_bf16, check_f32, dev_bf16, dev_f32, host_bits,
                                 host_values)
 
 pytestmark = pytest.mark.gpu
@@ -73,16 +73,14 @@ def test_sgemm_padded_strides(oracle_mod):
     assert np.all(np.isnan(host[:, N:])), "ldc padding was written"
 
 
-def test_sgemm_4096_sampled(oracle_mod):
+def test_sgemm_4096_full(oracle_mod):
     """The 4096^3 workload at full size, in the launch configuration the
-    benchmark times; rows spread over the tile grid are checked in full."""
-    _say("sgemm 4096^3 (sampled rows)")
+    benchmark times; every element against the oracle."""
+    _say("sgemm 4096^3 (every element)")
     A, B = gi.sgemm_inputs(4096, workload=gi.W_SGEMM_LARGE)
     C = g5.gemm_sgemm(dev_f32(A), dev_f32(B))
-    rows = np.array([0, 1, 127, 128, 129, 1000, 2047, 2048, 3071, 4094, 4095])
-    ref = oracle_mod.gemm_f32(np.ascontiguousarray(A[rows]), B)
-    got = host_values(C)[rows]
-    check_f32(got, ref, 4096, np.abs(A).max(), np.abs(B).max(), "sgemm 4096 rows")
+    ref = oracle_mod.gemm_f32(A, B)
+    check_f32(host_values(C), ref, 4096, np.abs(A).max(), np.abs(B).max(), "sgemm 4096")
 
 
 # ---------------------------------------------------------------- BF16
@@ -98,7 +96,7 @@ def test_bf16_ragged(oracle_mod, M, N, K, out):
     _say(f"bf16 {M}x{N}x{K} -> {out}")
     A, B = gi.small_case("bf16", M, N, K, seed=1, scale_b=0.125)
     od = torch.bfloat16 if out == "bf16" else torch.float32
-    C = g5.gemm_bf16(dev_bf16(A), dev_bf16(B), out_dtype=od)
+    C = g5.gemm_bf16(dev_bf16(A), dev_bf16(B), out_dtype=od, workspace=ws())
     ref = oracle_mod.gemm_bf16(A, B)
     if out == "bf16":
         check_bf16(host_values(C), ref, K, f"bf16 {M}x{N}x{K}")
@@ -119,7 +117,7 @@ def test_bf16_every_config(oracle_mod, monkeypatch, cfg):
     monkeypatch.setenv("GEMM_FORCE_CONFIG", cfg)
     for od in (torch.bfloat16, torch.float32):
         Cfull = torch.full((M, N + 7), float("nan"), device="cuda", dtype=od)
-        g5.gemm_bf16(dA[:, :K], dB[:K, :N], Cfull[:, :N])
+        g5.gemm_bf16(dA[:, :K], dB[:K, :N], Cfull[:, :N], workspace=ws())
         ref = oracle_mod.gemm_bf16(np.ascontiguousarray(A[:, :K]), np.ascontiguousarray(B[:K, :N]))
         host = host_values(Cfull)
         if od == torch.bfloat16:
@@ -161,44 +159,42 @@ def test_sgemm_whole_k(oracle_mod, M, N, K, pad):
         assert np.all(np.isnan(host[:, N:])), "ldc padding was written"
 
 
-def test_ffn_projection_full_size(oracle_mod):
-    """X[1024,4096] . W[4096,12288] -> bf16, the benchmarked launch; 48 rows
-    spread across every row tile and all 12288 columns are checked in full."""
-    _say("FFN 1024x12288x4096")
+@pytest.mark.parametrize("with_ws", [True, False])
+def test_ffn_projection_full_size(oracle_mod, with_ws):
+    """X[1024,4096] . W[4096,12288] -> bf16, the benchmarked launch (through
+    gemm_run with a workspace) and the named call without one; every element
+    against the oracle."""
+    _say(f"FFN 1024x12288x4096 workspace={with_ws}")
     X, W = gi.ffn_inputs()
-    C = g5.gemm_bf16(dev_bf16(X), dev_bf16(W))
-    st, plan = g5.plan_query(g5.GEMM_OP_BF16, 1024, 12288, 4096)
-    assert plan.name == b"bf16_256x192"
-    rows = np.unique(np.concatenate([np.arange(0, 1024, 32), np.arange(1, 1024, 97), [255, 256, 767, 1023]]))
-    ref = oracle_mod.gemm_bf16(np.ascontiguousarray(X[rows]), W)
-    got = host_values(C)[rows]
-    check_bf16(got, ref, 4096, "FFN rows")
+    C = g5.gemm_bf16(dev_bf16(X), dev_bf16(W), workspace=ws() if with_ws else None)
+    ref = oracle_mod.gemm_bf16(X, W)
+    check_bf16(host_values(C), ref, 4096, "FFN")
 
 
 @pytest.mark.parametrize("M,N,K,cfg", [(4096, 4096, 4096, b"bf16_256x256"), (2048, 2048, 8192, b"bf16_128x128")])
-def test_large_bf16_products_sampled(oracle_mod, M, N, K, cfg):
+def test_large_bf16_products(oracle_mod, M, N, K, cfg):
     """Large bf16 products on the tile shapes the selector gives them
     (256x256 tiles for a 4096^3 product, 128x128 tiles for an output too
-    small to fill the CUs with large tiles); rows from every row tile,
-    both edges of each, all columns."""
-    _say(f"bf16 {M}x{N}x{K} sampled rows ({cfg.decode()})")
+    small to fill the CUs with large tiles); every element."""
+    _say(f"bf16 {M}x{N}x{K} ({cfg.decode()})")
     st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
     assert st == 0 and plan.name == cfg, plan.name
     g = np.random.default_rng(M + N + K)
     A = gi.to_bf16_bits(gi.normal(g, (M, K)))
     B = gi.to_bf16_bits(gi.normal(g, (K, N), 0.125))
-    C = g5.gemm_bf16(dev_bf16(A), dev_bf16(B))
-    tile = plan.tile_m
-    rows = np.unique(np.concatenate([np.arange(0, M, tile), np.arange(tile - 1, M, tile), np.arange(7, M, 301)]))
-    ref = oracle_mod.gemm_bf16(np.ascontiguousarray(A[rows]), B)
-    check_bf16(host_values(C)[rows], ref, K, f"bf16 {M}x{N}x{K} rows")
+    C = g5.gemm_bf16(dev_bf16(A), dev_bf16(B), workspace=ws())
+    ref = oracle_mod.gemm_bf16(A, B)
+    check_bf16(host_values(C), ref, K, f"bf16 {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("with_ws", [True, False])
 @pytest.mark.parametrize("M", [1, 4, 16])
-def test_decode_full_size(oracle_mod, M):
-    _say(f"decode M={M}")
+def test_decode_full_size(oracle_mod, M, with_ws):
+    """Decode shapes at full size, with a workspace (the split small-M path)
+    and without (whole K per workgroup): every element."""
+    _say(f"decode M={M} workspace={with_ws}")
     X, W = gi.decode_inputs(M)
-    C = g5.gemm_bf16(dev_bf16(X), dev_bf16(W))
+    C = g5.gemm_bf16(dev_bf16(X), dev_bf16(W), workspace=ws() if with_ws else None)
     ref = oracle_mod.gemm_bf16(X, W)
     check_bf16(host_values(C), ref, 4096, f"decode M={M}")
 
@@ -217,7 +213,7 @@ def test_decode_paths_ragged(oracle_mod, monkeypatch, cfg, M, N, K, batch):
     st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K, batch=batch)
     assert st == 0 and plan.name.decode() == cfg
     for od in (torch.bfloat16, torch.float32):
-        C = g5.gemm_bf16_batched(dev_bf16(A), dev_bf16(B), out_dtype=od)
+        C = g5.gemm_bf16_batched(dev_bf16(A), dev_bf16(B), out_dtype=od, workspace=ws())
         host = host_values(C)
         for b in range(batch):
             ref = oracle_mod.gemm_bf16(A[b], B[b])
@@ -241,7 +237,7 @@ def test_decode_split_k(oracle_mod, monkeypatch, M, N, K, batch):
     W = gi.to_bf16_bits(gi.normal(g, (batch, K, N), 0.125))
     dX, dW = dev_bf16(X), dev_bf16(W)
     for rep in range(2):
-        C = g5.gemm_bf16_batched(dX, dW, out_dtype=torch.float32 if rep else torch.bfloat16)
+        C = g5.gemm_bf16_batched(dX, dW, out_dtype=torch.float32 if rep else torch.bfloat16, workspace=ws())
         host = host_values(C)
         for b in range(batch):
             ref = oracle_mod.gemm_bf16(X[b], W[b])
@@ -263,7 +259,7 @@ def test_decode_split_k_back_to_back(oracle_mod):
     dW = dev_bf16(W)
     st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
     assert plan.name == b"decode_splitk" and plan.grid == 16 * 4
-    outs = [g5.gemm_bf16(dev_bf16(X), dW, out_dtype=torch.float32) for X in Xs]
+    outs = [g5.gemm_bf16(dev_bf16(X), dW, out_dtype=torch.float32, workspace=ws()) for X in Xs]
     for i, (X, C) in enumerate(zip(Xs, outs)):
         ref = oracle_mod.gemm_bf16(X, W)
         check_f32(host_values(C), ref, K, amax_bf16(X), amax_bf16(W), f"call {i}")
@@ -274,26 +270,23 @@ def test_decode_batch_invariance():
     bit: the K split does not depend on M ("Operator & Runtime" §5.2.4)."""
     X16, W = gi.decode_inputs(16)
     dW = dev_bf16(W)
-    C16 = host_bits(g5.gemm_bf16(dev_bf16(X16), dW))
+    C16 = host_bits(g5.gemm_bf16(dev_bf16(X16), dW, workspace=ws()))
     for M in (1, 4, 9):
-        CM = host_bits(g5.gemm_bf16(dev_bf16(np.ascontiguousarray(X16[:M])), dW))
+        CM = host_bits(g5.gemm_bf16(dev_bf16(np.ascontiguousarray(X16[:M])), dW, workspace=ws()))
         assert np.array_equal(CM, C16[:M]), f"M={M} rows differ from M=16"
 
 
-def test_batched_attention_scores(oracle_mod):
-    """32 x Q[1024,128] . K^T[128,1024] -> f32; 4 entries in full, the rest
-    on sampled rows."""
-    _say("batched 32x1024x1024x128")
+@pytest.mark.parametrize("with_ws", [True, False])
+def test_batched_attention_scores(oracle_mod, with_ws):
+    """32 x Q[1024,128] . K^T[128,1024] -> f32: every element of every entry."""
+    _say(f"batched 32x1024x1024x128 workspace={with_ws}")
     Q, KT = gi.batched_inputs()
-    C = g5.gemm_bf16_batched(dev_bf16(Q), dev_bf16(KT), out_dtype=torch.float32)
+    C = g5.gemm_bf16_batched(dev_bf16(Q), dev_bf16(KT), out_dtype=torch.float32,
+                             workspace=ws() if with_ws else None)
     host = host_values(C)
-    for b in (0, 1, 17, 31):
-        ref = oracle_mod.gemm_bf16(Q[b], KT[b])
-        check_f32(host[b], ref, 128, amax_bf16(Q[b]), amax_bf16(KT[b]), f"batch entry {b}")
-    rows = np.array([0, 255, 256, 511, 777, 1023])
+    ref = oracle_mod.gemm_bf16_batched(Q, KT)
     for b in range(32):
-        ref = oracle_mod.gemm_bf16(np.ascontiguousarray(Q[b][rows]), KT[b])
-        check_f32(host[b][rows], ref, 128, amax_bf16(Q[b]), amax_bf16(KT[b]), f"batch {b} rows")
+        check_f32(host[b], ref[b], 128, amax_bf16(Q[b]), amax_bf16(KT[b]), f"batch entry {b}")
 
 
 @pytest.mark.parametrize("M,N,K,pa,batch", [(520, 1024, 2050, 1, 1), (520, 1024, 2050, 2, 1),
@@ -314,11 +307,12 @@ def test_bf16_realigned_rows(oracle_mod, M, N, K, pa, batch):
                              c_type=1)
     assert st == 0 and plan.family == 2 and plan.vec_a == 16 and plan.variant in (1, 2), (plan.name, plan.variant)
     split = 0
-    if plan.ksplit > 1:       # few tiles: K also split over workgroups (partial tiles, counters)
+    if plan.ksplit > 1:       # few tiles: K also split over workgroups (partial tiles)
         tiles = batch * -(-M // plan.tile_m) * -(-N // plan.tile_n)
-        split = tiles * plan.ksplit * plan.tile_m * plan.tile_n * 4 + tiles * 4
-    assert plan.workspace_bytes == batch * M * ((K + 7) // 8 * 8) * 2 + split
-    g5.gemm_bf16_batched(dA[:, :, :K], dB, C)
+        split = tiles * plan.ksplit * plan.tile_m * plan.tile_n * 4
+    r = lambda b: (b + 255) // 256 * 256
+    assert plan.workspace_bytes == 65536 + r(split) + r(batch * M * ((K + 7) // 8 * 8) * 2)
+    g5.gemm_bf16_batched(dA[:, :, :K], dB, C, workspace=ws())
     host = host_values(C)
     for b in range(batch):
         rows = np.arange(0, M, 7)
@@ -326,18 +320,22 @@ def test_bf16_realigned_rows(oracle_mod, M, N, K, pa, batch):
         check_f32(host[b][rows], ref, K, amax_bf16(A[b][:, :K]), amax_bf16(B[b]), f"realigned batch {b}")
 
 
-def test_ragged_single_gemm(oracle_mod):
+@pytest.mark.parametrize("with_ws", [True, False])
+def test_ragged_single_gemm(oracle_mod, with_ws):
     """M=1000, N=12280, K=4100 bf16 -> f32 (edge tiles in M and N, a K tail
-    of 4, 8-byte aligned rows of A); also with bf16 output."""
-    _say("ragged 1000x12280x4100")
+    of 4, 8-byte aligned rows of A, realigned first with a workspace and
+    copied 4 bytes per lane without); also with bf16 output.  Every element."""
+    _say(f"ragged 1000x12280x4100 workspace={with_ws}")
     A, B = gi.ragged_inputs()
     dA, dB = dev_bf16(A), dev_bf16(B)
-    rows = np.unique(np.concatenate([np.arange(0, 1000, 41), [255, 256, 767, 768, 998, 999]]))
-    refr = oracle_mod.gemm_bf16(np.ascontiguousarray(A[rows]), B)
-    C = g5.gemm_bf16(dA, dB, out_dtype=torch.float32)
-    check_f32(host_values(C)[rows], refr, 4100, amax_bf16(A), amax_bf16(B), "ragged f32")
-    Cb = g5.gemm_bf16(dA, dB, out_dtype=torch.bfloat16)
-    check_bf16(host_values(Cb)[rows], refr, 4100, "ragged bf16")
+    w = ws() if with_ws else None
+    st, plan = g5.plan_query(g5.GEMM_OP_BF16, 1000, 12280, 4100, c_type=1, with_workspace=with_ws)
+    assert st == 0 and plan.variant == (2 if with_ws else 3)
+    ref = oracle_mod.gemm_bf16(A, B)
+    C = g5.gemm_bf16(dA, dB, out_dtype=torch.float32, workspace=w)
+    check_f32(host_values(C), ref, 4100, amax_bf16(A), amax_bf16(B), "ragged f32")
+    Cb = g5.gemm_bf16(dA, dB, out_dtype=torch.bfloat16, workspace=w)
+    check_bf16(host_values(Cb), ref, 4100, "ragged bf16")
 
 
 def test_batched_strides_broadcast_and_single(oracle_mod):
@@ -345,13 +343,13 @@ def test_batched_strides_broadcast_and_single(oracle_mod):
     A = gi.to_bf16_bits(gi.normal(g, (3, 40, 50)))
     B = gi.to_bf16_bits(gi.normal(g, (1, 50, 70), 0.125))
     dA, dB = dev_bf16(A), dev_bf16(B)
-    C = g5.gemm_bf16_batched(dA, dB.expand(3, 50, 70), out_dtype=torch.float32)  # strideB = 0
+    C = g5.gemm_bf16_batched(dA, dB.expand(3, 50, 70), out_dtype=torch.float32, workspace=ws())  # strideB = 0
     host = host_values(C)
     for b in range(3):
         check_f32(host[b], oracle_mod.gemm_bf16(A[b], B[0]), 50, amax_bf16(A[b]), amax_bf16(B), f"bcast {b}")
     # batch of one equals the single GEMM bit for bit
-    C1 = g5.gemm_bf16_batched(dA[:1], dB, out_dtype=torch.float32)
-    Cs = g5.gemm_bf16(dA[0], dB[0], out_dtype=torch.float32)
+    C1 = g5.gemm_bf16_batched(dA[:1], dB, out_dtype=torch.float32, workspace=ws())
+    Cs = g5.gemm_bf16(dA[0], dB[0], out_dtype=torch.float32, workspace=ws())
     assert torch.equal(C1[0], Cs)
 
 
@@ -361,7 +359,7 @@ def test_k_zero_writes_zeros():
     A = torch.empty((5, 0), dtype=torch.bfloat16, device="cuda")
     B = torch.empty((0, 7), dtype=torch.bfloat16, device="cuda")
     C = torch.full((5, 7), 3.0, dtype=torch.bfloat16, device="cuda")
-    g5.gemm_bf16(A, B, C)
+    g5.gemm_bf16(A, B, C, workspace=ws())
     assert torch.count_nonzero(C).item() == 0
     Cf = torch.full((5, 7), 3.0, device="cuda")
     g5.gemm_sgemm(A.float(), B.float(), Cf)
@@ -378,7 +376,7 @@ def test_k_zero_fill_shapes(M, N, pad, batch, od):
     A = torch.empty((batch, M, 0), dtype=torch.bfloat16, device="cuda")
     B = torch.empty((batch, 0, N), dtype=torch.bfloat16, device="cuda")
     Cfull = torch.full((batch, M, N + pad), float("nan"), dtype=od, device="cuda")
-    g5.gemm_bf16_batched(A, B, Cfull[:, :, :N])
+    g5.gemm_bf16_batched(A, B, Cfull[:, :, :N], workspace=ws())
     host = Cfull.float().cpu().numpy()
     assert np.all(host[:, :, :N] == 0)
     assert np.all(np.isnan(host[:, :, N:]))
@@ -388,7 +386,7 @@ def test_empty_m_leaves_c_untouched():
     A = torch.empty((0, 9), dtype=torch.bfloat16, device="cuda")
     B = torch.ones((9, 4), dtype=torch.bfloat16, device="cuda")
     C = torch.empty((0, 4), dtype=torch.bfloat16, device="cuda")
-    assert g5.gemm_bf16(A, B, C).shape == (0, 4)
+    assert g5.gemm_bf16(A, B, C, workspace=ws()).shape == (0, 4)
 
 
 @pytest.mark.parametrize("M", [1, 40])   # decode path and tiled path
@@ -397,7 +395,7 @@ def test_bf16_round_to_nearest_even_ties(M):
     (1+2^-7) + 2^-8 = 1 + 3*2^-8 -> tie -> 1 + 2^-6."""
     a = np.ones((M, 2), np.float32)
     b = np.array([[1.0, 1.0 + 2 ** -7], [2 ** -8, 2 ** -8]], np.float32)
-    C = g5.gemm_bf16(dev_bf16(gi.to_bf16_bits(a)), dev_bf16(gi.to_bf16_bits(b)))
+    C = g5.gemm_bf16(dev_bf16(gi.to_bf16_bits(a)), dev_bf16(gi.to_bf16_bits(b)), workspace=ws())
     bits = host_bits(C)
     assert np.all(bits[:, 0] == 0x3F80) and np.all(bits[:, 1] == 0x3F82), bits[:2]
 
@@ -408,9 +406,9 @@ def test_identity_and_all_ones(M, N, K):
     A = I gives C = B exactly."""
     ones_a = torch.ones((M, K), dtype=torch.bfloat16, device="cuda")
     ones_b = torch.ones((K, N), dtype=torch.bfloat16, device="cuda")
-    Cf = g5.gemm_bf16(ones_a, ones_b, out_dtype=torch.float32)
+    Cf = g5.gemm_bf16(ones_a, ones_b, out_dtype=torch.float32, workspace=ws())
     assert torch.all(Cf == K)
-    Cb = g5.gemm_bf16(ones_a, ones_b)
+    Cb = g5.gemm_bf16(ones_a, ones_b, workspace=ws())
     want = gi.bf16_bits_to_f32(gi.to_bf16_bits(np.array([K], np.float32)))[0]
     assert torch.all(Cb.float() == float(want))
     Cs = g5.gemm_sgemm(ones_a.float(), ones_b.float())
@@ -418,15 +416,15 @@ def test_identity_and_all_ones(M, N, K):
     if M == K:
         eye = torch.eye(K, dtype=torch.bfloat16, device="cuda")
         B = torch.randn((K, N), device="cuda").to(torch.bfloat16)
-        assert torch.equal(g5.gemm_bf16(eye, B), B)
+        assert torch.equal(g5.gemm_bf16(eye, B, workspace=ws()), B)
         assert torch.equal(g5.gemm_sgemm(eye.float(), B.float()), B.float())
 
 
 def test_deterministic_bitwise():
     X, W = gi.ffn_inputs(M=512, K=1024, N=3072)
     dX, dW = dev_bf16(X), dev_bf16(W)
-    c1 = host_bits(g5.gemm_bf16(dX, dW))
-    c2 = host_bits(g5.gemm_bf16(dX, dW))
+    c1 = host_bits(g5.gemm_bf16(dX, dW, workspace=ws()))
+    c2 = host_bits(g5.gemm_bf16(dX, dW, workspace=ws()))
     assert np.array_equal(c1, c2)
     A, B = gi.small_case("f32", 300, 300, 300)
     s1 = g5.gemm_sgemm(dev_f32(A), dev_f32(B))
@@ -441,7 +439,7 @@ def test_nan_sentinel_every_element_written_once():
     for (M, N, K) in [(257, 193, 70), (1000, 1000, 64), (5, 300, 40)]:
         A, B = gi.small_case("bf16", M, N, K, seed=3)
         buf = torch.full((M + 3, N + 9), float("nan"), device="cuda")
-        g5.gemm_bf16(dev_bf16(A), dev_bf16(B), buf[:M, :N])
+        g5.gemm_bf16(dev_bf16(A), dev_bf16(B), buf[:M, :N], workspace=ws())
         h = buf.cpu().numpy()
         assert np.all(np.isfinite(h[:M, :N]))
         assert np.all(np.isnan(h[:M, N:])) and np.all(np.isnan(h[M:, :]))
@@ -481,7 +479,7 @@ def test_bf16_kernel_variants(oracle_mod, monkeypatch, M, N, K, pa, pb, cfg, var
         st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K, lda=K + pa, ldb=N + pb, ldc=N + 8,
                                  a_addr=dA.data_ptr(), b_addr=dB.data_ptr(), c_addr=Cfull.data_ptr(), c_type=ct)
         assert st == 0 and plan.family == 2 and plan.variant == variant, (plan.name, plan.variant)
-        g5.gemm_bf16(dA[:, :K], dB[:, :N], Cfull[:, :N])
+        g5.gemm_bf16(dA[:, :K], dB[:, :N], Cfull[:, :N], workspace=ws())
         ref = oracle_mod.gemm_bf16(np.ascontiguousarray(A[:, :K]), np.ascontiguousarray(B[:, :N]))
         host = host_values(Cfull)
         if od == torch.bfloat16:
@@ -515,9 +513,9 @@ def test_bf16_ksplit(oracle_mod, monkeypatch, M, N, K, S, lda_pad, batch):
         outs = []
         for _ in range(2):
             if batch == 1:
-                g5.gemm_bf16(dA[0, :, :K], dB[0], Cfull[0, :, :N])
+                g5.gemm_bf16(dA[0, :, :K], dB[0], Cfull[0, :, :N], workspace=ws())
             else:
-                g5.gemm_bf16_batched(dA[:, :, :K], dB, Cfull[:, :, :N])
+                g5.gemm_bf16_batched(dA[:, :, :K], dB, Cfull[:, :, :N], workspace=ws())
             outs.append(Cfull.clone())
         assert torch.equal(outs[0].view(torch.int16 if od == torch.bfloat16 else torch.int32),
                            outs[1].view(torch.int16 if od == torch.bfloat16 else torch.int32)), "not deterministic"
@@ -541,7 +539,7 @@ def test_ksplit_back_to_back_changing_split(oracle_mod, monkeypatch):
     for M, N, K, S in cases:
         A, B = gi.small_case("bf16", M, N, K, seed=S, scale_b=0.125)
         monkeypatch.setenv("GEMM_FORCE_KSPLIT", str(S))
-        res.append((A, B, g5.gemm_bf16(dev_bf16(A), dev_bf16(B), out_dtype=torch.float32)))
+        res.append((A, B, g5.gemm_bf16(dev_bf16(A), dev_bf16(B), out_dtype=torch.float32, workspace=ws())))
     for (A, B, C), (M, N, K, S) in zip(res, cases):
         check_f32(host_values(C), oracle_mod.gemm_bf16(A, B), K, amax_bf16(A), amax_bf16(B), f"split {S}")
 
@@ -554,17 +552,16 @@ def test_ksplit_shard_full_size(oracle_mod):
     W = np.ascontiguousarray(W[:, :1536])
     st, plan = g5.plan_query(g5.GEMM_OP_BF16, 1024, 1536, 4096)
     assert st == 0 and plan.ksplit == 2
-    C = g5.gemm_bf16(dev_bf16(X), dev_bf16(W))
-    rows = np.unique(np.concatenate([np.arange(0, 1024, 64), np.arange(127, 1024, 128), [1, 1000]]))
-    ref = oracle_mod.gemm_bf16(np.ascontiguousarray(X[rows]), W)
-    check_bf16(host_values(C)[rows], ref, 4096, "shard rows")
+    C = g5.gemm_bf16(dev_bf16(X), dev_bf16(W), workspace=ws())
+    ref = oracle_mod.gemm_bf16(X, W)
+    check_bf16(host_values(C), ref, 4096, "shard")
 
 
-def test_workspace_shared_by_threads_on_one_stream():
-    """Two host threads enqueue K-split calls on the same stream at once
-    while one of them keeps needing larger workspaces (each growth
-    synchronises the stream, frees and reallocates the buffer): every
-    result equals the same call made alone, bit for bit."""
+def test_concurrent_calls_from_two_threads():
+    """Two host threads enqueue K-split calls on one stream at once, each with
+    its own workspace (the library keeps no state between calls), one of them
+    through sizes that keep growing its workspace: every result equals the
+    same call made alone, bit for bit."""
     import threading
     shapes_a = [(256, 256, 4096)] * 12
     shapes_b = [(128 * i, 256, 2048) for i in (1, 2, 3, 4, 2, 5, 6, 3, 7, 8, 4, 8)]
@@ -572,24 +569,23 @@ def test_workspace_shared_by_threads_on_one_stream():
     for (M, N, K) in set(shapes_a + shapes_b):
         A, B = gi.small_case("bf16", M, N, K, seed=90, scale_b=0.125)
         dA, dB = dev_bf16(A), dev_bf16(B)
-        cases[(M, N, K)] = (dA, dB, g5.gemm_bf16(dA, dB, out_dtype=torch.float32))
+        cases[(M, N, K)] = (dA, dB, g5.gemm_bf16(dA, dB, out_dtype=torch.float32, workspace=ws()))
     torch.cuda.synchronize()
     for key in cases:
         st, plan = g5.plan_query(g5.GEMM_OP_BF16, *key, c_type=1)
         assert st == 0 and plan.ksplit > 1, key
     outs = {0: [], 1: []}
     errors = []
-    # a new stream (default priority) starts with no workspace, so the
-    # growing sizes of the second thread reallocate it during the run
     shared = torch.cuda.Stream()
     shared.wait_stream(torch.cuda.current_stream())
 
     def worker(idx, shapes):
         try:
             with torch.cuda.stream(shared):
+                w = g5.Workspace()
                 for key in shapes:
                     dA, dB, _ = cases[key]
-                    outs[idx].append((key, g5.gemm_bf16(dA, dB, out_dtype=torch.float32)))
+                    outs[idx].append((key, g5.gemm_bf16(dA, dB, out_dtype=torch.float32, workspace=w)))
         except Exception as e:          # reported below
             errors.append(e)
 
@@ -604,3 +600,36 @@ def test_workspace_shared_by_threads_on_one_stream():
     for idx in (0, 1):
         for key, C in outs[idx]:
             assert torch.equal(C.view(torch.int32), cases[key][2].view(torch.int32)), (idx, key)
+
+
+def test_calls_allocate_nothing_on_a_fresh_stream(oracle_mod):
+    """The C entry points allocate, free and synchronise nothing: device
+    memory in use is the same before and after a split small-M call through
+    gemm_run (with a caller workspace) and a named call (without), both on a
+    stream that has never run a GEMM; and the results equal the oracle's."""
+    import ctypes
+    X, W = gi.small_case("bf16", 1, 12288, 4096, seed=95, scale_b=0.125)
+    dX, dW = dev_bf16(X), dev_bf16(W)
+    C1 = torch.empty((1, 12288), dtype=torch.bfloat16, device="cuda")
+    C2 = torch.empty_like(C1)
+    st, plan = g5.plan_query(g5.GEMM_OP_BF16, 1, 12288, 4096)
+    assert st == 0 and plan.name == b"decode_splitk"
+    wsbuf = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    L = g5.lib()
+    st1 = L.gemm_run(g5.GEMM_OP_BF16, 1, 1, 12288, 4096, dX.data_ptr(), 4096, 0, dW.data_ptr(), 12288, 0,
+                     C1.data_ptr(), 12288, 0, 0, 1.0, None, 0.0, None, None, wsbuf.data_ptr(), wsbuf.numel(),
+                     ctypes.c_void_p(s.cuda_stream))
+    st2 = L.gemm_bf16(1, 12288, 4096, dX.data_ptr(), 4096, dW.data_ptr(), 12288, C2.data_ptr(), 12288, 0,
+                      ctypes.c_void_p(s.cuda_stream))
+    s.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert st1 == 0 and st2 == 0
+    assert free1 == free0, f"device free memory changed by {free0 - free1} bytes"
+    assert int(wsbuf[:65536].count_nonzero()) == 0, "arrival counters not left at zero"
+    ref = oracle_mod.gemm_bf16(X, W)
+    check_bf16(host_values(C1), ref, 4096, "split small-M with workspace")
+    check_bf16(host_values(C2), ref, 4096, "whole-K small-M without workspace")

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import gemm_inputs as gi
-from _gpu_helpers import amax_bf16, check_bf16, check_f32, dev_bf16, host_values
+from _gpu_helpers import amax_bf16, check_bf16, check_f32, dev_bf16, host_values, ws
 
 import dense_gemm_05_amd as g5
 
@@ -61,7 +61,7 @@ def test_tn_ragged(oracle_mod, monkeypatch, cfg, M, N, K, pa, pb):
     ref = _ref(oracle_mod, At, B, M, N)
     for od in (torch.float32, torch.bfloat16):
         Cfull = torch.full((M, N + 5), float("nan"), device="cuda", dtype=od)
-        g5.gemm_bf16_tn(dA[:, :M], dB[:, :N], Cfull[:, :N])
+        g5.gemm_bf16_tn(dA[:, :M], dB[:, :N], Cfull[:, :N], workspace=ws())
         host = host_values(Cfull)
         if od == torch.bfloat16:
             check_bf16(host[:, :N], ref, K, f"tn {cfg} bf16")
@@ -79,7 +79,7 @@ def test_tn_ksplit(oracle_mod, monkeypatch, S):
     monkeypatch.setenv("GEMM_FORCE_KSPLIT", str(S))
     st, plan = g5.plan_query(g5.GEMM_OP_BF16_TN, M, N, K, lda=M + 8, ldb=N + 8, c_type=1)
     assert st == 0 and plan.ksplit == S
-    C = g5.gemm_bf16_tn(dev_bf16(At)[:, :M], dev_bf16(B)[:, :N], out_dtype=torch.float32)
+    C = g5.gemm_bf16_tn(dev_bf16(At)[:, :M], dev_bf16(B)[:, :N], out_dtype=torch.float32, workspace=ws())
     check_f32(host_values(C), _ref(oracle_mod, At, B, M, N), K, amax_bf16(At[:, :M]), amax_bf16(B[:, :N]),
               f"tn split {S}")
 
@@ -94,8 +94,8 @@ def test_tn_matches_nn_bitwise(monkeypatch, cfg):
     dA = dAt.t().contiguous()
     monkeypatch.setenv("GEMM_FORCE_CONFIG", cfg)
     monkeypatch.setenv("GEMM_FORCE_KSPLIT", "1")
-    c1 = g5.gemm_bf16(dA, dB, out_dtype=torch.float32)
-    c2 = g5.gemm_bf16_tn(dAt, dB, out_dtype=torch.float32)
+    c1 = g5.gemm_bf16(dA, dB, out_dtype=torch.float32, workspace=ws())
+    c2 = g5.gemm_bf16_tn(dAt, dB, out_dtype=torch.float32, workspace=ws())
     assert torch.equal(c1.view(torch.int32), c2.view(torch.int32))
 
 
@@ -104,7 +104,7 @@ def test_tn_batched_broadcast(oracle_mod):
     _say("tn batched")
     At, B = _case(136, 200, 300, 0, 0, 4, batch=3)
     dB = dev_bf16(B[0]).unsqueeze(0).expand(3, -1, -1)
-    C = g5.gemm_bf16_tn_batched(dev_bf16(At), dB, out_dtype=torch.float32)
+    C = g5.gemm_bf16_tn_batched(dev_bf16(At), dB, out_dtype=torch.float32, workspace=ws())
     host = host_values(C)
     for b in range(3):
         ref = oracle_mod.gemm_bf16(np.ascontiguousarray(At[b].T), B[0])
@@ -115,7 +115,7 @@ def test_tn_k_zero():
     C = torch.full((40, 64), float("nan"), device="cuda", dtype=torch.bfloat16)
     At = torch.zeros((0, 40), device="cuda", dtype=torch.bfloat16)
     B = torch.zeros((0, 64), device="cuda", dtype=torch.bfloat16)
-    g5.gemm_bf16_tn(At, B, C)
+    g5.gemm_bf16_tn(At, B, C, workspace=ws())
     assert torch.all(C == 0)
 
 
@@ -126,7 +126,7 @@ def test_tn_weight_gradient_full_size(oracle_mod):
     X, dY = gi.wgrad_inputs()
     st, plan = g5.plan_query(g5.GEMM_OP_BF16_TN, 4096, 12288, 1024)
     assert st == 0 and plan.variant == 1 and plan.workspace_bytes == 0
-    C = g5.gemm_bf16_tn(dev_bf16(X), dev_bf16(dY))
+    C = g5.gemm_bf16_tn(dev_bf16(X), dev_bf16(dY), workspace=ws())
     rows = np.array([0, 1, 255, 256, 2047, 3000, 4095])
     ref = oracle_mod.gemm_bf16(np.ascontiguousarray(X[:, rows].T), dY)
     check_bf16(host_values(C)[rows], ref, 1024, "wgrad rows")
