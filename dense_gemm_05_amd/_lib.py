@@ -37,7 +37,7 @@ EXPORTS = ("gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm
            "gemm_bf16_tn", "gemm_bf16_tn_batched",
            "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_bf16_silu_batched", "gemm_bf16_swiglu_batched",
            "gemm_fp8_quantize_rows", "gemm_fp8_nt", "gemm_bf16_affine", "gemm_bf16_nt_affine",
-           "gemm_bf16_tn_affine", "gemm_run", "gemm_workspace_size",
+           "gemm_bf16_tn_affine", "gemm_run", "gemm_run_noalloc", "gemm_workspace_size",
            "gemm_status_string",
            "gemm_plan_query", "gemm_plan_query_ex", "gemm_model_local_bytes", "gemm_model_traffic_bytes", "gemm_model_quant_traffic",
            "gemm_tile_map")
@@ -117,6 +117,8 @@ def lib():
     L.gemm_run.argtypes = [i32, i64, i64, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64, i32,
                            f32, p, f32, p, p, p, u64, p]
     L.gemm_run.restype = i32
+    L.gemm_run_noalloc.argtypes = L.gemm_run.argtypes[:20] + [p]
+    L.gemm_run_noalloc.restype = i32
     L.gemm_model_local_bytes.argtypes = [i64, i64, i64, i64]
     L.gemm_model_local_bytes.restype = i64
     L.gemm_model_traffic_bytes.argtypes = [i64, i64, i64, i64, i64, i64]

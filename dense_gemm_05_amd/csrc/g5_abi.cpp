@@ -625,6 +625,14 @@ bool log_enabled()
     return v == 1;
 }
 
+// Arrival counters a plan uses (at the start of the workspace).
+int64_t counters_used(const Problem &p, const Plan &pl)
+{
+    if (pl.config == CFG_DECODE_SPLIT) return p.batch * pl.tiles_n;
+    if (pl.ksplit > 1) return p.batch * pl.tiles_m * pl.tiles_n;
+    return 0;
+}
+
 // The plan a call runs: with the workspace paths when the caller passes a
 // workspace (which must then hold what the plan needs), else without.
 int plan_for_call(const Problem &p, const void *ws, size_t ws_bytes, Plan &pl, WsLayout &L)
@@ -960,17 +968,15 @@ int gemm_workspace_size(int op, int64_t batch, int64_t M, int64_t N, int64_t K, 
     return st;
 }
 
-int gemm_run(int op, int64_t batch, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int64_t strideA,
-             const void *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc, int64_t strideC, int c_type,
-             float alpha, const uint16_t *bias, float beta, const float *scale_a, const float *scale_b,
-             void *workspace, uint64_t workspace_bytes, void *stream)
+static g5::Problem run_problem(int op, int64_t batch, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                               int64_t strideA, const void *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc,
+                               int64_t strideC, int c_type, float alpha, const uint16_t *bias, float beta,
+                               const float *scale_a, const float *scale_b)
 {
-    if (op < GEMM_OP_SGEMM || op > GEMM_OP_BF16_TN_AFFINE) return GEMM_ERR_INVALID_ARG;
     Problem p{op, batch, M, N, K, (uint64_t)A, (uint64_t)B, (uint64_t)C, lda, ldb, ldc, strideA, strideB, strideC,
               op == GEMM_OP_SGEMM ? (int)GEMM_OUT_F32
               : (op == GEMM_OP_BF16_SILU || op == GEMM_OP_BF16_SWIGLU) ? (int)GEMM_OUT_BF16
                                                                         : c_type};
-    if (op == GEMM_OP_SGEMM && batch != 1) return GEMM_ERR_INVALID_ARG;
     if (op == GEMM_OP_FP8_NT) {
         p.scale_a = (uint64_t)scale_a;
         p.scale_b = (uint64_t)scale_b;
@@ -980,7 +986,47 @@ int gemm_run(int op, int64_t batch, int64_t M, int64_t N, int64_t K, const void 
         p.beta = beta;
         p.bias = (uint64_t)bias;
     }
+    return p;
+}
+
+int gemm_run(int op, int64_t batch, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int64_t strideA,
+             const void *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc, int64_t strideC, int c_type,
+             float alpha, const uint16_t *bias, float beta, const float *scale_a, const float *scale_b,
+             void *workspace, uint64_t workspace_bytes, void *stream)
+{
+    if (op < GEMM_OP_SGEMM || op > GEMM_OP_BF16_TN_AFFINE) return GEMM_ERR_INVALID_ARG;
+    if (op == GEMM_OP_SGEMM && batch != 1) return GEMM_ERR_INVALID_ARG;
+    const Problem p = run_problem(op, batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, c_type, alpha,
+                                  bias, beta, scale_a, scale_b);
     return g5::run(p, stream, workspace, (size_t)workspace_bytes);
+}
+
+int gemm_run_noalloc(int op, int64_t batch, int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                     int64_t strideA, const void *B, int64_t ldb, int64_t strideB, void *C, int64_t ldc,
+                     int64_t strideC, int c_type, float alpha, const uint16_t *bias, float beta,
+                     const float *scale_a, const float *scale_b, void *stream)
+{
+    if (op < GEMM_OP_SGEMM || op > GEMM_OP_BF16_TN_AFFINE) return GEMM_ERR_INVALID_ARG;
+    if (op == GEMM_OP_SGEMM && batch != 1) return GEMM_ERR_INVALID_ARG;
+    const Problem p = run_problem(op, batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, c_type, alpha,
+                                  bias, beta, scale_a, scale_b);
+    int st = g5::validate(p);
+    if (st != GEMM_OK) return st;
+    g5::Plan pl;
+    st = g5::select_plan(p, pl, true);
+    if (st != GEMM_OK) return st;
+    if (pl.config == g5::CFG_NONE) return GEMM_OK;
+    if (g5::ws_layout(p, pl).total > g5::kScratchBytes) return GEMM_ERR_WORKSPACE;
+    st = g5::check_device();
+    if (st != GEMM_OK) return st;
+    void *scratch = nullptr;
+    if (g5::noalloc_scratch(&scratch) != hipSuccess) return GEMM_ERR_LAUNCH;
+    // The scratch keeps the last call's contents: the arrival counters this
+    // call uses are cleared first (every call leaves them zero, but a call
+    // that overlapped another on this GPU may not have).
+    if (g5::launch_clear_counters(scratch, g5::counters_used(p, pl), (hipStream_t)stream) != hipSuccess)
+        return GEMM_ERR_LAUNCH;
+    return g5::run(p, stream, scratch, g5::kScratchBytes);
 }
 
 int64_t gemm_model_local_bytes(int64_t m, int64_t n, int64_t k, int64_t elem_bytes)

@@ -48,17 +48,25 @@ hipError_t launch_fused(int config_id, int epi, const GemmArgs &a, int variant, 
 // over a.batch x a.M x a.N, reading C only when a.beta != 0.
 hipError_t launch_affine_no_product(const GemmArgs &a, int64_t grid, hipStream_t s);
 
-// Small-M path with K split over `ks` workgroups per 128-column strip
-// (a.tiles_n strips): `ws` holds batch x strips x ks x 16 x 128 floats of
-// partial sums, `cnt` batch x strips counters that are zero on entry and
-// left zero on exit.  Requires N % 128 == 0, K % 32 == 0, 16-byte aligned
-// rows of X and W.
 // Copy batch x M rows of K bf16 elements (row stride lda, batch stride sA,
 // rows `align`-byte aligned) into A2 with row stride lda2 (a multiple of 8,
 // >= K) and batch stride M x lda2, zero-filling columns K..lda2-1.
 hipError_t launch_realign_rows(const uint16_t *A, int64_t lda, int64_t sA, int64_t batch, int64_t M, int64_t K,
                                int align, uint16_t *A2, int64_t lda2, hipStream_t s);
 
+// Small-M path with K split over `ks` workgroups per 128-column strip
+// (a.tiles_n strips): `ws` holds batch x strips x ks x 16 x 128 floats of
+// partial sums, `cnt` batch x strips counters that are zero on entry and
+// left zero on exit.  Requires N % 128 == 0, K % 32 == 0, 16-byte aligned
+// rows of X and W.
 hipError_t launch_decode_split(const GemmArgs &a, float *ws, unsigned *cnt, int ks, hipStream_t s);
+
+// The library's own scratch memory (gemm_run_noalloc): kScratchBytes of
+// device memory per GPU, in a file-scope device array.  noalloc_scratch
+// returns the current device's copy (its address looked up once per
+// device); launch_clear_counters zeroes its first n arrival counters.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+hipError_t noalloc_scratch(void **ptr);
+hipError_t launch_clear_counters(void *base, int64_t n, hipStream_t s);
 
 }  // namespace g5

@@ -341,6 +341,27 @@ int gemm_run(int op, int64_t batch, int64_t M, int64_t N, int64_t K,
              void *workspace, uint64_t workspace_bytes,
              void *stream);
 
+/* For callers that cannot allocate a workspace -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation: gemm_run
+ * with the library's own scratch memory in place of a caller workspace.
+ * That memory is a file-scope device array of 16 MiB, one copy per GPU the
+ * library runs on (kept until the process ends), shared by every
+ * gemm_run_noalloc call on that GPU and keeping the last call's contents;
+ * each call first clears the arrival counters it uses (a small fill kernel
+ * on `stream`), then runs as gemm_run.  Calls that overlap in time on one
+ * GPU (several streams or threads) race on it: the caller must order them.
+ * A call whose plan needs more than 16 MiB (gemm_workspace_size) returns
+ * GEMM_ERR_WORKSPACE and enqueues nothing.  Allocates nothing: no hipMalloc,
+ * hipFree or allocating library call.  Arguments, results and the other
+ * errors as gemm_run. */
+int gemm_run_noalloc(int op, int64_t batch, int64_t M, int64_t N, int64_t K,
+                     const void *A, int64_t lda, int64_t strideA,
+                     const void *B, int64_t ldb, int64_t strideB,
+                     void *C, int64_t ldc, int64_t strideC, int c_type,
+                     float alpha, const uint16_t *bias, float beta,
+                     const float *scale_a, const float *scale_b,
+                     void *stream);
+
 /* Workspace bytes gemm_run needs for a call (0: none; host only, no GPU
  * work).  Arguments as gemm_plan_query; writes *bytes and returns the
  * validation status. */
