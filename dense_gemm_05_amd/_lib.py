@@ -49,7 +49,7 @@ class GemmPlan(ctypes.Structure):
                 ("threads", ctypes.c_int), ("vec_a", ctypes.c_int), ("vec_b", ctypes.c_int),
                 ("even", ctypes.c_int), ("variant", ctypes.c_int), ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int64),
                 ("model_bytes", ctypes.c_double), ("name", ctypes.c_char * 48),
-                ("workspace_bytes", ctypes.c_int64), ("ksplit", ctypes.c_int)]
+                ("workspace_bytes", ctypes.c_int64), ("ksplit", ctypes.c_int), ("streamk", ctypes.c_int)]
 
 
 class GemmError(RuntimeError):

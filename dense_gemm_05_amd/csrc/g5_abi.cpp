@@ -68,6 +68,7 @@ struct Plan {
     int64_t lda2 = 0;        // row stride of that copy (elements)
     bool realign_b = false;  // the same for the rows of a transposed B (Bt [N, K])
     int64_t ldb2 = 0;
+    bool streamk = false;    // tiled bf16 call on the persistent stream-K schedule (grid = kNumCU)
     double model_bytes = 0.0;
 };
 
@@ -359,6 +360,17 @@ constexpr int64_t kMaxCounters = (int64_t)(kCounterBytes / sizeof(unsigned));
 // The plan of a call.  `ws`: a caller workspace will be passed, so the
 // paths that need scratch memory (K split over workgroups, the split small-M
 // path, realigned row copies) may be chosen; without one they are not.
+// The persistent stream-K schedule runs plain bf16 products (A as [M, K], B
+// as [K, N], no fused epilogue) on the 256x256 and 256x192 ring kernels with
+// 16-byte rows (variants 1 and 2), whole 32-deep stages, a workspace and at
+// most one counter per tile in its counter region.
+bool streamk_ok(const Problem &p, const Plan &pl, bool ws)
+{
+    return ws && p.op == GEMM_OP_BF16 && (pl.config == CFG_BF16_256x256 || pl.config == CFG_BF16_256x192) &&
+           (pl.variant == 1 || pl.variant == 2) && !pl.realign_a && p.K % 32 == 0 && p.K > 0 &&
+           p.batch * pl.tiles_m * pl.tiles_n <= kMaxCounters;
+}
+
 // Returns GEMM_OK or GEMM_ERR_UNSUPPORTED.
 int select_plan(const Problem &p, Plan &pl, bool ws)
 {
@@ -525,6 +537,16 @@ int select_plan(const Problem &p, Plan &pl, bool ws)
     }
     // fused epilogues and a transposed B exist in the ring kernels only (variants 1-3)
     if (ring_only(p) && tiled(pl.config) && pl.variant == 0) return GEMM_ERR_UNSUPPORTED;
+    if (const char *fs = std::getenv("GEMM_FORCE_STREAMK")) {
+        // diagnostic: the persistent stream-K schedule for the chosen tile
+        if (*fs == '1') {
+            if (!streamk_ok(p, pl, ws)) return GEMM_ERR_UNSUPPORTED;
+            pl.streamk = true;
+            pl.ksplit = 1;
+            const int64_t units = p.batch * pl.tiles_m * pl.tiles_n * (p.K / 32);
+            pl.grid = units < kNumCU ? units : kNumCU;
+        }
+    }
     return GEMM_OK;
 }
 
@@ -545,6 +567,7 @@ size_t partial_bytes(const Problem &p, const Plan &pl)
 {
     if (pl.config == CFG_DECODE_SPLIT) return (size_t)p.batch * pl.tiles_n * pl.ks * 16 * 128 * sizeof(float);
     const ConfigInfo &c = kConfigs[pl.config];
+    if (pl.streamk) return (size_t)2 * pl.grid * c.tile_m * c.tile_n * 4;
     return pl.ksplit > 1 ? (size_t)p.batch * pl.tiles_m * pl.tiles_n * pl.ksplit * c.tile_m * c.tile_n * 4 : 0;
 }
 
@@ -595,6 +618,7 @@ void fill_public_plan(const Problem &p, const Plan &pl, gemm_plan *out)
     std::snprintf(out->name, sizeof out->name, "%s", c.name);
     out->workspace_bytes = (int64_t)ws_layout(p, pl).total;
     out->ksplit = pl.ksplit;
+    out->streamk = pl.streamk ? 1 : 0;
 }
 
 // ------------------------------------------------------------ device check
@@ -629,7 +653,7 @@ bool log_enabled()
 int64_t counters_used(const Problem &p, const Plan &pl)
 {
     if (pl.config == CFG_DECODE_SPLIT) return p.batch * pl.tiles_n;
-    if (pl.ksplit > 1) return p.batch * pl.tiles_m * pl.tiles_n;
+    if (pl.ksplit > 1 || pl.streamk) return p.batch * pl.tiles_m * pl.tiles_n;
     return 0;
 }
 
@@ -711,11 +735,15 @@ int run(const Problem &p, void *stream, void *ws = nullptr, size_t ws_bytes = 0)
     }
     a.ws_part = nullptr;
     a.ws_cnt = nullptr;
-    if (pl.ksplit > 1) {
+    if (pl.ksplit > 1 || pl.streamk) {
         a.ksplit = pl.ksplit;
-        a.kt_per = split_kt_per(p, pl.ksplit);
+        a.kt_per = pl.ksplit > 1 ? split_kt_per(p, pl.ksplit) : 0;
         a.ws_part = (float *)(wsb + L.part);
         a.ws_cnt = counters;
+    }
+    if (pl.streamk) {
+        const hipError_t e = launch_streamk(pl.config, a, pl.variant, pl.grid, (hipStream_t)stream);
+        return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
     }
     if (pl.realign_a) {
         uint16_t *A2 = (uint16_t *)(wsb + L.rows_a);

@@ -281,7 +281,9 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
     constexpr int FITS = LDS_BYTES / PITCH;                  // rows that fit
     constexpr int RP = FITS >= BM ? BM : (FITS >= BM / 2 ? BM / 2 : BM / 4);
     static_assert(RP % 16 == 0 && RP * PITCH <= LDS_BYTES, "staging passes");
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));   // offsets derived anew in every call (see RingTile::accumulate)
+    const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
     const int g = lane >> 4, li = lane & 15;
     char *L = (char *)lds;
@@ -478,57 +480,68 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
 //    multiplied by p.scale_a[row] and
 //    p.scale_b[column] before the epilogue ("Operator & Runtime" §5.4.3,
 //    Example 5-7: dequantization by the row's factor).
+// One output tile of the bf16 LDS-ring kernel, as device functions that the
+// tile kernels below call: `accumulate` multiplies K columns
+// [kbase, kbase + K) of the tile's A row panel and B column panel into the
+// FP32 accumulators (the LDS ring must be free on entry and is free again on
+// return); `store` applies the fp8 factors and the epilogue and writes the
+// tile to C through LDS.
 template <int BM, int BN, int WGM, int WGN, int NSA, int NSB, int AV, bool MASKED, int EPI = EPI_NONE,
-          bool SK = false, bool BT = false, bool F8 = false, bool AT = false>
-__global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
-{
-    constexpr int NWAVE = WGM * WGN;
-    constexpr int BK = 32;                                    // slot row: 32 bf16 = 64 bytes
-    constexpr int EB = F8 ? 1 : 2;                            // bytes per operand element
-    constexpr int KS = 64 / EB;                               // K per stage
+          bool BT = false, bool F8 = false, bool AT = false>
+struct RingTile {
+    static constexpr int NWAVE = WGM * WGN;
+    static constexpr int BK = 32;                                    // slot row: 32 bf16 = 64 bytes
+    static constexpr int EB = F8 ? 1 : 2;                            // bytes per operand element
+    static constexpr int KS = 64 / EB;                               // K per stage
     static_assert(!F8 || (BT && EPI == EPI_NONE), "fp8 operands: A and Bt, no fused epilogue");
     static_assert(!AT || (!F8 && !BT && AV == 16 && (EPI == EPI_NONE || EPI == EPI_AFFINE)),
                   "transposed A: bf16, B as [K, N], plain or affine epilogue");
     static_assert(!AT || ((BM / 8) % 8 == 0 && (BM % 128 != 0 || (BM / 8) % 16 == 0)), "At slot rows: whole swizzle groups");
-    constexpr int TM = BM / WGM, TN = BN / WGN;
-    constexpr int FM = TM / 16, FN = TN / 16;
-    constexpr int NMFMA = FM * FN;
-    constexpr int TAIL = NMFMA / 2;                           // MFMAs run after the barrier
-    constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN;
-    constexpr int B_BASE = NSA * A_ELEMS;                     // B ring after the A ring (elements)
-    constexpr int LDS_BYTES = (NSA * A_ELEMS + NSB * B_ELEMS) * 2;
-    constexpr int A_INS = A_ELEMS * 2 / (64 * AV), B_INS = B_ELEMS * 2 / 1024;   // copy instructions
-    constexpr int A_W = NWAVE / 2, B_W = NWAVE / 2;           // copying waves per operand
-    constexpr int LA = A_INS / A_W, LB = B_INS / B_W;         // copies per wave per stage
-    constexpr int ROWS_PER_A = 64 * AV / 64;                  // A rows per copy instruction
+    static constexpr int TM = BM / WGM, TN = BN / WGN;
+    static constexpr int FM = TM / 16, FN = TN / 16;
+    static constexpr int NMFMA = FM * FN;
+    static constexpr int TAIL = NMFMA / 2;                           // MFMAs run after the barrier
+    static constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN;
+    static constexpr int B_BASE = NSA * A_ELEMS;                     // B ring after the A ring (elements)
+    static constexpr int LDS_BYTES = (NSA * A_ELEMS + NSB * B_ELEMS) * 2;
+    static constexpr int A_INS = A_ELEMS * 2 / (64 * AV), B_INS = B_ELEMS * 2 / 1024;   // copy instructions
+    static constexpr int A_W = NWAVE / 2, B_W = NWAVE / 2;           // copying waves per operand
+    static constexpr int LA = A_INS / A_W, LB = B_INS / B_W;         // copies per wave per stage
+    static constexpr int ROWS_PER_A = 64 * AV / 64;                  // A rows per copy instruction
     static_assert(NWAVE == 8, "two waves per SIMD");
     static_assert(AV == 16 || AV == 4, "A copy width");
     static_assert(A_INS % A_W == 0 && B_INS % B_W == 0, "slab split");
     static_assert((BN / 8) % 8 == 0 && (BN % 128 != 0 || (BN / 8) % 16 == 0), "B slot rows must be whole swizzle groups");
     static_assert(NSA >= 3 && NSB >= 3 && LA * (NSA - 2) < 64 && LB * (NSB - 2) < 64, "vmcnt accounting");
     static_assert(TAIL > 0 && TAIL < NMFMA, "tail");
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[LDS_BYTES / 2];
+    static constexpr bool GLU = EPI == EPI_SWIGLU;
+    static constexpr int HALF = BN / 2;                       // GLU: columns per weight half
+    static_assert(!GLU || HALF % 8 == 0, "GLU halves must be whole chunks");
+    static_assert(!(GLU && BT), "SwiGLU takes B as [K, 2N]");
+    using Acc = f32x4[FN][FM];
 
-    const int tid = threadIdx.x;
+    __device__ static __forceinline__ void zero(Acc &acc)
+    {
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    __device__ static __forceinline__ void accumulate(const GemmArgs &p, uint16_t *smem, const TileCoord &tc,
+                                                      const int64_t kbase, const int64_t K, Acc &acc)
+    {
+    // The lane's offsets derive from the thread index anew in every call
+    // (opaque to the compiler), so a kernel that calls this in a loop does
+    // not keep them live in vector registers across the loop.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
     const int g = lane >> 4, li = lane & 15;
-
-    constexpr bool GLU = EPI == EPI_SWIGLU;
-    constexpr int HALF = BN / 2;                              // GLU: columns per weight half
-    static_assert(!GLU || HALF % 8 == 0, "GLU halves must be whole chunks");
-    static_assert(!(GLU && BT), "SwiGLU takes B as [K, 2N]");
-    const int64_t ntiles = p.batch * p.tiles_m * p.tiles_n;
-    const int64_t wg = SK ? (int64_t)blockIdx.x % ntiles : (int64_t)blockIdx.x;
-    const int slice = SK ? (int)((int64_t)blockIdx.x / ntiles) : 0;
-    const TileCoord tc = tile_map(wg, p.batch, p.tiles_m, p.tiles_n, p.group_m);
     // n0: first output column (GLU: first column of each weight half)
     const int64_t m0 = tc.tm * BM, n0 = tc.tn * (GLU ? HALF : BN);
     const int64_t M = p.M, N = p.N, lda = p.lda, ldb = p.ldb;
-    // This workgroup's part of K starts at kbase; the operand bases below are
-    // moved there, so everything after this works on K columns from them.
-    const int64_t kbase = SK ? (int64_t)slice * p.kt_per * KS : 0;
-    const int64_t K = SK && slice < p.ksplit - 1 ? (int64_t)p.kt_per * KS : p.K - kbase;
     const char *Abat = (const char *)p.A + (tc.b * p.sA + (AT ? kbase * lda : kbase)) * EB;
     const char *Bbat = (const char *)p.B + (tc.b * p.sB + (BT ? kbase : kbase * ldb)) * EB;
     // Byte extents of this batch entry's operands from those bases (reads
@@ -670,11 +683,6 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         }
     };
 
-    f32x4 acc[FN][FM];
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto mfma_range = [&](const Frags &f, int first, int count) {
 #pragma unroll
         for (int t = 0; t < NMFMA; ++t) {
@@ -827,51 +835,18 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
     }
     __builtin_amdgcn_s_waitcnt(0);
 
-    if constexpr (SK) {
-        // Publish this slice's FP32 tile in register order (block, wave,
-        // lane: each wave writes 1 KiB runs) with device-scope (sc1) stores,
-        // wait for them, then count the arrival.  The workgroup that brings
-        // the tile's counter to ksplit adds the slices 0, 1, ... in order
-        // (its own from registers, bit-identical to what it stored), resets
-        // the counter for the next call and stores the tile.
-        __shared__ unsigned sk_arrived;
-        constexpr int TILE_F = BM * BN;
-        float *tile_ws = p.ws_part + wg * p.ksplit * (int64_t)TILE_F;
-        const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-            tile_ws + (int64_t)slice * TILE_F, 0, TILE_F * 4, 0x00020000);
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int off = (((fn * FM + fm) * NWAVE + wave) * 64 + lane) * 16;
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[fn][fm]), wr, off, 0, 16);
-            }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0) sk_arrived = __hip_atomic_fetch_add(p.ws_cnt + wg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        if (sk_arrived != (unsigned)(p.ksplit - 1)) return;
-        f32x4 tot[FN][FM];
-        for (int s2 = 0; s2 < p.ksplit; ++s2) {
-            const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
-                tile_ws + (int64_t)s2 * TILE_F, 0, TILE_F * 4, 0x00020000);
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm) {
-                    const int off = (((fn * FM + fm) * NWAVE + wave) * 64 + lane) * 16;
-                    const f32x4 v = s2 == slice ? acc[fn][fm]
-                                                : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, 16));
-                    tot[fn][fm] = s2 == 0 ? v : tot[fn][fm] + v;
-                }
-        }
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = tot[fn][fm];
-        if (tid == 0) __hip_atomic_store(p.ws_cnt + wg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
+    __device__ static __forceinline__ void store(const GemmArgs &p, uint16_t *smem, const TileCoord &tc, Acc &acc)
+    {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int g = lane >> 4, li = lane & 15;
+    // n0: first output column (GLU: first column of each weight half)
+    const int64_t m0 = tc.tm * BM, n0 = tc.tn * (GLU ? HALF : BN);
+    const int64_t M = p.M, N = p.N, lda = p.lda, ldb = p.ldb;
     if constexpr (F8) {
         // Dequantization: the row's factor, then the column's, in FP32.
         if (p.scale_a || p.scale_b) {
@@ -923,6 +898,76 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
             const bool full = !MASKED || (n + 4 <= N);
             store4(Cb, p.out_f32 != 0, p.ldc, m, n, acc[fn][fm], full, M, N, p.align_c);
         }
+    }
+};
+
+template <int BM, int BN, int WGM, int WGN, int NSA, int NSB, int AV, bool MASKED, int EPI = EPI_NONE,
+          bool SK = false, bool BT = false, bool F8 = false, bool AT = false>
+__global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
+{
+    using R = RingTile<BM, BN, WGM, WGN, NSA, NSB, AV, MASKED, EPI, BT, F8, AT>;
+    constexpr int FM = R::FM, FN = R::FN, NWAVE = R::NWAVE, KS = R::KS;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[R::LDS_BYTES / 2];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int64_t ntiles = p.batch * p.tiles_m * p.tiles_n;
+    const int64_t wg = SK ? (int64_t)blockIdx.x % ntiles : (int64_t)blockIdx.x;
+    const int slice = SK ? (int)((int64_t)blockIdx.x / ntiles) : 0;
+    const TileCoord tc = tile_map(wg, p.batch, p.tiles_m, p.tiles_n, p.group_m);
+    // This workgroup's part of K starts at kbase; the operand bases below are
+    // moved there, so everything after this works on K columns from them.
+    const int64_t kbase = SK ? (int64_t)slice * p.kt_per * KS : 0;
+    const int64_t Kpart = SK && slice < p.ksplit - 1 ? (int64_t)p.kt_per * KS : p.K - kbase;
+    f32x4 acc[FN][FM];
+    R::zero(acc);
+    R::accumulate(p, smem, tc, kbase, Kpart, acc);
+
+    if constexpr (SK) {
+        // Publish this slice's FP32 tile in register order (block, wave,
+        // lane: each wave writes 1 KiB runs) with device-scope (sc1) stores,
+        // wait for them, then count the arrival.  The workgroup that brings
+        // the tile's counter to ksplit adds the slices 0, 1, ... in order
+        // (its own from registers, bit-identical to what it stored), resets
+        // the counter for the next call and stores the tile.
+        __shared__ unsigned sk_arrived;
+        constexpr int TILE_F = BM * BN;
+        float *tile_ws = p.ws_part + wg * p.ksplit * (int64_t)TILE_F;
+        const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+            tile_ws + (int64_t)slice * TILE_F, 0, TILE_F * 4, 0x00020000);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int off = (((fn * FM + fm) * NWAVE + wave) * 64 + lane) * 16;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[fn][fm]), wr, off, 0, 16);
+            }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) sk_arrived = __hip_atomic_fetch_add(p.ws_cnt + wg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (sk_arrived != (unsigned)(p.ksplit - 1)) return;
+        f32x4 tot[FN][FM];
+        for (int s2 = 0; s2 < p.ksplit; ++s2) {
+            const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+                tile_ws + (int64_t)s2 * TILE_F, 0, TILE_F * 4, 0x00020000);
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    const int off = (((fn * FM + fm) * NWAVE + wave) * 64 + lane) * 16;
+                    const f32x4 v = s2 == slice ? acc[fn][fm]
+                                                : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, 16));
+                    tot[fn][fm] = s2 == 0 ? v : tot[fn][fm] + v;
+                }
+        }
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) acc[fn][fm] = tot[fn][fm];
+        if (tid == 0) __hip_atomic_store(p.ws_cnt + wg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    R::store(p, smem, tc, acc);
 }
 
 // Ring kernel variants 1-3 (16-byte A copies aligned / masked, 4-byte A copies masked).

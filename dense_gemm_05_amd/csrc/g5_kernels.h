@@ -61,6 +61,12 @@ hipError_t launch_realign_rows(const uint16_t *A, int64_t lda, int64_t sA, int64
 // rows of X and W.
 hipError_t launch_decode_split(const GemmArgs &a, float *ws, unsigned *cnt, int ks, hipStream_t s);
 
+// The bf16 ring kernel on a persistent stream-K schedule (variants 1 and 2
+// of the configs 256x256 and 256x192; `grid` workgroups, a multiple of 8):
+// a.ws_part holds 2 x grid partial tiles of FP32, a.ws_cnt one counter per
+// output tile (zero on entry, left zero).  Requires K % 32 == 0.
+hipError_t launch_streamk(int config_id, const GemmArgs &a, int variant, int64_t grid, hipStream_t s);
+
 // The library's own scratch memory (gemm_run_noalloc): kScratchBytes of
 // device memory per GPU, in a file-scope device array.  noalloc_scratch
 // returns the current device's copy (its address looked up once per

@@ -412,6 +412,9 @@ typedef struct {
                                 bytes; 0 when it needs none */
     int ksplit;        /* tiled bf16 calls: workgroups sharing each output
                           tile's K range (1: no split); grid counts them all */
+    int streamk;       /* 1: the persistent stream-K schedule (grid = one
+                          workgroup per CU, each walking an equal share of
+                          the (tile, K stage) pairs) */
 } gemm_plan;
 
 /* Operation selector for gemm_plan_query. */
