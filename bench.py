@@ -9,9 +9,16 @@ the ragged 1000x12280x4100 GEMM) are reported in "workloads".
 
 Timing: inputs are generated on the host from fixed seeds, copied to HBM, and
 rotated over R buffer sets (R x working set >= 512 MiB) so that successive
-calls cannot be served from the 256 MiB Infinity Cache.  After W warmup calls,
-K back-to-back calls are bracketed by HIP events recorded on the stream the
-kernels run on; the time per call is the event interval / K.
+calls cannot be served from the 256 MiB Infinity Cache.  After about a second
+of untimed calls (clocks settle) and W warmup calls, each workload runs 7
+batches of n back-to-back calls (n such that a batch lasts >= 20 ms and
+7 n >= K for the headline), each batch bracketed by HIP events recorded on
+the stream the kernels run on.  The time per call of a batch is its event
+interval / n; reported are the median over the batches (the headline value)
+with the minimum and maximum.  GPU clocks and power are read with rocm-smi
+before and after the run; the host's CPU model is recorded with the oracle's
+CPU times (all threads on a sample of the FFN projection, and one thread on
+the FP32 256^3 product).
 
 One JSON line is printed on stdout.
 """
@@ -46,9 +53,36 @@ def parse():
     ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "sgemm", "batched", "ragged", "swiglu", "shard", "fp8", "scores_nt", "decode_nt", "affine", "linear_nt", "wgrad_tn", "copy"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--batches", type=int, default=7, help="timed batches per workload (median reported)")
+    ap.add_argument("--batch-ms", type=float, default=20.0, help="minimum length of a timed batch")
     ap.add_argument("--prewarm-seconds", type=float, default=1.0,
                     help="untimed calls before each workload's warmup, so that GPU clocks settle")
     return ap.parse_args()
+
+
+def gpu_clocks():
+    """Clock levels and power of GPU 0 as rocm-smi reports them (None fields
+    when the tool is missing or fails; it runs as a child process)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "-d", "0", "--showclocks", "--showpower", "--showperflevel", "--json"],
+                           capture_output=True, text=True, timeout=30)
+        data = json.loads(r.stdout)
+        card = next(iter(data.values())) if isinstance(data, dict) and data else {}
+        return {"time": time.strftime("%H:%M:%S"), **{k.strip(): v for k, v in card.items()}}
+    except Exception as e:  # noqa: BLE001 -- a missing tool must not stop the benchmark
+        return {"time": time.strftime("%H:%M:%S"), "error": f"{type(e).__name__}: {e}"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def kernel_label(plan):
@@ -89,6 +123,7 @@ def main():
     _ensure_built()
     import dense_gemm_05_amd as g5
 
+    clocks_before = gpu_clocks()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
@@ -99,13 +134,24 @@ def main():
     def to_dev_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
-    def timed(fn_list, steps, warmup, prewarm=None):
-        """fn_list: one closure per buffer set.  Returns ms per call.
+    timings = {}
+
+    def timed(fn_list, steps, warmup, prewarm=None, label=None):
+        """fn_list: one closure per buffer set.  Returns the median ms per call.
 
         Before the W warmup calls, the workload runs untimed for about
         `prewarm` seconds: the GPU's clocks take a fraction of a second of
         sustained load to settle, and the first hundreds of microseconds of
-        calls otherwise run measurably slower than the steady state."""
+        calls otherwise run measurably slower than the steady state.
+
+        Then `batches` batches of n back-to-back calls are each bracketed by
+        HIP events on the stream the calls run on, with n chosen so that a
+        batch lasts at least `batch_ms` (from a probe after the warmup) and
+        n x batches >= steps.  The time per call of a batch is its event
+        interval / n; the median over the batches is returned and the
+        median, minimum and maximum are kept under `label`, with the host's
+        own enqueue time per call (a host time close to the device time would
+        mean the GPU waits for the host)."""
         R = len(fn_list)
         t_end = time.time() + (args.prewarm_seconds if prewarm is None else prewarm)
         i = 0
@@ -117,14 +163,45 @@ def main():
         for i in range(warmup):
             fn_list[i % R]()
         torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for i in range(steps):
-            fn_list[i % R]()
-        t1.record(stream)
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / steps
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        # batch size: grown from a probe until one untimed batch lasts
+        # batch_ms (a short probe overestimates the steady-state time)
+        n = max(10, min(200, warmup))
+        for _ in range(4):
+            e0.record(stream)
+            for i in range(n):
+                fn_list[i % R]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            took = e0.elapsed_time(e1)
+            if took >= args.batch_ms:
+                break
+            n = int(n * args.batch_ms * 1.1 / max(took, 1e-3)) + 1
+        nb = args.batches
+        n = max(-(-steps // nb), n)
+        per_call, host = [], []
+        for b in range(nb):
+            e0.record(stream)
+            h0 = time.perf_counter()
+            for i in range(n):
+                fn_list[i % R]()
+            h1 = time.perf_counter()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per_call.append(e0.elapsed_time(e1) / n)
+            host.append((h1 - h0) * 1e3 / n)
+        srt = sorted(per_call)
+        med = srt[nb // 2] if nb % 2 else 0.5 * (srt[nb // 2 - 1] + srt[nb // 2])
+        if label is not None:
+            timings[label] = {"median_us": round(med * 1e3, 3), "min_us": round(srt[0] * 1e3, 3),
+                              "max_us": round(srt[-1] * 1e3, 3), "batches": nb, "calls_per_batch": n,
+                              "batch_ms_median": round(med * n, 2),
+                              "host_enqueue_us_per_call": round(min(host) * 1e3, 3)}
+            if min(host) > 0.9 * med:
+                log(f"{label}: host enqueue {min(host) * 1e3:.1f} us/call is close to the device time "
+                    f"{med * 1e3:.1f} us: the GPU may be waiting for the host")
+        return med
 
     def rotations(set_bytes):
         return min(64, max(1, -(-512 * 2 ** 20 // set_bytes)))
@@ -161,13 +238,20 @@ def main():
         dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
         fns = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
         st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
-        ms = timed(fns, args.steps, args.warmup)
+        ms = timed(fns, args.steps, args.warmup, label="ffn_bf16_1024x12288x4096")
         flops = 2.0 * M * N * K
         tflops = flops / (ms * 1e-3) / 1e12
         log(f"FFN: {ms * 1e3:.2f} us/call, {tflops:.1f} TFLOPS ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak), "
             f"config {plan.name.decode()}, R={R}")
+        tm = timings["ffn_bf16_1024x12288x4096"]
         out["value"] = round(tflops, 2)
+        out["value_min"] = round(flops / (tm["max_us"] * 1e-6) / 1e12, 2)
+        out["value_max"] = round(flops / (tm["min_us"] * 1e-6) / 1e12, 2)
         out["ms_per_step"] = round(ms, 5)
+        out["steps"] = tm["batches"] * tm["calls_per_batch"]
+        out["timing"] = {"batches": tm["batches"], "calls_per_batch": tm["calls_per_batch"],
+                         "median_us": tm["median_us"], "min_us": tm["min_us"], "max_us": tm["max_us"],
+                         "statistic": "median over batches of (event interval / calls)"}
         traffic = None
         if os.path.exists(TRAFFIC_FILE):
             with open(TRAFFIC_FILE) as fh:
@@ -194,7 +278,7 @@ def main():
             dW = [to_dev_bf16(W) for _ in range(R)]
             dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
             fns = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
-            ms = timed(fns, max(200, args.steps), args.warmup)
+            ms = timed(fns, max(200, args.steps), args.warmup, label=f"decode_bf16_m{M}_12288x4096")
             gbps = alg_bytes / (ms * 1e-3) / 1e9
             log(f"decode M={M}: {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM)")
             rec = {"name": f"decode_bf16_m{M}_12288x4096", "us": round(ms * 1e3, 3), "GBps": round(gbps, 1),
@@ -219,7 +303,7 @@ def main():
             dW = [to_dev_bf16(Wt) for _ in range(R)]
             dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
             fns = [(lambda i=i: g5.gemm_bf16_nt(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
-            ms = timed(fns, max(200, args.steps), args.warmup)
+            ms = timed(fns, max(200, args.steps), args.warmup, label=f"decode_nt_bf16_m{M}_12288x4096")
             gbps = alg_bytes / (ms * 1e-3) / 1e9
             log(f"decode NT M={M}: {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM)")
             workloads.append({"name": f"decode_nt_bf16_m{M}_12288x4096", "us": round(ms * 1e3, 3),
@@ -236,7 +320,7 @@ def main():
             dB = [torch.from_numpy(B).to(dev) for _ in range(R)]
             dC = [torch.empty((n, n), device=dev) for _ in range(R)]
             fns = [(lambda i=i: g5.gemm_sgemm(dA[i], dB[i], dC[i])) for i in range(R)]
-            ms = timed(fns, steps, 5)
+            ms = timed(fns, steps, 5, label=f"sgemm_f32_{n}^3")
             tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
             log(f"sgemm {n}^3: {ms * 1e3:.2f} us/call, {tf:.1f} TFLOPS ({100 * tf / PEAK_F32_TFLOPS:.1f}% of fp32 peak)")
             workloads.append({"name": f"sgemm_f32_{n}^3", "us": round(ms * 1e3, 3), "tflops": round(tf, 2),
@@ -254,7 +338,7 @@ def main():
         dK = [to_dev_bf16(KT) for _ in range(R)]
         dC = [torch.empty((bt, M, N), device=dev) for _ in range(R)]
         fns = [(lambda i=i: g5.gemm_bf16_batched(dQ[i], dK[i], dC[i], workspace=ws)) for i in range(R)]
-        ms = timed(fns, 100, 10)
+        ms = timed(fns, 100, 10, label="batched_bf16_32x1024x1024x128_f32out")
         flops = 2.0 * bt * M * N * K
         t_roof = max(flops / (PEAK_BF16_TFLOPS * 1e12), alg_bytes / (PEAK_HBM_GBPS * 1e9))
         gbps = alg_bytes / (ms * 1e-3) / 1e9
@@ -274,7 +358,7 @@ def main():
         dB = [to_dev_bf16(B) for _ in range(R)]
         dC = [torch.empty((M, N), device=dev) for _ in range(R)]
         fns = [(lambda i=i: g5.gemm_bf16(dA[i], dB[i], dC[i], workspace=ws)) for i in range(R)]
-        ms = timed(fns, 30, 5)
+        ms = timed(fns, 30, 5, label="ragged_bf16_1000x12280x4100_f32out")
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
         log(f"ragged 1000x12280x4100: {ms * 1e3:.2f} us/call, {tf:.1f} TFLOPS ({100 * tf / PEAK_BF16_TFLOPS:.1f}%)")
         workloads.append({"name": "ragged_bf16_1000x12280x4100_f32out", "us": round(ms * 1e3, 3),
@@ -298,8 +382,8 @@ def main():
         fused = [(lambda i=i: g5.gemm_bf16_swiglu(dX[i], dW[i], dZ[i], workspace=ws)) for i in range(R)]
         plain = [(lambda i=i: (g5.gemm_bf16(dX[i], dW[i][:, :N], dG[i], workspace=ws), g5.gemm_bf16(dX[i], dW[i][:, N:], dU[i], workspace=ws)))
                  for i in range(R)]
-        ms = timed(fused, 30, 5)
-        ms_plain = timed(plain, 30, 5)
+        ms = timed(fused, 30, 5, label="swiglu_ffn_bf16_1024x2x12288x4096")
+        ms_plain = timed(plain, 30, 5, label="swiglu_ffn_two_plain_projections")
         flops = 2.0 * 2 * M * N * K
         tf = flops / (ms * 1e-3) / 1e12
         log(f"swiglu FFN 1024x(2x12288)x4096: fused {ms * 1e3:.2f} us ({tf:.1f} TFLOPS); "
@@ -323,7 +407,7 @@ def main():
         dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
         fns = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
         st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
-        ms = timed(fns, 100, 10)
+        ms = timed(fns, 100, 10, label="shard_bf16_1024x1536x4096")
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
         log(f"shard 1024x1536x4096: {ms * 1e3:.2f} us/call, {tf:.1f} TFLOPS, {plan.name.decode()} ksplit {plan.ksplit}")
         workloads.append({"name": "shard_bf16_1024x1536x4096", "us": round(ms * 1e3, 3), "tflops": round(tf, 2),
@@ -348,9 +432,9 @@ def main():
         quant = [(lambda i=i: g5.gemm_fp8_quantize_rows(dX[i], qX[i][0], qX[i][1])) for i in range(R)]
         both = [(lambda i=i: (g5.gemm_fp8_quantize_rows(dX[i], qX[i][0], qX[i][1]),
                               g5.gemm_fp8_nt(qX[i][0], qX[i][1], qW[i][0], qW[i][1], dC[i], workspace=ws))) for i in range(R)]
-        ms_g = timed(gemm, 50, 10)
-        ms_q = timed(quant, 100, 10)
-        ms_b = timed(both, 50, 10)
+        ms_g = timed(gemm, 50, 10, label="fp8_ffn_e4m3_1024x12288x4096")
+        ms_q = timed(quant, 100, 10, label="fp8_quantize_x_1024x4096")
+        ms_b = timed(both, 50, 10, label="fp8_quantize_and_gemm")
         fl = 2.0 * M * N * K
         tf = fl / (ms_g * 1e-3) / 1e12
         log(f"fp8 FFN: GEMM {ms_g * 1e3:.2f} us ({tf:.1f} TFLOPS, {tf / PEAK_FP8_TFLOPS:.3f} of fp8 peak); "
@@ -369,7 +453,7 @@ def main():
             qXd = [g5.gemm_fp8_quantize_rows(to_dev_bf16(Xd)) for _ in range(Rd)]
             dCd = [torch.empty((Md, N), dtype=torch.bfloat16, device=dev) for _ in range(Rd)]
             fns = [(lambda i=i: g5.gemm_fp8_nt(qXd[i][0], qXd[i][1], qW2[i][0], qW2[i][1], dCd[i], workspace=ws)) for i in range(Rd)]
-            ms_d = timed(fns, 200, 10)
+            ms_d = timed(fns, 200, 10, label=f"fp8_decode_m{Md}_12288x4096")
             gbps = alg / (ms_d * 1e-3) / 1e9
             log(f"fp8 decode M={Md}: {ms_d * 1e3:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM)")
             workloads.append({"name": f"fp8_decode_m{Md}_12288x4096", "us": round(ms_d * 1e3, 3), "GBps": round(gbps, 1),
@@ -389,7 +473,7 @@ def main():
         dK = [to_dev_bf16(Km) for _ in range(R)]
         dC = [torch.empty((bt, M, N), device=dev) for _ in range(R)]
         fns = [(lambda i=i: g5.gemm_bf16_nt_batched(dQ[i], dK[i], dC[i], workspace=ws)) for i in range(R)]
-        ms = timed(fns, 100, 10)
+        ms = timed(fns, 100, 10, label="scores_nt_bf16_32x1024x1024x128_f32out")
         gbps = alg_bytes / (ms * 1e-3) / 1e9
         log(f"scores Q.K^T from row-major K (NT): {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s")
         workloads.append({"name": "scores_nt_bf16_32x1024x1024x128_f32out", "us": round(ms * 1e3, 3),
@@ -412,8 +496,8 @@ def main():
         dC = [torch.zeros((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
         fns = [(lambda i=i: g5.gemm_bf16_affine(dX[i], dW[i], dC[i], bias=db[i], beta=1.0, workspace=ws)) for i in range(R)]
         plain = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
-        ms = timed(fns, 50, 10)
-        ms_plain = timed(plain, 50, 10)
+        ms = timed(fns, 50, 10, label="ffn_bias_residual_bf16_1024x12288x4096")
+        ms_plain = timed(plain, 50, 10, label="ffn_plain_same_buffers")
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
         log(f"FFN + bias + residual: {ms * 1e3:.2f} us ({tf:.1f} TFLOPS); plain projection {ms_plain * 1e3:.2f} us")
         workloads.append({"name": "ffn_bias_residual_bf16_1024x12288x4096", "us": round(ms * 1e3, 3),
@@ -437,8 +521,8 @@ def main():
         dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
         fns = [(lambda i=i: g5.gemm_bf16_nt_affine(dX[i], dW[i], dC[i], bias=db[i], workspace=ws)) for i in range(R)]
         plain = [(lambda i=i: g5.gemm_bf16_nt(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
-        ms = timed(fns, 50, 10)
-        ms_plain = timed(plain, 50, 10)
+        ms = timed(fns, 50, 10, label="linear_nt_bias_bf16_1024x12288x4096")
+        ms_plain = timed(plain, 50, 10, label="linear_nt_without_bias")
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
         log(f"linear layer X.W^T + b (W [12288,4096]): {ms * 1e3:.2f} us ({tf:.1f} TFLOPS); "
             f"without bias {ms_plain * 1e3:.2f} us")
@@ -460,7 +544,7 @@ def main():
         dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
         fns = [(lambda i=i: g5.gemm_bf16_tn(dX[i], dD[i], dC[i], workspace=ws)) for i in range(R)]
         st, plan = g5.plan_query(g5.GEMM_OP_BF16_TN, M, N, K)
-        ms = timed(fns, 50, 10)
+        ms = timed(fns, 50, 10, label="wgrad_tn_bf16_4096x12288x1024")
         tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
         log(f"weight gradient X^T.dY 4096x12288x1024 (TN): {ms * 1e3:.2f} us ({tf:.1f} TFLOPS), {plan.name.decode()}")
         workloads.append({"name": "wgrad_tn_bf16_4096x12288x1024", "us": round(ms * 1e3, 3), "tflops": round(tf, 2),
@@ -469,12 +553,22 @@ def main():
         del dX, dD, dC
 
     out["workloads"] = workloads
+    out["workload_timing"] = timings
+    out["gpu_clocks"] = {"before": clocks_before, "after": gpu_clocks()}
 
     # ------------------------------------------------------------ CPU oracle
     if not args.no_cpu and ffn_rows_gpu is not None:
+        import resource
+
         import oracle
+
+        def cpu_seconds():
+            ru = resource.getrusage(resource.RUSAGE_SELF)
+            return ru.ru_utime + ru.ru_stime
+
         X, W, dCl = ffn_rows_gpu
         Cg = dCl.view(torch.int16).cpu().numpy().view(np.uint16)
+        threads = oracle.num_threads()
         t = time.time()
         oracle.gemm_bf16(np.ascontiguousarray(X[:8]), W)       # calibration, 8 rows
         per_row = (time.time() - t) / 8
@@ -482,22 +576,37 @@ def main():
         # The whole projection is repeated until about cpu_seconds of CPU
         # work have been timed (one pass when a pass is longer than that).
         Xs = np.ascontiguousarray(X[:rows])
-        reps, secs = 0, 0.0
+        reps, secs, cpu0 = 0, 0.0, cpu_seconds()
         while reps == 0 or (secs < args.cpu_seconds and reps < 20):
             t = time.time()
             ref = oracle.gemm_bf16(Xs, W)
             secs += time.time() - t
             reps += 1
+        busy = (cpu_seconds() - cpu0) / secs
         cpu_tflops = 2.0 * reps * rows * 12288 * 4096 / secs / 1e12
         got = gi.bf16_bits_to_f32(Cg[:rows]).astype(np.float64)
         bound = 2.0 ** -8 * np.abs(ref) + 1e-3 * 64.0
         worst = float((np.abs(got - ref) / bound).max())
-        log(f"oracle: {reps} x {rows} rows in {secs:.1f} s on {oracle.num_threads()} threads -> {cpu_tflops * 1e3:.2f} GFLOPS; "
-            f"GPU rows within bar, worst err/bound {worst:.3f}")
-        out["cpu_baseline"] = {"value": round(cpu_tflops, 6), "unit": "TFLOPS", "cores": oracle.num_threads(),
+        log(f"oracle: {reps} x {rows} rows in {secs:.1f} s on {threads} threads ({busy:.1f} cores busy) -> "
+            f"{cpu_tflops * 1e3:.2f} GFLOPS; GPU rows within bar, worst err/bound {worst:.3f}")
+        # FP32 256^3 (the small square product) on one thread, best of 5
+        A1, B1 = gi.sgemm_inputs(256, workload=gi.W_SGEMM_SMALL)
+        oracle.set_num_threads(1)
+        one = []
+        for _ in range(5):
+            t = time.time()
+            oracle.gemm_f32(A1, B1)
+            one.append(time.time() - t)
+        oracle.set_num_threads(threads)
+        log(f"oracle FP32 256^3 on 1 thread: {min(one) * 1e3:.1f} ms")
+        out["cpu_baseline"] = {"value": round(cpu_tflops, 6), "unit": "TFLOPS", "cores": threads,
                                "kind": "oracle",
                                "sample": f"{reps} pass(es) over the first {rows} of 1024 rows of the FFN projection "
                                          f"(x 12288 cols, K=4096), FP64 triple loop, {secs:.1f} s in total",
+                               "cores_busy": round(busy, 2),
+                               "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+                               "cpus_allowed": len(os.sched_getaffinity(0)),
+                               "sgemm_256_1thread_ms": round(min(one) * 1e3, 3),
                                "gpu_rows_worst_err_over_bound": round(worst, 4)}
     print(json.dumps(out), flush=True)
 

@@ -17,7 +17,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import GemmError, GemmPlan, lib
+from ._lib import GEMM_ERR_WORKSPACE, GemmError, GemmPlan, lib
 
 __all__ = ["gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm_bf16_nt_batched",
            "gemm_bf16_tn", "gemm_bf16_tn_batched",
@@ -131,10 +131,19 @@ def _gemm(what, named, named_args, workspace, dev, op, batch, M, N, K, A, lda, s
             if not isinstance(buf, torch.Tensor) or buf.dtype != torch.uint8 or buf.dim() != 1:
                 raise ValueError("a workspace tensor must be a 1-D uint8 tensor")
             _check_dev(A, buf)
-        st = _launch(lib().gemm_run, dev, op, batch, M, N, K, A.data_ptr(), lda, sA, B.data_ptr(), ldb, sB,
-                     C.data_ptr(), ldc, sC, code, float(alpha), None if bias is None else bias.data_ptr(),
-                     float(beta), None if scale_a is None else scale_a.data_ptr(),
-                     None if scale_b is None else scale_b.data_ptr(), buf.data_ptr(), buf.numel())
+        def run(buf):
+            return _launch(lib().gemm_run, dev, op, batch, M, N, K, A.data_ptr(), lda, sA, B.data_ptr(), ldb, sB,
+                           C.data_ptr(), ldc, sC, code, float(alpha), None if bias is None else bias.data_ptr(),
+                           float(beta), None if scale_a is None else scale_a.data_ptr(),
+                           None if scale_b is None else scale_b.data_ptr(), buf.data_ptr(), buf.numel())
+        st = run(buf)
+        if st == GEMM_ERR_WORKSPACE and isinstance(workspace, Workspace):
+            # The cached size went stale (the plan also follows the
+            # library's environment overrides): a call refused for its
+            # workspace has launched nothing, so ask again and retry once.
+            need = workspace_size(op, batch, M, N, K, pa, lda, sA, pb, ldb, sB, pc, ldc, sC, code)
+            workspace._need[key] = need
+            st = run(workspace.reserve(need))
     if st != 0:
         raise GemmError(st, what)
     return C

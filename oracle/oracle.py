@@ -62,6 +62,8 @@ def _load():
     lib.oracle_quantize_rows_e4m3.argtypes = [i64, i64, p, i64, p, i64, p]
     lib.oracle_gemm_fp8_nt.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, p, i64]
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
     _lib = lib
     return lib
 
@@ -267,3 +269,8 @@ def gemm_fp8_nt(A, sa, Bt, sb):
 
 def num_threads():
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n):
+    """Thread count of the oracle's parallel loops (results do not depend on it)."""
+    _load().oracle_set_num_threads(int(n))

@@ -409,3 +409,15 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Thread count of the parallel loops above (timing the oracle on one core
+ * and on all of them); no effect on any result. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}

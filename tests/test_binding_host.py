@@ -87,3 +87,42 @@ def test_host_bias_scale_codes_and_workspace_rejected(no_lib):
         g5.gemm_fp8_nt(qa, None, qb, torch.ones(24), C)
     with pytest.raises(ValueError):
         g5.gemm_fp8_nt(qa, None, qb, None, torch.empty((8, 24), dtype=torch.bfloat16))
+
+
+def test_stale_workspace_size_is_queried_again(monkeypatch):
+    """A call refused for its workspace (GEMM_ERR_WORKSPACE, nothing launched)
+    is retried once after a fresh size query and a larger reservation."""
+    calls = []
+
+    class StubLib:
+        def gemm_workspace_size(self, *a):
+            calls.append("size")
+            a[-1]._obj.value = 4096 if calls.count("size") > 1 else 1024
+            return 0
+
+        def gemm_run(self, *a):
+            nbytes = a[-2]
+            calls.append(("run", nbytes))
+            return 0 if nbytes >= 4096 else g5.GEMM_ERR_WORKSPACE
+
+    class FakeBuf:
+        def __init__(self, n):
+            self.n = n
+
+        def numel(self):
+            return self.n
+
+        def data_ptr(self):
+            return 0x7F0000100000
+
+    stub = StubLib()
+    monkeypatch.setattr(gm, "lib", lambda: stub)
+    monkeypatch.setattr(gm, "_launch", lambda fn, dev, *a: fn(*a, None))
+    ws = gm.Workspace.__new__(gm.Workspace)
+    ws.device, ws.buf, ws._need = torch.device("cuda:0"), None, {}
+    monkeypatch.setattr(gm.Workspace, "reserve",
+                        lambda self, n: setattr(self, "buf", FakeBuf(max(n, 256))) or self.buf)
+    A, B, C = _bf(8, 16), _bf(16, 24), _bf(8, 24)
+    g5.gemm_bf16(A, B, C, workspace=ws)
+    assert calls == ["size", ("run", 1024), "size", ("run", 4096)]
+    assert list(ws._need.values()) == [4096]
