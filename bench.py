@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "sgemm", "batched", "ragged", "swiglu", "shard", "fp8", "scores_nt", "decode_nt", "affine", "linear_nt", "wgrad_tn", "copy"])
+    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "decode_swiglu", "sgemm", "batched", "ragged", "swiglu", "shard", "fp8", "scores_nt", "decode_nt", "affine", "linear_nt", "wgrad_tn", "copy"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--batches", type=int, default=7, help="timed batches per workload (median reported)")
@@ -288,6 +288,40 @@ def main():
                 out["decode_m1"] = {"GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
                                     "us": round(ms * 1e3, 3), "alg_bytes": alg_bytes}
             del dX, dW, dC
+
+    # ------------------------------------------------------------ decode through the fused SwiGLU
+    if args.only in ("all", "decode_swiglu"):
+        # One token through the FFN's gate and up projections with the merged
+        # weight Wgu [4096, 2 x 12288] and the SwiGLU product applied as the
+        # small-M kernels store, next to the plain product of the same token
+        # with the same merged weight (the same 192 MiB read, 24576 bf16
+        # outputs): the fusion's cost over the bytes it has to read.
+        N, K = 12288, 4096
+        X, Wgu = gi.swiglu_inputs(16, K, N)
+        for M in (1, 16):
+            Xm = np.ascontiguousarray(X[:M])
+            alg_bytes = 2 * (M * K + K * 2 * N + M * N)
+            R = rotations(alg_bytes)
+            dX = [to_dev_bf16(Xm) for _ in range(R)]
+            dW = [to_dev_bf16(Wgu) for _ in range(R)]
+            dZ = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+            dP = [torch.empty((M, 2 * N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+            fused = [(lambda i=i: g5.gemm_bf16_swiglu(dX[i], dW[i], dZ[i], workspace=ws)) for i in range(R)]
+            fused_nows = [(lambda i=i: g5.gemm_bf16_swiglu(dX[i], dW[i], dZ[i])) for i in range(R)]
+            plain = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dP[i], workspace=ws)) for i in range(R)]
+            ms = timed(fused, 200, args.warmup, label=f"decode_swiglu_m{M}_2x12288x4096")
+            ms_n = timed(fused_nows, 200, args.warmup, label=f"decode_swiglu_m{M}_no_workspace")
+            ms_p = timed(plain, 200, args.warmup, label=f"decode_plain_merged_m{M}_24576x4096")
+            gbps = alg_bytes / (ms * 1e-3) / 1e9
+            log(f"decode SwiGLU M={M}: fused {ms * 1e3:.2f} us ({gbps:.0f} GB/s), without workspace "
+                f"{ms_n * 1e3:.2f} us; plain product with the merged weight {ms_p * 1e3:.2f} us "
+                f"(fused / plain {ms / ms_p:.3f})")
+            workloads.append({"name": f"decode_swiglu_bf16_m{M}_2x12288x4096", "us": round(ms * 1e3, 3),
+                              "GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
+                              "no_workspace_us": round(ms_n * 1e3, 3),
+                              "plain_merged_product_us": round(ms_p * 1e3, 3),
+                              "fused_over_plain": round(ms / ms_p, 4), "alg_bytes": alg_bytes, "rotations": R})
+            del dX, dW, dZ, dP
 
     # ------------------------------------------------------------ decode with a linear layer's weight
     if args.only in ("all", "decode_nt"):

@@ -237,9 +237,9 @@ bool has_epilogues(int id) { return id == CFG_BF16_256x192 || id == CFG_BF16_256
 bool config_fits(const Problem &p, int id)
 {
     const ConfigInfo &c = kConfigs[id];
-    if (is_affine(p) && c.family == GEMM_FAMILY_DECODE) {       // the small-M kernels apply it too
+    if (epi_of(p) != EPI_NONE && c.family == GEMM_FAMILY_DECODE) {   // the small-M kernels apply them too
         if (a_trans(p)) return false;
-        if (b_trans(p)) return id == CFG_DECODE_NT && p.M <= 16 && p.batch <= 65535;
+        if (b_trans(p)) return id == CFG_DECODE_NT && p.M <= 16 && p.batch <= 65535;   // (affine only)
         return (id == CFG_DECODE_64 || id == CFG_DECODE_SPLIT) && p.M <= 16 && p.batch <= 65535;
     }
     if (epi_of(p) != EPI_NONE) return has_epilogues(id);
@@ -258,7 +258,7 @@ bool config_fits(const Problem &p, int id)
     }
 }
 
-void fill_grid(const Problem &p, Plan &pl)
+void fill_grid(const Problem &p, Plan &pl, bool ws)
 {
     const ConfigInfo &c = kConfigs[pl.config];
     switch (c.family) {
@@ -275,8 +275,11 @@ void fill_grid(const Problem &p, Plan &pl)
         pl.tiles_n = cdiv(p.N, c.tile_n * (pl.config == CFG_DECODE_NT && p.M > 1 ? 3 : 1));
         pl.grid = pl.tiles_n;  // x; batch goes to grid y
         if (pl.config == CFG_DECODE_SPLIT) {
-            pl.ks = decode_slices(pl.tiles_n * p.batch, p.K);
-            pl.grid = pl.tiles_n * pl.ks;
+            // (SwiGLU: a strip's gate and up columns are read by separate workgroups)
+            // (one slice, a direct store, without a workspace)
+            const int64_t groups = pl.tiles_n * (p.op == GEMM_OP_BF16_SWIGLU ? 2 : 1);
+            pl.ks = ws ? decode_slices(groups * p.batch, p.K) : 1;
+            pl.grid = groups * pl.ks;
         }
         break;
     default:
@@ -385,7 +388,7 @@ int select_plan(const Problem &p, Plan &pl, bool ws)
     pl.align_c = row_alignment(p.c, p.ldc, p.sC, p.batch, ec);
     if (p.K == 0 || no_product(p)) {
         pl.config = CFG_ZERO;
-        fill_grid(p, pl);
+        fill_grid(p, pl, ws);
         return GEMM_OK;
     }
 
@@ -409,14 +412,22 @@ int select_plan(const Problem &p, Plan &pl, bool ws)
                p.batch <= 65535 && pl.align_b >= 16) {
         // Small M with B transposed: a GEMV over the contiguous rows of Bt.
         pl.config = CFG_DECODE_NT;
-    } else if ((p.op == GEMM_OP_BF16 || p.op == GEMM_OP_BF16_AFFINE) && p.M <= 16 && p.batch <= 65535) {
-        // The split path when its preconditions hold and it would use more
-        // than one slice; else whole-K strips of 64 columns.
+    } else if ((p.op == GEMM_OP_BF16 || p.op == GEMM_OP_BF16_AFFINE || p.op == GEMM_OP_BF16_SILU ||
+                p.op == GEMM_OP_BF16_SWIGLU) &&
+               p.M <= 16 && p.batch <= 65535) {
+        // The split path (128-column strips, 256 bytes of each W row) when
+        // its preconditions hold and it would use more than one slice, or
+        // enough whole-K strips to occupy most CUs on their own (one slice:
+        // no partial sums, no workspace); SwiGLU always combines its gate and
+        // up workgroups, so it needs the workspace.  Else whole-K strips of
+        // 64 columns.
         pl.config = CFG_DECODE_SPLIT;
         bool ev = false;
-        if (!ws || pick_variant(p, pl, &ev) < 0 || decode_slices(cdiv(p.N, 128) * p.batch, p.K) < 2 ||
-            cdiv(p.N, 128) * p.batch > kMaxCounters)
-            pl.config = CFG_DECODE_64;
+        const bool glu = p.op == GEMM_OP_BF16_SWIGLU;
+        const int64_t strips = cdiv(p.N, 128) * p.batch;
+        const int ks = ws ? decode_slices(strips * (glu ? 2 : 1), p.K) : 1;
+        const bool split = glu ? ws : (ks >= 2 || strips >= kNumCU * 3 / 4);
+        if (!split || pick_variant(p, pl, &ev) < 0 || strips > kMaxCounters) pl.config = CFG_DECODE_64;
     } else {
         // Candidates with their measured relative efficiency; the model
         // picks the fastest (page "Operator & Runtime" §5.4.5: feasibility,
@@ -491,8 +502,10 @@ int select_plan(const Problem &p, Plan &pl, bool ws)
             pl.ksplit = S;
         }
     }
-    fill_grid(p, pl);
+    fill_grid(p, pl, ws);
     if (pl.grid <= 0 || pl.grid > (int64_t)1 << 24) return GEMM_ERR_UNSUPPORTED;
+    // (a forced split path that would need partial sums without a workspace)
+    if (pl.config == CFG_DECODE_SPLIT && !ws && p.op == GEMM_OP_BF16_SWIGLU) return GEMM_ERR_UNSUPPORTED;
     pl.variant = pick_variant(p, pl, &pl.even);
     if (pl.variant < 0) return GEMM_ERR_UNSUPPORTED;   // forced split path without its preconditions
     // A large bf16 product whose A rows are not 16-byte aligned: multiply
@@ -559,13 +572,24 @@ size_t realign_b_bytes(const Problem &p, const Plan &pl)
     return pl.realign_b ? (size_t)p.batch * p.N * pl.ldb2 * 2 : 0;
 }
 
+// The split small-M path with one workgroup per strip stores C directly
+// (no partial sums, no counters).
+bool decode_split_direct(const Problem &p, const Plan &pl)
+{
+    return pl.config == CFG_DECODE_SPLIT && pl.ks == 1 && p.op != GEMM_OP_BF16_SWIGLU;
+}
+
 // Partial sums of the split small-M path: one slot of 16 x 128 FP32 per
 // (batch entry, strip, K slice); of a K-split tiled call: ksplit FP32 tiles
 // per output tile.  The arrival counters (one per strip or tile) are in the
 // workspace's counter region.
 size_t partial_bytes(const Problem &p, const Plan &pl)
 {
-    if (pl.config == CFG_DECODE_SPLIT) return (size_t)p.batch * pl.tiles_n * pl.ks * 16 * 128 * sizeof(float);
+    if (pl.config == CFG_DECODE_SPLIT)
+        return decode_split_direct(p, pl)
+                   ? 0
+                   : (size_t)p.batch * pl.tiles_n * pl.ks * (p.op == GEMM_OP_BF16_SWIGLU ? 2 : 1) * 16 * 128 *
+                         sizeof(float);
     const ConfigInfo &c = kConfigs[pl.config];
     if (pl.streamk) return (size_t)2 * pl.grid * c.tile_m * c.tile_n * 4;
     return pl.ksplit > 1 ? (size_t)p.batch * pl.tiles_m * pl.tiles_n * pl.ksplit * c.tile_m * c.tile_n * 4 : 0;
@@ -652,7 +676,7 @@ bool log_enabled()
 // Arrival counters a plan uses (at the start of the workspace).
 int64_t counters_used(const Problem &p, const Plan &pl)
 {
-    if (pl.config == CFG_DECODE_SPLIT) return p.batch * pl.tiles_n;
+    if (pl.config == CFG_DECODE_SPLIT) return decode_split_direct(p, pl) ? 0 : p.batch * pl.tiles_n;
     if (pl.ksplit > 1 || pl.streamk) return p.batch * pl.tiles_m * pl.tiles_n;
     return 0;
 }
@@ -722,6 +746,7 @@ int run(const Problem &p, void *stream, void *ws = nullptr, size_t ws_bytes = 0)
     a.align_bias = row_alignment(p.bias, 0, 0, 1, 2);
     a.affine = is_affine(p) ? 1 : 0;
     a.a_trans = a_trans(p) ? 1 : 0;
+    a.epi = epi_of(p);
     if (pl.realign_b) {
         uint16_t *B2 = (uint16_t *)(wsb + L.rows_b);
         const hipError_t e = launch_realign_rows((const uint16_t *)p.b, p.ldb, p.sB, p.batch, p.N, p.K,

@@ -86,6 +86,10 @@ struct GemmArgs {
     int32_t align_bias;
     int32_t affine;          // 1: the small-M kernels apply the affine epilogue
     int32_t a_trans;         // 1: A is given as At [K, M] (element (m, k) at A + k*lda + m)
+    // Epilogue of the small-M kernels (an Epilogue value).  EPI_SWIGLU: B is
+    // the merged gate|up weight [K, 2N] (gate columns [0, N), up columns
+    // [N, 2N)) and C the N columns of bf16(bf16(SiLU(g)) * u).
+    int32_t epi;
 };
 
 // Fused epilogues of the bf16 ring kernels.

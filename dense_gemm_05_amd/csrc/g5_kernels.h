@@ -55,10 +55,11 @@ hipError_t launch_realign_rows(const uint16_t *A, int64_t lda, int64_t sA, int64
                                int align, uint16_t *A2, int64_t lda2, hipStream_t s);
 
 // Small-M path with K split over `ks` workgroups per 128-column strip
-// (a.tiles_n strips): `ws` holds batch x strips x ks x 16 x 128 floats of
-// partial sums, `cnt` batch x strips counters that are zero on entry and
-// left zero on exit.  Requires N % 128 == 0, K % 32 == 0, 16-byte aligned
-// rows of X and W.
+// (a.tiles_n strips; 2 ks for a.epi == EPI_SWIGLU: ks on the gate columns,
+// ks on the up columns): `ws` holds batch x strips x (ks or 2 ks) x 16 x 128
+// floats of partial sums, `cnt` batch x strips counters that are zero on
+// entry and left zero on exit.  Requires N % 128 == 0, K % 32 == 0, 16-byte
+// aligned rows of X and W.
 hipError_t launch_decode_split(const GemmArgs &a, float *ws, unsigned *cnt, int ks, hipStream_t s);
 
 // The bf16 ring kernel on a persistent stream-K schedule (variants 1 and 2

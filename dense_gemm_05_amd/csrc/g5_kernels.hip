@@ -450,14 +450,32 @@ __device__ __forceinline__ void store_out(const GemmArgs &p, int64_t b, int64_t 
         }
         sum = __builtin_fmaf(p.alpha, sum, t);
     }
+    // SiLU of the bf16-rounded product, rounded again (as the ring kernels'
+    // fused epilogue: the roundings of the unfused program)
+    if (p.epi == EPI_SILU) sum = silu_f32(__uint_as_float(bf16_rne(sum) << 16));
     if (p.out_f32) ((float *)p.C)[off] = sum;
     else ((uint16_t *)p.C)[off] = (uint16_t)bf16_rne(sum);
 }
 
-template <int NW, bool FAST>
+// The SwiGLU output of the small-M kernels ("Operator & Runtime" §5.3.1):
+// z = bf16(t * u) with t = bf16(SiLU(bf16(g))), u = bf16(u) -- the gate and
+// up FP32 sums each rounded once as the unfused products would be; t * u is
+// exact in FP32.
+__device__ __forceinline__ void store_swiglu(const GemmArgs &p, int64_t b, int64_t m, int64_t n, float g, float u)
+{
+    const float t = __uint_as_float(bf16_rne(silu_f32(__uint_as_float(bf16_rne(g) << 16))) << 16);
+    const float ub = __uint_as_float(bf16_rne(u) << 16);
+    ((uint16_t *)p.C)[b * p.sC + m * p.ldc + n] = (uint16_t)bf16_rne(t * ub);
+}
+
+// GLU: SwiGLU epilogue -- the workgroup's 64 output columns take their gate
+// sums from columns n of the merged weight [K, 2N] and their up sums from
+// columns N + n, both accumulated in the same pass over K.
+template <int NW, bool FAST, bool GLU>
 __global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
 {
-    constexpr int NC = 64;                   // columns per workgroup
+    constexpr int NC = 64;                   // output columns per workgroup
+    constexpr int NB = GLU ? 2 : 1;          // column groups read per row: gate (and up)
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, li = lane & 15;
@@ -477,22 +495,26 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
     const uint16_t *xr = X + (int64_t)(m_ok ? li : 0) * lda;
     const uint16_t *wcol = W + ncol;
 
-    f32x4 acc[4];
+    f32x4 acc[4 * NB];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < 4 * NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // W rows kb + j (j = 0..7) for this lane's 4 columns, whole step in range.
-    auto load_w = [&](int64_t s, u32x2 *w) {
-        const uint16_t *src = wcol + (s * 32 + g * 8) * ldb;
+    // W rows kb + j (j = 0..7) for this lane's 4 columns of group h (column
+    // offset h * N in the merged weight), whole step in range.
+    auto load_w = [&](int64_t s, u32x2 (*w)[8]) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if (FAST) {
-                w[j] = __builtin_nontemporal_load((const u32x2 *)(src + j * ldb));
-            } else {
-                uint32_t e[4];
+        for (int h = 0; h < NB; ++h) {
+            const uint16_t *src = wcol + h * N + (s * 32 + g * 8) * ldb;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) e[c] = (ncol + c < N) ? (uint32_t)src[j * ldb + c] : 0u;
-                w[j] = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+            for (int j = 0; j < 8; ++j) {
+                if (FAST) {
+                    w[h][j] = __builtin_nontemporal_load((const u32x2 *)(src + j * ldb));
+                } else {
+                    uint32_t e[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) e[c] = (ncol + c < N) ? (uint32_t)src[j * ldb + c] : 0u;
+                    w[h][j] = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+                }
             }
         }
     };
@@ -503,24 +525,27 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
         return v;
     };
     // 4x8 transpose of 16-bit halves: block b takes column b of the 8 rows.
-    auto mma = [&](const u32x2 *w, u32x4 xv) {
+    auto mma = [&](const u32x2 (*w)[8], u32x4 xv) {
         const bf16x8 xf = __builtin_bit_cast(bf16x8, xv);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            u32x4 a;
+        for (int h = 0; h < NB; ++h)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t lo = w[2 * q][b >> 1], hi = w[2 * q + 1][b >> 1];
-                a[q] = (b & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+            for (int b = 0; b < 4; ++b) {
+                u32x4 a;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t lo = w[h][2 * q][b >> 1], hi = w[h][2 * q + 1][b >> 1];
+                    a[q] = (b & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+                }
+                acc[4 * h + b] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), xf, acc[4 * h + b], 0, 0, 0);
             }
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), xf, acc[b], 0, 0, 0);
-        }
     };
 
     // Whole steps, software pipelined: the next step's loads are issued
     // before the current step's transpose and MFMAs.
     if (s_begin < s_full_end) {
-        u32x2 w0[8], w1[8];
+        u32x2 w0[NB][8], w1[NB][8];
         u32x4 x0 = load_x(s_begin), x1;
         load_w(s_begin, w0);
         int64_t s = s_begin;
@@ -541,41 +566,53 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
     // A partial last step (K % 32), rows beyond K read as zero.
     for (int64_t s = s_full_end > s_begin ? s_full_end : s_begin; s < s_end; ++s) {
         const int64_t kb = s * 32 + g * 8;
-        u32x2 w[8];
+        u32x2 w[NB][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t k = kb + j;
-            uint32_t e[4] = {0u, 0u, 0u, 0u};
-            if (k < K) {
-                const uint16_t *src = wcol + k * ldb;
+        for (int h = 0; h < NB; ++h)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) e[c] = (ncol + c < N) ? (uint32_t)src[c] : 0u;
+            for (int j = 0; j < 8; ++j) {
+                const int64_t k = kb + j;
+                uint32_t e[4] = {0u, 0u, 0u, 0u};
+                if (k < K) {
+                    const uint16_t *src = wcol + h * N + k * ldb;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) e[c] = (ncol + c < N) ? (uint32_t)src[c] : 0u;
+                }
+                w[h][j] = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
             }
-            w[j] = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-        }
         u32x4 xv = load_chunk8_bf16(xr, kb, K, true, 2);
         if (!m_ok) xv = u32x4{0u, 0u, 0u, 0u};
         mma(w, xv);
     }
 
-    // acc[b][q] of lane (g, li) is the partial C[li][n0 + 16 g + 4 q + b].
-    // Each lane's 16 partials go to LDS at a stride of 17 floats, so the 64
-    // lanes of one write instruction fall on 64 different banks.
-    constexpr int RS = 17;
+    // acc[4 h + b][q] of lane (g, li) is the partial C[li][n0 + 16 g + 4 q + b]
+    // of column group h.  Each lane's 16 NB partials go to LDS at a stride
+    // of 16 NB + 1 floats, so the 64 lanes of one write instruction fall on
+    // 64 different banks.
+    constexpr int RS = 16 * NB + 1;
     __shared__ float red[NW * 64 * RS];
     float *mine = red + (wave * 64 + lane) * RS;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int h = 0; h < NB; ++h)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) mine[q * 4 + b] = acc[b][q];
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) mine[h * 16 + q * 4 + b] = acc[4 * h + b][q];
     __syncthreads();
     for (int t = tid; t < 64 * 16; t += NW * 64) {
         const int L = t >> 4, v = t & 15;
-        float sum = 0.f;
-        for (int w2 = 0; w2 < NW; ++w2) sum += red[(w2 * 64 + L) * RS + v];
+        float sum[NB];
+#pragma unroll
+        for (int h = 0; h < NB; ++h) {
+            sum[h] = 0.f;
+            for (int w2 = 0; w2 < NW; ++w2) sum[h] += red[(w2 * 64 + L) * RS + h * 16 + v];
+        }
         const int64_t m = L & 15;
         const int64_t n = n0 + 16 * (L >> 4) + v;
-        if (m < M && n < N) store_out(p, bidx, m, n, sum);
+        if (m < M && n < N) {
+            if constexpr (GLU) store_swiglu(p, bidx, m, n, sum[0], sum[1]);
+            else store_out(p, bidx, m, n, sum[0]);
+        }
     }
 }
 
@@ -604,6 +641,11 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
 //    XCDs' L2s on their own, so no L2 write-back or invalidation (a full
 //    fence) is needed; with fences the path measured twice as slow.
 //  * W is read once: its loads are non-temporal.
+//  * SwiGLU (p.epi == EPI_SWIGLU): a strip's gate columns (n0.. of the
+//    merged weight [K, 2N]) and its up columns (N + n0..) are read by
+//    separate workgroups, KS of each, which all publish their partial sums;
+//    the last of the 2 KS adds the gate slices and the up slices, each in
+//    slice order, and stores bf16(bf16(SiLU(g)) * u).
 // Requires N % 128 == 0, K % 32 == 0, 16-byte aligned rows of X and W.
 // DB: double-buffer the W rows of two steps in registers.
 template <int NW, bool DB>
@@ -615,7 +657,10 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode_sk(GemmArgs p, float *ws,
     const int g = lane >> 4, li = lane & 15;
     const int64_t M = p.M, K = p.K, lda = p.lda, ldb = p.ldb;
     const int64_t nstrip = p.tiles_n;
-    const int64_t strip = (int64_t)blockIdx.x / KS, slice = (int64_t)blockIdx.x % KS;
+    const bool glu = p.epi == EPI_SWIGLU;
+    const int nmem = glu ? 2 * KS : KS;      // workgroups per strip
+    const int64_t group = (int64_t)blockIdx.x / KS, slice = (int64_t)blockIdx.x % KS;
+    const int64_t strip = glu ? group >> 1 : group, half = glu ? group & 1 : 0;
     const int64_t n0 = strip * NC;
     const int64_t bidx = blockIdx.y;
     const uint16_t *X = (const uint16_t *)p.A + bidx * p.sA;
@@ -627,7 +672,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode_sk(GemmArgs p, float *ws,
     const int64_t s_begin = sl0 + (sl1 - sl0) * wave / NW, s_end = sl0 + (sl1 - sl0) * (wave + 1) / NW;
     const bool m_ok = li < M;
     const uint16_t *xr = X + (int64_t)(m_ok ? li : 0) * lda;
-    const uint16_t *wcol = W + n0 + 8 * li;
+    const uint16_t *wcol = W + half * p.N + n0 + 8 * li;
 
     f32x4 acc[8];
 #pragma unroll
@@ -694,7 +739,8 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode_sk(GemmArgs p, float *ws,
 #pragma unroll
         for (int c = 0; c < 8; ++c) mine[q * 8 + c] = acc[c][q];
     __syncthreads();
-    float *part = ws + ((bidx * nstrip + strip) * KS + slice) * (16 * NC);
+    float *part = ws + ((bidx * nstrip + strip) * nmem + half * KS + slice) * (16 * NC);
+    const bool direct = KS == 1 && !glu;     // one workgroup per strip: no partial sums
     // Entry t: lane L = t / 32, q = (t / 8) % 4, c = t % 8 -> row L % 16,
     // column 32 (L / 16) + 8 q + c of the strip.
     for (int t = tid; t < 64 * 32; t += NW * 64) {
@@ -702,28 +748,35 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode_sk(GemmArgs p, float *ws,
         float sum = 0.f;
         for (int w2 = 0; w2 < NW; ++w2) sum += red[(w2 * 64 + L) * RS + (t & 31)];
         const int m = L & 15, n = 32 * (L >> 4) + 8 * q + c;
-        if (KS == 1) {
+        if (direct) {
             if (m < M) store_out(p, bidx, m, n0 + n, sum);
         } else if (m < M) {                  // rows past M are never read back
             __hip_atomic_store(part + m * NC + n, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    if (KS == 1) return;
-    // Publish this slice; the last of the KS workgroups of the strip sums.
+    if (direct) return;
+    // Publish this slice; the last of the nmem workgroups of the strip sums.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     unsigned *c_strip = cnt + bidx * nstrip + strip;
     if (tid == 0) arrived = __hip_atomic_fetch_add(c_strip, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    if (arrived != (unsigned)(KS - 1)) return;
-    const float *parts = ws + (bidx * nstrip + strip) * KS * (16 * NC);
+    if (arrived != (unsigned)(nmem - 1)) return;
+    const float *parts = ws + (bidx * nstrip + strip) * nmem * (16 * NC);
     for (int t = tid; t < 16 * NC; t += NW * 64) {
         const int m = t / NC, n = t % NC;
         if (m >= M) continue;
         float sum = 0.f;
         for (int k2 = 0; k2 < KS; ++k2)
             sum += __hip_atomic_load(parts + k2 * (16 * NC) + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        store_out(p, bidx, m, n0 + n, sum);
+        if (glu) {
+            float up = 0.f;
+            for (int k2 = KS; k2 < 2 * KS; ++k2)
+                up += __hip_atomic_load(parts + k2 * (16 * NC) + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            store_swiglu(p, bidx, m, n0 + n, sum, up);
+        } else {
+            store_out(p, bidx, m, n0 + n, sum);
+        }
     }
     if (tid == 0) __hip_atomic_store(c_strip, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -732,7 +785,8 @@ hipError_t launch_decode_split(const GemmArgs &a, float *ws, unsigned *cnt, int 
 {
     // 16 waves, one 32-row step in registers at a time (two would spill at
     // 16 waves per CU; the waves themselves keep enough loads in flight).
-    hipLaunchKernelGGL((k_decode_sk<16, false>), dim3((unsigned)(a.tiles_n * ks), (unsigned)a.batch), dim3(16 * 64), 0,
+    const int64_t groups = a.epi == EPI_SWIGLU ? 2 * a.tiles_n : a.tiles_n;
+    hipLaunchKernelGGL((k_decode_sk<16, false>), dim3((unsigned)(groups * ks), (unsigned)a.batch), dim3(16 * 64), 0,
                        s, a, ws, cnt, ks);
     return hipGetLastError();
 }
@@ -1002,10 +1056,21 @@ hipError_t launch_config(int config_id, bool f32_inputs, const GemmArgs &a, int 
     case CFG_DECODE_64:
         // variant 1: every column chunk in range, 8-byte aligned W rows and
         // 16-byte aligned X rows
-        if (variant == 1)
-            hipLaunchKernelGGL((k_decode<16, true>), dim3((unsigned)grid, (unsigned)a.batch), dim3(16 * 64), 0, s, a);
-        else
-            hipLaunchKernelGGL((k_decode<16, false>), dim3((unsigned)grid, (unsigned)a.batch), dim3(16 * 64), 0, s, a);
+        if (a.epi == EPI_SWIGLU) {
+            // (8 waves: the gate and up rows of two steps in flight take
+            // more registers than 4 waves per SIMD leave)
+            if (variant == 1)
+                hipLaunchKernelGGL((k_decode<8, true, true>), dim3((unsigned)grid, (unsigned)a.batch), dim3(8 * 64), 0, s,
+                                   a);
+            else
+                hipLaunchKernelGGL((k_decode<8, false, true>), dim3((unsigned)grid, (unsigned)a.batch), dim3(8 * 64), 0, s,
+                                   a);
+        } else if (variant == 1) {
+            hipLaunchKernelGGL((k_decode<16, true, false>), dim3((unsigned)grid, (unsigned)a.batch), dim3(16 * 64), 0, s, a);
+        } else {
+            hipLaunchKernelGGL((k_decode<16, false, false>), dim3((unsigned)grid, (unsigned)a.batch), dim3(16 * 64), 0, s,
+                               a);
+        }
         return hipGetLastError();
     case CFG_DECODE_NT:
         if (a.fp8) return launch_decode_nt_f8(a, variant, grid, s);

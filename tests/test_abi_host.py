@@ -139,8 +139,15 @@ def test_selector_choices_for_the_workloads(L):
         assert p.variant == 1 and p.workspace_bytes == ws_bytes(96 * 2 * 16 * 128 * 4)
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 4, 12290, 4096)
     assert st == 0 and p.name == b"decode_64" and p.variant == 0 and p.workspace_bytes == 0
-    st, p = g5.plan_query(g5.GEMM_OP_BF16, 1, 32768, 4096)     # 256 strips: one slice, whole-K path
-    assert st == 0 and p.name == b"decode_64"
+    # 192 or more strips: one slice each, stored directly (no partial sums,
+    # no workspace), 256 bytes of each W row per workgroup -- faster than
+    # the whole-K 64-column strips (N = 24576: 35.8 against 44.2 us)
+    for N, grid in ((24576, 192), (32768, 256)):
+        for with_ws in (True, False):
+            st, p = g5.plan_query(g5.GEMM_OP_BF16, 1, N, 4096, with_workspace=with_ws)
+            assert st == 0 and p.name == b"decode_splitk" and p.grid == grid and p.workspace_bytes == 0
+    st, p = g5.plan_query(g5.GEMM_OP_BF16, 1, 12288, 4096, with_workspace=False)   # 96 strips: too few
+    assert st == 0 and p.name == b"decode_64" and p.grid == 192
     # a bf16 4096^3 product: 256x256 tiles fill the 256 CUs exactly once
     # (256x192 would need 352 tiles, two waves; measured 116.6 against
     # 164.9 us); an output with too few large tiles for the 256 CUs takes
@@ -290,6 +297,8 @@ def test_fused_arguments(L, op):
     st, p = g5.plan_query(opc, 4, 8, 0)
     assert st == 0 and p.family == 1                                         # K = 0: fill with zeros
     st, p = g5.plan_query(opc, 4, 8, 4, batch=2)
+    assert st == 0 and p.family == 4                                         # batched, small M: small-M kernels
+    st, p = g5.plan_query(opc, 32, 8, 4, batch=2)
     assert st == 0 and p.family == 2                                         # batched (e.g. MoE experts)
     st, _ = g5.plan_query(opc, 4, 8, 4, batch=2, sC=8 * 4 - 1)
     assert st == g5.GEMM_ERR_INVALID_ARG                                     # output entries overlap
@@ -312,6 +321,29 @@ def test_fused_plans(L):
     assert st == 0 and p.name == b"bf16_256x192" and p.grid == 4 * 128 and p.variant == 1
     st, p = g5.plan_query(g5.GEMM_OP_BF16_SILU, 1024, 12288, 4096)
     assert st == 0 and p.name == b"bf16_256x192" and p.grid == 256
+
+
+def test_fused_small_m_plans(L):
+    """M <= 16: SiLU and SwiGLU run on the small-M kernels.  With a workspace
+    the K-split path (SwiGLU: separate workgroups for a strip's gate and up
+    columns, 2 x 96 strips for N = 12288; SiLU: 96 strips x 2 slices), its
+    partial sums in the workspace; without one the whole-K 64-column kernel;
+    K % 32 != 0 only the latter."""
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_SWIGLU, 1, 12288, 4096)
+    assert st == 0 and p.name == b"decode_splitk" and p.grid == 192
+    assert p.workspace_bytes == ws_bytes(96 * 2 * 16 * 128 * 4)
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_SILU, 16, 12288, 4096)
+    assert st == 0 and p.name == b"decode_splitk" and p.grid == 192
+    assert p.workspace_bytes == ws_bytes(96 * 2 * 16 * 128 * 4)
+    for op in (g5.GEMM_OP_BF16_SILU, g5.GEMM_OP_BF16_SWIGLU):
+        st, p = g5.plan_query(op, 1, 12288, 4096, with_workspace=False)
+        assert st == 0 and p.name == b"decode_64" and p.grid == 192 and p.workspace_bytes == 0
+        st, p = g5.plan_query(op, 8, 384, 4100, lda=4104)
+        assert st == 0 and p.name == b"decode_64" and p.variant == 1
+        st, p = g5.plan_query(op, 8, 200, 64)
+        assert st == 0 and p.name == b"decode_64" and p.variant == 0
+        st, p = g5.plan_query(op, 17, 384, 640)
+        assert st == 0 and p.family == 2
 
 
 def test_ksplit_plans(L, monkeypatch):

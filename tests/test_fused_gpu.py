@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import gemm_inputs as gi
-from _gpu_helpers import check_silu, check_swiglu, dev_bf16, host_values, ws
+from _gpu_helpers import check_silu, check_swiglu, dev_bf16, host_bits, host_values, ws
 
 import dense_gemm_05_amd as g5
 
@@ -201,3 +201,81 @@ def test_silu_batched(oracle_mod, monkeypatch):
             check_silu(host[b, :M], oracle_mod.gemm_bf16(A[b], B[b]), oracle_mod.gemm_bf16_silu(A[b], B[b]), K,
                        f"silu {cfg} entry {b}")
         assert np.all(np.isnan(host[:, M:])), "rows between entries were written"
+
+
+# ----------------------------------------------------------------- small M
+# M <= 16 runs on the small-M kernels, which apply SiLU and SwiGLU as they
+# store: with a workspace the K-split path (for SwiGLU the gate and up
+# columns of a strip are read by separate workgroups and combined by the
+# last to finish), without one the whole-K 64-column kernel (both halves in
+# one workgroup).  K % 32 != 0 and N % 64 != 0 take the whole-K kernel's
+# general variant.
+SMALL_M = [(1, 12288, 4096), (4, 384, 640), (16, 640, 1024), (3, 200, 100), (2, 256, 4128)]
+
+
+def _small_m_plan(op, M, N, K, with_ws):
+    st, plan = g5.plan_query(op, M, N, K, with_workspace=with_ws)
+    assert st == 0 and plan.name.decode().startswith("decode"), (st, plan.name)
+    return plan.name.decode()
+
+
+@pytest.mark.parametrize("with_ws", [True, False])
+@pytest.mark.parametrize("M,N,K", SMALL_M)
+def test_silu_small_m(oracle_mod, M, N, K, with_ws):
+    cfg = _small_m_plan(g5.GEMM_OP_BF16_SILU, M, N, K, with_ws)
+    _say(f"silu small M {M}x{N}x{K} ws={with_ws} -> {cfg}")
+    A, B = gi.small_case("bf16", M, N, K, seed=23, scale_b=0.125)
+    Y = g5.gemm_bf16_silu(dev_bf16(A), dev_bf16(B), workspace=ws() if with_ws else None)
+    torch.cuda.synchronize()
+    G = oracle_mod.gemm_bf16(A, B)
+    check_silu(host_values(Y), G, oracle_mod.gemm_bf16_silu(A, B), K, f"silu {M}x{N}x{K} {cfg}")
+
+
+@pytest.mark.parametrize("with_ws", [True, False])
+@pytest.mark.parametrize("M,N,K", SMALL_M)
+def test_swiglu_small_m(oracle_mod, M, N, K, with_ws):
+    cfg = _small_m_plan(g5.GEMM_OP_BF16_SWIGLU, M, N, K, with_ws)
+    _say(f"swiglu small M {M}x{N}x{K} ws={with_ws} -> {cfg}")
+    X, Wgu = _swiglu_case(M, N, K, 7)
+    Z = g5.gemm_bf16_swiglu(dev_bf16(X), dev_bf16(Wgu), workspace=ws() if with_ws else None)
+    torch.cuda.synchronize()
+    Zr, G, U, t, u = _swiglu_ref(oracle_mod, X, Wgu)
+    check_swiglu(host_values(Z), G, U, t, u, Zr, K, f"swiglu {M}x{N}x{K} {cfg}")
+
+
+@pytest.mark.parametrize("with_ws", [True, False])
+def test_small_m_fused_rows_independent_of_m(with_ws):
+    """The small-M kernels split K the same way for every row count, so a
+    row's SiLU or SwiGLU output does not depend on how many rows the call
+    has: the first 3 rows of a 16-row call equal a 3-row call, bit for bit."""
+    M, N, K = 16, 1024, 2048
+    X, Wgu = _swiglu_case(M, N, K, 8)
+    dX, dW = dev_bf16(X), dev_bf16(Wgu)
+    w = ws() if with_ws else None
+    z16 = host_bits(g5.gemm_bf16_swiglu(dX, dW, workspace=w))
+    z3 = host_bits(g5.gemm_bf16_swiglu(dX[:3].contiguous(), dW, workspace=w))
+    y16 = host_bits(g5.gemm_bf16_silu(dX, dW[:, :N].contiguous(), workspace=w))
+    y3 = host_bits(g5.gemm_bf16_silu(dX[:3].contiguous(), dW[:, :N].contiguous(), workspace=w))
+    assert np.array_equal(z16[:3], z3)
+    assert np.array_equal(y16[:3], y3)
+
+
+@pytest.mark.parametrize("broadcast_x", [False, True])
+@pytest.mark.parametrize("with_ws", [True, False])
+def test_swiglu_batched_small_m(oracle_mod, broadcast_x, with_ws):
+    """Batched SwiGLU with a few tokens per expert (the small-M kernels take
+    the batch as their second grid dimension)."""
+    batch, M, N, K = 4, 5, 384, 512
+    st, plan = g5.plan_query(g5.GEMM_OP_BF16_SWIGLU, M, N, K, batch=batch, with_workspace=with_ws)
+    assert st == 0 and plan.name.decode().startswith("decode"), (st, plan.name)
+    g = np.random.default_rng([gi.SEED_BASE + 4200, int(broadcast_x)])
+    X = gi.to_bf16_bits(gi.normal(g, (1 if broadcast_x else batch, M, K)))
+    Wgu = gi.to_bf16_bits(gi.normal(g, (batch, K, 2 * N), 0.125))
+    dX = dev_bf16(X)
+    if broadcast_x:
+        dX = dX.expand(batch, -1, -1)
+    Z = g5.gemm_bf16_swiglu_batched(dX, dev_bf16(Wgu), workspace=ws() if with_ws else None)
+    got = host_values(Z)
+    for b in range(batch):
+        Zr, G, U, t, u = _swiglu_ref(oracle_mod, X[0 if broadcast_x else b], Wgu[b])
+        check_swiglu(got[b], G, U, t, u, Zr, K, f"swiglu small-M expert {b}")

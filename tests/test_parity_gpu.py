@@ -199,6 +199,23 @@ def test_decode_full_size(oracle_mod, M, with_ws):
     check_bf16(host_values(C), ref, 4096, f"decode M={M}")
 
 
+@pytest.mark.parametrize("with_ws", [True, False])
+@pytest.mark.parametrize("M", [1, 16])
+def test_decode_one_slice_direct(oracle_mod, M, with_ws):
+    """Decode rows against a weight with 192 strips of 128 columns (the
+    merged gate|up weight [4096, 24576]): one workgroup per strip over all
+    of K, stored directly with or without a workspace; every element."""
+    N, K = 24576, 4096
+    st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K, with_workspace=with_ws)
+    assert st == 0 and plan.name == b"decode_splitk" and plan.grid == 192 and plan.workspace_bytes == 0
+    _say(f"decode one slice M={M} N={N} workspace={with_ws}")
+    X, Wgu = gi.swiglu_inputs(16, K, N // 2)
+    X = np.ascontiguousarray(X[:M])
+    C = g5.gemm_bf16(dev_bf16(X), dev_bf16(Wgu), workspace=ws() if with_ws else None)
+    ref = oracle_mod.gemm_bf16(X, Wgu)
+    check_bf16(host_values(C), ref, K, f"decode one slice M={M}")
+
+
 @pytest.mark.parametrize("cfg", ["decode_64"])
 @pytest.mark.parametrize("M,N,K,batch", [(7, 1000, 1000, 1), (1, 512, 4096, 1), (16, 1536, 520, 1),
                                          (4, 1000, 264, 3), (3, 2048, 24, 1), (5, 130, 31, 2)])
