@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "decode_swiglu", "sgemm", "batched", "ragged", "swiglu", "shard", "fp8", "scores_nt", "decode_nt", "affine", "linear_nt", "wgrad_tn", "copy"])
+    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "decode_swiglu", "sgemm", "batched", "ragged", "swiglu", "shard", "fp8", "scores_nt", "decode_nt", "fp8_example_5_8", "affine", "linear_nt", "wgrad_tn", "copy"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--batches", type=int, default=7, help="timed batches per workload (median reported)")
@@ -494,6 +494,42 @@ def main():
                               "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "alg_bytes": alg, "rotations": Rd})
             del qXd, dCd, qW2
         del qW
+
+    # ------------------------------------------------------------ FP8, Example 5-8's shape
+    if args.only in ("all", "fp8_example_5_8"):
+        # A [4096, 4096] (bf16 here, fp16 on the page) quantized per row on
+        # every call, then multiplied by an FP8 weight stored [4096, 1536]
+        # (quantized per output column once, into Bt), 16-bit output: the
+        # separate quantization the page's traffic count favours (444 MiB
+        # with 128x128 tiles, against 620 MiB fused into the GEMM).
+        import ctypes
+        M, N, K = 4096, 1536, 4096
+        g = np.random.default_rng([gi.SEED_BASE + 7400])
+        X = gi.to_bf16_bits(gi.normal(g, (M, K)))
+        W = gi.to_bf16_bits(gi.normal(g, (K, N), 0.125))
+        R = rotations(2 * M * K + M * K + K * N + 2 * M * N)
+        dX = [to_dev_bf16(X) for _ in range(R)]
+        qW = [g5.gemm_fp8_quantize_cols(to_dev_bf16(W)) for _ in range(R)]
+        qX = [g5.gemm_fp8_quantize_rows(dX[i]) for i in range(R)]
+        dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        both = [(lambda i=i: (g5.gemm_fp8_quantize_rows(dX[i], qX[i][0], qX[i][1]),
+                              g5.gemm_fp8_nt(qX[i][0], qX[i][1], qW[i][0], qW[i][1], dC[i], workspace=ws)))
+                for i in range(R)]
+        gemm = [(lambda i=i: g5.gemm_fp8_nt(qX[i][0], qX[i][1], qW[i][0], qW[i][1], dC[i], workspace=ws))
+                for i in range(R)]
+        ms_b = timed(both, 50, 10, label="fp8_example_5_8_quantize_and_gemm")
+        ms_g = timed(gemm, 50, 10, label="fp8_example_5_8_gemm")
+        sep, fus = ctypes.c_double(), ctypes.c_double()
+        g5.lib().gemm_model_quant_traffic(M, N, K, 128, 128, 2, 1, 1, 2, ctypes.byref(sep), ctypes.byref(fus))
+        tf = 2.0 * M * N * K / (ms_g * 1e-3) / 1e12
+        log(f"fp8 Example 5-8 4096x1536x4096: quantize + GEMM {ms_b * 1e3:.2f} us, GEMM {ms_g * 1e3:.2f} us "
+            f"({tf:.1f} TFLOPS); model traffic separate {sep.value / 2**20:.0f} MiB, fused {fus.value / 2**20:.0f} MiB")
+        workloads.append({"name": "fp8_example_5_8_4096x1536x4096", "us": round(ms_b * 1e3, 3),
+                          "gemm_us": round(ms_g * 1e3, 3), "gemm_tflops": round(tf, 2),
+                          "gemm_frac_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                          "model_traffic_separate_MiB": round(sep.value / 2**20, 1),
+                          "model_traffic_fused_MiB": round(fus.value / 2**20, 1), "rotations": R})
+        del dX, qW, qX, dC
 
     # ------------------------------------------------------------ attention scores from row-major K
     if args.only in ("all", "scores_nt"):

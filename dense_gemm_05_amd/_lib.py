@@ -29,6 +29,7 @@ GEMM_OP_BF16_AFFINE = 6
 GEMM_OP_BF16_TN = 7
 GEMM_OP_BF16_NT_AFFINE = 8
 GEMM_OP_BF16_TN_AFFINE = 9
+GEMM_OP_FP8_NT_AFFINE = 10
 
 GEMM_FAMILY = {0: "none", 1: "zero", 2: "bf16_mfma", 3: "f32_mfma", 4: "decode", 5: "generic"}
 
@@ -36,7 +37,8 @@ GEMM_FAMILY = {0: "none", 1: "zero", 2: "bf16_mfma", 3: "f32_mfma", 4: "decode",
 EXPORTS = ("gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm_bf16_nt_batched",
            "gemm_bf16_tn", "gemm_bf16_tn_batched",
            "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_bf16_silu_batched", "gemm_bf16_swiglu_batched",
-           "gemm_fp8_quantize_rows", "gemm_fp8_nt", "gemm_bf16_affine", "gemm_bf16_nt_affine",
+           "gemm_fp8_quantize_rows", "gemm_fp8_quantize_cols", "gemm_fp8_nt", "gemm_fp8_nt_batched",
+           "gemm_fp8_nt_affine", "gemm_bf16_affine", "gemm_bf16_nt_affine",
            "gemm_bf16_tn_affine", "gemm_run", "gemm_run_noalloc", "gemm_workspace_size",
            "gemm_status_string",
            "gemm_plan_query", "gemm_plan_query_ex", "gemm_model_local_bytes", "gemm_model_traffic_bytes", "gemm_model_quant_traffic",
@@ -86,8 +88,15 @@ def lib():
     L.gemm_bf16_tn_batched.restype = i32
     L.gemm_fp8_quantize_rows.argtypes = [i64, i64, p, i64, p, i64, p, p]
     L.gemm_fp8_quantize_rows.restype = i32
+    L.gemm_fp8_quantize_cols.argtypes = [i64, i64, p, i64, p, i64, p, p]
+    L.gemm_fp8_quantize_cols.restype = i32
     L.gemm_fp8_nt.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, p, i64, i32, p]
     L.gemm_fp8_nt.restype = i32
+    L.gemm_fp8_nt_batched.argtypes = [i64, i64, i64, i64, p, i64, i64, p, p, i64, i64, p, p, i64, i64, i32, p]
+    L.gemm_fp8_nt_batched.restype = i32
+    L.gemm_fp8_nt_affine.argtypes = [i64, i64, i64, i64, p, i64, i64, p, p, i64, i64, p, ctypes.c_float, p,
+                                     ctypes.c_float, p, i64, i64, i32, p]
+    L.gemm_fp8_nt_affine.restype = i32
     L.gemm_bf16_affine.argtypes = [i64, i64, i64, i64, p, i64, i64, p, i64, i64, ctypes.c_float, p, ctypes.c_float,
                                    p, i64, i64, i32, p]
     L.gemm_bf16_affine.restype = i32

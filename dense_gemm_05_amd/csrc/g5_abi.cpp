@@ -83,15 +83,23 @@ int decode_slices(int64_t strips, int64_t K)
     return ks < 1 ? 1 : (int)ks;
 }
 
-int elem_a(const Problem &p) { return p.op == GEMM_OP_SGEMM ? 4 : p.op == GEMM_OP_FP8_NT ? 1 : 2; }
+// E4M3FN operands (A and Bt codes with per-row factors).
+bool is_fp8(const Problem &p) { return p.op == GEMM_OP_FP8_NT || p.op == GEMM_OP_FP8_NT_AFFINE; }
+int elem_a(const Problem &p) { return p.op == GEMM_OP_SGEMM ? 4 : is_fp8(p) ? 1 : 2; }
 // K per stage of the LDS-ring kernels: 64-byte slot rows of bf16 or fp8.
-int stage_k(const Problem &p) { return p.op == GEMM_OP_FP8_NT ? 64 : 32; }
+int stage_k(const Problem &p) { return is_fp8(p) ? 64 : 32; }
+// Batch strides of the fp8 factors (floats): an operand shared by every
+// batch entry (stride 0, or a single entry) shares its factors too; else
+// entry b's factors follow entry b-1's (M of A's rows, N of Bt's).
+int64_t scale_stride_a(const Problem &p) { return p.batch > 1 && p.sA != 0 ? p.M : 0; }
+int64_t scale_stride_b(const Problem &p) { return p.batch > 1 && p.sB != 0 ? p.N : 0; }
 // Fused epilogue of an operation (EPI_NONE for the plain products).
 int epi_of(const Problem &p)
 {
     return p.op == GEMM_OP_BF16_SILU     ? EPI_SILU
            : p.op == GEMM_OP_BF16_SWIGLU ? EPI_SWIGLU
-           : p.op == GEMM_OP_BF16_AFFINE || p.op == GEMM_OP_BF16_NT_AFFINE || p.op == GEMM_OP_BF16_TN_AFFINE
+           : p.op == GEMM_OP_BF16_AFFINE || p.op == GEMM_OP_BF16_NT_AFFINE || p.op == GEMM_OP_BF16_TN_AFFINE ||
+                   p.op == GEMM_OP_FP8_NT_AFFINE
                ? EPI_AFFINE
                : EPI_NONE;
 }
@@ -101,7 +109,7 @@ bool no_product(const Problem &p) { return is_affine(p) && p.alpha == 0.0f; }
 // B is given transposed, Bt [N, K].
 bool b_trans(const Problem &p)
 {
-    return p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_FP8_NT || p.op == GEMM_OP_BF16_NT_AFFINE;
+    return p.op == GEMM_OP_BF16_NT || is_fp8(p) || p.op == GEMM_OP_BF16_NT_AFFINE;
 }
 // A is given transposed, At [K, M].
 bool a_trans(const Problem &p) { return p.op == GEMM_OP_BF16_TN || p.op == GEMM_OP_BF16_TN_AFFINE; }
@@ -149,14 +157,14 @@ int validate(const Problem &p)
 {
     if (p.op != GEMM_OP_SGEMM && p.op != GEMM_OP_BF16 && p.op != GEMM_OP_BF16_SILU && p.op != GEMM_OP_BF16_SWIGLU &&
         p.op != GEMM_OP_BF16_NT && p.op != GEMM_OP_FP8_NT && p.op != GEMM_OP_BF16_AFFINE && p.op != GEMM_OP_BF16_TN &&
-        p.op != GEMM_OP_BF16_NT_AFFINE && p.op != GEMM_OP_BF16_TN_AFFINE)
+        p.op != GEMM_OP_BF16_NT_AFFINE && p.op != GEMM_OP_BF16_TN_AFFINE && p.op != GEMM_OP_FP8_NT_AFFINE)
         return GEMM_ERR_INVALID_ARG;
     if (p.batch < 0 || p.M < 0 || p.N < 0 || p.K < 0) return GEMM_ERR_INVALID_ARG;
-    if ((p.op == GEMM_OP_BF16 || p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_FP8_NT || is_affine(p) ||
+    if ((p.op == GEMM_OP_BF16 || p.op == GEMM_OP_BF16_NT || is_fp8(p) || is_affine(p) ||
          p.op == GEMM_OP_BF16_TN) &&
         p.c_type != GEMM_OUT_BF16 && p.c_type != GEMM_OUT_F32)
         return GEMM_ERR_INVALID_ARG;
-    if (p.op == GEMM_OP_FP8_NT && (p.batch > 1 || (p.scale_a % 4) || (p.scale_b % 4))) return GEMM_ERR_INVALID_ARG;
+    if (is_fp8(p) && ((p.scale_a % 4) || (p.scale_b % 4))) return GEMM_ERR_INVALID_ARG;
     if ((p.op == GEMM_OP_BF16_SILU || p.op == GEMM_OP_BF16_SWIGLU) && p.c_type != GEMM_OUT_BF16)
         return GEMM_ERR_INVALID_ARG;
     if (is_affine(p) && (!std::isfinite(p.alpha) || !std::isfinite(p.beta) || (p.bias % 2)))
@@ -174,10 +182,10 @@ int validate(const Problem &p)
     const Range rb = extent(p.b, p.batch, b_rows(p), b_cols(p), p.ldb, p.sB, elem_a(p));
     if (ra.hi > ((__int128)1 << 63) || rb.hi > ((__int128)1 << 63)) return GEMM_ERR_INVALID_ARG;
     if (overlap(rc, ra) || overlap(rc, rb)) return GEMM_ERR_INVALID_ARG;
-    if (p.scale_a && overlap(rc, Range{(__int128)p.scale_a, (__int128)p.scale_a + 4 * (__int128)p.M}))
-        return GEMM_ERR_INVALID_ARG;
-    if (p.scale_b && overlap(rc, Range{(__int128)p.scale_b, (__int128)p.scale_b + 4 * (__int128)p.N}))
-        return GEMM_ERR_INVALID_ARG;
+    const __int128 na = (__int128)(p.batch - 1) * scale_stride_a(p) + p.M;
+    const __int128 nb = (__int128)(p.batch - 1) * scale_stride_b(p) + p.N;
+    if (p.scale_a && overlap(rc, Range{(__int128)p.scale_a, (__int128)p.scale_a + 4 * na})) return GEMM_ERR_INVALID_ARG;
+    if (p.scale_b && overlap(rc, Range{(__int128)p.scale_b, (__int128)p.scale_b + 4 * nb})) return GEMM_ERR_INVALID_ARG;
     return GEMM_OK;
 }
 
@@ -408,7 +416,7 @@ int select_plan(const Problem &p, Plan &pl, bool ws)
         // staged at once (one load latency per tile instead of one per slab;
         // 256^3 measured 9.4 us with the double-buffered 64x64 kernel).
         pl.config = CFG_F32_32x32_WK;
-    } else if ((p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_BF16_NT_AFFINE || p.op == GEMM_OP_FP8_NT) && p.M <= 16 &&
+    } else if ((p.op == GEMM_OP_BF16_NT || p.op == GEMM_OP_BF16_NT_AFFINE || is_fp8(p)) && p.M <= 16 &&
                p.batch <= 65535 && pl.align_b >= 16) {
         // Small M with B transposed: a GEMV over the contiguous rows of Bt.
         pl.config = CFG_DECODE_NT;
@@ -515,7 +523,7 @@ int select_plan(const Problem &p, Plan &pl, bool ws)
     // The fused epilogues and a transposed B exist only in the ring kernels,
     // so such a call whose rows no ring variant takes is realigned at any
     // size: Bt's rows first, then A's.
-    if (ws && kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && b_trans(p) && p.op != GEMM_OP_FP8_NT &&
+    if (ws && kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && b_trans(p) && !is_fp8(p) &&
         pl.align_b < 16) {
         pl.realign_b = true;
         pl.ldb2 = (p.K + 7) / 8 * 8;
@@ -525,7 +533,7 @@ int select_plan(const Problem &p, Plan &pl, bool ws)
         q.sB = p.N * pl.ldb2;
         pl.variant = pick_variant(q, pl, &pl.even);
     }
-    if (ws && kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && p.op != GEMM_OP_FP8_NT &&
+    if (ws && kConfigs[pl.config].family == GEMM_FAMILY_BF16_MFMA && !is_fp8(p) &&
         (pl.align_a < 16 || (a_trans(p) && p.M % 8 != 0)) &&
         ((double)p.batch * p.M * p.N * p.K >= (double)(1 << 30) || (ring_only(p) && pl.variant == 0))) {
         Problem q = p;
@@ -737,9 +745,11 @@ int run(const Problem &p, void *stream, void *ws = nullptr, size_t ws_bytes = 0)
     a.ksplit = 1;
     a.kt_per = 0;
     a.b_trans = b_trans(p) ? 1 : 0;
-    a.fp8 = p.op == GEMM_OP_FP8_NT ? 1 : 0;
+    a.fp8 = is_fp8(p) ? 1 : 0;
     a.scale_a = (const float *)p.scale_a;
     a.scale_b = (const float *)p.scale_b;
+    a.s_scale_a = scale_stride_a(p);
+    a.s_scale_b = scale_stride_b(p);
     a.alpha = p.alpha;
     a.beta = p.beta;
     a.bias = (const uint16_t *)p.bias;
@@ -852,6 +862,32 @@ int gemm_fp8_nt(int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda, 
     return g5::run(p, stream);
 }
 
+int gemm_fp8_nt_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
+                        int64_t strideA, const float *scale_a, const uint8_t *Bt, int64_t ldbt, int64_t strideBt,
+                        const float *scale_b, void *C, int64_t ldc, int64_t strideC, int c_type, void *stream)
+{
+    Problem p{GEMM_OP_FP8_NT, batch, M, N, K, (uint64_t)A, (uint64_t)Bt, (uint64_t)C, lda, ldbt, ldc, strideA,
+              strideBt, strideC, c_type};
+    p.scale_a = (uint64_t)scale_a;
+    p.scale_b = (uint64_t)scale_b;
+    return g5::run(p, stream);
+}
+
+int gemm_fp8_nt_affine(int64_t batch, int64_t M, int64_t N, int64_t K, const uint8_t *A, int64_t lda,
+                       int64_t strideA, const float *scale_a, const uint8_t *Bt, int64_t ldbt, int64_t strideBt,
+                       const float *scale_b, float alpha, const uint16_t *bias, float beta, void *C, int64_t ldc,
+                       int64_t strideC, int c_type, void *stream)
+{
+    Problem p{GEMM_OP_FP8_NT_AFFINE, batch, M, N, K, (uint64_t)A, (uint64_t)Bt, (uint64_t)C, lda, ldbt, ldc, strideA,
+              strideBt, strideC, c_type};
+    p.scale_a = (uint64_t)scale_a;
+    p.scale_b = (uint64_t)scale_b;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.bias = (uint64_t)bias;
+    return g5::run(p, stream);
+}
+
 int gemm_fp8_quantize_rows(int64_t rows, int64_t cols, const uint16_t *X, int64_t ldx, uint8_t *Q, int64_t ldq,
                            float *scale, void *stream)
 {
@@ -869,6 +905,27 @@ int gemm_fp8_quantize_rows(int64_t rows, int64_t cols, const uint16_t *X, int64_
     if (st != GEMM_OK) return st;
     const hipError_t e = g5::launch_quant_rows_e4m3(X, ldx, rows, cols, g5::row_alignment((uint64_t)X, ldx, 0, 1, 2),
                                                     Q, ldq, g5::row_alignment((uint64_t)Q, ldq, 0, 1, 1), scale,
+                                                    (hipStream_t)stream);
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
+int gemm_fp8_quantize_cols(int64_t K, int64_t N, const uint16_t *W, int64_t ldw, uint8_t *Qt, int64_t ldq,
+                           float *scale, void *stream)
+{
+    if (K < 0 || N < 0 || N > ((int64_t)1 << 36)) return GEMM_ERR_INVALID_ARG;
+    if (N == 0) return GEMM_OK;
+    if (!scale || ((uint64_t)scale % 4)) return GEMM_ERR_INVALID_ARG;
+    if (K > 0 && (!W || !Qt || ((uint64_t)W % 2) || ldw < N || ldq < K)) return GEMM_ERR_INVALID_ARG;
+    const g5::Range rs{(__int128)(uint64_t)scale, (__int128)(uint64_t)scale + 4 * (__int128)N};
+    if (K > 0) {
+        const g5::Range rw = g5::extent((uint64_t)W, 1, K, N, ldw, 0, 2);
+        const g5::Range rq = g5::extent((uint64_t)Qt, 1, N, K, ldq, 0, 1);
+        if (g5::overlap(rw, rq) || g5::overlap(rs, rw) || g5::overlap(rs, rq)) return GEMM_ERR_INVALID_ARG;
+    }
+    int st = g5::check_device();
+    if (st != GEMM_OK) return st;
+    const hipError_t e = g5::launch_quant_cols_e4m3(W, ldw, K, N, g5::row_alignment((uint64_t)W, ldw, 0, 1, 2), Qt, ldq,
+                                                    g5::row_alignment((uint64_t)Qt, ldq, 0, 1, 1), scale,
                                                     (hipStream_t)stream);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
@@ -1030,11 +1087,12 @@ static g5::Problem run_problem(int op, int64_t batch, int64_t M, int64_t N, int6
               op == GEMM_OP_SGEMM ? (int)GEMM_OUT_F32
               : (op == GEMM_OP_BF16_SILU || op == GEMM_OP_BF16_SWIGLU) ? (int)GEMM_OUT_BF16
                                                                         : c_type};
-    if (op == GEMM_OP_FP8_NT) {
+    if (op == GEMM_OP_FP8_NT || op == GEMM_OP_FP8_NT_AFFINE) {
         p.scale_a = (uint64_t)scale_a;
         p.scale_b = (uint64_t)scale_b;
     }
-    if (op == GEMM_OP_BF16_AFFINE || op == GEMM_OP_BF16_NT_AFFINE || op == GEMM_OP_BF16_TN_AFFINE) {
+    if (op == GEMM_OP_BF16_AFFINE || op == GEMM_OP_BF16_NT_AFFINE || op == GEMM_OP_BF16_TN_AFFINE ||
+        op == GEMM_OP_FP8_NT_AFFINE) {
         p.alpha = alpha;
         p.beta = beta;
         p.bias = (uint64_t)bias;
@@ -1047,7 +1105,7 @@ int gemm_run(int op, int64_t batch, int64_t M, int64_t N, int64_t K, const void 
              float alpha, const uint16_t *bias, float beta, const float *scale_a, const float *scale_b,
              void *workspace, uint64_t workspace_bytes, void *stream)
 {
-    if (op < GEMM_OP_SGEMM || op > GEMM_OP_BF16_TN_AFFINE) return GEMM_ERR_INVALID_ARG;
+    if (op < GEMM_OP_SGEMM || op > GEMM_OP_FP8_NT_AFFINE) return GEMM_ERR_INVALID_ARG;
     if (op == GEMM_OP_SGEMM && batch != 1) return GEMM_ERR_INVALID_ARG;
     const Problem p = run_problem(op, batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, c_type, alpha,
                                   bias, beta, scale_a, scale_b);
@@ -1059,7 +1117,7 @@ int gemm_run_noalloc(int op, int64_t batch, int64_t M, int64_t N, int64_t K, con
                      int64_t strideC, int c_type, float alpha, const uint16_t *bias, float beta,
                      const float *scale_a, const float *scale_b, void *stream)
 {
-    if (op < GEMM_OP_SGEMM || op > GEMM_OP_BF16_TN_AFFINE) return GEMM_ERR_INVALID_ARG;
+    if (op < GEMM_OP_SGEMM || op > GEMM_OP_FP8_NT_AFFINE) return GEMM_ERR_INVALID_ARG;
     if (op == GEMM_OP_SGEMM && batch != 1) return GEMM_ERR_INVALID_ARG;
     const Problem p = run_problem(op, batch, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, c_type, alpha,
                                   bias, beta, scale_a, scale_b);

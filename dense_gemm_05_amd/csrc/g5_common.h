@@ -77,6 +77,8 @@ struct GemmArgs {
     int32_t fp8;             // 1: A and Bt hold E4M3FN codes (with b_trans)
     const float *scale_a;    // fp8: factor of each row of A (M floats) or NULL
     const float *scale_b;    // fp8: factor of each row of Bt (N floats) or NULL
+    int64_t s_scale_a;       // fp8: batch strides of the factors (floats; 0: shared by every entry)
+    int64_t s_scale_b;
     float *ws_part;
     unsigned *ws_cnt;
     // EPI_AFFINE: C := alpha * (A.B) + bias[n] + beta * C (C read only when

@@ -69,6 +69,39 @@ __device__ __forceinline__ u32x4 epi_swiglu8(u32x4 g, u32x4 u)
     return z;
 }
 
+// One output element of the small-M kernels: the FP32 sum of batch entry
+// b, or with the affine epilogue alpha * sum + bias[n] + beta * C[m][n]
+// (C read only when beta != 0), rounded once to C's type.
+__device__ __forceinline__ void store_out(const GemmArgs &p, int64_t b, int64_t m, int64_t n, float sum)
+{
+    const int64_t off = b * p.sC + m * p.ldc + n;
+    if (p.affine) {
+        float t = p.bias ? __uint_as_float((uint32_t)p.bias[n] << 16) : 0.f;
+        if (p.beta != 0.f) {
+            const float old = p.out_f32 ? ((const float *)p.C)[off]
+                                        : __uint_as_float((uint32_t)((const uint16_t *)p.C)[off] << 16);
+            t = __builtin_fmaf(p.beta, old, t);
+        }
+        sum = __builtin_fmaf(p.alpha, sum, t);
+    }
+    // SiLU of the bf16-rounded product, rounded again (as the ring kernels'
+    // fused epilogue: the roundings of the unfused program)
+    if (p.epi == EPI_SILU) sum = silu_f32(__uint_as_float(bf16_rne(sum) << 16));
+    if (p.out_f32) ((float *)p.C)[off] = sum;
+    else ((uint16_t *)p.C)[off] = (uint16_t)bf16_rne(sum);
+}
+
+// The SwiGLU output of the small-M kernels ("Operator & Runtime" §5.3.1):
+// z = bf16(t * u) with t = bf16(SiLU(bf16(g))), u = bf16(u) -- the gate and
+// up FP32 sums each rounded once as the unfused products would be; t * u is
+// exact in FP32.
+__device__ __forceinline__ void store_swiglu(const GemmArgs &p, int64_t b, int64_t m, int64_t n, float g, float u)
+{
+    const float t = __uint_as_float(bf16_rne(silu_f32(__uint_as_float(bf16_rne(g) << 16))) << 16);
+    const float ub = __uint_as_float(bf16_rne(u) << 16);
+    ((uint16_t *)p.C)[b * p.sC + m * p.ldc + n] = (uint16_t)bf16_rne(t * ub);
+}
+
 // Load 8 consecutive bf16 elements (one 16-byte chunk) starting at element
 // `col` of a row, zero for elements at or beyond `limit` or when the row is
 // out of range.  `align` is the byte alignment of the row start (16/8/4/2);
@@ -477,9 +510,9 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
 //    otherwise each 16-byte fragment feeds two v_mfma_f32_16x16x32_fp8_fp8
 //    (the first takes bytes 0-7 of every lane, the second bytes 8-15: one
 //    permutation of K, the same for both operands).  The FP32 sums are
-//    multiplied by p.scale_a[row] and
-//    p.scale_b[column] before the epilogue ("Operator & Runtime" §5.4.3,
-//    Example 5-7: dequantization by the row's factor).
+//    multiplied by p.scale_a[row] and p.scale_b[column] (of the batch
+//    entry) before the epilogue, plain or affine ("Operator & Runtime"
+//    §5.4.3, Example 5-7: dequantization by the row's factor).
 // One output tile of the bf16 LDS-ring kernel, as device functions that the
 // tile kernels below call: `accumulate` multiplies K columns
 // [kbase, kbase + K) of the tile's A row panel and B column panel into the
@@ -493,7 +526,7 @@ struct RingTile {
     static constexpr int BK = 32;                                    // slot row: 32 bf16 = 64 bytes
     static constexpr int EB = F8 ? 1 : 2;                            // bytes per operand element
     static constexpr int KS = 64 / EB;                               // K per stage
-    static_assert(!F8 || (BT && EPI == EPI_NONE), "fp8 operands: A and Bt, no fused epilogue");
+    static_assert(!F8 || (BT && (EPI == EPI_NONE || EPI == EPI_AFFINE)), "fp8 operands: A and Bt, plain or affine epilogue");
     static_assert(!AT || (!F8 && !BT && AV == 16 && (EPI == EPI_NONE || EPI == EPI_AFFINE)),
                   "transposed A: bf16, B as [K, N], plain or affine epilogue");
     static_assert(!AT || ((BM / 8) % 8 == 0 && (BM % 128 != 0 || (BM / 8) % 16 == 0)), "At slot rows: whole swizzle groups");
@@ -848,18 +881,21 @@ struct RingTile {
     const int64_t m0 = tc.tm * BM, n0 = tc.tn * (GLU ? HALF : BN);
     const int64_t M = p.M, N = p.N, lda = p.lda, ldb = p.ldb;
     if constexpr (F8) {
-        // Dequantization: the row's factor, then the column's, in FP32.
-        if (p.scale_a || p.scale_b) {
+        // Dequantization: the row's factor, then the column's, in FP32 (the
+        // batch entry's factors).
+        const float *scale_a = p.scale_a ? p.scale_a + tc.b * p.s_scale_a : nullptr;
+        const float *scale_b = p.scale_b ? p.scale_b + tc.b * p.s_scale_b : nullptr;
+        if (scale_a || scale_b) {
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
                 const int64_t m = m0 + wm * TM + fm * 16 + li;
-                const float sa = (p.scale_a && m < M) ? p.scale_a[m] : 1.0f;
+                const float sa = (scale_a && m < M) ? scale_a[m] : 1.0f;
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn) {
                     const int64_t n = n0 + wn * TN + fn * 16 + g * 4;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float sb = (p.scale_b && n + i < N) ? p.scale_b[n + i] : 1.0f;
+                        const float sb = (scale_b && n + i < N) ? scale_b[n + i] : 1.0f;
                         acc[fn][fm][i] = acc[fn][fm][i] * sa * sb;
                     }
                 }

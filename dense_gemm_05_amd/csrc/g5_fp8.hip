@@ -102,24 +102,122 @@ hipError_t launch_quant_rows_e4m3(const uint16_t *X, int64_t ldx, int64_t rows, 
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WGM, int WGN>
+// Per-column quantization of a weight W [K, N] (bf16) into the rows of
+// Qt [N, K]: column j gets the factor of its own largest magnitude and the
+// codes of the row quantizer above (same quotient, same rounding), written
+// transposed so that the FP8 products read them as Bt.  One workgroup per 64
+// columns: 8 lanes cover 128 bytes of a row (8 columns each), 32 rows per
+// pass.  Pass 1: the column maxima (per lane over its rows, then over the 32
+// lanes of a column chunk in LDS).  Pass 2: per 64-row block, every lane
+// quantizes 8 columns of 2 rows into an LDS tile laid out [column][k], and
+// the tile goes out as 64 rows of 64 code bytes.
+__global__ void __launch_bounds__(256) k_quant_cols_e4m3(const uint16_t *W, int64_t ldw, int64_t K, int64_t N,
+                                                         int align_w, uint8_t *Qt, int64_t ldq, int align_q,
+                                                         float *scale)
+{
+    constexpr int TP = 68;                   // tile pitch (bytes): 64 codes + 4, rows on different banks
+    __shared__ float red[32][65];
+    __shared__ float amax_s[64];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[64 * TP];
+    const int tid = threadIdx.x, cc = tid & 7, r0 = tid >> 3;
+    const int64_t n0 = (int64_t)blockIdx.x * 64;
+    const int64_t col = n0 + 8 * cc;
+    float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int64_t k = r0; k < K; k += 32) {
+        const u32x4 v = load_chunk8_bf16(W + k * ldw, col, N, true, align_w);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            m[2 * i] = fmaxf(m[2 * i], fabsf(bf16_lo(v[i])));
+            m[2 * i + 1] = fmaxf(m[2 * i + 1], fabsf(bf16_hi(v[i])));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[r0][8 * cc + i] = m[i];
+    __syncthreads();
+    if (tid < 64) {
+        float a = 0.f;
+        for (int r = 0; r < 32; ++r) a = fmaxf(a, red[r][tid]);
+        amax_s[tid] = a;
+        if (n0 + tid < N) scale[n0 + tid] = a / 448.0f;
+    }
+    __syncthreads();
+    float amax[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax[i] = amax_s[8 * cc + i];
+    // (see k_quant_rows_e4m3: one correctly rounded division, then the
+    // round-to-nearest-even conversion, gives the code nearest to x*448/amax)
+    auto code = [](float x, float a) -> uint32_t {
+        float y = a > 0.0f ? __fdiv_rn(x * 448.0f, a) : x * 0.0f;
+        y = y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);
+        return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xffu;
+    };
+    for (int64_t kb = 0; kb < K; kb += 64) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int kr = r0 + 32 * h;
+            const int64_t k = kb + kr;
+            const u32x4 v = k < K ? load_chunk8_bf16(W + k * ldw, col, N, true, align_w) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                tile[(8 * cc + 2 * i) * TP + kr] = (uint8_t)code(bf16_lo(v[i]), amax[2 * i]);
+                tile[(8 * cc + 2 * i + 1) * TP + kr] = (uint8_t)code(bf16_hi(v[i]), amax[2 * i + 1]);
+            }
+        }
+        __syncthreads();
+        // lane t: 16 codes (k = kb + 16 (t % 4) ..) of column n0 + t / 4
+        const int c = tid >> 2, part = (tid & 3) * 16;
+        const int64_t n = n0 + c, k = kb + part;
+        if (n < N && k < K) {
+            uint8_t *dst = Qt + n * ldq + k;
+            const uint8_t *src = tile + c * TP + part;
+            if (k + 16 <= K && align_q >= 16) {
+                const uint32_t *s4 = (const uint32_t *)src;
+                *(u32x4 *)dst = u32x4{s4[0], s4[1], s4[2], s4[3]};
+            } else {
+                for (int i = 0; i < 16 && k + i < K; ++i) dst[i] = src[i];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_quant_cols_e4m3(const uint16_t *W, int64_t ldw, int64_t K, int64_t N, int align_w, uint8_t *Qt,
+                                  int64_t ldq, int align_q, float *scale, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_quant_cols_e4m3, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, s, W, ldw, K, N, align_w, Qt,
+                       ldq, align_q, scale);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN, int EPI>
 static hipError_t launch_f8(const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
 {
     const dim3 g((unsigned)grid), b8(WGM * WGN * 64);
     if constexpr (BM == 128 && BN == 128) {
-        if (a.ksplit > 1) return launch_ring<BM, BN, WGM, WGN, 4, 4, EPI_NONE, true, true, true>(a, variant, g, b8, s);
+        if (a.ksplit > 1) return launch_ring<BM, BN, WGM, WGN, 4, 4, EPI, true, true, true>(a, variant, g, b8, s);
     }
-    return launch_ring<BM, BN, WGM, WGN, 4, 4, EPI_NONE, false, true, true>(a, variant, g, b8, s);
+    return launch_ring<BM, BN, WGM, WGN, 4, 4, EPI, false, true, true>(a, variant, g, b8, s);
+}
+
+template <int EPI>
+static hipError_t launch_f8_cfg(int config_id, const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
+{
+    switch (config_id) {
+    case CFG_BF16_256x192: return launch_f8<256, 192, 2, 4, EPI>(a, variant, grid, s);
+    case CFG_BF16_256x256: return launch_f8<256, 256, 2, 4, EPI>(a, variant, grid, s);
+    case CFG_BF16_128x128: return launch_f8<128, 128, 4, 2, EPI>(a, variant, grid, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_ring_fp8(int config_id, const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
 {
-    switch (config_id) {
-    case CFG_BF16_256x192: return launch_f8<256, 192, 2, 4>(a, variant, grid, s);
-    case CFG_BF16_256x256: return launch_f8<256, 256, 2, 4>(a, variant, grid, s);
-    case CFG_BF16_128x128: return launch_f8<128, 128, 4, 2>(a, variant, grid, s);
-    default: return hipErrorInvalidValue;
-    }
+    return launch_f8_cfg<EPI_NONE>(config_id, a, variant, grid, s);
+}
+
+hipError_t launch_ring_fp8_affine(int config_id, const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
+{
+    return launch_f8_cfg<EPI_AFFINE>(config_id, a, variant, grid, s);
 }
 
 // Small M on E4M3FN operands: C[M, N] = (X[M, K] . Bt[N, K]^T) scaled by
@@ -130,8 +228,10 @@ hipError_t launch_ring_fp8(int config_id, const GemmArgs &a, int variant, int64_
 // v_mfma_f32_16x16x32_fp8_fp8 (bytes 0-7, then 8-15: the same permutation
 // of K for both operands).  A K remainder (K % 64) is a final step loaded
 // element by element with zero fill.  The waves' partial sums are added in
-// LDS in wave order (so a row's result does not depend on M), then scaled
-// and rounded once.  Requires 16-byte aligned rows of Bt.
+// LDS in wave order (so a row's result does not depend on M), then scaled,
+// passed through the affine epilogue when the call has one, and rounded
+// once.  Batch entries are the second grid dimension.  Requires 16-byte
+// aligned rows of Bt.
 template <int NW, int RB>
 __global__ void __launch_bounds__(NW * 64) k_decode_nt_f8(GemmArgs p)
 {
@@ -139,8 +239,11 @@ __global__ void __launch_bounds__(NW * 64) k_decode_nt_f8(GemmArgs p)
     const int g = lane >> 4, li = lane & 15;
     const int64_t M = p.M, N = p.N, K = p.K, lda = p.lda, ldb = p.ldb;
     const int64_t n0 = (int64_t)blockIdx.x * 16 * RB;
-    const uint8_t *X = (const uint8_t *)p.A;
-    const uint8_t *Bt = (const uint8_t *)p.B;
+    const int64_t bidx = blockIdx.y;
+    const uint8_t *X = (const uint8_t *)p.A + bidx * p.sA;
+    const uint8_t *Bt = (const uint8_t *)p.B + bidx * p.sB;
+    const float *scale_a = p.scale_a ? p.scale_a + bidx * p.s_scale_a : nullptr;
+    const float *scale_b = p.scale_b ? p.scale_b + bidx * p.s_scale_b : nullptr;
     const bool m_ok = li < M;
     bool n_ok[RB];
     const uint8_t *brow[RB];
@@ -206,15 +309,13 @@ __global__ void __launch_bounds__(NW * 64) k_decode_nt_f8(GemmArgs p)
         for (int w2 = 1; w2 < NW; ++w2) sum += red[w2][r][t];
         const int m = t & 15, gg = t >> 4;
         if (m < M) {
-            const float sa = p.scale_a ? p.scale_a[m] : 1.0f;
+            const float sa = scale_a ? scale_a[m] : 1.0f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int64_t n = n0 + 16 * r + 4 * gg + q;
                 if (n >= N) continue;
-                const float sb = p.scale_b ? p.scale_b[n] : 1.0f;
-                const float v = sum[q] * sa * sb;
-                if (p.out_f32) ((float *)p.C)[m * p.ldc + n] = v;
-                else ((uint16_t *)p.C)[m * p.ldc + n] = (uint16_t)bf16_rne(v);
+                const float sb = scale_b ? scale_b[n] : 1.0f;
+                store_out(p, bidx, m, n, sum[q] * sa * sb);
             }
         }
     }
@@ -223,9 +324,9 @@ __global__ void __launch_bounds__(NW * 64) k_decode_nt_f8(GemmArgs p)
 hipError_t launch_decode_nt_f8(const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
 {
     if (variant == 2)
-        hipLaunchKernelGGL((k_decode_nt_f8<8, 3>), dim3((unsigned)grid), dim3(8 * 64), 0, s, a);
+        hipLaunchKernelGGL((k_decode_nt_f8<8, 3>), dim3((unsigned)grid, (unsigned)a.batch), dim3(8 * 64), 0, s, a);
     else
-        hipLaunchKernelGGL((k_decode_nt_f8<8, 1>), dim3((unsigned)grid), dim3(8 * 64), 0, s, a);
+        hipLaunchKernelGGL((k_decode_nt_f8<8, 1>), dim3((unsigned)grid, (unsigned)a.batch), dim3(8 * 64), 0, s, a);
     return hipGetLastError();
 }
 

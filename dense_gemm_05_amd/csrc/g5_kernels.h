@@ -28,6 +28,9 @@ hipError_t launch_ring_at(int config_id, const GemmArgs &a, int variant, int64_t
 // the configs 256x192, 256x256 and 128x128, the last also with K split.
 hipError_t launch_ring_fp8(int config_id, const GemmArgs &a, int variant, int64_t grid, hipStream_t s);
 
+// The same with the affine epilogue applied to the dequantized sums.
+hipError_t launch_ring_fp8_affine(int config_id, const GemmArgs &a, int variant, int64_t grid, hipStream_t s);
+
 // Small M (<= 16) on E4M3FN operands with B given transposed: variant 1
 // one 16-row block of Bt per workgroup, 2 three (grid = blocks of Bt rows).
 hipError_t launch_decode_nt_f8(const GemmArgs &a, int variant, int64_t grid, hipStream_t s);
@@ -37,6 +40,12 @@ hipError_t launch_decode_nt_f8(const GemmArgs &a, int variant, int64_t grid, hip
 // into codes Q and dequantization factors scale[rows].
 hipError_t launch_quant_rows_e4m3(const uint16_t *X, int64_t ldx, int64_t rows, int64_t cols, int align_x,
                                   uint8_t *Q, int64_t ldq, int align_q, float *scale, hipStream_t s);
+
+// Per-column E4M3FN quantization of W [K, N] (bf16, row stride ldw, rows
+// `align_w`-byte aligned) into the rows of Qt [N, K] (row stride ldq, rows
+// `align_q`-byte aligned) with the factors scale[N].
+hipError_t launch_quant_cols_e4m3(const uint16_t *W, int64_t ldw, int64_t K, int64_t N, int align_w, uint8_t *Qt,
+                                  int64_t ldq, int align_q, float *scale, hipStream_t s);
 
 // The same for a bf16 product with a fused epilogue (EPI_SILU, EPI_SWIGLU
 // or EPI_AFFINE; ring kernel variants 1-3 of the configs 256x192, 256x256

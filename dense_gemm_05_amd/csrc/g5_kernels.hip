@@ -435,39 +435,7 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_f32_wholek(GemmArgs p)
 //    maps to physical column 4r + b;
 //  * X rows (zero beyond M) are the other MFMA operand; the 16-row MFMA
 //    covers any M <= 16 at no extra memory traffic.
-// One output element of the small-M kernels: the FP32 sum of batch entry
-// b, or with the affine epilogue alpha * sum + bias[n] + beta * C[m][n]
-// (C read only when beta != 0), rounded once to C's type.
-__device__ __forceinline__ void store_out(const GemmArgs &p, int64_t b, int64_t m, int64_t n, float sum)
-{
-    const int64_t off = b * p.sC + m * p.ldc + n;
-    if (p.affine) {
-        float t = p.bias ? __uint_as_float((uint32_t)p.bias[n] << 16) : 0.f;
-        if (p.beta != 0.f) {
-            const float old = p.out_f32 ? ((const float *)p.C)[off]
-                                        : __uint_as_float((uint32_t)((const uint16_t *)p.C)[off] << 16);
-            t = __builtin_fmaf(p.beta, old, t);
-        }
-        sum = __builtin_fmaf(p.alpha, sum, t);
-    }
-    // SiLU of the bf16-rounded product, rounded again (as the ring kernels'
-    // fused epilogue: the roundings of the unfused program)
-    if (p.epi == EPI_SILU) sum = silu_f32(__uint_as_float(bf16_rne(sum) << 16));
-    if (p.out_f32) ((float *)p.C)[off] = sum;
-    else ((uint16_t *)p.C)[off] = (uint16_t)bf16_rne(sum);
-}
-
-// The SwiGLU output of the small-M kernels ("Operator & Runtime" §5.3.1):
-// z = bf16(t * u) with t = bf16(SiLU(bf16(g))), u = bf16(u) -- the gate and
-// up FP32 sums each rounded once as the unfused products would be; t * u is
-// exact in FP32.
-__device__ __forceinline__ void store_swiglu(const GemmArgs &p, int64_t b, int64_t m, int64_t n, float g, float u)
-{
-    const float t = __uint_as_float(bf16_rne(silu_f32(__uint_as_float(bf16_rne(g) << 16))) << 16);
-    const float ub = __uint_as_float(bf16_rne(u) << 16);
-    ((uint16_t *)p.C)[b * p.sC + m * p.ldc + n] = (uint16_t)bf16_rne(t * ub);
-}
-
+//
 // GLU: SwiGLU epilogue -- the workgroup's 64 output columns take their gate
 // sums from columns n of the merged weight [K, 2N] and their up sums from
 // columns N + n, both accumulated in the same pass over K.

@@ -73,7 +73,8 @@ hipError_t launch_fused(int config_id, int epi, const GemmArgs &a, int variant, 
     if (epi == EPI_SILU) return launch_fused_epi<EPI_SILU>(config_id, a, variant, grid, s);
     if (epi == EPI_SWIGLU) return launch_fused_epi<EPI_SWIGLU>(config_id, a, variant, grid, s);
     if (epi == EPI_AFFINE)
-        return a.b_trans   ? launch_affine_bt(config_id, a, variant, grid, s)
+        return a.fp8       ? launch_ring_fp8_affine(config_id, a, variant, grid, s)
+               : a.b_trans ? launch_affine_bt(config_id, a, variant, grid, s)
                : a.a_trans ? launch_affine_at(config_id, a, variant, grid, s)
                            : launch_fused_epi<EPI_AFFINE>(config_id, a, variant, grid, s);
     return hipErrorInvalidValue;

@@ -22,7 +22,8 @@ from ._lib import GEMM_ERR_WORKSPACE, GemmError, GemmPlan, lib
 __all__ = ["gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm_bf16_nt_batched",
            "gemm_bf16_tn", "gemm_bf16_tn_batched",
            "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_bf16_silu_batched", "gemm_bf16_swiglu_batched",
-           "gemm_fp8_quantize_rows", "gemm_fp8_nt", "gemm_bf16_affine",
+           "gemm_fp8_quantize_rows", "gemm_fp8_quantize_cols", "gemm_fp8_nt", "gemm_fp8_nt_affine",
+           "gemm_bf16_affine",
            "gemm_bf16_nt_affine", "gemm_bf16_tn_affine", "plan_query", "workspace_size", "Workspace",
            "GemmError"]
 
@@ -345,30 +346,109 @@ def gemm_fp8_quantize_rows(X, Q=None, scale=None):
     return Q, scale
 
 
-def gemm_fp8_nt(A, scale_a, Bt, scale_b, C=None, out_dtype=torch.bfloat16, workspace=None):
-    """C[M,N] = (dec(A) . dec(Bt)^T) * scale_a[:, None] * scale_b[None, :] for
-    E4M3FN codes A [M,K] and Bt [N,K] (gemm_fp8_nt); a scale may be None."""
+def gemm_fp8_quantize_cols(W, Qt=None, scale=None):
+    """Per-column E4M3FN quantization of a bfloat16 weight W [K, N] stored as
+    [in, out] (gemm_fp8_quantize_cols): returns (codes uint8 Qt [N, K], the
+    Bt operand of the FP8 products, and float32 factors [N])."""
+    if W.dtype != torch.bfloat16 or W.dim() != 2:
+        raise TypeError("gemm_fp8_quantize_cols takes a 2-D bfloat16 tensor")
+    K, N = W.shape
+    dev = _check_dev(W, Qt, scale)
+    if Qt is None:
+        Qt = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty((N,), dtype=torch.float32, device=dev)
+    Qt = _codes(Qt)
+    if tuple(Qt.shape) != (N, K) or tuple(scale.shape) != (N,) or scale.dtype != torch.float32:
+        raise ValueError("Qt must be [N, K] codes and scale float32 [N]")
+    if N > 1 and scale.stride(0) != 1:
+        raise ValueError("scale must be contiguous")
+    st = _launch(lib().gemm_fp8_quantize_cols, dev, K, N, W.data_ptr(), _ld(W, N), Qt.data_ptr(), _ld(Qt, K),
+                 scale.data_ptr())
+    if st != 0:
+        raise GemmError(st, "gemm_fp8_quantize_cols")
+    return Qt, scale
+
+
+def _fp8_scale(sc, shared, batch, n, what):
+    """A factor vector: [n] for an operand shared by the batch entries (or a
+    single product), else [batch, n], contiguous float32."""
+    if sc is None:
+        return None
+    want = (n,) if shared else (batch, n)
+    if sc.dtype != torch.float32 or (tuple(sc.shape) != want and not (shared and tuple(sc.shape) == (1, n))):
+        raise ValueError(f"{what} must be float32 {list(want)}")
+    if sc.numel() > 1 and not sc.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return sc
+
+
+def _fp8(A, scale_a, Bt, scale_b, C, out_dtype, workspace, affine=None):
+    """The FP8 products: 2-D operands, or stacks [batch, M, K] / [batch, N, K]
+    (stride 0 along the batch broadcasts an operand, and its factors)."""
     A, Bt = _codes(A), _codes(Bt)
-    M, K = A.shape
-    N, K2 = Bt.shape
-    if K != K2:
-        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
-    dev = _check_dev(A, Bt, C, scale_a, scale_b)
-    for sc, n, what in ((scale_a, M, "scale_a"), (scale_b, N, "scale_b")):
-        if sc is not None and (sc.dtype != torch.float32 or tuple(sc.shape) != (n,) or (n > 1 and sc.stride(0) != 1)):
-            raise ValueError(f"{what} must be a contiguous float32 vector of {n}")
+    if A.dim() != Bt.dim() or A.dim() not in (2, 3):
+        raise ValueError("A and Bt must both be 2-D or both be 3-D")
+    three = A.dim() == 3
+    A3, B3 = (A, Bt) if three else (A.unsqueeze(0), Bt.unsqueeze(0))
+    batch, M, K = A3.shape
+    b2, N, K2 = B3.shape
+    if batch != b2 or K != K2:
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, Bt {tuple(Bt.shape)}")
+    dev = _check_dev(A, Bt, C, scale_a, scale_b, None if affine is None else affine[1])
+    sA, sB = _bstride(A3), _bstride(B3)
+    scale_a = _fp8_scale(scale_a, batch == 1 or sA == 0, batch, M, "scale_a")
+    scale_b = _fp8_scale(scale_b, batch == 1 or sB == 0, batch, N, "scale_b")
     if C is None:
-        C = torch.empty((M, N), dtype=out_dtype, device=dev)
-    if C.shape != (M, N):
-        raise ValueError("C must be [M, N]")
+        if affine is not None:
+            raise ValueError("the affine FP8 product updates a given C")
+        C = torch.empty((batch, M, N) if three else (M, N), dtype=out_dtype, device=dev)
+    C3 = C if three else C.unsqueeze(0)
+    if tuple(C3.shape) != (batch, M, N):
+        raise ValueError("C must be [M, N] (or [batch, M, N])")
     code = _out_code(C.dtype)
-    lda, ldb, ldc = _ld(A, K), _ld(Bt, K), _ld(C, N)
+    lda, ldb, ldc = _ld(A3, K), _ld(B3, K), _ld(C3, N)
+    sC = _bstride(C3)
     pa = None if scale_a is None else scale_a.data_ptr()
     pb = None if scale_b is None else scale_b.data_ptr()
-    return _gemm("gemm_fp8_nt", "gemm_fp8_nt",
-                 (M, N, K, A.data_ptr(), lda, pa, Bt.data_ptr(), ldb, pb, C.data_ptr(), ldc, code), workspace, dev,
-                 _lib.GEMM_OP_FP8_NT, 1, M, N, K, A, lda, 0, Bt, ldb, 0, C, ldc, 0, code,
-                 scale_a=scale_a, scale_b=scale_b)
+    if affine is None:
+        if three:
+            named, args = "gemm_fp8_nt_batched", (batch, M, N, K, A3.data_ptr(), lda, sA, pa, B3.data_ptr(), ldb, sB,
+                                                  pb, C3.data_ptr(), ldc, sC, code)
+        else:
+            named, args = "gemm_fp8_nt", (M, N, K, A.data_ptr(), lda, pa, Bt.data_ptr(), ldb, pb, C.data_ptr(), ldc,
+                                          code)
+        _gemm(named, named, args, workspace, dev, _lib.GEMM_OP_FP8_NT, batch, M, N, K, A3, lda, sA, B3, ldb, sB,
+              C3, ldc, sC, code, scale_a=scale_a, scale_b=scale_b)
+        return C
+    alpha, bias, beta = affine
+    if bias is not None and (bias.dtype != torch.bfloat16 or tuple(bias.shape) != (N,) or
+                             (N > 1 and bias.stride(0) != 1)):
+        raise ValueError("bias must be a contiguous bfloat16 vector of N elements")
+    bp = None if bias is None else bias.data_ptr()
+    _gemm("gemm_fp8_nt_affine", "gemm_fp8_nt_affine",
+          (batch, M, N, K, A3.data_ptr(), lda, sA, pa, B3.data_ptr(), ldb, sB, pb, float(alpha), bp, float(beta),
+           C3.data_ptr(), ldc, sC, code),
+          workspace, dev, _lib.GEMM_OP_FP8_NT_AFFINE, batch, M, N, K, A3, lda, sA, B3, ldb, sB, C3, ldc, sC, code,
+          alpha=alpha, bias=bias, beta=beta, scale_a=scale_a, scale_b=scale_b)
+    return C
+
+
+def gemm_fp8_nt(A, scale_a, Bt, scale_b, C=None, out_dtype=torch.bfloat16, workspace=None):
+    """C[M,N] = (dec(A) . dec(Bt)^T) * scale_a[:, None] * scale_b[None, :] for
+    E4M3FN codes A [M,K] and Bt [N,K] (gemm_fp8_nt); a scale may be None.
+    Stacks A [batch, M, K], Bt [batch, N, K] (gemm_fp8_nt_batched) take
+    factors [batch, M] / [batch, N], or [M] / [N] for an operand broadcast
+    along the batch (stride 0)."""
+    return _fp8(A, scale_a, Bt, scale_b, C, out_dtype, workspace)
+
+
+def gemm_fp8_nt_affine(A, scale_a, Bt, scale_b, C, alpha=1.0, bias=None, beta=0.0, workspace=None):
+    """C := alpha * (dec(A) . dec(Bt)^T * scale_a * scale_b) + bias + beta * C
+    in place (gemm_fp8_nt_affine), 2-D or batched as gemm_fp8_nt; C bfloat16
+    or float32 (read when beta != 0), bias a bfloat16 vector of N or None.
+    Returns C."""
+    return _fp8(A, scale_a, Bt, scale_b, C, C.dtype, workspace, affine=(alpha, bias, beta))
 
 
 def gemm_bf16_silu(A, B, C=None, workspace=None):
@@ -518,7 +598,7 @@ def _affine(A, B, C, alpha, bias, beta, b_trans, a_trans=False, workspace=None):
 def _plan_args(op, M, N, K, batch, lda, ldb, ldc, sA, sB, sC):
     tn = op in (_lib.GEMM_OP_BF16_TN, _lib.GEMM_OP_BF16_TN_AFFINE)
     lda = (M if tn else K) if lda is None else lda
-    nt = op in (_lib.GEMM_OP_BF16_NT, _lib.GEMM_OP_FP8_NT, _lib.GEMM_OP_BF16_NT_AFFINE)
+    nt = op in (_lib.GEMM_OP_BF16_NT, _lib.GEMM_OP_FP8_NT, _lib.GEMM_OP_BF16_NT_AFFINE, _lib.GEMM_OP_FP8_NT_AFFINE)
     ldb = (2 * N if op == _lib.GEMM_OP_BF16_SWIGLU else K if nt else N) if ldb is None else ldb
     ldc = N if ldc is None else ldc
     sA = (K if tn else M) * lda if sA is None else sA

@@ -182,6 +182,21 @@ int gemm_fp8_quantize_rows(int64_t rows, int64_t cols,
                            uint8_t *Q, int64_t ldq, float *scale,
                            void *stream);
 
+/* Per-column E4M3FN quantization of a weight stored [K, N] (the layout of
+ * Example 5-8's FP8 weight): column j of W (bf16 bit patterns, K rows, row
+ * stride ldw >= N elements) is quantized with its own factor exactly as
+ * gemm_fp8_quantize_rows quantizes a row -- codes nearest to
+ * W[k][j] * 448 / amax_j, scale[j] = amax_j / 448 -- and its codes are
+ * written as row j of Qt [N, K] (row stride ldq >= K bytes), the Bt operand
+ * of the FP8 products.  Caller-owned device memory, nothing else touched;
+ * deterministic.  GEMM_ERR_INVALID_ARG: negative sizes, ldw < N or
+ * ldq < K, NULL or unaligned pointers (W 2-byte, scale 4-byte), or
+ * overlapping W, Qt and scale. */
+int gemm_fp8_quantize_cols(int64_t K, int64_t N,
+                           const uint16_t *W, int64_t ldw,
+                           uint8_t *Qt, int64_t ldq, float *scale,
+                           void *stream);
+
 /* Scaled FP8 GEMM with B given transposed:
  *     C[i][j] = (sum_k dec(A[i][k]) * dec(Bt[j][k])) * scale_a[i] * scale_b[j]
  * A [M,K] and Bt [N,K] E4M3FN codes (row strides lda, ldbt >= K, bytes);
@@ -190,13 +205,40 @@ int gemm_fp8_quantize_rows(int64_t rows, int64_t cols,
  * (rounded once, to nearest even) or float by c_type.  Layout and errors as
  * gemm_bf16_nt, with: GEMM_ERR_INVALID_ARG for unaligned scale pointers or C
  * overlapping a scale vector; GEMM_ERR_UNSUPPORTED when Bt's rows are not
- * 16-byte aligned or A's rows not 4-byte aligned.  Small M runs on the
- * tiled kernels. */
+ * 16-byte aligned or A's rows not 4-byte aligned.  M <= 16 runs on a GEMV
+ * kernel over the rows of Bt, larger M on the tiled kernels. */
 int gemm_fp8_nt(int64_t M, int64_t N, int64_t K,
                 const uint8_t *A, int64_t lda, const float *scale_a,
                 const uint8_t *Bt, int64_t ldbt, const float *scale_b,
                 void *C, int64_t ldc, int c_type,
                 void *stream);
+
+/* The same for a batch of products (e.g. the experts of a mixture-of-
+ * experts layer): entry b multiplies A + b*strideA by Bt + b*strideBt into
+ * C + b*strideC (strides in elements; a stride of 0 broadcasts an operand).
+ * An operand's factors follow its stride: a broadcast operand (stride 0, or
+ * batch 1) has one vector (scale_a[M], scale_b[N]) for every entry, else
+ * entry b's factors start at scale_a + b*M (scale_b + b*N).  Errors as
+ * gemm_fp8_nt and gemm_bf16_batched. */
+int gemm_fp8_nt_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                        const uint8_t *A, int64_t lda, int64_t strideA, const float *scale_a,
+                        const uint8_t *Bt, int64_t ldbt, int64_t strideBt, const float *scale_b,
+                        void *C, int64_t ldc, int64_t strideC, int c_type,
+                        void *stream);
+
+/* The scaled FP8 product (batched as gemm_fp8_nt_batched, batch >= 1) with
+ * the affine epilogue of gemm_bf16_affine:
+ *     C := alpha * D + bias[j] + beta * C,  D the dequantized sum above,
+ * evaluated in FP32 and rounded once to C's type (C read only when
+ * beta != 0; bias bf16 [N] or NULL, shared by the batch entries).  Layout
+ * and errors as gemm_fp8_nt_batched and gemm_bf16_affine (output rows
+ * 16-byte aligned and N % 8 == 0, else GEMM_ERR_UNSUPPORTED). */
+int gemm_fp8_nt_affine(int64_t batch, int64_t M, int64_t N, int64_t K,
+                       const uint8_t *A, int64_t lda, int64_t strideA, const float *scale_a,
+                       const uint8_t *Bt, int64_t ldbt, int64_t strideBt, const float *scale_b,
+                       float alpha, const uint16_t *bias, float beta,
+                       void *C, int64_t ldc, int64_t strideC, int c_type,
+                       void *stream);
 
 /* ---- fused epilogues ------------------------------------------------------
  *
@@ -328,10 +370,10 @@ int gemm_bf16_tn_affine(int64_t batch, int64_t M, int64_t N, int64_t K,
  * may share one.
  * Arguments: A, lda, strideA and B, ldb, strideB as the op's entry point
  * names them (A = At for the TN ops, B = Bt for the NT and FP8 ops, B = Wgu
- * for SwiGLU), batch 1 for the ops without a batched form (gemm_sgemm,
- * gemm_fp8_nt); c_type is ignored where the op fixes it (SGEMM: float;
+ * for SwiGLU), batch 1 for GEMM_OP_SGEMM (the one op without a batched
+ * form); c_type is ignored where the op fixes it (SGEMM: float;
  * SiLU, SwiGLU: bf16); alpha, bias and beta are read by the affine ops only,
- * scale_a and scale_b by GEMM_OP_FP8_NT only. */
+ * scale_a and scale_b by the FP8 ops only. */
 int gemm_run(int op, int64_t batch, int64_t M, int64_t N, int64_t K,
              const void *A, int64_t lda, int64_t strideA,
              const void *B, int64_t ldb, int64_t strideB,
@@ -424,12 +466,13 @@ typedef enum {
     GEMM_OP_BF16_SILU = 2,   /* gemm_bf16_silu(_batched) (c_type ignored) */
     GEMM_OP_BF16_SWIGLU = 3, /* gemm_bf16_swiglu(_batched) (b = Wgu, c_type ignored) */
     GEMM_OP_BF16_NT = 4,     /* gemm_bf16_nt, gemm_bf16_nt_batched (b = Bt, ldb = ldbt) */
-    GEMM_OP_FP8_NT = 5,      /* gemm_fp8_nt (batch 1, b = Bt; scales do not change the plan) */
+    GEMM_OP_FP8_NT = 5,      /* gemm_fp8_nt(_batched) (b = Bt; scales do not change the plan) */
     GEMM_OP_BF16_AFFINE = 6, /* gemm_bf16_affine with alpha = 1 (alpha, beta and bias do not change the
                                 plan; alpha == 0 plans the element-wise pass of K == 0) */
     GEMM_OP_BF16_TN = 7,     /* gemm_bf16_tn, gemm_bf16_tn_batched (a = At, lda = ldat) */
     GEMM_OP_BF16_NT_AFFINE = 8, /* gemm_bf16_nt_affine with alpha = 1 (b = Bt, ldb = ldbt) */
-    GEMM_OP_BF16_TN_AFFINE = 9  /* gemm_bf16_tn_affine with alpha = 1 (a = At, lda = ldat) */
+    GEMM_OP_BF16_TN_AFFINE = 9, /* gemm_bf16_tn_affine with alpha = 1 (a = At, lda = ldat) */
+    GEMM_OP_FP8_NT_AFFINE = 10  /* gemm_fp8_nt_affine with alpha = 1 (b = Bt, ldb = ldbt) */
 } gemm_op;
 
 /* Validate the arguments of a call and report the plan gemm_run launches

@@ -61,6 +61,9 @@ def _load():
     lib.oracle_e4m3_encode_array.argtypes = [i64, p, p]
     lib.oracle_quantize_rows_e4m3.argtypes = [i64, i64, p, i64, p, i64, p]
     lib.oracle_gemm_fp8_nt.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, p, i64]
+    lib.oracle_gemm_fp8_nt_affine.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, ctypes.c_double, p,
+                                              ctypes.c_double, p, i64, ctypes.c_int, p, i64]
+    lib.oracle_gemm_fp8_nt_affine.restype = None
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     lib.oracle_set_num_threads.restype = None
@@ -264,6 +267,42 @@ def gemm_fp8_nt(A, sa, Bt, sb):
     _load().oracle_gemm_fp8_nt(M, N, K, A.ctypes.data, lda, None if sa_p is None else sa_p.ctypes.data,
                                Bt.ctypes.data, ldb, None if sb_p is None else sb_p.ctypes.data,
                                C.ctypes.data, max(N, 1))
+    return C
+
+
+def quantize_cols_e4m3(W):
+    """Per-column E4M3FN quantization of bf16 bit patterns W [K, N] (a weight
+    stored [in, out]): column j quantized with its own factor exactly as a
+    row of quantize_rows_e4m3, returned transposed -- (codes uint8 [N, K],
+    factors float32 [N]) -- the Bt operand of gemm_fp8_nt."""
+    W = np.asarray(W, np.uint16)
+    return quantize_rows_e4m3(np.ascontiguousarray(W.T))
+
+
+def gemm_fp8_nt_affine(A, sa, Bt, sb, alpha=1.0, bias=None, beta=0.0, C_old=None):
+    """alpha * D + bias[j] + beta * C_old[i][j] in double, D = gemm_fp8_nt(A,
+    sa, Bt, sb); bias and a bf16 C_old as bf16 bit patterns, or a float32
+    C_old."""
+    A, lda = _rows(A, np.uint8)
+    Bt, ldb = _rows(Bt, np.uint8)
+    M, K = A.shape
+    N, K2 = Bt.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    sa_p = np.ascontiguousarray(sa, np.float32) if sa is not None else None
+    sb_p = np.ascontiguousarray(sb, np.float32) if sb is not None else None
+    bias_p = None if bias is None else np.ascontiguousarray(bias, np.uint16)
+    if beta != 0.0:
+        old_f32 = C_old.dtype == np.float32
+        C_old, ldo = _rows(C_old, np.float32 if old_f32 else np.uint16)
+        old_p = C_old.ctypes.data
+    else:
+        old_f32, ldo, old_p = False, 1, None
+    C = np.empty((M, N), np.float64)
+    _load().oracle_gemm_fp8_nt_affine(M, N, K, A.ctypes.data, lda, None if sa_p is None else sa_p.ctypes.data,
+                                      Bt.ctypes.data, ldb, None if sb_p is None else sb_p.ctypes.data, float(alpha),
+                                      None if bias_p is None else bias_p.ctypes.data, float(beta), old_p, ldo,
+                                      int(old_f32), C.ctypes.data, max(N, 1))
     return C
 
 

@@ -400,6 +400,30 @@ void oracle_gemm_fp8_nt(int64_t M, int64_t N, int64_t K,
         }
 }
 
+/* The scaled FP8 product followed by the affine epilogue of the bf16 path:
+ * C = alpha * D + bias[j] + beta * C_old[i][j] with D as oracle_gemm_fp8_nt
+ * computes it, in double (bias and a bf16 C_old widened exactly). */
+void oracle_gemm_fp8_nt_affine(int64_t M, int64_t N, int64_t K,
+                               const uint8_t *A, int64_t lda, const float *sa,
+                               const uint8_t *Bt, int64_t ldb, const float *sb,
+                               double alpha, const uint16_t *bias, double beta,
+                               const void *C_old, int64_t ldc_old, int c_old_f32,
+                               double *C, int64_t ldc)
+{
+    oracle_gemm_fp8_nt(M, N, K, A, lda, sa, Bt, ldb, sb, C, ldc);
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) {
+            double v = alpha * C[i * ldc + j];
+            if (bias) v += widen_bf16(bias[j]);
+            if (beta != 0.0) {
+                const double old = c_old_f32 ? (double)((const float *)C_old)[i * ldc_old + j]
+                                             : widen_bf16(((const uint16_t *)C_old)[i * ldc_old + j]);
+                v += beta * old;
+            }
+            C[i * ldc + j] = v;
+        }
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -669,3 +669,34 @@ def test_library_source_allocates_nothing():
             with open(os.path.join(csrc, name)) as fh:
                 for i, line in enumerate(fh, 1):
                     assert not banned.search(line), f"{name}:{i}: {line.strip()}"
+
+
+def test_fp8_batched_affine_and_cols_arguments(L):
+    """FP8: batched products and the affine op plan like their bf16
+    counterparts (small M on the GEMV over Bt's rows); factor vectors are
+    checked against C over every batch entry; the column quantizer
+    validates before touching the GPU."""
+    st, p = g5.plan_query(g5.GEMM_OP_FP8_NT, 300, 392, 256, batch=3)
+    assert st == 0 and p.family == 2
+    st, p = g5.plan_query(g5.GEMM_OP_FP8_NT, 5, 392, 256, batch=3)
+    assert st == 0 and p.name == b"decode_nt"
+    st, p = g5.plan_query(g5.GEMM_OP_FP8_NT_AFFINE, 7, 200, 144)
+    assert st == 0 and p.name == b"decode_nt"
+    st, p = g5.plan_query(g5.GEMM_OP_FP8_NT_AFFINE, 1024, 12288, 4096)
+    assert st == 0 and p.name == b"bf16_256x192" and p.grid == 256
+    st, _ = g5.plan_query(g5.GEMM_OP_FP8_NT_AFFINE, 300, 392, 256, ldc=396, c_addr=C_ADDR + 8)
+    assert st == g5.GEMM_ERR_UNSUPPORTED                       # tiled affine: C rows 16-byte aligned
+    # C (3 x 8 x 16 floats) overlapping the last entry's factors of A
+    M, N, K, batch = 8, 16, 64, 3
+    run = lambda sa, sb, sA=M * K: L.gemm_run(g5.GEMM_OP_FP8_NT, batch, M, N, K, A_ADDR, K, sA, B_ADDR, K, N * K,
+                                            C_ADDR, N, M * N, 1, 1.0, None, 0.0, sa, sb, None, 0, None)
+    before_c = C_ADDR - 4 * (M + 1)            # M factors end 4 bytes before C; 3 M reach into it
+    assert run(before_c, None) == g5.GEMM_ERR_INVALID_ARG                        # one vector per entry
+    assert run(before_c, None, sA=0) != g5.GEMM_ERR_INVALID_ARG                  # broadcast A: M factors only
+    assert run(None, C_ADDR + 2) == g5.GEMM_ERR_INVALID_ARG                      # unaligned factors
+    q = L.gemm_fp8_quantize_cols
+    assert q(64, 32, A_ADDR, 31, B_ADDR, 64, C_ADDR, None) == g5.GEMM_ERR_INVALID_ARG    # ldw < N
+    assert q(64, 32, A_ADDR, 32, B_ADDR, 63, C_ADDR, None) == g5.GEMM_ERR_INVALID_ARG    # ldq < K
+    assert q(64, 32, A_ADDR + 1, 32, B_ADDR, 64, C_ADDR, None) == g5.GEMM_ERR_INVALID_ARG  # W not 2-byte aligned
+    assert q(64, 32, A_ADDR, 32, A_ADDR + 100, 64, C_ADDR, None) == g5.GEMM_ERR_INVALID_ARG  # Qt overlaps W
+    assert q(64, 0, None, 0, None, 64, None, None) == g5.GEMM_OK                       # nothing to do

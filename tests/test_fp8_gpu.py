@@ -237,3 +237,133 @@ def test_fp8_small_m_exact_and_row_invariant(oracle_mod):
     for M in (1, 5):
         cm = g5.gemm_fp8_nt(dA[:M], dsa[:M], dB, dsb, out_dtype=torch.float32, workspace=ws())
         assert torch.equal(cm.view(torch.int32), c16[:M].view(torch.int32)), f"M={M}"
+
+
+# ------------------------------------------------ weights stored [K, N]
+@pytest.mark.parametrize("K,N,ldw_pad,ldq_pad", [(64, 64, 0, 0), (300, 130, 6, 3), (4096, 200, 0, 0),
+                                                 (1000, 77, 1, 16), (5, 9, 0, 0)])
+def test_quantize_cols_bit_exact(oracle_mod, K, N, ldw_pad, ldq_pad):
+    """Per-column quantization of a weight stored [K, N] into the rows of
+    Qt [N, K]: codes and factors equal the oracle's bit for bit; columns of
+    several magnitudes, a zero column, a column whose maximum is negative;
+    padded and odd strides, row padding of Qt untouched."""
+    _say(f"quantize cols {K}x{N} pads {ldw_pad},{ldq_pad}")
+    g = np.random.default_rng([gi.SEED_BASE + 7300, K, N])
+    w = gi.normal(g, (K, N + ldw_pad)) * np.float32(2.0) ** g.integers(-10, 10, (1, N + ldw_pad)).astype(np.float32)
+    w[:, 0] = 0
+    if N > 1:
+        w[K // 2, 1] = -np.float32(1e3)
+    W = gi.to_bf16_bits(w)
+    Qref, sref = oracle_mod.quantize_cols_e4m3(np.ascontiguousarray(W[:, :N]))
+    Qfull = torch.full((N, K + ldq_pad), 0xAB, dtype=torch.uint8, device="cuda")
+    scale = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda")
+    g5.gemm_fp8_quantize_cols(dev_bf16(W)[:, :N], Qfull[:, :K], scale)
+    Q = Qfull.cpu().numpy()
+    assert np.array_equal(Q[:, :K], Qref), f"{int((Q[:, :K] != Qref).sum())} codes differ"
+    assert np.array_equal(scale.cpu().numpy().view(np.uint32), sref.view(np.uint32)), "factors differ"
+    assert np.all(Q[:, K:] == 0xAB), "row padding of Qt was written"
+
+
+def test_fp8_example_5_8_weight_k_by_n(oracle_mod):
+    """Operator & Runtime §5.4.3, Example 5-8: a [4096, 4096] input quantized
+    per row, an FP8 weight [4096, 1536] stored [K, N] (quantized per output
+    column into Bt), 16-bit output; sampled rows of every column against
+    the oracle, the codes of both operands bit-exact."""
+    _say("fp8 Example 5-8 shape 4096x1536x4096")
+    g = np.random.default_rng([gi.SEED_BASE + 7400])
+    X = gi.to_bf16_bits(gi.normal(g, (4096, 4096)))
+    W = gi.to_bf16_bits(gi.normal(g, (4096, 1536), 0.125))
+    qX, sX = g5.gemm_fp8_quantize_rows(dev_bf16(X))
+    qW, sW = g5.gemm_fp8_quantize_cols(dev_bf16(W))
+    rX, rsX = oracle_mod.quantize_rows_e4m3(X)
+    rW, rsW = oracle_mod.quantize_cols_e4m3(W)
+    assert np.array_equal(qX.cpu().numpy(), rX) and np.array_equal(sX.cpu().numpy(), rsX)
+    assert np.array_equal(qW.cpu().numpy(), rW) and np.array_equal(sW.cpu().numpy(), rsW)
+    C = g5.gemm_fp8_nt(qX, sX, qW, sW, workspace=ws())
+    rows = np.array([0, 1, 127, 128, 2047, 3000, 4095])
+    ref = oracle_mod.gemm_fp8_nt(np.ascontiguousarray(rX[rows]), rsX[rows], rW, rsW)
+    check_fp8(host_values(C)[rows], ref, 4096, _amax(oracle_mod, rX, rsX), _amax(oracle_mod, rW, rsW), "bf16",
+              "Example 5-8 rows")
+
+
+# ------------------------------------------------ batched FP8 products
+@pytest.mark.parametrize("with_ws", [True, False])
+@pytest.mark.parametrize("M,N,K", [(300, 392, 256), (5, 392, 320)])
+@pytest.mark.parametrize("bcast", ["none", "a", "b"])
+def test_fp8_nt_batched(oracle_mod, M, N, K, bcast, with_ws):
+    """A batch of scaled FP8 products (the experts of an MoE layer): each
+    entry its own codes and factors, or one operand (and its factors)
+    broadcast along the batch; tiled (M = 300) and small-M (M = 5) paths."""
+    batch = 3
+    _say(f"fp8 batched {batch}x{M}x{N}x{K} broadcast {bcast} ws={with_ws}")
+    cases = [_fp8_case(M, N, K, 10 + b) for b in range(batch)]
+    A = np.stack([c[0] for c in cases])
+    Bt = np.stack([c[1] for c in cases])
+    sa = np.stack([c[2] for c in cases])
+    sb = np.stack([c[3] for c in cases])
+    dA, dB = dev_u8(A), dev_u8(Bt)
+    dsa, dsb = torch.from_numpy(sa).cuda(), torch.from_numpy(sb).cuda()
+    if bcast == "a":
+        dA, dsa = dA[:1].expand(batch, -1, -1), dsa[0]
+    if bcast == "b":
+        dB, dsb = dB[:1].expand(batch, -1, -1), dsb[0]
+    C = g5.gemm_fp8_nt(dA, dsa, dB, dsb, out_dtype=torch.float32, workspace=ws() if with_ws else None)
+    got = host_values(C)
+    for b in range(batch):
+        ia = 0 if bcast == "a" else b
+        ib = 0 if bcast == "b" else b
+        ref = oracle_mod.gemm_fp8_nt(A[ia], sa[ia], Bt[ib], sb[ib])
+        check_fp8(got[b], ref, K, _amax(oracle_mod, A[ia], sa[ia]), _amax(oracle_mod, Bt[ib], sb[ib]), "f32",
+                  f"fp8 batched entry {b}")
+
+
+# ------------------------------------------------ FP8 with the affine epilogue
+def _check_fp8_affine(C, ref, D, K, am, bm, alpha, bias_vals, beta, old_vals, out, what):
+    """The FP32 accumulation bar on D scaled by |alpha|, the FP32 epilogue's
+    fused multiply-adds (2^-20 of the magnitudes), and a bf16 output's
+    rounding (2^-8 |C_ref|)."""
+    mags = np.abs(alpha * D) + np.abs(bias_vals)[None, :] + np.abs(beta * old_vals)
+    bound = abs(alpha) * 1e-5 * max(K, 1) * am * bm + 2.0 ** -20 * mags
+    if out == "bf16":
+        bound = bound + 2.0 ** -8 * np.abs(ref)
+    err = np.abs(C - ref)
+    assert np.all(np.isfinite(C)), f"{what}: non-finite output"
+    bad = err > bound
+    if np.any(bad):
+        idx = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} out of bound, first at {idx}: got {C[idx]!r} want {ref[idx]!r}")
+
+
+@pytest.mark.parametrize("cfg", [None, "bf16_256x256", "bf16_128x128"])
+@pytest.mark.parametrize("M,N,K", [(300, 392, 256), (7, 200, 144), (512, 384, 1024)])
+def test_fp8_nt_affine(oracle_mod, monkeypatch, cfg, M, N, K):
+    """C := alpha * (scaled FP8 product) + bias + beta * C, both outputs,
+    tiled and small-M paths (a forced config applies to M > 16 only)."""
+    if cfg and M <= 16:
+        pytest.skip("small M runs on the GEMV kernel")
+    _say(f"fp8 affine {cfg} {M}x{N}x{K}")
+    A, Bt, sa, sb = _fp8_case(M, N, K, 20)
+    g = np.random.default_rng([gi.SEED_BASE + 7500, M])
+    bias = gi.to_bf16_bits(gi.normal(g, (N,)))
+    bv = gi.bf16_bits_to_f32(bias).astype(np.float64)
+    if cfg:
+        monkeypatch.setenv("GEMM_FORCE_CONFIG", cfg)
+    am, bm = _amax(oracle_mod, A, sa), _amax(oracle_mod, Bt, sb)
+    D = oracle_mod.gemm_fp8_nt(A, sa, Bt, sb)
+    dA, dB = dev_u8(A), dev_u8(Bt)
+    dsa, dsb, db = torch.from_numpy(sa).cuda(), torch.from_numpy(sb).cuda(), dev_bf16(bias)
+    for out, od in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+        old = gi.normal(g, (M, N)).astype(np.float32)
+        if od == torch.bfloat16:
+            old_bits = gi.to_bf16_bits(old)
+            C = dev_bf16(old_bits)
+            ov = gi.bf16_bits_to_f32(old_bits).astype(np.float64)
+            C_old = old_bits
+        else:
+            C = torch.from_numpy(old).cuda()
+            ov = old.astype(np.float64)
+            C_old = old
+        alpha, beta = 0.5, -1.25
+        g5.gemm_fp8_nt_affine(dA, dsa, dB, dsb, C, alpha=alpha, bias=db, beta=beta, workspace=ws())
+        ref = oracle_mod.gemm_fp8_nt_affine(A, sa, Bt, sb, alpha=alpha, bias=bias, beta=beta, C_old=C_old)
+        _check_fp8_affine(host_values(C), ref, D, K, am, bm, alpha, bv, beta, ov, out, f"fp8 affine {cfg} {out}")

@@ -218,3 +218,62 @@ def test_quantize_rows_exact_ties(oracle_mod):
         alt = lo if abs(Fraction(y32) - lo) < abs(Fraction(y32) - hi) else hi
         flips += alt != v
     assert flips >= 1                                            # the pin separates the two rules
+
+
+def test_quantize_cols_exact_against_rationals(oracle_mod):
+    """Per-column quantization of a weight [K, N]: every code of column j is
+    the E4M3FN value nearest to W[k][j] * 448 / amax_j (rational arithmetic,
+    brute force), written at [j][k], with factor amax_j / 448; a zero
+    column, a column whose maximum is negative, columns of very different
+    magnitudes and an exact tie."""
+    mags = [Fraction(float(v)) for v in oracle_mod.e4m3_decode(np.arange(127, dtype=np.uint8))]
+    g = np.random.default_rng(6)
+    K, N = 24, 7
+    w = gi.normal(g, (K, N)) * np.float32(2.0) ** np.arange(-6, 8, 2, dtype=np.float32)[None, :]
+    w[:, 0] = 0
+    w[5, 1] = -np.float32(40.0)
+    x, amax = _TIES[0]
+    w[:, 2] = 0
+    w[0, 2], w[1, 2], w[2, 2] = x, -amax, amax * 0.25
+    W = gi.to_bf16_bits(w)
+    Qt, s = oracle_mod.quantize_cols_e4m3(W)
+    assert Qt.shape == (N, K) and s.shape == (N,)
+    wf = gi.bf16_bits_to_f32(W).astype(np.float64)
+    for j in range(N):
+        am = float(np.abs(wf[:, j]).max())
+        assert s[j] == np.float32(am / 448.0)
+        for k in range(K):
+            assert int(Qt[j, k]) == _nearest_code_exact(float(wf[k, j]), am, mags), (j, k)
+    assert np.all(Qt[0] == 0) and s[0] == 0
+    assert Qt[1, 5] == 0xFE                                     # -448: the column's maximum, negative
+    assert Qt[2, 0] == oracle_mod.e4m3_encode(np.array([200.0]))[0] and Qt[2, 0] % 2 == 0   # the tie, even code
+
+
+def test_fp8_affine_reductions(oracle_mod):
+    """The FP8 affine oracle against its parts: alpha = 1, no bias, beta = 0
+    is the scaled product; alpha = 0 is bias + beta * C_old alone; in
+    general it is alpha * D + bias + beta * C_old with D in rationals on a
+    tiny case (brute force over the decoded codes)."""
+    g = np.random.default_rng(8)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    M, N, K = 3, 5, 7
+    A, Bt = g.choice(finite, (M, K)), g.choice(finite, (N, K))
+    sa = (2.0 ** g.integers(-4, 4, M)).astype(np.float32)
+    sb = (2.0 ** g.integers(-4, 4, N)).astype(np.float32)
+    bias = gi.to_bf16_bits(gi.normal(g, (N,)))
+    old = gi.to_bf16_bits(gi.normal(g, (M, N)))
+    D = oracle_mod.gemm_fp8_nt(A, sa, Bt, sb)
+    assert np.array_equal(oracle_mod.gemm_fp8_nt_affine(A, sa, Bt, sb), D)
+    bv = gi.bf16_bits_to_f32(bias).astype(np.float64)
+    ov = gi.bf16_bits_to_f32(old).astype(np.float64)
+    C0 = oracle_mod.gemm_fp8_nt_affine(A, sa, Bt, sb, alpha=0.0, bias=bias, beta=-2.0, C_old=old)
+    assert np.array_equal(C0, bv[None, :] - 2.0 * ov)
+    alpha, beta = 0.75, 0.5
+    C = oracle_mod.gemm_fp8_nt_affine(A, sa, Bt, sb, alpha=alpha, bias=bias, beta=beta, C_old=old)
+    da = [[Fraction(float(v)) for v in row] for row in oracle_mod.e4m3_decode(A)]
+    db = [[Fraction(float(v)) for v in row] for row in oracle_mod.e4m3_decode(Bt)]
+    for i in range(M):
+        for j in range(N):
+            d = sum(da[i][k] * db[j][k] for k in range(K)) * Fraction(float(sa[i])) * Fraction(float(sb[j]))
+            exact = Fraction(alpha) * d + Fraction(float(bv[j])) + Fraction(beta) * Fraction(float(ov[i, j]))
+            assert abs(Fraction(float(C[i, j])) - exact) <= abs(exact) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 60)
