@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "decode_swiglu", "sgemm", "batched", "ragged", "swiglu", "shard", "fp8", "scores_nt", "decode_nt", "fp8_example_5_8", "affine", "linear_nt", "wgrad_tn", "copy"])
+    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "decode_swiglu", "sgemm", "batched", "ragged", "swiglu", "shard", "fp8", "scores_nt", "decode_nt", "fp8_example_5_8", "square", "affine", "linear_nt", "wgrad_tn", "copy"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--batches", type=int, default=7, help="timed batches per workload (median reported)")
@@ -360,6 +360,28 @@ def main():
             workloads.append({"name": f"sgemm_f32_{n}^3", "us": round(ms * 1e3, 3), "tflops": round(tf, 2),
                               "frac_peak": round(tf / PEAK_F32_TFLOPS, 4), "rotations": R})
             del dA, dB, dC
+
+    # ------------------------------------------------------------ bf16 square
+    if args.only in ("all", "square"):
+        # bf16 4096^3 -> bf16: 256 tiles of 256x256, one per CU.
+        n = 4096
+        g = np.random.default_rng([gi.SEED_BASE + 900, n])
+        A = gi.to_bf16_bits(gi.normal(g, (n, n)))
+        B = gi.to_bf16_bits(gi.normal(g, (n, n), 0.125))
+        R = rotations(2 * 3 * n * n)
+        dA = [to_dev_bf16(A) for _ in range(R)]
+        dB = [to_dev_bf16(B) for _ in range(R)]
+        dC = [torch.empty((n, n), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        fns = [(lambda i=i: g5.gemm_bf16(dA[i], dB[i], dC[i], workspace=ws)) for i in range(R)]
+        st, plan = g5.plan_query(g5.GEMM_OP_BF16, n, n, n)
+        ms = timed(fns, 50, 10, label="square_bf16_4096^3")
+        tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+        log(f"bf16 4096^3: {ms * 1e3:.2f} us/call, {tf:.1f} TFLOPS ({100 * tf / PEAK_BF16_TFLOPS:.1f}%), "
+            f"{plan.name.decode()}")
+        workloads.append({"name": "square_bf16_4096^3", "us": round(ms * 1e3, 3), "tflops": round(tf, 2),
+                          "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "config": plan.name.decode(),
+                          "rotations": R})
+        del dA, dB, dC
 
     # ------------------------------------------------------------ batched
     if args.only in ("all", "batched"):

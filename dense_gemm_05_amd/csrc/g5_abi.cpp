@@ -299,6 +299,13 @@ void fill_grid(const Problem &p, Plan &pl, bool ws)
     // Column bands as tall as the whole M extent when it is only a few tiles
     // (each XCD then owns whole column panels of B), else 8 tiles tall.
     pl.group_m = pl.tiles_m <= 8 ? (pl.tiles_m > 0 ? pl.tiles_m : 1) : 8;
+    // diagnostic: the orders the map is measured against (GEMM_TILE_ORDER =
+    // "rowmajor": tile w for workgroup w; "bands": the same column bands
+    // without gathering each XCD's workgroups)
+    if (const char *o = std::getenv("GEMM_TILE_ORDER")) {
+        if (std::strcmp(o, "rowmajor") == 0) pl.group_m = 0;
+        else if (std::strcmp(o, "bands") == 0) pl.group_m = -pl.group_m;
+    }
     pl.model_bytes = (c.tile_m > 0 && p.K > 0)
                          ? p.batch * gemm_model_traffic_bytes(p.M, p.N, p.K, c.tile_m, c.tile_n, elem_a(p))
                          : 0.0;
@@ -1170,7 +1177,7 @@ void gemm_model_quant_traffic(int64_t M, int64_t N, int64_t K, int64_t m, int64_
 int gemm_tile_map(int64_t wg, int64_t batch, int64_t tiles_m, int64_t tiles_n, int64_t group_m, int64_t *b,
                   int64_t *tm, int64_t *tn)
 {
-    if (batch <= 0 || tiles_m <= 0 || tiles_n <= 0 || group_m <= 0 || wg < 0 ||
+    if (batch <= 0 || tiles_m <= 0 || tiles_n <= 0 || group_m < -tiles_m || wg < 0 ||
         wg >= batch * tiles_m * tiles_n || !b || !tm || !tn)
         return -1;
     const g5::TileCoord t = g5::tile_map(wg, batch, tiles_m, tiles_n, group_m);

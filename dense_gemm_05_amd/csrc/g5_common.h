@@ -29,15 +29,26 @@ struct TileCoord {
     int64_t b, tm, tn;
 };
 
+// group_m <= 0 selects the orders the XCD-aware one is measured against:
+// 0 plain row-major tile order (workgroup w takes tile w, rows of tiles one
+// after another), -g column bands g tiles tall without the XCD regrouping.
 G5_HD inline TileCoord tile_map(int64_t wg, int64_t batch, int64_t tiles_m, int64_t tiles_n,
                                 int64_t group_m)
 {
     const int64_t per_batch = tiles_m * tiles_n;
+    TileCoord t;
+    if (group_m == 0) {
+        t.b = wg / per_batch;
+        const int64_t r = wg - t.b * per_batch;
+        t.tm = r / tiles_n;
+        t.tn = r - t.tm * tiles_n;
+        return t;
+    }
     const int64_t total = batch * per_batch;
     const int64_t rounds = total / kNumXcd;
     int64_t L = wg;
-    if (wg < rounds * kNumXcd) L = (wg % kNumXcd) * rounds + wg / kNumXcd;
-    TileCoord t;
+    if (group_m > 0 && wg < rounds * kNumXcd) L = (wg % kNumXcd) * rounds + wg / kNumXcd;
+    if (group_m < 0) group_m = -group_m;
     t.b = L / per_batch;
     const int64_t r = L - t.b * per_batch;
     const int64_t band_tiles = group_m * tiles_n;

@@ -39,11 +39,14 @@ __device__ __forceinline__ TileCoord sk_tile(int64_t t, const GemmArgs &p)
     TileCoord c;
     c.b = t / per_batch;
     const int64_t r = t - c.b * per_batch;
-    const int64_t band_tiles = p.group_m * p.tiles_n;
+    // (the diagnostic orders of tile_map, group_m <= 0, give bands of
+    // |group_m| tiles, or of 1)
+    const int64_t gm = p.group_m > 0 ? p.group_m : p.group_m < 0 ? -p.group_m : 1;
+    const int64_t band_tiles = gm * p.tiles_n;
     const int64_t band = r / band_tiles;
-    const int64_t first_m = band * p.group_m;
+    const int64_t first_m = band * gm;
     const int64_t rem_m = p.tiles_m - first_m;
-    const int64_t h = rem_m < p.group_m ? rem_m : p.group_m;
+    const int64_t h = rem_m < gm ? rem_m : gm;
     const int64_t rr = r - band * band_tiles;
     c.tm = first_m + rr % h;
     c.tn = rr / h;

@@ -520,8 +520,10 @@ void gemm_model_quant_traffic(int64_t M, int64_t N, int64_t K, int64_t m, int64_
  * accelerator complex dies (XCDs); the map gives each XCD a contiguous run
  * of tiles, ordered in column bands `group_m` tiles tall, so that the tiles
  * resident on one XCD share rows of A and columns of B in that die's L2.
- * The map is a bijection on [0, batch*tiles_m*tiles_n).  Returns 0, or -1
- * for out-of-range arguments. */
+ * group_m <= 0 gives the orders it is measured against (environment
+ * GEMM_TILE_ORDER): 0 plain row-major order, -g column bands g tiles tall
+ * without the per-XCD gathering.  The map is a bijection on
+ * [0, batch*tiles_m*tiles_n).  Returns 0, or -1 for out-of-range arguments. */
 int gemm_tile_map(int64_t wg, int64_t batch, int64_t tiles_m, int64_t tiles_n,
                   int64_t group_m, int64_t *b, int64_t *tm, int64_t *tn);
 

@@ -226,7 +226,8 @@ def test_tile_map_is_a_bijection(L):
     i64 = ctypes.c_int64
     b, tm, tn = i64(), i64(), i64()
     for batch, tiles_m, tiles_n, group in [(1, 4, 64, 4), (1, 7, 5, 3), (3, 3, 11, 8), (2, 13, 9, 8),
-                                           (1, 1, 1, 1), (32, 4, 6, 4), (1, 16, 16, 8), (5, 1, 13, 1)]:
+                                           (1, 1, 1, 1), (32, 4, 6, 4), (1, 16, 16, 8), (5, 1, 13, 1),
+                                           (1, 4, 64, 0), (3, 3, 11, 0), (1, 4, 64, -4), (2, 13, 9, -8)]:
         seen = set()
         total = batch * tiles_m * tiles_n
         for w in range(total):
@@ -251,6 +252,27 @@ def test_tile_map_gives_each_xcd_a_compact_block(L):
             cols.add(tn.value)
             rowset.add(tm.value)
         assert rowset == {0, 1, 2, 3} and cols == set(range(8 * x, 8 * x + 8))
+
+
+def test_tile_map_diagnostic_orders(L):
+    """The orders the XCD-aware map is compared with: group 0 is plain
+    row-major (workgroup w -> tile row w / tiles_n, column w % tiles_n); a
+    negative group is the column-band walk without the per-XCD gathering,
+    so XCD x then holds every 8th tile of the walk, spread over 32 column
+    tiles of the FFN grid instead of 8."""
+    i64 = ctypes.c_int64
+    b, tm, tn = i64(), i64(), i64()
+    for w in range(256):
+        L.gemm_tile_map(w, 1, 4, 64, 0, ctypes.byref(b), ctypes.byref(tm), ctypes.byref(tn))
+        assert (tm.value, tn.value) == (w // 64, w % 64)
+        L.gemm_tile_map(w, 1, 4, 64, -4, ctypes.byref(b), ctypes.byref(tm), ctypes.byref(tn))
+        assert (tm.value, tn.value) == (w % 4, w // 4)
+    for x in range(8):
+        cols = set()
+        for w in range(x, 256, 8):
+            L.gemm_tile_map(w, 1, 4, 64, -4, ctypes.byref(b), ctypes.byref(tm), ctypes.byref(tn))
+            cols.add(tn.value)
+        assert len(cols) == 32
 
 
 @pytest.mark.parametrize("M,N,K,batch", [(1, 12288, 4096, 1), (5, 1664, 4160, 1), (16, 384, 1024, 3),

@@ -650,3 +650,18 @@ def test_calls_allocate_nothing_on_a_fresh_stream(oracle_mod):
     ref = oracle_mod.gemm_bf16(X, W)
     check_bf16(host_values(C1), ref, 4096, "split small-M with workspace")
     check_bf16(host_values(C2), ref, 4096, "whole-K small-M without workspace")
+
+
+@pytest.mark.parametrize("order", ["rowmajor", "bands"])
+def test_tile_orders_give_identical_results(monkeypatch, order):
+    """The tile orders the XCD-aware map is measured against (environment
+    GEMM_TILE_ORDER) only move tiles between workgroups: every tile is
+    computed the same way, so C is bitwise the default order's."""
+    M, N, K = 1024, 3072, 1024
+    _say(f"tile order {order} {M}x{N}x{K}")
+    A, B = gi.small_case("bf16", M, N, K, seed=41, scale_b=0.125)
+    dA, dB = dev_bf16(A), dev_bf16(B)
+    ref = host_bits(g5.gemm_bf16(dA, dB, workspace=ws()))
+    monkeypatch.setenv("GEMM_TILE_ORDER", order)
+    got = host_bits(g5.gemm_bf16(dA, dB, workspace=ws()))
+    assert np.array_equal(got, ref)
