@@ -964,7 +964,12 @@ __global__ void __launch_bounds__(WGM *WGN * 64, 2) k_bf16_ms(GemmArgs p)
         // wait for them, then count the arrival.  The workgroup that brings
         // the tile's counter to ksplit adds the slices 0, 1, ... in order
         // (its own from registers, bit-identical to what it stored), resets
-        // the counter for the next call and stores the tile.
+        // the counter for the next call and stores the tile.  No fence: the
+        // sc1 (device-scope) stores and loads of the partial tiles complete
+        // at the device's coherence point, never in an XCD's private L2,
+        // the wait and barrier retire every store before the counter
+        // atomic (performed at that point) is issued, and the last arriver
+        // loads only after reading the atomic's result.
         __shared__ unsigned sk_arrived;
         constexpr int TILE_F = BM * BN;
         float *tile_ws = p.ws_part + wg * p.ksplit * (int64_t)TILE_F;

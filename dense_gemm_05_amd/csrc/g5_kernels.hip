@@ -560,24 +560,29 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
     constexpr int RS = 16 * NB + 1;
     __shared__ float red[NW * 64 * RS];
     float *mine = red + (wave * 64 + lane) * RS;
+    if (li < M) {                            // rows < M only (the others are zero X rows)
 #pragma unroll
-    for (int h = 0; h < NB; ++h)
+        for (int h = 0; h < NB; ++h)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) mine[h * 16 + q * 4 + b] = acc[4 * h + b][q];
+                for (int b = 0; b < 4; ++b) mine[h * 16 + q * 4 + b] = acc[4 * h + b][q];
+    }
     __syncthreads();
-    for (int t = tid; t < 64 * 16; t += NW * 64) {
-        const int L = t >> 4, v = t & 15;
+    // Entry e of the 64 M kept ones: g = e / (16 M), row m = (e / 16) % M,
+    // v = e % 16 -> lane L = 16 g + m, column n0 + 16 g + v.
+    const int Mi = (int)M;
+    for (int e = tid; e < 64 * Mi; e += NW * 64) {
+        const int g2 = e / (16 * Mi), r = e - g2 * 16 * Mi, m = r >> 4, v = r & 15;
+        const int L = 16 * g2 + m;
         float sum[NB];
 #pragma unroll
         for (int h = 0; h < NB; ++h) {
             sum[h] = 0.f;
             for (int w2 = 0; w2 < NW; ++w2) sum[h] += red[(w2 * 64 + L) * RS + h * 16 + v];
         }
-        const int64_t m = L & 15;
-        const int64_t n = n0 + 16 * (L >> 4) + v;
-        if (m < M && n < N) {
+        const int64_t n = n0 + 16 * g2 + v;
+        if (n < N) {
             if constexpr (GLU) store_swiglu(p, bidx, m, n, sum[0], sum[1]);
             else store_out(p, bidx, m, n, sum[0]);
         }
@@ -605,9 +610,16 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
 //    order -- the same order whichever workgroup arrives last, so the result
 //    is deterministic and, the partition being independent of M, the same
 //    for every row count -- then writes C and resets the counter for the
-//    next call.  Device-scope loads and stores are coherent across the
-//    XCDs' L2s on their own, so no L2 write-back or invalidation (a full
-//    fence) is needed; with fences the path measured twice as slow.
+//    next call.  Why no fence is needed: the partials are written and read
+//    only by device-scope (sc1) atomic stores and loads, which gfx950 never
+//    leaves dirty in, nor serves stale from, an XCD's private L2 -- they
+//    complete at the device's coherence point; s_waitcnt(0) plus the
+//    barrier make every store of the workgroup complete before the counter
+//    atomic (performed at that same point) is issued; and the last
+//    arriver's loads are issued only after it has read the atomic's
+//    result.  A release/acquire pair would add an L2 write-back and an L2
+//    invalidate, needed only for data moved by ordinary loads and stores;
+//    with them the path measured twice as slow.
 //  * W is read once: its loads are non-temporal.
 //  * SwiGLU (p.epi == EPI_SWIGLU): a strip's gate columns (n0.. of the
 //    merged weight [K, 2N]) and its up columns (N + n0..) are read by
@@ -702,25 +714,28 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode_sk(GemmArgs p, float *ws,
     __shared__ float red[NW * 64 * RS];
     __shared__ unsigned arrived;
     float *mine = red + (wave * 64 + lane) * RS;
+    // Only the lanes of rows < M hold partial sums that are stored; the
+    // others (zero X rows) skip the LDS round trip.
+    if (li < M) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) mine[q * 8 + c] = acc[c][q];
+            for (int c = 0; c < 8; ++c) mine[q * 8 + c] = acc[c][q];
+    }
     __syncthreads();
     float *part = ws + ((bidx * nstrip + strip) * nmem + half * KS + slice) * (16 * NC);
     const bool direct = KS == 1 && !glu;     // one workgroup per strip: no partial sums
-    // Entry t: lane L = t / 32, q = (t / 8) % 4, c = t % 8 -> row L % 16,
-    // column 32 (L / 16) + 8 q + c of the strip.
-    for (int t = tid; t < 64 * 32; t += NW * 64) {
-        const int L = t >> 5, q = (t >> 3) & 3, c = t & 7;
+    // Entry e of the 128 M kept ones: g = e / (32 M), row m = (e / 32) % M,
+    // j = e % 32 = 8 q + c -> lane L = 16 g + m, column 32 g + j of the strip.
+    const int Mi = (int)M;
+    for (int e = tid; e < 128 * Mi; e += NW * 64) {
+        const int g2 = e / (32 * Mi), r = e - g2 * 32 * Mi, m = r >> 5, j = r & 31;
+        const int L = 16 * g2 + m;
         float sum = 0.f;
-        for (int w2 = 0; w2 < NW; ++w2) sum += red[(w2 * 64 + L) * RS + (t & 31)];
-        const int m = L & 15, n = 32 * (L >> 4) + 8 * q + c;
-        if (direct) {
-            if (m < M) store_out(p, bidx, m, n0 + n, sum);
-        } else if (m < M) {                  // rows past M are never read back
-            __hip_atomic_store(part + m * NC + n, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        for (int w2 = 0; w2 < NW; ++w2) sum += red[(w2 * 64 + L) * RS + j];
+        const int n = 32 * g2 + j;
+        if (direct) store_out(p, bidx, m, n0 + n, sum);
+        else __hip_atomic_store(part + m * NC + n, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (direct) return;
     // Publish this slice; the last of the nmem workgroups of the strip sums.
@@ -731,9 +746,8 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode_sk(GemmArgs p, float *ws,
     __syncthreads();
     if (arrived != (unsigned)(nmem - 1)) return;
     const float *parts = ws + (bidx * nstrip + strip) * nmem * (16 * NC);
-    for (int t = tid; t < 16 * NC; t += NW * 64) {
+    for (int t = tid; t < Mi * NC; t += NW * 64) {
         const int m = t / NC, n = t % NC;
-        if (m >= M) continue;
         float sum = 0.f;
         for (int k2 = 0; k2 < KS; ++k2)
             sum += __hip_atomic_load(parts + k2 * (16 * NC) + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
