@@ -105,12 +105,14 @@ hipError_t launch_quant_rows_e4m3(const uint16_t *X, int64_t ldx, int64_t rows, 
 // Per-column quantization of a weight W [K, N] (bf16) into the rows of
 // Qt [N, K]: column j gets the factor of its own largest magnitude and the
 // codes of the row quantizer above (same quotient, same rounding), written
-// transposed so that the FP8 products read them as Bt.  One workgroup per 64
-// columns: 8 lanes cover 128 bytes of a row (8 columns each), 32 rows per
-// pass.  Pass 1: the column maxima (per lane over its rows, then over the 32
-// lanes of a column chunk in LDS).  Pass 2: per 64-row block, every lane
-// quantizes 8 columns of 2 rows into an LDS tile laid out [column][k], and
-// the tile goes out as 64 rows of 64 code bytes.
+// transposed so that the FP8 products read them as Bt.  Workgroup (x, y)
+// owns 64 columns and the y-th of gridDim.y ranges of 64-row blocks: 8
+// lanes cover 128 bytes of a row (8 columns each), 32 rows per pass.
+// Pass 1: the column maxima over all K (per lane over its rows, then over the
+// 32 lanes of a column chunk in LDS; every workgroup of a column strip
+// computes them, from L2 after the first).  Pass 2: per 64-row block of its
+// range, every lane quantizes 8 columns of 2 rows into an LDS tile laid out
+// [column][k], and the tile goes out as 64 rows of 64 code bytes.
 __global__ void __launch_bounds__(256) k_quant_cols_e4m3(const uint16_t *W, int64_t ldw, int64_t K, int64_t N,
                                                          int align_w, uint8_t *Qt, int64_t ldq, int align_q,
                                                          float *scale)
@@ -138,7 +140,7 @@ __global__ void __launch_bounds__(256) k_quant_cols_e4m3(const uint16_t *W, int6
         float a = 0.f;
         for (int r = 0; r < 32; ++r) a = fmaxf(a, red[r][tid]);
         amax_s[tid] = a;
-        if (n0 + tid < N) scale[n0 + tid] = a / 448.0f;
+        if (blockIdx.y == 0 && n0 + tid < N) scale[n0 + tid] = a / 448.0f;
     }
     __syncthreads();
     float amax[8];
@@ -151,7 +153,9 @@ __global__ void __launch_bounds__(256) k_quant_cols_e4m3(const uint16_t *W, int6
         y = y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);
         return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xffu;
     };
-    for (int64_t kb = 0; kb < K; kb += 64) {
+    const int64_t blocks = (K + 63) / 64;
+    const int64_t b0 = blocks * blockIdx.y / gridDim.y, b1 = blocks * (blockIdx.y + 1) / gridDim.y;
+    for (int64_t kb = b0 * 64; kb < b1 * 64; kb += 64) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int kr = r0 + 32 * h;
@@ -184,8 +188,14 @@ __global__ void __launch_bounds__(256) k_quant_cols_e4m3(const uint16_t *W, int6
 hipError_t launch_quant_cols_e4m3(const uint16_t *W, int64_t ldw, int64_t K, int64_t N, int align_w, uint8_t *Qt,
                                   int64_t ldq, int align_q, float *scale, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_quant_cols_e4m3, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, s, W, ldw, K, N, align_w, Qt,
-                       ldq, align_q, scale);
+    // enough workgroups for the 256 CUs: column strips times ranges of K
+    const int64_t strips = (N + 63) / 64, blocks = (K + 63) / 64;
+    int64_t ky = (512 + strips - 1) / strips;
+    if (ky > blocks) ky = blocks;
+    if (ky > 64) ky = 64;
+    if (ky < 1) ky = 1;
+    hipLaunchKernelGGL(k_quant_cols_e4m3, dim3((unsigned)strips, (unsigned)ky), dim3(256), 0, s, W, ldw, K, N, align_w,
+                       Qt, ldq, align_q, scale);
     return hipGetLastError();
 }
 
