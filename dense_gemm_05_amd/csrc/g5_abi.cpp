@@ -207,7 +207,10 @@ double model_time(const Problem &p, const ConfigInfo &c, double eff)
     const int64_t tm = cdiv(p.M, c.tile_m), tn = cdiv(p.N, out_tile_n(p, c));
     const int64_t tiles = p.batch * tm * tn;
     const int64_t per_cu = cdiv(tiles, (int64_t)kNumCU);
-    const double rate = (p.op == GEMM_OP_SGEMM ? kF32FlopsPerCUperS : kBf16FlopsPerCUperS);
+    // (E4M3 operands: the double-rate fp8 matrix instruction)
+    const double rate = p.op == GEMM_OP_SGEMM ? kF32FlopsPerCUperS
+                        : is_fp8(p)           ? 2.0 * kBf16FlopsPerCUperS
+                                              : kBf16FlopsPerCUperS;
     const double kpad = (double)cdiv(p.K, c.tile_k) * c.tile_k;
     const double t_mfma = (2.0 * c.tile_m * c.tile_n * kpad) / rate;
     const double tile_bytes =
@@ -466,9 +469,16 @@ int select_plan(const Problem &p, Plan &pl, bool ws)
         static const Cand bf16_short_k[] = {{CFG_BF16_256x192, 0.7}, {CFG_BF16_256x256, 0.65}, {CFG_BF16_256x128, 0.75},
                                             {CFG_BF16_128x128, 1.0}};
         static const Cand f32c[] = {{CFG_F32_128x128, 1.0}, {CFG_F32_64x64, 0.8}};
+        // FP8 ring kernels (256x192, 256x256, 128x128): the 256x256 one runs
+        // single-rate stages (its registers do not hold stage pairs) and is
+        // half as fast; two co-resident 128x128 workgroups per CU beat the
+        // model's copy rate (measured: 4096x1536x4096 39.2 against 51.6 us
+        // for 256x192, 4096^3 90.3 against 105.7 us for 256x256, while the
+        // FFN's one tile per CU stays on 256x192, 58.8 against 67.6 us).
+        static const Cand fp8c[] = {{CFG_BF16_256x192, 1.0}, {CFG_BF16_256x256, 0.5}, {CFG_BF16_128x128, 1.4}};
         const bool bf16 = p.op != GEMM_OP_SGEMM;
-        const Cand *cands = bf16 ? (p.K <= 8 * 32 ? bf16_short_k : bf16c) : f32c;
-        const int nc = bf16 ? 4 : 2;
+        const Cand *cands = is_fp8(p) ? fp8c : bf16 ? (p.K <= 8 * 32 ? bf16_short_k : bf16c) : f32c;
+        const int nc = is_fp8(p) ? 3 : bf16 ? 4 : 2;
         double best = 0.0;
         for (int i = 0; i < nc; ++i) {
             if (!config_fits(p, cands[i].id)) continue;
@@ -489,7 +499,7 @@ int select_plan(const Problem &p, Plan &pl, bool ws)
         // (page "Operator & Runtime" §5.2.4 splits the reduction dimension
         // to occupy the device).
         if (ws && bf16 && (epi_of(p) == EPI_NONE || epi_of(p) == EPI_AFFINE) &&
-            p.batch * cdiv(p.M, 128) * cdiv(p.N, 128) <= kMaxCounters) {
+            p.batch * cdiv(p.M, 128) * cdiv(p.N, 128) < kNumCU) {
             Plan t = pl;
             t.config = CFG_BF16_128x128;
             bool ev = false;
@@ -498,7 +508,9 @@ int select_plan(const Problem &p, Plan &pl, bool ws)
             if (a_trans(p) && var == 0) var = 2;                          // At rows realigned below
             for (int S = 2; S <= 8 && var >= 1; ++S) {
                 if (!split_ok(p, S)) continue;
-                const double eff = (p.K <= 8 * 32 ? 1.0 : 0.85) * (var == 1 ? 1.0 : 0.85);
+                // (the 128x128 entry of the candidate table above)
+                const double base = is_fp8(p) ? 1.4 : p.K <= 8 * 32 ? 1.0 : 0.85;
+                const double eff = base * (var == 1 ? 1.0 : 0.85);
                 const double tm = model_time_split(p, kConfigs[CFG_BF16_128x128], S, eff);
                 if (tm < best) {
                     best = tm;
