@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
 from .gemm import (  # noqa: F401
     gemm_sgemm, gemm_bf16, gemm_bf16_batched, gemm_bf16_nt, gemm_bf16_nt_batched, gemm_bf16_tn,
     gemm_bf16_tn_batched, gemm_fp8_quantize_rows, gemm_fp8_quantize_cols, gemm_fp8_nt, gemm_fp8_nt_affine,
+    gemm_fp8_nt_quant_a,
     gemm_bf16_silu, gemm_bf16_swiglu, gemm_bf16_silu_batched,
     gemm_bf16_swiglu_batched, gemm_bf16_affine,
     gemm_bf16_nt_affine, gemm_bf16_tn_affine, plan_query, workspace_size, Workspace,

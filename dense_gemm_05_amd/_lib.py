@@ -38,7 +38,7 @@ EXPORTS = ("gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm
            "gemm_bf16_tn", "gemm_bf16_tn_batched",
            "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_bf16_silu_batched", "gemm_bf16_swiglu_batched",
            "gemm_fp8_quantize_rows", "gemm_fp8_quantize_cols", "gemm_fp8_nt", "gemm_fp8_nt_batched",
-           "gemm_fp8_nt_affine", "gemm_bf16_affine", "gemm_bf16_nt_affine",
+           "gemm_fp8_nt_affine", "gemm_fp8_nt_quant_a", "gemm_bf16_affine", "gemm_bf16_nt_affine",
            "gemm_bf16_tn_affine", "gemm_run", "gemm_run_noalloc", "gemm_workspace_size",
            "gemm_status_string",
            "gemm_plan_query", "gemm_plan_query_ex", "gemm_model_local_bytes", "gemm_model_traffic_bytes", "gemm_model_quant_traffic",
@@ -97,6 +97,8 @@ def lib():
     L.gemm_fp8_nt_affine.argtypes = [i64, i64, i64, i64, p, i64, i64, p, p, i64, i64, p, ctypes.c_float, p,
                                      ctypes.c_float, p, i64, i64, i32, p]
     L.gemm_fp8_nt_affine.restype = i32
+    L.gemm_fp8_nt_quant_a.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, p, i64, i32, p, u64, p]
+    L.gemm_fp8_nt_quant_a.restype = i32
     L.gemm_bf16_affine.argtypes = [i64, i64, i64, i64, p, i64, i64, p, i64, i64, ctypes.c_float, p, ctypes.c_float,
                                    p, i64, i64, i32, p]
     L.gemm_bf16_affine.restype = i32

@@ -907,6 +907,65 @@ int gemm_fp8_nt_affine(int64_t batch, int64_t M, int64_t N, int64_t K, const uin
     return g5::run(p, stream);
 }
 
+int gemm_fp8_nt_quant_a(int64_t M, int64_t N, int64_t K, const uint16_t *X, int64_t ldx, float *scale_x,
+                        const uint8_t *Bt, int64_t ldbt, const float *scale_b, void *C, int64_t ldc, int c_type,
+                        void *workspace, uint64_t workspace_bytes, void *stream)
+{
+    using g5::Range;
+    if (M < 0 || N < 0 || K < 0 || M > 0x7fffffff) return GEMM_ERR_INVALID_ARG;
+    if (c_type != GEMM_OUT_BF16 && c_type != GEMM_OUT_F32) return GEMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return GEMM_OK;
+    if (!X || !Bt || !C || !scale_x || ldx < K || ldbt < K || ldc < N) return GEMM_ERR_INVALID_ARG;
+    if (((uint64_t)scale_x % 4) || ((uint64_t)scale_b % 4) || ((uint64_t)X % 2)) return GEMM_ERR_INVALID_ARG;
+    const int ec = c_type == GEMM_OUT_F32 ? 4 : 2;
+    const Range rx = g5::extent((uint64_t)X, 1, M, K > 0 ? K : 1, ldx, 0, 2);
+    const Range rb = g5::extent((uint64_t)Bt, 1, N, K > 0 ? K : 1, ldbt, 0, 1);
+    const Range rc = g5::extent((uint64_t)C, 1, M, N, ldc, 0, ec);
+    const Range rs{(__int128)(uint64_t)scale_x, (__int128)(uint64_t)scale_x + 4 * (__int128)M};
+    const Range rw{(__int128)(uint64_t)workspace, (__int128)(uint64_t)workspace + 4 * (__int128)M};
+    if (g5::overlap(rc, rx) || g5::overlap(rc, rb) || g5::overlap(rc, rs) || g5::overlap(rs, rx) || g5::overlap(rs, rb))
+        return GEMM_ERR_INVALID_ARG;
+    if (scale_b && g5::overlap(rc, Range{(__int128)(uint64_t)scale_b, (__int128)(uint64_t)scale_b + 4 * (__int128)N}))
+        return GEMM_ERR_INVALID_ARG;
+    // whole 64-deep stages, 16-byte rows of X and Bt, 32-bit buffer offsets
+    if (K == 0 || K % 64 != 0 || g5::row_alignment((uint64_t)X, ldx, 0, 1, 2) < 16 ||
+        g5::row_alignment((uint64_t)Bt, ldbt, 0, 1, 1) < 16 || rx.hi - rx.lo >= ((__int128)1 << 31) ||
+        rb.hi - rb.lo >= ((__int128)1 << 31))
+        return GEMM_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < 4 * (uint64_t)M) return GEMM_ERR_WORKSPACE;
+    if (((uint64_t)workspace % 256) || g5::overlap(rw, rx) || g5::overlap(rw, rb) || g5::overlap(rw, rc) ||
+        g5::overlap(rw, rs))
+        return GEMM_ERR_INVALID_ARG;
+    const int st = g5::check_device();
+    if (st != GEMM_OK) return st;
+    g5::GemmArgs a{};
+    a.A = X;
+    a.B = Bt;
+    a.C = C;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.lda = ldx;
+    a.ldb = ldbt;
+    a.ldc = ldc;
+    a.batch = 1;
+    a.tiles_m = (M + 127) / 128;
+    a.tiles_n = (N + 127) / 128;
+    a.group_m = a.tiles_m <= 8 ? a.tiles_m : 8;
+    a.align_a = 16;
+    a.align_b = 16;
+    a.align_c = g5::row_alignment((uint64_t)C, ldc, 0, 1, ec);
+    a.out_f32 = ec == 4 ? 1 : 0;
+    a.ksplit = 1;
+    a.b_trans = 1;
+    a.fp8 = 1;
+    a.scale_a = scale_x;
+    a.scale_b = scale_b;
+    a.alpha = 1.0f;
+    const hipError_t e = g5::launch_fp8_quant_a(a, (float *)workspace, a.tiles_m * a.tiles_n, (hipStream_t)stream);
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
 int gemm_fp8_quantize_rows(int64_t rows, int64_t cols, const uint16_t *X, int64_t ldx, uint8_t *Q, int64_t ldq,
                            float *scale, void *stream)
 {

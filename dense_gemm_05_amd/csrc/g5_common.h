@@ -90,6 +90,9 @@ struct GemmArgs {
     const float *scale_b;    // fp8: factor of each row of Bt (N floats) or NULL
     int64_t s_scale_a;       // fp8: batch strides of the factors (floats; 0: shared by every entry)
     int64_t s_scale_b;
+    // fp8 with A quantized on load: A holds bf16 rows and amax_a each row's
+    // largest magnitude (M floats); scale_a = amax_a / 448.
+    const float *amax_a;
     float *ws_part;
     unsigned *ws_cnt;
     // EPI_AFFINE: C := alpha * (A.B) + bias[n] + beta * C (C read only when

@@ -520,7 +520,7 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
 // return); `store` applies the fp8 factors and the epilogue and writes the
 // tile to C through LDS.
 template <int BM, int BN, int WGM, int WGN, int NSA, int NSB, int AV, bool MASKED, int EPI = EPI_NONE,
-          bool BT = false, bool F8 = false, bool AT = false>
+          bool BT = false, bool F8 = false, bool AT = false, bool QA = false>
 struct RingTile {
     static constexpr int NWAVE = WGM * WGN;
     static constexpr int BK = 32;                                    // slot row: 32 bf16 = 64 bytes
@@ -530,13 +530,21 @@ struct RingTile {
     static_assert(!AT || (!F8 && !BT && AV == 16 && (EPI == EPI_NONE || EPI == EPI_AFFINE)),
                   "transposed A: bf16, B as [K, N], plain or affine epilogue");
     static_assert(!AT || ((BM / 8) % 8 == 0 && (BM % 128 != 0 || (BM / 8) % 16 == 0)), "At slot rows: whole swizzle groups");
+    // QA: A is given as bf16 rows and quantized to E4M3FN codes on the way
+    // into LDS (see accumulate); fp8 B codes given transposed, 4-slot rings.
+    static_assert(!QA || (F8 && BT && !AT && EPI == EPI_NONE && NSA == 2 && NSB == 4 && AV == 16 &&
+                          BM * 4 == WGM * WGN * 64),
+                  "quantized-on-load A: fp8, Bt, 2 code slots and 4 B slots, one 16-code chunk per lane");
     static constexpr int TM = BM / WGM, TN = BN / WGN;
     static constexpr int FM = TM / 16, FN = TN / 16;
     static constexpr int NMFMA = FM * FN;
     static constexpr int TAIL = NMFMA / 2;                           // MFMAs run after the barrier
     static constexpr int A_ELEMS = BM * BK, B_ELEMS = BK * BN;
     static constexpr int B_BASE = NSA * A_ELEMS;                     // B ring after the A ring (elements)
-    static constexpr int LDS_BYTES = (NSA * A_ELEMS + NSB * B_ELEMS) * 2;
+    // (QA: two stages of the bf16 A slab staged after the rings, 2 BM x 64
+    // bf16 per stage)
+    static constexpr int QA_STAGE_BYTES = QA ? BM * 64 * 2 : 0;
+    static constexpr int LDS_BYTES = (NSA * A_ELEMS + NSB * B_ELEMS) * 2 + 2 * QA_STAGE_BYTES;
     static constexpr int A_INS = A_ELEMS * 2 / (64 * AV), B_INS = B_ELEMS * 2 / 1024;   // copy instructions
     static constexpr int A_W = NWAVE / 2, B_W = NWAVE / 2;           // copying waves per operand
     static constexpr int LA = A_INS / A_W, LB = B_INS / B_W;         // copies per wave per stage
@@ -545,7 +553,7 @@ struct RingTile {
     static_assert(AV == 16 || AV == 4, "A copy width");
     static_assert(A_INS % A_W == 0 && B_INS % B_W == 0, "slab split");
     static_assert((BN / 8) % 8 == 0 && (BN % 128 != 0 || (BN / 8) % 16 == 0), "B slot rows must be whole swizzle groups");
-    static_assert(NSA >= 3 && NSB >= 3 && LA * (NSA - 2) < 64 && LB * (NSB - 2) < 64, "vmcnt accounting");
+    static_assert((QA || NSA >= 3) && NSB >= 3 && LA * (NSA - 2) < 64 && LB * (NSB - 2) < 64, "vmcnt accounting");
     static_assert(TAIL > 0 && TAIL < NMFMA, "tail");
     static constexpr bool GLU = EPI == EPI_SWIGLU;
     static constexpr int HALF = BN / 2;                       // GLU: columns per weight half
@@ -575,7 +583,7 @@ struct RingTile {
     // n0: first output column (GLU: first column of each weight half)
     const int64_t m0 = tc.tm * BM, n0 = tc.tn * (GLU ? HALF : BN);
     const int64_t M = p.M, N = p.N, lda = p.lda, ldb = p.ldb;
-    const char *Abat = (const char *)p.A + (tc.b * p.sA + (AT ? kbase * lda : kbase)) * EB;
+    const char *Abat = (const char *)p.A + (tc.b * p.sA + (AT ? kbase * lda : kbase)) * (QA ? 2 : EB);
     const char *Bbat = (const char *)p.B + (tc.b * p.sB + (BT ? kbase : kbase * ldb)) * EB;
     // Byte extents of this batch entry's operands from those bases (reads
     // past them return 0).
@@ -583,7 +591,7 @@ struct RingTile {
     // guarantees is inside the allocation: M % 8 == 0 or padded rows.)
     const uint32_t a_bytes = !MASKED ? 0x7fffffffu
                              : AT    ? (uint32_t)(((p.K - kbase - 1) * lda + ((M + 7) & ~(int64_t)7)) * 2)
-                                     : (uint32_t)(((M - 1) * lda + (p.K - kbase)) * EB);
+                                     : (uint32_t)(((M - 1) * lda + (p.K - kbase)) * (QA ? 2 : EB));
     const uint32_t b_bytes =
         !MASKED ? 0x7fffffffu
         : BT    ? (uint32_t)(((N - 1) * ldb + (p.K - kbase)) * EB)
@@ -636,6 +644,7 @@ struct RingTile {
     // Each copying wave issues only its operand: A waves copy stage kt into
     // the A slot of stage ks (ks % NSA), B waves into B slot ks % NSB.
     auto issue = [&](int kt, int ks) {
+        if (QA && a_wave) return;          // (QA: A goes through registers, qa_point below)
         if (a_wave) {
             uint16_t *sl = smem + (ks % NSA) * A_ELEMS;
             // 64 bytes of each A row, or BK rows of At, per stage
@@ -735,23 +744,107 @@ struct RingTile {
     // NSA-2 (A waves) or NSB-2 (B waves) stages of its copies may still be in
     // flight -- and its LDS reads are done, then the workgroup barrier.
     auto stage_barrier = [&]() {
-        if (a_wave) __builtin_amdgcn_s_waitcnt(waitcnt_imm(LA * (NSA - 2), 0));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_imm(LB * (NSB - 2), 0));
+        if constexpr (QA) {
+            // at the barrier after point s the B stage s - 2 must have
+            // landed; issued after it: 2 staging copies and LB B copies at
+            // each of points s - 1 and s (4 + 2 LB), of which the oldest two
+            // (stage s - 2's staging, already converted) may be waited for too
+            if (a_wave) __builtin_amdgcn_s_waitcnt(waitcnt_imm(2, 0));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * LB + 2, 0));
+        } else {
+            if (a_wave) __builtin_amdgcn_s_waitcnt(waitcnt_imm(LA * (NSA - 2), 0));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_imm(LB * (NSB - 2), 0));
+        }
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");   // no LDS access moves across the barrier
     };
 
     const int KT = (int)(K / KS);                             // whole stages
+
+    // QA: A arrives as bf16 rows [M, K] (p.A, row stride p.lda elements) with
+    // each row's largest magnitude in p.amax_a[m], and is quantized on the
+    // way into LDS by the rule of the row quantizer (the code nearest to
+    // x * 448 / amax, one correctly rounded division, then the
+    // round-to-nearest-even conversion), so the codes are those a separate
+    // quantization pass would have written.  Lane tid owns one 16-code chunk
+    // of each stage's A slab: tile row qa_r = tid / 4, K columns
+    // 16 (tid % 4) .. + 15 of the stage.  Its 32 bytes of bf16 are copied by
+    // two direct-to-LDS loads into a staging area that only this lane reads
+    // (lane order, 16 bytes per lane per copy), one point ahead, then read
+    // back, converted and written as 16 codes to the chunk's place in the
+    // swizzled code slot.  At the point that copies B stage s: convert A
+    // stage s - 2 (its staging landed: only this wave's B copies of the
+    // previous point were issued after it), then copy A stage s - 1's bf16,
+    // then B stage s.  Requires K % 64 == 0.
+    const int qa_r = tid >> 2, qa_c = tid & 3;
+    const bool qa_row = QA && m0 + qa_r < M;
+    const uint32_t qa_off = qa_row ? (uint32_t)(((m0 + qa_r) * lda + 16 * qa_c) * 2) : 0x80000000u;
+    const float qa_amax = qa_row ? p.amax_a[m0 + qa_r] : 0.f;
+    uint16_t *const qa_stage = smem + (NSA * A_ELEMS + NSB * B_ELEMS);
+    auto qa_copy = [&](int st) {          // bf16 of stage st (clamped) into staging st % 2
+        const int sc = st < KT ? st : KT - 1;
+        const uint32_t adv = (uint32_t)sc * 128;
+        const i32x4_t r = make_rsrc(Abat + adv, a_bytes - adv);
+        uint16_t *dst = qa_stage + (st & 1) * (QA_STAGE_BYTES / 2) + wave * 512;
+        dma<16>(r, qa_off, 0, dst);
+        dma<16>(r, qa_off + 16, 0, dst + NWAVE * 512);
+    };
+    auto qa_convert = [&](int st) {       // staging st % 2 -> codes in A slot st % NSA
+        const uint16_t *src = qa_stage + (st & 1) * (QA_STAGE_BYTES / 2) + tid * 8;
+        const u32x4 lo = *(const u32x4 *)src, hi = *(const u32x4 *)(src + NWAVE * 512);
+        auto q = [&](float x) {
+            const float y = qa_amax > 0.0f ? __fdiv_rn(x * 448.0f, qa_amax) : x * 0.0f;
+            return y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);
+        };
+        auto code4 = [&](uint32_t w0, uint32_t w1) {
+            int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q(bf16_lo(w0)), q(bf16_hi(w0)), 0, false);
+            pk = __builtin_amdgcn_cvt_pk_fp8_f32(q(bf16_lo(w1)), q(bf16_hi(w1)), pk, true);
+            return (uint32_t)pk;
+        };
+        const u32x4 codes = {code4(lo[0], lo[1]), code4(lo[2], lo[3]), code4(hi[0], hi[1]), code4(hi[2], hi[3])};
+        *(u32x4 *)(smem + (st % NSA) * A_ELEMS + qa_r * BK + ((qa_c ^ ((qa_r >> 1) & 3)) * 8)) = codes;
+    };
+    auto qa_point = [&](int s) {
+        if (a_wave) __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_imm(LB, 15));
+        asm volatile("" ::: "memory");
+        if (s - 2 < KT) qa_convert(s - 2);
+        qa_copy(s - 1);
+    };
+
     // A stage past the last reloads the last one, into the slot of the stage
     // it stands for, which is never read again.
-    auto issue_clamped = [&](int ks) { issue(ks < KT ? ks : KT - 1, ks); };
+    auto issue_clamped = [&](int ks) {
+        // (QA: the point is B's stage number for every wave; A waves are
+        // called with their A ring's stage, NSB - NSA behind)
+        if constexpr (QA) qa_point(a_wave ? ks + NSB - NSA : ks);
+        issue(ks < KT ? ks : KT - 1, ks);
+    };
     Frags f0, f1;
     if (KT > 0) {
+        if constexpr (QA) {
+            // Prologue: bf16 A stages 0 and 1 and B stages 0..NSB-2; A stage
+            // 0 converted once its staging landed (issued after it: A stage
+            // 1's 2 copies and this wave's B copies), B stage 0 landed.
+            qa_copy(0);
+            qa_copy(1);
+            if (!a_wave)
+                for (int s2 = 0; s2 < NSB - 1; ++s2) issue(s2 < KT ? s2 : KT - 1, s2);
+            if (a_wave) __builtin_amdgcn_s_waitcnt(waitcnt_imm(2, 15));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 + LB * (NSB - 1), 15));
+            asm volatile("" ::: "memory");
+            qa_convert(0);
+            if (a_wave) __builtin_amdgcn_s_waitcnt(waitcnt_imm(2, 0));
+            else __builtin_amdgcn_s_waitcnt(waitcnt_imm(LB * (NSB - 2), 0));
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        } else {
         // Prologue: A stages 0..NSA-2 and B stages 0..NSB-2 (clamped, see
         // below), stage 0 complete.
         const int NPRO = a_wave ? NSA - 1 : NSB - 1;
         for (int s2 = 0; s2 < NPRO; ++s2) issue_clamped(s2);
         stage_barrier();
+        }
         read_frags(f0, 0);
 
         // One stage: copies for stage kt+NSA-1 (A waves) or kt+NSB-1 (B
@@ -818,7 +911,7 @@ struct RingTile {
             if (kt < KT) step(kt, f0, f1);
         }
     }
-    if (MASKED && K % KS != 0) {
+    if (!QA && MASKED && K % KS != 0) {
         // K remainder: every copy in flight lands first, then the last stage
         // is loaded element by element with zero fill into slot 0.
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));

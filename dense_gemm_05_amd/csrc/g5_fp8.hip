@@ -199,6 +199,58 @@ hipError_t launch_quant_cols_e4m3(const uint16_t *W, int64_t ldw, int64_t K, int
     return hipGetLastError();
 }
 
+// The largest magnitude of each bf16 row of X (pass 1 of the row quantizer,
+// the same reduction) into amax[r], and its factor amax / 448 into scale[r].
+__global__ void __launch_bounds__(256) k_row_amax(const uint16_t *X, int64_t ldx, int64_t cols, int align_x,
+                                                  float *amax_out, float *scale)
+{
+    const int64_t r = blockIdx.x;
+    const uint16_t *x = X + r * ldx;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float m = 0.0f;
+    for (int64_t c = (int64_t)tid * 8; c < cols; c += 2048) {
+        const u32x4 v = load_chunk8_bf16(x, c, cols, true, align_x);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[i])), fabsf(bf16_hi(v[i]))));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    __shared__ float red[4];
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    if (tid == 0) {
+        const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        amax_out[r] = amax;
+        scale[r] = amax / 448.0f;
+    }
+}
+
+// The scaled FP8 product with A quantized on load (Example 5-8's fused
+// alternative): 128x128 ring tiles whose A slab is read as bf16 and
+// converted to codes in LDS (RingTile QA).  Masked edges; K % 64 == 0.
+__global__ void __launch_bounds__(512, 4) k_f8_qa(GemmArgs p)
+{
+    using R = RingTile<128, 128, 4, 2, 2, 4, 16, true, EPI_NONE, true, true, false, true>;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[R::LDS_BYTES / 2];
+    const TileCoord tc = tile_map(blockIdx.x, p.batch, p.tiles_m, p.tiles_n, p.group_m);
+    f32x4 acc[R::FN][R::FM];
+    R::zero(acc);
+    R::accumulate(p, smem, tc, 0, p.K, acc);
+    R::store(p, smem, tc, acc);
+}
+
+hipError_t launch_fp8_quant_a(const GemmArgs &a, float *amax, int64_t grid, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_row_amax, dim3((unsigned)a.M), dim3(256), 0, s, (const uint16_t *)a.A, a.lda, a.K, a.align_a,
+                       amax, const_cast<float *>(a.scale_a));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    GemmArgs b = a;
+    b.amax_a = amax;
+    hipLaunchKernelGGL(k_f8_qa, dim3((unsigned)grid), dim3(512), 0, s, b);
+    return hipGetLastError();
+}
+
 template <int BM, int BN, int WGM, int WGN, int EPI>
 static hipError_t launch_f8(const GemmArgs &a, int variant, int64_t grid, hipStream_t s)
 {

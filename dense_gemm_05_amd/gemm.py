@@ -23,6 +23,7 @@ __all__ = ["gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm
            "gemm_bf16_tn", "gemm_bf16_tn_batched",
            "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_bf16_silu_batched", "gemm_bf16_swiglu_batched",
            "gemm_fp8_quantize_rows", "gemm_fp8_quantize_cols", "gemm_fp8_nt", "gemm_fp8_nt_affine",
+           "gemm_fp8_nt_quant_a",
            "gemm_bf16_affine",
            "gemm_bf16_nt_affine", "gemm_bf16_tn_affine", "plan_query", "workspace_size", "Workspace",
            "GemmError"]
@@ -441,6 +442,51 @@ def gemm_fp8_nt(A, scale_a, Bt, scale_b, C=None, out_dtype=torch.bfloat16, works
     factors [batch, M] / [batch, N], or [M] / [N] for an operand broadcast
     along the batch (stride 0)."""
     return _fp8(A, scale_a, Bt, scale_b, C, out_dtype, workspace)
+
+
+def gemm_fp8_nt_quant_a(X, Bt, scale_b, C=None, scale_x=None, out_dtype=torch.bfloat16, workspace=None):
+    """The FP8 product with X [M, K] (bfloat16) quantized inside the GEMM
+    (gemm_fp8_nt_quant_a): returns (C [M, N], scale_x float32 [M], X's row
+    factors).  Bt [N, K] codes with factors scale_b [N] (or None).  The
+    workspace (a Workspace or a uint8 tensor) holds M floats; a Workspace is
+    created for the call when None is given."""
+    if X.dtype != torch.bfloat16 or X.dim() != 2:
+        raise TypeError("gemm_fp8_nt_quant_a takes a 2-D bfloat16 X")
+    Bt = _codes(Bt)
+    M, K = X.shape
+    N, K2 = Bt.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    dev = _check_dev(X, Bt, C, scale_b, scale_x)
+    if scale_b is not None and (scale_b.dtype != torch.float32 or tuple(scale_b.shape) != (N,) or
+                                (N > 1 and scale_b.stride(0) != 1)):
+        raise ValueError(f"scale_b must be a contiguous float32 vector of {N}")
+    if scale_x is None:
+        scale_x = torch.empty((M,), dtype=torch.float32, device=dev)
+    if scale_x.dtype != torch.float32 or tuple(scale_x.shape) != (M,) or (M > 1 and scale_x.stride(0) != 1):
+        raise ValueError(f"scale_x must be a contiguous float32 vector of {M}")
+    if C is None:
+        C = torch.empty((M, N), dtype=out_dtype, device=dev)
+    if C.shape != (M, N):
+        raise ValueError("C must be [M, N]")
+    if workspace is None:
+        workspace = Workspace(dev)
+    if isinstance(workspace, Workspace):
+        if workspace.device != dev:
+            raise ValueError("the workspace must be on the operands' GPU")
+        buf = workspace.reserve(4 * M)
+    else:
+        buf = workspace
+        if not isinstance(buf, torch.Tensor) or buf.dtype != torch.uint8 or buf.dim() != 1:
+            raise ValueError("a workspace tensor must be a 1-D uint8 tensor")
+        _check_dev(X, buf)
+    code = _out_code(C.dtype)
+    st = _launch(lib().gemm_fp8_nt_quant_a, dev, M, N, K, X.data_ptr(), _ld(X, K), scale_x.data_ptr(), Bt.data_ptr(),
+                 _ld(Bt, K), None if scale_b is None else scale_b.data_ptr(), C.data_ptr(), _ld(C, N), code,
+                 buf.data_ptr(), buf.numel())
+    if st != 0:
+        raise GemmError(st, "gemm_fp8_nt_quant_a")
+    return C, scale_x
 
 
 def gemm_fp8_nt_affine(A, scale_a, Bt, scale_b, C, alpha=1.0, bias=None, beta=0.0, workspace=None):

@@ -213,6 +213,28 @@ int gemm_fp8_nt(int64_t M, int64_t N, int64_t K,
                 void *C, int64_t ldc, int c_type,
                 void *stream);
 
+/* The scaled FP8 product with the input quantized inside the GEMM, the
+ * alternative Example 5-8 ("Operator & Runtime" §5.4.3) weighs against
+ * quantizing it first: X [M, K] bf16 rows (row stride ldx elements), Bt
+ * [N, K] E4M3FN codes with factors scale_b (or NULL).  A first pass reads X
+ * once for each row's largest magnitude (into the caller's workspace, M
+ * floats) and writes the row's factor amax/448 to scale_x[M]; the product
+ * then reads X as bf16 in every 128x128 output tile and converts it to codes
+ * on the way into local memory, by the rule of gemm_fp8_quantize_rows, so C
+ * equals gemm_fp8_nt on the codes gemm_fp8_quantize_rows(X) gives, computed
+ * with the same tiles (bit for bit).  C bf16 or float by c_type.  Requires
+ * K % 64 == 0 and 16-byte aligned rows of X and Bt (else
+ * GEMM_ERR_UNSUPPORTED); workspace: at least 4 M bytes, 256-byte aligned
+ * (else GEMM_ERR_WORKSPACE, or GEMM_ERR_INVALID_ARG for the alignment);
+ * GEMM_ERR_INVALID_ARG for negative sizes, short strides, NULL or unaligned
+ * pointers and overlapping buffers.  Nothing is allocated. */
+int gemm_fp8_nt_quant_a(int64_t M, int64_t N, int64_t K,
+                        const uint16_t *X, int64_t ldx, float *scale_x,
+                        const uint8_t *Bt, int64_t ldbt, const float *scale_b,
+                        void *C, int64_t ldc, int c_type,
+                        void *workspace, uint64_t workspace_bytes,
+                        void *stream);
+
 /* The same for a batch of products (e.g. the experts of a mixture-of-
  * experts layer): entry b multiplies A + b*strideA by Bt + b*strideBt into
  * C + b*strideC (strides in elements; a stride of 0 broadcasts an operand).

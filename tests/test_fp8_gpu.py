@@ -367,3 +367,57 @@ def test_fp8_nt_affine(oracle_mod, monkeypatch, cfg, M, N, K):
         g5.gemm_fp8_nt_affine(dA, dsa, dB, dsb, C, alpha=alpha, bias=db, beta=beta, workspace=ws())
         ref = oracle_mod.gemm_fp8_nt_affine(A, sa, Bt, sb, alpha=alpha, bias=bias, beta=beta, C_old=C_old)
         _check_fp8_affine(host_values(C), ref, D, K, am, bm, alpha, bv, beta, ov, out, f"fp8 affine {cfg} {out}")
+
+
+# ------------------------------------------------ quantization inside the GEMM
+@pytest.mark.parametrize("M,N,K", [(300, 392, 256), (257, 200, 320), (4096, 1536, 1024), (1, 128, 64),
+                                   (130, 1000, 4096)])
+def test_fp8_quant_a_equals_separate(oracle_mod, monkeypatch, M, N, K):
+    """Example 5-8's fused alternative: X quantized inside the GEMM gives the
+    factors of gemm_fp8_quantize_rows bit for bit and the C of the separate
+    path on the same 128x128 tiles bit for bit (whole stage pairs, K % 128
+    == 0, and an odd stage count); ragged M and N; also within the FP8 bar
+    of the oracle."""
+    _say(f"fp8 quant-A {M}x{N}x{K}")
+    g = np.random.default_rng([gi.SEED_BASE + 7600, M, N, K])
+    X = gi.to_bf16_bits(gi.normal(g, (M, K)) * np.float32(2.0) ** g.integers(-6, 6, (M, 1)).astype(np.float32))
+    Wt = gi.to_bf16_bits(gi.normal(g, (N, K), 0.125))
+    dX = dev_bf16(X)
+    qW, sW = g5.gemm_fp8_quantize_rows(dev_bf16(Wt))
+    qX, sX = g5.gemm_fp8_quantize_rows(dX)
+    monkeypatch.setenv("GEMM_FORCE_CONFIG", "bf16_128x128")
+    monkeypatch.setenv("GEMM_FORCE_KSPLIT", "1")
+    C_sep = g5.gemm_fp8_nt(qX, sX, qW, sW, out_dtype=torch.float32, workspace=ws())
+    C_f, sX_f = g5.gemm_fp8_nt_quant_a(dX, qW, sW, out_dtype=torch.float32, workspace=ws())
+    assert torch.equal(sX_f.view(torch.int32), sX.view(torch.int32)), "row factors differ"
+    assert torch.equal(C_f.view(torch.int32), C_sep.view(torch.int32)), \
+        f"{int((C_f != C_sep).sum())} of {M * N} outputs differ from the separate path"
+    rX, rsX = oracle_mod.quantize_rows_e4m3(X)
+    rW, rsW = oracle_mod.quantize_rows_e4m3(Wt)
+    rows = np.unique(np.linspace(0, M - 1, min(M, 9)).astype(int))
+    ref = oracle_mod.gemm_fp8_nt(np.ascontiguousarray(rX[rows]), rsX[rows], rW, rsW)
+    check_fp8(host_values(C_f)[rows], ref, K, _amax(oracle_mod, rX, rsX), _amax(oracle_mod, rW, rsW), "f32",
+              "fp8 quant-A rows")
+
+
+def test_fp8_quant_a_bf16_out_and_repeat():
+    """bf16 output, the same bits on a second call with a caller tensor as
+    workspace, and the nearest-code rule at exact ties inside the GEMM."""
+    M, N, K = 64, 256, 128
+    g = np.random.default_rng([gi.SEED_BASE + 7650])
+    x = gi.normal(g, (M, K))
+    for i, (t, amax) in enumerate(_TIES):                   # quotients exactly on midpoints
+        x[i, 0], x[i, 1] = t, -amax
+    X = gi.to_bf16_bits(x)
+    dX = dev_bf16(X)
+    qW, sW = g5.gemm_fp8_quantize_rows(dev_bf16(gi.to_bf16_bits(gi.normal(g, (N, K), 0.125))))
+    wsb = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    C1, s1 = g5.gemm_fp8_nt_quant_a(dX, qW, sW, workspace=wsb)
+    C2, s2 = g5.gemm_fp8_nt_quant_a(dX, qW, sW, workspace=wsb)
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16)) and torch.equal(s1, s2)
+    qX, sX = g5.gemm_fp8_quantize_rows(dX)
+    C_sep = g5.gemm_fp8_nt(qX, sX, qW, sW)
+    # (the separate product may take other tiles: compare within the bar)
+    assert torch.equal(s1.view(torch.int32), sX.view(torch.int32))
+    got, ref = host_values(C1), host_values(C_sep)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-6)
