@@ -47,6 +47,61 @@ __device__ __forceinline__ float silu_f32(float x) { return x * __builtin_amdgcn
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// E4M3FN quantization of bf16 values against their row's (or column's)
+// largest magnitude amax (page "Operator & Runtime" §5.4.3, Example 5-7): the code nearest
+// to x * 448 / amax.  t = x * 448 is exact in binary32 (a bf16 significand
+// times 7 * 64).  A quotient of two bf16 values sits either exactly on a
+// midpoint between two E4M3FN values (at most 5 significant bits) or at
+// least ~2^-13 of its size away from every midpoint, so any binary32
+// quotient within ~2^-20 of the exact one that is exact at those midpoints
+// gives, after the round-to-nearest-even conversion, the same code as the
+// exact quotient.  Two such quotients:
+//  - div: the correctly rounded division, clamped to +-448 (the conversion
+//    turns larger values into NaN); defined for every amax > 0;
+//  - fast: q0 = t * r with r = 1/amax correctly rounded, then one residual
+//    step q0 + (t - q0 * amax) * r, both with single-rounding fmas
+//    (Markstein's correction): exact whenever the quotient is, within ~1
+//    ulp otherwise, and four instructions instead of a dozen.  For every
+//    bf16 amax in [2^-126, 2^118] (x * 448 cannot overflow; the reciprocal
+//    and the residual stay normal) and every bf16 x with |x| <= amax it
+//    gives the code of div, never exceeds 448 in magnitude, and keeps the
+//    sign of -0 (the residual is formed as q0 * amax - t and negated inside
+//    the second fma): checked exhaustively on the host over all such pairs.
+// A zero row (amax = 0) gives signed zeros.  Each quantizer takes the fast
+// form when its amax is in range (uniform over a row) and div otherwise.
+struct E4m3Quot {
+    float amax, rcp;
+    bool fast;
+    __device__ __forceinline__ explicit E4m3Quot(float a)
+        : amax(a), rcp(__frcp_rn(a)), fast(a >= 0x1p-126f && a <= 0x1p118f) {}
+    __device__ __forceinline__ float q_fast(float x) const
+    {
+        const float t = x * 448.0f;
+        const float q0 = t * rcp;
+        const float e = __builtin_fmaf(q0, amax, -t);
+        return __builtin_fmaf(-e, rcp, q0);
+    }
+    __device__ __forceinline__ float q_div(float x) const
+    {
+        const float y = amax > 0.0f ? __fdiv_rn(x * 448.0f, amax) : x * 0.0f;
+        return y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);
+    }
+    // codes of 8 bf16 values (4 words, low half first), 4 per 32-bit word
+    template <bool FAST>
+    __device__ __forceinline__ uint32_t code4(uint32_t w0, uint32_t w1) const
+    {
+        auto q = [&](float x) { return FAST ? q_fast(x) : q_div(x); };
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q(bf16_lo(w0)), q(bf16_hi(w0)), 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(q(bf16_lo(w1)), q(bf16_hi(w1)), pk, true);
+        return (uint32_t)pk;
+    }
+    __device__ __forceinline__ uint32_t code1(float x) const
+    {
+        const float y = fast ? q_fast(x) : q_div(x);
+        return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xffu;
+    }
+};
+
 // Fused epilogues of a bf16 output chunk (8 values, already rounded once to
 // bf16 from the FP32 sums: the rounding of the unfused program survives,
 // §5.4.3).  SiLU: y = bf16(SiLU(g)).  SwiGLU (§5.3.1): z = bf16(t * u) with
@@ -763,10 +818,9 @@ struct RingTile {
 
     // QA: A arrives as bf16 rows [M, K] (p.A, row stride p.lda elements) with
     // each row's largest magnitude in p.amax_a[m], and is quantized on the
-    // way into LDS by the rule of the row quantizer (the code nearest to
-    // x * 448 / amax, one correctly rounded division, then the
-    // round-to-nearest-even conversion), so the codes are those a separate
-    // quantization pass would have written.  Lane tid owns one 16-code chunk
+    // way into LDS by the row quantizer's rule (E4m3Quot: the code nearest
+    // to x * 448 / amax), so the codes are those a separate quantization
+    // pass would have written.  Lane tid owns one 16-code chunk
     // of each stage's A slab: tile row qa_r = tid / 4, K columns
     // 16 (tid % 4) .. + 15 of the stage.  Its 32 bytes of bf16 are copied by
     // two direct-to-LDS loads into a staging area that only this lane reads
@@ -779,7 +833,7 @@ struct RingTile {
     const int qa_r = tid >> 2, qa_c = tid & 3;
     const bool qa_row = QA && m0 + qa_r < M;
     const uint32_t qa_off = qa_row ? (uint32_t)(((m0 + qa_r) * lda + 16 * qa_c) * 2) : 0x80000000u;
-    const float qa_amax = qa_row ? p.amax_a[m0 + qa_r] : 0.f;
+    const E4m3Quot qa_q(qa_row ? p.amax_a[m0 + qa_r] : 0.f);
     uint16_t *const qa_stage = smem + (NSA * A_ELEMS + NSB * B_ELEMS);
     auto qa_copy = [&](int st) {          // bf16 of stage st (clamped) into staging st % 2
         const int sc = st < KT ? st : KT - 1;
@@ -792,16 +846,13 @@ struct RingTile {
     auto qa_convert = [&](int st) {       // staging st % 2 -> codes in A slot st % NSA
         const uint16_t *src = qa_stage + (st & 1) * (QA_STAGE_BYTES / 2) + tid * 8;
         const u32x4 lo = *(const u32x4 *)src, hi = *(const u32x4 *)(src + NWAVE * 512);
-        auto q = [&](float x) {
-            const float y = qa_amax > 0.0f ? __fdiv_rn(x * 448.0f, qa_amax) : x * 0.0f;
-            return y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);
-        };
-        auto code4 = [&](uint32_t w0, uint32_t w1) {
-            int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q(bf16_lo(w0)), q(bf16_hi(w0)), 0, false);
-            pk = __builtin_amdgcn_cvt_pk_fp8_f32(q(bf16_lo(w1)), q(bf16_hi(w1)), pk, true);
-            return (uint32_t)pk;
-        };
-        const u32x4 codes = {code4(lo[0], lo[1]), code4(lo[2], lo[3]), code4(hi[0], hi[1]), code4(hi[2], hi[3])};
+        u32x4 codes;
+        if (qa_q.fast)
+            codes = u32x4{qa_q.code4<true>(lo[0], lo[1]), qa_q.code4<true>(lo[2], lo[3]),
+                          qa_q.code4<true>(hi[0], hi[1]), qa_q.code4<true>(hi[2], hi[3])};
+        else
+            codes = u32x4{qa_q.code4<false>(lo[0], lo[1]), qa_q.code4<false>(lo[2], lo[3]),
+                          qa_q.code4<false>(hi[0], hi[1]), qa_q.code4<false>(hi[2], hi[3])};
         *(u32x4 *)(smem + (st % NSA) * A_ELEMS + qa_r * BK + ((qa_c ^ ((qa_r >> 1) & 3)) * 8)) = codes;
     };
     auto qa_point = [&](int s) {

@@ -5,100 +5,99 @@
 // dequantize the FP32 sums by the row and column factors).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "g5_common.h"
 #include "g5_device.h"
 #include "g5_kernels.h"
 
 namespace g5 {
 
-// One workgroup per row.  Pass 1 finds the row's largest magnitude (each
-// thread over its 16-byte chunks, then across the wave by butterfly
-// exchanges, then across the 4 waves in LDS: the tree reduction of the
-// reduce page, "3.1 Tối ưu toán tử CUDA Reduce").  Pass 2 writes the codes:
-// y = (x * 448) / amax in binary32 (one correctly rounded division), then
-// the hardware conversion, which rounds to the nearest E4M3FN value, ties
-// to even -- the code nearest to the exact quotient of Example 5-7 (see
-// quot below).  The row's dequantization factor is amax / 448; a row of
-// zeros gets zero codes and factor 0.  Rows of up to
-// NCH * 2048 elements stay in registers between the passes; longer rows
-// are read again in pass 2.
+// One wave per row, four rows per workgroup.  Pass 1 finds the row's
+// largest magnitude: each lane over its 16-byte chunks (all of a held row's
+// loads issued before the first is used), then across the wave by butterfly
+// exchanges (the tree reduction of the reduce page, "3.1 Tối ưu toán tử
+// CUDA Reduce", at wave scope: no LDS, no barrier).  Pass 2 writes the
+// codes: the quotient x * 448 / amax in binary32 (E4m3Quot), then the
+// hardware conversion, which rounds to the nearest E4M3FN value, ties to
+// even -- the code nearest to the exact quotient of Example 5-7.  The row's
+// dequantization factor is amax / 448; a row of zeros gets zero codes and
+// factor 0.  Rows of up to NCH * 512 elements stay in registers between the
+// passes; longer rows are read again in pass 2.
 template <int NCH>
-__global__ void __launch_bounds__(256) k_quant_rows_e4m3(const uint16_t *X, int64_t ldx, int64_t cols, int align_x,
-                                                         uint8_t *Q, int64_t ldq, int align_q, float *scale)
+__device__ __forceinline__ float wave_row_amax(const uint16_t *x, int64_t cols, int align_x, int lane, u32x4 (&v)[NCH],
+                                               bool held)
 {
-    const int64_t r = blockIdx.x;
-    const uint16_t *x = X + r * ldx;
-    uint8_t *q = Q + r * ldq;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const bool held = cols <= (int64_t)NCH * 2048;
-    u32x4 v[NCH];
-    float m = 0.0f;
     auto absmax8 = [](float m, const u32x4 &c) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(c[i])), fabsf(bf16_hi(c[i]))));
         return m;
     };
+    float m = 0.0f;
     if (held) {
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
-            const int64_t c = (int64_t)tid * 8 + (int64_t)j * 2048;
+            const int64_t c = (int64_t)lane * 8 + (int64_t)j * 512;
             v[j] = c < cols ? load_chunk8_bf16(x, c, cols, true, align_x) : u32x4{0u, 0u, 0u, 0u};
-            m = absmax8(m, v[j]);
         }
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) m = absmax8(m, v[j]);
     } else {
-        for (int64_t c = (int64_t)tid * 8; c < cols; c += 2048) m = absmax8(m, load_chunk8_bf16(x, c, cols, true, align_x));
+        for (int64_t c = (int64_t)lane * 8; c < cols; c += 512) m = absmax8(m, load_chunk8_bf16(x, c, cols, true, align_x));
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    __shared__ float red[4];
-    if (lane == 0) red[wave] = m;
-    __syncthreads();
-    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    if (tid == 0) scale[r] = amax / 448.0f;
-    // y = x * 448 / amax with one rounding: x * 448 is exact in binary32 (a
-    // bf16 significand times 7 * 64), and the division is correctly rounded.
-    // A quotient that is exactly the midpoint of two E4M3FN values (at most
-    // 5 significant bits) is then exact, and any other lies at least
-    // ~2^-13 of its size away from every midpoint, far beyond the 2^-24 of
-    // the rounding, so the conversion below (round to nearest even) picks
-    // the code nearest to the exact quotient.  |x| <= amax keeps |y| <= 448
-    // (the clamp only guards the conversion, which turns larger values into
-    // NaN).  A row of zeros gives signed zeros.
-    auto clamp448 = [](float y) { return y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y); };
-    auto quot = [&](float x) { return amax > 0.0f ? clamp448(__fdiv_rn(x * 448.0f, amax)) : x * 0.0f; };
-    auto emit = [&](int64_t c, const u32x4 &cv) {
-        uint32_t w[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const float y0 = quot(bf16_lo(cv[2 * h])), y1 = quot(bf16_hi(cv[2 * h]));
-            const float y2 = quot(bf16_lo(cv[2 * h + 1])), y3 = quot(bf16_hi(cv[2 * h + 1]));
-            int packed = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-            packed = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, packed, true);
-            w[h] = (uint32_t)packed;
-        }
+    return m;
+}
+
+template <int NCH>
+__global__ void __launch_bounds__(256) k_quant_rows_e4m3(const uint16_t *X, int64_t ldx, int64_t rows, int64_t cols,
+                                                         int align_x, uint8_t *Q, int64_t ldq, int align_q,
+                                                         float *scale)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows) return;                   // a whole wave; nothing below synchronises waves
+    const uint16_t *x = X + r * ldx;
+    uint8_t *q = Q + r * ldq;
+    const bool held = cols <= (int64_t)NCH * 512;
+    u32x4 v[NCH];
+    const float amax = wave_row_amax<NCH>(x, cols, align_x, lane, v, held);
+    if (lane == 0) scale[r] = amax / 448.0f;
+    // amax is the same for the whole wave, so is the choice of quotient
+    const E4m3Quot qz(amax);
+    auto emit = [&](auto fast, int64_t c, const u32x4 &cv) {
+        constexpr bool F = decltype(fast)::value;
+        const uint32_t w0 = qz.code4<F>(cv[0], cv[1]), w1 = qz.code4<F>(cv[2], cv[3]);
         if (c + 8 <= cols && align_q >= 8) {
-            u32x2 st = {w[0], w[1]};
+            u32x2 st = {w0, w1};
             *(u32x2 *)(q + c) = st;
         } else {
+            const uint32_t w[2] = {w0, w1};
             for (int i = 0; i < 8 && c + i < cols; ++i) q[c + i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
         }
     };
-    if (held) {
+    auto pass2 = [&](auto fast) {
+        if (held) {
 #pragma unroll
-        for (int j = 0; j < NCH; ++j) {
-            const int64_t c = (int64_t)tid * 8 + (int64_t)j * 2048;
-            if (c < cols) emit(c, v[j]);
+            for (int j = 0; j < NCH; ++j) {
+                const int64_t c = (int64_t)lane * 8 + (int64_t)j * 512;
+                if (c < cols) emit(fast, c, v[j]);
+            }
+        } else {
+            for (int64_t c = (int64_t)lane * 8; c < cols; c += 512)
+                emit(fast, c, load_chunk8_bf16(x, c, cols, true, align_x));
         }
-    } else {
-        for (int64_t c = (int64_t)tid * 8; c < cols; c += 2048) emit(c, load_chunk8_bf16(x, c, cols, true, align_x));
-    }
+    };
+    if (qz.fast) pass2(std::true_type{});
+    else pass2(std::false_type{});
 }
 
 hipError_t launch_quant_rows_e4m3(const uint16_t *X, int64_t ldx, int64_t rows, int64_t cols, int align_x,
                                   uint8_t *Q, int64_t ldq, int align_q, float *scale, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_quant_rows_e4m3<4>, dim3((unsigned)rows), dim3(256), 0, s, X, ldx, cols, align_x, Q, ldq,
-                       align_q, scale);
+    hipLaunchKernelGGL(k_quant_rows_e4m3<8>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, X, ldx, rows, cols,
+                       align_x, Q, ldq, align_q, scale);
     return hipGetLastError();
 }
 
@@ -146,13 +145,10 @@ __global__ void __launch_bounds__(256) k_quant_cols_e4m3(const uint16_t *W, int6
     float amax[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax[i] = amax_s[8 * cc + i];
-    // (see k_quant_rows_e4m3: one correctly rounded division, then the
-    // round-to-nearest-even conversion, gives the code nearest to x*448/amax)
-    auto code = [](float x, float a) -> uint32_t {
-        float y = a > 0.0f ? __fdiv_rn(x * 448.0f, a) : x * 0.0f;
-        y = y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);
-        return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xffu;
-    };
+    // codes by E4m3Quot, one per column (the quotient's form is chosen per
+    // column)
+    const E4m3Quot qz[8] = {E4m3Quot(amax[0]), E4m3Quot(amax[1]), E4m3Quot(amax[2]), E4m3Quot(amax[3]),
+                            E4m3Quot(amax[4]), E4m3Quot(amax[5]), E4m3Quot(amax[6]), E4m3Quot(amax[7])};
     const int64_t blocks = (K + 63) / 64;
     const int64_t b0 = blocks * blockIdx.y / gridDim.y, b1 = blocks * (blockIdx.y + 1) / gridDim.y;
     for (int64_t kb = b0 * 64; kb < b1 * 64; kb += 64) {
@@ -163,8 +159,8 @@ __global__ void __launch_bounds__(256) k_quant_cols_e4m3(const uint16_t *W, int6
             const u32x4 v = k < K ? load_chunk8_bf16(W + k * ldw, col, N, true, align_w) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                tile[(8 * cc + 2 * i) * TP + kr] = (uint8_t)code(bf16_lo(v[i]), amax[2 * i]);
-                tile[(8 * cc + 2 * i + 1) * TP + kr] = (uint8_t)code(bf16_hi(v[i]), amax[2 * i + 1]);
+                tile[(8 * cc + 2 * i) * TP + kr] = (uint8_t)qz[2 * i].code1(bf16_lo(v[i]));
+                tile[(8 * cc + 2 * i + 1) * TP + kr] = (uint8_t)qz[2 * i + 1].code1(bf16_hi(v[i]));
             }
         }
         __syncthreads();
@@ -201,25 +197,15 @@ hipError_t launch_quant_cols_e4m3(const uint16_t *W, int64_t ldw, int64_t K, int
 
 // The largest magnitude of each bf16 row of X (pass 1 of the row quantizer,
 // the same reduction) into amax[r], and its factor amax / 448 into scale[r].
-__global__ void __launch_bounds__(256) k_row_amax(const uint16_t *X, int64_t ldx, int64_t cols, int align_x,
-                                                  float *amax_out, float *scale)
+__global__ void __launch_bounds__(256) k_row_amax(const uint16_t *X, int64_t ldx, int64_t rows, int64_t cols,
+                                                  int align_x, float *amax_out, float *scale)
 {
-    const int64_t r = blockIdx.x;
-    const uint16_t *x = X + r * ldx;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    float m = 0.0f;
-    for (int64_t c = (int64_t)tid * 8; c < cols; c += 2048) {
-        const u32x4 v = load_chunk8_bf16(x, c, cols, true, align_x);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[i])), fabsf(bf16_hi(v[i]))));
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    __shared__ float red[4];
-    if (lane == 0) red[wave] = m;
-    __syncthreads();
-    if (tid == 0) {
-        const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    u32x4 v[8];
+    const float amax = wave_row_amax<8>(X + r * ldx, cols, align_x, lane, v, cols <= 8 * 512);
+    if (lane == 0) {
         amax_out[r] = amax;
         scale[r] = amax / 448.0f;
     }
@@ -241,8 +227,8 @@ __global__ void __launch_bounds__(512, 4) k_f8_qa(GemmArgs p)
 
 hipError_t launch_fp8_quant_a(const GemmArgs &a, float *amax, int64_t grid, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_row_amax, dim3((unsigned)a.M), dim3(256), 0, s, (const uint16_t *)a.A, a.lda, a.K, a.align_a,
-                       amax, const_cast<float *>(a.scale_a));
+    hipLaunchKernelGGL(k_row_amax, dim3((unsigned)((a.M + 3) / 4)), dim3(256), 0, s, (const uint16_t *)a.A, a.lda, a.M,
+                       a.K, a.align_a, amax, const_cast<float *>(a.scale_a));
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     GemmArgs b = a;

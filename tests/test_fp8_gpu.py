@@ -421,3 +421,61 @@ def test_fp8_quant_a_bf16_out_and_repeat():
     assert torch.equal(s1.view(torch.int32), sX.view(torch.int32))
     got, ref = host_values(C1), host_values(C_sep)
     assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-6)
+
+
+def _fp8_midpoints():
+    """Every positive rounding midpoint of E4M3FN below 448: (2f+1)·2^-10
+    between subnormals, T·2^(E-4) (T odd, 17..31) between normals."""
+    mids = [(2 * f + 1) * 2.0 ** -10 for f in range(8)]
+    mids += [T * 2.0 ** (E - 4) for E in range(-6, 9) for T in range(17, 32, 2) if T * 2.0 ** (E - 4) < 448]
+    return np.array(mids, np.float64)
+
+
+def test_fp8_quant_a_codes_exact(oracle_mod):
+    """The codes made inside the GEMM equal the oracle's exact ones bit for
+    bit, including rows whose quotients sit exactly on rounding midpoints
+    (amax = 7·2^k or 448), next to them (amax = 1, 3), bf16 subnormals, -0,
+    and row maxima at and beyond both ends of the range where the kernel
+    uses the reciprocal-and-residual quotient (2^-126 and 2^118) as well as
+    outside it (2^-127, 2^-130, 2^119, just above 2^118).  Bt is the
+    identity in codes (1.0 = 0x38) with factors 1, so C[m, n] is the code of
+    X[m, n] times the row factor, one rounding, which separates every code
+    (but not the two zeros)."""
+    K = N = 256
+    amaxes = [1.0, 3.0, 7.0, 448.0, 7 * 2.0 ** -40, 7 * 2.0 ** 60, 2.0 ** -126, 1.5 * 2.0 ** -126,
+              2.0 ** -127, 2.0 ** -130, 2.0 ** 118, 1.0078125 * 2.0 ** 118, 2.0 ** 119, 0.3828125]
+    g = np.random.default_rng([gi.SEED_BASE + 7700])
+    mids = _fp8_midpoints()
+    rows = []
+    for amax in amaxes:
+        for variant in range(3):
+            x = np.empty(K, np.float64)
+            x[0] = amax if variant != 1 else -amax
+            t = mids * amax / 448.0
+            x[1:1 + len(t)] = t * np.where(g.random(len(t)) < 0.5, -1.0, 1.0)
+            rest = 1 + len(t)
+            if variant == 2:                                   # neighbours of the midpoints
+                k = K - rest
+                x[rest:] = np.nextafter(x[1:1 + k].astype(np.float32), np.float32(np.inf)).astype(np.float64) * 1.003
+            else:
+                x[rest:] = g.uniform(-amax, amax, K - rest)
+            x[rest] = -0.0
+            x[rest + 1] = 2.0 ** -133                          # bf16 subnormals
+            x[rest + 2] = -3 * 2.0 ** -131
+            rows.append(np.clip(x, -amax, amax))
+    M = len(rows)
+    X = gi.to_bf16_bits(np.array(rows, np.float32))
+    assert np.all(np.isfinite(gi.bf16_bits_to_f32(X)))
+    _say(f"fp8 quant-A codes {M}x{N}x{K}")
+    ident = np.zeros((N, K), np.uint8)
+    ident[np.arange(N), np.arange(K)] = 0x38
+    qI = dev_u8(ident)
+    ones = torch.ones(N, dtype=torch.float32, device="cuda")
+    C, sX = g5.gemm_fp8_nt_quant_a(dev_bf16(X), qI, ones, out_dtype=torch.float32, workspace=ws())
+    codes, scales = oracle_mod.quantize_rows_e4m3(X)
+    assert np.array_equal(sX.cpu().numpy().view(np.int32), scales.astype(np.float32).view(np.int32))
+    expect = (oracle_mod.e4m3_decode(codes).astype(np.float32) * scales.astype(np.float32)[:, None]).astype(np.float32)
+    got = C.cpu().numpy()
+    bad = np.argwhere(got.view(np.int32) != expect.view(np.int32))
+    bad = [tuple(b) for b in bad if not (got[tuple(b)] == 0 and expect[tuple(b)] == 0)]
+    assert not bad, f"{len(bad)} codes differ, first at {bad[:4]} (row amax {[amaxes[b[0] // 3] for b in bad[:4]]})"
