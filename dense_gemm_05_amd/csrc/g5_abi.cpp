@@ -949,8 +949,25 @@ int gemm_fp8_nt_quant_a(int64_t M, int64_t N, int64_t K, const uint16_t *X, int6
     a.ldb = ldbt;
     a.ldc = ldc;
     a.batch = 1;
-    a.tiles_m = (M + 127) / 128;
-    a.tiles_n = (N + 127) / 128;
+    // Tile width: 256 columns convert each A element half as often as 128
+    // (the conversion, not the MFMAs, bounds the loop), at one workgroup
+    // per CU instead of two.  Per-CU costs measured with K = 4096 (both
+    // scale with K alike): one 128x256 tile 72 us; two 128x128 tiles
+    // sharing a CU 87 us, one alone 50 us.  The width with the smaller
+    // estimate for the busiest CU is taken (e.g. 4096x1536: 256, one tile
+    // per CU on 192 CUs; 1024x12288: 128, three tiles per CU against two
+    // rounds of the wider ones).  GEMM_QA_TILE_N=128|256 forces one
+    // (diagnostic).
+    const int64_t tm = (M + 127) / 128;
+    const int64_t k256 = (tm * ((N + 255) / 256) + g5::kNumCU - 1) / g5::kNumCU;
+    const int64_t k128 = (tm * ((N + 127) / 128) + g5::kNumCU - 1) / g5::kNumCU;
+    int tile_n = 72.0 * k256 < 87.0 * (k128 / 2) + 50.0 * (k128 % 2) ? 256 : 128;
+    if (const char *f = std::getenv("GEMM_QA_TILE_N")) {
+        if (std::strcmp(f, "128") == 0) tile_n = 128;
+        else if (std::strcmp(f, "256") == 0) tile_n = 256;
+    }
+    a.tiles_m = tm;
+    a.tiles_n = (N + tile_n - 1) / tile_n;
     a.group_m = a.tiles_m <= 8 ? a.tiles_m : 8;
     a.align_a = 16;
     a.align_b = 16;
@@ -962,7 +979,7 @@ int gemm_fp8_nt_quant_a(int64_t M, int64_t N, int64_t K, const uint16_t *X, int6
     a.scale_a = scale_x;
     a.scale_b = scale_b;
     a.alpha = 1.0f;
-    const hipError_t e = g5::launch_fp8_quant_a(a, (float *)workspace, a.tiles_m * a.tiles_n, (hipStream_t)stream);
+    const hipError_t e = g5::launch_fp8_quant_a(a, (float *)workspace, tile_n, a.tiles_m * a.tiles_n, (hipStream_t)stream);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 

@@ -212,11 +212,16 @@ __global__ void __launch_bounds__(256) k_row_amax(const uint16_t *X, int64_t ldx
 }
 
 // The scaled FP8 product with A quantized on load (Example 5-8's fused
-// alternative): 128x128 ring tiles whose A slab is read as bf16 and
+// alternative): ring tiles 128 rows tall whose A slab is read as bf16 and
 // converted to codes in LDS (RingTile QA).  Masked edges; K % 64 == 0.
-__global__ void __launch_bounds__(512, 4) k_f8_qa(GemmArgs p)
+// Each A element is converted once per column tile, so wider tiles convert
+// less per flop: 128x256 (8 waves 2x4, 112 KiB of LDS, one workgroup per
+// CU) or 128x128 (8 waves 4x2, 80 KiB, two per CU: its registers are held
+// to 128 so that both fit).
+template <int BN, int WGM, int WGN, int MINW>
+__global__ void __launch_bounds__(512, MINW) k_f8_qa(GemmArgs p)
 {
-    using R = RingTile<128, 128, 4, 2, 2, 4, 16, true, EPI_NONE, true, true, false, true>;
+    using R = RingTile<128, BN, WGM, WGN, 2, 4, 16, true, EPI_NONE, true, true, false, true>;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[R::LDS_BYTES / 2];
     const TileCoord tc = tile_map(blockIdx.x, p.batch, p.tiles_m, p.tiles_n, p.group_m);
     f32x4 acc[R::FN][R::FM];
@@ -225,15 +230,17 @@ __global__ void __launch_bounds__(512, 4) k_f8_qa(GemmArgs p)
     R::store(p, smem, tc, acc);
 }
 
-hipError_t launch_fp8_quant_a(const GemmArgs &a, float *amax, int64_t grid, hipStream_t s)
+hipError_t launch_fp8_quant_a(const GemmArgs &a, float *amax, int tile_n, int64_t grid, hipStream_t s)
 {
+    if (tile_n != 128 && tile_n != 256) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_row_amax, dim3((unsigned)((a.M + 3) / 4)), dim3(256), 0, s, (const uint16_t *)a.A, a.lda, a.M,
                        a.K, a.align_a, amax, const_cast<float *>(a.scale_a));
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     GemmArgs b = a;
     b.amax_a = amax;
-    hipLaunchKernelGGL(k_f8_qa, dim3((unsigned)grid), dim3(512), 0, s, b);
+    if (tile_n == 256) hipLaunchKernelGGL((k_f8_qa<256, 2, 4, 2>), dim3((unsigned)grid), dim3(512), 0, s, b);
+    else hipLaunchKernelGGL((k_f8_qa<128, 4, 2, 4>), dim3((unsigned)grid), dim3(512), 0, s, b);
     return hipGetLastError();
 }
 

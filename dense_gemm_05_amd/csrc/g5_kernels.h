@@ -33,9 +33,10 @@ hipError_t launch_ring_fp8_affine(int config_id, const GemmArgs &a, int variant,
 
 // The FP8 product with A quantized on load: each bf16 row's largest
 // magnitude into amax[M] (device scratch) and its factor into a.scale_a,
-// then 128x128 tiles (grid of them) that convert A to codes in LDS.  a.A
+// then 128 x tile_n tiles (tile_n 128 or 256; grid of them) that convert A
+// to codes in LDS.  a.A
 // holds bf16 rows (16-byte aligned), a.B the Bt codes; K % 64 == 0.
-hipError_t launch_fp8_quant_a(const GemmArgs &a, float *amax, int64_t grid, hipStream_t s);
+hipError_t launch_fp8_quant_a(const GemmArgs &a, float *amax, int tile_n, int64_t grid, hipStream_t s);
 
 // Small M (<= 16) on E4M3FN operands with B given transposed: variant 1
 // one 16-row block of Bt per workgroup, 2 three (grid = blocks of Bt rows).

@@ -219,10 +219,11 @@ int gemm_fp8_nt(int64_t M, int64_t N, int64_t K,
  * [N, K] E4M3FN codes with factors scale_b (or NULL).  A first pass reads X
  * once for each row's largest magnitude (into the caller's workspace, M
  * floats) and writes the row's factor amax/448 to scale_x[M]; the product
- * then reads X as bf16 in every 128x128 output tile and converts it to codes
- * on the way into local memory, by the rule of gemm_fp8_quantize_rows, so C
- * equals gemm_fp8_nt on the codes gemm_fp8_quantize_rows(X) gives, computed
- * with the same tiles (bit for bit).  C bf16 or float by c_type.  Requires
+ * then reads X as bf16 in every output tile (128 rows by 128 or 256
+ * columns) and converts it to codes on the way into local memory, by the
+ * rule of gemm_fp8_quantize_rows, so C equals gemm_fp8_nt on the codes
+ * gemm_fp8_quantize_rows(X) gives, computed with 128x128 tiles and no K
+ * split (bit for bit).  C bf16 or float by c_type.  Requires
  * K % 64 == 0 and 16-byte aligned rows of X and Bt (else
  * GEMM_ERR_UNSUPPORTED); workspace: at least 4 M bytes, 256-byte aligned
  * (else GEMM_ERR_WORKSPACE, or GEMM_ERR_INVALID_ARG for the alignment);

@@ -26,6 +26,7 @@ def _say(msg):
 def _no_forced_config(monkeypatch):
     monkeypatch.delenv("GEMM_FORCE_CONFIG", raising=False)
     monkeypatch.delenv("GEMM_FORCE_KSPLIT", raising=False)
+    monkeypatch.delenv("GEMM_QA_TILE_N", raising=False)
 
 
 def dev_u8(a):
@@ -370,15 +371,19 @@ def test_fp8_nt_affine(oracle_mod, monkeypatch, cfg, M, N, K):
 
 
 # ------------------------------------------------ quantization inside the GEMM
+@pytest.mark.parametrize("tile_n", ["auto", "128", "256"])
 @pytest.mark.parametrize("M,N,K", [(300, 392, 256), (257, 200, 320), (4096, 1536, 1024), (1, 128, 64),
                                    (130, 1000, 4096)])
-def test_fp8_quant_a_equals_separate(oracle_mod, monkeypatch, M, N, K):
+def test_fp8_quant_a_equals_separate(oracle_mod, monkeypatch, M, N, K, tile_n):
     """Example 5-8's fused alternative: X quantized inside the GEMM gives the
     factors of gemm_fp8_quantize_rows bit for bit and the C of the separate
-    path on the same 128x128 tiles bit for bit (whole stage pairs, K % 128
-    == 0, and an odd stage count); ragged M and N; also within the FP8 bar
+    path on 128x128 tiles bit for bit, with 128- or 256-column tiles (each
+    output's sum is the same sequence of MFMAs: whole stage pairs, K % 128
+    == 0, or an odd stage count); ragged M and N; also within the FP8 bar
     of the oracle."""
-    _say(f"fp8 quant-A {M}x{N}x{K}")
+    _say(f"fp8 quant-A {M}x{N}x{K} tile_n {tile_n}")
+    if tile_n != "auto":
+        monkeypatch.setenv("GEMM_QA_TILE_N", tile_n)
     g = np.random.default_rng([gi.SEED_BASE + 7600, M, N, K])
     X = gi.to_bf16_bits(gi.normal(g, (M, K)) * np.float32(2.0) ** g.integers(-6, 6, (M, 1)).astype(np.float32))
     Wt = gi.to_bf16_bits(gi.normal(g, (N, K), 0.125))
@@ -431,7 +436,8 @@ def _fp8_midpoints():
     return np.array(mids, np.float64)
 
 
-def test_fp8_quant_a_codes_exact(oracle_mod):
+@pytest.mark.parametrize("tile_n", ["128", "256"])
+def test_fp8_quant_a_codes_exact(oracle_mod, monkeypatch, tile_n):
     """The codes made inside the GEMM equal the oracle's exact ones bit for
     bit, including rows whose quotients sit exactly on rounding midpoints
     (amax = 7·2^k or 448), next to them (amax = 1, 3), bf16 subnormals, -0,
@@ -466,7 +472,8 @@ def test_fp8_quant_a_codes_exact(oracle_mod):
     M = len(rows)
     X = gi.to_bf16_bits(np.array(rows, np.float32))
     assert np.all(np.isfinite(gi.bf16_bits_to_f32(X)))
-    _say(f"fp8 quant-A codes {M}x{N}x{K}")
+    _say(f"fp8 quant-A codes {M}x{N}x{K} tile_n {tile_n}")
+    monkeypatch.setenv("GEMM_QA_TILE_N", tile_n)
     ident = np.zeros((N, K), np.uint8)
     ident[np.arange(N), np.arange(K)] = 0x38
     qI = dev_u8(ident)
