@@ -104,27 +104,44 @@ hipError_t launch_quant_rows_e4m3(const uint16_t *X, int64_t ldx, int64_t rows, 
 // Per-column quantization of a weight W [K, N] (bf16) into the rows of
 // Qt [N, K]: column j gets the factor of its own largest magnitude and the
 // codes of the row quantizer above (same quotient, same rounding), written
-// transposed so that the FP8 products read them as Bt.  Workgroup (x, y)
-// owns 64 columns and the y-th of gridDim.y ranges of 64-row blocks: 8
-// lanes cover 128 bytes of a row (8 columns each), 32 rows per pass.
-// Pass 1: the column maxima over all K (per lane over its rows, then over the
-// 32 lanes of a column chunk in LDS; every workgroup of a column strip
-// computes them, from L2 after the first).  Pass 2: per 64-row block of its
-// range, every lane quantizes 8 columns of 2 rows into an LDS tile laid out
-// [column][k], and the tile goes out as 64 rows of 64 code bytes.
-__global__ void __launch_bounds__(256) k_quant_cols_e4m3(const uint16_t *W, int64_t ldw, int64_t K, int64_t N,
-                                                         int align_w, uint8_t *Qt, int64_t ldq, int align_q,
-                                                         float *scale)
+// transposed so that the FP8 products read them as Bt.  Three passes over a
+// grid of workgroups (x, y), each owning 64 columns and the y-th of
+// gridDim.y ranges of 64-row blocks (8 lanes cover 128 bytes of a row, 8
+// columns each; 32 rows per step); the column maxima live in scale[] as
+// float bit patterns until the last pass turns them into factors.
+//  1. k_cols_amax: each workgroup's maxima over its rows (per lane, then
+//     over the 32 lanes of a column chunk in LDS), merged into scale[] by an
+//     atomic maximum on the bits (non-negative floats order like their bit
+//     patterns; scale[] was zeroed first; fmaxf drops NaN, so none enters).
+//  2. k_quant_cols_e4m3: per 64-row block of its range, every lane
+//     quantizes 8 columns of 2 rows into an LDS tile laid out [column][k],
+//     and the tile goes out as 64 rows of 64 code bytes.
+//  3. k_cols_factor: scale[n] = amax / 448.
+__global__ void __launch_bounds__(256) k_fill_u32(uint32_t *p, int64_t n)
 {
-    constexpr int TP = 68;                   // tile pitch (bytes): 64 codes + 4, rows on different banks
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+__device__ __forceinline__ void cols_block_range(int64_t K, int64_t &b0, int64_t &b1)
+{
+    const int64_t blocks = (K + 63) / 64;
+    b0 = blocks * blockIdx.y / gridDim.y;
+    b1 = blocks * (blockIdx.y + 1) / gridDim.y;
+}
+
+__global__ void __launch_bounds__(256) k_cols_amax(const uint16_t *W, int64_t ldw, int64_t K, int64_t N, int align_w,
+                                                   uint32_t *amax_bits)
+{
     __shared__ float red[32][65];
-    __shared__ float amax_s[64];
-    __shared__ __attribute__((aligned(16))) uint8_t tile[64 * TP];
     const int tid = threadIdx.x, cc = tid & 7, r0 = tid >> 3;
     const int64_t n0 = (int64_t)blockIdx.x * 64;
     const int64_t col = n0 + 8 * cc;
+    int64_t b0, b1;
+    cols_block_range(K, b0, b1);
+    const int64_t kend = b1 * 64 < K ? b1 * 64 : K;
     float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int64_t k = r0; k < K; k += 32) {
+    for (int64_t k = b0 * 64 + r0; k < kend; k += 32) {
         const u32x4 v = load_chunk8_bf16(W + k * ldw, col, N, true, align_w);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -135,22 +152,32 @@ __global__ void __launch_bounds__(256) k_quant_cols_e4m3(const uint16_t *W, int6
 #pragma unroll
     for (int i = 0; i < 8; ++i) red[r0][8 * cc + i] = m[i];
     __syncthreads();
-    if (tid < 64) {
+    if (tid < 64 && n0 + tid < N) {
         float a = 0.f;
         for (int r = 0; r < 32; ++r) a = fmaxf(a, red[r][tid]);
-        amax_s[tid] = a;
-        if (blockIdx.y == 0 && n0 + tid < N) scale[n0 + tid] = a / 448.0f;
+        if (a > 0.f)
+            __hip_atomic_fetch_max(amax_bits + n0 + tid, __float_as_uint(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __syncthreads();
+}
+
+__global__ void __launch_bounds__(256) k_quant_cols_e4m3(const uint16_t *W, int64_t ldw, int64_t K, int64_t N,
+                                                         int align_w, uint8_t *Qt, int64_t ldq, int align_q,
+                                                         const float *amax_n)
+{
+    constexpr int TP = 68;                   // tile pitch (bytes): 64 codes + 4, rows on different banks
+    __shared__ __attribute__((aligned(16))) uint8_t tile[64 * TP];
+    const int tid = threadIdx.x, cc = tid & 7, r0 = tid >> 3;
+    const int64_t n0 = (int64_t)blockIdx.x * 64;
+    const int64_t col = n0 + 8 * cc;
     float amax[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax[i] = amax_s[8 * cc + i];
+    for (int i = 0; i < 8; ++i) amax[i] = col + i < N ? amax_n[col + i] : 0.f;
     // codes by E4m3Quot, one per column (the quotient's form is chosen per
     // column)
     const E4m3Quot qz[8] = {E4m3Quot(amax[0]), E4m3Quot(amax[1]), E4m3Quot(amax[2]), E4m3Quot(amax[3]),
                             E4m3Quot(amax[4]), E4m3Quot(amax[5]), E4m3Quot(amax[6]), E4m3Quot(amax[7])};
-    const int64_t blocks = (K + 63) / 64;
-    const int64_t b0 = blocks * blockIdx.y / gridDim.y, b1 = blocks * (blockIdx.y + 1) / gridDim.y;
+    int64_t b0, b1;
+    cols_block_range(K, b0, b1);
     for (int64_t kb = b0 * 64; kb < b1 * 64; kb += 64) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -181,17 +208,33 @@ __global__ void __launch_bounds__(256) k_quant_cols_e4m3(const uint16_t *W, int6
     }
 }
 
+__global__ void __launch_bounds__(256) k_cols_factor(float *scale, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) scale[i] = scale[i] / 448.0f;
+}
+
 hipError_t launch_quant_cols_e4m3(const uint16_t *W, int64_t ldw, int64_t K, int64_t N, int align_w, uint8_t *Qt,
                                   int64_t ldq, int align_q, float *scale, hipStream_t s)
 {
     // enough workgroups for the 256 CUs: column strips times ranges of K
     const int64_t strips = (N + 63) / 64, blocks = (K + 63) / 64;
-    int64_t ky = (512 + strips - 1) / strips;
+    int64_t ky = (1024 + strips - 1) / strips;
     if (ky > blocks) ky = blocks;
     if (ky > 64) ky = 64;
     if (ky < 1) ky = 1;
-    hipLaunchKernelGGL(k_quant_cols_e4m3, dim3((unsigned)strips, (unsigned)ky), dim3(256), 0, s, W, ldw, K, N, align_w,
-                       Qt, ldq, align_q, scale);
+    const dim3 g((unsigned)strips, (unsigned)ky), g1((unsigned)((N + 255) / 256));
+    hipLaunchKernelGGL(k_fill_u32, g1, dim3(256), 0, s, (uint32_t *)scale, N);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (K > 0) {
+        hipLaunchKernelGGL(k_cols_amax, g, dim3(256), 0, s, W, ldw, K, N, align_w, (uint32_t *)scale);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(k_quant_cols_e4m3, g, dim3(256), 0, s, W, ldw, K, N, align_w, Qt, ldq, align_q,
+                           (const float *)scale);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(k_cols_factor, g1, dim3(256), 0, s, scale, N);
+    }
     return hipGetLastError();
 }
 
