@@ -47,7 +47,9 @@ def check_fp8(C, ref, K, amax_a, amax_b, out, what):
 
 @pytest.mark.parametrize("rows,cols,ldx_pad,ldq_pad", [
     (7, 300, 0, 0), (64, 4096, 0, 0), (33, 1000, 5, 3), (5, 8, 0, 1), (3, 13, 2, 0), (300, 264, 8, 8),
-    (4, 8192, 0, 0), (3, 9000, 4, 2),         # rows held in registers up to 8192; longer rows are read twice
+    (4, 8192, 0, 0), (3, 9000, 4, 2),         # rows held in registers up to 4096; longer rows are read twice
+    (2050, 1000, 3, 5), (4099, 4096, 0, 0),   # thousands of rows, ragged last workgroup
+    (2049, 4100, 2, 0),
 ])
 def test_quantize_rows_bit_exact(oracle_mod, rows, cols, ldx_pad, ldq_pad):
     """Codes and factors equal the oracle's bit for bit: normal rows of
