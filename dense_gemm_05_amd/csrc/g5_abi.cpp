@@ -922,7 +922,10 @@ int gemm_fp8_nt_quant_a(int64_t M, int64_t N, int64_t K, const uint16_t *X, int6
     const Range rb = g5::extent((uint64_t)Bt, 1, N, K > 0 ? K : 1, ldbt, 0, 1);
     const Range rc = g5::extent((uint64_t)C, 1, M, N, ldc, 0, ec);
     const Range rs{(__int128)(uint64_t)scale_x, (__int128)(uint64_t)scale_x + 4 * (__int128)M};
-    const Range rw{(__int128)(uint64_t)workspace, (__int128)(uint64_t)workspace + 4 * (__int128)M};
+    // the row maxima go after the workspace's arrival counters, which other
+    // calls sharing the workspace expect to find at zero
+    const Range rw{(__int128)(uint64_t)workspace + (__int128)g5::kCounterBytes,
+                   (__int128)(uint64_t)workspace + (__int128)g5::kCounterBytes + 4 * (__int128)M};
     if (g5::overlap(rc, rx) || g5::overlap(rc, rb) || g5::overlap(rc, rs) || g5::overlap(rs, rx) || g5::overlap(rs, rb))
         return GEMM_ERR_INVALID_ARG;
     if (scale_b && g5::overlap(rc, Range{(__int128)(uint64_t)scale_b, (__int128)(uint64_t)scale_b + 4 * (__int128)N}))
@@ -932,7 +935,7 @@ int gemm_fp8_nt_quant_a(int64_t M, int64_t N, int64_t K, const uint16_t *X, int6
         g5::row_alignment((uint64_t)Bt, ldbt, 0, 1, 1) < 16 || rx.hi - rx.lo >= ((__int128)1 << 31) ||
         rb.hi - rb.lo >= ((__int128)1 << 31))
         return GEMM_ERR_UNSUPPORTED;
-    if (!workspace || workspace_bytes < 4 * (uint64_t)M) return GEMM_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < g5::kCounterBytes + 4 * (uint64_t)M) return GEMM_ERR_WORKSPACE;
     if (((uint64_t)workspace % 256) || g5::overlap(rw, rx) || g5::overlap(rw, rb) || g5::overlap(rw, rc) ||
         g5::overlap(rw, rs))
         return GEMM_ERR_INVALID_ARG;
@@ -979,7 +982,8 @@ int gemm_fp8_nt_quant_a(int64_t M, int64_t N, int64_t K, const uint16_t *X, int6
     a.scale_a = scale_x;
     a.scale_b = scale_b;
     a.alpha = 1.0f;
-    const hipError_t e = g5::launch_fp8_quant_a(a, (float *)workspace, tile_n, a.tiles_m * a.tiles_n, (hipStream_t)stream);
+    const hipError_t e = g5::launch_fp8_quant_a(a, (float *)((char *)workspace + g5::kCounterBytes), tile_n,
+                                                a.tiles_m * a.tiles_n, (hipStream_t)stream);
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 

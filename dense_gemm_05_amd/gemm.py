@@ -448,8 +448,9 @@ def gemm_fp8_nt_quant_a(X, Bt, scale_b, C=None, scale_x=None, out_dtype=torch.bf
     """The FP8 product with X [M, K] (bfloat16) quantized inside the GEMM
     (gemm_fp8_nt_quant_a): returns (C [M, N], scale_x float32 [M], X's row
     factors).  Bt [N, K] codes with factors scale_b [N] (or None).  The
-    workspace (a Workspace or a uint8 tensor) holds M floats; a Workspace is
-    created for the call when None is given."""
+    workspace (a Workspace or a uint8 tensor) holds M floats after its first
+    64 KiB (the arrival counters of gemm_run calls, left untouched); a
+    Workspace is created for the call when None is given."""
     if X.dtype != torch.bfloat16 or X.dim() != 2:
         raise TypeError("gemm_fp8_nt_quant_a takes a 2-D bfloat16 X")
     Bt = _codes(Bt)
@@ -474,7 +475,7 @@ def gemm_fp8_nt_quant_a(X, Bt, scale_b, C=None, scale_x=None, out_dtype=torch.bf
     if isinstance(workspace, Workspace):
         if workspace.device != dev:
             raise ValueError("the workspace must be on the operands' GPU")
-        buf = workspace.reserve(4 * M)
+        buf = workspace.reserve(65536 + 4 * M)
     else:
         buf = workspace
         if not isinstance(buf, torch.Tensor) or buf.dtype != torch.uint8 or buf.dim() != 1:

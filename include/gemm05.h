@@ -218,15 +218,18 @@ int gemm_fp8_nt(int64_t M, int64_t N, int64_t K,
  * quantizing it first: X [M, K] bf16 rows (row stride ldx elements), Bt
  * [N, K] E4M3FN codes with factors scale_b (or NULL).  A first pass reads X
  * once for each row's largest magnitude (into the caller's workspace, M
- * floats) and writes the row's factor amax/448 to scale_x[M]; the product
+ * floats after its first 64 KiB) and writes the row's factor amax/448 to
+ * scale_x[M]; the product
  * then reads X as bf16 in every output tile (128 rows by 128 or 256
  * columns) and converts it to codes on the way into local memory, by the
  * rule of gemm_fp8_quantize_rows, so C equals gemm_fp8_nt on the codes
  * gemm_fp8_quantize_rows(X) gives, computed with 128x128 tiles and no K
  * split (bit for bit).  C bf16 or float by c_type.  Requires
  * K % 64 == 0 and 16-byte aligned rows of X and Bt (else
- * GEMM_ERR_UNSUPPORTED); workspace: at least 4 M bytes, 256-byte aligned
- * (else GEMM_ERR_WORKSPACE, or GEMM_ERR_INVALID_ARG for the alignment);
+ * GEMM_ERR_UNSUPPORTED); workspace: at least 65536 + 4 M bytes, 256-byte
+ * aligned (else GEMM_ERR_WORKSPACE, or GEMM_ERR_INVALID_ARG for the
+ * alignment); its first 64 KiB are left untouched, so the same workspace
+ * serves gemm_run calls, whose arrival counters live there;
  * GEMM_ERR_INVALID_ARG for negative sizes, short strides, NULL or unaligned
  * pointers and overlapping buffers.  Nothing is allocated. */
 int gemm_fp8_nt_quant_a(int64_t M, int64_t N, int64_t K,

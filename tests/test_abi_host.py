@@ -726,18 +726,20 @@ def test_fp8_batched_affine_and_cols_arguments(L):
 
 def test_fp8_quant_a_arguments(L):
     """The FP8 product with X quantized inside the GEMM validates before
-    touching the GPU: whole 64-deep stages and 16-byte rows, a workspace of M
-    floats, 256-byte aligned, and no overlaps."""
+    touching the GPU: whole 64-deep stages and 16-byte rows, a workspace of
+    64 KiB (counters, untouched) plus M floats, 256-byte aligned, and no
+    overlaps."""
     M, N, K = 64, 128, 256
     W = P + (3 << 34)
-    def call(K=K, ldx=K, x=A_ADDR, ws=W, wsb=4 * M, sx=P + (4 << 34), c=C_ADDR):
+    def call(K=K, ldx=K, x=A_ADDR, ws=W, wsb=65536 + 4 * M, sx=P + (4 << 34), c=C_ADDR):
         return L.gemm_fp8_nt_quant_a(M, N, K, x, ldx, sx, B_ADDR, K, None, c, N, 0, ws, wsb, None)
     assert call(K=200, ldx=200) == g5.GEMM_ERR_UNSUPPORTED           # K % 64
     assert call(ldx=260) == g5.GEMM_ERR_UNSUPPORTED                  # X rows 8-byte aligned
-    assert call(wsb=4 * M - 4) == g5.GEMM_ERR_WORKSPACE
+    assert call(wsb=65536 + 4 * M - 4) == g5.GEMM_ERR_WORKSPACE
+    assert call(wsb=4 * M) == g5.GEMM_ERR_WORKSPACE                  # no room past the counters
     assert call(ws=None, wsb=0) == g5.GEMM_ERR_WORKSPACE
     assert call(ws=W + 64) == g5.GEMM_ERR_INVALID_ARG                # workspace not 256-byte aligned
     assert call(ldx=100) == g5.GEMM_ERR_INVALID_ARG                  # ldx < K
     assert call(sx=C_ADDR + 16) == g5.GEMM_ERR_INVALID_ARG           # factors inside C
-    assert call(ws=C_ADDR) == g5.GEMM_ERR_INVALID_ARG                # workspace inside C
+    assert call(ws=C_ADDR - 65536) == g5.GEMM_ERR_INVALID_ARG        # the maxima would land in C
     assert L.gemm_fp8_nt_quant_a(0, N, K, None, K, None, None, K, None, None, N, 0, None, 0, None) == g5.GEMM_OK

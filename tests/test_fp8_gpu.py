@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import gemm_inputs as gi
-from _gpu_helpers import dev_bf16, host_values, ws
+from _gpu_helpers import check_bf16, dev_bf16, host_values, ws
 
 import dense_gemm_05_amd as g5
 
@@ -418,7 +418,7 @@ def test_fp8_quant_a_bf16_out_and_repeat():
     X = gi.to_bf16_bits(x)
     dX = dev_bf16(X)
     qW, sW = g5.gemm_fp8_quantize_rows(dev_bf16(gi.to_bf16_bits(gi.normal(g, (N, K), 0.125))))
-    wsb = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    wsb = torch.zeros(65536 + 4096, dtype=torch.uint8, device="cuda")
     C1, s1 = g5.gemm_fp8_nt_quant_a(dX, qW, sW, workspace=wsb)
     C2, s2 = g5.gemm_fp8_nt_quant_a(dX, qW, sW, workspace=wsb)
     assert torch.equal(C1.view(torch.int16), C2.view(torch.int16)) and torch.equal(s1, s2)
@@ -457,14 +457,14 @@ def test_fp8_quant_a_codes_exact(oracle_mod, monkeypatch, tile_n):
     rows = []
     for amax in amaxes:
         for variant in range(3):
-            x = np.empty(K, np.float64)
+            x = np.zeros(K, np.float64)
             x[0] = amax if variant != 1 else -amax
             t = mids * amax / 448.0
             x[1:1 + len(t)] = t * np.where(g.random(len(t)) < 0.5, -1.0, 1.0)
             rest = 1 + len(t)
             if variant == 2:                                   # neighbours of the midpoints
-                k = K - rest
-                x[rest:] = np.nextafter(x[1:1 + k].astype(np.float32), np.float32(np.inf)).astype(np.float64) * 1.003
+                near = np.resize(x[1:rest], K - rest)             # the midpoint quotients, cycled
+                x[rest:] = np.nextafter(near.astype(np.float32), np.float32(np.inf)).astype(np.float64) * 1.003
             else:
                 x[rest:] = g.uniform(-amax, amax, K - rest)
             x[rest] = -0.0
@@ -488,3 +488,22 @@ def test_fp8_quant_a_codes_exact(oracle_mod, monkeypatch, tile_n):
     bad = np.argwhere(got.view(np.int32) != expect.view(np.int32))
     bad = [tuple(b) for b in bad if not (got[tuple(b)] == 0 and expect[tuple(b)] == 0)]
     assert not bad, f"{len(bad)} codes differ, first at {bad[:4]} (row amax {[amaxes[b[0] // 3] for b in bad[:4]]})"
+
+
+def test_fp8_quant_a_leaves_workspace_counters_zero(oracle_mod):
+    """The row maxima go past the workspace's first 64 KiB, so a Workspace
+    shared with gemm_run calls keeps its arrival counters at zero: a K-split
+    small-M product right after a quantized-inside call on the same
+    workspace is still correct."""
+    w = g5.Workspace()
+    X = torch.randn(300, 256, device="cuda").to(torch.bfloat16)
+    qW, sW = g5.gemm_fp8_quantize_rows((torch.randn(512, 256, device="cuda") * 0.125).to(torch.bfloat16))
+    g5.gemm_fp8_nt_quant_a(X, qW, sW, workspace=w)
+    torch.cuda.synchronize()
+    assert int(w.buf[:65536].count_nonzero()) == 0, "counters written"
+    M, N, K = 1, 12288, 4096
+    A, B = gi.small_case("bf16", M, N, K, seed=31, scale_b=0.125)
+    st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
+    assert st == 0 and plan.name == b"decode_splitk", plan.name
+    C = g5.gemm_bf16(dev_bf16(A), dev_bf16(B), workspace=w)
+    check_bf16(host_values(C), oracle_mod.gemm_bf16(A, B), K, "split small-M after quant-A")
