@@ -438,15 +438,23 @@ def main():
         fused = [(lambda i=i: g5.gemm_bf16_swiglu(dX[i], dW[i], dZ[i], workspace=ws)) for i in range(R)]
         plain = [(lambda i=i: (g5.gemm_bf16(dX[i], dW[i][:, :N], dG[i], workspace=ws), g5.gemm_bf16(dX[i], dW[i][:, N:], dU[i], workspace=ws)))
                  for i in range(R)]
+        # The unfused program: the two projections, then Z = bf16(bf16(SiLU(g)) * u)
+        # as element-wise passes over the written g and u (torch's bf16 silu
+        # and multiply, the same roundings as the fused epilogue).
+        unfused = [(lambda i=i: (plain[i](), torch.mul(torch.nn.functional.silu(dG[i]), dU[i], out=dZ[i])))
+                   for i in range(R)]
         ms = timed(fused, 30, 5, label="swiglu_ffn_bf16_1024x2x12288x4096")
         ms_plain = timed(plain, 30, 5, label="swiglu_ffn_two_plain_projections")
+        ms_unfused = timed(unfused, 30, 5, label="swiglu_ffn_unfused_program")
         flops = 2.0 * 2 * M * N * K
         tf = flops / (ms * 1e-3) / 1e12
         log(f"swiglu FFN 1024x(2x12288)x4096: fused {ms * 1e3:.2f} us ({tf:.1f} TFLOPS); "
-            f"two plain projections {ms_plain * 1e3:.2f} us")
+            f"two plain projections {ms_plain * 1e3:.2f} us; unfused program (projections + element-wise "
+            f"SiLU and product) {ms_unfused * 1e3:.2f} us")
         workloads.append({"name": "swiglu_ffn_bf16_1024x2x12288x4096", "us": round(ms * 1e3, 3),
                           "tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                          "two_plain_projections_us": round(ms_plain * 1e3, 3), "rotations": R})
+                          "two_plain_projections_us": round(ms_plain * 1e3, 3),
+                          "unfused_program_us": round(ms_unfused * 1e3, 3), "rotations": R})
         del dX, dW, dZ, dG, dU
 
     # ------------------------------------------------------------ column shard (split K)
