@@ -171,8 +171,10 @@ int gemm_bf16_tn_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
  * scale[rows] (float, 4-byte aligned): with amax the row's largest
  * magnitude, the code of x is the E4M3FN value nearest to the exact
  * quotient x * 448 / amax (ties to the even mantissa; Example 5-7), reached
- * with one correctly rounded binary32 division of x * 448 by amax, and
- * scale = amax / 448 rounded to binary32.  A row of zeros gives zero codes
+ * through a binary32 quotient of x * 448 by amax whose code is that of the
+ * correctly rounded division (a reciprocal and one residual step for amax
+ * in [2^-126, 2^118], the division itself otherwise), and scale =
+ * amax / 448 rounded to binary32.  A row of zeros gives zero codes
  * (signed) and factor 0.  Inputs are expected finite (a NaN element becomes
  * a NaN code).
  * GEMM_ERR_INVALID_ARG: negative sizes, ldx or ldq < cols, NULL or
@@ -188,8 +190,9 @@ int gemm_fp8_quantize_rows(int64_t rows, int64_t cols,
  * gemm_fp8_quantize_rows quantizes a row -- codes nearest to
  * W[k][j] * 448 / amax_j, scale[j] = amax_j / 448 -- and its codes are
  * written as row j of Qt [N, K] (row stride ldq >= K bytes), the Bt operand
- * of the FP8 products.  Caller-owned device memory, nothing else touched;
- * deterministic.  GEMM_ERR_INVALID_ARG: negative sizes, ldw < N or
+ * of the FP8 products.  Caller-owned device memory, nothing else touched
+ * (scale[] holds the column maxima until the call's last pass turns them
+ * into factors); deterministic.  GEMM_ERR_INVALID_ARG: negative sizes, ldw < N or
  * ldq < K, NULL or unaligned pointers (W 2-byte, scale 4-byte), or
  * overlapping W, Qt and scale. */
 int gemm_fp8_quantize_cols(int64_t K, int64_t N,
