@@ -606,6 +606,16 @@ bool decode_split_direct(const Problem &p, const Plan &pl)
     return pl.config == CFG_DECODE_SPLIT && pl.ks == 1 && p.op != GEMM_OP_BF16_SWIGLU;
 }
 
+// Two slices whose outputs fit the counter region as exchange slots (one
+// 32-bit word per output, zero between calls): the split small-M path pairs
+// the slices' partial sums by atomic exchange instead of counters and a
+// partial-sum buffer (the same sums, in the same order).
+bool decode_split_pair(const Problem &p, const Plan &pl)
+{
+    return pl.config == CFG_DECODE_SPLIT && pl.ks == 2 && p.op != GEMM_OP_BF16_SWIGLU &&
+           (uint64_t)p.batch * p.M * p.N * 4 <= kCounterBytes;
+}
+
 // Partial sums of the split small-M path: one slot of 16 x 128 FP32 per
 // (batch entry, strip, K slice); of a K-split tiled call: ksplit FP32 tiles
 // per output tile.  The arrival counters (one per strip or tile) are in the
@@ -613,7 +623,7 @@ bool decode_split_direct(const Problem &p, const Plan &pl)
 size_t partial_bytes(const Problem &p, const Plan &pl)
 {
     if (pl.config == CFG_DECODE_SPLIT)
-        return decode_split_direct(p, pl)
+        return decode_split_direct(p, pl) || decode_split_pair(p, pl)
                    ? 0
                    : (size_t)p.batch * pl.tiles_n * pl.ks * (p.op == GEMM_OP_BF16_SWIGLU ? 2 : 1) * 16 * 128 *
                          sizeof(float);
@@ -625,16 +635,18 @@ size_t partial_bytes(const Problem &p, const Plan &pl)
 // Workspace layout (byte offsets from its start, each region 256-byte
 // aligned): [0, kCounterBytes) arrival counters, then the partial sums,
 // then the realigned copy of A, then that of Bt.  A plan that needs none of
-// them needs no workspace (0 bytes).
+// them and no counters (or exchange slots) needs no workspace (0 bytes).
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 struct WsLayout {
     size_t part = 0, rows_a = 0, rows_b = 0, total = 0;
 };
+int64_t counters_used(const Problem &p, const Plan &pl);
+
 WsLayout ws_layout(const Problem &p, const Plan &pl)
 {
     WsLayout L;
     const size_t pb = partial_bytes(p, pl), ab = realign_bytes(p, pl), bb = realign_b_bytes(p, pl);
-    if (pb == 0 && ab == 0 && bb == 0) return L;
+    if (pb == 0 && ab == 0 && bb == 0 && counters_used(p, pl) == 0) return L;
     L.part = kCounterBytes;
     L.rows_a = L.part + round256(pb);
     L.rows_b = L.rows_a + round256(ab);
@@ -700,10 +712,12 @@ bool log_enabled()
     return v == 1;
 }
 
-// Arrival counters a plan uses (at the start of the workspace).
+// Arrival counters, or exchange slots, a plan uses (32-bit words at the
+// start of the workspace, zero between calls).
 int64_t counters_used(const Problem &p, const Plan &pl)
 {
-    if (pl.config == CFG_DECODE_SPLIT) return decode_split_direct(p, pl) ? 0 : p.batch * pl.tiles_n;
+    if (pl.config == CFG_DECODE_SPLIT)
+        return decode_split_direct(p, pl) ? 0 : decode_split_pair(p, pl) ? p.batch * p.M * p.N : p.batch * pl.tiles_n;
     if (pl.ksplit > 1 || pl.streamk) return p.batch * pl.tiles_m * pl.tiles_n;
     return 0;
 }
@@ -811,7 +825,9 @@ int run(const Problem &p, void *stream, void *ws = nullptr, size_t ws_bytes = 0)
         a.align_a = 16;
     }
     if (pl.config == CFG_DECODE_SPLIT) {
-        const hipError_t e = launch_decode_split(a, (float *)(wsb + L.part), counters, pl.ks, (hipStream_t)stream);
+        const bool pair = decode_split_pair(p, pl);
+        const hipError_t e = launch_decode_split(a, pair ? nullptr : (float *)(wsb + L.part), counters, pl.ks,
+                                                 pair ? counters : nullptr, (hipStream_t)stream);
         return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
     }
     const hipError_t e =

@@ -628,8 +628,17 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
 //    slice order, and stores bf16(bf16(SiLU(g)) * u).
 // Requires N % 128 == 0, K % 32 == 0, 16-byte aligned rows of X and W.
 // DB: double-buffer the W rows of two steps in registers.
+//  * Two slices (pair != NULL): no counter.  Each output has a 32-bit slot
+//    in pair[] (zero on entry; [batch][M][N]); a workgroup exchanges its
+//    partial, stored as its bit pattern with every bit flipped, into the
+//    slot (a device-scope atomic exchange).  The one that gets a nonzero
+//    value back holds both partials, adds them in slice order -- (0 + p0) +
+//    p1, the sum the counter path computes -- stores the output and puts
+//    the slot back to zero.  One atomic round trip per output instead of the
+//    store-wait-count-reload sequence; the value read is the atomic's own
+//    result, so no ordering beyond the atomic is needed.
 template <int NW, bool DB>
-__global__ void __launch_bounds__(NW * 64, 1) k_decode_sk(GemmArgs p, float *ws, unsigned *cnt, int KS)
+__global__ void __launch_bounds__(NW * 64, 1) k_decode_sk(GemmArgs p, float *ws, unsigned *cnt, int KS, unsigned *pair)
 {
     constexpr int NC = 128;
     const int tid = threadIdx.x;
@@ -734,10 +743,24 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode_sk(GemmArgs p, float *ws,
         float sum = 0.f;
         for (int w2 = 0; w2 < NW; ++w2) sum += red[(w2 * 64 + L) * RS + j];
         const int n = 32 * g2 + j;
-        if (direct) store_out(p, bidx, m, n0 + n, sum);
-        else __hip_atomic_store(part + m * NC + n, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (direct) {
+            store_out(p, bidx, m, n0 + n, sum);
+        } else if (pair) {
+            unsigned *slot = pair + (bidx * M + m) * p.N + n0 + n;
+            unsigned mine = ~__float_as_uint(sum);
+            if (mine == 0u) mine = 1u;           // (a NaN pattern no bf16 product produces)
+            const unsigned other = __hip_atomic_exchange(slot, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (other != 0u) {
+                const float o = __uint_as_float(~other);
+                const float p0 = slice == 0 ? sum : o, p1 = slice == 0 ? o : sum;
+                store_out(p, bidx, m, n0 + n, (0.f + p0) + p1);
+                __hip_atomic_store(slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        } else {
+            __hip_atomic_store(part + m * NC + n, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
-    if (direct) return;
+    if (direct || pair) return;
     // Publish this slice; the last of the nmem workgroups of the strip sums.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -763,13 +786,14 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode_sk(GemmArgs p, float *ws,
     if (tid == 0) __hip_atomic_store(c_strip, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-hipError_t launch_decode_split(const GemmArgs &a, float *ws, unsigned *cnt, int ks, hipStream_t s)
+hipError_t launch_decode_split(const GemmArgs &a, float *ws, unsigned *cnt, int ks, unsigned *pair, hipStream_t s)
 {
+    if (pair && (ks != 2 || a.epi == EPI_SWIGLU)) return hipErrorInvalidValue;
     // 16 waves, one 32-row step in registers at a time (two would spill at
     // 16 waves per CU; the waves themselves keep enough loads in flight).
     const int64_t groups = a.epi == EPI_SWIGLU ? 2 * a.tiles_n : a.tiles_n;
     hipLaunchKernelGGL((k_decode_sk<16, false>), dim3((unsigned)(groups * ks), (unsigned)a.batch), dim3(16 * 64), 0,
-                       s, a, ws, cnt, ks);
+                       s, a, ws, cnt, ks, pair);
     return hipGetLastError();
 }
 

@@ -293,6 +293,30 @@ def test_decode_batch_invariance():
         assert np.array_equal(CM, C16[:M]), f"M={M} rows differ from M=16"
 
 
+def test_decode_exchange_slots_reset(oracle_mod):
+    """M = 1 with a workspace pairs the two K slices through exchange slots in
+    the counter region: back-to-back calls with different rows on one
+    workspace each match the oracle (a slot left set would mix two calls),
+    the region is all zero afterwards, and a repeat gives the same bits."""
+    N, K = 12288, 4096
+    st, plan = g5.plan_query(g5.GEMM_OP_BF16, 1, N, K)
+    assert st == 0 and plan.name == b"decode_splitk" and plan.workspace_bytes == 65536
+    w = g5.Workspace()
+    _, W = gi.decode_inputs(1)
+    dW = dev_bf16(W)
+    g = np.random.default_rng(gi.SEED_BASE + 9100)
+    outs = []
+    for i in range(3):
+        X = gi.to_bf16_bits(gi.normal(g, (1, K)) * np.float32(2.0 ** (i - 1)))
+        C = g5.gemm_bf16(dev_bf16(X), dW, workspace=w)
+        check_bf16(host_values(C), oracle_mod.gemm_bf16(X, W), K, f"exchange call {i}")
+        outs.append((X, host_bits(C)))
+    torch.cuda.synchronize()
+    assert int(w.buf[:65536].count_nonzero()) == 0, "exchange slots left set"
+    X, bits = outs[0]
+    assert np.array_equal(host_bits(g5.gemm_bf16(dev_bf16(X), dW, workspace=w)), bits)
+
+
 @pytest.mark.parametrize("with_ws", [True, False])
 def test_batched_attention_scores(oracle_mod, with_ws):
     """32 x Q[1024,128] . K^T[128,1024] -> f32: every element of every entry."""
