@@ -4,6 +4,7 @@ accumulation), single and batched, with fused SiLU, SwiGLU and affine
 behind the C ABI of include/gemm05.h."""
 from ._lib import (  # noqa: F401
     GEMM_OK, GEMM_ERR_INVALID_ARG, GEMM_ERR_UNSUPPORTED, GEMM_ERR_LAUNCH, GEMM_ERR_NO_DEVICE, GEMM_ERR_WORKSPACE,
+    GEMM_WORKSPACE_COUNTER_BYTES,
     GEMM_OUT_BF16, GEMM_OUT_F32, GEMM_OP_SGEMM, GEMM_OP_BF16, GEMM_OP_BF16_SILU, GEMM_OP_BF16_SWIGLU, GEMM_OP_BF16_NT, GEMM_OP_FP8_NT,
     GEMM_OP_BF16_AFFINE, GEMM_OP_BF16_TN, GEMM_OP_BF16_NT_AFFINE,
     GEMM_OP_BF16_TN_AFFINE, GEMM_OP_FP8_NT_AFFINE,

@@ -16,6 +16,9 @@ GEMM_ERR_LAUNCH = -3
 GEMM_ERR_NO_DEVICE = -4
 GEMM_ERR_WORKSPACE = -5
 
+# GEMM_WORKSPACE_COUNTER_BYTES: the zeroed counter region at the start of a workspace
+GEMM_WORKSPACE_COUNTER_BYTES = 1 << 20
+
 GEMM_OUT_BF16 = 0
 GEMM_OUT_F32 = 1
 

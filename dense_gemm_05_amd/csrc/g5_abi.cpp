@@ -374,8 +374,9 @@ bool split_ok(const Problem &p, int S)
 int split_kt_per(const Problem &p, int S) { return (int)((p.K / stage_k(p)) / S); }
 
 // Counters live in the first kCounterBytes of a workspace: a split call
-// needs one per output tile (tiled kernels) or per strip (small-M path).
-constexpr size_t kCounterBytes = 64 * 1024;
+// needs one per output tile (tiled kernels) or per strip (small-M path), or
+// one exchange slot per output (small-M path with two slices).
+constexpr size_t kCounterBytes = GEMM_WORKSPACE_COUNTER_BYTES;
 constexpr int64_t kMaxCounters = (int64_t)(kCounterBytes / sizeof(unsigned));
 
 // The plan of a call.  `ws`: a caller workspace will be passed, so the

@@ -17,7 +17,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import GEMM_ERR_WORKSPACE, GemmError, GemmPlan, lib
+from ._lib import GEMM_ERR_WORKSPACE, GEMM_WORKSPACE_COUNTER_BYTES, GemmError, GemmPlan, lib
 
 __all__ = ["gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm_bf16_nt_batched",
            "gemm_bf16_tn", "gemm_bf16_tn_batched",
@@ -77,8 +77,9 @@ def _launch(fn, dev, *args):
 class Workspace:
     """Caller-owned scratch memory for the workspace paths of gemm_run.
 
-    Device memory from torch (zero-filled when allocated: the first 64 KiB
-    are arrival counters that every call leaves at zero).  ``reserve(n)``
+    Device memory from torch (zero-filled when allocated: the first
+    GEMM_WORKSPACE_COUNTER_BYTES hold arrival counters and exchange slots
+    that every call leaves at zero).  ``reserve(n)``
     replaces the buffer with a larger one when a call needs more; the old
     one is released to torch's stream-ordered allocator.  One Workspace
     serves calls on one stream (calls that may overlap in time need separate
@@ -449,7 +450,8 @@ def gemm_fp8_nt_quant_a(X, Bt, scale_b, C=None, scale_x=None, out_dtype=torch.bf
     (gemm_fp8_nt_quant_a): returns (C [M, N], scale_x float32 [M], X's row
     factors).  Bt [N, K] codes with factors scale_b [N] (or None).  The
     workspace (a Workspace or a uint8 tensor) holds M floats after its first
-    64 KiB (the arrival counters of gemm_run calls, left untouched); a
+    GEMM_WORKSPACE_COUNTER_BYTES (the counter region of gemm_run calls,
+    left untouched); a
     Workspace is created for the call when None is given."""
     if X.dtype != torch.bfloat16 or X.dim() != 2:
         raise TypeError("gemm_fp8_nt_quant_a takes a 2-D bfloat16 X")
@@ -475,7 +477,7 @@ def gemm_fp8_nt_quant_a(X, Bt, scale_b, C=None, scale_x=None, out_dtype=torch.bf
     if isinstance(workspace, Workspace):
         if workspace.device != dev:
             raise ValueError("the workspace must be on the operands' GPU")
-        buf = workspace.reserve(65536 + 4 * M)
+        buf = workspace.reserve(GEMM_WORKSPACE_COUNTER_BYTES + 4 * M)
     else:
         buf = workspace
         if not isinstance(buf, torch.Tensor) or buf.dtype != torch.uint8 or buf.dim() != 1:

@@ -221,7 +221,8 @@ int gemm_fp8_nt(int64_t M, int64_t N, int64_t K,
  * quantizing it first: X [M, K] bf16 rows (row stride ldx elements), Bt
  * [N, K] E4M3FN codes with factors scale_b (or NULL).  A first pass reads X
  * once for each row's largest magnitude (into the caller's workspace, M
- * floats after its first 64 KiB) and writes the row's factor amax/448 to
+ * floats after its first GEMM_WORKSPACE_COUNTER_BYTES) and writes the
+ * row's factor amax/448 to
  * scale_x[M]; the product
  * then reads X as bf16 in every output tile (128 rows by 128 or 256
  * columns) and converts it to codes on the way into local memory, by the
@@ -229,10 +230,10 @@ int gemm_fp8_nt(int64_t M, int64_t N, int64_t K,
  * gemm_fp8_quantize_rows(X) gives, computed with 128x128 tiles and no K
  * split (bit for bit).  C bf16 or float by c_type.  Requires
  * K % 64 == 0 and 16-byte aligned rows of X and Bt (else
- * GEMM_ERR_UNSUPPORTED); workspace: at least 65536 + 4 M bytes, 256-byte
- * aligned (else GEMM_ERR_WORKSPACE, or GEMM_ERR_INVALID_ARG for the
- * alignment); its first 64 KiB are left untouched, so the same workspace
- * serves gemm_run calls, whose arrival counters live there;
+ * GEMM_ERR_UNSUPPORTED); workspace: at least GEMM_WORKSPACE_COUNTER_BYTES +
+ * 4 M bytes, 256-byte aligned (else GEMM_ERR_WORKSPACE, or
+ * GEMM_ERR_INVALID_ARG for the alignment); its counter region is left
+ * untouched, so the same workspace serves gemm_run calls;
  * GEMM_ERR_INVALID_ARG for negative sizes, short strides, NULL or unaligned
  * pointers and overlapping buffers.  Nothing is allocated. */
 int gemm_fp8_nt_quant_a(int64_t M, int64_t N, int64_t K,
@@ -383,6 +384,10 @@ int gemm_bf16_tn_affine(int64_t batch, int64_t M, int64_t N, int64_t K,
                         void *C, int64_t ldc, int64_t strideC, int c_type,
                         void *stream);
 
+/* Bytes at the start of a gemm_run workspace that hold arrival counters and
+ * exchange slots (zero between calls). */
+#define GEMM_WORKSPACE_COUNTER_BYTES (1u << 20)
+
 /* ---- one entry point for every operation, with a caller workspace --------
  *
  * gemm_run performs the call that the named entry point of `op` (a
@@ -391,9 +396,10 @@ int gemm_bf16_tn_affine(int64_t batch, int64_t M, int64_t N, int64_t K,
  * current device, owned by the caller, 256-byte aligned, holding at least
  * what gemm_workspace_size reports for the same call (GEMM_ERR_WORKSPACE
  * otherwise; NULL runs the call without scratch, exactly as the named entry
- * point).  Its first 64 KiB are arrival counters: they must be zero before a
- * workspace is first used (e.g. zero-filled at allocation) and every call
- * leaves them zero when it completes; the rest needs no initial value.
+ * point).  Its first GEMM_WORKSPACE_COUNTER_BYTES (1 MiB) hold arrival
+ * counters and exchange slots: they must be zero before a workspace is
+ * first used (e.g. zero-filled at allocation) and every call leaves them
+ * zero when it completes; the rest needs no initial value.
  * A workspace serves one call at a time: calls that may overlap in time
  * (on different streams) need different workspaces; calls on one stream
  * may share one.
@@ -476,7 +482,7 @@ typedef struct {
     double model_bytes;/* traffic model of "Operator & Runtime" §5.2.2 for the chosen tile */
     char name[48];     /* configuration name, as accepted by GEMM_FORCE_CONFIG */
     int64_t workspace_bytes; /* workspace the planned call needs (gemm_run):
-                                64 KiB of arrival counters plus the partial
+                                the 1 MiB counter region plus the partial
                                 sums of the split small-M path or of a
                                 K-split tiled call and the realigned row
                                 copies of A and Bt, each rounded up to 256

@@ -41,12 +41,15 @@ def test_status_strings(L):
     assert "unknown" in g5.status_string(7)
 
 
+CR = g5.GEMM_WORKSPACE_COUNTER_BYTES   # the workspace's counter region
+
+
 def ws_bytes(part=0, rows_a=0, rows_b=0):
-    """Workspace a plan needs (include/gemm05.h, gemm_run): 64 KiB of arrival
+    """Workspace a plan needs (include/gemm05.h, gemm_run): the counter region
     counters, then the partial sums and the realigned row copies, each
     rounded up to 256 bytes; nothing when none of them is needed."""
     r = lambda b: (b + 255) // 256 * 256
-    return 0 if part == rows_a == rows_b == 0 else 65536 + r(part) + r(rows_a) + r(rows_b)
+    return 0 if part == rows_a == rows_b == 0 else CR + r(part) + r(rows_a) + r(rows_b)
 
 
 P = 0x7F0000000000  # fake, well-aligned, non-overlapping addresses (never dereferenced)
@@ -134,12 +137,11 @@ def test_selector_choices_for_the_workloads(L):
     # strips with K split in 2 (96 x 2 workgroups) when N % 128 == 0 and the
     # rows are 16-byte aligned; else whole-K strips of 64 columns.  M = 1:
     # the two slices meet in exchange slots, one word per output inside the
-    # 64 KiB counter region (no partial-sum buffer); M = 4 and 16: partial
-    # sums and counters
+    # counter region (no partial-sum buffer) for every M <= 16 here
     for M in (1, 4, 16):
         st, p = g5.plan_query(g5.GEMM_OP_BF16, M, 12288, 4096)
         assert st == 0 and p.family == 4 and p.name == b"decode_splitk" and p.grid == 96 * 2
-        want = 65536 if M * 12288 * 4 <= 65536 else ws_bytes(96 * 2 * 16 * 128 * 4)
+        want = CR if M * 12288 * 4 <= CR else ws_bytes(96 * 2 * 16 * 128 * 4)
         assert p.variant == 1 and p.workspace_bytes == want, (M, p.workspace_bytes)
     st, p = g5.plan_query(g5.GEMM_OP_BF16, 4, 12290, 4096)
     assert st == 0 and p.name == b"decode_64" and p.variant == 0 and p.workspace_bytes == 0
@@ -286,19 +288,19 @@ def test_split_small_m_workspace_covers_every_slot(M, N, K, batch):
     writes partial-sum slot (b*strips + strip)*KS + slice of 16 x 128 floats
     and counter b*strips + strip; the workspace the plan reports must hold
     the largest of each, for the KS the launch uses (grid = strips*KS*batch).
-    Two slices whose batch x M x N outputs fit the 64 KiB counter region
+    Two slices whose batch x M x N outputs fit the counter region
     meet in one exchange word per output there instead."""
     st, p = g5.plan_query(g5.GEMM_OP_BF16, M, N, K, batch=batch)
     assert st == 0 and p.name == b"decode_splitk", p.name
     strips = N // 128
     ks = p.grid // (strips * batch)
     assert p.grid == strips * ks * batch and 2 <= ks <= 8
-    if ks == 2 and batch * M * N * 4 <= 65536:
-        assert p.workspace_bytes == 65536
+    if ks == 2 and batch * M * N * 4 <= CR:
+        assert p.workspace_bytes == CR
         return
     top_slot = ((batch - 1) * strips + strips - 1) * ks + ks - 1
     top_cnt = (batch - 1) * strips + strips - 1
-    assert (top_cnt + 1) * 4 <= 65536 and 65536 + (top_slot + 1) * 16 * 128 * 4 <= p.workspace_bytes
+    assert (top_cnt + 1) * 4 <= CR and CR + (top_slot + 1) * 16 * 128 * 4 <= p.workspace_bytes
 
 
 def call_fused(L, op, M, N, K, a=A_ADDR, lda=None, b=B_ADDR, ldb=None, c=C_ADDR, ldc=None):
@@ -358,14 +360,15 @@ def test_fused_small_m_plans(L):
     """M <= 16: SiLU and SwiGLU run on the small-M kernels.  With a workspace
     the K-split path (SwiGLU: separate workgroups for a strip's gate and up
     columns, 2 x 96 strips for N = 12288; SiLU: 96 strips x 2 slices), its
-    partial sums in the workspace; without one the whole-K 64-column kernel;
-    K % 32 != 0 only the latter."""
+    partial sums in the workspace (SiLU with two slices: exchange slots in
+    the counter region, no partial sums); without one the whole-K
+    64-column kernel; K % 32 != 0 only the latter."""
     st, p = g5.plan_query(g5.GEMM_OP_BF16_SWIGLU, 1, 12288, 4096)
     assert st == 0 and p.name == b"decode_splitk" and p.grid == 192
     assert p.workspace_bytes == ws_bytes(96 * 2 * 16 * 128 * 4)
     st, p = g5.plan_query(g5.GEMM_OP_BF16_SILU, 16, 12288, 4096)
     assert st == 0 and p.name == b"decode_splitk" and p.grid == 192
-    assert p.workspace_bytes == ws_bytes(96 * 2 * 16 * 128 * 4)
+    assert p.workspace_bytes == CR
     for op in (g5.GEMM_OP_BF16_SILU, g5.GEMM_OP_BF16_SWIGLU):
         st, p = g5.plan_query(op, 1, 12288, 4096, with_workspace=False)
         assert st == 0 and p.name == b"decode_64" and p.grid == 192 and p.workspace_bytes == 0
@@ -679,7 +682,7 @@ def test_run_rejects_small_or_unaligned_workspace(L):
     M, N, K = 1, 12288, 4096
     st, p = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
     need = p.workspace_bytes
-    assert need >= 65536
+    assert need >= CR
     WS = P + (3 << 34)
     run = lambda ws, n: L.gemm_run(g5.GEMM_OP_BF16, 1, M, N, K, A_ADDR, K, 0, B_ADDR, N, 0, C_ADDR, N, 0, 0,
                                    1.0, None, 0.0, None, None, ws, n, None)
@@ -736,19 +739,19 @@ def test_fp8_batched_affine_and_cols_arguments(L):
 def test_fp8_quant_a_arguments(L):
     """The FP8 product with X quantized inside the GEMM validates before
     touching the GPU: whole 64-deep stages and 16-byte rows, a workspace of
-    64 KiB (counters, untouched) plus M floats, 256-byte aligned, and no
+    the counter region (untouched) plus M floats, 256-byte aligned, and no
     overlaps."""
     M, N, K = 64, 128, 256
     W = P + (3 << 34)
-    def call(K=K, ldx=K, x=A_ADDR, ws=W, wsb=65536 + 4 * M, sx=P + (4 << 34), c=C_ADDR):
+    def call(K=K, ldx=K, x=A_ADDR, ws=W, wsb=CR + 4 * M, sx=P + (4 << 34), c=C_ADDR):
         return L.gemm_fp8_nt_quant_a(M, N, K, x, ldx, sx, B_ADDR, K, None, c, N, 0, ws, wsb, None)
     assert call(K=200, ldx=200) == g5.GEMM_ERR_UNSUPPORTED           # K % 64
     assert call(ldx=260) == g5.GEMM_ERR_UNSUPPORTED                  # X rows 8-byte aligned
-    assert call(wsb=65536 + 4 * M - 4) == g5.GEMM_ERR_WORKSPACE
+    assert call(wsb=CR + 4 * M - 4) == g5.GEMM_ERR_WORKSPACE
     assert call(wsb=4 * M) == g5.GEMM_ERR_WORKSPACE                  # no room past the counters
     assert call(ws=None, wsb=0) == g5.GEMM_ERR_WORKSPACE
     assert call(ws=W + 64) == g5.GEMM_ERR_INVALID_ARG                # workspace not 256-byte aligned
     assert call(ldx=100) == g5.GEMM_ERR_INVALID_ARG                  # ldx < K
     assert call(sx=C_ADDR + 16) == g5.GEMM_ERR_INVALID_ARG           # factors inside C
-    assert call(ws=C_ADDR - 65536) == g5.GEMM_ERR_INVALID_ARG        # the maxima would land in C
+    assert call(ws=C_ADDR - CR) == g5.GEMM_ERR_INVALID_ARG           # the maxima would land in C
     assert L.gemm_fp8_nt_quant_a(0, N, K, None, K, None, None, K, None, None, N, 0, None, 0, None) == g5.GEMM_OK

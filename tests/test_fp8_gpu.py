@@ -418,7 +418,7 @@ def test_fp8_quant_a_bf16_out_and_repeat():
     X = gi.to_bf16_bits(x)
     dX = dev_bf16(X)
     qW, sW = g5.gemm_fp8_quantize_rows(dev_bf16(gi.to_bf16_bits(gi.normal(g, (N, K), 0.125))))
-    wsb = torch.zeros(65536 + 4096, dtype=torch.uint8, device="cuda")
+    wsb = torch.zeros(g5.GEMM_WORKSPACE_COUNTER_BYTES + 4096, dtype=torch.uint8, device="cuda")
     C1, s1 = g5.gemm_fp8_nt_quant_a(dX, qW, sW, workspace=wsb)
     C2, s2 = g5.gemm_fp8_nt_quant_a(dX, qW, sW, workspace=wsb)
     assert torch.equal(C1.view(torch.int16), C2.view(torch.int16)) and torch.equal(s1, s2)
@@ -491,7 +491,7 @@ def test_fp8_quant_a_codes_exact(oracle_mod, monkeypatch, tile_n):
 
 
 def test_fp8_quant_a_leaves_workspace_counters_zero(oracle_mod):
-    """The row maxima go past the workspace's first 64 KiB, so a Workspace
+    """The row maxima go past the workspace's counter region, so a Workspace
     shared with gemm_run calls keeps its arrival counters at zero: a K-split
     small-M product right after a quantized-inside call on the same
     workspace is still correct."""
@@ -500,7 +500,7 @@ def test_fp8_quant_a_leaves_workspace_counters_zero(oracle_mod):
     qW, sW = g5.gemm_fp8_quantize_rows((torch.randn(512, 256, device="cuda") * 0.125).to(torch.bfloat16))
     g5.gemm_fp8_nt_quant_a(X, qW, sW, workspace=w)
     torch.cuda.synchronize()
-    assert int(w.buf[:65536].count_nonzero()) == 0, "counters written"
+    assert int(w.buf[:g5.GEMM_WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0, "counters written"
     M, N, K = 1, 12288, 4096
     A, B = gi.small_case("bf16", M, N, K, seed=31, scale_b=0.125)
     st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)

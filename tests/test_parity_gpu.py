@@ -300,7 +300,7 @@ def test_decode_exchange_slots_reset(oracle_mod):
     the region is all zero afterwards, and a repeat gives the same bits."""
     N, K = 12288, 4096
     st, plan = g5.plan_query(g5.GEMM_OP_BF16, 1, N, K)
-    assert st == 0 and plan.name == b"decode_splitk" and plan.workspace_bytes == 65536
+    assert st == 0 and plan.name == b"decode_splitk" and plan.workspace_bytes == g5.GEMM_WORKSPACE_COUNTER_BYTES
     w = g5.Workspace()
     _, W = gi.decode_inputs(1)
     dW = dev_bf16(W)
@@ -312,7 +312,7 @@ def test_decode_exchange_slots_reset(oracle_mod):
         check_bf16(host_values(C), oracle_mod.gemm_bf16(X, W), K, f"exchange call {i}")
         outs.append((X, host_bits(C)))
     torch.cuda.synchronize()
-    assert int(w.buf[:65536].count_nonzero()) == 0, "exchange slots left set"
+    assert int(w.buf[:g5.GEMM_WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0, "exchange slots left set"
     X, bits = outs[0]
     assert np.array_equal(host_bits(g5.gemm_bf16(dev_bf16(X), dW, workspace=w)), bits)
 
@@ -352,7 +352,7 @@ def test_bf16_realigned_rows(oracle_mod, M, N, K, pa, batch):
         tiles = batch * -(-M // plan.tile_m) * -(-N // plan.tile_n)
         split = tiles * plan.ksplit * plan.tile_m * plan.tile_n * 4
     r = lambda b: (b + 255) // 256 * 256
-    assert plan.workspace_bytes == 65536 + r(split) + r(batch * M * ((K + 7) // 8 * 8) * 2)
+    assert plan.workspace_bytes == g5.GEMM_WORKSPACE_COUNTER_BYTES + r(split) + r(batch * M * ((K + 7) // 8 * 8) * 2)
     g5.gemm_bf16_batched(dA[:, :, :K], dB, C, workspace=ws())
     host = host_values(C)
     for b in range(batch):
@@ -670,7 +670,7 @@ def test_calls_allocate_nothing_on_a_fresh_stream(oracle_mod):
     free1, _ = torch.cuda.mem_get_info()
     assert st1 == 0 and st2 == 0
     assert free1 == free0, f"device free memory changed by {free0 - free1} bytes"
-    assert int(wsbuf[:65536].count_nonzero()) == 0, "arrival counters not left at zero"
+    assert int(wsbuf[:g5.GEMM_WORKSPACE_COUNTER_BYTES].count_nonzero()) == 0, "arrival counters not left at zero"
     ref = oracle_mod.gemm_bf16(X, W)
     check_bf16(host_values(C1), ref, 4096, "split small-M with workspace")
     check_bf16(host_values(C2), ref, 4096, "whole-K small-M without workspace")
