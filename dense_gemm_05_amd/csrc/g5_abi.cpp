@@ -607,14 +607,17 @@ bool decode_split_direct(const Problem &p, const Plan &pl)
     return pl.config == CFG_DECODE_SPLIT && pl.ks == 1 && p.op != GEMM_OP_BF16_SWIGLU;
 }
 
-// Two slices whose outputs fit the counter region as exchange slots (one
+// Two workgroups per strip (two K slices, or SwiGLU's gate and up with one
+// slice each) whose outputs fit the counter region as exchange slots (one
 // 32-bit word per output, zero between calls): the split small-M path pairs
-// the slices' partial sums by atomic exchange instead of counters and a
+// their partial sums by atomic exchange instead of counters and a
 // partial-sum buffer (the same sums, in the same order).
 bool decode_split_pair(const Problem &p, const Plan &pl)
 {
-    return pl.config == CFG_DECODE_SPLIT && pl.ks == 2 && p.op != GEMM_OP_BF16_SWIGLU &&
-           (uint64_t)p.batch * p.M * p.N * 4 <= kCounterBytes;
+    const bool two = p.op == GEMM_OP_BF16_SWIGLU ? pl.ks == 1 : pl.ks == 2;
+    if (const char *e = std::getenv("GEMM_DECODE_PAIR"))    // diagnostic: 0 = counters and partial sums
+        if (std::strcmp(e, "0") == 0) return false;
+    return pl.config == CFG_DECODE_SPLIT && two && (uint64_t)p.batch * p.M * p.N * 4 <= kCounterBytes;
 }
 
 // Partial sums of the split small-M path: one slot of 16 x 128 FP32 per

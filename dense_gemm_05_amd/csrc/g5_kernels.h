@@ -74,10 +74,10 @@ hipError_t launch_realign_rows(const uint16_t *A, int64_t lda, int64_t sA, int64
 // (a.tiles_n strips; 2 ks for a.epi == EPI_SWIGLU: ks on the gate columns,
 // ks on the up columns): `ws` holds batch x strips x (ks or 2 ks) x 16 x 128
 // floats of partial sums, `cnt` batch x strips counters that are zero on
-// entry and left zero on exit.  With `pair` (ks == 2, not SwiGLU): no partial
-// sums or counters, but batch x M x N 32-bit exchange slots, zero on entry
-// and left zero.  Requires N % 128 == 0, K % 32 == 0, 16-byte aligned rows of
-// X and W.
+// entry and left zero on exit.  With `pair` (ks == 2, or ks == 1 for
+// SwiGLU: two members per strip): no partial sums or counters, but
+// batch x M x N 32-bit exchange slots, zero on entry and left zero.
+// Requires N % 128 == 0, K % 32 == 0, 16-byte aligned rows of X and W.
 hipError_t launch_decode_split(const GemmArgs &a, float *ws, unsigned *cnt, int ks, unsigned *pair, hipStream_t s);
 
 // The bf16 ring kernel on a persistent stream-K schedule (variants 1 and 2

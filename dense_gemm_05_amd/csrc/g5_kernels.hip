@@ -628,13 +628,14 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
 //    slice order, and stores bf16(bf16(SiLU(g)) * u).
 // Requires N % 128 == 0, K % 32 == 0, 16-byte aligned rows of X and W.
 // DB: double-buffer the W rows of two steps in registers.
-//  * Two slices (pair != NULL): no counter.  Each output has a 32-bit slot
-//    in pair[] (zero on entry; [batch][M][N]); a workgroup exchanges its
-//    partial, stored as its bit pattern with every bit flipped, into the
-//    slot (a device-scope atomic exchange).  The one that gets a nonzero
-//    value back holds both partials, adds them in slice order -- (0 + p0) +
-//    p1, the sum the counter path computes -- stores the output and puts
-//    the slot back to zero.  One atomic round trip per output instead of the
+//  * Two members per strip (pair != NULL: two K slices, or SwiGLU's gate
+//    and up workgroups with one slice each): no counter.  Each output has a
+//    32-bit slot in pair[] (zero on entry; [batch][M][N]); a workgroup
+//    exchanges its partial, stored as its bit pattern with every bit
+//    flipped, into the slot (a device-scope atomic exchange).  The one that
+//    gets a nonzero value back holds both partials and finishes the output
+//    as the counter path would -- (0 + p0) + p1 in slice order, or SwiGLU
+//    of (0 + g) and (0 + u) -- then puts the slot back to zero.  One atomic round trip per output instead of the
 //    store-wait-count-reload sequence; the value read is the atomic's own
 //    result, so no ordering beyond the atomic is needed.
 template <int NW, bool DB>
@@ -752,8 +753,10 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode_sk(GemmArgs p, float *ws,
             const unsigned other = __hip_atomic_exchange(slot, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (other != 0u) {
                 const float o = __uint_as_float(~other);
-                const float p0 = slice == 0 ? sum : o, p1 = slice == 0 ? o : sum;
-                store_out(p, bidx, m, n0 + n, (0.f + p0) + p1);
+                const bool first = (glu ? half : slice) == 0;   // this member's partial comes first
+                const float p0 = first ? sum : o, p1 = first ? o : sum;
+                if (glu) store_swiglu(p, bidx, m, n0 + n, 0.f + p0, 0.f + p1);
+                else store_out(p, bidx, m, n0 + n, (0.f + p0) + p1);
                 __hip_atomic_store(slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         } else {
@@ -788,7 +791,7 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode_sk(GemmArgs p, float *ws,
 
 hipError_t launch_decode_split(const GemmArgs &a, float *ws, unsigned *cnt, int ks, unsigned *pair, hipStream_t s)
 {
-    if (pair && (ks != 2 || a.epi == EPI_SWIGLU)) return hipErrorInvalidValue;
+    if (pair && (a.epi == EPI_SWIGLU ? ks != 1 : ks != 2)) return hipErrorInvalidValue;
     // 16 waves, one 32-row step in registers at a time (two would spill at
     // 16 waves per CU; the waves themselves keep enough loads in flight).
     const int64_t groups = a.epi == EPI_SWIGLU ? 2 * a.tiles_n : a.tiles_n;

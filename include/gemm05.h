@@ -38,7 +38,9 @@
  * GEMM_FORCE_KSPLIT=S (diagnostics and tests) forces a split of S slices on
  * gemm_run calls with a workspace that use 128x128 tiles (1 = none;
  * GEMM_ERR_UNSUPPORTED when S slices of at least 4 32-deep stages do not
- * fit K, or without a workspace).
+ * fit K, or without a workspace); GEMM_DECODE_PAIR=0 makes the small-M path
+ * combine its two workgroups per strip through counters and partial sums
+ * instead of exchange slots (the same bits, either way).
  * No alignment is required; aligned operands (16-byte rows and pointers)
  * select the faster kernel variants.
  *

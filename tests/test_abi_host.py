@@ -360,12 +360,12 @@ def test_fused_small_m_plans(L):
     """M <= 16: SiLU and SwiGLU run on the small-M kernels.  With a workspace
     the K-split path (SwiGLU: separate workgroups for a strip's gate and up
     columns, 2 x 96 strips for N = 12288; SiLU: 96 strips x 2 slices), its
-    partial sums in the workspace (SiLU with two slices: exchange slots in
-    the counter region, no partial sums); without one the whole-K
-    64-column kernel; K % 32 != 0 only the latter."""
+    two members of a strip meeting in exchange slots in the workspace's
+    counter region (no partial sums); without one the whole-K 64-column
+    kernel; K % 32 != 0 only the latter."""
     st, p = g5.plan_query(g5.GEMM_OP_BF16_SWIGLU, 1, 12288, 4096)
     assert st == 0 and p.name == b"decode_splitk" and p.grid == 192
-    assert p.workspace_bytes == ws_bytes(96 * 2 * 16 * 128 * 4)
+    assert p.workspace_bytes == CR
     st, p = g5.plan_query(g5.GEMM_OP_BF16_SILU, 16, 12288, 4096)
     assert st == 0 and p.name == b"decode_splitk" and p.grid == 192
     assert p.workspace_bytes == CR

@@ -279,3 +279,32 @@ def test_swiglu_batched_small_m(oracle_mod, broadcast_x, with_ws):
     for b in range(batch):
         Zr, G, U, t, u = _swiglu_ref(oracle_mod, X[0 if broadcast_x else b], Wgu[b])
         check_swiglu(got[b], G, U, t, u, Zr, K, f"swiglu small-M expert {b}")
+
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_small_m_exchange_equals_counter_combine(monkeypatch, M):
+    """The small-M path's two workgroups per strip (two K slices of the
+    plain product or SiLU; SwiGLU's gate and up) meet in exchange slots by
+    default; GEMM_DECODE_PAIR=0 sends them through counters and partial sums
+    instead.  Both give the same bits, for the product, SiLU and SwiGLU."""
+    N, K = 12288, 4096
+    _say(f"exchange against counter combine, M={M}")
+    g = np.random.default_rng([gi.SEED_BASE + 9200, M])
+    dX = dev_bf16(gi.to_bf16_bits(gi.normal(g, (M, K))))
+    _, W = gi.decode_inputs(1)
+    _, Wgu = gi.swiglu_inputs(1, K, N)
+    dW, dWgu = dev_bf16(W), dev_bf16(Wgu)
+    w = ws()
+    calls = {"product": lambda: g5.gemm_bf16(dX, dW, workspace=w),
+             "silu": lambda: g5.gemm_bf16_silu(dX, dW, workspace=w),
+             "swiglu": lambda: g5.gemm_bf16_swiglu(dX, dWgu, workspace=w)}
+    for name, op in (("product", g5.GEMM_OP_BF16), ("swiglu", g5.GEMM_OP_BF16_SWIGLU)):
+        st, plan = g5.plan_query(op, M, N, K)
+        assert st == 0 and plan.name == b"decode_splitk" and plan.workspace_bytes == g5.GEMM_WORKSPACE_COUNTER_BYTES, name
+    paired = {k: host_bits(f()) for k, f in calls.items()}
+    monkeypatch.setenv("GEMM_DECODE_PAIR", "0")
+    st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
+    assert st == 0 and plan.workspace_bytes > g5.GEMM_WORKSPACE_COUNTER_BYTES      # partial sums
+    for k, f in calls.items():
+        assert np.array_equal(host_bits(f()), paired[k]), k
