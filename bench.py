@@ -45,6 +45,29 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+class guarded:
+    """Runs one workload so that a Python-level failure (a status error, a
+    parity assertion) is logged and recorded under its name in `workloads`
+    instead of ending the run: the JSON line, with every other workload, is
+    still printed.  A fault that breaks the GPU context ends the process as
+    before."""
+
+    def __init__(self, name, workloads):
+        self.name, self.workloads = name, workloads
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, et, ev, tb):
+        if et is None or not issubclass(et, Exception):
+            return False
+        import traceback
+        traceback.print_exception(et, ev, tb, file=sys.stderr)
+        log(f"{self.name}: FAILED ({et.__name__}: {ev})")
+        self.workloads.append({"name": self.name, "error": f"{et.__name__}: {ev}"})
+        return True
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,434 +252,450 @@ def main():
 
     # ------------------------------------------------------------ FFN (headline)
     if args.only in ("all", "ffn"):
-        M, N, K = 1024, 12288, 4096
-        log("FFN: generating inputs")
-        X, W = gi.ffn_inputs(M, K, N)
-        R = rotations(2 * (M * K + K * N + M * N))
-        dX = [to_dev_bf16(X) for _ in range(R)]
-        dW = [to_dev_bf16(W) for _ in range(R)]
-        dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        fns = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
-        st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
-        ms = timed(fns, args.steps, args.warmup, label="ffn_bf16_1024x12288x4096")
-        flops = 2.0 * M * N * K
-        tflops = flops / (ms * 1e-3) / 1e12
-        log(f"FFN: {ms * 1e3:.2f} us/call, {tflops:.1f} TFLOPS ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak), "
-            f"config {plan.name.decode()}, R={R}")
-        tm = timings["ffn_bf16_1024x12288x4096"]
-        out["value"] = round(tflops, 2)
-        out["value_min"] = round(flops / (tm["max_us"] * 1e-6) / 1e12, 2)
-        out["value_max"] = round(flops / (tm["min_us"] * 1e-6) / 1e12, 2)
-        out["ms_per_step"] = round(ms, 5)
-        out["steps"] = tm["batches"] * tm["calls_per_batch"]
-        out["timing"] = {"batches": tm["batches"], "calls_per_batch": tm["calls_per_batch"],
-                         "median_us": tm["median_us"], "min_us": tm["min_us"], "max_us": tm["max_us"],
-                         "statistic": "median over batches of (event interval / calls)"}
-        traffic = None
-        if os.path.exists(TRAFFIC_FILE):
-            with open(TRAFFIC_FILE) as fh:
-                tr = json.load(fh)
-            if tr.get("kernel_sha256_16") == kernel_hash():
-                traffic = tr.get("hbm_bytes_per_launch")
-        out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                           "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                           "kernel": kernel_label(plan),
-                           "flops_per_launch": flops}
-        workloads.append({"name": "ffn_bf16_1024x12288x4096", "us": round(ms * 1e3, 3),
-                          "tflops": round(tflops, 2), "frac_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
-                          "config": plan.name.decode(), "rotations": R})
-        ffn_rows_gpu = (X, W, dC[(args.steps - 1) % R])
-
-    # ------------------------------------------------------------ decode
-    if args.only in ("all", "decode"):
-        N, K = 12288, 4096
-        for M in (1, 4, 16):
-            X, W = gi.decode_inputs(M, K, N)
-            alg_bytes = 2 * (M * K + K * N + M * N)
-            R = rotations(alg_bytes)
+        with guarded("ffn", workloads):
+            M, N, K = 1024, 12288, 4096
+            log("FFN: generating inputs")
+            X, W = gi.ffn_inputs(M, K, N)
+            R = rotations(2 * (M * K + K * N + M * N))
             dX = [to_dev_bf16(X) for _ in range(R)]
             dW = [to_dev_bf16(W) for _ in range(R)]
             dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
             fns = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
-            ms = timed(fns, max(200, args.steps), args.warmup, label=f"decode_bf16_m{M}_12288x4096")
-            gbps = alg_bytes / (ms * 1e-3) / 1e9
-            log(f"decode M={M}: {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM)")
-            rec = {"name": f"decode_bf16_m{M}_12288x4096", "us": round(ms * 1e3, 3), "GBps": round(gbps, 1),
-                   "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "alg_bytes": alg_bytes, "rotations": R}
-            workloads.append(rec)
-            if M == 1:
-                out["decode_m1"] = {"GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
-                                    "us": round(ms * 1e3, 3), "alg_bytes": alg_bytes}
-            del dX, dW, dC
+            st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
+            ms = timed(fns, args.steps, args.warmup, label="ffn_bf16_1024x12288x4096")
+            flops = 2.0 * M * N * K
+            tflops = flops / (ms * 1e-3) / 1e12
+            log(f"FFN: {ms * 1e3:.2f} us/call, {tflops:.1f} TFLOPS ({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of peak), "
+                f"config {plan.name.decode()}, R={R}")
+            tm = timings["ffn_bf16_1024x12288x4096"]
+            out["value"] = round(tflops, 2)
+            out["value_min"] = round(flops / (tm["max_us"] * 1e-6) / 1e12, 2)
+            out["value_max"] = round(flops / (tm["min_us"] * 1e-6) / 1e12, 2)
+            out["ms_per_step"] = round(ms, 5)
+            out["steps"] = tm["batches"] * tm["calls_per_batch"]
+            out["timing"] = {"batches": tm["batches"], "calls_per_batch": tm["calls_per_batch"],
+                             "median_us": tm["median_us"], "min_us": tm["min_us"], "max_us": tm["max_us"],
+                             "statistic": "median over batches of (event interval / calls)"}
+            traffic = None
+            if os.path.exists(TRAFFIC_FILE):
+                with open(TRAFFIC_FILE) as fh:
+                    tr = json.load(fh)
+                if tr.get("kernel_sha256_16") == kernel_hash():
+                    traffic = tr.get("hbm_bytes_per_launch")
+            out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                               "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                               "kernel": kernel_label(plan),
+                               "flops_per_launch": flops}
+            workloads.append({"name": "ffn_bf16_1024x12288x4096", "us": round(ms * 1e3, 3),
+                              "tflops": round(tflops, 2), "frac_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+                              "config": plan.name.decode(), "rotations": R})
+            ffn_rows_gpu = (X, W, dC[(args.steps - 1) % R])
+
+    # ------------------------------------------------------------ decode
+    if args.only in ("all", "decode"):
+        with guarded("decode", workloads):
+            N, K = 12288, 4096
+            for M in (1, 4, 16):
+                X, W = gi.decode_inputs(M, K, N)
+                alg_bytes = 2 * (M * K + K * N + M * N)
+                R = rotations(alg_bytes)
+                dX = [to_dev_bf16(X) for _ in range(R)]
+                dW = [to_dev_bf16(W) for _ in range(R)]
+                dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+                fns = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
+                ms = timed(fns, max(200, args.steps), args.warmup, label=f"decode_bf16_m{M}_12288x4096")
+                gbps = alg_bytes / (ms * 1e-3) / 1e9
+                log(f"decode M={M}: {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM)")
+                rec = {"name": f"decode_bf16_m{M}_12288x4096", "us": round(ms * 1e3, 3), "GBps": round(gbps, 1),
+                       "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "alg_bytes": alg_bytes, "rotations": R}
+                workloads.append(rec)
+                if M == 1:
+                    out["decode_m1"] = {"GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
+                                        "us": round(ms * 1e3, 3), "alg_bytes": alg_bytes}
+                del dX, dW, dC
 
     # ------------------------------------------------------------ decode through the fused SwiGLU
     if args.only in ("all", "decode_swiglu"):
-        # One token through the FFN's gate and up projections with the merged
-        # weight Wgu [4096, 2 x 12288] and the SwiGLU product applied as the
-        # small-M kernels store, next to the plain product of the same token
-        # with the same merged weight (the same 192 MiB read, 24576 bf16
-        # outputs): the fusion's cost over the bytes it has to read.
-        N, K = 12288, 4096
-        X, Wgu = gi.swiglu_inputs(16, K, N)
-        for M in (1, 16):
-            Xm = np.ascontiguousarray(X[:M])
-            alg_bytes = 2 * (M * K + K * 2 * N + M * N)
-            R = rotations(alg_bytes)
-            dX = [to_dev_bf16(Xm) for _ in range(R)]
-            dW = [to_dev_bf16(Wgu) for _ in range(R)]
-            dZ = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-            dP = [torch.empty((M, 2 * N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-            fused = [(lambda i=i: g5.gemm_bf16_swiglu(dX[i], dW[i], dZ[i], workspace=ws)) for i in range(R)]
-            fused_nows = [(lambda i=i: g5.gemm_bf16_swiglu(dX[i], dW[i], dZ[i])) for i in range(R)]
-            plain = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dP[i], workspace=ws)) for i in range(R)]
-            ms = timed(fused, 200, args.warmup, label=f"decode_swiglu_m{M}_2x12288x4096")
-            ms_n = timed(fused_nows, 200, args.warmup, label=f"decode_swiglu_m{M}_no_workspace")
-            ms_p = timed(plain, 200, args.warmup, label=f"decode_plain_merged_m{M}_24576x4096")
-            gbps = alg_bytes / (ms * 1e-3) / 1e9
-            log(f"decode SwiGLU M={M}: fused {ms * 1e3:.2f} us ({gbps:.0f} GB/s), without workspace "
-                f"{ms_n * 1e3:.2f} us; plain product with the merged weight {ms_p * 1e3:.2f} us "
-                f"(fused / plain {ms / ms_p:.3f})")
-            workloads.append({"name": f"decode_swiglu_bf16_m{M}_2x12288x4096", "us": round(ms * 1e3, 3),
-                              "GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
-                              "no_workspace_us": round(ms_n * 1e3, 3),
-                              "plain_merged_product_us": round(ms_p * 1e3, 3),
-                              "fused_over_plain": round(ms / ms_p, 4), "alg_bytes": alg_bytes, "rotations": R})
-            del dX, dW, dZ, dP
+        with guarded("decode_swiglu", workloads):
+            # One token through the FFN's gate and up projections with the merged
+            # weight Wgu [4096, 2 x 12288] and the SwiGLU product applied as the
+            # small-M kernels store, next to the plain product of the same token
+            # with the same merged weight (the same 192 MiB read, 24576 bf16
+            # outputs): the fusion's cost over the bytes it has to read.
+            N, K = 12288, 4096
+            X, Wgu = gi.swiglu_inputs(16, K, N)
+            for M in (1, 16):
+                Xm = np.ascontiguousarray(X[:M])
+                alg_bytes = 2 * (M * K + K * 2 * N + M * N)
+                R = rotations(alg_bytes)
+                dX = [to_dev_bf16(Xm) for _ in range(R)]
+                dW = [to_dev_bf16(Wgu) for _ in range(R)]
+                dZ = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+                dP = [torch.empty((M, 2 * N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+                fused = [(lambda i=i: g5.gemm_bf16_swiglu(dX[i], dW[i], dZ[i], workspace=ws)) for i in range(R)]
+                fused_nows = [(lambda i=i: g5.gemm_bf16_swiglu(dX[i], dW[i], dZ[i])) for i in range(R)]
+                plain = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dP[i], workspace=ws)) for i in range(R)]
+                ms = timed(fused, 200, args.warmup, label=f"decode_swiglu_m{M}_2x12288x4096")
+                ms_n = timed(fused_nows, 200, args.warmup, label=f"decode_swiglu_m{M}_no_workspace")
+                ms_p = timed(plain, 200, args.warmup, label=f"decode_plain_merged_m{M}_24576x4096")
+                gbps = alg_bytes / (ms * 1e-3) / 1e9
+                log(f"decode SwiGLU M={M}: fused {ms * 1e3:.2f} us ({gbps:.0f} GB/s), without workspace "
+                    f"{ms_n * 1e3:.2f} us; plain product with the merged weight {ms_p * 1e3:.2f} us "
+                    f"(fused / plain {ms / ms_p:.3f})")
+                workloads.append({"name": f"decode_swiglu_bf16_m{M}_2x12288x4096", "us": round(ms * 1e3, 3),
+                                  "GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
+                                  "no_workspace_us": round(ms_n * 1e3, 3),
+                                  "plain_merged_product_us": round(ms_p * 1e3, 3),
+                                  "fused_over_plain": round(ms / ms_p, 4), "alg_bytes": alg_bytes, "rotations": R})
+                del dX, dW, dZ, dP
 
     # ------------------------------------------------------------ decode with a linear layer's weight
     if args.only in ("all", "decode_nt"):
-        # The same decode rows against W stored as a linear layer's weight,
-        # Wt [12288, 4096]: a GEMV over the contiguous rows of Wt.
-        N, K = 12288, 4096
-        for M in (1, 4, 16):
-            X, W = gi.decode_inputs(M, K, N)
-            Wt = np.ascontiguousarray(W.T)
-            alg_bytes = 2 * (M * K + K * N + M * N)
-            R = rotations(alg_bytes)
-            dX = [to_dev_bf16(X) for _ in range(R)]
-            dW = [to_dev_bf16(Wt) for _ in range(R)]
-            dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-            fns = [(lambda i=i: g5.gemm_bf16_nt(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
-            ms = timed(fns, max(200, args.steps), args.warmup, label=f"decode_nt_bf16_m{M}_12288x4096")
-            gbps = alg_bytes / (ms * 1e-3) / 1e9
-            log(f"decode NT M={M}: {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM)")
-            workloads.append({"name": f"decode_nt_bf16_m{M}_12288x4096", "us": round(ms * 1e3, 3),
-                              "GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
-                              "alg_bytes": alg_bytes, "rotations": R})
-            del dX, dW, dC
+        with guarded("decode_nt", workloads):
+            # The same decode rows against W stored as a linear layer's weight,
+            # Wt [12288, 4096]: a GEMV over the contiguous rows of Wt.
+            N, K = 12288, 4096
+            for M in (1, 4, 16):
+                X, W = gi.decode_inputs(M, K, N)
+                Wt = np.ascontiguousarray(W.T)
+                alg_bytes = 2 * (M * K + K * N + M * N)
+                R = rotations(alg_bytes)
+                dX = [to_dev_bf16(X) for _ in range(R)]
+                dW = [to_dev_bf16(Wt) for _ in range(R)]
+                dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+                fns = [(lambda i=i: g5.gemm_bf16_nt(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
+                ms = timed(fns, max(200, args.steps), args.warmup, label=f"decode_nt_bf16_m{M}_12288x4096")
+                gbps = alg_bytes / (ms * 1e-3) / 1e9
+                log(f"decode NT M={M}: {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM)")
+                workloads.append({"name": f"decode_nt_bf16_m{M}_12288x4096", "us": round(ms * 1e3, 3),
+                                  "GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
+                                  "alg_bytes": alg_bytes, "rotations": R})
+                del dX, dW, dC
 
     # ------------------------------------------------------------ FP32
     if args.only in ("all", "sgemm"):
-        for n, wl, steps in ((256, gi.W_SGEMM_SMALL, 500), (4096, gi.W_SGEMM_LARGE, 20)):
-            A, B = gi.sgemm_inputs(n, workload=wl)
-            R = rotations(4 * 3 * n * n)
-            dA = [torch.from_numpy(A).to(dev) for _ in range(R)]
-            dB = [torch.from_numpy(B).to(dev) for _ in range(R)]
-            dC = [torch.empty((n, n), device=dev) for _ in range(R)]
-            fns = [(lambda i=i: g5.gemm_sgemm(dA[i], dB[i], dC[i])) for i in range(R)]
-            ms = timed(fns, steps, 5, label=f"sgemm_f32_{n}^3")
-            tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
-            log(f"sgemm {n}^3: {ms * 1e3:.2f} us/call, {tf:.1f} TFLOPS ({100 * tf / PEAK_F32_TFLOPS:.1f}% of fp32 peak)")
-            workloads.append({"name": f"sgemm_f32_{n}^3", "us": round(ms * 1e3, 3), "tflops": round(tf, 2),
-                              "frac_peak": round(tf / PEAK_F32_TFLOPS, 4), "rotations": R})
-            del dA, dB, dC
+        with guarded("sgemm", workloads):
+            for n, wl, steps in ((256, gi.W_SGEMM_SMALL, 500), (4096, gi.W_SGEMM_LARGE, 20)):
+                A, B = gi.sgemm_inputs(n, workload=wl)
+                R = rotations(4 * 3 * n * n)
+                dA = [torch.from_numpy(A).to(dev) for _ in range(R)]
+                dB = [torch.from_numpy(B).to(dev) for _ in range(R)]
+                dC = [torch.empty((n, n), device=dev) for _ in range(R)]
+                fns = [(lambda i=i: g5.gemm_sgemm(dA[i], dB[i], dC[i])) for i in range(R)]
+                ms = timed(fns, steps, 5, label=f"sgemm_f32_{n}^3")
+                tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+                log(f"sgemm {n}^3: {ms * 1e3:.2f} us/call, {tf:.1f} TFLOPS ({100 * tf / PEAK_F32_TFLOPS:.1f}% of fp32 peak)")
+                workloads.append({"name": f"sgemm_f32_{n}^3", "us": round(ms * 1e3, 3), "tflops": round(tf, 2),
+                                  "frac_peak": round(tf / PEAK_F32_TFLOPS, 4), "rotations": R})
+                del dA, dB, dC
 
     # ------------------------------------------------------------ bf16 square
     if args.only in ("all", "square"):
-        # bf16 4096^3 -> bf16: 256 tiles of 256x256, one per CU.
-        n = 4096
-        g = np.random.default_rng([gi.SEED_BASE + 900, n])
-        A = gi.to_bf16_bits(gi.normal(g, (n, n)))
-        B = gi.to_bf16_bits(gi.normal(g, (n, n), 0.125))
-        R = rotations(2 * 3 * n * n)
-        dA = [to_dev_bf16(A) for _ in range(R)]
-        dB = [to_dev_bf16(B) for _ in range(R)]
-        dC = [torch.empty((n, n), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        fns = [(lambda i=i: g5.gemm_bf16(dA[i], dB[i], dC[i], workspace=ws)) for i in range(R)]
-        st, plan = g5.plan_query(g5.GEMM_OP_BF16, n, n, n)
-        ms = timed(fns, 50, 10, label="square_bf16_4096^3")
-        tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
-        log(f"bf16 4096^3: {ms * 1e3:.2f} us/call, {tf:.1f} TFLOPS ({100 * tf / PEAK_BF16_TFLOPS:.1f}%), "
-            f"{plan.name.decode()}")
-        workloads.append({"name": "square_bf16_4096^3", "us": round(ms * 1e3, 3), "tflops": round(tf, 2),
-                          "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "config": plan.name.decode(),
-                          "rotations": R})
-        del dA, dB, dC
+        with guarded("square", workloads):
+            # bf16 4096^3 -> bf16: 256 tiles of 256x256, one per CU.
+            n = 4096
+            g = np.random.default_rng([gi.SEED_BASE + 900, n])
+            A = gi.to_bf16_bits(gi.normal(g, (n, n)))
+            B = gi.to_bf16_bits(gi.normal(g, (n, n), 0.125))
+            R = rotations(2 * 3 * n * n)
+            dA = [to_dev_bf16(A) for _ in range(R)]
+            dB = [to_dev_bf16(B) for _ in range(R)]
+            dC = [torch.empty((n, n), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+            fns = [(lambda i=i: g5.gemm_bf16(dA[i], dB[i], dC[i], workspace=ws)) for i in range(R)]
+            st, plan = g5.plan_query(g5.GEMM_OP_BF16, n, n, n)
+            ms = timed(fns, 50, 10, label="square_bf16_4096^3")
+            tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+            log(f"bf16 4096^3: {ms * 1e3:.2f} us/call, {tf:.1f} TFLOPS ({100 * tf / PEAK_BF16_TFLOPS:.1f}%), "
+                f"{plan.name.decode()}")
+            workloads.append({"name": "square_bf16_4096^3", "us": round(ms * 1e3, 3), "tflops": round(tf, 2),
+                              "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "config": plan.name.decode(),
+                              "rotations": R})
+            del dA, dB, dC
 
     # ------------------------------------------------------------ batched
     if args.only in ("all", "batched"):
-        Q, KT = gi.batched_inputs()
-        bt, M, K = Q.shape
-        N = KT.shape[2]
-        alg_bytes = 2 * Q.size + 2 * KT.size + 4 * bt * M * N
-        R = rotations(alg_bytes)
-        dQ = [to_dev_bf16(Q) for _ in range(R)]
-        dK = [to_dev_bf16(KT) for _ in range(R)]
-        dC = [torch.empty((bt, M, N), device=dev) for _ in range(R)]
-        fns = [(lambda i=i: g5.gemm_bf16_batched(dQ[i], dK[i], dC[i], workspace=ws)) for i in range(R)]
-        ms = timed(fns, 100, 10, label="batched_bf16_32x1024x1024x128_f32out")
-        flops = 2.0 * bt * M * N * K
-        t_roof = max(flops / (PEAK_BF16_TFLOPS * 1e12), alg_bytes / (PEAK_HBM_GBPS * 1e9))
-        gbps = alg_bytes / (ms * 1e-3) / 1e9
-        log(f"batched 32x1024x1024x128: {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s, roofline frac {t_roof / (ms * 1e-3):.3f}")
-        workloads.append({"name": "batched_bf16_32x1024x1024x128_f32out", "us": round(ms * 1e3, 3),
-                          "GBps": round(gbps, 1), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
-                          "frac_roofline": round(t_roof / (ms * 1e-3), 4), "alg_bytes": alg_bytes, "rotations": R})
-        del dQ, dK, dC
+        with guarded("batched", workloads):
+            Q, KT = gi.batched_inputs()
+            bt, M, K = Q.shape
+            N = KT.shape[2]
+            alg_bytes = 2 * Q.size + 2 * KT.size + 4 * bt * M * N
+            R = rotations(alg_bytes)
+            dQ = [to_dev_bf16(Q) for _ in range(R)]
+            dK = [to_dev_bf16(KT) for _ in range(R)]
+            dC = [torch.empty((bt, M, N), device=dev) for _ in range(R)]
+            fns = [(lambda i=i: g5.gemm_bf16_batched(dQ[i], dK[i], dC[i], workspace=ws)) for i in range(R)]
+            ms = timed(fns, 100, 10, label="batched_bf16_32x1024x1024x128_f32out")
+            flops = 2.0 * bt * M * N * K
+            t_roof = max(flops / (PEAK_BF16_TFLOPS * 1e12), alg_bytes / (PEAK_HBM_GBPS * 1e9))
+            gbps = alg_bytes / (ms * 1e-3) / 1e9
+            log(f"batched 32x1024x1024x128: {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s, roofline frac {t_roof / (ms * 1e-3):.3f}")
+            workloads.append({"name": "batched_bf16_32x1024x1024x128_f32out", "us": round(ms * 1e3, 3),
+                              "GBps": round(gbps, 1), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                              "frac_roofline": round(t_roof / (ms * 1e-3), 4), "alg_bytes": alg_bytes, "rotations": R})
+            del dQ, dK, dC
 
     # ------------------------------------------------------------ ragged
     if args.only in ("all", "ragged"):
-        A, B = gi.ragged_inputs()
-        M, K = A.shape
-        N = B.shape[1]
-        R = rotations(2 * (M * K + K * N) + 4 * M * N)
-        dA = [to_dev_bf16(A) for _ in range(R)]
-        dB = [to_dev_bf16(B) for _ in range(R)]
-        dC = [torch.empty((M, N), device=dev) for _ in range(R)]
-        fns = [(lambda i=i: g5.gemm_bf16(dA[i], dB[i], dC[i], workspace=ws)) for i in range(R)]
-        ms = timed(fns, 30, 5, label="ragged_bf16_1000x12280x4100_f32out")
-        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-        log(f"ragged 1000x12280x4100: {ms * 1e3:.2f} us/call, {tf:.1f} TFLOPS ({100 * tf / PEAK_BF16_TFLOPS:.1f}%)")
-        workloads.append({"name": "ragged_bf16_1000x12280x4100_f32out", "us": round(ms * 1e3, 3),
-                          "tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "rotations": R})
-        del dA, dB, dC
+        with guarded("ragged", workloads):
+            A, B = gi.ragged_inputs()
+            M, K = A.shape
+            N = B.shape[1]
+            R = rotations(2 * (M * K + K * N) + 4 * M * N)
+            dA = [to_dev_bf16(A) for _ in range(R)]
+            dB = [to_dev_bf16(B) for _ in range(R)]
+            dC = [torch.empty((M, N), device=dev) for _ in range(R)]
+            fns = [(lambda i=i: g5.gemm_bf16(dA[i], dB[i], dC[i], workspace=ws)) for i in range(R)]
+            ms = timed(fns, 30, 5, label="ragged_bf16_1000x12280x4100_f32out")
+            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            log(f"ragged 1000x12280x4100: {ms * 1e3:.2f} us/call, {tf:.1f} TFLOPS ({100 * tf / PEAK_BF16_TFLOPS:.1f}%)")
+            workloads.append({"name": "ragged_bf16_1000x12280x4100_f32out", "us": round(ms * 1e3, 3),
+                              "tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "rotations": R})
+            del dA, dB, dC
 
     # ------------------------------------------------------------ fused SwiGLU FFN
     if args.only in ("all", "swiglu"):
-        # The FFN's gate and up projections of X with one merged weight
-        # [4096, 2 x 12288] and the SwiGLU product in the epilogue, next to
-        # the same two projections as plain calls (bf16 g and u written out).
-        M, N, K = 1024, 12288, 4096
-        X, Wgu = gi.swiglu_inputs(M, K, N)
-        alg_bytes = 2 * (M * K + K * 2 * N + M * N)
-        R = rotations(alg_bytes)
-        dX = [to_dev_bf16(X) for _ in range(R)]
-        dW = [to_dev_bf16(Wgu) for _ in range(R)]
-        dZ = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        dG = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        dU = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        fused = [(lambda i=i: g5.gemm_bf16_swiglu(dX[i], dW[i], dZ[i], workspace=ws)) for i in range(R)]
-        plain = [(lambda i=i: (g5.gemm_bf16(dX[i], dW[i][:, :N], dG[i], workspace=ws), g5.gemm_bf16(dX[i], dW[i][:, N:], dU[i], workspace=ws)))
-                 for i in range(R)]
-        # The unfused program: the two projections, then Z = bf16(bf16(SiLU(g)) * u)
-        # as element-wise passes over the written g and u (torch's bf16 silu
-        # and multiply, the same roundings as the fused epilogue).
-        unfused = [(lambda i=i: (plain[i](), torch.mul(torch.nn.functional.silu(dG[i]), dU[i], out=dZ[i])))
-                   for i in range(R)]
-        ms = timed(fused, 30, 5, label="swiglu_ffn_bf16_1024x2x12288x4096")
-        ms_plain = timed(plain, 30, 5, label="swiglu_ffn_two_plain_projections")
-        ms_unfused = timed(unfused, 30, 5, label="swiglu_ffn_unfused_program")
-        flops = 2.0 * 2 * M * N * K
-        tf = flops / (ms * 1e-3) / 1e12
-        log(f"swiglu FFN 1024x(2x12288)x4096: fused {ms * 1e3:.2f} us ({tf:.1f} TFLOPS); "
-            f"two plain projections {ms_plain * 1e3:.2f} us; unfused program (projections + element-wise "
-            f"SiLU and product) {ms_unfused * 1e3:.2f} us")
-        workloads.append({"name": "swiglu_ffn_bf16_1024x2x12288x4096", "us": round(ms * 1e3, 3),
-                          "tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                          "two_plain_projections_us": round(ms_plain * 1e3, 3),
-                          "unfused_program_us": round(ms_unfused * 1e3, 3), "rotations": R})
-        del dX, dW, dZ, dG, dU
+        with guarded("swiglu", workloads):
+            # The FFN's gate and up projections of X with one merged weight
+            # [4096, 2 x 12288] and the SwiGLU product in the epilogue, next to
+            # the same two projections as plain calls (bf16 g and u written out).
+            M, N, K = 1024, 12288, 4096
+            X, Wgu = gi.swiglu_inputs(M, K, N)
+            alg_bytes = 2 * (M * K + K * 2 * N + M * N)
+            R = rotations(alg_bytes)
+            dX = [to_dev_bf16(X) for _ in range(R)]
+            dW = [to_dev_bf16(Wgu) for _ in range(R)]
+            dZ = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+            dG = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+            dU = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+            fused = [(lambda i=i: g5.gemm_bf16_swiglu(dX[i], dW[i], dZ[i], workspace=ws)) for i in range(R)]
+            plain = [(lambda i=i: (g5.gemm_bf16(dX[i], dW[i][:, :N], dG[i], workspace=ws), g5.gemm_bf16(dX[i], dW[i][:, N:], dU[i], workspace=ws)))
+                     for i in range(R)]
+            # The unfused program: the two projections, then Z = bf16(bf16(SiLU(g)) * u)
+            # as element-wise passes over the written g and u (torch's bf16 silu
+            # and multiply, the same roundings as the fused epilogue).
+            unfused = [(lambda i=i: (plain[i](), torch.mul(torch.nn.functional.silu(dG[i]), dU[i], out=dZ[i])))
+                       for i in range(R)]
+            ms = timed(fused, 30, 5, label="swiglu_ffn_bf16_1024x2x12288x4096")
+            ms_plain = timed(plain, 30, 5, label="swiglu_ffn_two_plain_projections")
+            ms_unfused = timed(unfused, 30, 5, label="swiglu_ffn_unfused_program")
+            flops = 2.0 * 2 * M * N * K
+            tf = flops / (ms * 1e-3) / 1e12
+            log(f"swiglu FFN 1024x(2x12288)x4096: fused {ms * 1e3:.2f} us ({tf:.1f} TFLOPS); "
+                f"two plain projections {ms_plain * 1e3:.2f} us; unfused program (projections + element-wise "
+                f"SiLU and product) {ms_unfused * 1e3:.2f} us")
+            workloads.append({"name": "swiglu_ffn_bf16_1024x2x12288x4096", "us": round(ms * 1e3, 3),
+                              "tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                              "two_plain_projections_us": round(ms_plain * 1e3, 3),
+                              "unfused_program_us": round(ms_unfused * 1e3, 3), "rotations": R})
+            del dX, dW, dZ, dG, dU
 
     # ------------------------------------------------------------ column shard (split K)
     if args.only in ("all", "shard"):
-        # The 1024x1536x4096 shard of an 8-way column split of the FFN
-        # projection: 96 tiles of 128x128 for 256 CUs, so K is split over
-        # workgroups.
-        M, N, K = 1024, 1536, 4096
-        X, W = gi.ffn_inputs()
-        W = np.ascontiguousarray(W[:, :N])
-        R = rotations(2 * (M * K + K * N + M * N))
-        dX = [to_dev_bf16(X) for _ in range(R)]
-        dW = [to_dev_bf16(W) for _ in range(R)]
-        dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        fns = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
-        st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
-        ms = timed(fns, 100, 10, label="shard_bf16_1024x1536x4096")
-        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-        log(f"shard 1024x1536x4096: {ms * 1e3:.2f} us/call, {tf:.1f} TFLOPS, {plan.name.decode()} ksplit {plan.ksplit}")
-        workloads.append({"name": "shard_bf16_1024x1536x4096", "us": round(ms * 1e3, 3), "tflops": round(tf, 2),
-                          "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "config": plan.name.decode(),
-                          "ksplit": plan.ksplit, "rotations": R})
-        del dX, dW, dC
+        with guarded("shard", workloads):
+            # The 1024x1536x4096 shard of an 8-way column split of the FFN
+            # projection: 96 tiles of 128x128 for 256 CUs, so K is split over
+            # workgroups.
+            M, N, K = 1024, 1536, 4096
+            X, W = gi.ffn_inputs()
+            W = np.ascontiguousarray(W[:, :N])
+            R = rotations(2 * (M * K + K * N + M * N))
+            dX = [to_dev_bf16(X) for _ in range(R)]
+            dW = [to_dev_bf16(W) for _ in range(R)]
+            dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+            fns = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
+            st, plan = g5.plan_query(g5.GEMM_OP_BF16, M, N, K)
+            ms = timed(fns, 100, 10, label="shard_bf16_1024x1536x4096")
+            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            log(f"shard 1024x1536x4096: {ms * 1e3:.2f} us/call, {tf:.1f} TFLOPS, {plan.name.decode()} ksplit {plan.ksplit}")
+            workloads.append({"name": "shard_bf16_1024x1536x4096", "us": round(ms * 1e3, 3), "tflops": round(tf, 2),
+                              "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "config": plan.name.decode(),
+                              "ksplit": plan.ksplit, "rotations": R})
+            del dX, dW, dC
 
     # ------------------------------------------------------------ FP8 FFN
     if args.only in ("all", "fp8"):
-        # The FFN projection in E4M3FN: W^T [12288,4096] quantized per output
-        # channel once (weights), X quantized per token on every call, then
-        # the scaled FP8 product into bf16.
-        M, N, K = 1024, 12288, 4096
-        X, W = gi.ffn_inputs()
-        Wt = np.ascontiguousarray(W.T)
-        R = rotations(M * K * 3 + N * K + 2 * M * N)
-        dX = [to_dev_bf16(X) for _ in range(R)]
-        qW = [g5.gemm_fp8_quantize_rows(to_dev_bf16(Wt)) for _ in range(R)]
-        qX = [g5.gemm_fp8_quantize_rows(dX[i]) for i in range(R)]
-        dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        gemm = [(lambda i=i: g5.gemm_fp8_nt(qX[i][0], qX[i][1], qW[i][0], qW[i][1], dC[i], workspace=ws)) for i in range(R)]
-        quant = [(lambda i=i: g5.gemm_fp8_quantize_rows(dX[i], qX[i][0], qX[i][1])) for i in range(R)]
-        both = [(lambda i=i: (g5.gemm_fp8_quantize_rows(dX[i], qX[i][0], qX[i][1]),
-                              g5.gemm_fp8_nt(qX[i][0], qX[i][1], qW[i][0], qW[i][1], dC[i], workspace=ws))) for i in range(R)]
-        ms_g = timed(gemm, 50, 10, label="fp8_ffn_e4m3_1024x12288x4096")
-        ms_q = timed(quant, 100, 10, label="fp8_quantize_x_1024x4096")
-        ms_b = timed(both, 50, 10, label="fp8_quantize_and_gemm")
-        fl = 2.0 * M * N * K
-        tf = fl / (ms_g * 1e-3) / 1e12
-        log(f"fp8 FFN: GEMM {ms_g * 1e3:.2f} us ({tf:.1f} TFLOPS, {tf / PEAK_FP8_TFLOPS:.3f} of fp8 peak); "
-            f"quantize X {ms_q * 1e3:.2f} us; both {ms_b * 1e3:.2f} us")
-        workloads.append({"name": "fp8_ffn_e4m3_1024x12288x4096", "us": round(ms_g * 1e3, 3), "tflops": round(tf, 2),
-                          "frac_peak": round(tf / PEAK_FP8_TFLOPS, 4), "peak": PEAK_FP8_TFLOPS,
-                          "quantize_x_us": round(ms_q * 1e3, 3), "quantize_and_gemm_us": round(ms_b * 1e3, 3),
-                          "rotations": R})
-        del dX, qX, dC
-        # decode with the FP8 weight: M rows of X quantized, the GEMV over Wt's codes
-        for Md in (1, 16):
-            Xd, _ = gi.decode_inputs(Md, K, N)
-            alg = N * K + Md * K + 4 * Md + 4 * N + 2 * Md * N        # codes, factors, bf16 C
-            Rd = rotations(alg)
-            qW2 = [qW[i % R] for i in range(Rd)]
-            qXd = [g5.gemm_fp8_quantize_rows(to_dev_bf16(Xd)) for _ in range(Rd)]
-            dCd = [torch.empty((Md, N), dtype=torch.bfloat16, device=dev) for _ in range(Rd)]
-            fns = [(lambda i=i: g5.gemm_fp8_nt(qXd[i][0], qXd[i][1], qW2[i][0], qW2[i][1], dCd[i], workspace=ws)) for i in range(Rd)]
-            ms_d = timed(fns, 200, 10, label=f"fp8_decode_m{Md}_12288x4096")
-            gbps = alg / (ms_d * 1e-3) / 1e9
-            log(f"fp8 decode M={Md}: {ms_d * 1e3:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM)")
-            workloads.append({"name": f"fp8_decode_m{Md}_12288x4096", "us": round(ms_d * 1e3, 3), "GBps": round(gbps, 1),
-                              "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "alg_bytes": alg, "rotations": Rd})
-            del qXd, dCd, qW2
-        del qW
+        with guarded("fp8", workloads):
+            # The FFN projection in E4M3FN: W^T [12288,4096] quantized per output
+            # channel once (weights), X quantized per token on every call, then
+            # the scaled FP8 product into bf16.
+            M, N, K = 1024, 12288, 4096
+            X, W = gi.ffn_inputs()
+            Wt = np.ascontiguousarray(W.T)
+            R = rotations(M * K * 3 + N * K + 2 * M * N)
+            dX = [to_dev_bf16(X) for _ in range(R)]
+            qW = [g5.gemm_fp8_quantize_rows(to_dev_bf16(Wt)) for _ in range(R)]
+            qX = [g5.gemm_fp8_quantize_rows(dX[i]) for i in range(R)]
+            dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+            gemm = [(lambda i=i: g5.gemm_fp8_nt(qX[i][0], qX[i][1], qW[i][0], qW[i][1], dC[i], workspace=ws)) for i in range(R)]
+            quant = [(lambda i=i: g5.gemm_fp8_quantize_rows(dX[i], qX[i][0], qX[i][1])) for i in range(R)]
+            both = [(lambda i=i: (g5.gemm_fp8_quantize_rows(dX[i], qX[i][0], qX[i][1]),
+                                  g5.gemm_fp8_nt(qX[i][0], qX[i][1], qW[i][0], qW[i][1], dC[i], workspace=ws))) for i in range(R)]
+            ms_g = timed(gemm, 50, 10, label="fp8_ffn_e4m3_1024x12288x4096")
+            ms_q = timed(quant, 100, 10, label="fp8_quantize_x_1024x4096")
+            ms_b = timed(both, 50, 10, label="fp8_quantize_and_gemm")
+            fl = 2.0 * M * N * K
+            tf = fl / (ms_g * 1e-3) / 1e12
+            log(f"fp8 FFN: GEMM {ms_g * 1e3:.2f} us ({tf:.1f} TFLOPS, {tf / PEAK_FP8_TFLOPS:.3f} of fp8 peak); "
+                f"quantize X {ms_q * 1e3:.2f} us; both {ms_b * 1e3:.2f} us")
+            workloads.append({"name": "fp8_ffn_e4m3_1024x12288x4096", "us": round(ms_g * 1e3, 3), "tflops": round(tf, 2),
+                              "frac_peak": round(tf / PEAK_FP8_TFLOPS, 4), "peak": PEAK_FP8_TFLOPS,
+                              "quantize_x_us": round(ms_q * 1e3, 3), "quantize_and_gemm_us": round(ms_b * 1e3, 3),
+                              "rotations": R})
+            del dX, qX, dC
+            # decode with the FP8 weight: M rows of X quantized, the GEMV over Wt's codes
+            for Md in (1, 16):
+                Xd, _ = gi.decode_inputs(Md, K, N)
+                alg = N * K + Md * K + 4 * Md + 4 * N + 2 * Md * N        # codes, factors, bf16 C
+                Rd = rotations(alg)
+                qW2 = [qW[i % R] for i in range(Rd)]
+                qXd = [g5.gemm_fp8_quantize_rows(to_dev_bf16(Xd)) for _ in range(Rd)]
+                dCd = [torch.empty((Md, N), dtype=torch.bfloat16, device=dev) for _ in range(Rd)]
+                fns = [(lambda i=i: g5.gemm_fp8_nt(qXd[i][0], qXd[i][1], qW2[i][0], qW2[i][1], dCd[i], workspace=ws)) for i in range(Rd)]
+                ms_d = timed(fns, 200, 10, label=f"fp8_decode_m{Md}_12288x4096")
+                gbps = alg / (ms_d * 1e-3) / 1e9
+                log(f"fp8 decode M={Md}: {ms_d * 1e3:.2f} us/call, {gbps:.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM)")
+                workloads.append({"name": f"fp8_decode_m{Md}_12288x4096", "us": round(ms_d * 1e3, 3), "GBps": round(gbps, 1),
+                                  "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "alg_bytes": alg, "rotations": Rd})
+                del qXd, dCd, qW2
+            del qW
 
     # ------------------------------------------------------------ FP8, Example 5-8's shape
     if args.only in ("all", "fp8_example_5_8"):
-        # A [4096, 4096] (bf16 here, fp16 on the page) quantized per row on
-        # every call, then multiplied by an FP8 weight stored [4096, 1536]
-        # (quantized per output column once, into Bt), 16-bit output: the
-        # separate quantization the page's traffic count favours (444 MiB
-        # with 128x128 tiles, against 620 MiB fused into the GEMM).
-        import ctypes
-        M, N, K = 4096, 1536, 4096
-        g = np.random.default_rng([gi.SEED_BASE + 7400])
-        X = gi.to_bf16_bits(gi.normal(g, (M, K)))
-        W = gi.to_bf16_bits(gi.normal(g, (K, N), 0.125))
-        R = rotations(2 * M * K + M * K + K * N + 2 * M * N)
-        dX = [to_dev_bf16(X) for _ in range(R)]
-        qW = [g5.gemm_fp8_quantize_cols(to_dev_bf16(W)) for _ in range(R)]
-        qX = [g5.gemm_fp8_quantize_rows(dX[i]) for i in range(R)]
-        dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        both = [(lambda i=i: (g5.gemm_fp8_quantize_rows(dX[i], qX[i][0], qX[i][1]),
-                              g5.gemm_fp8_nt(qX[i][0], qX[i][1], qW[i][0], qW[i][1], dC[i], workspace=ws)))
-                for i in range(R)]
-        gemm = [(lambda i=i: g5.gemm_fp8_nt(qX[i][0], qX[i][1], qW[i][0], qW[i][1], dC[i], workspace=ws))
-                for i in range(R)]
-        sxf = [torch.empty((M,), dtype=torch.float32, device=dev) for _ in range(R)]
-        fused = [(lambda i=i: g5.gemm_fp8_nt_quant_a(dX[i], qW[i][0], qW[i][1], dC[i], scale_x=sxf[i],
-                                                     workspace=ws)) for i in range(R)]
-        ms_b = timed(both, 50, 10, label="fp8_example_5_8_quantize_and_gemm")
-        ms_g = timed(gemm, 50, 10, label="fp8_example_5_8_gemm")
-        ms_f = timed(fused, 50, 10, label="fp8_example_5_8_quantized_inside_gemm")
-        sep, fus = ctypes.c_double(), ctypes.c_double()
-        g5.lib().gemm_model_quant_traffic(M, N, K, 128, 128, 2, 1, 1, 2, ctypes.byref(sep), ctypes.byref(fus))
-        tf = 2.0 * M * N * K / (ms_g * 1e-3) / 1e12
-        log(f"fp8 Example 5-8 4096x1536x4096: quantize + GEMM {ms_b * 1e3:.2f} us, GEMM {ms_g * 1e3:.2f} us "
-            f"({tf:.1f} TFLOPS); quantized inside the GEMM {ms_f * 1e3:.2f} us; "
-            f"model traffic separate {sep.value / 2**20:.0f} MiB, fused {fus.value / 2**20:.0f} MiB")
-        workloads.append({"name": "fp8_example_5_8_4096x1536x4096", "us": round(ms_b * 1e3, 3),
-                          "gemm_us": round(ms_g * 1e3, 3), "gemm_tflops": round(tf, 2),
-                          "quantized_inside_gemm_us": round(ms_f * 1e3, 3),
-                          "gemm_frac_peak": round(tf / PEAK_FP8_TFLOPS, 4),
-                          "model_traffic_separate_MiB": round(sep.value / 2**20, 1),
-                          "model_traffic_fused_MiB": round(fus.value / 2**20, 1), "rotations": R})
-        del dX, qW, qX, dC, sxf
+        with guarded("fp8_example_5_8", workloads):
+            # A [4096, 4096] (bf16 here, fp16 on the page) quantized per row on
+            # every call, then multiplied by an FP8 weight stored [4096, 1536]
+            # (quantized per output column once, into Bt), 16-bit output: the
+            # separate quantization the page's traffic count favours (444 MiB
+            # with 128x128 tiles, against 620 MiB fused into the GEMM).
+            import ctypes
+            M, N, K = 4096, 1536, 4096
+            g = np.random.default_rng([gi.SEED_BASE + 7400])
+            X = gi.to_bf16_bits(gi.normal(g, (M, K)))
+            W = gi.to_bf16_bits(gi.normal(g, (K, N), 0.125))
+            R = rotations(2 * M * K + M * K + K * N + 2 * M * N)
+            dX = [to_dev_bf16(X) for _ in range(R)]
+            qW = [g5.gemm_fp8_quantize_cols(to_dev_bf16(W)) for _ in range(R)]
+            qX = [g5.gemm_fp8_quantize_rows(dX[i]) for i in range(R)]
+            dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+            both = [(lambda i=i: (g5.gemm_fp8_quantize_rows(dX[i], qX[i][0], qX[i][1]),
+                                  g5.gemm_fp8_nt(qX[i][0], qX[i][1], qW[i][0], qW[i][1], dC[i], workspace=ws)))
+                    for i in range(R)]
+            gemm = [(lambda i=i: g5.gemm_fp8_nt(qX[i][0], qX[i][1], qW[i][0], qW[i][1], dC[i], workspace=ws))
+                    for i in range(R)]
+            sxf = [torch.empty((M,), dtype=torch.float32, device=dev) for _ in range(R)]
+            fused = [(lambda i=i: g5.gemm_fp8_nt_quant_a(dX[i], qW[i][0], qW[i][1], dC[i], scale_x=sxf[i],
+                                                         workspace=ws)) for i in range(R)]
+            ms_b = timed(both, 50, 10, label="fp8_example_5_8_quantize_and_gemm")
+            ms_g = timed(gemm, 50, 10, label="fp8_example_5_8_gemm")
+            ms_f = timed(fused, 50, 10, label="fp8_example_5_8_quantized_inside_gemm")
+            sep, fus = ctypes.c_double(), ctypes.c_double()
+            g5.lib().gemm_model_quant_traffic(M, N, K, 128, 128, 2, 1, 1, 2, ctypes.byref(sep), ctypes.byref(fus))
+            tf = 2.0 * M * N * K / (ms_g * 1e-3) / 1e12
+            log(f"fp8 Example 5-8 4096x1536x4096: quantize + GEMM {ms_b * 1e3:.2f} us, GEMM {ms_g * 1e3:.2f} us "
+                f"({tf:.1f} TFLOPS); quantized inside the GEMM {ms_f * 1e3:.2f} us; "
+                f"model traffic separate {sep.value / 2**20:.0f} MiB, fused {fus.value / 2**20:.0f} MiB")
+            workloads.append({"name": "fp8_example_5_8_4096x1536x4096", "us": round(ms_b * 1e3, 3),
+                              "gemm_us": round(ms_g * 1e3, 3), "gemm_tflops": round(tf, 2),
+                              "quantized_inside_gemm_us": round(ms_f * 1e3, 3),
+                              "gemm_frac_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                              "model_traffic_separate_MiB": round(sep.value / 2**20, 1),
+                              "model_traffic_fused_MiB": round(fus.value / 2**20, 1), "rotations": R})
+            del dX, qW, qX, dC, sxf
 
     # ------------------------------------------------------------ attention scores from row-major K
     if args.only in ("all", "scores_nt"):
-        Q, KT = gi.batched_inputs()
-        Km = np.ascontiguousarray(np.transpose(KT, (0, 2, 1)))
-        bt, M, K = Q.shape
-        N = Km.shape[1]
-        alg_bytes = 2 * Q.size + 2 * Km.size + 4 * bt * M * N
-        R = rotations(alg_bytes)
-        dQ = [to_dev_bf16(Q) for _ in range(R)]
-        dK = [to_dev_bf16(Km) for _ in range(R)]
-        dC = [torch.empty((bt, M, N), device=dev) for _ in range(R)]
-        fns = [(lambda i=i: g5.gemm_bf16_nt_batched(dQ[i], dK[i], dC[i], workspace=ws)) for i in range(R)]
-        ms = timed(fns, 100, 10, label="scores_nt_bf16_32x1024x1024x128_f32out")
-        gbps = alg_bytes / (ms * 1e-3) / 1e9
-        log(f"scores Q.K^T from row-major K (NT): {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s")
-        workloads.append({"name": "scores_nt_bf16_32x1024x1024x128_f32out", "us": round(ms * 1e3, 3),
-                          "GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "alg_bytes": alg_bytes,
-                          "rotations": R})
-        del dQ, dK, dC
+        with guarded("scores_nt", workloads):
+            Q, KT = gi.batched_inputs()
+            Km = np.ascontiguousarray(np.transpose(KT, (0, 2, 1)))
+            bt, M, K = Q.shape
+            N = Km.shape[1]
+            alg_bytes = 2 * Q.size + 2 * Km.size + 4 * bt * M * N
+            R = rotations(alg_bytes)
+            dQ = [to_dev_bf16(Q) for _ in range(R)]
+            dK = [to_dev_bf16(Km) for _ in range(R)]
+            dC = [torch.empty((bt, M, N), device=dev) for _ in range(R)]
+            fns = [(lambda i=i: g5.gemm_bf16_nt_batched(dQ[i], dK[i], dC[i], workspace=ws)) for i in range(R)]
+            ms = timed(fns, 100, 10, label="scores_nt_bf16_32x1024x1024x128_f32out")
+            gbps = alg_bytes / (ms * 1e-3) / 1e9
+            log(f"scores Q.K^T from row-major K (NT): {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s")
+            workloads.append({"name": "scores_nt_bf16_32x1024x1024x128_f32out", "us": round(ms * 1e3, 3),
+                              "GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4), "alg_bytes": alg_bytes,
+                              "rotations": R})
+            del dQ, dK, dC
 
     # ------------------------------------------------------------ FFN projection with bias and residual
     if args.only in ("all", "affine"):
-        # C := X.W + bias + C (beta = 1: a residual add into the bf16 output),
-        # against the plain projection on the same buffers.
-        M, N, K = 1024, 12288, 4096
-        X, W = gi.ffn_inputs()
-        g = np.random.default_rng([gi.SEED_BASE + gi.W_FFN, 6])
-        bias = gi.to_bf16_bits(gi.normal(g, (N,)))
-        R = rotations(2 * (M * K + K * N + 2 * M * N))
-        dX = [to_dev_bf16(X) for _ in range(R)]
-        dW = [to_dev_bf16(W) for _ in range(R)]
-        db = [to_dev_bf16(bias) for _ in range(R)]
-        dC = [torch.zeros((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        fns = [(lambda i=i: g5.gemm_bf16_affine(dX[i], dW[i], dC[i], bias=db[i], beta=1.0, workspace=ws)) for i in range(R)]
-        plain = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
-        ms = timed(fns, 50, 10, label="ffn_bias_residual_bf16_1024x12288x4096")
-        ms_plain = timed(plain, 50, 10, label="ffn_plain_same_buffers")
-        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-        log(f"FFN + bias + residual: {ms * 1e3:.2f} us ({tf:.1f} TFLOPS); plain projection {ms_plain * 1e3:.2f} us")
-        workloads.append({"name": "ffn_bias_residual_bf16_1024x12288x4096", "us": round(ms * 1e3, 3),
-                          "tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                          "plain_projection_us": round(ms_plain * 1e3, 3), "rotations": R})
-        del dX, dW, db, dC
+        with guarded("affine", workloads):
+            # C := X.W + bias + C (beta = 1: a residual add into the bf16 output),
+            # against the plain projection on the same buffers.
+            M, N, K = 1024, 12288, 4096
+            X, W = gi.ffn_inputs()
+            g = np.random.default_rng([gi.SEED_BASE + gi.W_FFN, 6])
+            bias = gi.to_bf16_bits(gi.normal(g, (N,)))
+            R = rotations(2 * (M * K + K * N + 2 * M * N))
+            dX = [to_dev_bf16(X) for _ in range(R)]
+            dW = [to_dev_bf16(W) for _ in range(R)]
+            db = [to_dev_bf16(bias) for _ in range(R)]
+            dC = [torch.zeros((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+            fns = [(lambda i=i: g5.gemm_bf16_affine(dX[i], dW[i], dC[i], bias=db[i], beta=1.0, workspace=ws)) for i in range(R)]
+            plain = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
+            ms = timed(fns, 50, 10, label="ffn_bias_residual_bf16_1024x12288x4096")
+            ms_plain = timed(plain, 50, 10, label="ffn_plain_same_buffers")
+            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            log(f"FFN + bias + residual: {ms * 1e3:.2f} us ({tf:.1f} TFLOPS); plain projection {ms_plain * 1e3:.2f} us")
+            workloads.append({"name": "ffn_bias_residual_bf16_1024x12288x4096", "us": round(ms * 1e3, 3),
+                              "tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                              "plain_projection_us": round(ms_plain * 1e3, 3), "rotations": R})
+            del dX, dW, db, dC
 
     # ------------------------------------------------------------ linear layer: weight [out, in] and bias (NT)
     if args.only in ("all", "linear_nt"):
-        # y = X . W^T + b with W stored [12288, 4096] as a linear layer keeps
-        # it, bf16 out, next to the same product without the bias.
-        M, N, K = 1024, 12288, 4096
-        X, W = gi.ffn_inputs()
-        Wt = np.ascontiguousarray(W.T)
-        g = np.random.default_rng([gi.SEED_BASE + gi.W_FFN, 7])
-        bias = gi.to_bf16_bits(gi.normal(g, (N,)))
-        R = rotations(2 * (M * K + K * N + M * N))
-        dX = [to_dev_bf16(X) for _ in range(R)]
-        dW = [to_dev_bf16(Wt) for _ in range(R)]
-        db = [to_dev_bf16(bias) for _ in range(R)]
-        dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        fns = [(lambda i=i: g5.gemm_bf16_nt_affine(dX[i], dW[i], dC[i], bias=db[i], workspace=ws)) for i in range(R)]
-        plain = [(lambda i=i: g5.gemm_bf16_nt(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
-        ms = timed(fns, 50, 10, label="linear_nt_bias_bf16_1024x12288x4096")
-        ms_plain = timed(plain, 50, 10, label="linear_nt_without_bias")
-        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-        log(f"linear layer X.W^T + b (W [12288,4096]): {ms * 1e3:.2f} us ({tf:.1f} TFLOPS); "
-            f"without bias {ms_plain * 1e3:.2f} us")
-        workloads.append({"name": "linear_nt_bias_bf16_1024x12288x4096", "us": round(ms * 1e3, 3),
-                          "tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                          "without_bias_us": round(ms_plain * 1e3, 3), "rotations": R})
-        del dX, dW, db, dC
+        with guarded("linear_nt", workloads):
+            # y = X . W^T + b with W stored [12288, 4096] as a linear layer keeps
+            # it, bf16 out, next to the same product without the bias.
+            M, N, K = 1024, 12288, 4096
+            X, W = gi.ffn_inputs()
+            Wt = np.ascontiguousarray(W.T)
+            g = np.random.default_rng([gi.SEED_BASE + gi.W_FFN, 7])
+            bias = gi.to_bf16_bits(gi.normal(g, (N,)))
+            R = rotations(2 * (M * K + K * N + M * N))
+            dX = [to_dev_bf16(X) for _ in range(R)]
+            dW = [to_dev_bf16(Wt) for _ in range(R)]
+            db = [to_dev_bf16(bias) for _ in range(R)]
+            dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+            fns = [(lambda i=i: g5.gemm_bf16_nt_affine(dX[i], dW[i], dC[i], bias=db[i], workspace=ws)) for i in range(R)]
+            plain = [(lambda i=i: g5.gemm_bf16_nt(dX[i], dW[i], dC[i], workspace=ws)) for i in range(R)]
+            ms = timed(fns, 50, 10, label="linear_nt_bias_bf16_1024x12288x4096")
+            ms_plain = timed(plain, 50, 10, label="linear_nt_without_bias")
+            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            log(f"linear layer X.W^T + b (W [12288,4096]): {ms * 1e3:.2f} us ({tf:.1f} TFLOPS); "
+                f"without bias {ms_plain * 1e3:.2f} us")
+            workloads.append({"name": "linear_nt_bias_bf16_1024x12288x4096", "us": round(ms * 1e3, 3),
+                              "tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                              "without_bias_us": round(ms_plain * 1e3, 3), "rotations": R})
+            del dX, dW, db, dC
 
     # ------------------------------------------------------------ weight gradient from row-major X (TN)
     if args.only in ("all", "wgrad_tn"):
-        # dW [4096, 12288] = X^T . dY with X [1024, 4096] as stored (At) and
-        # dY [1024, 12288]: 103 GFLOP over K = 1024 tokens.
-        X, dY = gi.wgrad_inputs()
-        K, M = X.shape
-        N = dY.shape[1]
-        R = rotations(2 * (M * K + K * N + M * N))
-        dX = [to_dev_bf16(X) for _ in range(R)]
-        dD = [to_dev_bf16(dY) for _ in range(R)]
-        dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
-        fns = [(lambda i=i: g5.gemm_bf16_tn(dX[i], dD[i], dC[i], workspace=ws)) for i in range(R)]
-        st, plan = g5.plan_query(g5.GEMM_OP_BF16_TN, M, N, K)
-        ms = timed(fns, 50, 10, label="wgrad_tn_bf16_4096x12288x1024")
-        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
-        log(f"weight gradient X^T.dY 4096x12288x1024 (TN): {ms * 1e3:.2f} us ({tf:.1f} TFLOPS), {plan.name.decode()}")
-        workloads.append({"name": "wgrad_tn_bf16_4096x12288x1024", "us": round(ms * 1e3, 3), "tflops": round(tf, 2),
-                          "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "config": plan.name.decode(),
-                          "rotations": R})
-        del dX, dD, dC
+        with guarded("wgrad_tn", workloads):
+            # dW [4096, 12288] = X^T . dY with X [1024, 4096] as stored (At) and
+            # dY [1024, 12288]: 103 GFLOP over K = 1024 tokens.
+            X, dY = gi.wgrad_inputs()
+            K, M = X.shape
+            N = dY.shape[1]
+            R = rotations(2 * (M * K + K * N + M * N))
+            dX = [to_dev_bf16(X) for _ in range(R)]
+            dD = [to_dev_bf16(dY) for _ in range(R)]
+            dC = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+            fns = [(lambda i=i: g5.gemm_bf16_tn(dX[i], dD[i], dC[i], workspace=ws)) for i in range(R)]
+            st, plan = g5.plan_query(g5.GEMM_OP_BF16_TN, M, N, K)
+            ms = timed(fns, 50, 10, label="wgrad_tn_bf16_4096x12288x1024")
+            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            log(f"weight gradient X^T.dY 4096x12288x1024 (TN): {ms * 1e3:.2f} us ({tf:.1f} TFLOPS), {plan.name.decode()}")
+            workloads.append({"name": "wgrad_tn_bf16_4096x12288x1024", "us": round(ms * 1e3, 3), "tflops": round(tf, 2),
+                              "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4), "config": plan.name.decode(),
+                              "rotations": R})
+            del dX, dD, dC
 
     out["workloads"] = workloads
     out["workload_timing"] = timings
