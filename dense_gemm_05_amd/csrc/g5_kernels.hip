@@ -602,8 +602,10 @@ __global__ void __launch_bounds__(NW * 64, 1) k_decode(GemmArgs p)
 //    load instruction covering 4 rows x 256 contiguous bytes; an 8x8
 //    transpose of 16-bit halves in registers feeds 8 matrix-core blocks
 //    whose logical column r is physical column 8r + c.
-//  * Slices are combined without atomics on data: every workgroup writes
-//    its partial sums to the workspace with device-scope stores, waits until
+//  * Counter path (more than two members, or outputs that do not fit the
+//    exchange slots): slices are combined without atomics on data: every
+//    workgroup writes its partial sums to the workspace with device-scope
+//    stores, waits until
 //    they have completed, and then one thread adds 1 to the strip's counter
 //    (device-scope atomic).  The workgroup that brings the counter to KS
 //    reads the KS partials with device-scope loads and adds them in slice
