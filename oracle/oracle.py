@@ -5,6 +5,7 @@ rounding); this module only builds it with gcc, loads it and marshals numpy
 arrays.  Nothing here imports the GPU package.
 """
 import ctypes
+import math
 import os
 import subprocess
 
@@ -59,6 +60,8 @@ def _load():
     lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
     lib.oracle_e4m3_encode.restype = ctypes.c_uint8
     lib.oracle_e4m3_encode_array.argtypes = [i64, p, p]
+    lib.oracle_quantize_fixed_e4m3.argtypes = [i64, p, ctypes.c_float, p]
+    lib.oracle_quantize_fixed_e4m3.restype = None
     lib.oracle_quantize_rows_e4m3.argtypes = [i64, i64, p, i64, p, i64, p]
     lib.oracle_gemm_fp8_nt.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, p, i64]
     lib.oracle_gemm_fp8_nt_affine.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, ctypes.c_double, p,
@@ -239,6 +242,25 @@ def e4m3_encode(x):
     out = np.empty(x.shape, np.uint8)
     _load().oracle_e4m3_encode_array(x.size, x.ctypes.data, out.ctypes.data)
     return out
+
+
+def quantize_fixed_e4m3(v, amax):
+    """Fixed-range E4M3FN codes of exact products v (doubles): the value
+    nearest to fl32(fl32(fl32(v) * 448) / amax), saturating at 448."""
+    amax = float(np.float32(amax))
+    if not (math.isfinite(amax) and amax > 0):
+        raise ValueError("amax must be finite and positive")
+    v = np.ascontiguousarray(np.asarray(v, np.float64))
+    out = np.empty(v.shape, np.uint8)
+    _load().oracle_quantize_fixed_e4m3(v.size, v.ctypes.data, amax, out.ctypes.data)
+    return out
+
+
+def swiglu_e4m3(X, Wgu, amax):
+    """SwiGLU on a merged [K, 2N] weight with its output quantized to E4M3FN
+    codes against the fixed range amax (uint8 [M, N])."""
+    Z, _, _, _ = swiglu_bf16(X, Wgu)
+    return quantize_fixed_e4m3(Z, amax)
 
 
 def quantize_rows_e4m3(X):

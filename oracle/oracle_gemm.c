@@ -318,6 +318,40 @@ void oracle_e4m3_encode_array(int64_t n, const double *x, uint8_t *out)
     for (int64_t i = 0; i < n; ++i) out[i] = e4m3_encode(x[i]);
 }
 
+/* Nearest binary32 value of x (ties to even), overflow to +-infinity: the
+ * rounding of one binary32 operation whose exact result is x. */
+static float rn_f32(double x)
+{
+    if (x != x) return (float)x;
+    /* 2^128 - 2^103 is the midpoint between FLT_MAX and 2^128; from there on
+     * binary32 rounding overflows */
+    if (fabs(x) >= ldexp(1.0, 128) - ldexp(1.0, 103)) return x > 0 ? INFINITY : -INFINITY;
+    return (float)x;
+}
+
+/* Fixed-range E4M3FN quantization of the SwiGLU output, page "Operator &
+ * Runtime" §5.3.1 (Example 5-4 carried on: Z is stored with one fixed scale
+ * factor, one byte per element).  The range amax (finite, > 0) maps to the
+ * format's largest finite value 448, as in the per-row quantizer of §5.4.3,
+ * and the factor that undoes it is amax / 448.  The page leaves the
+ * precision of that quotient open; it is taken in binary32, the precision of
+ * the output tile it is fused into: z = fl(t * u) (the product of the two
+ * bf16 factors, exact unless it leaves the binary32 range), p = fl(z * 448),
+ * y = fl(p / amax), each correctly rounded, and the code is the E4M3FN value
+ * nearest to y (ties to the even mantissa, beyond +-448 saturating to
+ * +-448, NaN to 0x7f).  v holds the exact products t * u in double; the
+ * double quotient rounded to binary32 equals the binary32 quotient (53 >=
+ * 2 * 24 + 2: rounding twice is innocuous for a division). */
+void oracle_quantize_fixed_e4m3(int64_t n, const double *v, float amax, uint8_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        const float z = rn_f32(v[i]);
+        const float p = rn_f32((double)z * 448.0);
+        const float y = rn_f32((double)p / (double)amax);
+        out[i] = e4m3_encode((double)y);
+    }
+}
+
 /* Per-row E4M3FN quantization of bf16 rows X [rows, cols] into codes Q
  * (row stride ldq) and dequantization factors scale[rows], as page
  * "Operator & Runtime" defines it (§5.4.3, Example 5-7): the row's largest

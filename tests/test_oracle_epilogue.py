@@ -10,6 +10,7 @@ prints, identities of SiLU, exact integer products, the bit-level bf16
 rounding already pinned in test_oracle.py, and hand-worked bf16 values.
 """
 import math
+from fractions import Fraction
 import os
 
 import numpy as np
@@ -162,6 +163,96 @@ def test_swiglu_matches_its_parts(oracle_mod):
     T = oracle_mod.round_bf16_value(oracle_mod.silu(G))
     assert np.array_equal(gg, G) and np.array_equal(uu, U) and np.array_equal(tt, T)
     assert np.array_equal(Z, T * U)
+
+
+def _e4m3_mags(oracle_mod):
+    return [Fraction(float(v)) for v in oracle_mod.e4m3_decode(np.arange(127, dtype=np.uint8))]
+
+
+def _nearest_code_of(y, mags):
+    """Nearest E4M3FN code of the binary32 value y by brute force over the
+    127 magnitudes in rational arithmetic, ties to the even code, beyond 448
+    saturating."""
+    q = min(abs(Fraction(float(y))), mags[-1])
+    best = min(range(len(mags)), key=lambda c: (abs(q - mags[c]), c % 2))
+    return (0x80 if math.copysign(1.0, float(y)) < 0 else 0x00) | best
+
+
+def _fixed_quotient_f32(z, amax):
+    """The binary32 steps of the fixed-range quantization, in numpy float32
+    arithmetic (IEEE, correctly rounded): fl(fl(fl(z) * 448) / amax)."""
+    with np.errstate(over="ignore"):
+        return (np.float32(z) * np.float32(448.0)) / np.float32(amax)
+
+
+def test_swiglu_e4m3_codes_brute_force(oracle_mod):
+    """Section 5.3.1 quantizes Z = SiLU(G) (.) U with one fixed scale: each
+    code is the E4M3FN value nearest to the binary32 quotient z * 448 / amax
+    (z the product of the bf16 factors).  Checked element by element against
+    numpy's float32 arithmetic and a brute-force rational nearest-value
+    search, for a range that saturates a fifth of the outputs and for one
+    that saturates none (both a bf16 value and a general binary32 value)."""
+    mags = _e4m3_mags(oracle_mod)
+    g = np.random.default_rng(31)
+    X = bits(g.standard_normal((7, 48)))
+    W = _merged(bits(g.standard_normal((48, 9)) * 0.25), bits(g.standard_normal((48, 9)) * 0.25))
+    Z, gg, uu, tt = oracle_mod.swiglu_bf16(X, W)
+    top = float(np.abs(Z).max())
+    for amax in (np.float32(np.quantile(np.abs(Z), 0.8)), np.float32(top * 1.0001), np.float32(0.75)):
+        Q = oracle_mod.swiglu_e4m3(X, W, amax)
+        for (i, j), z in np.ndenumerate(tt * uu):
+            assert int(Q[i, j]) == _nearest_code_of(_fixed_quotient_f32(z, amax), mags), (amax, i, j)
+    sat = oracle_mod.swiglu_e4m3(X, W, np.float32(np.quantile(np.abs(Z), 0.8)))
+    assert 0.1 < np.mean((sat & 0x7f) == 0x7e) < 0.3
+
+
+def test_swiglu_e4m3_closed_forms(oracle_mod):
+    """With amax = 448 the quotient is z itself: z = t * u on an E4M3FN value
+    keeps it exactly, z on a midpoint goes to the even neighbour, z beyond
+    448 saturates, and a zero gate (SiLU(0) = 0) or -0 gives the signed zero
+    code.  g >= 17 keeps t = g (SiLU(g) rounds to g in bf16)."""
+    d = lambda c: float(oracle_mod.e4m3_decode([c])[0])
+    # gate 32, up u: z = 32 u
+    ups = [0.25, 1.5 / 32, -3.0 / 32, 1.0625 / 32, 1.1875 / 32, 500.0 / 32, -480.0 / 32, 0.0]
+    X = bits([[1.0]])
+    Wg = bits([[32.0] * len(ups)]); Wu = bits([ups])
+    Q = oracle_mod.swiglu_e4m3(X, _merged(Wg, Wu), 448.0)[0]
+    assert [d(c) for c in Q[:3]] == [8.0, 1.5, -3.0]           # exact E4M3FN values
+    assert d(Q[3]) == 1.0 and d(Q[4]) == 1.25                  # ties: 1.0625 -> 1.0, 1.1875 -> 1.25 (even)
+    assert Q[5] == 0x7e and Q[6] == 0xfe                       # +-448
+    assert Q[7] == 0x00
+    Qz = oracle_mod.swiglu_e4m3(bits([[1.0]]), _merged(bits([[0.0]]), bits([[-5.0]])), 1.0)
+    assert Qz[0, 0] == 0x80                                    # 0 * -5 = -0
+    # the range scales the quotient: amax = 4 * 448 divides z by 4
+    Q4 = oracle_mod.swiglu_e4m3(X, _merged(Wg, Wu), 4 * 448.0)[0]
+    assert [d(c) for c in Q4[:3]] == [2.0, 0.375, -0.75]
+
+
+def test_swiglu_e4m3_decision_in_binary32(oracle_mod):
+    """The page leaves the quotient's precision open; the oracle takes it in
+    binary32.  For a range amax that is no bf16 value, the exact quotient can
+    lie just above a midpoint while its binary32 rounding lands on it: the
+    oracle then takes the even neighbour, as the binary32 quotient says, not
+    the odd one the exact quotient is nearer to.  Such pairs are found by
+    search and checked in rational arithmetic."""
+    mags = _e4m3_mags(oracle_mod)
+    found = 0
+    X = bits([[1.0]])
+    for mid_lo in range(40, 100):                              # midpoints between codes c and c + 1
+        m = (mags[mid_lo] + mags[mid_lo + 1]) / 2
+        z = 17.0 * float(np.float32(mags[mid_lo]))             # z = 17 v, exact in bf16 * bf16
+        a0 = np.float32(float(Fraction(z) * 448 / m))
+        for amax in (a0, np.nextafter(a0, np.float32(0)), np.nextafter(a0, np.float32(1e30))):
+            exact = Fraction(z) * 448 / Fraction(float(amax))
+            y = _fixed_quotient_f32(z, amax)
+            if Fraction(float(y)) != m or exact == m:
+                continue
+            Q = oracle_mod.swiglu_e4m3(X, _merged(bits([[17.0]]), bits([[float(mags[mid_lo])]])), amax)
+            even = mid_lo if mid_lo % 2 == 0 else mid_lo + 1
+            nearer = mid_lo + 1 if exact > m else mid_lo
+            assert int(Q[0, 0]) == even
+            found += even != nearer
+    assert found >= 1                                          # the pin separates the two readings
 
 
 # ---------------------------------------------------------------- affine epilogue
