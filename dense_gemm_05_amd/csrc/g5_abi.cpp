@@ -53,6 +53,8 @@ struct Problem {
     // affine epilogue: C := alpha * (A.B) + bias[n] + beta * C
     float alpha = 1.0f, beta = 0.0f;
     uint64_t bias = 0;                   // bf16 [N], 0 = none
+    // SwiGLU with c_type GEMM_OUT_E4M3: the fixed range that maps to 448
+    float out_amax = 0.0f;
 };
 
 struct Plan {
@@ -104,6 +106,15 @@ int epi_of(const Problem &p)
                : EPI_NONE;
 }
 bool is_affine(const Problem &p) { return epi_of(p) == EPI_AFFINE; }
+// The output type of the generic entry points: FP32 for SGEMM, bf16 for
+// SiLU, bf16 or (when asked for) E4M3FN codes for SwiGLU, else the caller's.
+int op_c_type(int op, int c_type)
+{
+    if (op == GEMM_OP_SGEMM) return GEMM_OUT_F32;
+    if (op == GEMM_OP_BF16_SILU) return GEMM_OUT_BF16;
+    if (op == GEMM_OP_BF16_SWIGLU) return c_type == GEMM_OUT_E4M3 ? GEMM_OUT_E4M3 : GEMM_OUT_BF16;
+    return c_type;
+}
 // An affine call with no product to form (alpha == 0: A and B are not read).
 bool no_product(const Problem &p) { return is_affine(p) && p.alpha == 0.0f; }
 // B is given transposed, Bt [N, K].
@@ -129,7 +140,10 @@ int64_t out_tile_n(const Problem &p, const ConfigInfo &c)
 {
     return p.op == GEMM_OP_BF16_SWIGLU ? c.tile_n / 2 : c.tile_n;
 }
-int elem_c(const Problem &p) { return (p.op == GEMM_OP_SGEMM || p.c_type == GEMM_OUT_F32) ? 4 : 2; }
+int elem_c(const Problem &p)
+{
+    return p.c_type == GEMM_OUT_E4M3 ? 1 : (p.op == GEMM_OP_SGEMM || p.c_type == GEMM_OUT_F32) ? 4 : 2;
+}
 
 // Largest power of two <= 16 dividing the address of every row start of an
 // operand (pointer, row stride and batch stride all in bytes).
@@ -165,7 +179,10 @@ int validate(const Problem &p)
         p.c_type != GEMM_OUT_BF16 && p.c_type != GEMM_OUT_F32)
         return GEMM_ERR_INVALID_ARG;
     if (is_fp8(p) && ((p.scale_a % 4) || (p.scale_b % 4))) return GEMM_ERR_INVALID_ARG;
-    if ((p.op == GEMM_OP_BF16_SILU || p.op == GEMM_OP_BF16_SWIGLU) && p.c_type != GEMM_OUT_BF16)
+    if (p.op == GEMM_OP_BF16_SILU && p.c_type != GEMM_OUT_BF16) return GEMM_ERR_INVALID_ARG;
+    // SwiGLU writes bf16, or E4M3FN codes against a finite positive range
+    if (p.op == GEMM_OP_BF16_SWIGLU && p.c_type != GEMM_OUT_BF16 &&
+        (p.c_type != GEMM_OUT_E4M3 || !std::isfinite(p.out_amax) || !(p.out_amax > 0.0f)))
         return GEMM_ERR_INVALID_ARG;
     if (is_affine(p) && (!std::isfinite(p.alpha) || !std::isfinite(p.beta) || (p.bias % 2)))
         return GEMM_ERR_INVALID_ARG;
@@ -794,6 +811,8 @@ int run(const Problem &p, void *stream, void *ws = nullptr, size_t ws_bytes = 0)
     a.affine = is_affine(p) ? 1 : 0;
     a.a_trans = a_trans(p) ? 1 : 0;
     a.epi = epi_of(p);
+    a.c_e4m3 = p.c_type == GEMM_OUT_E4M3 ? 1 : 0;
+    a.c_amax = p.out_amax;
     if (pl.realign_b) {
         uint16_t *B2 = (uint16_t *)(wsb + L.rows_b);
         const hipError_t e = launch_realign_rows((const uint16_t *)p.b, p.ldb, p.sB, p.batch, p.N, p.K,
@@ -1065,6 +1084,15 @@ int gemm_bf16_swiglu(int64_t M, int64_t N, int64_t K, const uint16_t *X, int64_t
     return g5::run(p, stream);
 }
 
+int gemm_bf16_swiglu_e4m3(int64_t M, int64_t N, int64_t K, const uint16_t *X, int64_t ldx, const uint16_t *Wgu,
+                          int64_t ldw, uint8_t *Zq, int64_t ldz, float amax, void *stream)
+{
+    Problem p{GEMM_OP_BF16_SWIGLU, 1, M, N, K, (uint64_t)X, (uint64_t)Wgu, (uint64_t)Zq, ldx, ldw, ldz, 0, 0,
+              0, GEMM_OUT_E4M3};
+    p.out_amax = amax;
+    return g5::run(p, stream);
+}
+
 int gemm_bf16_silu_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
                            int64_t strideA, const uint16_t *B, int64_t ldb, int64_t strideB, uint16_t *C, int64_t ldc,
                            int64_t strideC, void *stream)
@@ -1080,6 +1108,16 @@ int gemm_bf16_swiglu_batched(int64_t batch, int64_t M, int64_t N, int64_t K, con
 {
     const Problem p{GEMM_OP_BF16_SWIGLU, batch, M, N, K, (uint64_t)X, (uint64_t)Wgu, (uint64_t)Z, ldx, ldw, ldz,
                     strideX, strideW, strideZ, GEMM_OUT_BF16};
+    return g5::run(p, stream);
+}
+
+int gemm_bf16_swiglu_e4m3_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const uint16_t *X, int64_t ldx,
+                                  int64_t strideX, const uint16_t *Wgu, int64_t ldw, int64_t strideW, uint8_t *Zq,
+                                  int64_t ldz, int64_t strideZ, float amax, void *stream)
+{
+    Problem p{GEMM_OP_BF16_SWIGLU, batch, M, N, K, (uint64_t)X, (uint64_t)Wgu, (uint64_t)Zq, ldx, ldw, ldz,
+              strideX, strideW, strideZ, GEMM_OUT_E4M3};
+    p.out_amax = amax;
     return g5::run(p, stream);
 }
 
@@ -1157,10 +1195,9 @@ static int plan_query_impl(int with_workspace, int op, int64_t batch, int64_t M,
                            int64_t strideB, uint64_t c_addr, int64_t ldc, int64_t strideC, int c_type,
                            gemm_plan *out)
 {
-    const Problem p{op, batch, M, N, K, a_addr, b_addr, c_addr, lda, ldb, ldc, strideA, strideB, strideC,
-                    op == GEMM_OP_SGEMM ? (int)GEMM_OUT_F32
-                    : (op == GEMM_OP_BF16_SILU || op == GEMM_OP_BF16_SWIGLU) ? (int)GEMM_OUT_BF16
-                                                                              : c_type};
+    Problem p{op, batch, M, N, K, a_addr, b_addr, c_addr, lda, ldb, ldc, strideA, strideB, strideC,
+              g5::op_c_type(op, c_type)};
+    if (p.c_type == GEMM_OUT_E4M3) p.out_amax = 1.0f;   // (the range does not change the plan)
     int st = g5::validate(p);
     if (st != GEMM_OK) return st;
     g5::Plan pl;
@@ -1203,9 +1240,8 @@ static g5::Problem run_problem(int op, int64_t batch, int64_t M, int64_t N, int6
                                const float *scale_a, const float *scale_b)
 {
     Problem p{op, batch, M, N, K, (uint64_t)A, (uint64_t)B, (uint64_t)C, lda, ldb, ldc, strideA, strideB, strideC,
-              op == GEMM_OP_SGEMM ? (int)GEMM_OUT_F32
-              : (op == GEMM_OP_BF16_SILU || op == GEMM_OP_BF16_SWIGLU) ? (int)GEMM_OUT_BF16
-                                                                        : c_type};
+              g5::op_c_type(op, c_type)};
+    if (p.c_type == GEMM_OUT_E4M3) p.out_amax = alpha;   // SwiGLU's fixed range
     if (op == GEMM_OP_FP8_NT || op == GEMM_OP_FP8_NT_AFFINE) {
         p.scale_a = (uint64_t)scale_a;
         p.scale_b = (uint64_t)scale_b;

@@ -106,6 +106,11 @@ struct GemmArgs {
     // the merged gate|up weight [K, 2N] (gate columns [0, N), up columns
     // [N, 2N)) and C the N columns of bf16(bf16(SiLU(g)) * u).
     int32_t epi;
+    // EPI_SWIGLU with c_e4m3 = 1: C holds one E4M3FN code per output (bytes,
+    // ldc and sC in bytes), the code nearest to z * 448 / c_amax for the
+    // product z = t * u (c_amax: the caller's fixed range, finite and > 0).
+    int32_t c_e4m3 = 0;
+    float c_amax = 0.f;
 };
 
 // Fused epilogues of the bf16 ring kernels.

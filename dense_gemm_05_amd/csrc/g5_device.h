@@ -102,6 +102,20 @@ struct E4m3Quot {
     }
 };
 
+// Fixed-range E4M3FN code of one SwiGLU output z = t * u (page "Operator &
+// Runtime" §5.3.1 stores Z with one fixed scale factor, a byte per element):
+// the code nearest to the binary32 quotient fl(fl(z * 448) / amax), taken
+// with the correctly rounded division (z carries up to 16 significant bits,
+// beyond the bf16 numerators the fast quotient above was checked for),
+// clamped to +-448 before the conversion; NaN gives 0x7f.  amax > 0.
+__device__ __forceinline__ uint32_t e4m3_fixed_code(float z, float amax)
+{
+    float y = __fdiv_rn(z * 448.0f, amax);
+    y = y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xffu;
+    return y != y ? 0x7fu : c;
+}
+
 // Fused epilogues of a bf16 output chunk (8 values, already rounded once to
 // bf16 from the FP32 sums: the rounding of the unfused program survives,
 // §5.4.3).  SiLU: y = bf16(SiLU(g)).  SwiGLU (§5.3.1): z = bf16(t * u) with
@@ -122,6 +136,20 @@ __device__ __forceinline__ u32x4 epi_swiglu8(u32x4 g, u32x4 u)
     for (int i = 0; i < 4; ++i)
         z[i] = pack_bf16x2(bf16_lo(t[i]) * bf16_lo(u[i]), bf16_hi(t[i]) * bf16_hi(u[i]));
     return z;
+}
+// The same 8 outputs as fixed-range E4M3FN codes (4 per word, the lowest
+// column in the lowest byte).
+__device__ __forceinline__ u32x2 epi_swiglu8_e4m3(u32x4 g, u32x4 u, float amax)
+{
+    const u32x4 t = epi_silu8(g);
+    u32x2 q = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = e4m3_fixed_code(bf16_lo(t[i]) * bf16_lo(u[i]), amax);
+        const uint32_t hi = e4m3_fixed_code(bf16_hi(t[i]) * bf16_hi(u[i]), amax);
+        q[i / 2] |= (lo | (hi << 8)) << (16 * (i % 2));
+    }
+    return q;
 }
 
 // One output element of the small-M kernels: the FP32 sum of batch entry
@@ -154,7 +182,9 @@ __device__ __forceinline__ void store_swiglu(const GemmArgs &p, int64_t b, int64
 {
     const float t = __uint_as_float(bf16_rne(silu_f32(__uint_as_float(bf16_rne(g) << 16))) << 16);
     const float ub = __uint_as_float(bf16_rne(u) << 16);
-    ((uint16_t *)p.C)[b * p.sC + m * p.ldc + n] = (uint16_t)bf16_rne(t * ub);
+    const int64_t off = b * p.sC + m * p.ldc + n;
+    if (p.c_e4m3) ((uint8_t *)p.C)[off] = (uint8_t)e4m3_fixed_code(t * ub, p.c_amax);
+    else ((uint16_t *)p.C)[off] = (uint16_t)bf16_rne(t * ub);
 }
 
 // Load 8 consecutive bf16 elements (one 16-byte chunk) starting at element
@@ -423,14 +453,27 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
         if constexpr (EPI == EPI_SWIGLU) {
             // Tile columns [0, BN/2) hold the gate product g, [BN/2, BN) the
             // up product u of the same BN/2 output columns starting at n0.
+            // Fixed-range E4M3FN output (pa->c_e4m3): 8 codes, 8 bytes, per chunk.
             constexpr int OPR = CPR / 2;                     // output chunks per row
-            for (int q = tid; q < RP * OPR; q += NT) {
-                const int r = q / OPR, c = q % OPR;
-                if (MASKED && (m0 + pass * RP + r >= M || n0 + (int64_t)(c + 1) * 8 > N)) continue;
-                const u32x4 g = *(const u32x4 *)(L + r * PITCH + c * 16);
-                const u32x4 u = *(const u32x4 *)(L + r * PITCH + (c + OPR) * 16);
-                char *dst = (char *)Cb + ((m0 + pass * RP + r) * ldc + n0) * 2 + c * 16;
-                __builtin_nontemporal_store(epi_swiglu8(g, u), (u32x4 *)dst);
+            if (pa->c_e4m3) {
+                const float amax = pa->c_amax;
+                for (int q = tid; q < RP * OPR; q += NT) {
+                    const int r = q / OPR, c = q % OPR;
+                    if (MASKED && (m0 + pass * RP + r >= M || n0 + (int64_t)(c + 1) * 8 > N)) continue;
+                    const u32x4 g = *(const u32x4 *)(L + r * PITCH + c * 16);
+                    const u32x4 u = *(const u32x4 *)(L + r * PITCH + (c + OPR) * 16);
+                    char *dst = (char *)Cb + (m0 + pass * RP + r) * ldc + n0 + c * 8;
+                    __builtin_nontemporal_store(epi_swiglu8_e4m3(g, u, amax), (u32x2 *)dst);
+                }
+            } else {
+                for (int q = tid; q < RP * OPR; q += NT) {
+                    const int r = q / OPR, c = q % OPR;
+                    if (MASKED && (m0 + pass * RP + r >= M || n0 + (int64_t)(c + 1) * 8 > N)) continue;
+                    const u32x4 g = *(const u32x4 *)(L + r * PITCH + c * 16);
+                    const u32x4 u = *(const u32x4 *)(L + r * PITCH + (c + OPR) * 16);
+                    char *dst = (char *)Cb + ((m0 + pass * RP + r) * ldc + n0) * 2 + c * 16;
+                    __builtin_nontemporal_store(epi_swiglu8(g, u), (u32x4 *)dst);
+                }
             }
         } else if constexpr (EPI == EPI_AFFINE) {
             // 8 columns per step: v = alpha * sum + (bias[n] + beta * C[m][n])
@@ -1047,7 +1090,7 @@ struct RingTile {
         }
     }
 
-    void *Cb = (char *)p.C + tc.b * p.sC * (p.out_f32 ? 4 : 2);
+    void *Cb = (char *)p.C + tc.b * p.sC * (p.c_e4m3 ? 1 : p.out_f32 ? 4 : 2);
     if (p.align_c >= 16 && (!MASKED || N % (p.out_f32 ? 4 : 8) == 0)) {
         // 16-byte aligned rows of C: stage the results through LDS (free
         // once every wave's copies and reads are done) and write whole
@@ -1060,7 +1103,8 @@ struct RingTile {
         if constexpr (EPI == EPI_AFFINE) {
             store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, float, MASKED, EPI>(acc, smem, Cb, p.ldc, m0, n0, M, N, &p);
         } else if constexpr (EPI != EPI_NONE) {
-            store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, uint16_t, MASKED, EPI>(acc, smem, Cb, p.ldc, m0, n0, M, N);
+            store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, uint16_t, MASKED, EPI>(acc, smem, Cb, p.ldc, m0, n0, M, N,
+                                                                                 &p);
         } else {
             if (p.out_f32) store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, float, MASKED>(acc, smem, Cb, p.ldc, m0, n0, M, N);
             else store_tile_via_lds<BM, BN, WGM, WGN, LDS_BYTES, uint16_t, MASKED>(acc, smem, Cb, p.ldc, m0, n0, M, N);

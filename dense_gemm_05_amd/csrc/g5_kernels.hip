@@ -981,12 +981,14 @@ __global__ void __launch_bounds__(256) k_generic(GemmArgs p)
 // chunk element by element; other rows element by element.
 __global__ void __launch_bounds__(256) k_zero(GemmArgs p)
 {
-    const int esz = p.out_f32 ? 4 : 2;
+    // (E4M3FN codes of SwiGLU: the output of zero sums is SiLU(0) * 0 = +0, code 0)
+    const int esz = p.c_e4m3 ? 1 : p.out_f32 ? 4 : 2;
     const int64_t rows = p.batch * p.M;
     const int64_t stride = (int64_t)gridDim.x * 256, first = (int64_t)blockIdx.x * 256 + threadIdx.x;
     auto elem = [&](int64_t r, int64_t n) {
         const int64_t b = r / p.M, m = r % p.M;
-        if (p.out_f32) ((float *)p.C + b * p.sC)[m * p.ldc + n] = 0.f;
+        if (p.c_e4m3) ((uint8_t *)p.C + b * p.sC)[m * p.ldc + n] = 0;
+        else if (p.out_f32) ((float *)p.C + b * p.sC)[m * p.ldc + n] = 0.f;
         else ((uint16_t *)p.C + b * p.sC)[m * p.ldc + n] = 0;
     };
     int64_t done_cols = 0;                              // columns written as chunks

@@ -22,6 +22,7 @@ from ._lib import GEMM_ERR_WORKSPACE, GEMM_WORKSPACE_COUNTER_BYTES, GemmError, G
 __all__ = ["gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm_bf16_nt_batched",
            "gemm_bf16_tn", "gemm_bf16_tn_batched",
            "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_bf16_silu_batched", "gemm_bf16_swiglu_batched",
+           "gemm_bf16_swiglu_e4m3", "gemm_bf16_swiglu_e4m3_batched",
            "gemm_fp8_quantize_rows", "gemm_fp8_quantize_cols", "gemm_fp8_nt", "gemm_fp8_nt_affine",
            "gemm_fp8_nt_quant_a",
            "gemm_bf16_affine",
@@ -584,6 +585,57 @@ def gemm_bf16_swiglu_batched(X, Wgu, Z=None, workspace=None):
                  (batch, M, N, K, X.data_ptr(), ldx, sA, Wgu.data_ptr(), ldw, sB, Z.data_ptr(), ldz, sC), workspace,
                  dev, _lib.GEMM_OP_BF16_SWIGLU, batch, M, N, K, X, ldx, sA, Wgu, ldw, sB, Z, ldz, sC,
                  _lib.GEMM_OUT_BF16)
+
+
+def _swiglu_e4m3_shapes(X, Wgu, Zq, what, batched):
+    if X.dtype != torch.bfloat16 or Wgu.dtype != torch.bfloat16:
+        raise TypeError(f"{what} takes bfloat16 operands")
+    if batched:
+        batch, M, K = X.shape
+        b2, K2, N2 = Wgu.shape
+        ok = batch == b2 and K == K2 and N2 % 2 == 0
+    else:
+        (M, K), (K2, N2), batch = X.shape, Wgu.shape, None
+        ok = K == K2 and N2 % 2 == 0
+    if not ok:
+        raise ValueError(f"{what}: expected X [..., M, K] and Wgu [..., K, 2N]")
+    N = N2 // 2
+    dev = _check_dev(X, Wgu, Zq)
+    shape = (M, N) if batch is None else (batch, M, N)
+    if Zq is None:
+        Zq = torch.empty(shape, dtype=torch.uint8, device=dev)
+    if tuple(Zq.shape) != shape or Zq.dtype != torch.uint8:
+        raise ValueError(f"{what}: Zq must be uint8 {list(shape)}")
+    return batch, M, N, K, N2, dev, Zq
+
+
+def gemm_bf16_swiglu_e4m3(X, Wgu, amax, Zq=None, workspace=None):
+    """SwiGLU of X [M, K] with the merged weight Wgu [K, 2N], stored as
+    E4M3FN codes (uint8 [M, N]) against the fixed range amax: the code
+    nearest to z * 448 / amax, saturating at 448 (gemm_bf16_swiglu_e4m3).
+    The codes dequantize by amax / 448 (``Zq.view(torch.float8_e4m3fn)``
+    reads them as float8)."""
+    _, M, N, K, N2, dev, Zq = _swiglu_e4m3_shapes(X, Wgu, Zq, "gemm_bf16_swiglu_e4m3", False)
+    ldx, ldw, ldz = _ld(X, K), _ld(Wgu, N2), _ld(Zq, N)
+    amax = float(amax)
+    return _gemm("gemm_bf16_swiglu_e4m3", "gemm_bf16_swiglu_e4m3",
+                 (M, N, K, X.data_ptr(), ldx, Wgu.data_ptr(), ldw, Zq.data_ptr(), ldz, amax), workspace, dev,
+                 _lib.GEMM_OP_BF16_SWIGLU, 1, M, N, K, X, ldx, 0, Wgu, ldw, 0, Zq, ldz, 0, _lib.GEMM_OUT_E4M3,
+                 alpha=amax)
+
+
+def gemm_bf16_swiglu_e4m3_batched(X, Wgu, amax, Zq=None, workspace=None):
+    """The batched form of gemm_bf16_swiglu_e4m3: X [batch, M, K], Wgu
+    [batch, K, 2N], codes uint8 [batch, M, N], one range for every entry; a
+    batch stride of 0 broadcasts an operand."""
+    batch, M, N, K, N2, dev, Zq = _swiglu_e4m3_shapes(X, Wgu, Zq, "gemm_bf16_swiglu_e4m3_batched", True)
+    ldx, ldw, ldz = _ld(X, K), _ld(Wgu, N2), _ld(Zq, N)
+    sA, sB, sC = _bstride(X), _bstride(Wgu), _bstride(Zq)
+    amax = float(amax)
+    return _gemm("gemm_bf16_swiglu_e4m3_batched", "gemm_bf16_swiglu_e4m3_batched",
+                 (batch, M, N, K, X.data_ptr(), ldx, sA, Wgu.data_ptr(), ldw, sB, Zq.data_ptr(), ldz, sC, amax),
+                 workspace, dev, _lib.GEMM_OP_BF16_SWIGLU, batch, M, N, K, X, ldx, sA, Wgu, ldw, sB, Zq, ldz, sC,
+                 _lib.GEMM_OUT_E4M3, alpha=amax)
 
 
 def gemm_bf16_affine(A, B, C, alpha=1.0, bias=None, beta=0.0, workspace=None):

@@ -85,7 +85,9 @@ typedef enum {
 /* Output element type of the BF16 entry points. */
 typedef enum {
     GEMM_OUT_BF16 = 0, /* C holds bf16 bit patterns (uint16_t), RNE of the FP32 sum */
-    GEMM_OUT_F32 = 1   /* C holds float, the FP32 sum */
+    GEMM_OUT_F32 = 1,  /* C holds float, the FP32 sum */
+    GEMM_OUT_E4M3 = 2  /* SwiGLU only: C holds E4M3FN codes (uint8_t) against a fixed
+                          range (gemm_bf16_swiglu_e4m3) */
 } gemm_out_type;
 
 /* FP32 GEMM: A [M,K] float, B [K,N] float, C [M,N] float (FP32 products and
@@ -326,6 +328,30 @@ int gemm_bf16_swiglu_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
                              uint16_t *Z, int64_t ldz, int64_t strideZ,
                              void *stream);
 
+/* SwiGLU with its output stored as one byte per element ("Operator &
+ * Runtime" §5.3.1 carries Example 5-4 on: Z is quantized with one fixed
+ * scale factor, and fusing the quantization too leaves the reads of the
+ * operands and the write of the codes).  The product z = t * u is formed as
+ * in gemm_bf16_swiglu (exact in FP32); Zq [M,N] (uint8_t, ldz and strideZ
+ * in bytes) receives the E4M3FN code nearest to the binary32 quotient
+ * fl(fl(z * 448) / amax) (ties to the even mantissa; beyond +-448
+ * saturating to +-448; NaN to 0x7f).  amax is the caller's fixed range:
+ * the magnitude that maps to 448, so the codes dequantize by the factor
+ * amax / 448; finite and > 0, else GEMM_ERR_INVALID_ARG.  Everything else
+ * -- operands, ownership, streams, determinism, the other errors (16-byte
+ * aligned Zq rows: pointer and ldz multiples of 16 bytes) -- as
+ * gemm_bf16_swiglu and its batched form. */
+int gemm_bf16_swiglu_e4m3(int64_t M, int64_t N, int64_t K,
+                          const uint16_t *X, int64_t ldx,
+                          const uint16_t *Wgu, int64_t ldw,
+                          uint8_t *Zq, int64_t ldz, float amax,
+                          void *stream);
+int gemm_bf16_swiglu_e4m3_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                                  const uint16_t *X, int64_t ldx, int64_t strideX,
+                                  const uint16_t *Wgu, int64_t ldw, int64_t strideW,
+                                  uint8_t *Zq, int64_t ldz, int64_t strideZ, float amax,
+                                  void *stream);
+
 /* ---- affine epilogue -------------------------------------------------------
  *
  * C := alpha * (A.B) + bias + beta * C, the scaling and accumulation of the
@@ -409,7 +435,9 @@ int gemm_bf16_tn_affine(int64_t batch, int64_t M, int64_t N, int64_t K,
  * names them (A = At for the TN ops, B = Bt for the NT and FP8 ops, B = Wgu
  * for SwiGLU), batch 1 for GEMM_OP_SGEMM (the one op without a batched
  * form); c_type is ignored where the op fixes it (SGEMM: float;
- * SiLU, SwiGLU: bf16); alpha, bias and beta are read by the affine ops only,
+ * SiLU: bf16; SwiGLU: bf16 unless c_type is GEMM_OUT_E4M3, which writes the
+ * codes of gemm_bf16_swiglu_e4m3 with alpha as the range amax); alpha, bias
+ * and beta are read by the affine ops only (and alpha by that SwiGLU form),
  * scale_a and scale_b by the FP8 ops only. */
 int gemm_run(int op, int64_t batch, int64_t M, int64_t N, int64_t K,
              const void *A, int64_t lda, int64_t strideA,
@@ -501,7 +529,8 @@ typedef enum {
     GEMM_OP_SGEMM = 0,       /* gemm_sgemm */
     GEMM_OP_BF16 = 1,        /* gemm_bf16, gemm_bf16_batched */
     GEMM_OP_BF16_SILU = 2,   /* gemm_bf16_silu(_batched) (c_type ignored) */
-    GEMM_OP_BF16_SWIGLU = 3, /* gemm_bf16_swiglu(_batched) (b = Wgu, c_type ignored) */
+    GEMM_OP_BF16_SWIGLU = 3, /* gemm_bf16_swiglu(_batched) (b = Wgu; c_type GEMM_OUT_E4M3:
+                                gemm_bf16_swiglu_e4m3(_batched), range in alpha) */
     GEMM_OP_BF16_NT = 4,     /* gemm_bf16_nt, gemm_bf16_nt_batched (b = Bt, ldb = ldbt) */
     GEMM_OP_FP8_NT = 5,      /* gemm_fp8_nt(_batched) (b = Bt; scales do not change the plan) */
     GEMM_OP_BF16_AFFINE = 6, /* gemm_bf16_affine with alpha = 1 (alpha, beta and bias do not change the

@@ -89,6 +89,70 @@ def check_swiglu(Z, G, U, t, u, Zref, K, what=""):
     return _check(Z, Zref, bound, what)
 
 
+# E4M3FN codes of the SwiGLU output (fixed range amax).  A code has 3
+# mantissa bits, so the bf16 GEMM bar above is far too loose to decide one;
+# the check instead bounds what the kernel can have computed.  Its FP32 sum
+# of K exact bf16 products is within K 2^-24 S of the exact sum (S the sum of
+# the products' magnitudes; any order of K - 1 additions, each rounding at
+# most 2^-24 of a partial sum no larger than S), so its bf16 g and u lie
+# between the bf16 roundings of the interval's ends; SiLU in FP32 (exp and
+# reciprocal of a few ulp, a relative error below 2^-17 for |g| < 100) and its
+# bf16 rounding give t between the rounded ends of the SiLU image of that
+# range (SiLU falls below x = -1.27846 and rises above it); z = t * u lies
+# between the corner products, and the binary32 quotient z * 448 / amax moves
+# by at most 2^-22 relative.  The kernel's code must lie between the codes of
+# the two ends, and equal them where they coincide.
+
+SILU_ARGMIN = -1.2784645427610738
+
+
+def swiglu_code_range(oracle_mod, X, Wgu, amax):
+    """(c_lo, c_hi): E4M3FN codes bracketing every code the kernel may give
+    for SwiGLU(X, Wgu) against the range amax (bf16 bit patterns)."""
+    K = X.shape[1]
+    N = Wgu.shape[1] // 2
+    Wg, Wu = np.ascontiguousarray(Wgu[:, :N]), np.ascontiguousarray(Wgu[:, N:])
+    Xa = X & 0x7fff
+    G, U = oracle_mod.gemm_bf16(X, Wg), oracle_mod.gemm_bf16(X, Wu)
+    SG, SU = oracle_mod.gemm_bf16(Xa, Wg & 0x7fff), oracle_mod.gemm_bf16(Xa, Wu & 0x7fff)
+    e = 1.01 * K * 2.0 ** -24
+    rb = oracle_mod.round_bf16_value
+    g_lo, g_hi = rb(G - e * SG), rb(G + e * SG)
+    u_lo, u_hi = rb(U - e * SU), rb(U + e * SU)
+    s_lo, s_hi = oracle_mod.silu(g_lo), oracle_mod.silu(g_hi)
+    tmin, tmax = np.minimum(s_lo, s_hi), np.maximum(s_lo, s_hi)
+    tmin = np.where((g_lo < SILU_ARGMIN) & (g_hi > SILU_ARGMIN), oracle_mod.silu(np.array(SILU_ARGMIN)), tmin)
+    t_lo = rb(tmin - 2.0 ** -17 * np.abs(tmin) - 1e-38)
+    t_hi = rb(tmax + 2.0 ** -17 * np.abs(tmax) + 1e-38)
+    corners = np.stack([t_lo * u_lo, t_lo * u_hi, t_hi * u_lo, t_hi * u_hi])
+    s = 448.0 / float(np.float32(amax))
+    y_lo, y_hi = corners.min(0) * s, corners.max(0) * s
+    return (oracle_mod.e4m3_encode(y_lo - 2.0 ** -22 * np.abs(y_lo)),
+            oracle_mod.e4m3_encode(y_hi + 2.0 ** -22 * np.abs(y_hi)))
+
+
+def check_swiglu_codes(oracle_mod, Q, c_lo, c_hi, what="", min_unique=0.0):
+    """Every code between c_lo and c_hi (by value), equal to them where they
+    coincide; returns the fraction of such unique codes."""
+    d = oracle_mod.e4m3_decode
+    v, lo, hi = d(Q), d(c_lo), d(c_hi)
+    assert not np.isnan(v).any(), f"{what}: NaN code"
+    bad = (v < lo) | (v > hi)
+    if bad.any():
+        idx = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} codes outside their range, first at {idx}: "
+                             f"got {int(Q[idx]):#04x} range [{int(c_lo[idx]):#04x}, {int(c_hi[idx]):#04x}]")
+    uniq = c_lo == c_hi
+    wrong = uniq & (Q != c_lo)
+    if wrong.any():
+        idx = tuple(np.argwhere(wrong)[0])
+        raise AssertionError(f"{what}: {int(wrong.sum())} decided codes differ, first at {idx}: "
+                             f"got {int(Q[idx]):#04x} want {int(c_lo[idx]):#04x}")
+    frac = float(uniq.mean()) if uniq.size else 1.0
+    assert frac >= min_unique, f"{what}: only {frac:.3f} of the codes are decided"
+    return frac
+
+
 def _check(C, ref, bound, what):
     err = np.abs(C - ref)
     assert np.all(np.isfinite(C)), f"{what}: non-finite output"

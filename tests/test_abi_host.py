@@ -337,6 +337,57 @@ def test_fused_arguments(L, op):
     assert st == g5.GEMM_ERR_INVALID_ARG                                     # output entries overlap
 
 
+def test_swiglu_e4m3_arguments(L):
+    """E4M3FN SwiGLU output: the range must be finite and positive; the
+    output type belongs to SwiGLU alone; output rows are bytes, so 16-byte
+    aligned rows need ldz % 16 == 0 (N = 8 with ldz = 8 is unsupported where
+    bf16 rows of 16 bytes were fine)."""
+    f = L.gemm_bf16_swiglu_e4m3
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert f(4, 16, 4, A_ADDR, 4, B_ADDR, 32, C_ADDR, 16, bad, None) == g5.GEMM_ERR_INVALID_ARG
+    assert f(4, 16, 4, A_ADDR, 4, B_ADDR, 31, C_ADDR, 16, 1.0, None) == g5.GEMM_ERR_INVALID_ARG   # ldw < 2N
+    assert f(4, 16, 4, A_ADDR, 4, B_ADDR, 32, C_ADDR, 15, 1.0, None) == g5.GEMM_ERR_INVALID_ARG   # ldz < N
+    assert f(4, 8, 4, A_ADDR, 4, B_ADDR, 16, C_ADDR, 8, 1.0, None) == g5.GEMM_ERR_UNSUPPORTED     # 8-byte rows
+    assert f(4, 16, 4, A_ADDR, 4, B_ADDR, 32, C_ADDR + 8, 16, 1.0, None) == g5.GEMM_ERR_UNSUPPORTED
+    assert f(0, 16, 4, A_ADDR, 4, B_ADDR, 32, C_ADDR, 16, 1.0, None) == g5.GEMM_OK               # empty
+    # the codes take N bytes per row: C may start N bytes (not 2N) after B's end
+    b_end = B_ADDR + (3 * 32 + 32) * 2
+    assert f(4, 16, 4, A_ADDR, 4, B_ADDR, 32, b_end - 8, 16, 1.0, None) == g5.GEMM_ERR_INVALID_ARG
+    fb = L.gemm_bf16_swiglu_e4m3_batched
+    assert fb(2, 4, 16, 4, A_ADDR, 4, 16, B_ADDR, 32, 128, C_ADDR, 16, 63, 1.0, None) == g5.GEMM_ERR_INVALID_ARG
+    assert fb(2, 4, 16, 4, A_ADDR, 4, 16, B_ADDR, 32, 128, C_ADDR, 16, 64, 0.0, None) == g5.GEMM_ERR_INVALID_ARG
+    # GEMM_OUT_E4M3 is SwiGLU's alone
+    for op in (g5.GEMM_OP_BF16, g5.GEMM_OP_BF16_NT, g5.GEMM_OP_FP8_NT, g5.GEMM_OP_BF16_AFFINE, g5.GEMM_OP_BF16_TN):
+        st, _ = g5.plan_query(op, 64, 64, 64, c_type=g5.GEMM_OUT_E4M3)
+        assert st == g5.GEMM_ERR_INVALID_ARG, op
+    # SiLU ignores c_type (bf16 always), as before
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_SILU, 64, 64, 64, c_type=g5.GEMM_OUT_E4M3)
+    assert st == 0
+    # gemm_run: the range travels in alpha
+    args = (g5.GEMM_OP_BF16_SWIGLU, 1, 4, 16, 4, A_ADDR, 4, 0, B_ADDR, 32, 0, C_ADDR, 16, 0, g5.GEMM_OUT_E4M3)
+    assert L.gemm_run(*args, 0.0, None, 0.0, None, None, None, 0, None) == g5.GEMM_ERR_INVALID_ARG
+    assert L.gemm_run(*args[:1], 0, *args[2:], 1.0, None, 0.0, None, None, None, 0, None) == g5.GEMM_OK
+
+
+def test_swiglu_e4m3_plans(L):
+    """The E4M3FN output runs on the same kernels as the bf16 one: the FFN
+    gate/up shape on the 256x192 ring kernel (grid 4 x 128), decode on the
+    split small-M path with the same workspace (exchange slots only)."""
+    e4 = dict(c_type=g5.GEMM_OUT_E4M3)
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_SWIGLU, 1024, 12288, 4096, **e4)
+    assert st == 0 and p.name == b"bf16_256x192" and p.grid == 4 * 128 and p.variant == 1
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_SWIGLU, 1, 12288, 4096, **e4)
+    assert st == 0 and p.name == b"decode_splitk" and p.grid == 192 and p.workspace_bytes == CR
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_SWIGLU, 300, 392, 261, lda=266, ldb=792, ldc=400, **e4)
+    assert st == 0 and p.variant == 3
+    # 392-byte code rows are 8-byte, not 16-byte, aligned (bf16 rows of 392
+    # elements, 784 bytes, are 16-byte aligned)
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_SWIGLU, 300, 392, 261, lda=266, ldb=792, ldc=392, **e4)
+    assert st == g5.GEMM_ERR_UNSUPPORTED
+    st, p = g5.plan_query(g5.GEMM_OP_BF16_SWIGLU, 300, 392, 261, lda=266, ldb=792, ldc=392)
+    assert st == 0 and p.variant == 3
+
+
 def test_fused_plans(L):
     """Ring-kernel variants of the fused calls (the epilogues exist in the
     ring kernels only): 4-byte A copies for 4-byte aligned rows, 16-byte for
