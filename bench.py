@@ -331,23 +331,28 @@ def main():
                 dX = [to_dev_bf16(Xm) for _ in range(R)]
                 dW = [to_dev_bf16(Wgu) for _ in range(R)]
                 dZ = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+                dQ = [torch.empty((M, N), dtype=torch.uint8, device=dev) for _ in range(R)]
                 dP = [torch.empty((M, 2 * N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
                 fused = [(lambda i=i: g5.gemm_bf16_swiglu(dX[i], dW[i], dZ[i], workspace=ws)) for i in range(R)]
+                fused8 = [(lambda i=i: g5.gemm_bf16_swiglu_e4m3(dX[i], dW[i], 16.0, dQ[i], workspace=ws))
+                          for i in range(R)]
                 fused_nows = [(lambda i=i: g5.gemm_bf16_swiglu(dX[i], dW[i], dZ[i])) for i in range(R)]
                 plain = [(lambda i=i: g5.gemm_bf16(dX[i], dW[i], dP[i], workspace=ws)) for i in range(R)]
                 ms = timed(fused, 200, args.warmup, label=f"decode_swiglu_m{M}_2x12288x4096")
                 ms_n = timed(fused_nows, 200, args.warmup, label=f"decode_swiglu_m{M}_no_workspace")
                 ms_p = timed(plain, 200, args.warmup, label=f"decode_plain_merged_m{M}_24576x4096")
+                ms8 = timed(fused8, 200, args.warmup, label=f"decode_swiglu_e4m3_m{M}")
                 gbps = alg_bytes / (ms * 1e-3) / 1e9
                 log(f"decode SwiGLU M={M}: fused {ms * 1e3:.2f} us ({gbps:.0f} GB/s), without workspace "
                     f"{ms_n * 1e3:.2f} us; plain product with the merged weight {ms_p * 1e3:.2f} us "
-                    f"(fused / plain {ms / ms_p:.3f})")
+                    f"(fused / plain {ms / ms_p:.3f}); E4M3FN output {ms8 * 1e3:.2f} us")
                 workloads.append({"name": f"decode_swiglu_bf16_m{M}_2x12288x4096", "us": round(ms * 1e3, 3),
                                   "GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
                                   "no_workspace_us": round(ms_n * 1e3, 3),
                                   "plain_merged_product_us": round(ms_p * 1e3, 3),
-                                  "fused_over_plain": round(ms / ms_p, 4), "alg_bytes": alg_bytes, "rotations": R})
-                del dX, dW, dZ, dP
+                                  "fused_over_plain": round(ms / ms_p, 4), "e4m3_output_us": round(ms8 * 1e3, 3),
+                                  "alg_bytes": alg_bytes, "rotations": R})
+                del dX, dW, dZ, dP, dQ
 
     # ------------------------------------------------------------ decode with a linear layer's weight
     if args.only in ("all", "decode_nt"):
@@ -475,19 +480,36 @@ def main():
             # and multiply, the same roundings as the fused epilogue).
             unfused = [(lambda i=i: (plain[i](), torch.mul(torch.nn.functional.silu(dG[i]), dU[i], out=dZ[i])))
                        for i in range(R)]
+            # Z stored as E4M3FN codes against a fixed range (the page's
+            # continuation of the example): fused into the same epilogue, next
+            # to the bf16 SwiGLU followed by a separate quantization pass
+            # (torch element-wise ops: scale, clamp, convert).
+            amax = 16.0
+            dQ = [torch.empty((M, N), dtype=torch.uint8, device=dev) for _ in range(R)]
+            fused8 = [(lambda i=i: g5.gemm_bf16_swiglu_e4m3(dX[i], dW[i], amax, dQ[i], workspace=ws)) for i in range(R)]
+            quant_after = [(lambda i=i: (fused[i](), dQ[i].view(torch.float8_e4m3fn).copy_(
+                torch.clamp(dZ[i].float() * (448.0 / amax), -448.0, 448.0)))) for i in range(R)]
             ms = timed(fused, 30, 5, label="swiglu_ffn_bf16_1024x2x12288x4096")
             ms_plain = timed(plain, 30, 5, label="swiglu_ffn_two_plain_projections")
             ms_unfused = timed(unfused, 30, 5, label="swiglu_ffn_unfused_program")
+            ms8 = timed(fused8, 30, 5, label="swiglu_ffn_e4m3_1024x2x12288x4096")
+            ms_qa = timed(quant_after, 30, 5, label="swiglu_ffn_bf16_then_quantize")
             flops = 2.0 * 2 * M * N * K
             tf = flops / (ms * 1e-3) / 1e12
+            tf8 = flops / (ms8 * 1e-3) / 1e12
             log(f"swiglu FFN 1024x(2x12288)x4096: fused {ms * 1e3:.2f} us ({tf:.1f} TFLOPS); "
                 f"two plain projections {ms_plain * 1e3:.2f} us; unfused program (projections + element-wise "
-                f"SiLU and product) {ms_unfused * 1e3:.2f} us")
+                f"SiLU and product) {ms_unfused * 1e3:.2f} us; E4M3FN output fused {ms8 * 1e3:.2f} us "
+                f"({tf8:.1f} TFLOPS), bf16 output then a separate quantization {ms_qa * 1e3:.2f} us")
             workloads.append({"name": "swiglu_ffn_bf16_1024x2x12288x4096", "us": round(ms * 1e3, 3),
                               "tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                               "two_plain_projections_us": round(ms_plain * 1e3, 3),
                               "unfused_program_us": round(ms_unfused * 1e3, 3), "rotations": R})
-            del dX, dW, dZ, dG, dU
+            workloads.append({"name": "swiglu_ffn_e4m3_1024x2x12288x4096", "us": round(ms8 * 1e3, 3),
+                              "tflops": round(tf8, 2), "frac_peak": round(tf8 / PEAK_BF16_TFLOPS, 4),
+                              "bf16_output_us": round(ms * 1e3, 3),
+                              "bf16_then_quantize_us": round(ms_qa * 1e3, 3), "amax": amax, "rotations": R})
+            del dX, dW, dZ, dG, dU, dQ
 
     # ------------------------------------------------------------ column shard (split K)
     if args.only in ("all", "shard"):

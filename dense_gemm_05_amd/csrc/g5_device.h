@@ -7,6 +7,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 
 #include "g5_common.h"
 
@@ -102,19 +103,47 @@ struct E4m3Quot {
     }
 };
 
-// Fixed-range E4M3FN code of one SwiGLU output z = t * u (page "Operator &
+// Fixed-range E4M3FN codes of the SwiGLU output z = t * u (page "Operator &
 // Runtime" §5.3.1 stores Z with one fixed scale factor, a byte per element):
-// the code nearest to the binary32 quotient fl(fl(z * 448) / amax), taken
-// with the correctly rounded division (z carries up to 16 significant bits,
-// beyond the bf16 numerators the fast quotient above was checked for),
-// clamped to +-448 before the conversion; NaN gives 0x7f.  amax > 0.
-__device__ __forceinline__ uint32_t e4m3_fixed_code(float z, float amax)
-{
-    float y = __fdiv_rn(z * 448.0f, amax);
-    y = y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);
-    const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xffu;
-    return y != y ? 0x7fu : c;
-}
+// the code nearest to the binary32 quotient fl(fl(z * 448) / amax),
+// saturating at +-448, NaN giving 0x7f; amax > 0 is the call's range.
+//  - div: the correctly rounded division, clamped; any amax.
+//  - fast: |z| > amax saturates at once; else the reciprocal-and-residual
+//    quotient of E4m3Quot.  z has at most 16 significant bits (a product
+//    of two bf16 values), so z * 448 has at most 19 and, for a bf16 amax,
+//    a midpoint between two E4M3FN values times amax at most 13: a quotient
+//    not on a midpoint is at least ~2^-19 of its size away from every one,
+//    and the fast quotient (within an ulp, exact when the quotient is
+//    representable) gives the code of the correctly rounded one.  Checked
+//    exhaustively on the host for every bf16 amax significand and every
+//    16-bit z significand; taken when amax is a bf16 value in [2^-80,
+//    2^118] (below, the residual of small quotients goes subnormal).
+struct E4m3Fixed {
+    float amax, rcp;
+    bool fast;
+    __device__ __forceinline__ explicit E4m3Fixed(float a)
+        : amax(a), rcp(__frcp_rn(a)),
+          fast((__float_as_uint(a) & 0xffffu) == 0u && a >= 0x1p-80f && a <= 0x1p118f) {}
+    template <bool FAST>
+    __device__ __forceinline__ uint32_t code(float z) const
+    {
+        float y;
+        if constexpr (FAST) {
+            const float t = z * 448.0f;
+            const float q0 = t * rcp;
+            const float e = __builtin_fmaf(q0, amax, -t);
+            y = __builtin_fmaf(-e, rcp, q0);
+            // |z| > amax: the quotient lies beyond 448 (and t may be infinite)
+            if (__builtin_fabsf(z) > amax) y = __builtin_copysignf(448.0f, z);
+        } else {
+            y = __fdiv_rn(z * 448.0f, amax);
+            y = y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);
+        }
+        const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xffu;
+        return y != y ? 0x7fu : c;
+    }
+    __device__ __forceinline__ uint32_t code(float z) const { return fast ? code<true>(z) : code<false>(z); }
+};
 
 // Fused epilogues of a bf16 output chunk (8 values, already rounded once to
 // bf16 from the FP32 sums: the rounding of the unfused program survives,
@@ -139,14 +168,15 @@ __device__ __forceinline__ u32x4 epi_swiglu8(u32x4 g, u32x4 u)
 }
 // The same 8 outputs as fixed-range E4M3FN codes (4 per word, the lowest
 // column in the lowest byte).
-__device__ __forceinline__ u32x2 epi_swiglu8_e4m3(u32x4 g, u32x4 u, float amax)
+template <bool FAST>
+__device__ __forceinline__ u32x2 epi_swiglu8_e4m3(u32x4 g, u32x4 u, const E4m3Fixed &fq)
 {
     const u32x4 t = epi_silu8(g);
     u32x2 q = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = e4m3_fixed_code(bf16_lo(t[i]) * bf16_lo(u[i]), amax);
-        const uint32_t hi = e4m3_fixed_code(bf16_hi(t[i]) * bf16_hi(u[i]), amax);
+        const uint32_t lo = fq.code<FAST>(bf16_lo(t[i]) * bf16_lo(u[i]));
+        const uint32_t hi = fq.code<FAST>(bf16_hi(t[i]) * bf16_hi(u[i]));
         q[i / 2] |= (lo | (hi << 8)) << (16 * (i % 2));
     }
     return q;
@@ -183,7 +213,7 @@ __device__ __forceinline__ void store_swiglu(const GemmArgs &p, int64_t b, int64
     const float t = __uint_as_float(bf16_rne(silu_f32(__uint_as_float(bf16_rne(g) << 16))) << 16);
     const float ub = __uint_as_float(bf16_rne(u) << 16);
     const int64_t off = b * p.sC + m * p.ldc + n;
-    if (p.c_e4m3) ((uint8_t *)p.C)[off] = (uint8_t)e4m3_fixed_code(t * ub, p.c_amax);
+    if (p.c_e4m3) ((uint8_t *)p.C)[off] = (uint8_t)E4m3Fixed(p.c_amax).code(t * ub);
     else ((uint16_t *)p.C)[off] = (uint16_t)bf16_rne(t * ub);
 }
 
@@ -456,15 +486,20 @@ __device__ __forceinline__ void store_tile_via_lds(const f32x4 (&acc)[NFN][NFM],
             // Fixed-range E4M3FN output (pa->c_e4m3): 8 codes, 8 bytes, per chunk.
             constexpr int OPR = CPR / 2;                     // output chunks per row
             if (pa->c_e4m3) {
-                const float amax = pa->c_amax;
-                for (int q = tid; q < RP * OPR; q += NT) {
-                    const int r = q / OPR, c = q % OPR;
-                    if (MASKED && (m0 + pass * RP + r >= M || n0 + (int64_t)(c + 1) * 8 > N)) continue;
-                    const u32x4 g = *(const u32x4 *)(L + r * PITCH + c * 16);
-                    const u32x4 u = *(const u32x4 *)(L + r * PITCH + (c + OPR) * 16);
-                    char *dst = (char *)Cb + (m0 + pass * RP + r) * ldc + n0 + c * 8;
-                    __builtin_nontemporal_store(epi_swiglu8_e4m3(g, u, amax), (u32x2 *)dst);
-                }
+                // (the quotient's form is fixed per call: one loop each)
+                const E4m3Fixed fq(pa->c_amax);
+                auto codes = [&](auto fast) {
+                    for (int q = tid; q < RP * OPR; q += NT) {
+                        const int r = q / OPR, c = q % OPR;
+                        if (MASKED && (m0 + pass * RP + r >= M || n0 + (int64_t)(c + 1) * 8 > N)) continue;
+                        const u32x4 g = *(const u32x4 *)(L + r * PITCH + c * 16);
+                        const u32x4 u = *(const u32x4 *)(L + r * PITCH + (c + OPR) * 16);
+                        char *dst = (char *)Cb + (m0 + pass * RP + r) * ldc + n0 + c * 8;
+                        __builtin_nontemporal_store(epi_swiglu8_e4m3<decltype(fast)::value>(g, u, fq), (u32x2 *)dst);
+                    }
+                };
+                if (fq.fast) codes(std::true_type{});
+                else codes(std::false_type{});
             } else {
                 for (int q = tid; q < RP * OPR; q += NT) {
                     const int r = q / OPR, c = q % OPR;

@@ -136,20 +136,24 @@ def test_swiglu_e4m3_random(oracle_mod, M, N, K, with_ws):
         rows = np.arange(M)
     Xs = np.ascontiguousarray(X[rows])
     Zr, *_ = oracle_mod.swiglu_bf16(Xs, Wgu)
-    amax = np.float32(0.6 * np.abs(Zr).max())
-    full = torch.full((M, ldz + 16), 0xAA, dtype=torch.uint8, device="cuda")
-    Zq = full[:, :N]
-    g5.gemm_bf16_swiglu_e4m3(dev_bf16(X), dev_bf16(Wgu), float(amax), Zq, workspace=ws() if with_ws else None)
-    host = _host_u8(full)
-    assert np.all(host[:, N:] == 0xAA), "row padding was written"
-    c_lo, c_hi = swiglu_code_range(oracle_mod, Xs, Wgu, amax)
-    frac = check_swiglu_codes(oracle_mod, host[rows, :N], c_lo, c_hi, f"{M}x{N}x{K} {name}", min_unique=0.15)
-    _say(f"  decided {frac:.3f}")
-    # the codes saturate where the oracle's do, and the decided codes carry
-    # the oracle's (checked above); the oracle itself lies in the range
-    want = oracle_mod.swiglu_e4m3(Xs, Wgu, amax)
-    d = oracle_mod.e4m3_decode
-    assert np.all((d(c_lo) <= d(want)) & (d(want) <= d(c_hi)))
+    # a general binary32 range (the division) and a bf16 one (the fast quotient)
+    a32 = np.float32(0.6 * np.abs(Zr).max())
+    a16 = np.float32(oracle_mod.round_bf16_value([0.45 * float(a32)])[0])
+    dX, dW = dev_bf16(X), dev_bf16(Wgu)
+    for amax in (a32, a16):
+        full = torch.full((M, ldz + 16), 0xAA, dtype=torch.uint8, device="cuda")
+        Zq = full[:, :N]
+        g5.gemm_bf16_swiglu_e4m3(dX, dW, float(amax), Zq, workspace=ws() if with_ws else None)
+        host = _host_u8(full)
+        assert np.all(host[:, N:] == 0xAA), "row padding was written"
+        c_lo, c_hi = swiglu_code_range(oracle_mod, Xs, Wgu, amax)
+        frac = check_swiglu_codes(oracle_mod, host[rows, :N], c_lo, c_hi, f"{M}x{N}x{K} {name} amax={amax}",
+                                  min_unique=0.15)
+        _say(f"  amax {amax}: decided {frac:.3f}")
+        # the oracle itself lies in the range
+        want = oracle_mod.swiglu_e4m3(Xs, Wgu, amax)
+        d = oracle_mod.e4m3_decode
+        assert np.all((d(c_lo) <= d(want)) & (d(want) <= d(c_hi)))
 
 
 def test_swiglu_e4m3_ffn_full_size(oracle_mod):
@@ -162,12 +166,14 @@ def test_swiglu_e4m3_ffn_full_size(oracle_mod):
     rows = np.array([0, 1, 255, 256, 511, 600, 767, 768, 1023])
     Xs = np.ascontiguousarray(X[rows])
     Zr, *_ = oracle_mod.swiglu_bf16(Xs, Wgu)
-    amax = np.float32(0.5 * np.abs(Zr).max())
-    Zq = g5.gemm_bf16_swiglu_e4m3(dev_bf16(X), dev_bf16(Wgu), float(amax), workspace=ws())
-    host = _host_u8(Zq)
-    c_lo, c_hi = swiglu_code_range(oracle_mod, Xs, Wgu, amax)
-    frac = check_swiglu_codes(oracle_mod, host[rows], c_lo, c_hi, "ffn rows", min_unique=0.15)
-    _say(f"  decided {frac:.3f}")
+    dX, dW = dev_bf16(X), dev_bf16(Wgu)
+    a32 = np.float32(0.5 * np.abs(Zr).max())
+    for amax in (a32, np.float32(oracle_mod.round_bf16_value([float(a32)])[0])):
+        Zq = g5.gemm_bf16_swiglu_e4m3(dX, dW, float(amax), workspace=ws())
+        host = _host_u8(Zq)
+        c_lo, c_hi = swiglu_code_range(oracle_mod, Xs, Wgu, amax)
+        frac = check_swiglu_codes(oracle_mod, host[rows], c_lo, c_hi, f"ffn rows amax={amax}", min_unique=0.15)
+        _say(f"  amax {amax}: decided {frac:.3f}")
 
 
 @pytest.mark.parametrize("broadcast_x", [False, True])
@@ -180,7 +186,7 @@ def test_swiglu_e4m3_batched(oracle_mod, broadcast_x):
     g = np.random.default_rng([gi.SEED_BASE + 3300, int(broadcast_x)])
     X = gi.to_bf16_bits(gi.normal(g, (1 if broadcast_x else batch, M, K)))
     Wgu = gi.to_bf16_bits(gi.normal(g, (batch, K, 2 * N), 0.125))
-    amax = np.float32(4.0)
+    amax = np.float32(4.0)                        # (a bf16 value: the fast quotient)
     dX = dev_bf16(X)
     if broadcast_x:
         dX = dX.expand(batch, -1, -1)
