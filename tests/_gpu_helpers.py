@@ -106,15 +106,22 @@ def check_swiglu(Z, G, U, t, u, Zref, K, what=""):
 SILU_ARGMIN = -1.2784645427610738
 
 
-def swiglu_code_range(oracle_mod, X, Wgu, amax):
-    """(c_lo, c_hi): E4M3FN codes bracketing every code the kernel may give
-    for SwiGLU(X, Wgu) against the range amax (bf16 bit patterns)."""
-    K = X.shape[1]
+def swiglu_sums(oracle_mod, X, Wgu):
+    """The exact gate and up sums G, U and the sums of their terms'
+    magnitudes SG, SU (oracle products of bf16 bit patterns)."""
     N = Wgu.shape[1] // 2
     Wg, Wu = np.ascontiguousarray(Wgu[:, :N]), np.ascontiguousarray(Wgu[:, N:])
     Xa = X & 0x7fff
-    G, U = oracle_mod.gemm_bf16(X, Wg), oracle_mod.gemm_bf16(X, Wu)
-    SG, SU = oracle_mod.gemm_bf16(Xa, Wg & 0x7fff), oracle_mod.gemm_bf16(Xa, Wu & 0x7fff)
+    return (oracle_mod.gemm_bf16(X, Wg), oracle_mod.gemm_bf16(X, Wu),
+            oracle_mod.gemm_bf16(Xa, Wg & 0x7fff), oracle_mod.gemm_bf16(Xa, Wu & 0x7fff))
+
+
+def swiglu_code_range(oracle_mod, X, Wgu, amax, sums=None):
+    """(c_lo, c_hi): E4M3FN codes bracketing every code the kernel may give
+    for SwiGLU(X, Wgu) against the range amax (bf16 bit patterns); `sums`:
+    swiglu_sums of the same operands, when already computed."""
+    K = X.shape[1]
+    G, U, SG, SU = sums if sums is not None else swiglu_sums(oracle_mod, X, Wgu)
     e = 1.01 * K * 2.0 ** -24
     rb = oracle_mod.round_bf16_value
     g_lo, g_hi = rb(G - e * SG), rb(G + e * SG)

@@ -24,7 +24,7 @@ import pytest
 import torch
 
 import gemm_inputs as gi
-from _gpu_helpers import check_swiglu_codes, dev_bf16, swiglu_code_range, ws
+from _gpu_helpers import check_swiglu_codes, dev_bf16, swiglu_code_range, swiglu_sums, ws
 
 import dense_gemm_05_amd as g5
 
@@ -159,20 +159,21 @@ def test_swiglu_e4m3_random(oracle_mod, M, N, K, with_ws):
 def test_swiglu_e4m3_ffn_full_size(oracle_mod):
     """The FFN's gate and up projections, X [1024, 4096] and the merged
     weight [4096, 2 x 12288], with the output stored as codes: the
-    benchmarked launch; rows from every row tile, all columns."""
-    _say("ffn 1024x12288x4096")
+    benchmarked launch; every element, for a general and a bf16 range."""
+    _say("ffn 1024x12288x4096 (every element)")
     X, Wgu = gi.swiglu_inputs()
     assert _plan_name(1024, 12288, 4096, True) == "bf16_256x192"
-    rows = np.array([0, 1, 255, 256, 511, 600, 767, 768, 1023])
-    Xs = np.ascontiguousarray(X[rows])
-    Zr, *_ = oracle_mod.swiglu_bf16(Xs, Wgu)
+    Zr, *_ = oracle_mod.swiglu_bf16(np.ascontiguousarray(X[:64]), Wgu)
     dX, dW = dev_bf16(X), dev_bf16(Wgu)
     a32 = np.float32(0.5 * np.abs(Zr).max())
-    for amax in (a32, np.float32(oracle_mod.round_bf16_value([float(a32)])[0])):
-        Zq = g5.gemm_bf16_swiglu_e4m3(dX, dW, float(amax), workspace=ws())
-        host = _host_u8(Zq)
-        c_lo, c_hi = swiglu_code_range(oracle_mod, Xs, Wgu, amax)
-        frac = check_swiglu_codes(oracle_mod, host[rows], c_lo, c_hi, f"ffn rows amax={amax}", min_unique=0.15)
+    a16 = np.float32(oracle_mod.round_bf16_value([float(a32)])[0])
+    got = {}
+    for amax in (a32, a16):
+        got[float(amax)] = _host_u8(g5.gemm_bf16_swiglu_e4m3(dX, dW, float(amax), workspace=ws()))
+    sums = swiglu_sums(oracle_mod, X, Wgu)
+    for amax in (a32, a16):
+        c_lo, c_hi = swiglu_code_range(oracle_mod, X, Wgu, amax, sums)
+        frac = check_swiglu_codes(oracle_mod, got[float(amax)], c_lo, c_hi, f"ffn amax={amax}", min_unique=0.15)
         _say(f"  amax {amax}: decided {frac:.3f}")
 
 
