@@ -62,6 +62,8 @@ def _load():
     lib.oracle_e4m3_encode_array.argtypes = [i64, p, p]
     lib.oracle_quantize_fixed_e4m3.argtypes = [i64, p, ctypes.c_float, p]
     lib.oracle_quantize_fixed_e4m3.restype = None
+    lib.oracle_silu_mul_bf16.argtypes = [i64, p, p, p, p]
+    lib.oracle_silu_mul_bf16.restype = None
     lib.oracle_quantize_rows_e4m3.argtypes = [i64, i64, p, i64, p, i64, p]
     lib.oracle_gemm_fp8_nt.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, p, i64]
     lib.oracle_gemm_fp8_nt_affine.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, ctypes.c_double, p,
@@ -245,8 +247,8 @@ def e4m3_encode(x):
 
 
 def quantize_fixed_e4m3(v, amax):
-    """Fixed-range E4M3FN codes of exact products v (doubles): the value
-    nearest to fl32(fl32(fl32(v) * 448) / amax), saturating at 448."""
+    """Fixed-range E4M3FN codes of values v (doubles): the value nearest to
+    fl32(fl32(fl32(v) * 448) / amax), saturating at 448."""
     amax = float(np.float32(amax))
     if not (math.isfinite(amax) and amax > 0):
         raise ValueError("amax must be finite and positive")
@@ -258,9 +260,23 @@ def quantize_fixed_e4m3(v, amax):
 
 def swiglu_e4m3(X, Wgu, amax):
     """SwiGLU on a merged [K, 2N] weight with its output quantized to E4M3FN
-    codes against the fixed range amax (uint8 [M, N])."""
+    codes against the fixed range amax (uint8 [M, N]): the codes of the bf16
+    Z the unfused program stores."""
     Z, _, _, _ = swiglu_bf16(X, Wgu)
-    return quantize_fixed_e4m3(Z, amax)
+    return quantize_fixed_e4m3(round_bf16_value(Z), amax)
+
+
+def silu_mul_bf16(G, U):
+    """The activation chain on stored bf16 G and U (bit patterns, same
+    shape): returns (t, z) in double, t = bf16(SiLU(g)), z = t * u
+    unrounded."""
+    G = np.ascontiguousarray(G, np.uint16)
+    U = np.ascontiguousarray(U, np.uint16)
+    if G.shape != U.shape:
+        raise ValueError("G and U differ in shape")
+    t, z = np.empty(G.shape, np.float64), np.empty(G.shape, np.float64)
+    _load().oracle_silu_mul_bf16(G.size, G.ctypes.data, U.ctypes.data, t.ctypes.data, z.ctypes.data)
+    return t, z
 
 
 def quantize_rows_e4m3(X):

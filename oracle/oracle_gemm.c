@@ -208,6 +208,18 @@ void oracle_gemm_bf16_silu(int64_t M, int64_t N, int64_t K,
  * 0..N-1 and W_u in columns N..2N-1.  With G and U the double products,
  * g = round_bf16(G), u = round_bf16(U), t = round_bf16(SiLU(g)) and
  * Z = t * u (unrounded).  g, u and t are returned too ([M][N], ldz). */
+/* The activation chain of page "Operator & Runtime" §5.3.1 on stored bf16
+ * G and U (Example 5-4), element by element: t = bf16(SiLU(g)) -- the value
+ * the separate SiLU step stores -- and z = t * u, returned unrounded (the
+ * product step stores bf16(z)). */
+void oracle_silu_mul_bf16(int64_t n, const uint16_t *G, const uint16_t *U, double *t, double *z)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        t[i] = round_bf16_d(silu(widen_bf16(G[i])));
+        z[i] = t[i] * widen_bf16(U[i]);
+    }
+}
+
 void oracle_swiglu_bf16(int64_t M, int64_t N, int64_t K,
                         const uint16_t *X, int64_t ldx,
                         const uint16_t *Wgu, int64_t ldw,
@@ -329,21 +341,23 @@ static float rn_f32(double x)
     return (float)x;
 }
 
-/* Fixed-range E4M3FN quantization of the SwiGLU output, page "Operator &
- * Runtime" §5.3.1 (Example 5-4 carried on: Z is stored with one fixed scale
- * factor, one byte per element).  The range amax (finite, > 0) maps to the
- * format's largest finite value 448, as in the per-row quantizer of §5.4.3,
- * and the factor that undoes it is amax / 448.  The page leaves the
- * precision of that quotient open; it is taken in binary32, the precision of
- * the output tile it is fused into: z = fl(t * u) (the product of the two
- * bf16 factors, exact unless it leaves the binary32 range), p = fl(z * 448),
+/* Fixed-range E4M3FN quantization, page "Operator & Runtime" §5.3.1
+ * (Example 5-4 carried on: Z is stored with one fixed scale factor, one byte
+ * per element).  The range amax (finite, > 0) maps to the format's largest
+ * finite value 448, as in the per-row quantizer of §5.4.3, and the factor
+ * that undoes it is amax / 448.  The page leaves the precision of that
+ * quotient open; it is taken in binary32: z = fl(v), p = fl(z * 448),
  * y = fl(p / amax), each correctly rounded, and the code is the E4M3FN value
  * nearest to y (ties to the even mantissa, beyond +-448 saturating to
- * +-448, NaN to 0x7f).  v holds the exact products t * u in double; the
- * double quotient rounded to binary32 equals the binary32 quotient (53 >=
- * 2 * 24 + 2: rounding twice is innocuous for a division). */
+ * +-448, NaN to 0x7f).  The double quotient rounded to binary32 equals the
+ * binary32 quotient (53 >= 2 * 24 + 2: rounding twice is innocuous for a
+ * division).  What is quantized is the value the unfused program stores:
+ * for SwiGLU the bf16 Z (§5.4.3 keeps the unfused program's roundings when
+ * steps are fused), so v holds bf16 values there and fl(v), fl(z * 448)
+ * are exact. */
 void oracle_quantize_fixed_e4m3(int64_t n, const double *v, float amax, uint8_t *out)
 {
+    /* (amax finite and > 0: the Python wrapper checks it) */
     for (int64_t i = 0; i < n; ++i) {
         const float z = rn_f32(v[i]);
         const float p = rn_f32((double)z * 448.0);

@@ -187,11 +187,12 @@ def _fixed_quotient_f32(z, amax):
 
 def test_swiglu_e4m3_codes_brute_force(oracle_mod):
     """Section 5.3.1 quantizes Z = SiLU(G) (.) U with one fixed scale: each
-    code is the E4M3FN value nearest to the binary32 quotient z * 448 / amax
-    (z the product of the bf16 factors).  Checked element by element against
-    numpy's float32 arithmetic and a brute-force rational nearest-value
-    search, for a range that saturates a fifth of the outputs and for one
-    that saturates none (both a bf16 value and a general binary32 value)."""
+    code is the E4M3FN value nearest to the binary32 quotient z * 448 / amax,
+    z the bf16 value the unfused program stores (section 5.4.3 keeps that
+    rounding under fusion).  Checked element by element against numpy's
+    float32 arithmetic and a brute-force rational nearest-value search, for
+    a range that saturates a fifth of the outputs and for one that saturates
+    none (both a bf16 value and a general binary32 value)."""
     mags = _e4m3_mags(oracle_mod)
     g = np.random.default_rng(31)
     X = bits(g.standard_normal((7, 48)))
@@ -200,7 +201,7 @@ def test_swiglu_e4m3_codes_brute_force(oracle_mod):
     top = float(np.abs(Z).max())
     for amax in (np.float32(np.quantile(np.abs(Z), 0.8)), np.float32(top * 1.0001), np.float32(0.75)):
         Q = oracle_mod.swiglu_e4m3(X, W, amax)
-        for (i, j), z in np.ndenumerate(tt * uu):
+        for (i, j), z in np.ndenumerate(oracle_mod.round_bf16_value(tt * uu)):
             assert int(Q[i, j]) == _nearest_code_of(_fixed_quotient_f32(z, amax), mags), (amax, i, j)
     sat = oracle_mod.swiglu_e4m3(X, W, np.float32(np.quantile(np.abs(Z), 0.8)))
     assert 0.1 < np.mean((sat & 0x7f) == 0x7e) < 0.3
@@ -253,6 +254,35 @@ def test_swiglu_e4m3_decision_in_binary32(oracle_mod):
             assert int(Q[0, 0]) == even
             found += even != nearer
     assert found >= 1                                          # the pin separates the two readings
+
+
+def test_silu_mul_chain_matches_swiglu(oracle_mod):
+    """The activation chain on stored G and U (section 5.3.1, Example 5-4)
+    is the element-wise part of the SwiGLU reference: fed the bf16 g and u
+    that the pinned SwiGLU reference rounds its products to, it returns the
+    same t and z."""
+    g = np.random.default_rng(33)
+    X = bits(g.standard_normal((5, 24)))
+    W = _merged(bits(g.standard_normal((24, 7)) * 0.5), bits(g.standard_normal((24, 7)) * 0.5))
+    Z, gg, uu, tt = oracle_mod.swiglu_bf16(X, W)
+    t, z = oracle_mod.silu_mul_bf16(bits(gg), bits(uu))
+    assert np.array_equal(t, tt) and np.array_equal(z, Z)
+
+
+def test_silu_mul_chain_closed_forms(oracle_mod):
+    """t = bf16(SiLU(g)): SiLU(1) = 0.7310585... rounds to 187 * 2^-8, so
+    with u = 3, z = 2.19140625; SiLU(0) = 0; SiLU(g) rounds to g for g >= 17
+    (e^-17 < 2^-24); SiLU(-90) ~ -7.4e-38 is a tiny negative bf16 value
+    whose product with a positive u keeps the sign; SiLU(-100) ~ -3.7e-42
+    lies below half the smallest bf16 subnormal (2^-134) and rounds to -0."""
+    G = bits([1.0, 0.0, 17.0, 250.0, -90.0, -100.0])
+    U = bits([3.0, -5.0, 0.5, -2.0, 1.0, 1.0])
+    t, z = oracle_mod.silu_mul_bf16(G, U)
+    assert t[0] == 187 * 2.0 ** -8 and z[0] == 2.19140625
+    assert t[1] == 0.0 and z[1] == 0.0 and math.copysign(1.0, z[1]) < 0   # 0 * -5 = -0
+    assert t[2] == 17.0 and z[2] == 8.5 and t[3] == 250.0 and z[3] == -500.0
+    assert -1e-37 < t[4] < -1e-38 and z[4] == t[4]
+    assert t[5] == 0.0 and math.copysign(1.0, t[5]) < 0
 
 
 # ---------------------------------------------------------------- affine epilogue
