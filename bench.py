@@ -73,7 +73,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "decode_swiglu", "sgemm", "batched", "ragged", "swiglu", "shard", "fp8", "scores_nt", "decode_nt", "fp8_example_5_8", "square", "affine", "linear_nt", "wgrad_tn", "copy"])
+    ap.add_argument("--only", default="all", choices=["all", "ffn", "decode", "decode_swiglu", "sgemm", "batched", "ragged", "swiglu", "shard", "fp8", "scores_nt", "decode_nt", "fp8_example_5_8", "square", "affine", "linear_nt", "wgrad_tn", "act_chain", "copy"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--batches", type=int, default=7, help="timed batches per workload (median reported)")
@@ -510,6 +510,54 @@ def main():
                               "bf16_output_us": round(ms * 1e3, 3),
                               "bf16_then_quantize_us": round(ms_qa * 1e3, 3), "amax": amax, "rotations": R})
             del dX, dW, dZ, dG, dU, dQ
+
+    # ------------------------------------------------------------ the activation chain (Example 5-4)
+    if args.only in ("all", "act_chain"):
+        with guarded("act_chain", workloads):
+            # The activation chain on stored G and U [1024, 12288] (bf16, 24 MiB
+            # each): T = SiLU(G), Z = T (.) U and Z quantized to one byte, as
+            # separate passes and fused.  Each program's bytes are the page's
+            # accounting of the tensors it reads and writes once.
+            M, N = 1024, 12288
+            G, U = gi.act_chain_inputs(M, N)
+            E = 2 * M * N                                  # one bf16 tensor
+            R = rotations(3 * E)
+            dG = [to_dev_bf16(G) for _ in range(R)]
+            dU = [to_dev_bf16(U) for _ in range(R)]
+            dT = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+            dZ = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+            dQ = [torch.empty((M, N), dtype=torch.uint8, device=dev) for _ in range(R)]
+            amax = 256.0
+            progs = [
+                ("silu_then_product", 5 * E,
+                 lambda i: (g5.act_silu(dG[i], dT[i]), g5.act_mul(dT[i], dU[i], dZ[i]))),
+                ("fused_silu_product", 3 * E, lambda i: g5.act_swiglu(dG[i], dU[i], dZ[i])),
+                ("three_steps", 5 * E + 3 * E // 2,
+                 lambda i: (g5.act_silu(dG[i], dT[i]), g5.act_mul(dT[i], dU[i], dZ[i]),
+                            g5.act_quantize_e4m3(dZ[i], amax, dQ[i]))),
+                ("fused_two_then_quantize", 3 * E + 3 * E // 2,
+                 lambda i: (g5.act_swiglu(dG[i], dU[i], dZ[i]), g5.act_quantize_e4m3(dZ[i], amax, dQ[i]))),
+                ("fused_three", 5 * E // 2, lambda i: g5.act_swiglu_e4m3(dG[i], dU[i], amax, dQ[i])),
+            ]
+            res = {}
+            for name, nbytes, fn in progs:
+                ms = timed([(lambda i=i, fn=fn: fn(i)) for i in range(R)], 200, args.warmup,
+                           label=f"act_chain_{name}")
+                res[name] = (ms * 1e3, nbytes / (ms * 1e-3) / 1e9, nbytes)
+            log("activation chain 1024x12288 (Example 5-4): " + "; ".join(
+                f"{k} {v[0]:.2f} us ({v[2] / 2**20:.0f} MiB, {v[1]:.0f} GB/s)" for k, v in res.items()))
+            f2, u2 = res["fused_silu_product"], res["silu_then_product"]
+            f3, u3 = res["fused_three"], res["three_steps"]
+            workloads.append({"name": "act_chain_example_5_4_1024x12288",
+                              "us": round(f2[0], 3), "GBps": round(f2[1], 1), "frac_hbm": round(f2[1] / PEAK_HBM_GBPS, 4),
+                              "programs": {k: {"us": round(v[0], 3), "GBps": round(v[1], 1),
+                                               "MiB": round(v[2] / 2**20, 1)} for k, v in res.items()},
+                              "fused_over_separate_two_steps": round(f2[0] / u2[0], 4),
+                              "page_traffic_ratio_two_steps": round(3 / 5, 4),
+                              "fused_over_separate_three_steps": round(f3[0] / u3[0], 4),
+                              "page_traffic_ratio_three_steps": round(2.5 / 6.5, 4),
+                              "amax": amax, "rotations": R})
+            del dG, dU, dT, dZ, dQ
 
     # ------------------------------------------------------------ column shard (split K)
     if args.only in ("all", "shard"):

@@ -22,6 +22,7 @@ GEMM_WORKSPACE_COUNTER_BYTES = 1 << 20
 GEMM_OUT_BF16 = 0
 GEMM_OUT_F32 = 1
 GEMM_OUT_E4M3 = 2
+GEMM_ACT_SILU, GEMM_ACT_MUL, GEMM_ACT_SWIGLU, GEMM_ACT_QUANT, GEMM_ACT_SWIGLU_E4M3 = range(5)
 
 GEMM_OP_SGEMM = 0
 GEMM_OP_BF16 = 1
@@ -41,7 +42,7 @@ GEMM_FAMILY = {0: "none", 1: "zero", 2: "bf16_mfma", 3: "f32_mfma", 4: "decode",
 EXPORTS = ("gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm_bf16_nt_batched",
            "gemm_bf16_tn", "gemm_bf16_tn_batched",
            "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_bf16_silu_batched", "gemm_bf16_swiglu_batched",
-           "gemm_bf16_swiglu_e4m3", "gemm_bf16_swiglu_e4m3_batched",
+           "gemm_bf16_swiglu_e4m3", "gemm_bf16_swiglu_e4m3_batched", "gemm_act_chain",
            "gemm_fp8_quantize_rows", "gemm_fp8_quantize_cols", "gemm_fp8_nt", "gemm_fp8_nt_batched",
            "gemm_fp8_nt_affine", "gemm_fp8_nt_quant_a", "gemm_bf16_affine", "gemm_bf16_nt_affine",
            "gemm_bf16_tn_affine", "gemm_run", "gemm_run_noalloc", "gemm_workspace_size",
@@ -124,6 +125,8 @@ def lib():
     L.gemm_bf16_swiglu_e4m3_batched.argtypes = [i64, i64, i64, i64, p, i64, i64, p, i64, i64, p, i64, i64,
                                                 ctypes.c_float, p]
     L.gemm_bf16_swiglu_e4m3_batched.restype = i32
+    L.gemm_act_chain.argtypes = [i32, i64, i64, p, i64, p, i64, p, i64, ctypes.c_float, p]
+    L.gemm_act_chain.restype = i32
     L.gemm_status_string.argtypes = [i32]
     L.gemm_status_string.restype = ctypes.c_char_p
     L.gemm_plan_query.argtypes = [i32, i64, i64, i64, i64, u64, i64, i64, u64, i64, i64, u64, i64, i64,

@@ -10,7 +10,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 
 # Compiled in parallel: the ring kernel's instantiations are spread over
 # several translation units.
-SOURCES = ["g5_kernels.hip", "g5_ring_bt.hip", "g5_ring_at.hip", "g5_ring_epi.hip", "g5_fp8.hip", "g5_noalloc.hip", "g5_streamk.hip",
+SOURCES = ["g5_kernels.hip", "g5_ring_bt.hip", "g5_ring_at.hip", "g5_ring_epi.hip", "g5_fp8.hip", "g5_noalloc.hip", "g5_streamk.hip", "g5_act.hip",
            "g5_abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: keep the compiler from emitting packed FP32 VALU

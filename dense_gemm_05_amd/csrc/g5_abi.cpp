@@ -1047,6 +1047,37 @@ int gemm_fp8_quantize_rows(int64_t rows, int64_t cols, const uint16_t *X, int64_
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
+int gemm_act_chain(int step, int64_t M, int64_t N, const uint16_t *in0, int64_t ld0, const uint16_t *in1,
+                   int64_t ld1, void *out, int64_t ldo, float amax, void *stream)
+{
+    if (step < GEMM_ACT_SILU || step > GEMM_ACT_SWIGLU_E4M3 || M < 0 || N < 0) return GEMM_ERR_INVALID_ARG;
+    const bool two = step == GEMM_ACT_MUL || step == GEMM_ACT_SWIGLU || step == GEMM_ACT_SWIGLU_E4M3;
+    const bool codes = step == GEMM_ACT_QUANT || step == GEMM_ACT_SWIGLU_E4M3;
+    if (codes && !(std::isfinite(amax) && amax > 0.0f)) return GEMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return GEMM_OK;
+    const int eo = codes ? 1 : 2;
+    if (!in0 || !out || (two && !in1) || ld0 < N || ldo < N || (two && ld1 < N)) return GEMM_ERR_INVALID_ARG;
+    if (((uint64_t)in0 % 2) || (two && ((uint64_t)in1 % 2)) || ((uint64_t)out % eo)) return GEMM_ERR_INVALID_ARG;
+    const g5::Range r0 = g5::extent((uint64_t)in0, 1, M, N, ld0, 0, 2);
+    const g5::Range ro = g5::extent((uint64_t)out, 1, M, N, ldo, 0, eo);
+    if (r0.hi > ((__int128)1 << 63) || ro.hi > ((__int128)1 << 63) || g5::overlap(r0, ro)) return GEMM_ERR_INVALID_ARG;
+    if (two) {
+        const g5::Range r1 = g5::extent((uint64_t)in1, 1, M, N, ld1, 0, 2);
+        if (r1.hi > ((__int128)1 << 63) || g5::overlap(r1, ro)) return GEMM_ERR_INVALID_ARG;
+    }
+    int st = g5::check_device();
+    if (st != GEMM_OK) return st;
+    // 16-byte chunks when every row holds whole chunks at aligned starts
+    const bool vec = N % 8 == 0 && (__int128)M * (N / 8) < ((__int128)1 << 31) &&
+                     g5::row_alignment((uint64_t)in0, ld0, 0, 1, 2) >= 16 &&
+                     (!two || g5::row_alignment((uint64_t)in1, ld1, 0, 1, 2) >= 16) &&
+                     g5::row_alignment((uint64_t)out, ldo, 0, 1, eo) >= 8 * eo;
+    const bool contig = ld0 == N && ldo == N && (!two || ld1 == N);
+    const g5::ActArgs a{in0, two ? in1 : nullptr, out, M, N, ld0, two ? ld1 : N, ldo, codes ? amax : 1.0f};
+    const hipError_t e = g5::launch_act_chain(step, a, vec, contig, (hipStream_t)stream);
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
 int gemm_fp8_quantize_cols(int64_t K, int64_t N, const uint16_t *W, int64_t ldw, uint8_t *Qt, int64_t ldq,
                            float *scale, void *stream)
 {

@@ -25,19 +25,20 @@ typedef long i64x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- helpers
 
-// FP32 -> bf16 bits, round to nearest even; NaN stays NaN (quiet bit set),
-// infinities keep their sign.
-__device__ __forceinline__ uint32_t bf16_rne(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u) return (u & 0x007fffffu) ? ((u >> 16) | 0x40u) : (u >> 16);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// FP32 -> bf16 bits, round to nearest even; NaN stays NaN (quiet bit set,
+// payload kept), infinities keep their sign.  gfx950 converts a pair of
+// floats in one instruction (v_cvt_pk_bf16_f32); over every binary32
+// pattern, in both halves, it gives the same bits as the arithmetic rule
+// (u + 0x7fff + bit 16 of u) >> 16 for non-NaN u and (u >> 16) | 0x40 for
+// NaN (checked exhaustively on an MI355X), about a twelfth of its cost.
+__device__ __forceinline__ uint32_t bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    return bf16_rne(lo) | (bf16_rne(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // SiLU(x) = x * sigmoid(x) = x / (1 + e^-x), in FP32 ("Operator & Runtime"
@@ -103,44 +104,27 @@ struct E4m3Quot {
     }
 };
 
-// Fixed-range E4M3FN codes of the SwiGLU output z = t * u (page "Operator &
-// Runtime" §5.3.1 stores Z with one fixed scale factor, a byte per element):
-// the code nearest to the binary32 quotient fl(fl(z * 448) / amax),
-// saturating at +-448, NaN giving 0x7f; amax > 0 is the call's range.
-//  - div: the correctly rounded division, clamped; any amax.
-//  - fast: |z| > amax saturates at once; else the reciprocal-and-residual
-//    quotient of E4m3Quot.  z has at most 16 significant bits (a product
-//    of two bf16 values), so z * 448 has at most 19 and, for a bf16 amax,
-//    a midpoint between two E4M3FN values times amax at most 13: a quotient
-//    not on a midpoint is at least ~2^-19 of its size away from every one,
-//    and the fast quotient (within an ulp, exact when the quotient is
-//    representable) gives the code of the correctly rounded one.  Checked
-//    exhaustively on the host for every bf16 amax significand and every
-//    16-bit z significand; taken when amax is a bf16 value in [2^-80,
-//    2^118] (below, the residual of small quotients goes subnormal).
+// Fixed-range E4M3FN codes (page "Operator & Runtime" §5.3.1 stores Z with
+// one fixed scale factor, a byte per element): for a bf16 value z, the code
+// nearest to the binary32 quotient fl(z * 448 / amax), saturating at +-448,
+// NaN giving 0x7f; amax > 0 is the call's range.  What is quantized is the
+// bf16 value the unfused program stores (SwiGLU: bf16(t * u)), so the
+// quotient is that of E4m3Quot: for a bf16 amax in [2^-126, 2^118], z is
+// first clamped to [-amax, amax] (beyond, the code saturates; at +-amax the
+// fast quotient is exactly +-448) and takes the fast quotient (checked
+// exhaustively for bf16 |z| <= amax); other ranges take the division.  Both
+// forms are selects, no branches; NaN is decided on z itself.
 struct E4m3Fixed {
-    float amax, rcp;
+    E4m3Quot q;
     bool fast;
     __device__ __forceinline__ explicit E4m3Fixed(float a)
-        : amax(a), rcp(__frcp_rn(a)),
-          fast((__float_as_uint(a) & 0xffffu) == 0u && a >= 0x1p-80f && a <= 0x1p118f) {}
+        : q(a), fast(q.fast && (__float_as_uint(a) & 0xffffu) == 0u) {}
     template <bool FAST>
     __device__ __forceinline__ uint32_t code(float z) const
     {
-        float y;
-        if constexpr (FAST) {
-            const float t = z * 448.0f;
-            const float q0 = t * rcp;
-            const float e = __builtin_fmaf(q0, amax, -t);
-            y = __builtin_fmaf(-e, rcp, q0);
-            // |z| > amax: the quotient lies beyond 448 (and t may be infinite)
-            if (__builtin_fabsf(z) > amax) y = __builtin_copysignf(448.0f, z);
-        } else {
-            y = __fdiv_rn(z * 448.0f, amax);
-            y = y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);
-        }
+        const float y = FAST ? q.q_fast(__builtin_fminf(__builtin_fmaxf(z, -q.amax), q.amax)) : q.q_div(z);
         const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xffu;
-        return y != y ? 0x7fu : c;
+        return z != z ? 0x7fu : c;
     }
     __device__ __forceinline__ uint32_t code(float z) const { return fast ? code<true>(z) : code<false>(z); }
 };
@@ -166,20 +150,35 @@ __device__ __forceinline__ u32x4 epi_swiglu8(u32x4 g, u32x4 u)
         z[i] = pack_bf16x2(bf16_lo(t[i]) * bf16_lo(u[i]), bf16_hi(t[i]) * bf16_hi(u[i]));
     return z;
 }
-// The same 8 outputs as fixed-range E4M3FN codes (4 per word, the lowest
-// column in the lowest byte).
-template <bool FAST>
-__device__ __forceinline__ u32x2 epi_swiglu8_e4m3(u32x4 g, u32x4 u, const E4m3Fixed &fq)
+// The product step alone: bf16(t * u) of 8 packed bf16 t and u (exact in
+// FP32, rounded once).
+__device__ __forceinline__ u32x4 mul8_bf16(u32x4 t, u32x4 u)
 {
-    const u32x4 t = epi_silu8(g);
+    u32x4 z;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        z[i] = pack_bf16x2(bf16_lo(t[i]) * bf16_lo(u[i]), bf16_hi(t[i]) * bf16_hi(u[i]));
+    return z;
+}
+// The fixed-range E4M3FN codes of 8 packed bf16 values (4 per word, the lowest column
+// in the lowest byte).
+template <bool FAST>
+__device__ __forceinline__ u32x2 codes8_e4m3(u32x4 z, const E4m3Fixed &fq)
+{
     u32x2 q = {0u, 0u};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = fq.code<FAST>(bf16_lo(t[i]) * bf16_lo(u[i]));
-        const uint32_t hi = fq.code<FAST>(bf16_hi(t[i]) * bf16_hi(u[i]));
+        const uint32_t lo = fq.code<FAST>(bf16_lo(z[i]));
+        const uint32_t hi = fq.code<FAST>(bf16_hi(z[i]));
         q[i / 2] |= (lo | (hi << 8)) << (16 * (i % 2));
     }
     return q;
+}
+// The SwiGLU outputs of a chunk as codes: those of the bf16 outputs.
+template <bool FAST>
+__device__ __forceinline__ u32x2 epi_swiglu8_e4m3(u32x4 g, u32x4 u, const E4m3Fixed &fq)
+{
+    return codes8_e4m3<FAST>(epi_swiglu8(g, u), fq);
 }
 
 // One output element of the small-M kernels: the FP32 sum of batch entry
@@ -213,8 +212,9 @@ __device__ __forceinline__ void store_swiglu(const GemmArgs &p, int64_t b, int64
     const float t = __uint_as_float(bf16_rne(silu_f32(__uint_as_float(bf16_rne(g) << 16))) << 16);
     const float ub = __uint_as_float(bf16_rne(u) << 16);
     const int64_t off = b * p.sC + m * p.ldc + n;
-    if (p.c_e4m3) ((uint8_t *)p.C)[off] = (uint8_t)E4m3Fixed(p.c_amax).code(t * ub);
-    else ((uint16_t *)p.C)[off] = (uint16_t)bf16_rne(t * ub);
+    const uint32_t z = bf16_rne(t * ub);
+    if (p.c_e4m3) ((uint8_t *)p.C)[off] = (uint8_t)E4m3Fixed(p.c_amax).code(__uint_as_float(z << 16));
+    else ((uint16_t *)p.C)[off] = (uint16_t)z;
 }
 
 // Load 8 consecutive bf16 elements (one 16-byte chunk) starting at element

@@ -94,4 +94,26 @@ constexpr size_t kScratchBytes = (size_t)16 << 20;
 hipError_t noalloc_scratch(void **ptr);
 hipError_t launch_clear_counters(void *base, int64_t n, hipStream_t s);
 
+// The activation chain on stored bf16 operands (g5_act.hip): steps of page
+// "Operator & Runtime" §5.3.1, Example 5-4, each alone or fused.
+enum ActStep {
+    ACT_SILU = 0,         // in0 = G -> out = T = bf16(SiLU(g))
+    ACT_MUL = 1,          // in0 = T, in1 = U -> out = Z = bf16(t * u)
+    ACT_SWIGLU = 2,       // in0 = G, in1 = U -> out = Z (SiLU and product fused)
+    ACT_QUANT = 3,        // in0 = Z -> out = E4M3FN codes against amax
+    ACT_SWIGLU_E4M3 = 4   // in0 = G, in1 = U -> out = the codes of Z (all three fused)
+};
+struct ActArgs {
+    const uint16_t *in0;
+    const uint16_t *in1;     // NULL for the one-input steps
+    void *out;               // bf16, or E4M3FN codes (bytes) for the quantizing steps
+    int64_t M, N;
+    int64_t ld0, ld1, ldo;   // row strides in elements
+    float amax;              // the quantizing steps' range (> 0)
+};
+// vec: N % 8 == 0, 16-byte aligned input rows, 16-byte (bf16) or 8-byte
+// (codes) aligned output rows and M * N / 8 < 2^32; contig additionally every
+// ld == N.  Else one element per thread.
+hipError_t launch_act_chain(int step, const ActArgs &a, bool vec, bool contig, hipStream_t s);
+
 }  // namespace g5

@@ -23,6 +23,7 @@ __all__ = ["gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm
            "gemm_bf16_tn", "gemm_bf16_tn_batched",
            "gemm_bf16_silu", "gemm_bf16_swiglu", "gemm_bf16_silu_batched", "gemm_bf16_swiglu_batched",
            "gemm_bf16_swiglu_e4m3", "gemm_bf16_swiglu_e4m3_batched",
+           "act_chain", "act_silu", "act_mul", "act_swiglu", "act_quantize_e4m3", "act_swiglu_e4m3",
            "gemm_fp8_quantize_rows", "gemm_fp8_quantize_cols", "gemm_fp8_nt", "gemm_fp8_nt_affine",
            "gemm_fp8_nt_quant_a",
            "gemm_bf16_affine",
@@ -636,6 +637,61 @@ def gemm_bf16_swiglu_e4m3_batched(X, Wgu, amax, Zq=None, workspace=None):
                  (batch, M, N, K, X.data_ptr(), ldx, sA, Wgu.data_ptr(), ldw, sB, Zq.data_ptr(), ldz, sC, amax),
                  workspace, dev, _lib.GEMM_OP_BF16_SWIGLU, batch, M, N, K, X, ldx, sA, Wgu, ldw, sB, Zq, ldz, sC,
                  _lib.GEMM_OUT_E4M3, alpha=amax)
+
+
+def act_chain(step, in0, in1=None, out=None, amax=None):
+    """One step of the activation chain on stored bf16 tensors [M, N]
+    (gemm_act_chain; step one of GEMM_ACT_*): SiLU, the product, SwiGLU, the
+    fixed-range E4M3FN quantization, or SwiGLU and the quantization fused.
+    Returns `out` (bfloat16, or uint8 codes for the quantizing steps)."""
+    two = step in (_lib.GEMM_ACT_MUL, _lib.GEMM_ACT_SWIGLU, _lib.GEMM_ACT_SWIGLU_E4M3)
+    codes = step in (_lib.GEMM_ACT_QUANT, _lib.GEMM_ACT_SWIGLU_E4M3)
+    if step not in range(5):
+        raise ValueError("unknown activation-chain step")
+    if in0.dtype != torch.bfloat16 or in0.dim() != 2 or (two and (in1 is None or in1.dtype != torch.bfloat16)):
+        raise TypeError("the activation chain takes bfloat16 [M, N] inputs")
+    if two and tuple(in1.shape) != tuple(in0.shape):
+        raise ValueError("in0 and in1 differ in shape")
+    if codes and amax is None:
+        raise ValueError("the quantizing steps take a range amax")
+    M, N = in0.shape
+    dev = _check_dev(in0, in1 if two else None, out)
+    odt = torch.uint8 if codes else torch.bfloat16
+    if out is None:
+        out = torch.empty((M, N), dtype=odt, device=dev)
+    if tuple(out.shape) != (M, N) or out.dtype != odt:
+        raise ValueError(f"out must be {odt} [M, N]")
+    st = _launch(lib().gemm_act_chain, dev, step, M, N, in0.data_ptr(), _ld(in0, N),
+                 in1.data_ptr() if two else None, _ld(in1, N) if two else N, out.data_ptr(), _ld(out, N),
+                 float(amax) if codes else 1.0)
+    if st != 0:
+        raise GemmError(st, "gemm_act_chain")
+    return out
+
+
+def act_silu(G, out=None):
+    """T = bf16(SiLU(G)) element by element (the chain's first step)."""
+    return act_chain(_lib.GEMM_ACT_SILU, G, None, out)
+
+
+def act_mul(T, U, out=None):
+    """Z = bf16(T * U) element by element (the chain's second step)."""
+    return act_chain(_lib.GEMM_ACT_MUL, T, U, out)
+
+
+def act_swiglu(G, U, out=None):
+    """Z = bf16(bf16(SiLU(G)) * U), the first two steps fused."""
+    return act_chain(_lib.GEMM_ACT_SWIGLU, G, U, out)
+
+
+def act_quantize_e4m3(Z, amax, out=None):
+    """E4M3FN codes of bf16 Z against the fixed range amax (the third step)."""
+    return act_chain(_lib.GEMM_ACT_QUANT, Z, None, out, amax)
+
+
+def act_swiglu_e4m3(G, U, amax, out=None):
+    """The codes of bf16(bf16(SiLU(G)) * U), all three steps fused."""
+    return act_chain(_lib.GEMM_ACT_SWIGLU_E4M3, G, U, out, amax)
 
 
 def gemm_bf16_affine(A, B, C, alpha=1.0, bias=None, beta=0.0, workspace=None):

@@ -98,6 +98,16 @@ def swiglu_inputs(M=1024, K=4096, N=12288, workload=W_FFN):
     return X, np.ascontiguousarray(np.concatenate([Wg, Wu], axis=1))
 
 
+def act_chain_inputs(M=1024, N=12288, workload=W_FFN):
+    """The stored gate and up activations of the FFN, G and U [M, N], for the
+    activation chain that follows the projections: each ~ N(0, 64), the
+    distribution of X.W for X ~ N(0,1) and W ~ N(0,1/64) over K = 4096
+    (tensor ids 6 and 7); bf16 bit patterns."""
+    G = to_bf16_bits(normal(rng(workload, 6), (M, N), 8.0))
+    U = to_bf16_bits(normal(rng(workload, 7), (M, N), 8.0))
+    return G, U
+
+
 def wgrad_inputs(tokens=1024, d_in=4096, d_out=12288, workload=W_FFN):
     """The weight gradient of the FFN projection, dW = X^T . dY: X ~ N(0,1)
     [tokens, d_in] (the FFN projection's X, given as At [K, M] with

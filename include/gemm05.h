@@ -328,6 +328,43 @@ int gemm_bf16_swiglu_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
                              uint16_t *Z, int64_t ldz, int64_t strideZ,
                              void *stream);
 
+/* ---- the activation chain on stored operands -----------------------------
+ *
+ * "Operator & Runtime" §5.3.1, Example 5-4: with G = X.W_g and U = X.W_u
+ * already stored (bf16 [M,N], e.g. by two separate projections), the chain
+ * computes T = SiLU(G), Z = T (.) U and quantizes Z to one byte with a fixed
+ * scale factor -- each step as its own pass over HBM, or fused so that the
+ * intermediates are never written and read back (the page counts 156 MiB of
+ * traffic for the three passes at [1024, 12288], 108 with the first two
+ * fused, 60 with all three).  Element by element, as the fused epilogues:
+ * t = bf16(SiLU(g)) in FP32, z = bf16(t * u), and the code of z as
+ * gemm_bf16_swiglu_e4m3 forms it against the range amax; so a fused step
+ * gives the same bits as the separate steps in sequence. */
+typedef enum {
+    GEMM_ACT_SILU = 0,        /* out = T [M,N] bf16 from in0 = G */
+    GEMM_ACT_MUL = 1,         /* out = Z [M,N] bf16 from in0 = T, in1 = U */
+    GEMM_ACT_SWIGLU = 2,      /* out = Z bf16 from in0 = G, in1 = U (SiLU and product fused) */
+    GEMM_ACT_QUANT = 3,       /* out = E4M3FN codes [M,N] (uint8_t) of in0 = Z against amax */
+    GEMM_ACT_SWIGLU_E4M3 = 4  /* out = the codes of Z from in0 = G, in1 = U (all three fused) */
+} gemm_act_step;
+
+/* One step of the chain: in0 and in1 (the latter read by the two-input steps
+ * only, else ignored) bf16 bit patterns [M,N] with row strides ld0, ld1; out
+ * [M,N] with row stride ldo, all strides in elements (bytes for codes); amax
+ * read by the quantizing steps only (finite, > 0).  Device pointers; the
+ * caller owns the memory; enqueued on `stream`.  Rows of whole 16-byte
+ * chunks at 16-byte aligned starts (8-byte for codes) stream 16 bytes per
+ * lane; any other shape or alignment runs element by element, with the same
+ * results.  Deterministic.  Errors, nothing enqueued: GEMM_ERR_INVALID_ARG
+ * for an unknown step, M or N < 0, a missing pointer, a stride below N, a
+ * misaligned element, the output overlapping an input (no in-place form),
+ * or a bad amax; M == 0 or N == 0 is a no-op. */
+int gemm_act_chain(int step, int64_t M, int64_t N,
+                   const uint16_t *in0, int64_t ld0,
+                   const uint16_t *in1, int64_t ld1,
+                   void *out, int64_t ldo, float amax,
+                   void *stream);
+
 /* SwiGLU with its output stored as one byte per element ("Operator &
  * Runtime" §5.3.1 carries Example 5-4 on: Z is quantized with one fixed
  * scale factor, and fusing the quantization too leaves the reads of the

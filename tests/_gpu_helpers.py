@@ -98,10 +98,11 @@ def check_swiglu(Z, G, U, t, u, Zref, K, what=""):
 # between the bf16 roundings of the interval's ends; SiLU in FP32 (exp and
 # reciprocal of a few ulp, a relative error below 2^-17 for |g| < 100) and its
 # bf16 rounding give t between the rounded ends of the SiLU image of that
-# range (SiLU falls below x = -1.27846 and rises above it); z = t * u lies
-# between the corner products, and the binary32 quotient z * 448 / amax moves
-# by at most 2^-22 relative.  The kernel's code must lie between the codes of
-# the two ends, and equal them where they coincide.
+# range (SiLU falls below x = -1.27846 and rises above it); t * u lies
+# between the corner products and its bf16 rounding z (the value quantized)
+# between their roundings; the binary32 quotient z * 448 / amax moves by at
+# most 2^-22 relative.  The kernel's code must lie between the codes of the
+# two ends, and equal them where they coincide.
 
 SILU_ARGMIN = -1.2784645427610738
 
@@ -133,7 +134,7 @@ def swiglu_code_range(oracle_mod, X, Wgu, amax, sums=None):
     t_hi = rb(tmax + 2.0 ** -17 * np.abs(tmax) + 1e-38)
     corners = np.stack([t_lo * u_lo, t_lo * u_hi, t_hi * u_lo, t_hi * u_hi])
     s = 448.0 / float(np.float32(amax))
-    y_lo, y_hi = corners.min(0) * s, corners.max(0) * s
+    y_lo, y_hi = rb(corners.min(0)) * s, rb(corners.max(0)) * s
     return (oracle_mod.e4m3_encode(y_lo - 2.0 ** -22 * np.abs(y_lo)),
             oracle_mod.e4m3_encode(y_hi + 2.0 ** -22 * np.abs(y_hi)))
 

@@ -369,6 +369,36 @@ def test_swiglu_e4m3_arguments(L):
     assert L.gemm_run(*args[:1], 0, *args[2:], 1.0, None, 0.0, None, None, None, 0, None) == g5.GEMM_OK
 
 
+def test_act_chain_arguments(L):
+    """gemm_act_chain validates before any device call: the step, sizes,
+    pointers, strides, element alignment, the output overlapping an input,
+    and the range of the quantizing steps (ignored by the others)."""
+    f = L.gemm_act_chain
+    G, U, O = A_ADDR, B_ADDR, C_ADDR
+    INV = g5.GEMM_ERR_INVALID_ARG
+    assert f(5, 4, 16, G, 16, U, 16, O, 16, 1.0, None) == INV                  # unknown step
+    assert f(-1, 4, 16, G, 16, U, 16, O, 16, 1.0, None) == INV
+    assert f(g5.GEMM_ACT_SILU, -1, 16, G, 16, None, 0, O, 16, 1.0, None) == INV
+    assert f(g5.GEMM_ACT_SILU, 4, 16, G, 15, None, 0, O, 16, 1.0, None) == INV  # ld0 < N
+    assert f(g5.GEMM_ACT_SILU, 4, 16, G, 16, None, 0, O, 15, 1.0, None) == INV  # ldo < N
+    assert f(g5.GEMM_ACT_MUL, 4, 16, G, 16, None, 16, O, 16, 1.0, None) == INV  # missing U
+    assert f(g5.GEMM_ACT_MUL, 4, 16, G, 16, U, 15, O, 16, 1.0, None) == INV     # ld1 < N
+    assert f(g5.GEMM_ACT_SILU, 4, 16, G + 1, 16, None, 0, O, 16, 1.0, None) == INV   # odd bf16 address
+    assert f(g5.GEMM_ACT_SILU, 4, 16, G, 16, None, 0, O + 1, 16, 1.0, None) == INV   # odd bf16 output
+    assert f(g5.GEMM_ACT_SILU, 4, 16, G, 16, None, 0, G + 64, 16, 1.0, None) == INV  # out inside G
+    assert f(g5.GEMM_ACT_MUL, 4, 16, G, 16, U, 16, U, 16, 1.0, None) == INV         # in place on U
+    for step in (g5.GEMM_ACT_QUANT, g5.GEMM_ACT_SWIGLU_E4M3):
+        for bad in (0.0, -2.0, float("nan"), float("inf")):
+            assert f(step, 4, 16, G, 16, U, 16, O, 16, bad, None) == INV, (step, bad)
+    # codes are bytes: an odd output address passes validation (the call
+    # then needs a device)
+    assert f(g5.GEMM_ACT_QUANT, 4, 16, G, 16, None, 0, O + 1, 16, 1.0, None) != INV
+    # (M == 0 or N == 0: nothing to do, no device needed)
+    assert f(g5.GEMM_ACT_SWIGLU_E4M3, 0, 16, G, 16, U, 16, O, 16, 1.0, None) == g5.GEMM_OK
+    assert f(g5.GEMM_ACT_SILU, 4, 0, 0, 0, None, 0, 0, 0, 0.0, None) == g5.GEMM_OK
+    assert f(g5.GEMM_ACT_SILU, 0, 16, G, 16, None, 0, O, 16, float("nan"), None) == g5.GEMM_OK
+
+
 def test_swiglu_e4m3_plans(L):
     """The E4M3FN output runs on the same kernels as the bf16 one: the FFN
     gate/up shape on the 256x192 ring kernel (grid 4 x 128), decode on the

@@ -214,17 +214,22 @@ def test_swiglu_e4m3_k_zero_and_empty():
     assert np.all(_host_u8(Zq) == 0xAA)
 
 
-def test_swiglu_e4m3_matches_bf16_swiglu_rounding(oracle_mod):
-    """The two output forms share the gate/up sums: on the exact operands,
-    the bf16 output is bf16(z) and the codes are those of z, for the same z
-    -- the codes of the bf16 output's values equal the codes whenever bf16(z)
-    = z (products of at most 8 significant bits: the crafted half)."""
-    M, K, N = 300, 64, 256
-    X, Wgu = _exact_case(oracle_mod, M, K, N, 2)
+@pytest.mark.parametrize("M,with_ws", [(300, True), (1, True), (16, False)])
+def test_swiglu_e4m3_is_the_quantized_bf16_output(M, with_ws):
+    """Fusing the quantization keeps the unfused program's rounding: the
+    codes equal, bit for bit, the separate quantization step
+    (act_quantize_e4m3) applied to the bf16 SwiGLU output of the same call
+    shape, on the ring kernel and the small-M paths, for a bf16 range (the
+    fast quotient) and a general one (the division)."""
+    N, K = 384, 640
+    _say(f"fused vs separate quantization {M}x{N}x{K} ws={with_ws}")
+    g = np.random.default_rng([gi.SEED_BASE + 3400, M])
+    X = gi.to_bf16_bits(gi.normal(g, (M, K)))
+    Wgu = gi.to_bf16_bits(gi.normal(g, (K, 2 * N), 0.125))
     dX, dW = dev_bf16(X), dev_bf16(Wgu)
-    Zb = g5.gemm_bf16_swiglu(dX, dW, workspace=ws())
-    Zq = g5.gemm_bf16_swiglu_e4m3(dX, dW, 448.0, workspace=ws())
-    torch.cuda.synchronize()
-    zb = Zb.float().cpu().numpy()[:, :128].astype(np.float64)
-    q = Zq.cpu().numpy()[:, :128]
-    assert np.array_equal(q, oracle_mod.quantize_fixed_e4m3(zb, 448.0))
+    w = ws() if with_ws else None
+    Zb = g5.gemm_bf16_swiglu(dX, dW, workspace=w)
+    for amax in (3.0, 2.9):
+        q_fused = _host_u8(g5.gemm_bf16_swiglu_e4m3(dX, dW, amax, workspace=w))
+        q_sep = _host_u8(g5.act_quantize_e4m3(Zb, amax))
+        assert np.array_equal(q_fused, q_sep), f"amax={amax}: {int((q_fused != q_sep).sum())} codes differ"
