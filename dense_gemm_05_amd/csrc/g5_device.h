@@ -113,20 +113,37 @@ struct E4m3Quot {
 // first clamped to [-amax, amax] (beyond, the code saturates; at +-amax the
 // fast quotient is exactly +-448) and takes the fast quotient (checked
 // exhaustively for bf16 |z| <= amax); other ranges take the division.  Both
-// forms are selects, no branches; NaN is decided on z itself.
+// forms are selects, no branches.  The conversion writes 0xff for a NaN, so
+// the bytes of NaN inputs are set to 0x7f afterwards.
 struct E4m3Fixed {
     E4m3Quot q;
     bool fast;
     __device__ __forceinline__ explicit E4m3Fixed(float a)
         : q(a), fast(q.fast && (__float_as_uint(a) & 0xffffu) == 0u) {}
+    // the value converted for z (a NaN z gives some value; its byte is replaced)
+    template <bool FAST>
+    __device__ __forceinline__ float quot(float z) const
+    {
+        return FAST ? q.q_fast(__builtin_amdgcn_fmed3f(z, -q.amax, q.amax)) : q.q_div(z);
+    }
     template <bool FAST>
     __device__ __forceinline__ uint32_t code(float z) const
     {
-        const float y = FAST ? q.q_fast(__builtin_fminf(__builtin_fmaxf(z, -q.amax), q.amax)) : q.q_div(z);
-        const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xffu;
+        const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(quot<FAST>(z), 0.0f, 0, false) & 0xffu;
         return z != z ? 0x7fu : c;
     }
     __device__ __forceinline__ uint32_t code(float z) const { return fast ? code<true>(z) : code<false>(z); }
+    // the codes of 4 values in one word, the first in the lowest byte (two
+    // pair conversions, into the low and the high half)
+    template <bool FAST>
+    __device__ __forceinline__ uint32_t code4(float a, float b, float c, float d) const
+    {
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(quot<FAST>(a), quot<FAST>(b), 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(quot<FAST>(c), quot<FAST>(d), pk, true);
+        const uint32_t m = (a != a ? 0xffu : 0u) | (b != b ? 0xff00u : 0u) | (c != c ? 0xff0000u : 0u) |
+                           (d != d ? 0xff000000u : 0u);
+        return ((uint32_t)pk & ~m) | (0x7f7f7f7fu & m);
+    }
 };
 
 // Fused epilogues of a bf16 output chunk (8 values, already rounded once to
@@ -165,14 +182,8 @@ __device__ __forceinline__ u32x4 mul8_bf16(u32x4 t, u32x4 u)
 template <bool FAST>
 __device__ __forceinline__ u32x2 codes8_e4m3(u32x4 z, const E4m3Fixed &fq)
 {
-    u32x2 q = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = fq.code<FAST>(bf16_lo(z[i]));
-        const uint32_t hi = fq.code<FAST>(bf16_hi(z[i]));
-        q[i / 2] |= (lo | (hi << 8)) << (16 * (i % 2));
-    }
-    return q;
+    return u32x2{fq.code4<FAST>(bf16_lo(z[0]), bf16_hi(z[0]), bf16_lo(z[1]), bf16_hi(z[1])),
+                 fq.code4<FAST>(bf16_lo(z[2]), bf16_hi(z[2]), bf16_lo(z[3]), bf16_hi(z[3]))};
 }
 // The SwiGLU outputs of a chunk as codes: those of the bf16 outputs.
 template <bool FAST>
