@@ -108,7 +108,8 @@ struct GemmArgs {
     int32_t epi;
     // EPI_SWIGLU with c_e4m3 = 1: C holds one E4M3FN code per output (bytes,
     // ldc and sC in bytes), the code nearest to z * 448 / c_amax for the
-    // product z = t * u (c_amax: the caller's fixed range, finite and > 0).
+    // bf16 output z = bf16(t * u) (c_amax: the caller's fixed range, finite
+    // and > 0).
     int32_t c_e4m3 = 0;
     float c_amax = 0.f;
 };

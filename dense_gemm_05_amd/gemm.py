@@ -613,7 +613,8 @@ def _swiglu_e4m3_shapes(X, Wgu, Zq, what, batched):
 def gemm_bf16_swiglu_e4m3(X, Wgu, amax, Zq=None, workspace=None):
     """SwiGLU of X [M, K] with the merged weight Wgu [K, 2N], stored as
     E4M3FN codes (uint8 [M, N]) against the fixed range amax: the code
-    nearest to z * 448 / amax, saturating at 448 (gemm_bf16_swiglu_e4m3).
+    nearest to z * 448 / amax for the bf16 output z, saturating at 448
+    (gemm_bf16_swiglu_e4m3).
     The codes dequantize by amax / 448 (``Zq.view(torch.float8_e4m3fn)``
     reads them as float8)."""
     _, M, N, K, N2, dev, Zq = _swiglu_e4m3_shapes(X, Wgu, Zq, "gemm_bf16_swiglu_e4m3", False)

@@ -368,11 +368,12 @@ int gemm_act_chain(int step, int64_t M, int64_t N,
 /* SwiGLU with its output stored as one byte per element ("Operator &
  * Runtime" §5.3.1 carries Example 5-4 on: Z is quantized with one fixed
  * scale factor, and fusing the quantization too leaves the reads of the
- * operands and the write of the codes).  The product z = t * u is formed as
- * in gemm_bf16_swiglu (exact in FP32); Zq [M,N] (uint8_t, ldz and strideZ
- * in bytes) receives the E4M3FN code nearest to the binary32 quotient
- * fl(fl(z * 448) / amax) (ties to the even mantissa; beyond +-448
- * saturating to +-448; NaN to 0x7f).  amax is the caller's fixed range:
+ * operands and the write of the codes).  What is quantized is the bf16
+ * output of gemm_bf16_swiglu, z = bf16(t * u), the value the unfused program
+ * stores, so the codes equal gemm_act_chain's quantization of that output
+ * bit for bit; Zq [M,N] (uint8_t, ldz and strideZ in bytes) receives the
+ * E4M3FN code nearest to the binary32 quotient fl(z * 448 / amax) (ties to
+ * the even mantissa; beyond +-448 saturating to +-448; NaN to 0x7f).  amax is the caller's fixed range:
  * the magnitude that maps to 448, so the codes dequantize by the factor
  * amax / 448; finite and > 0, else GEMM_ERR_INVALID_ARG.  Everything else
  * -- operands, ownership, streams, determinism, the other errors (16-byte
