@@ -528,16 +528,20 @@ def main():
             dZ = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
             dQ = [torch.empty((M, N), dtype=torch.uint8, device=dev) for _ in range(R)]
             amax = 256.0
+            # each program's bytes: the library's per-call model summed over its calls
+            mb = lambda *steps: int(sum(g5.lib().gemm_model_act_chain_bytes(st, M, N) for st in steps))
+            S, P, F, Q, F3 = (g5.GEMM_ACT_SILU, g5.GEMM_ACT_MUL, g5.GEMM_ACT_SWIGLU, g5.GEMM_ACT_QUANT,
+                              g5.GEMM_ACT_SWIGLU_E4M3)
             progs = [
-                ("silu_then_product", 5 * E,
+                ("silu_then_product", mb(S, P),
                  lambda i: (g5.act_silu(dG[i], dT[i]), g5.act_mul(dT[i], dU[i], dZ[i]))),
-                ("fused_silu_product", 3 * E, lambda i: g5.act_swiglu(dG[i], dU[i], dZ[i])),
-                ("three_steps", 5 * E + 3 * E // 2,
+                ("fused_silu_product", mb(F), lambda i: g5.act_swiglu(dG[i], dU[i], dZ[i])),
+                ("three_steps", mb(S, P, Q),
                  lambda i: (g5.act_silu(dG[i], dT[i]), g5.act_mul(dT[i], dU[i], dZ[i]),
                             g5.act_quantize_e4m3(dZ[i], amax, dQ[i]))),
-                ("fused_two_then_quantize", 3 * E + 3 * E // 2,
+                ("fused_two_then_quantize", mb(F, Q),
                  lambda i: (g5.act_swiglu(dG[i], dU[i], dZ[i]), g5.act_quantize_e4m3(dZ[i], amax, dQ[i]))),
-                ("fused_three", 5 * E // 2, lambda i: g5.act_swiglu_e4m3(dG[i], dU[i], amax, dQ[i])),
+                ("fused_three", mb(F3), lambda i: g5.act_swiglu_e4m3(dG[i], dU[i], amax, dQ[i])),
             ]
             res = {}
             for name, nbytes, fn in progs:
@@ -553,9 +557,9 @@ def main():
                               "programs": {k: {"us": round(v[0], 3), "GBps": round(v[1], 1),
                                                "MiB": round(v[2] / 2**20, 1)} for k, v in res.items()},
                               "fused_over_separate_two_steps": round(f2[0] / u2[0], 4),
-                              "page_traffic_ratio_two_steps": round(3 / 5, 4),
+                              "page_traffic_ratio_two_steps": round(mb(F) / mb(S, P), 4),
                               "fused_over_separate_three_steps": round(f3[0] / u3[0], 4),
-                              "page_traffic_ratio_three_steps": round(2.5 / 6.5, 4),
+                              "page_traffic_ratio_three_steps": round(mb(F3) / mb(S, P, Q), 4),
                               "amax": amax, "rotations": R})
             del dG, dU, dT, dZ, dQ
 

@@ -47,7 +47,7 @@ EXPORTS = ("gemm_sgemm", "gemm_bf16", "gemm_bf16_batched", "gemm_bf16_nt", "gemm
            "gemm_fp8_nt_affine", "gemm_fp8_nt_quant_a", "gemm_bf16_affine", "gemm_bf16_nt_affine",
            "gemm_bf16_tn_affine", "gemm_run", "gemm_run_noalloc", "gemm_workspace_size",
            "gemm_status_string",
-           "gemm_plan_query", "gemm_plan_query_ex", "gemm_model_local_bytes", "gemm_model_traffic_bytes", "gemm_model_quant_traffic",
+           "gemm_plan_query", "gemm_plan_query_ex", "gemm_model_local_bytes", "gemm_model_traffic_bytes", "gemm_model_quant_traffic", "gemm_model_act_chain_bytes",
            "gemm_tile_map")
 
 
@@ -149,6 +149,8 @@ def lib():
     L.gemm_model_traffic_bytes.restype = ctypes.c_double
     L.gemm_model_quant_traffic.argtypes = [i64] * 9 + [ctypes.POINTER(ctypes.c_double)] * 2
     L.gemm_model_quant_traffic.restype = None
+    L.gemm_model_act_chain_bytes.argtypes = [i32, i64, i64]
+    L.gemm_model_act_chain_bytes.restype = ctypes.c_double
     L.gemm_tile_map.argtypes = [i64, i64, i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64),
                                 ctypes.POINTER(i64)]
     L.gemm_tile_map.restype = i32

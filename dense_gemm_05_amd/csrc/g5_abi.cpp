@@ -1353,6 +1353,14 @@ void gemm_model_quant_traffic(int64_t M, int64_t N, int64_t K, int64_t m, int64_
     if (fused) *fused = fus;
 }
 
+double gemm_model_act_chain_bytes(int step, int64_t M, int64_t N)
+{
+    // bytes per element: the inputs read plus the output written
+    static const int kPerElem[5] = {2 + 2, 2 + 2 + 2, 2 + 2 + 2, 2 + 1, 2 + 2 + 1};
+    if (step < GEMM_ACT_SILU || step > GEMM_ACT_SWIGLU_E4M3 || M < 0 || N < 0) return 0.0;
+    return (double)kPerElem[step] * (double)M * (double)N;
+}
+
 int gemm_tile_map(int64_t wg, int64_t batch, int64_t tiles_m, int64_t tiles_n, int64_t group_m, int64_t *b,
                   int64_t *tm, int64_t *tn)
 {

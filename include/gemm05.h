@@ -618,6 +618,15 @@ void gemm_model_quant_traffic(int64_t M, int64_t N, int64_t K, int64_t m, int64_
                               int64_t q_bytes, int64_t w_bytes, int64_t out_bytes, double *separate,
                               double *fused);
 
+/* Traffic of one gemm_act_chain call of step `step` on [M,N] operands
+ * ("Operator & Runtime" §5.3.1, Example 5-4): every input read once and the
+ * output written once, bf16 2 bytes and codes 1 byte per element -- SiLU
+ * 4MN, the product 6MN, SiLU and product fused 6MN, the quantization 3MN,
+ * all three fused 5MN.  A program's traffic is the sum over its calls (the
+ * page's 120, 72, 156, 108 and 60 MiB at [1024, 12288]).  0 for an unknown
+ * step or negative sizes. */
+double gemm_model_act_chain_bytes(int step, int64_t M, int64_t N);
+
 /* The workgroup -> output-tile map used by the tiled kernels: workgroup id
  * `wg` of a launch covering `batch` x tiles_m x tiles_n tiles is assigned
  * (b, tm, tn).  Workgroups are dispatched round-robin over the chip's 8

@@ -605,6 +605,32 @@ def test_quant_traffic_model_reproduces_example_5_8(L):
     assert (sep.value - common) / MiB == rows["input_separate"] and (fus.value - common) / MiB == rows["input_fused"]
 
 
+def test_act_chain_traffic_model_reproduces_example_5_4(L):
+    """gemm_model_act_chain_bytes summed over each program's calls gives the
+    page's Example 5-4 figures: 120 -> 72 MiB for SiLU and the product,
+    156 -> 108 -> 60 MiB with the quantization."""
+    rows, shape = {}, None
+    with open(os.path.join(GOLDEN, "op_runtime_5_3_1_act_chain_traffic.txt")) as fh:
+        for line in fh:
+            if not line.strip() or line.startswith("#"):
+                continue
+            parts = line.split()
+            if shape is None:
+                shape = [int(v) for v in parts]
+            else:
+                rows[parts[0]] = int(parts[1])
+    M, N = shape
+    b = lambda step: L.gemm_model_act_chain_bytes(step, M, N) / 2.0 ** 20
+    S, P, F, Q, F3 = (g5.GEMM_ACT_SILU, g5.GEMM_ACT_MUL, g5.GEMM_ACT_SWIGLU, g5.GEMM_ACT_QUANT,
+                      g5.GEMM_ACT_SWIGLU_E4M3)
+    assert b(S) + b(P) == rows["silu_then_product"]
+    assert b(F) == rows["fused_silu_product"]
+    assert b(S) + b(P) + b(Q) == rows["three_steps"]
+    assert b(F) + b(Q) == rows["fused_two_then_quantize"]
+    assert b(F3) == rows["fused_three"]
+    assert L.gemm_model_act_chain_bytes(5, M, N) == 0.0 and L.gemm_model_act_chain_bytes(S, -1, N) == 0.0
+
+
 def call_affine(L, M, N, K, batch=1, a=A_ADDR, lda=None, b=B_ADDR, ldb=None, c=C_ADDR, ldc=None, alpha=1.0,
                 bias=0, beta=0.0, c_type=0, sA=None, sB=None, sC=None):
     lda = K if lda is None else lda
