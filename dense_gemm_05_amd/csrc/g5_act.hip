@@ -5,8 +5,10 @@
 // the work is a stream: HBM-bound, with no reuse for LDS or the matrix
 // cores.  Each thread moves 16-byte chunks (8 bf16 values) of every operand,
 // consecutive lanes on consecutive chunks of a row, with four chunks' loads
-// issued before any of them is used; outputs go out with non-temporal
-// stores (nothing reads them back in the call).  The element arithmetic is
+// issued before any of them is used; three persistent workgroups per CU walk
+// the chunks and load the next four before storing the current ones;
+// outputs go out with non-temporal stores (nothing reads them back in the
+// call).  The element arithmetic is
 // that of the fused GEMM epilogues (epi_silu8, mul8_bf16, epi_swiglu8,
 // codes8_e4m3), so a chain step gives the same bits as the epilogue that
 // fuses it.
@@ -21,6 +23,7 @@ namespace {
 
 constexpr int kActThreads = 256;
 constexpr int kActUnroll = 4;   // chunks per thread, loads issued together
+constexpr uint64_t kActGrid = 256 * 3;   // persistent workgroups: three per CU
 
 constexpr bool act_two_inputs(int step) { return step == ACT_MUL || step == ACT_SWIGLU || step == ACT_SWIGLU_E4M3; }
 constexpr bool act_codes(int step) { return step == ACT_QUANT || step == ACT_SWIGLU_E4M3; }
@@ -37,9 +40,11 @@ __device__ __forceinline__ void act_store(void *dst, u32x4 x0, u32x4 x1, const E
 }
 
 // Whole 16-byte chunks: N % 8 == 0, every input row start 16-byte aligned,
-// output rows 16-byte (bf16) or 8-byte (codes) aligned; M * N / 8 < 2^32.
+// output rows 16-byte (bf16) or 8-byte (codes) aligned; M * N / 8 < 2^31.
 // CONTIG: every operand's rows follow each other (ld == N), so chunk c sits
-// at element 8c of each operand.
+// at element 8c of each operand.  Persistent: a workgroup walks groups of
+// kActUnroll chunks per thread, gridDim.x groups apart, and issues the next
+// group's loads before it stores the current one.
 template <int STEP, bool FAST, bool CONTIG>
 __global__ void __launch_bounds__(kActThreads) k_act_vec(ActArgs a)
 {
@@ -48,29 +53,45 @@ __global__ void __launch_bounds__(kActThreads) k_act_vec(ActArgs a)
     const uint32_t cpr = (uint32_t)(a.N >> 3);
     const uint32_t total = (uint32_t)a.M * cpr;
     const E4m3Fixed fq(a.amax);
-    const uint32_t first = blockIdx.x * (uint32_t)(kActThreads * kActUnroll) + threadIdx.x;
-    u32x4 x0[kActUnroll], x1[kActUnroll];
-    int64_t e0[kActUnroll], e1[kActUnroll], eo[kActUnroll];   // element offsets of the chunks
+    const uint32_t stride = gridDim.x * (uint32_t)(kActThreads * kActUnroll);
+    struct Group {
+        u32x4 x0[kActUnroll], x1[kActUnroll];
+        int64_t eo[kActUnroll];   // output element offsets of the chunks
+    };
+    auto load = [&](uint32_t first, Group &g) {
 #pragma unroll
-    for (int j = 0; j < kActUnroll; ++j) {
-        const uint32_t c = first + (uint32_t)(j * kActThreads);
-        if (CONTIG) {
-            e0[j] = e1[j] = eo[j] = (int64_t)c * 8;
-        } else {
-            const uint32_t r = c / cpr, col = (c - r * cpr) * 8;
-            e0[j] = (int64_t)r * a.ld0 + col;
-            e1[j] = (int64_t)r * a.ld1 + col;
-            eo[j] = (int64_t)r * a.ldo + col;
+        for (int j = 0; j < kActUnroll; ++j) {
+            const uint32_t c = first + (uint32_t)(j * kActThreads);
+            int64_t e0, e1;
+            if (CONTIG) {
+                e0 = e1 = g.eo[j] = (int64_t)c * 8;
+            } else {
+                const uint32_t r = c / cpr, col = (c - r * cpr) * 8;
+                e0 = (int64_t)r * a.ld0 + col;
+                e1 = (int64_t)r * a.ld1 + col;
+                g.eo[j] = (int64_t)r * a.ldo + col;
+            }
+            if (c < total) {
+                g.x0[j] = __builtin_nontemporal_load((const u32x4 *)(a.in0 + e0));
+                if constexpr (TWO) g.x1[j] = __builtin_nontemporal_load((const u32x4 *)(a.in1 + e1));
+            }
         }
-        if (c < total) {
-            x0[j] = __builtin_nontemporal_load((const u32x4 *)(a.in0 + e0[j]));
-            if constexpr (TWO) x1[j] = __builtin_nontemporal_load((const u32x4 *)(a.in1 + e1[j]));
-        }
-    }
+    };
+    auto store = [&](uint32_t first, const Group &g) {
 #pragma unroll
-    for (int j = 0; j < kActUnroll; ++j) {
-        const uint32_t c = first + (uint32_t)(j * kActThreads);
-        if (c < total) act_store<STEP, FAST>((char *)a.out + eo[j] * OB, x0[j], TWO ? x1[j] : x0[j], fq);
+        for (int j = 0; j < kActUnroll; ++j) {
+            const uint32_t c = first + (uint32_t)(j * kActThreads);
+            if (c < total) act_store<STEP, FAST>((char *)a.out + g.eo[j] * OB, g.x0[j], TWO ? g.x1[j] : g.x0[j], fq);
+        }
+    };
+    uint32_t first = blockIdx.x * (uint32_t)(kActThreads * kActUnroll) + threadIdx.x;
+    Group cur, nxt;
+    load(first, cur);
+    // (total + stride < 2^32: the host keeps the chunk count below 2^31)
+    for (; first < total; first += stride) {
+        load(first + stride, nxt);
+        store(first, cur);
+        cur = nxt;
     }
 }
 
@@ -100,7 +121,8 @@ hipError_t launch_step(const ActArgs &a, bool vec, bool contig, hipStream_t s)
 {
     if (vec) {
         const uint64_t chunks = (uint64_t)a.M * (uint64_t)(a.N >> 3);
-        const dim3 g((unsigned)((chunks + kActThreads * kActUnroll - 1) / (kActThreads * kActUnroll)));
+        const uint64_t groups = (chunks + kActThreads * kActUnroll - 1) / (kActThreads * kActUnroll);
+        const dim3 g((unsigned)(groups < kActGrid ? groups : kActGrid));
         // (the quotient's form is uniform over a call: one kernel each)
         bool fast = false;
         if constexpr (act_codes(STEP)) {
