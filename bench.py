@@ -476,19 +476,19 @@ def main():
             plain = [(lambda i=i: (g5.gemm_bf16(dX[i], dW[i][:, :N], dG[i], workspace=ws), g5.gemm_bf16(dX[i], dW[i][:, N:], dU[i], workspace=ws)))
                      for i in range(R)]
             # The unfused program: the two projections, then Z = bf16(bf16(SiLU(g)) * u)
-            # as element-wise passes over the written g and u (torch's bf16 silu
-            # and multiply, the same roundings as the fused epilogue).
-            unfused = [(lambda i=i: (plain[i](), torch.mul(torch.nn.functional.silu(dG[i]), dU[i], out=dZ[i])))
+            # as the activation chain's separate passes over the written g and u
+            # (SiLU, then the product: the same roundings as the fused epilogue).
+            dT = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+            unfused = [(lambda i=i: (plain[i](), g5.act_silu(dG[i], dT[i]), g5.act_mul(dT[i], dU[i], dZ[i])))
                        for i in range(R)]
             # Z stored as E4M3FN codes against a fixed range (the page's
             # continuation of the example): fused into the same epilogue, next
-            # to the bf16 SwiGLU followed by a separate quantization pass
-            # (torch element-wise ops: scale, clamp, convert).
+            # to the bf16 SwiGLU followed by the separate quantization pass
+            # (the activation chain's quantization step: the same codes).
             amax = 16.0
             dQ = [torch.empty((M, N), dtype=torch.uint8, device=dev) for _ in range(R)]
             fused8 = [(lambda i=i: g5.gemm_bf16_swiglu_e4m3(dX[i], dW[i], amax, dQ[i], workspace=ws)) for i in range(R)]
-            quant_after = [(lambda i=i: (fused[i](), dQ[i].view(torch.float8_e4m3fn).copy_(
-                torch.clamp(dZ[i].float() * (448.0 / amax), -448.0, 448.0)))) for i in range(R)]
+            quant_after = [(lambda i=i: (fused[i](), g5.act_quantize_e4m3(dZ[i], amax, dQ[i]))) for i in range(R)]
             ms = timed(fused, 30, 5, label="swiglu_ffn_bf16_1024x2x12288x4096")
             ms_plain = timed(plain, 30, 5, label="swiglu_ffn_two_plain_projections")
             ms_unfused = timed(unfused, 30, 5, label="swiglu_ffn_unfused_program")
@@ -509,7 +509,7 @@ def main():
                               "tflops": round(tf8, 2), "frac_peak": round(tf8 / PEAK_BF16_TFLOPS, 4),
                               "bf16_output_us": round(ms * 1e3, 3),
                               "bf16_then_quantize_us": round(ms_qa * 1e3, 3), "amax": amax, "rotations": R})
-            del dX, dW, dZ, dG, dU, dQ
+            del dX, dW, dZ, dG, dU, dQ, dT
 
     # ------------------------------------------------------------ the activation chain (Example 5-4)
     if args.only in ("all", "act_chain"):
