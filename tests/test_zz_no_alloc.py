@@ -66,6 +66,36 @@ def test_noalloc_matches_gemm_run_twice(oracle_mod, first, second, plan_name):
         check_bf16(host_values(C_na), oracle_mod.gemm_bf16(A, B), K, f"noalloc {M}x{N}x{K}")
 
 
+def test_noalloc_swiglu_e4m3_matches_gemm_run_twice():
+    """The SwiGLU with E4M3FN output through the scratch: the first call's
+    small-M plan pairs gate and up workgroups in exchange slots, the second
+    (smaller) splits K over four slices with counters and partial sums; the
+    codes equal gemm_run's with a caller workspace bit for bit, the range
+    travelling in alpha."""
+    L = g5.lib()
+    amax = 6.0
+    for i, (M, N, K, ks) in enumerate(((1, 12288, 4096, 1), (16, 4096, 2048, 4))):
+        _say(f"swiglu e4m3 {M}x{N}x{K} call {i}")
+        st, plan = g5.plan_query(g5.GEMM_OP_BF16_SWIGLU, M, N, K, c_type=g5.GEMM_OUT_E4M3)
+        assert st == 0 and plan.name == b"decode_splitk" and 0 < plan.workspace_bytes <= 16 << 20
+        assert plan.grid == (N // 128) * 2 * ks, plan.grid
+        g = np.random.default_rng([gi.SEED_BASE + 3800, i])
+        X = gi.to_bf16_bits(gi.normal(g, (M, K)))
+        Wgu = gi.to_bf16_bits(gi.normal(g, (K, 2 * N), 0.125))
+        dX, dW = dev_bf16(X), dev_bf16(Wgu)
+        Q_na = torch.full((M, N), 0xAA, dtype=torch.uint8, device="cuda")
+        Q_ws = torch.full((M, N), 0x55, dtype=torch.uint8, device="cuda")
+        wsbuf = torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+        args = lambda Q: (g5.GEMM_OP_BF16_SWIGLU, 1, M, N, K, dX.data_ptr(), K, 0, dW.data_ptr(), 2 * N, 0,
+                          Q.data_ptr(), N, 0, g5.GEMM_OUT_E4M3, amax, None, 0.0, None, None)
+        st_na = L.gemm_run_noalloc(*args(Q_na), _stream())
+        st_ws = L.gemm_run(*args(Q_ws), wsbuf.data_ptr(), wsbuf.numel(), _stream())
+        torch.cuda.synchronize()
+        assert st_na == 0 and st_ws == 0, (st_na, st_ws)
+        assert torch.equal(Q_na, Q_ws), "noalloc codes differ from gemm_run"
+        assert int((Q_na == 0x7e).sum()) + int((Q_na == 0xfe).sum()) > 0   # the range saturates some outputs
+
+
 def test_noalloc_rejects_calls_beyond_its_scratch():
     """A call whose plan needs more than the 16 MiB of scratch (here a
     realigned copy of 64 MiB of A rows) is refused before anything runs."""
