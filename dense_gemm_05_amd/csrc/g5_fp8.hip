@@ -50,21 +50,58 @@ __device__ __forceinline__ float wave_row_amax(const uint16_t *x, int64_t cols, 
     return m;
 }
 
-template <int NCH>
+// WPR waves per row (4 / WPR rows per workgroup of 4 waves): wave `part`
+// of a row holds its chunks (512 columns each) part, part + WPR, ...; the
+// row's maximum is the largest of its waves' (through LDS when WPR > 1: a
+// maximum does not depend on the order, so the codes are those of one wave
+// per row).  Several waves per row give a short matrix enough loads in
+// flight: X [1024, 4096] is 1024 rows, 4 per CU at one wave each.
+template <int NCH, int WPR>
 __global__ void __launch_bounds__(256) k_quant_rows_e4m3(const uint16_t *X, int64_t ldx, int64_t rows, int64_t cols,
                                                          int align_x, uint8_t *Q, int64_t ldq, int align_q,
                                                          float *scale)
 {
-    const int lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (r >= rows) return;                   // a whole wave; nothing below synchronises waves
-    const uint16_t *x = X + r * ldx;
-    uint8_t *q = Q + r * ldq;
-    const bool held = cols <= (int64_t)NCH * 512;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, part = wv % WPR;
+    const int64_t r = (int64_t)blockIdx.x * (4 / WPR) + wv / WPR;
+    const bool r_ok = r < rows;
+    if (WPR == 1 && !r_ok) return;          // a whole wave; nothing below synchronises waves
+    const uint16_t *x = X + (r_ok ? r : 0) * ldx;
+    uint8_t *q = Q + (r_ok ? r : 0) * ldq;
+    const bool held = cols <= (int64_t)NCH * 512 * WPR;
     u32x4 v[NCH];
-    const float amax = wave_row_amax<NCH>(x, cols, align_x, lane, v, held);
-    if (lane == 0) scale[r] = amax / 448.0f;
-    // amax is the same for the whole wave, so is the choice of quotient
+    auto absmax8 = [](float m, const u32x4 &c) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(c[i])), fabsf(bf16_hi(c[i]))));
+        return m;
+    };
+    float amax = 0.0f;
+    if (r_ok) {
+        if (held) {
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                const int64_t c = (int64_t)lane * 8 + (int64_t)(j * WPR + part) * 512;
+                v[j] = c < cols ? load_chunk8_bf16(x, c, cols, true, align_x) : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) amax = absmax8(amax, v[j]);
+        } else {
+            for (int64_t c = (int64_t)lane * 8 + (int64_t)part * 512; c < cols; c += 512 * WPR)
+                amax = absmax8(amax, load_chunk8_bf16(x, c, cols, true, align_x));
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    }
+    if constexpr (WPR > 1) {
+        __shared__ float wmax[4];
+        if (lane == 0) wmax[wv] = amax;
+        __syncthreads();
+        const int w0 = wv - part;
+#pragma unroll
+        for (int k = 0; k < WPR; ++k) amax = fmaxf(amax, wmax[w0 + k]);
+    }
+    if (!r_ok) return;
+    if (lane == 0 && part == 0) scale[r] = amax / 448.0f;
+    // amax is the same for the whole row, so is the choice of quotient
     const E4m3Quot qz(amax);
     auto emit = [&](auto fast, int64_t c, const u32x4 &cv) {
         constexpr bool F = decltype(fast)::value;
@@ -81,11 +118,11 @@ __global__ void __launch_bounds__(256) k_quant_rows_e4m3(const uint16_t *X, int6
         if (held) {
 #pragma unroll
             for (int j = 0; j < NCH; ++j) {
-                const int64_t c = (int64_t)lane * 8 + (int64_t)j * 512;
+                const int64_t c = (int64_t)lane * 8 + (int64_t)(j * WPR + part) * 512;
                 if (c < cols) emit(fast, c, v[j]);
             }
         } else {
-            for (int64_t c = (int64_t)lane * 8; c < cols; c += 512)
+            for (int64_t c = (int64_t)lane * 8 + (int64_t)part * 512; c < cols; c += 512 * WPR)
                 emit(fast, c, load_chunk8_bf16(x, c, cols, true, align_x));
         }
     };
@@ -96,8 +133,13 @@ __global__ void __launch_bounds__(256) k_quant_rows_e4m3(const uint16_t *X, int6
 hipError_t launch_quant_rows_e4m3(const uint16_t *X, int64_t ldx, int64_t rows, int64_t cols, int align_x,
                                   uint8_t *Q, int64_t ldq, int align_q, float *scale, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_quant_rows_e4m3<8>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, X, ldx, rows, cols,
-                       align_x, Q, ldq, align_q, scale);
+    // four waves per row while that leaves rows for at most 16 waves per CU
+    if (rows <= 1024)
+        hipLaunchKernelGGL((k_quant_rows_e4m3<2, 4>), dim3((unsigned)rows), dim3(256), 0, s, X, ldx, rows, cols,
+                           align_x, Q, ldq, align_q, scale);
+    else
+        hipLaunchKernelGGL((k_quant_rows_e4m3<8, 1>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, X, ldx,
+                           rows, cols, align_x, Q, ldq, align_q, scale);
     return hipGetLastError();
 }
 
