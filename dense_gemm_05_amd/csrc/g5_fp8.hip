@@ -13,11 +13,12 @@
 
 namespace g5 {
 
-// One wave per row, four rows per workgroup.  Pass 1 finds the row's
-// largest magnitude: each lane over its 16-byte chunks (all of a held row's
-// loads issued before the first is used), then across the wave by butterfly
-// exchanges (the tree reduction of the reduce page, "3.1 Tối ưu toán tử
-// CUDA Reduce", at wave scope: no LDS, no barrier).  Pass 2 writes the
+// Per-row quantization.  Pass 1 finds the row's largest magnitude: each
+// lane over its 16-byte chunks (all of a held row's loads issued before the
+// first is used), then across the wave by butterfly exchanges (the tree
+// reduction of the reduce page, "3.1 Tối ưu toán tử CUDA Reduce", at wave
+// scope: no LDS, no barrier; wave_row_amax does this for one wave per row,
+// k_quant_rows_e4m3 also for several waves per row).  Pass 2 writes the
 // codes: the quotient x * 448 / amax in binary32 (E4m3Quot), then the
 // hardware conversion, which rounds to the nearest E4M3FN value, ties to
 // even -- the code nearest to the exact quotient of Example 5-7.  The row's
