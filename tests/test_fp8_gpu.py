@@ -50,6 +50,7 @@ def check_fp8(C, ref, K, amax_a, amax_b, out, what):
     (4, 8192, 0, 0), (3, 9000, 4, 2),         # rows held in registers up to 4096; longer rows are read twice
     (2050, 1000, 3, 5), (4099, 4096, 0, 0),   # thousands of rows, ragged last workgroup
     (2049, 4100, 2, 0),
+    (1024, 4096, 0, 0), (1025, 1000, 0, 0),   # the last size with four waves per row, the first with one
 ])
 def test_quantize_rows_bit_exact(oracle_mod, rows, cols, ldx_pad, ldq_pad):
     """Codes and factors equal the oracle's bit for bit: normal rows of
